@@ -1,0 +1,52 @@
+"""CPU oracle for mask-aware (column-interval) attention.  TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, obviously-correct numpy code in float64.  It shares no code with the
+HIP library in `mask_aware_sparse_amd/`: no kernels, headers, tables, constants or
+helpers, and neither side imports the other.  Only `tests/`, the `smoke()` check in
+`__graft_entry__.py` and the `cpu_baseline` leg of `bench.py` may import it; the
+product path never does.
+
+Contents and the passage each part follows:
+
+  mask.py       dense expansion of the four column vectors (FlashMask-3 page,
+                Overview: per-key row bounds LTS/LTE/UTS/UTE); conversion from the
+                two-vector visible-interval form and its closed-form encoders
+                (FlashMask Guide, "Mathematical Formalization of Column-Wise
+                Sparsity").
+  attention.py  masked softmax attention forward (plain two-pass softmax) and its
+                analytic backward (Flash MSA guide, "Why Standard Attention Broke"
+                and "The Backward Pass: The Real Beast"; FlashMask Guide, dense
+                additive-mask formula).
+  tiles.py      block min/max, tile classification, per-block queues, tile costs
+                and the cost-descending (LPT) order (FlashMask-3 page, §3.1 tile
+                rule and KV Index Generator; §3.3 tile costs; FlashMask Guide,
+                "On-Chip Block-Skipping Logic").
+  schedule.py   list scheduling of weighted work items over P slots, the lower
+                bound max(ceil(sum/P), max w) and a brute-force optimum
+                (FlashMask-3 page, §3.3 and the IPO ablation table).
+
+Readings taken where the pages are silent are listed in the design doc; the main ones:
+masked intervals are half-open; rows masked everywhere give O = 0, LSE = -inf,
+dQ = 0 and add nothing to dK/dV; query head h uses kv head h // (H_q/H_kv);
+the softmax scale is 1/sqrt(d) and appears in dQ and dK by the chain rule.
+
+Every function is pinned by a `-m "not gpu"` test against something other than
+itself (printed mask pictures, closed forms, library routines on special cases,
+brute force, invariants); see tests/test_oracle_*.py.  Full-size numeric outputs
+have no printed values on the pages: beyond those pins they are parity unpinned.
+"""
+from .mask import (masked_rows, dense_mask, visible_interval_to_vectors,
+                   encode_causal, encode_packed, encode_dpo)
+from .attention import (attention_fwd, attention_bwd, attention_rows, attention_cols,
+                        attention_fwd_bwd)
+from .tiles import (block_minmax, classify, tile_truth, queues, tile_costs, lpt_order,
+                    ALPHA_PARTIAL, ALPHA_UNMASKED)
+from .schedule import list_schedule, lower_bound, brute_force_optimum
+
+__all__ = [
+    "masked_rows", "dense_mask", "visible_interval_to_vectors", "encode_causal",
+    "encode_packed", "encode_dpo", "attention_fwd", "attention_bwd", "attention_rows",
+    "attention_cols", "attention_fwd_bwd", "block_minmax", "classify", "tile_truth",
+    "queues", "tile_costs", "lpt_order", "ALPHA_PARTIAL", "ALPHA_UNMASKED",
+    "list_schedule", "lower_bound", "brute_force_optimum",
+]

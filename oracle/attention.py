@@ -1,0 +1,199 @@
+"""Masked softmax attention, forward and analytic backward, in float64 (oracle).
+
+Test infrastructure only.  What is computed (the method reaches exactly this, up
+to rounding order, because skipped tiles are fully hidden and contribute 0):
+
+  S = scale * Q K^T with S_ij = -inf where the column mask hides (i, j)
+  (FlashMask Guide, dense additive-mask formula S = QK^T/sqrt(d) + M);
+  O = softmax(S) V, computed here as the plain two-pass softmax (row max, then
+  exp and sum), not the online form, so that the GPU's online form is checked
+  against it (Flash MSA guide, "Why Standard Attention Broke" and "The Flash
+  Core"); LSE_i = m_i + ln l_i, the statistics the forward keeps for the backward
+  (same guide, "The Backward Pass").
+
+  Backward by the chain rule (Flash MSA guide, "The Backward Pass"; the page drops
+  the softmax scale in dQ and dK, restored here):
+  P_ij = exp(S_ij - LSE_i); dV = P^T dO; dP = dO V^T;
+  D_i = sum_j P_ij dP_ij; dS = P o (dP - D); dQ = scale dS K; dK = scale dS^T Q.
+
+Readings: a row whose every key is hidden gets O = 0, LSE = -inf, dQ = 0 and adds
+nothing to dK/dV.  Query head h uses kv head h // (H_q / H_kv) (GQA: K/V heads are
+shared by contiguous groups of query heads, Flash MSA guide FAQ).  dK/dV of a kv
+head sum over the query heads of its group.
+
+Rows are processed in blocks; each block expands only its own rows of the mask
+(never the full N x N matrix) and restricts its products to the columns that at
+least one of its rows can see, which is exact because hidden columns contribute 0.
+"""
+import numpy as np
+
+from .mask import masked_rows
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def _scale(d, scale):
+    return 1.0 / np.sqrt(d) if scale is None or scale <= 0 else float(scale)
+
+
+def _row_block(qh, kh, vh, vecs, r0, r1, scale, dOh=None):
+    """Forward (and, if dOh is given, backward) for rows [r0, r1) of one (b, h).
+
+    Returns O [R][d], LSE [R], and if dOh: dQ [R][d], cols, dK_part, dV_part where
+    the parts are [len(cols)][d] contributions to the key columns `cols`."""
+    lts, lte, uts, ute = vecs
+    hid = masked_rows(lts, lte, uts, ute, r0, r1)            # [R][N]
+    cols = np.nonzero(~hid.all(axis=0))[0]
+    R, d = r1 - r0, qh.shape[1]
+    O = np.zeros((R, d))
+    lse = np.full(R, -np.inf)
+    if dOh is not None:
+        dQ = np.zeros((R, d))
+        empty = np.zeros((0, d))
+    if cols.size == 0:
+        if dOh is None:
+            return O, lse
+        return O, lse, dQ, cols, empty, empty
+    q = qh[r0:r1]
+    k = kh[cols]
+    v = vh[cols]
+    h = hid[:, cols]
+    S = scale * (q @ k.T)
+    S[h] = -np.inf
+    m = S.max(axis=1)                                          # -inf for all-hidden rows
+    live = np.isfinite(m)
+    e = np.zeros_like(S)
+    e[live] = np.exp(S[live] - m[live, None])                  # exp(-inf) = 0 where hidden
+    l = e.sum(axis=1)
+    O[live] = (e[live] / l[live, None]) @ v
+    lse[live] = m[live] + np.log(l[live])
+    if dOh is None:
+        return O, lse
+    do = dOh[r0:r1]
+    P = np.zeros_like(S)
+    P[live] = np.exp(S[live] - lse[live, None])
+    dP = do @ v.T
+    D = (P * dP).sum(axis=1)
+    dS = P * (dP - D[:, None])
+    dQ = scale * (dS @ k)
+    dK_part = scale * (dS.T @ q)
+    dV_part = P.T @ do
+    return O, lse, dQ, cols, dK_part, dV_part
+
+
+def _check(q, k, v, vecs):
+    B, Hq, N, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    assert (B, N, d) == (Bk, Nk, dk) and v.shape == k.shape
+    assert Hq % Hkv == 0
+    for x in vecs:
+        assert np.asarray(x).shape == (B, N)
+    return B, Hq, Hkv, N, d, Hq // Hkv
+
+
+def attention_fwd(q, k, v, lts, lte, uts, ute, scale=None, row_block=256):
+    """O [B][H_q][N][d] and LSE [B][H_q][N] (natural log) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    vecs = (lts, lte, uts, ute)
+    B, Hq, Hkv, N, d, g = _check(q, k, v, vecs)
+    sc = _scale(d, scale)
+    O = np.zeros((B, Hq, N, d))
+    LSE = np.full((B, Hq, N), -np.inf)
+    for b in range(B):
+        vb = tuple(np.asarray(x)[b] for x in vecs)
+        for h in range(Hq):
+            kv = h // g
+            for r0 in range(0, N, row_block):
+                r1 = min(r0 + row_block, N)
+                O[b, h, r0:r1], LSE[b, h, r0:r1] = _row_block(q[b, h], k[b, kv], v[b, kv],
+                                                              vb, r0, r1, sc)
+    return O, LSE
+
+
+def attention_fwd_bwd(q, k, v, do, lts, lte, uts, ute, scale=None, row_block=256):
+    """(O, LSE, dQ, dK, dV) in float64; the backward recomputes the softmax from
+    its definition (no statistic comes from anywhere but this function)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    vecs = (lts, lte, uts, ute)
+    B, Hq, Hkv, N, d, g = _check(q, k, v, vecs)
+    sc = _scale(d, scale)
+    O = np.zeros((B, Hq, N, d))
+    LSE = np.full((B, Hq, N), -np.inf)
+    dQ = np.zeros((B, Hq, N, d))
+    dK = np.zeros((B, Hkv, N, d))
+    dV = np.zeros((B, Hkv, N, d))
+    for b in range(B):
+        vb = tuple(np.asarray(x)[b] for x in vecs)
+        for h in range(Hq):
+            kv = h // g
+            for r0 in range(0, N, row_block):
+                r1 = min(r0 + row_block, N)
+                o, lse, dq, cols, dkp, dvp = _row_block(q[b, h], k[b, kv], v[b, kv], vb,
+                                                        r0, r1, sc, dOh=do[b, h])
+                O[b, h, r0:r1], LSE[b, h, r0:r1], dQ[b, h, r0:r1] = o, lse, dq
+                dK[b, kv, cols] += dkp
+                dV[b, kv, cols] += dvp
+    return O, LSE, dQ, dK, dV
+
+
+def attention_bwd(q, k, v, do, lts, lte, uts, ute, scale=None, row_block=256):
+    """(dQ, dK, dV) in float64."""
+    _, _, dQ, dK, dV = attention_fwd_bwd(q, k, v, do, lts, lte, uts, ute, scale, row_block)
+    return dQ, dK, dV
+
+
+def attention_rows(q, k, v, do, lts, lte, uts, ute, b, h, rows, scale=None):
+    """O, LSE and dQ of selected query rows of one (b, h).  Each row is computed
+    on its own from the full key axis, so any row of a full-size problem can be
+    checked.  `do` may be None (then dQ is None)."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    kv = h // (Hq // Hkv)
+    d = q.shape[3]
+    sc = _scale(d, scale)
+    vb = tuple(np.asarray(x)[b] for x in (lts, lte, uts, ute))
+    qh, kh, vh = _f64(q[b, h]), _f64(k[b, kv]), _f64(v[b, kv])
+    dOh = None if do is None else _f64(do[b, h])
+    O = np.zeros((len(rows), d)); LSE = np.zeros(len(rows)); dQ = np.zeros((len(rows), d))
+    for t, r in enumerate(rows):
+        res = _row_block(qh, kh, vh, vb, int(r), int(r) + 1, sc, dOh=dOh)
+        O[t], LSE[t] = res[0][0], res[1][0]
+        if dOh is not None:
+            dQ[t] = res[2][0]
+    return O, LSE, (dQ if dOh is not None else None)
+
+
+def attention_cols(q, k, v, do, lts, lte, uts, ute, b, kv, cols, scale=None, row_block=256):
+    """dK and dV of selected key columns of one (b, kv head).  Every query row of
+    the group that sees any selected column is computed in full (its softmax needs
+    the whole row), so this is cheap only where the selected columns are seen by
+    few rows."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    g = Hq // Hkv
+    d = q.shape[3]
+    sc = _scale(d, scale)
+    lv = [np.asarray(x)[b] for x in (lts, lte, uts, ute)]
+    N = len(lv[0])
+    cols = np.asarray(cols)
+    # rows that see at least one selected column
+    need = np.zeros(N, dtype=bool)
+    for c in cols:
+        rows_hidden = masked_rows(*(x[c:c + 1] for x in lv), 0, N)[:, 0]
+        need |= ~rows_hidden
+    # Rows that see none of the selected columns contribute exactly 0 to them, so
+    # whole row blocks that contain at least one needed row can be computed.
+    starts = sorted({int(r) // row_block * row_block for r in np.nonzero(need)[0]})
+    kh, vh = _f64(k[b, kv]), _f64(v[b, kv])
+    dK = np.zeros((len(cols), d)); dV = np.zeros((len(cols), d))
+    for h in range(kv * g, (kv + 1) * g):
+        qh, dOh = _f64(q[b, h]), _f64(do[b, h])
+        for r0 in starts:
+            r1 = min(r0 + row_block, N)
+            _, _, _, cs, dkp, dvp = _row_block(qh, kh, vh, lv, r0, r1, sc, dOh=dOh)
+            where = np.searchsorted(cs, cols)
+            hit = (where < len(cs)) & (cs[np.minimum(where, len(cs) - 1)] == cols) \
+                if len(cs) else np.zeros(len(cols), dtype=bool)
+            dK[hit] += dkp[where[hit]]
+            dV[hit] += dvp[where[hit]]
+    return dK, dV

@@ -1,0 +1,75 @@
+"""Dense expansion of the column-wise mask (oracle; test infrastructure only).
+
+FlashMask-3 page, Overview: each key column j stores four query-row bounds
+LTS_j, LTE_j, UTS_j, UTE_j.  Reading adopted (the page prints no membership
+formula): the hidden rows of column j are the half-open intervals [LTS_j, LTE_j)
+and [UTS_j, UTE_j); an interval whose start is not below its end is empty.
+"""
+import numpy as np
+
+
+def masked_rows(lts, lte, uts, ute, r0, r1):
+    """Boolean [r1-r0][N] block of the dense mask for one batch row: True = hidden.
+
+    masked(i, j) = (LTS_j <= i < LTE_j) or (UTS_j <= i < UTE_j)."""
+    i = np.arange(r0, r1, dtype=np.int64)[:, None]
+    lts = np.asarray(lts, dtype=np.int64)[None, :]
+    lte = np.asarray(lte, dtype=np.int64)[None, :]
+    uts = np.asarray(uts, dtype=np.int64)[None, :]
+    ute = np.asarray(ute, dtype=np.int64)[None, :]
+    return ((lts <= i) & (i < lte)) | ((uts <= i) & (i < ute))
+
+
+def dense_mask(lts, lte, uts, ute):
+    """Full N x N dense mask for one batch row (small N only)."""
+    n = len(lts)
+    return masked_rows(lts, lte, uts, ute, 0, n)
+
+
+def visible_interval_to_vectors(fms, fme, n):
+    """FlashMask Guide, "Mathematical Formalization of Column-Wise Sparsity": key
+    column j is visible to rows FMS_j <= i <= FME_j (inclusive).  In the four-vector
+    form the hidden rows are [0, FMS_j) and [FME_j + 1, N):
+    UTS = 0, UTE = FMS, LTS = FME + 1, LTE = N."""
+    fms = np.asarray(fms, dtype=np.int64)
+    fme = np.asarray(fme, dtype=np.int64)
+    uts = np.zeros_like(fms)
+    ute = fms.copy()
+    lts = np.minimum(fme + 1, n)
+    lte = np.full_like(fms, n)
+    return lts, lte, uts, ute
+
+
+def encode_causal(n):
+    """Causal closed form (FlashMask Guide, same section): FMS_j = j, FME_j = N-1."""
+    j = np.arange(n)
+    return j.copy(), np.full(n, n - 1)
+
+
+def encode_packed(lengths, causal=True):
+    """Packed documents (same section): for key j in document [s_k, e_k]
+    FMS_j = j (causal) or s_k (bidirectional), FME_j = e_k."""
+    n = int(sum(lengths))
+    fms = np.zeros(n, dtype=np.int64)
+    fme = np.zeros(n, dtype=np.int64)
+    s = 0
+    for length in lengths:
+        e = s + length - 1
+        for j in range(s, e + 1):
+            fms[j] = j if causal else s
+            fme[j] = e
+        s = e + 1
+    return fms, fme
+
+
+def encode_dpo(prompt, chosen, rejected):
+    """DPO pair [prompt | chosen | rejected] (same section): prompt keys are
+    visible from j to the end of the sequence; chosen keys from j to the end of
+    the chosen span; rejected keys from j to the end of the sequence."""
+    n = prompt + chosen + rejected
+    fms = np.arange(n, dtype=np.int64)
+    fme = np.empty(n, dtype=np.int64)
+    fme[:prompt] = n - 1
+    fme[prompt:prompt + chosen] = prompt + chosen - 1
+    fme[prompt + chosen:] = n - 1
+    return fms, fme

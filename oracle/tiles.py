@@ -1,0 +1,141 @@
+"""Tile classification, queues, costs and LPT order (oracle; test infrastructure).
+
+FlashMask-3 page, §3.1 ("A third warp role that reads the mask"): for a tile of
+query rows [q0, q1) and a KV block, the block-wise max/min of the vectors decide
+whether the tile is skipped, unmasked or partial; the KV Index Generator emits,
+per Q-block, a queue of the KV blocks that are not skipped, each tagged partial or
+unmasked, visited right to left.  §3.3: a tile costs 0 (skipped), alpha_p
+(partial) or alpha_u (unmasked), with alpha_u = 1 and alpha_p = 1.3 given as
+illustrative values.  The FlashMask Guide ("On-Chip Block-Skipping Logic") states
+the same rule in the two-vector form.
+
+The page prints the rule for the LTS/UTE pair only (it assumes LTE = N and
+UTS = 0).  Reading adopted for all four vectors, which reduces to the printed rule
+in that case and is sound for any vectors:
+
+  skip     = (q0 >= max LTS and q1 <= min LTE) or (q0 >= max UTS and q1 <= min UTE)
+  unmasked = (q1 <= min LTS or q0 >= max LTE) and (q1 <= min UTS or q0 >= max UTE)
+  class    = 0 if skip, else 2 if unmasked, else 1 (partial)
+
+q1 and the block's last column are clamped to N (ragged tails).  The class is the
+rule's output: a tile the rule calls partial may still be hidden everywhere when
+both intervals cover it together (the rule is conservative, never unsound).
+"""
+import numpy as np
+
+from .mask import masked_rows
+
+SKIP, PARTIAL, UNMASKED = 0, 1, 2
+# alpha_p : alpha_u = 1.3 : 1 in integer units (FlashMask-3 page, §3.3).
+ALPHA_PARTIAL = 13
+ALPHA_UNMASKED = 10
+
+
+def _nblocks(n, b):
+    return (n + b - 1) // b
+
+
+def block_minmax(vec, bk):
+    """min and max of one vector [B][N] over each KV block -> two arrays [B][nKB]."""
+    vec = np.asarray(vec, dtype=np.int64)
+    B, N = vec.shape
+    nkb = _nblocks(N, bk)
+    mn = np.zeros((B, nkb), dtype=np.int64)
+    mx = np.zeros((B, nkb), dtype=np.int64)
+    for b in range(B):
+        for kb in range(nkb):
+            seg = vec[b, kb * bk:min((kb + 1) * bk, N)]
+            mn[b, kb] = seg.min()
+            mx[b, kb] = seg.max()
+    return mn, mx
+
+
+def classify(lts, lte, uts, ute, bq, bk):
+    """Tile class [B][nQB][nKB] (uint8: 0 skip, 1 partial, 2 unmasked)."""
+    B, N = np.asarray(lts).shape
+    nqb, nkb = _nblocks(N, bq), _nblocks(N, bk)
+    (mnLTS, mxLTS), (mnLTE, mxLTE), (mnUTS, mxUTS), (mnUTE, mxUTE) = (
+        block_minmax(x, bk) for x in (lts, lte, uts, ute))
+    cls = np.zeros((B, nqb, nkb), dtype=np.uint8)
+    for b in range(B):
+        for kb in range(nkb):
+            for qb in range(nqb):
+                q0 = qb * bq
+                q1 = min(q0 + bq, N)
+                skip = ((q0 >= mxLTS[b, kb] and q1 <= mnLTE[b, kb]) or
+                        (q0 >= mxUTS[b, kb] and q1 <= mnUTE[b, kb]))
+                unmasked = ((q1 <= mnLTS[b, kb] or q0 >= mxLTE[b, kb]) and
+                            (q1 <= mnUTS[b, kb] or q0 >= mxUTE[b, kb]))
+                cls[b, qb, kb] = SKIP if skip else (UNMASKED if unmasked else PARTIAL)
+    return cls
+
+
+def tile_truth(lts, lte, uts, ute, bq, bk):
+    """Brute force from the dense mask: 0 if every cell of the tile is hidden, 2 if
+    none is, 1 otherwise.  The rule's class must agree wherever it says 0 or 2."""
+    lts, lte, uts, ute = (np.asarray(x) for x in (lts, lte, uts, ute))
+    B, N = lts.shape
+    nqb, nkb = _nblocks(N, bq), _nblocks(N, bk)
+    out = np.zeros((B, nqb, nkb), dtype=np.uint8)
+    for b in range(B):
+        for qb in range(nqb):
+            q0, q1 = qb * bq, min(qb * bq + bq, N)
+            hid = masked_rows(lts[b], lte[b], uts[b], ute[b], q0, q1)
+            for kb in range(nkb):
+                t = hid[:, kb * bk:min(kb * bk + bk, N)]
+                out[b, qb, kb] = SKIP if t.all() else (UNMASKED if not t.any() else PARTIAL)
+    return out
+
+
+def queues(cls):
+    """Queues and counts from the class matrix.
+
+    Forward (per Q-block, KV blocks visited right to left as in §3.1's example):
+      q_queue[b][qb] = [kb | partial << 31 for kb = nKB-1 .. 0 if class != skip]
+      q_count[b][qb] = (n_partial, n_unmasked)
+    Backward (per KV block, Q-blocks in ascending order; a reading, the pages give
+    no order for it):
+      k_queue[b][kb] = [qb | partial << 31 for qb = 0 .. nQB-1 if class != skip]
+      k_count[b][kb] = (n_partial, n_unmasked)
+    Queues are returned as int32 arrays padded with -1 after their last entry."""
+    cls = np.asarray(cls)
+    B, nqb, nkb = cls.shape
+    tag = np.uint32(1 << 31)
+    q_queue = np.full((B, nqb, nkb), -1, dtype=np.int64)
+    q_count = np.zeros((B, nqb, 2), dtype=np.int32)
+    k_queue = np.full((B, nkb, nqb), -1, dtype=np.int64)
+    k_count = np.zeros((B, nkb, 2), dtype=np.int32)
+    for b in range(B):
+        for qb in range(nqb):
+            t = 0
+            for kb in range(nkb - 1, -1, -1):
+                c = cls[b, qb, kb]
+                if c != SKIP:
+                    q_queue[b, qb, t] = kb | (int(tag) if c == PARTIAL else 0)
+                    t += 1
+                    q_count[b, qb, 0 if c == PARTIAL else 1] += 1
+        for kb in range(nkb):
+            t = 0
+            for qb in range(nqb):
+                c = cls[b, qb, kb]
+                if c != SKIP:
+                    k_queue[b, kb, t] = qb | (int(tag) if c == PARTIAL else 0)
+                    t += 1
+                    k_count[b, kb, 0 if c == PARTIAL else 1] += 1
+    as_i32 = lambda a: np.where(a < 0, -1, a).astype(np.uint32).view(np.int32)
+    return as_i32(q_queue), q_count, as_i32(k_queue), k_count
+
+
+def tile_costs(count, alpha_p=ALPHA_PARTIAL, alpha_u=ALPHA_UNMASKED):
+    """cost = alpha_p * n_partial + alpha_u * n_unmasked (skipped tiles cost 0)."""
+    count = np.asarray(count, dtype=np.int64)
+    return alpha_p * count[..., 0] + alpha_u * count[..., 1]
+
+
+def lpt_order(costs):
+    """Longest-processing-time-first order of the flattened items: indices sorted
+    by cost descending, ties by ascending index (so (b, block) ascending)."""
+    c = np.asarray(costs, dtype=np.int64).reshape(-1)
+    idx = list(range(len(c)))
+    idx.sort(key=lambda i: (-c[i], i))
+    return np.asarray(idx, dtype=np.int32)

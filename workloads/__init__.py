@@ -1,0 +1,240 @@
+"""Seeded synthetic inputs for mask-aware attention: mask vectors and Q/K/V/dO.
+
+This module is shared by the CPU oracle and the HIP path.  It builds inputs only:
+it holds none of the method's arithmetic (no masking predicate, no tile rule, no
+softmax).  Every workload is a procedure on a seed, so the same seed gives the same
+bytes on every machine.
+
+Mask encoding.  Each key column j carries four int32 row bounds
+(LTS_j, LTE_j, UTS_j, UTE_j); the rows of column j that are hidden are the two
+half-open intervals [LTS_j, LTE_j) and [UTS_j, UTE_j).  This is the column-wise
+O(n) representation named in the Overview of "FlashMask-3: Efficient and Expressive
+Mask-Aware Distributed Attention".  Unless a workload says otherwise UTS = 0 and
+LTE = N, the common case in which the upper interval holds the rows above the
+diagonal band and the lower interval the rows below it.
+
+The mask families are the ones the pages list (document packing, prefix-LM,
+share-question / DPO, sliding window with sinks, random eviction: FlashMask-3 page,
+Overview and Results; FlashMask Guide, "The Diversity of Real-World Attention
+Masks").  The pages give families, not procedures; the procedures below are the
+plainest readings, fixed once so that runs are reproducible.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+HEAD_DIM = 128
+
+
+@dataclass
+class Workload:
+    name: str
+    batch: int
+    heads_q: int
+    heads_kv: int
+    seqlen: int
+    head_dim: int
+    lts: np.ndarray          # int32 [B][N]
+    lte: np.ndarray
+    uts: np.ndarray
+    ute: np.ndarray
+    seed: int
+    info: dict = field(default_factory=dict)
+
+    def vectors(self):
+        return self.lts, self.lte, self.uts, self.ute
+
+
+def _empty_vectors(batch: int, n: int):
+    lts = np.full((batch, n), n, dtype=np.int64)
+    lte = np.full((batch, n), n, dtype=np.int64)
+    uts = np.zeros((batch, n), dtype=np.int64)
+    ute = np.zeros((batch, n), dtype=np.int64)
+    return lts, lte, uts, ute
+
+
+def _finish(name, batch, hq, hkv, n, vecs, seed, info):
+    lts, lte, uts, ute = (np.ascontiguousarray(v, dtype=np.int32) for v in vecs)
+    return Workload(name, batch, hq, hkv, n, HEAD_DIM, lts, lte, uts, ute, seed, info)
+
+
+def causal_doc(seed: int = 0, n: int = 1024, ndocs: int = 4, batch: int = 1,
+               heads_q: int = 1, heads_kv: int = 1) -> Workload:
+    """Causal document packing: `ndocs` documents whose lengths come from
+    `ndocs-1` distinct sorted cut points.  Key j of document [s, e) is hidden
+    from rows >= e (LTS=e, LTE=N) and from rows < j (UTS=0, UTE=j)."""
+    rng = np.random.default_rng(seed)
+    lts, lte, uts, ute = _empty_vectors(batch, n)
+    docs = []
+    for b in range(batch):
+        cuts = np.sort(rng.choice(np.arange(1, n), ndocs - 1, replace=False))
+        bounds = np.r_[0, cuts, n]
+        docs.append(np.diff(bounds).tolist())
+        for s, e in zip(bounds[:-1], bounds[1:]):
+            j = np.arange(s, e)
+            lts[b, s:e] = e
+            ute[b, s:e] = j
+    return _finish("causal_doc", batch, heads_q, heads_kv, n, (lts, lte, uts, ute), seed,
+                   {"doc_lengths": docs})
+
+
+def prefix_lm_doc(seed: int = 0, n: int = 8192, batch: int = 4, heads_q: int = 32,
+                  heads_kv: int = 8, lo: int = 512, hi: int = 2048,
+                  prefix_frac: float = 0.25) -> Workload:
+    """Prefix-LM document packing.  Document lengths are drawn uniformly in
+    [lo, hi] until they cover N; the last one is cut to fit.  Each document
+    [s, e) has a bidirectional prefix of floor(L/4) keys (visible to every row
+    of the document: UTE=s) followed by causal keys (UTE=j); no key is visible
+    outside its document (LTS=e)."""
+    rng = np.random.default_rng(seed)
+    lts, lte, uts, ute = _empty_vectors(batch, n)
+    docs = []
+    for b in range(batch):
+        s = 0
+        lens = []
+        while s < n:
+            length = min(int(rng.integers(lo, hi + 1)), n - s)
+            e = s + length
+            p = int(length * prefix_frac)
+            lts[b, s:e] = e
+            ute[b, s:s + p] = s
+            ute[b, s + p:e] = np.arange(s + p, e)
+            lens.append(length)
+            s = e
+        docs.append(lens)
+    return _finish("prefix_lm_doc", batch, heads_q, heads_kv, n, (lts, lte, uts, ute), seed,
+                   {"doc_lengths": docs})
+
+
+def share_question(seed: int = 0, n: int = 32768, batch: int = 1, heads_q: int = 64,
+                   heads_kv: int = 1, samples: int = 4, answers: int = 3,
+                   prompt_range=(2048, 4096), answer_range=(1024, 2048)) -> Workload:
+    """Share-question (DPO-style) packing: `samples` packed samples, each a causal
+    prompt followed by `answers` causal answers that see the prompt but not each
+    other.  Lengths are redrawn together until they fit in N; the tail is padding
+    whose keys are hidden from every row (UTE=N), so padding rows see nothing."""
+    rng = np.random.default_rng(seed)
+    lts, lte, uts, ute = _empty_vectors(batch, n)
+    layout = []
+    for b in range(batch):
+        while True:
+            P = rng.integers(prompt_range[0], prompt_range[1] + 1, samples)
+            A = rng.integers(answer_range[0], answer_range[1] + 1, (samples, answers))
+            if int(P.sum() + A.sum()) <= n:
+                break
+        s = 0
+        for k in range(samples):
+            e = s + int(P[k]) + int(A[k].sum())
+            lts[b, s:s + P[k]] = e
+            ute[b, s:s + P[k]] = np.arange(s, s + P[k])
+            a0 = s + int(P[k])
+            for a in range(answers):
+                a1 = a0 + int(A[k, a])
+                lts[b, a0:a1] = a1
+                ute[b, a0:a1] = np.arange(a0, a1)
+                a0 = a1
+            s = e
+        ute[b, s:] = n                    # padding keys: hidden from all rows
+        layout.append({"prompts": P.tolist(), "answers": A.tolist(), "pad_start": s,
+                       "pad": n - s})
+    return _finish("share_question", batch, heads_q, heads_kv, n, (lts, lte, uts, ute), seed,
+                   {"layout": layout})
+
+
+def sliding_window_sinks(seed: int = 0, n: int = 131072, batch: int = 1, heads_q: int = 64,
+                         heads_kv: int = 1, window: int = 4096, sinks: int = 64) -> Workload:
+    """Causal sliding window plus global sink keys.  Key j is hidden from rows < j
+    (UTE=j) and, unless it is one of the first `sinks` keys, from rows
+    >= j + window (LTS=min(j+window, N)).  Deterministic; `seed` is recorded only."""
+    lts, lte, uts, ute = _empty_vectors(batch, n)
+    j = np.arange(n)
+    for b in range(batch):
+        ute[b] = j
+        lts[b] = np.minimum(j + window, n)
+        lts[b, :sinks] = n
+    return _finish("sliding_window_sinks", batch, heads_q, heads_kv, n, (lts, lte, uts, ute),
+                   seed, {"window": window, "sinks": sinks})
+
+
+def random_eviction(seed: int = 0, n: int = 131072, batch: int = 1, heads_q: int = 64,
+                    heads_kv: int = 1) -> Workload:
+    """Random-eviction causal mask: key j is visible to rows j .. LTS_j-1, where
+    LTS_j is uniform on [j+1, N] (one draw per key, in key order)."""
+    rng = np.random.default_rng(seed)
+    lts, lte, uts, ute = _empty_vectors(batch, n)
+    j = np.arange(n)
+    for b in range(batch):
+        lts[b] = rng.integers(j + 1, n + 1)
+        ute[b] = j
+    return _finish("random_eviction", batch, heads_q, heads_kv, n, (lts, lte, uts, ute), seed, {})
+
+
+def causal(n: int, batch: int = 1, heads_q: int = 1, heads_kv: int = 1) -> Workload:
+    """Plain causal attention: key j hidden from rows < j only."""
+    lts, lte, uts, ute = _empty_vectors(batch, n)
+    ute[:] = np.arange(n)
+    return _finish("causal", batch, heads_q, heads_kv, n, (lts, lte, uts, ute), 0, {})
+
+
+def random_intervals(seed: int, n: int, batch: int = 1, heads_q: int = 1,
+                     heads_kv: int = 1, p_empty: float = 0.2) -> Workload:
+    """Adversarial vectors: both intervals of every column are random, may be
+    empty (start >= end), may cover every row, and may overlap."""
+    rng = np.random.default_rng(seed)
+    a = rng.integers(0, n + 1, (4, batch, n))
+    lts = np.minimum(a[0], a[1]); lte = np.maximum(a[0], a[1])
+    uts = np.minimum(a[2], a[3]); ute = np.maximum(a[2], a[3])
+    e1 = rng.random((batch, n)) < p_empty
+    e2 = rng.random((batch, n)) < p_empty
+    lts = np.where(e1, lte, lts)            # empty lower interval (start == end)
+    uts = np.where(e2, ute + 1, uts)         # empty upper interval (start > end)
+    uts = np.minimum(uts, n)
+    return _finish("random_intervals", batch, heads_q, heads_kv, n, (lts, lte, uts, ute), seed, {})
+
+
+# The five benchmark workloads, in order.  Shapes and mask families follow the
+# synthetic stand-ins for the pages' mask families (see the design doc for the recipe).
+CONFIGS = {
+    "c1_causal_doc_1k": lambda seed=0: causal_doc(seed),
+    "c2_prefix_lm_doc_8k": lambda seed=0: prefix_lm_doc(seed),
+    "c3_share_question_32k": lambda seed=0: share_question(seed),
+    "c4_sliding_window_128k": lambda seed=0: sliding_window_sinks(seed),
+    "c5_random_eviction_128k": lambda seed=0: random_eviction(seed),
+}
+CONFIG_NAMES = list(CONFIGS)
+
+
+def make_workload(name: str, seed: int = 0) -> Workload:
+    return CONFIGS[name](seed)
+
+
+def make_tensors(w: Workload, seed: int | None = None, device: str = "cpu",
+                 need_grad_inputs: bool = True):
+    """Q, K, V, dO as bf16 drawn N(0,1) in that order, rounded to nearest even.
+
+    On the CPU the draws come from torch's CPU generator seeded with `seed`; on a
+    GPU device from that device's generator with the same seed (the large
+    workloads are drawn where they live).  Callers hand the *same* tensors to the
+    oracle (as host copies) and to the HIP path, so parity never depends on the
+    two generators agreeing."""
+    import torch
+    seed = w.seed if seed is None else seed
+    g = torch.Generator(device=device).manual_seed(seed)
+    shp_q = (w.batch, w.heads_q, w.seqlen, w.head_dim)
+    shp_k = (w.batch, w.heads_kv, w.seqlen, w.head_dim)
+
+    def draw(shape):
+        return torch.randn(shape, dtype=torch.float32, generator=g, device=device).to(torch.bfloat16)
+
+    q = draw(shp_q)
+    k = draw(shp_k)
+    v = draw(shp_k)
+    do = draw(shp_q) if need_grad_inputs else None
+    return q, k, v, do
+
+
+def mask_tensors(w: Workload, device: str = "cpu"):
+    import torch
+    return tuple(torch.from_numpy(np.ascontiguousarray(x)).to(device) for x in w.vectors())
