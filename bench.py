@@ -1,0 +1,185 @@
+#!/usr/bin/env python3
+"""Benchmark: mask-aware attention forward + backward on one MI355X.
+
+One step = fm_attn_fwd + fm_attn_bwd (classification, LPT order, attention kernels,
+backward pre/post kernels) over one batch of seeded synthetic inputs resident in HBM.
+
+Metric: effective TFLOP/s counting attended (q, k) pairs only, 4*d flop per pair in
+the forward and 10*d in the backward (14*d = 1792 flop per pair at d = 128), over the
+whole step time.  The roofline entry covers the dominant kernel (the backward attention
+kernel): algorithmic flop per launch (10*d per attended pair) / its average duration,
+measured with HIP events recorded around that kernel on the stream it runs on.
+
+Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+DEFAULT_WORKLOAD = "c2_prefix_lm_doc_8k"
+
+
+def attended_pairs(w):
+    """Attended (q, k) pairs summed over batch rows and query heads, by interval
+    arithmetic on the column vectors (N minus the union of the two hidden intervals)."""
+    total = 0
+    n = w.seqlen
+    for b in range(w.batch):
+        lts, lte, uts, ute = (np.asarray(x[b], dtype=np.int64) for x in w.vectors())
+        a1, b1 = np.clip(lts, 0, n), np.clip(lte, 0, n)
+        a2, b2 = np.clip(uts, 0, n), np.clip(ute, 0, n)
+        l1, l2 = np.maximum(b1 - a1, 0), np.maximum(b2 - a2, 0)
+        inter = np.maximum(np.minimum(b1, b2) - np.maximum(a1, a2), 0)
+        inter = np.where((l1 > 0) & (l2 > 0), inter, 0)
+        total += int((n - (l1 + l2 - inter)).sum())
+    return total * w.heads_q
+
+
+def cpu_baseline(w, q, k, v, do, budget_s):
+    """Time the fp64 oracle on a bounded sample of the same workload: whole (b, h)
+    problems, taken in order b = 0.., h spread over the heads, until the budget is
+    spent.  Reported in the metric's unit over the sample's attended pairs."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    g = w.heads_q // w.heads_kv
+    heads = list(range(0, w.heads_q, max(1, w.heads_q // 8)))
+    done, pairs, t_total = [], 0, 0.0
+    for b in range(w.batch):
+        for h in heads:
+            kvh = h // g
+            f = lambda t, hh: t[b:b + 1, hh:hh + 1].float().cpu().numpy().astype(np.float64)
+            sub = [x[b:b + 1] for x in w.vectors()]
+            args = (f(q, h), f(k, kvh), f(v, kvh), f(do, h))
+            t0 = time.perf_counter()
+            oracle.attention_fwd_bwd(*args, *sub)
+            t_total += time.perf_counter() - t0
+            one = workloads.Workload(w.name, 1, 1, 1, w.seqlen, w.head_dim,
+                                     *[np.ascontiguousarray(x) for x in sub], w.seed)
+            pairs += attended_pairs(one)
+            done.append((b, h))
+            if t_total >= budget_s:
+                break
+        if t_total >= budget_s:
+            break
+    flop = 14 * w.head_dim * pairs
+    return {"value": flop / t_total / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(done)} of {w.batch * w.heads_q} (b,h) problems of {w.name}, "
+                      f"fp64 numpy fwd+bwd, {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=workloads.CONFIG_NAMES)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the cpu_baseline sample (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; multi-GPU runs are not supported",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mask_aware_sparse_amd as fm
+
+    dev = "cuda"
+    w = workloads.make_workload(args.workload, args.seed)
+    q, k, v, do = workloads.make_tensors(w, device=dev)
+    vec = workloads.mask_tensors(w, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.heads_q, w.seqlen), dtype=torch.float32, device=dev)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    ws_f = torch.empty(fm.workspace_size(w.batch, w.heads_q, w.heads_kv, w.seqlen, fm.OP_FWD),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(fm.workspace_size(w.batch, w.heads_q, w.heads_kv, w.seqlen, fm.OP_BWD),
+                       dtype=torch.uint8, device=dev)
+    A = attended_pairs(w)
+    d = w.head_dim
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
+          for _ in range(args.steps)]
+
+    def step(e=None):
+        if e is not None:
+            e[0].record()
+        fm.attn_fwd(q, k, v, *vec, ws=ws_f, out=o, lse=lse,
+                    events=None if e is None else (e[1], e[2]))
+        fm.attn_bwd(q, k, v, o, lse, do, *vec, ws=ws_b, grads=grads,
+                    events=None if e is None else (e[3], e[4]))
+        if e is not None:
+            e[5].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    step_ms = np.array([e[0].elapsed_time(e[5]) for e in ev])
+    fwd_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    bwd_ms = np.array([e[3].elapsed_time(e[4]) for e in ev])
+    ms = wall * 1e3 / args.steps
+    value = 14 * d * A / (ms * 1e-3) / 1e12
+    bwd_flop = 10 * d * A
+    bwd_tflops = bwd_flop / (bwd_ms.mean() * 1e-3) / 1e12
+    fwd_tflops = 4 * d * A / (fwd_ms.mean() * 1e-3) / 1e12
+
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = cpu_baseline(w, q, k, v, do, args.cpu_budget)
+
+    out = {
+        "metric": "effective TFLOP/s (attended pairs only) fwd+bwd, bf16 d=128; % MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": w.batch, "heads_q": w.heads_q,
+                   "heads_kv": w.heads_kv, "seq_len": w.seqlen, "head_dim": d,
+                   "attended_pairs": A, "seed": args.seed},
+        "pct_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "fwd": {"kernel_ms": round(float(fwd_ms.mean()), 4),
+                "kernel_tflops": round(fwd_tflops, 2)},
+        "bwd": {"kernel_ms": round(float(bwd_ms.mean()), 4),
+                "kernel_tflops": round(bwd_tflops, 2)},
+        "event_ms_per_step": round(float(step_ms.mean()), 4),
+        "roofline": {"kernel": "k_attn_bwd", "bound": "mfma",
+                     "achieved": round(bwd_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(bwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

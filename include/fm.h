@@ -1,0 +1,166 @@
+/*
+ * fm.h -- C ABI of libfm: mask-aware (column-interval) attention on AMD MI355X (gfx950).
+ *
+ * The operation.  Attention softmax(scale * Q K^T + M) V where the mask M is given in
+ * the column-wise O(n) form of the FlashMask-3 project page ("FlashMask-3: Efficient
+ * and Expressive Mask-Aware Distributed Attention", Overview): every key column j of a
+ * batch row carries four int32 query-row bounds LTS_j, LTE_j, UTS_j, UTE_j, and query
+ * row i is hidden from key j iff
+ *
+ *     LTS_j <= i < LTE_j   or   UTS_j <= i < UTE_j        (half-open intervals).
+ *
+ * Tiles of query rows x key columns are classified from the block-wise min/max of the
+ * four vectors (same page, §3.1): fully hidden tiles are skipped, partial tiles get the
+ * row-interval mask applied, unmasked tiles run plain.  The forward is the tiled
+ * online-softmax attention of "Flash MSA Attention Kernel Implementation: A Practical
+ * Guide for Production AI" ("The Flash Core"), returning O and the per-row log-sum-exp;
+ * the backward recomputes the probabilities from that statistic (same guide, "The
+ * Backward Pass").  Work items are dispatched longest-processing-time first by tile
+ * cost {0, alpha_p, alpha_u} (FlashMask-3 page, §3.3).
+ *
+ * Conventions for every entry point:
+ *  - Device pointers.  Every array argument is a pointer to device memory on the
+ *    current HIP device, except the fm_problem / fm_mask / fm_tiles structs themselves,
+ *    which are host structs (read during the call only).  The caller owns and allocates
+ *    all memory: inputs, outputs and the workspace.  The library never allocates device
+ *    memory and keeps no state between calls.
+ *  - Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *    their kernels on it and return without synchronizing.
+ *  - Layouts (all contiguous, row-major):
+ *      Q, O, dO, dQ  bf16  [B][H_q][N][d]
+ *      K, V, dK, dV  bf16  [B][H_kv][N][d]
+ *      LSE           fp32  [B][H_q][N]      natural log; -inf for a row that sees no key
+ *      LTS/LTE/UTS/UTE int32 [B][N]         one set per batch row, shared by all heads
+ *  - GQA.  Query head h reads kv head h / (H_q / H_kv).
+ *  - Rows that see no key get O = 0, LSE = -inf, dQ = 0 and add nothing to dK/dV.
+ *  - Errors.  Arguments are validated on the host before anything is enqueued; on an
+ *    error nothing is launched and the outputs are untouched.  Vector values outside
+ *    [0, N] are not checked and give unspecified (but memory-safe) results.  No C++
+ *    exception crosses this interface.
+ */
+#ifndef FM_H
+#define FM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FM_OK = 0,
+  FM_ERR_INVALID_ARG = -1, /* null pointer, negative size, H_q % H_kv != 0, bad tile shape */
+  FM_ERR_UNSUPPORTED = -2, /* head_dim != 128, or a size beyond the documented limits    */
+  FM_ERR_WORKSPACE = -3,   /* ws_bytes smaller than fm_workspace_size() reports           */
+  FM_ERR_HIP = -4          /* a HIP launch failed                                         */
+} fm_status;
+
+typedef enum { FM_OP_CLASSIFY = 0, FM_OP_FWD = 1, FM_OP_BWD = 2 } fm_op;
+
+/* Problem shape.  batch, heads and seqlen may be 0 (nothing to do, FM_OK); head_dim must
+ * be 128.  softmax_scale <= 0 selects 1/sqrt(head_dim).  Limits: seqlen < 2^30 and
+ * batch * ceil(seqlen/block_q) and batch * ceil(seqlen/block_k) at most 8192 work blocks
+ * (the LPT sort runs in one workgroup's LDS); larger problems return FM_ERR_UNSUPPORTED. */
+typedef struct {
+  int32_t batch;
+  int32_t heads_q;
+  int32_t heads_kv;
+  int32_t seqlen;
+  int32_t head_dim;
+  float softmax_scale;
+} fm_problem;
+
+/* The four column vectors, each int32 [B][N] in device memory. */
+typedef struct {
+  const int32_t* lts;
+  const int32_t* lte;
+  const int32_t* uts;
+  const int32_t* ute;
+} fm_mask;
+
+/* Outputs of fm_classify_tiles, all device memory, nQB = ceil(N/block_q),
+ * nKB = ceil(N/block_k):
+ *   block_minmax [B][nKB][8]  int32: min,max of LTS, LTE, UTS, UTE over the block's columns
+ *   tile_class   [B][nQB][nKB] uint8: 0 skipped, 1 partial, 2 unmasked
+ *   q_queue      [B][nQB][nKB] int32: per Q-block the non-skipped KV blocks, right to left
+ *                (descending kb), each entry kb | (partial << 31); then -1 to the end
+ *   q_count      [B][nQB][2]   int32: {n_partial, n_unmasked} per Q-block
+ *   k_queue      [B][nKB][nQB] int32: per KV block the non-skipped Q-blocks, ascending,
+ *                each entry qb | (partial << 31); then -1 to the end
+ *   k_count      [B][nKB][2]   int32: {n_partial, n_unmasked} per KV block
+ *   q_order      [B*nQB]       int32: Q-blocks (b*nQB + qb) sorted by cost
+ *                13*n_partial + 10*n_unmasked descending, ties ascending
+ *   k_order      [B*nKB]       int32: the same over KV blocks (b*nKB + kb)          */
+typedef struct {
+  int32_t* block_minmax;
+  uint8_t* tile_class;
+  int32_t* q_queue;
+  int32_t* q_count;
+  int32_t* k_queue;
+  int32_t* k_count;
+  int32_t* q_order;
+  int32_t* k_order;
+} fm_tiles;
+
+/* Optional timing hook for fm_attn_fwd / fm_attn_bwd.  start and stop are hipEvent_t
+ * handles created by the caller (hipEventCreate, timing enabled); the call records start
+ * immediately before and stop immediately after the launch of its main attention kernel
+ * on `stream`, so hipEventElapsedTime(start, stop) is that kernel's duration.  Pass NULL
+ * for no timing.  The library keeps no reference after the call returns. */
+typedef struct {
+  void* start;
+  void* stop;
+} fm_kernel_events;
+
+/* Workspace bytes an entry point needs for this problem.  For FM_OP_CLASSIFY the tile
+ * shape is (block_q, block_k); for FM_OP_FWD / FM_OP_BWD those two arguments are ignored
+ * (the kernels' own shapes, see fm_tile_shape, are used).  Writes *bytes; returns
+ * FM_ERR_INVALID_ARG / FM_ERR_UNSUPPORTED for problems the op rejects. */
+fm_status fm_workspace_size(const fm_problem* p, fm_op op, int32_t block_q, int32_t block_k,
+                            size_t* bytes);
+
+/* The tile shape (rows of Q, columns of K per tile) the forward or backward kernel uses
+ * and classifies with.  FM_OP_CLASSIFY is invalid here. */
+fm_status fm_tile_shape(fm_op op, int32_t* block_q, int32_t* block_k);
+
+/* Tile classification (FlashMask-3 page, §3.1 tile rule, generalized to all four
+ * vectors: skip = (q0 >= max LTS and q1 <= min LTE) or (q0 >= max UTS and q1 <= min UTE);
+ * unmasked = (q1 <= min LTS or q0 >= max LTE) and (q1 <= min UTS or q0 >= max UTE);
+ * q1 and the block's last column clamped to N), the per-block queues with their tags
+ * (§3.1, KV Index Generator), tile costs and the LPT orders (§3.3).  block_q and block_k
+ * must be powers of two in [8, 256].  Any N >= 0 is accepted (ragged tails allowed). */
+fm_status fm_classify_tiles(const fm_problem* p, const fm_mask* m, int32_t block_q,
+                            int32_t block_k, const fm_tiles* out, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Forward: O (bf16) and LSE (fp32) from Q, K, V (bf16) under the mask.  Classifies
+ * internally into `ws` (fm_workspace_size(p, FM_OP_FWD, ...) bytes), then runs the
+ * attention kernel over the queued tiles only, in LPT order.  Any N >= 0. */
+fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const void* v,
+                      const fm_mask* m, void* o, float* lse, void* ws, size_t ws_bytes,
+                      void* stream, const fm_kernel_events* events);
+
+/* Backward: dQ, dK, dV (bf16) from Q, K, V, the forward's O and LSE, and dO.  Classifies
+ * internally, computes D = rowsum(dO * O) in fp32, runs the KV-block-outer kernel that
+ * recomputes P = exp(S - LSE) on queued tiles only (LPT order over KV blocks), and
+ * converts the fp32 accumulators held in `ws` to bf16.  Any N >= 0. */
+fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
+                      const void* o, const float* lse, const void* dout, const fm_mask* m,
+                      void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream,
+                      const fm_kernel_events* events);
+
+/* Dense expansion of rows [row0, row1) of batch row b: dense[(i-row0)*N + j] = 1 if the
+ * mask hides (i, j), else 0 -- the same predicate the attention kernels apply on partial
+ * tiles.  For checking only.  0 <= b < batch, 0 <= row0 <= row1 <= N. */
+fm_status fm_debug_expand_mask(const fm_problem* p, const fm_mask* m, int32_t b, int32_t row0,
+                               int32_t row1, uint8_t* dense, void* stream);
+
+/* Static description of a status code. */
+const char* fm_status_string(fm_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FM_H */

@@ -1,0 +1,265 @@
+"""Mask-aware (column-interval) attention on AMD MI355X: thin Python binding of libfm.
+
+Every function here marshals arguments and calls the C ABI declared in include/fm.h;
+all computation runs in the library's HIP kernels.  torch is used for device memory
+(outputs and workspaces are torch tensors) and for the current stream.  There is no
+fallback: if libfm.so is missing or fails to load, every call raises.
+
+The operation (FlashMask-3 project page, Overview and §3.1): key column j of batch row
+b hides query rows [LTS_j, LTE_j) and [UTS_j, UTE_j); tiles are skipped, masked or run
+plain according to the block min/max of those vectors; forward returns O and the
+per-row natural-log LSE, backward returns dQ, dK, dV (Flash MSA guide, "The Backward
+Pass").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "FMError", "library", "library_path", "tile_shape", "workspace_size", "classify_tiles",
+    "attn_fwd", "attn_bwd", "debug_expand_mask", "status_string",
+    "fm_tile_shape", "fm_workspace_size", "fm_classify_tiles", "fm_attn_fwd", "fm_attn_bwd",
+    "fm_debug_expand_mask", "fm_status_string",
+    "OP_CLASSIFY", "OP_FWD", "OP_BWD", "HEAD_DIM",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+OP_CLASSIFY, OP_FWD, OP_BWD = 0, 1, 2
+HEAD_DIM = 128
+FM_OK = 0
+
+
+def library_path() -> str:
+    return os.environ.get("FM_LIBRARY", os.path.join(HERE, "libfm.so"))
+
+
+class FMError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32),
+                ("heads_kv", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+class Mask(ctypes.Structure):
+    _fields_ = [("lts", ctypes.c_void_p), ("lte", ctypes.c_void_p),
+                ("uts", ctypes.c_void_p), ("ute", ctypes.c_void_p)]
+
+
+class KernelEvents(ctypes.Structure):
+    _fields_ = [("start", ctypes.c_void_p), ("stop", ctypes.c_void_p)]
+
+
+class Tiles(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("block_minmax", "tile_class", "q_queue", "q_count", "k_queue", "k_count",
+                 "q_order", "k_order")]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_STATUS = ctypes.c_int
+
+
+def library():
+    """Load libfm.so once; raises if it is missing (no fallback path exists)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"libfm.so not found at {path}; build it with "
+                               "`python -m mask_aware_sparse_amd.build`")
+        lib = ctypes.CDLL(path)
+        PP, PM, PT = ctypes.POINTER(Problem), ctypes.POINTER(Mask), ctypes.POINTER(Tiles)
+        PE = ctypes.POINTER(KernelEvents)
+        sig = {
+            "fm_status_string": ([_STATUS], ctypes.c_char_p),
+            "fm_tile_shape": ([_STATUS, ctypes.POINTER(ctypes.c_int32),
+                               ctypes.POINTER(ctypes.c_int32)], _STATUS),
+            "fm_workspace_size": ([PP, _STATUS, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.POINTER(ctypes.c_size_t)], _STATUS),
+            "fm_classify_tiles": ([PP, PM, ctypes.c_int32, ctypes.c_int32, PT, _P,
+                                   ctypes.c_size_t, _P], _STATUS),
+            "fm_attn_fwd": ([PP, _P, _P, _P, PM, _P, _P, _P, ctypes.c_size_t, _P, PE], _STATUS),
+            "fm_attn_bwd": ([PP, _P, _P, _P, _P, _P, _P, PM, _P, _P, _P, _P, ctypes.c_size_t,
+                             _P, PE], _STATUS),
+            "fm_debug_expand_mask": ([PP, PM, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      _P, _P], _STATUS),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return library().fm_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != FM_OK:
+        raise FMError(status, where)
+
+
+def _problem(batch, heads_q, heads_kv, seqlen, scale=None, head_dim=HEAD_DIM):
+    return Problem(int(batch), int(heads_q), int(heads_kv), int(seqlen), int(head_dim),
+                   float(scale) if scale is not None else 0.0)
+
+
+def _mask(lts, lte, uts, ute):
+    for t in (lts, lte, uts, ute):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("mask vectors must be contiguous int32 tensors [B][N]")
+    return Mask(lts.data_ptr(), lte.data_ptr(), uts.data_ptr(), ute.data_ptr())
+
+
+def _stream(device, stream=None):
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() else 0)
+
+
+def tile_shape(op: int):
+    bq, bk = ctypes.c_int32(), ctypes.c_int32()
+    _check(library().fm_tile_shape(int(op), ctypes.byref(bq), ctypes.byref(bk)), "fm_tile_shape")
+    return bq.value, bk.value
+
+
+def workspace_size(batch, heads_q, heads_kv, seqlen, op, block_q=0, block_k=0, head_dim=HEAD_DIM):
+    n = ctypes.c_size_t()
+    p = _problem(batch, heads_q, heads_kv, seqlen, head_dim=head_dim)
+    _check(library().fm_workspace_size(ctypes.byref(p), int(op), int(block_q), int(block_k),
+                                       ctypes.byref(n)), "fm_workspace_size")
+    return n.value
+
+
+def _workspace(nbytes, device, ws=None):
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError("workspace tensor too small")
+        return ws
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def classify_tiles(lts, lte, uts, ute, block_q, block_k, heads_q=1, heads_kv=1, stream=None):
+    """Run fm_classify_tiles; returns a dict of device tensors (see fm_tiles in fm.h)."""
+    B, N = lts.shape
+    dev = lts.device
+    nqb, nkb = -(-N // block_q), -(-N // block_k)
+    out = {
+        "block_minmax": torch.empty((B, nkb, 8), dtype=torch.int32, device=dev),
+        "tile_class": torch.empty((B, nqb, nkb), dtype=torch.uint8, device=dev),
+        "q_queue": torch.empty((B, nqb, nkb), dtype=torch.int32, device=dev),
+        "q_count": torch.empty((B, nqb, 2), dtype=torch.int32, device=dev),
+        "k_queue": torch.empty((B, nkb, nqb), dtype=torch.int32, device=dev),
+        "k_count": torch.empty((B, nkb, 2), dtype=torch.int32, device=dev),
+        "q_order": torch.empty((B * nqb,), dtype=torch.int32, device=dev),
+        "k_order": torch.empty((B * nkb,), dtype=torch.int32, device=dev),
+    }
+    tiles = Tiles(*(out[n].data_ptr() if out[n].numel() else 0 for n, _ in Tiles._fields_))
+    p = _problem(B, heads_q, heads_kv, N)
+    nbytes = workspace_size(B, heads_q, heads_kv, N, OP_CLASSIFY, block_q, block_k)
+    ws = _workspace(nbytes, dev)
+    m = _mask(lts, lte, uts, ute)
+    _check(library().fm_classify_tiles(ctypes.byref(p), ctypes.byref(m), int(block_q),
+                                       int(block_k), ctypes.byref(tiles), _ptr(ws),
+                                       ctypes.c_size_t(nbytes), _stream(dev, stream)),
+           "fm_classify_tiles")
+    return out
+
+
+def _shapes(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("expected Q [B][H_q][N][d] and K/V [B][H_kv][N][d]")
+    B, Hq, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError("Q and K/V shapes disagree")
+    return B, Hq, k.shape[1], N, d
+
+
+def _bf16(*ts):
+    for t in ts:
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("tensors must be contiguous bf16 on the GPU")
+
+
+def _events(ev):
+    """(start, stop) torch.cuda.Event pair -> fm_kernel_events pointer (or None)."""
+    if ev is None:
+        return None
+    for e in ev:
+        if e.cuda_event == 0:          # torch creates the event lazily on first record
+            e.record()
+    return ctypes.byref(KernelEvents(ev[0].cuda_event, ev[1].cuda_event))
+
+
+def attn_fwd(q, k, v, lts, lte, uts, ute, scale=None, ws=None, out=None, lse=None, stream=None,
+             events=None):
+    """O (bf16 [B][H_q][N][d]) and LSE (fp32 [B][H_q][N], natural log) via fm_attn_fwd.
+    `events`: optional (start, stop) torch.cuda.Event pair timing the attention kernel."""
+    _bf16(q, k, v)
+    B, Hq, Hkv, N, d = _shapes(q, k)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    p = _problem(B, Hq, Hkv, N, scale, head_dim=d)
+    nbytes = workspace_size(B, Hq, Hkv, N, OP_FWD, head_dim=d)
+    w = _workspace(nbytes, q.device, ws)
+    m = _mask(lts, lte, uts, ute)
+    _check(library().fm_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(m),
+                                 _ptr(o), _ptr(lse_t), _ptr(w), ctypes.c_size_t(nbytes),
+                                 _stream(q.device, stream), _events(events)), "fm_attn_fwd")
+    return o, lse_t
+
+
+def attn_bwd(q, k, v, o, lse, dout, lts, lte, uts, ute, scale=None, ws=None, grads=None,
+             stream=None, events=None):
+    """(dQ, dK, dV) in bf16 via fm_attn_bwd.  `events` as in attn_fwd."""
+    _bf16(q, k, v, o, dout)
+    B, Hq, Hkv, N, d = _shapes(q, k)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    p = _problem(B, Hq, Hkv, N, scale, head_dim=d)
+    nbytes = workspace_size(B, Hq, Hkv, N, OP_BWD, head_dim=d)
+    w = _workspace(nbytes, q.device, ws)
+    m = _mask(lts, lte, uts, ute)
+    _check(library().fm_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                 _ptr(dout), ctypes.byref(m), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _ptr(w), ctypes.c_size_t(nbytes), _stream(q.device, stream),
+                                 _events(events)), "fm_attn_bwd")
+    return dq, dk, dv
+
+
+def debug_expand_mask(lts, lte, uts, ute, b, row0, row1, stream=None):
+    """uint8 [row1-row0][N] dense expansion (1 = hidden) by the kernels' predicate."""
+    B, N = lts.shape
+    dense = torch.empty((row1 - row0, N), dtype=torch.uint8, device=lts.device)
+    p = _problem(B, 1, 1, N)
+    m = _mask(lts, lte, uts, ute)
+    _check(library().fm_debug_expand_mask(ctypes.byref(p), ctypes.byref(m), int(b), int(row0),
+                                          int(row1), _ptr(dense), _stream(lts.device, stream)),
+           "fm_debug_expand_mask")
+    return dense
+
+
+# The C names, for callers that prefer them.
+fm_tile_shape = tile_shape
+fm_workspace_size = workspace_size
+fm_classify_tiles = classify_tiles
+fm_attn_fwd = attn_fwd
+fm_attn_bwd = attn_bwd
+fm_debug_expand_mask = debug_expand_mask
+fm_status_string = status_string

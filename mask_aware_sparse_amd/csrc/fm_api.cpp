@@ -1,0 +1,313 @@
+// libfm C ABI: argument validation, workspace layout, kernel launch sequences.
+// The declarations and their contracts are in include/fm.h.
+#include "fm.h"
+#include "fm_internal.h"
+
+#include <cmath>
+#include <cstdint>
+
+namespace {
+
+using fm::MaskPtrs;
+
+inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+inline bool pow2_in(int32_t x, int32_t lo, int32_t hi) {
+  return x >= lo && x <= hi && (x & (x - 1)) == 0;
+}
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Problem checks shared by every entry point.
+fm_status check_problem(const fm_problem* p) {
+  if (!p) return FM_ERR_INVALID_ARG;
+  if (p->batch < 0 || p->heads_q < 0 || p->heads_kv < 1 || p->seqlen < 0)
+    return FM_ERR_INVALID_ARG;
+  if (p->heads_q % p->heads_kv != 0) return FM_ERR_INVALID_ARG;
+  if (!(p->softmax_scale <= 0.f || std::isfinite(p->softmax_scale))) return FM_ERR_INVALID_ARG;
+  if (p->head_dim != fm::kHeadDim) return FM_ERR_UNSUPPORTED;
+  if (p->seqlen >= (1 << 30)) return FM_ERR_UNSUPPORTED;
+  return FM_OK;
+}
+
+bool empty_problem(const fm_problem* p) {
+  return p->batch == 0 || p->seqlen == 0 || p->heads_q == 0;
+}
+
+fm_status check_mask(const fm_problem* p, const fm_mask* m) {
+  if (!m) return FM_ERR_INVALID_ARG;
+  if ((int64_t)p->batch * p->seqlen == 0) return FM_OK;
+  if (!m->lts || !m->lte || !m->uts || !m->ute) return FM_ERR_INVALID_ARG;
+  return FM_OK;
+}
+
+float scale_of(const fm_problem* p) {
+  return p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
+}
+
+struct Blocks {
+  int64_t nQB, nKB;
+};
+Blocks blocks(const fm_problem* p, int bq, int bk) {
+  return {cdiv(p->seqlen, bq), cdiv(p->seqlen, bk)};
+}
+
+fm_status check_sort_limits(const fm_problem* p, const Blocks& nb) {
+  if ((int64_t)p->batch * nb.nQB > fm::kMaxSortItems) return FM_ERR_UNSUPPORTED;
+  if ((int64_t)p->batch * nb.nKB > fm::kMaxSortItems) return FM_ERR_UNSUPPORTED;
+  return FM_OK;
+}
+
+// ---- workspace layouts ------------------------------------------------------------
+struct ClassifyWs { size_t q_cost, k_cost, total; };
+ClassifyWs classify_ws(const fm_problem* p, const Blocks& nb) {
+  ClassifyWs w{};
+  size_t off = 0;
+  w.q_cost = off; off += align_up((size_t)p->batch * nb.nQB * 4);
+  w.k_cost = off; off += align_up((size_t)p->batch * nb.nKB * 4);
+  w.total = off;
+  return w;
+}
+
+struct FwdWs { size_t mm, q_queue, q_count, q_cost, q_order, total; };
+FwdWs fwd_ws(const fm_problem* p, const Blocks& nb) {
+  FwdWs w{};
+  const size_t B = p->batch;
+  size_t off = 0;
+  w.mm = off; off += align_up(B * nb.nKB * 8 * 4);
+  w.q_queue = off; off += align_up(B * nb.nQB * nb.nKB * 4);
+  w.q_count = off; off += align_up(B * nb.nQB * 2 * 4);
+  w.q_cost = off; off += align_up(B * nb.nQB * 4);
+  w.q_order = off; off += align_up(B * nb.nQB * 4);
+  w.total = off;
+  return w;
+}
+
+struct BwdWs { size_t mm, k_queue, k_count, k_cost, k_order, lse2, delta, dq, dk, dv, total; };
+BwdWs bwd_ws(const fm_problem* p, const Blocks& nb) {
+  BwdWs w{};
+  const size_t B = p->batch, rq = B * p->heads_q * p->seqlen, rk = B * p->heads_kv * p->seqlen;
+  size_t off = 0;
+  w.mm = off; off += align_up(B * nb.nKB * 8 * 4);
+  w.k_queue = off; off += align_up(B * nb.nKB * nb.nQB * 4);
+  w.k_count = off; off += align_up(B * nb.nKB * 2 * 4);
+  w.k_cost = off; off += align_up(B * nb.nKB * 4);
+  w.k_order = off; off += align_up(B * nb.nKB * 4);
+  w.lse2 = off; off += align_up(rq * 4);
+  w.delta = off; off += align_up(rq * 4);
+  w.dq = off; off += align_up(rq * fm::kHeadDim * 4);
+  w.dk = off; off += align_up(rk * fm::kHeadDim * 4);
+  w.dv = off; off += align_up(rk * fm::kHeadDim * 4);
+  w.total = off;
+  return w;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+MaskPtrs mask_ptrs(const fm_mask* m) { return MaskPtrs{m->lts, m->lte, m->uts, m->ute}; }
+
+hipEvent_t ev_start(const fm_kernel_events* e) {
+  return e ? static_cast<hipEvent_t>(e->start) : nullptr;
+}
+hipEvent_t ev_stop(const fm_kernel_events* e) {
+  return e ? static_cast<hipEvent_t>(e->stop) : nullptr;
+}
+
+fm_status hip_status(hipError_t e) { return e == hipSuccess ? FM_OK : FM_ERR_HIP; }
+
+fm_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return FM_OK;
+  if (!ws) return FM_ERR_INVALID_ARG;
+  if (!aligned16(ws)) return FM_ERR_INVALID_ARG;
+  if (have < need) return FM_ERR_WORKSPACE;
+  return FM_OK;
+}
+
+fm_status check_grid(const fm_problem* p, const Blocks& fwd, const Blocks& bwd) {
+  const int64_t g = p->heads_q / p->heads_kv;
+  const int64_t hc = g < fm::kBwdHeadChunk ? g : fm::kBwdHeadChunk;
+  const int64_t nch = hc ? cdiv(g, hc) : 0;
+  if ((int64_t)p->batch * fwd.nQB * p->heads_q >= INT32_MAX) return FM_ERR_UNSUPPORTED;
+  if ((int64_t)p->batch * bwd.nKB * p->heads_kv * nch >= INT32_MAX) return FM_ERR_UNSUPPORTED;
+  return FM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fm_status_string(fm_status s) {
+  switch (s) {
+    case FM_OK: return "FM_OK";
+    case FM_ERR_INVALID_ARG: return "FM_ERR_INVALID_ARG: invalid argument";
+    case FM_ERR_UNSUPPORTED: return "FM_ERR_UNSUPPORTED: unsupported problem";
+    case FM_ERR_WORKSPACE: return "FM_ERR_WORKSPACE: workspace too small";
+    case FM_ERR_HIP: return "FM_ERR_HIP: HIP launch failed";
+  }
+  return "unknown fm_status";
+}
+
+fm_status fm_tile_shape(fm_op op, int32_t* block_q, int32_t* block_k) {
+  if (!block_q || !block_k) return FM_ERR_INVALID_ARG;
+  if (op == FM_OP_FWD) { *block_q = fm::kFwdBlockQ; *block_k = fm::kFwdBlockK; return FM_OK; }
+  if (op == FM_OP_BWD) { *block_q = fm::kBwdBlockQ; *block_k = fm::kBwdBlockK; return FM_OK; }
+  return FM_ERR_INVALID_ARG;
+}
+
+fm_status fm_workspace_size(const fm_problem* p, fm_op op, int32_t block_q, int32_t block_k,
+                            size_t* bytes) {
+  if (!bytes) return FM_ERR_INVALID_ARG;
+  fm_status st = check_problem(p);
+  if (st != FM_OK) return st;
+  switch (op) {
+    case FM_OP_CLASSIFY: {
+      if (!pow2_in(block_q, 8, 256) || !pow2_in(block_k, 8, 256)) return FM_ERR_INVALID_ARG;
+      Blocks nb = blocks(p, block_q, block_k);
+      if ((st = check_sort_limits(p, nb)) != FM_OK) return st;
+      *bytes = classify_ws(p, nb).total;
+      return FM_OK;
+    }
+    case FM_OP_FWD: {
+      Blocks nb = blocks(p, fm::kFwdBlockQ, fm::kFwdBlockK);
+      if ((st = check_sort_limits(p, nb)) != FM_OK) return st;
+      *bytes = fwd_ws(p, nb).total;
+      return FM_OK;
+    }
+    case FM_OP_BWD: {
+      Blocks nb = blocks(p, fm::kBwdBlockQ, fm::kBwdBlockK);
+      if ((st = check_sort_limits(p, nb)) != FM_OK) return st;
+      *bytes = bwd_ws(p, nb).total;
+      return FM_OK;
+    }
+  }
+  return FM_ERR_INVALID_ARG;
+}
+
+fm_status fm_classify_tiles(const fm_problem* p, const fm_mask* m, int32_t block_q,
+                            int32_t block_k, const fm_tiles* out, void* ws, size_t ws_bytes,
+                            void* stream) {
+  fm_status st = check_problem(p);
+  if (st != FM_OK) return st;
+  if ((st = check_mask(p, m)) != FM_OK) return st;
+  if (!pow2_in(block_q, 8, 256) || !pow2_in(block_k, 8, 256)) return FM_ERR_INVALID_ARG;
+  if (!out) return FM_ERR_INVALID_ARG;
+  Blocks nb = blocks(p, block_q, block_k);
+  if ((st = check_sort_limits(p, nb)) != FM_OK) return st;
+  if (p->batch == 0 || p->seqlen == 0) return FM_OK;
+  if (!out->block_minmax || !out->tile_class || !out->q_queue || !out->q_count ||
+      !out->k_queue || !out->k_count || !out->q_order || !out->k_order)
+    return FM_ERR_INVALID_ARG;
+  ClassifyWs w = classify_ws(p, nb);
+  if ((st = check_ws(ws, ws_bytes, w.total)) != FM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  fm::TileOut t{};
+  t.minmax = out->block_minmax;
+  t.tile_class = out->tile_class;
+  t.q_queue = out->q_queue;
+  t.q_count = out->q_count;
+  t.q_cost = at<int32_t>(ws, w.q_cost);
+  t.k_queue = out->k_queue;
+  t.k_count = out->k_count;
+  t.k_cost = at<int32_t>(ws, w.k_cost);
+  hipError_t e = fm::launch_classify(mask_ptrs(m), p->batch, p->seqlen, block_q, block_k, t, s);
+  if (e == hipSuccess) e = fm::launch_lpt_sort(t.q_cost, out->q_order, (int)(p->batch * nb.nQB), s);
+  if (e == hipSuccess) e = fm::launch_lpt_sort(t.k_cost, out->k_order, (int)(p->batch * nb.nKB), s);
+  return hip_status(e);
+}
+
+fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const void* v,
+                      const fm_mask* m, void* o, float* lse, void* ws, size_t ws_bytes,
+                      void* stream, const fm_kernel_events* events) {
+  fm_status st = check_problem(p);
+  if (st != FM_OK) return st;
+  if ((st = check_mask(p, m)) != FM_OK) return st;
+  Blocks nb = blocks(p, fm::kFwdBlockQ, fm::kFwdBlockK);
+  if ((st = check_sort_limits(p, nb)) != FM_OK) return st;
+  if ((st = check_grid(p, nb, blocks(p, fm::kBwdBlockQ, fm::kBwdBlockK))) != FM_OK) return st;
+  if (empty_problem(p)) return FM_OK;
+  if (!q || !k || !v || !o || !lse) return FM_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FM_ERR_INVALID_ARG;
+  FwdWs w = fwd_ws(p, nb);
+  if ((st = check_ws(ws, ws_bytes, w.total)) != FM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  fm::TileOut t{};
+  t.minmax = at<int32_t>(ws, w.mm);
+  t.q_queue = at<int32_t>(ws, w.q_queue);
+  t.q_count = at<int32_t>(ws, w.q_count);
+  t.q_cost = at<int32_t>(ws, w.q_cost);
+  hipError_t e = fm::launch_classify(mask_ptrs(m), p->batch, p->seqlen, fm::kFwdBlockQ,
+                                     fm::kFwdBlockK, t, s);
+  int32_t* order = at<int32_t>(ws, w.q_order);
+  if (e == hipSuccess) e = fm::launch_lpt_sort(t.q_cost, order, (int)(p->batch * nb.nQB), s);
+  if (e == hipSuccess) {
+    fm::FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.m = mask_ptrs(m); a.o = o; a.lse = lse;
+    a.q_queue = t.q_queue; a.q_count = t.q_count; a.q_order = order;
+    a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.N = p->seqlen;
+    a.nQB = (int)nb.nQB; a.nKB = (int)nb.nKB;
+    a.scale = scale_of(p);
+    e = fm::launch_fwd(a, s, ev_start(events), ev_stop(events));
+  }
+  return hip_status(e);
+}
+
+fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
+                      const void* o, const float* lse, const void* dout, const fm_mask* m,
+                      void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream,
+                      const fm_kernel_events* events) {
+  fm_status st = check_problem(p);
+  if (st != FM_OK) return st;
+  if ((st = check_mask(p, m)) != FM_OK) return st;
+  Blocks nb = blocks(p, fm::kBwdBlockQ, fm::kBwdBlockK);
+  if ((st = check_sort_limits(p, nb)) != FM_OK) return st;
+  if ((st = check_grid(p, blocks(p, fm::kFwdBlockQ, fm::kFwdBlockK), nb)) != FM_OK) return st;
+  if (empty_problem(p)) return FM_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FM_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FM_ERR_INVALID_ARG;
+  BwdWs w = bwd_ws(p, nb);
+  if ((st = check_ws(ws, ws_bytes, w.total)) != FM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  fm::TileOut t{};
+  t.minmax = at<int32_t>(ws, w.mm);
+  t.k_queue = at<int32_t>(ws, w.k_queue);
+  t.k_count = at<int32_t>(ws, w.k_count);
+  t.k_cost = at<int32_t>(ws, w.k_cost);
+  hipError_t e = fm::launch_classify(mask_ptrs(m), p->batch, p->seqlen, fm::kBwdBlockQ,
+                                     fm::kBwdBlockK, t, s);
+  int32_t* order = at<int32_t>(ws, w.k_order);
+  if (e == hipSuccess) e = fm::launch_lpt_sort(t.k_cost, order, (int)(p->batch * nb.nKB), s);
+  if (e == hipSuccess) {
+    fm::BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout; a.m = mask_ptrs(m);
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.k_queue = t.k_queue; a.k_count = t.k_count; a.k_order = order;
+    a.lse2 = at<float>(ws, w.lse2); a.delta = at<float>(ws, w.delta);
+    a.dq_acc = at<float>(ws, w.dq); a.dk_acc = at<float>(ws, w.dk); a.dv_acc = at<float>(ws, w.dv);
+    a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.N = p->seqlen;
+    a.nQB = (int)nb.nQB; a.nKB = (int)nb.nKB;
+    a.scale = scale_of(p);
+    e = fm::launch_bwd(a, s, ev_start(events), ev_stop(events));
+  }
+  return hip_status(e);
+}
+
+fm_status fm_debug_expand_mask(const fm_problem* p, const fm_mask* m, int32_t b, int32_t row0,
+                               int32_t row1, uint8_t* dense, void* stream) {
+  fm_status st = check_problem(p);
+  if (st != FM_OK) return st;
+  if ((st = check_mask(p, m)) != FM_OK) return st;
+  if (b < 0 || b >= p->batch || row0 < 0 || row1 < row0 || row1 > p->seqlen)
+    return FM_ERR_INVALID_ARG;
+  if (row1 == row0) return FM_OK;
+  if (!dense) return FM_ERR_INVALID_ARG;
+  return hip_status(fm::launch_expand_mask(mask_ptrs(m), b, p->seqlen, row0, row1, dense,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,389 @@
+// Mask-aware attention backward (gfx950, bf16 MFMA 32x32x16).
+//
+// Recomputation backward of the Flash MSA guide ("The Backward Pass: The Real Beast"):
+// with the forward's statistic LSE, P = exp(S - LSE) is recomputed per tile, then
+//   dV += P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dK += scale dS^T Q,
+//   dQ += scale dS K,   D_i = sum_j P_ij dP_ij = rowsum(dO o O).
+// (The guide writes dQ and dK without the softmax scale; the chain rule through
+// S = scale Q K^T puts it there.)
+//
+// Kernels:
+//   k_bwd_pre   D = rowsum(dO o O) in fp32, LSE in log2 units (+inf for rows that see
+//               nothing, so that P = 0 there), zeroes the fp32 dQ accumulator.
+//   k_zero      zeroes the fp32 dK/dV accumulators (a fill kernel, not a memset).
+//   k_attn_bwd  one workgroup per (b, kv head, 128-key KV block, chunk of <= 4 query
+//               heads), numbered in LPT order of the KV blocks' tile costs.  K and V of
+//               the block stay in registers (each of the 4 waves owns 32 keys); the
+//               workgroup walks the block's queue of Q-blocks (64 rows each), tiles
+//               tagged partial get the row-interval mask, and dK/dV accumulate in
+//               registers.  dQ partials go to the fp32 accumulator with atomics; dK/dV
+//               are added to theirs once per workgroup.
+//   k_bwd_convert  fp32 accumulators -> bf16 (with the softmax scale on dQ and dK).
+#include "fm_device.h"
+#include "fm_internal.h"
+
+namespace fm {
+namespace {
+
+constexpr int BQ = kBwdBlockQ;  // 64 query rows per step
+constexpr int BK = kBwdBlockK;  // 128 keys per workgroup
+constexpr int D = kHeadDim;
+constexpr int QS = D + 8;       // Q / dO row stride in LDS
+constexpr int KS = D + 16;      // K row stride in LDS (transposing reads)
+constexpr int SS = BQ + 16;     // dS^T row stride in LDS (transposing reads)
+
+// ---- KD: preprocess -----------------------------------------------------------------
+// 16 lanes per row (16 bytes each); a 256-thread block covers 16 rows.
+__global__ __launch_bounds__(256) void k_bwd_pre(const bf16* __restrict__ o,
+                                                 const bf16* __restrict__ dout,
+                                                 const float* __restrict__ lse,
+                                                 float* __restrict__ lse2,
+                                                 float* __restrict__ delta,
+                                                 float* __restrict__ dq_acc, size_t rows) {
+  const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int c = (threadIdx.x & 15) * 8;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * D + c);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(dout + row * D + c);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      acc += bf16lo_to_f32(a[t]) * bf16lo_to_f32(g[t]) + bf16hi_to_f32(a[t]) * bf16hi_to_f32(g[t]);
+    float4* z = reinterpret_cast<float4*>(dq_acc + row * D + c);
+    z[0] = float4{0.f, 0.f, 0.f, 0.f};
+    z[1] = float4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && (threadIdx.x & 15) == 0) {
+    delta[row] = acc;
+    const float l = lse[row];
+    lse2[row] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_zero(float4* __restrict__ p, size_t n4) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256)
+    p[i] = float4{0.f, 0.f, 0.f, 0.f};
+}
+
+__global__ __launch_bounds__(256) void k_bwd_convert(const float* __restrict__ src,
+                                                     bf16* __restrict__ dst, float mul,
+                                                     size_t n8) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
+    const float4 a = reinterpret_cast<const float4*>(src)[2 * i];
+    const float4 b = reinterpret_cast<const float4*>(src)[2 * i + 1];
+    u32x4 w;
+    w[0] = pack_bf16x2(a.x * mul, a.y * mul);
+    w[1] = pack_bf16x2(a.z * mul, a.w * mul);
+    w[2] = pack_bf16x2(b.x * mul, b.y * mul);
+    w[3] = pack_bf16x2(b.z * mul, b.w * mul);
+    reinterpret_cast<u32x4*>(dst)[i] = w;
+  }
+}
+
+// ---- KE: main backward ------------------------------------------------------------------
+struct BwdSmem {
+  bf16 q[2][BQ * QS];
+  bf16 dO[2][BQ * QS];
+  bf16 k[BK * KS];
+  bf16 dst[BK * SS];  // dS^T [key][q]
+  float lse2[2][BQ];
+  float dl[2][BQ];
+};
+
+__device__ __forceinline__ int perm_rows(int a) {
+  return (a & 0x13) | ((a & 4) << 1) | ((a & 8) >> 1);
+}
+
+struct BwdParams {
+  const bf16* __restrict__ q;
+  const bf16* __restrict__ k;
+  const bf16* __restrict__ v;
+  const bf16* __restrict__ dout;
+  const float* __restrict__ lse2;
+  const float* __restrict__ delta;
+  MaskPtrs m;
+  const int32_t* __restrict__ k_queue;
+  const int32_t* __restrict__ k_count;
+  const int32_t* __restrict__ k_order;
+  float* __restrict__ dq_acc;
+  float* __restrict__ dk_acc;
+  float* __restrict__ dv_acc;
+  int B, Hq, Hkv, N, nQB, nKB, hc, nch;
+  float c;  // scale * log2(e)
+};
+
+__global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdParams p) {
+  __shared__ BwdSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int N = p.N;
+
+  const int per = p.Hkv * p.nch;
+  const int r = blockIdx.x / per, rem = blockIdx.x - r * per;
+  const int kvh = rem / p.nch, ch = rem - kvh * p.nch;
+  const int item = p.k_order[r];
+  const int b = item / p.nKB, kb = item - b * p.nKB;
+  const int g = p.Hq / p.Hkv;
+  const int h0 = kvh * g + ch * p.hc;
+  const int nh = min(p.hc, kvh * g + g - h0);
+  const int nq = p.k_count[2 * item] + p.k_count[2 * item + 1];
+  if (nq == 0 || nh <= 0) return;
+  const int32_t* queue = p.k_queue + (size_t)item * p.nQB;
+  const bool ragged_k = (N % BK) != 0 && kb == p.nKB - 1;
+  const bool ragged_q_any = (N % BQ) != 0;
+
+  // ---- resident K, V (B operands of S = Q K^T and dP = dO V^T), and the lane's key
+  const int key = kb * BK + wave * 32 + l32;
+  const bool key_ok = key < N;
+  const bf16* kg = p.k + (size_t)(b * p.Hkv + kvh) * N * D;
+  const bf16* vg = p.v + (size_t)(b * p.Hkv + kvh) * N * D;
+  bf16x8 kr[8], vr[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    if (key_ok) {
+      kr[s] = *reinterpret_cast<const bf16x8*>(kg + (size_t)key * D + s * 16 + hh * 8);
+      vr[s] = *reinterpret_cast<const bf16x8*>(vg + (size_t)key * D + s * 16 + hh * 8);
+    } else {
+      kr[s] = bf16x8{};
+      vr[s] = bf16x8{};
+    }
+    *reinterpret_cast<bf16x8*>(&sm.k[(wave * 32 + l32) * KS + s * 16 + hh * 8]) = kr[s];
+  }
+  int mv[4] = {0, 0, 0, 0};
+  if (key_ok) {
+    const size_t o = (size_t)b * N + key;
+    mv[0] = p.m.lts[o]; mv[1] = p.m.lte[o]; mv[2] = p.m.uts[o]; mv[3] = p.m.ute[o];
+  }
+
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) { dk[d] = f32x16{}; dv[d] = f32x16{}; }
+
+  // ---- staging of the Q / dO tiles: thread copies rows (tid>>4)+16i, chunk tid&15
+  const int cp_row = tid >> 4, cp_ch = (tid & 15) * 8;
+  u32x4 qst[4], ost[4];
+  float lst = 0.f, dst_ = 0.f;
+  const int nsteps = nh * nq;
+
+  auto load_step = [&](int st) {
+    const int hi = st / nq, it = st - hi * nq;
+    const int h = h0 + hi;
+    const int qb = queue[it] & 0x7fffffff;
+    const size_t base = (size_t)(b * p.Hq + h) * N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = qb * BQ + cp_row + 16 * i;
+      if (row < N) {
+        qst[i] = *reinterpret_cast<const u32x4*>(p.q + (base + row) * D + cp_ch);
+        ost[i] = *reinterpret_cast<const u32x4*>(p.dout + (base + row) * D + cp_ch);
+      } else {
+        qst[i] = u32x4{0, 0, 0, 0};
+        ost[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+    if (tid < BQ) {
+      const int row = qb * BQ + tid;
+      lst = row < N ? p.lse2[base + row] : INFINITY;
+      dst_ = row < N ? p.delta[base + row] : 0.f;
+    }
+  };
+  auto store_step = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4*>(&sm.q[buf][(cp_row + 16 * i) * QS + cp_ch]) = qst[i];
+      *reinterpret_cast<u32x4*>(&sm.dO[buf][(cp_row + 16 * i) * QS + cp_ch]) = ost[i];
+    }
+    if (tid < BQ) {
+      sm.lse2[buf][tid] = lst;
+      sm.dl[buf][tid] = dst_;
+    }
+  };
+
+  load_step(0);
+  store_step(0);
+  __syncthreads();
+
+  const int arow = perm_rows(l32);
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+
+  for (int st = 0; st < nsteps; ++st) {
+    const int cur = st & 1;
+    const int hi = st / nq, it = st - hi * nq;
+    const int h = h0 + hi;
+    const int e = queue[it];
+    const int qb = e & 0x7fffffff;
+    const bool partial = (e < 0) || ragged_k || (ragged_q_any && qb == p.nQB - 1);
+    const bool has_next = st + 1 < nsteps;
+    if (has_next) load_step(st + 1);
+
+    // ---- S = Q K^T and dP = dO V^T (rows q, columns = this wave's keys) ----
+    f32x16 sacc[2], pacc[2];
+#pragma unroll
+    for (int qblk = 0; qblk < 2; ++qblk) {
+      sacc[qblk] = f32x16{};
+      pacc[qblk] = f32x16{};
+      const bf16* qp = &sm.q[cur][(qblk * 32 + arow) * QS + hh * 8];
+      const bf16* op = &sm.dO[cur][(qblk * 32 + arow) * QS + hh * 8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        sacc[qblk] = mfma32(*reinterpret_cast<const bf16x8*>(qp + s * 16), kr[s], sacc[qblk]);
+        pacc[qblk] = mfma32(*reinterpret_cast<const bf16x8*>(op + s * 16), vr[s], pacc[qblk]);
+      }
+    }
+
+    // ---- P = exp2(S c - LSE2), masked on partial tiles; dS = P (dP - D) ----
+    bf16x8 pa[4], sa[4];
+#pragma unroll
+    for (int qblk = 0; qblk < 2; ++qblk) {
+      uint32_t word = 0u;
+      if (partial)
+        word = key_ok ? hidden_rows32(mv[0], mv[1], mv[2], mv[3], qb * BQ + qblk * 32)
+                      : 0xFFFFFFFFu;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int q0 = qblk * 32 + j * 16 + hh * 8;
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][q0]);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][q0 + 4]);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sm.dl[cur][q0]);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sm.dl[cur][q0 + 4]);
+        u32x4 pw, sw;
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+          float pv[2], sv[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int tt = t + u;
+            const float l = tt < 4 ? l0[tt] : l1[tt - 4];
+            const float dd = tt < 4 ? d0[tt] : d1[tt - 4];
+            float pp = __builtin_amdgcn_exp2f(fmaf(sacc[qblk][j * 8 + tt], p.c, -l));
+            if (partial && ((word >> (j * 16 + hh * 8 + tt)) & 1u)) pp = 0.f;
+            pv[u] = pp;
+            sv[u] = pp * (pacc[qblk][j * 8 + tt] - dd);
+          }
+          pw[t / 2] = pack_bf16x2(pv[0], pv[1]);
+          sw[t / 2] = pack_bf16x2(sv[0], sv[1]);
+        }
+        pa[qblk * 2 + j] = __builtin_bit_cast(bf16x8, pw);
+        sa[qblk * 2 + j] = __builtin_bit_cast(bf16x8, sw);
+        // dS^T to LDS for the dQ product: row = this lane's key, 8 consecutive q
+        *reinterpret_cast<u32x4*>(&sm.dst[(wave * 32 + l32) * SS + q0]) = sw;
+      }
+    }
+
+    // ---- dV += P^T dO, dK += dS^T Q  (B operands through transposing reads) ----
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int r0 = ks * 16 + hh * 8 + tr_row;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const bf16* op = &sm.dO[cur][r0 * QS + d * 32 + tr_col];
+        const bf16* qp = &sm.q[cur][r0 * QS + d * 32 + tr_col];
+        dv[d] = mfma32(pa[ks], join_tr(lds_read_tr16(op), lds_read_tr16(op + 4 * QS)), dv[d]);
+        dk[d] = mfma32(sa[ks], join_tr(lds_read_tr16(qp), lds_read_tr16(qp + 4 * QS)), dk[d]);
+      }
+    }
+
+    if (has_next) store_step(cur ^ 1);
+    __syncthreads();  // dS^T complete
+
+    // ---- dQ (64 x 128) += dS K over this workgroup's 128 keys; wave w: d-block w ----
+    {
+      f32x16 qacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int r0 = ks * 16 + hh * 8 + tr_row;
+        const bf16* kp = &sm.k[r0 * KS + wave * 32 + tr_col];
+        const bf16x8 bk = join_tr(lds_read_tr16(kp), lds_read_tr16(kp + 4 * KS));
+#pragma unroll
+        for (int qblk = 0; qblk < 2; ++qblk) {
+          const bf16* sp = &sm.dst[r0 * SS + qblk * 32 + tr_col];
+          const bf16x8 as = join_tr(lds_read_tr16(sp), lds_read_tr16(sp + 4 * SS));
+          qacc[qblk] = mfma32(as, bk, qacc[qblk]);
+        }
+      }
+      float* dqg = p.dq_acc + (size_t)(b * p.Hq + h) * N * D;
+#pragma unroll
+      for (int qblk = 0; qblk < 2; ++qblk) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = qb * BQ + qblk * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
+          if (row < N)
+            atomicAdd(dqg + (size_t)row * D + wave * 32 + l32, qacc[qblk][i]);
+        }
+      }
+    }
+    __syncthreads();  // dS^T and the current Q/dO buffer are free again
+  }
+
+  // ---- dK, dV of this workgroup's keys into the fp32 accumulators ----
+  float* dkg = p.dk_acc + (size_t)(b * p.Hkv + kvh) * N * D;
+  float* dvg = p.dv_acc + (size_t)(b * p.Hkv + kvh) * N * D;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kk = kb * BK + wave * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
+      if (kk < N) {
+        atomicAdd(dkg + (size_t)kk * D + d * 32 + l32, dk[d][i]);
+        atomicAdd(dvg + (size_t)kk * D + d * 32 + l32, dv[d][i]);
+      }
+    }
+  }
+}
+
+unsigned grid_for(size_t n, unsigned cap) {
+  size_t g = (n + 255) / 256;
+  return (unsigned)(g < cap ? (g ? g : 1) : cap);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  if (a.B == 0 || a.N == 0 || a.Hq == 0) return hipSuccess;
+  const size_t rows_q = (size_t)a.B * a.Hq * a.N;
+  const size_t rows_k = (size_t)a.B * a.Hkv * a.N;
+  hipLaunchKernelGGL(k_bwd_pre, dim3((unsigned)((rows_q + 15) / 16)), dim3(256), 0, s,
+                     static_cast<const bf16*>(a.o), static_cast<const bf16*>(a.dout), a.lse,
+                     a.lse2, a.delta, a.dq_acc, rows_q);
+  hipLaunchKernelGGL(k_zero, dim3(grid_for(rows_k * D / 4, 8192)), dim3(256), 0, s,
+                     reinterpret_cast<float4*>(a.dk_acc), rows_k * D / 4);
+  hipLaunchKernelGGL(k_zero, dim3(grid_for(rows_k * D / 4, 8192)), dim3(256), 0, s,
+                     reinterpret_cast<float4*>(a.dv_acc), rows_k * D / 4);
+
+  BwdParams p;
+  p.q = static_cast<const bf16*>(a.q);
+  p.k = static_cast<const bf16*>(a.k);
+  p.v = static_cast<const bf16*>(a.v);
+  p.dout = static_cast<const bf16*>(a.dout);
+  p.lse2 = a.lse2;
+  p.delta = a.delta;
+  p.m = a.m;
+  p.k_queue = a.k_queue;
+  p.k_count = a.k_count;
+  p.k_order = a.k_order;
+  p.dq_acc = a.dq_acc;
+  p.dk_acc = a.dk_acc;
+  p.dv_acc = a.dv_acc;
+  p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N; p.nQB = a.nQB; p.nKB = a.nKB;
+  const int g = a.Hq / a.Hkv;
+  p.hc = g < kBwdHeadChunk ? g : kBwdHeadChunk;
+  p.nch = (g + p.hc - 1) / p.hc;
+  p.c = a.scale * kLog2e;
+  const unsigned grid = (unsigned)a.B * (unsigned)a.nKB * (unsigned)a.Hkv * (unsigned)p.nch;
+  if (ev0) (void)hipEventRecord(ev0, s);
+  hipLaunchKernelGGL(k_attn_bwd, dim3(grid), dim3(256), 0, s, p);
+  if (ev1) (void)hipEventRecord(ev1, s);
+
+  hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_q * D / 8, 16384)), dim3(256), 0, s,
+                     a.dq_acc, static_cast<bf16*>(a.dq), a.scale, rows_q * D / 8);
+  hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_k * D / 8, 16384)), dim3(256), 0, s,
+                     a.dk_acc, static_cast<bf16*>(a.dk), a.scale, rows_k * D / 8);
+  hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_k * D / 8, 16384)), dim3(256), 0, s,
+                     a.dv_acc, static_cast<bf16*>(a.dv), 1.0f, rows_k * D / 8);
+  return hipGetLastError();
+}
+
+}  // namespace fm

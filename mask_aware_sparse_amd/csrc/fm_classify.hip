@@ -1,0 +1,225 @@
+// Tile classification, queues, costs and the LPT order (gfx950).
+//
+// FlashMask-3 page, §3.1: the block-wise min/max of the column vectors decide for each
+// (Q-block, KV-block) tile whether it is skipped, partial or unmasked, and the KV
+// Index Generator emits per Q-block a queue of the KV blocks to visit (right to left),
+// each tagged partial or unmasked.  §3.3: a tile costs 0, alpha_p or alpha_u; work is
+// balanced by those costs.  Here the queues are built by one HBM pass over the
+// vectors plus one pass per queue row; the LPT order is a bitonic sort in LDS.
+#include "fm_device.h"
+#include "fm_internal.h"
+
+#include <climits>
+
+namespace fm {
+
+// ---- A2: block min/max of the four vectors -------------------------------------
+// One wave per (b, kb); lane l reduces columns kb*bk + l + 64t.
+__global__ __launch_bounds__(64) void k_block_minmax(MaskPtrs m, int N, int nKB, int bk,
+                                                     int32_t* __restrict__ mm) {
+  const int bkb = blockIdx.x;
+  const int b = bkb / nKB, kb = bkb - b * nKB;
+  const int lane = threadIdx.x;
+  const size_t rowoff = (size_t)b * N;
+  const int c0 = kb * bk, c1 = min(c0 + bk, N);
+  int v[8] = {INT_MAX, INT_MIN, INT_MAX, INT_MIN, INT_MAX, INT_MIN, INT_MAX, INT_MIN};
+  for (int c = c0 + lane; c < c1; c += 64) {
+    int x0 = m.lts[rowoff + c], x1 = m.lte[rowoff + c];
+    int x2 = m.uts[rowoff + c], x3 = m.ute[rowoff + c];
+    v[0] = min(v[0], x0); v[1] = max(v[1], x0);
+    v[2] = min(v[2], x1); v[3] = max(v[3], x1);
+    v[4] = min(v[4], x2); v[5] = max(v[5], x2);
+    v[6] = min(v[6], x3); v[7] = max(v[7], x3);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) {
+      v[t] = min(v[t], __shfl_xor(v[t], off));
+      v[t + 1] = max(v[t + 1], __shfl_xor(v[t + 1], off));
+    }
+  }
+  if (lane < 8) {
+    int out = v[0];
+#pragma unroll
+    for (int t = 1; t < 8; ++t) out = (lane == t) ? v[t] : out;
+    mm[(size_t)bkb * 8 + lane] = out;
+  }
+}
+
+__device__ __forceinline__ void load_mm(const int32_t* __restrict__ mm, size_t idx, int* r) {
+  const int4* p = reinterpret_cast<const int4*>(mm + idx * 8);
+  int4 a = p[0], c = p[1];
+  r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+  r[4] = c.x; r[5] = c.y; r[6] = c.z; r[7] = c.w;
+}
+
+// Workgroup-wide ordered compaction helper: returns (exclusive offset of this
+// thread among flagged threads, total flagged, total of `sub` among flagged).
+struct ScanResult { int off; int total; int sub; };
+__device__ __forceinline__ ScanResult block_scan_256(bool flag, bool sub, int* sh_cnt,
+                                                     int* sh_sub) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  unsigned long long bal = __ballot(flag);
+  unsigned long long bsub = __ballot(flag && sub);
+  if (lane == 0) { sh_cnt[w] = __popcll(bal); sh_sub[w] = __popcll(bsub); }
+  __syncthreads();
+  ScanResult r{0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < w) r.off += sh_cnt[i];
+    r.total += sh_cnt[i];
+    r.sub += sh_sub[i];
+  }
+  r.off += __popcll(bal & ((1ull << lane) - 1ull));
+  __syncthreads();
+  return r;
+}
+
+// ---- A3: classes and per-Q-block queues (KV blocks right to left) --------------
+__global__ __launch_bounds__(256) void k_classify_q(const int32_t* __restrict__ mm, int N,
+                                                    int nQB, int nKB, int bq,
+                                                    uint8_t* __restrict__ cls,
+                                                    int32_t* __restrict__ q_queue,
+                                                    int32_t* __restrict__ q_count,
+                                                    int32_t* __restrict__ q_cost) {
+  __shared__ int sh_cnt[4], sh_sub[4];
+  const int row = blockIdx.x;  // b * nQB + qb
+  const int b = row / nQB, qb = row - b * nQB;
+  const int q0 = qb * bq, q1 = min(q0 + bq, N);
+  const int tid = threadIdx.x;
+  int base = 0, np = 0;
+  for (int c0 = 0; c0 < nKB; c0 += 256) {
+    const int idx = c0 + tid;
+    const bool valid = idx < nKB;
+    const int kb = nKB - 1 - idx;
+    int c = 0;
+    if (valid) {
+      int v[8];
+      load_mm(mm, (size_t)b * nKB + kb, v);
+      c = tile_class(v, q0, q1);
+      if (cls) cls[(size_t)row * nKB + kb] = (uint8_t)c;
+    }
+    ScanResult s = block_scan_256(valid && c != 0, c == 1, sh_cnt, sh_sub);
+    if (q_queue && valid && c != 0)
+      q_queue[(size_t)row * nKB + base + s.off] = kb | (c == 1 ? (int)0x80000000 : 0);
+    base += s.total;
+    np += s.sub;
+  }
+  if (q_queue) {
+    for (int p = base + tid; p < nKB; p += 256) q_queue[(size_t)row * nKB + p] = -1;
+    if (tid == 0) {
+      q_count[(size_t)row * 2] = np;
+      q_count[(size_t)row * 2 + 1] = base - np;
+      q_cost[row] = kAlphaPartial * np + kAlphaUnmasked * (base - np);
+    }
+  }
+}
+
+// ---- A3 (backward direction): per-KV-block queues of Q-blocks, ascending -----------
+__global__ __launch_bounds__(256) void k_classify_k(const int32_t* __restrict__ mm, int N,
+                                                    int nQB, int nKB, int bq,
+                                                    int32_t* __restrict__ k_queue,
+                                                    int32_t* __restrict__ k_count,
+                                                    int32_t* __restrict__ k_cost) {
+  __shared__ int sh_cnt[4], sh_sub[4];
+  const int row = blockIdx.x;  // b * nKB + kb
+  const int tid = threadIdx.x;
+  int v[8];
+  load_mm(mm, (size_t)row, v);
+  int base = 0, np = 0;
+  for (int c0 = 0; c0 < nQB; c0 += 256) {
+    const int qb = c0 + tid;
+    const bool valid = qb < nQB;
+    int c = 0;
+    if (valid) c = tile_class(v, qb * bq, min(qb * bq + bq, N));
+    ScanResult s = block_scan_256(valid && c != 0, c == 1, sh_cnt, sh_sub);
+    if (valid && c != 0)
+      k_queue[(size_t)row * nQB + base + s.off] = qb | (c == 1 ? (int)0x80000000 : 0);
+    base += s.total;
+    np += s.sub;
+  }
+  for (int p = base + tid; p < nQB; p += 256) k_queue[(size_t)row * nQB + p] = -1;
+  if (tid == 0) {
+    k_count[(size_t)row * 2] = np;
+    k_count[(size_t)row * 2 + 1] = base - np;
+    k_cost[row] = kAlphaPartial * np + kAlphaUnmasked * (base - np);
+  }
+}
+
+// ---- A4: longest-processing-time-first order ----------------------------------
+// Keys (~cost << 32 | index) sorted ascending = cost descending, index ascending.
+__global__ __launch_bounds__(1024) void k_lpt_sort(const int32_t* __restrict__ cost,
+                                                   int32_t* __restrict__ order, int count) {
+  __shared__ unsigned long long keys[kMaxSortItems];
+  const int tid = threadIdx.x;
+  int P = 1;
+  while (P < count) P <<= 1;
+  for (int i = tid; i < P; i += 1024)
+    keys[i] = i < count ? ((unsigned long long)(0xFFFFFFFFu - (unsigned)cost[i]) << 32) |
+                              (unsigned)i
+                        : ~0ull;
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P; i += 1024) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const unsigned long long a = keys[i], c = keys[ixj];
+          const bool up = (i & k) == 0;
+          if ((a > c) == up) { keys[i] = c; keys[ixj] = a; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < count; i += 1024) order[i] = (int32_t)(keys[i] & 0xFFFFFFFFull);
+}
+
+// ---- Dense expansion through the kernels' own predicate (checking only) ----------
+__global__ __launch_bounds__(256) void k_expand_mask(MaskPtrs m, int b, int N, int row0,
+                                                     int row1, uint8_t* __restrict__ dense) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= N) return;
+  const size_t o = (size_t)b * N + j;
+  const int lts = m.lts[o], lte = m.lte[o], uts = m.uts[o], ute = m.ute[o];
+  for (int w = blockIdx.y; row0 + 32 * w < row1; w += gridDim.y) {
+    const int r0 = row0 + 32 * w;
+    const uint32_t word = hidden_rows32(lts, lte, uts, ute, r0);
+    const int nr = min(32, row1 - r0);
+    for (int r = 0; r < nr; ++r)
+      dense[(size_t)(r0 - row0 + r) * N + j] = (uint8_t)((word >> r) & 1u);
+  }
+}
+
+// ---- host launchers --------------------------------------------------------------
+hipError_t launch_classify(const MaskPtrs& m, int B, int N, int bq, int bk, const TileOut& out,
+                           hipStream_t s) {
+  const int nQB = (N + bq - 1) / bq, nKB = (N + bk - 1) / bk;
+  if (B == 0 || N == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_block_minmax, dim3(B * nKB), dim3(64), 0, s, m, N, nKB, bk, out.minmax);
+  if (out.tile_class || out.q_queue)
+    hipLaunchKernelGGL(k_classify_q, dim3(B * nQB), dim3(256), 0, s, out.minmax, N, nQB, nKB,
+                       bq, out.tile_class, out.q_queue, out.q_count, out.q_cost);
+  if (out.k_queue)
+    hipLaunchKernelGGL(k_classify_k, dim3(B * nKB), dim3(256), 0, s, out.minmax, N, nQB, nKB,
+                       bq, out.k_queue, out.k_count, out.k_cost);
+  return hipGetLastError();
+}
+
+hipError_t launch_lpt_sort(const int32_t* cost, int32_t* order, int count, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_lpt_sort, dim3(1), dim3(1024), 0, s, cost, order, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand_mask(const MaskPtrs& m, int b, int N, int row0, int row1,
+                              uint8_t* dense, hipStream_t s) {
+  if (N == 0 || row1 <= row0) return hipSuccess;
+  const int windows = (row1 - row0 + 31) / 32;
+  dim3 grid((N + 255) / 256, (unsigned)min(windows, 65535));
+  hipLaunchKernelGGL(k_expand_mask, grid, dim3(256), 0, s, m, b, N, row0, row1, dense);
+  return hipGetLastError();
+}
+
+}  // namespace fm

@@ -1,0 +1,102 @@
+// Device-side helpers shared by the libfm kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fm {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// The mask predicate.  Key column j hides query row i iff
+//   LTS_j <= i < LTE_j  or  UTS_j <= i < UTE_j
+// (column-wise row bounds, FlashMask-3 page, Overview).  Kernels evaluate it 32
+// rows at a time: bit r of the word is set iff row r0 + r is hidden.  Every
+// consumer of the mask (forward, backward, dense debug expansion) calls this
+// function, so they agree bit for bit.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t range_bits32(int a, int b, int r0) {
+  // bits r in [0, 32) with a <= r0 + r < b
+  int lo = min(max(a - r0, 0), 32);
+  int hi = min(max(b - r0, 0), 32);
+  uint32_t hm = (uint32_t)((1ull << hi) - 1ull);
+  uint32_t lm = (uint32_t)((1ull << lo) - 1ull);
+  return hm & ~lm;
+}
+
+__device__ __forceinline__ uint32_t hidden_rows32(int lts, int lte, int uts, int ute, int r0) {
+  return range_bits32(lts, lte, r0) | range_bits32(uts, ute, r0);
+}
+
+// ---------------------------------------------------------------------------
+// Tile classification rule (FlashMask-3 page, §3.1, generalized to both row
+// intervals).  mm = {minLTS, maxLTS, minLTE, maxLTE, minUTS, maxUTS, minUTE, maxUTE}
+// over the KV block's columns; rows [q0, q1).  0 skip, 1 partial, 2 unmasked.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int tile_class(const int* mm, int q0, int q1) {
+  bool skip = (q0 >= mm[1] && q1 <= mm[2]) || (q0 >= mm[5] && q1 <= mm[6]);
+  bool unm = (q1 <= mm[0] || q0 >= mm[3]) && (q1 <= mm[4] || q0 >= mm[7]);
+  return skip ? 0 : (unm ? 2 : 1);
+}
+
+// ---------------------------------------------------------------------------
+// Small numeric helpers.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  bf16x2 v = {(bf16)a, (bf16)b};  // round to nearest even
+  return __builtin_bit_cast(unsigned, v);
+}
+
+__device__ __forceinline__ float bf16lo_to_f32(unsigned u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(unsigned u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// value of lane (l ^ 32) of the same wave, combined with the own value
+__device__ __forceinline__ float max_with_partner32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_partner32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives element i%4 of the 64-bit words fetched by lanes
+// 4t + i/4 (t = 0..3).  With lane j of the group pointing at row (r0 + j/4),
+// columns (c0 + 4*(j%4)) .. +3 of a row-major 16-bit matrix, lane i receives
+// rows r0..r0+3 of column c0 + i.
+__device__ __forceinline__ i16x4 lds_read_tr16(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
+  u32x2 a = __builtin_bit_cast(u32x2, lo);
+  u32x2 b = __builtin_bit_cast(u32x2, hi);
+  u32x4 r = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace fm

@@ -1,0 +1,291 @@
+// Mask-aware attention forward (gfx950, bf16 MFMA 32x32x16).
+//
+// One workgroup = one (b, Q-block of 128 rows, query head).  Workgroups are numbered
+// in LPT order (Q-blocks by tile cost descending, heads of a Q-block adjacent), so the
+// hardware dispatcher performs greedy list scheduling in that order (FlashMask-3 page,
+// §3.3; Flash MSA guide, "Optimization Tricks That Actually Matter").  The workgroup
+// walks its Q-block's queue of KV blocks (right to left, FlashMask-3 page §3.1): only
+// queued blocks are loaded, and the row-interval mask is applied only on tiles tagged
+// partial.  Per tile it runs the online softmax of the Flash MSA guide ("The Flash
+// Core"): running row max and sum, rescaling of the accumulator, normalisation at the
+// end; O and the natural-log LSE are written.
+//
+// Layout of the work.  4 waves x 32 query rows.  Each wave computes S^T = K Q^T so that
+// a lane owns one query row (its 32 scores sit in one lane and its partner lane l^32),
+// then O^T += V^T P^T so that the same lane owns that row of the accumulator; the
+// softmax statistics therefore never leave the lane pair.  Q stays in registers; K and
+// V tiles are double-buffered through LDS (row-major; V is read with the transposing
+// ds_read_b64_tr_b16).  Two row sums are kept: l_f (fp32 sum of p) gives the LSE,
+// l_b (sum of the bf16-rounded p that the PV product actually used) normalises O.
+#include "fm_device.h"
+#include "fm_internal.h"
+
+namespace fm {
+namespace {
+
+constexpr int BQ = kFwdBlockQ;  // 128
+constexpr int BK = kFwdBlockK;  // 64
+constexpr int D = kHeadDim;     // 128
+constexpr int KS = D + 8;       // K row stride in LDS (elements)
+constexpr int VS = D + 16;      // V row stride in LDS (elements)
+
+struct FwdSmem {
+  bf16 k[2][BK * KS];
+  bf16 v[2][BK * VS];
+  uint32_t mw[2][4][BK];  // hidden-row words: [buffer][wave][key]
+};
+
+// A-operand row permutation for S^T = K Q^T: A row a holds key perm(a) so that the
+// accumulator rows a lane owns are runs of 8 consecutive keys, which is exactly the
+// k-ordering the following PV product wants for its B operand.
+__device__ __forceinline__ int perm_rows(int a) {
+  return (a & 0x13) | ((a & 4) << 1) | ((a & 8) >> 1);
+}
+
+struct FwdParams {
+  const bf16* __restrict__ q;
+  const bf16* __restrict__ k;
+  const bf16* __restrict__ v;
+  MaskPtrs m;
+  bf16* __restrict__ o;
+  float* __restrict__ lse;
+  const int32_t* __restrict__ q_queue;
+  const int32_t* __restrict__ q_count;
+  const int32_t* __restrict__ q_order;
+  int B, Hq, Hkv, N, nQB, nKB;
+  float c;  // softmax scale * log2(e)
+};
+
+__global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
+  __shared__ FwdSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  const int r = blockIdx.x / p.Hq, h = blockIdx.x - r * p.Hq;
+  const int item = p.q_order[r];
+  const int b = item / p.nQB, qb = item - b * p.nQB;
+  const int kvh = h / (p.Hq / p.Hkv);
+  const int n_tiles = p.q_count[2 * item] + p.q_count[2 * item + 1];
+  const int32_t* queue = p.q_queue + (size_t)item * p.nKB;
+  const bf16* qg = p.q + (size_t)(b * p.Hq + h) * p.N * D;
+  const bf16* kg = p.k + (size_t)(b * p.Hkv + kvh) * p.N * D;
+  const bf16* vg = p.v + (size_t)(b * p.Hkv + kvh) * p.N * D;
+  const size_t mrow = (size_t)b * p.N;
+  const int N = p.N;
+  const bool ragged = (N % BK) != 0;
+
+  const int row = qb * BQ + wave * 32 + l32;
+  const bool row_ok = row < N;
+
+  // Q^T operand: lane holds Q[row][s*16 + hh*8 .. +7] for s = 0..7
+  bf16x8 qr[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    if (row_ok) qr[s] = *reinterpret_cast<const bf16x8*>(qg + (size_t)row * D + s * 16 + hh * 8);
+    else qr[s] = bf16x8{};
+  }
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) oacc[d] = f32x16{};
+  float m_run = -INFINITY, lf = 0.f, lb = 0.f;
+
+  // staging for the tile copy: thread copies rows (tid>>4)+16i, 16-byte chunk tid&15
+  const int cp_row = tid >> 4, cp_ch = (tid & 15) * 8;
+  const int mk_key = tid & 63, mk_wave = tid >> 6;
+  u32x4 kst[4], vst[4];
+  int vec[4];
+
+  auto load_tile = [&](int e) {
+    const int kb = e & 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kb * BK + cp_row + 16 * i;
+      if (key < N) {
+        kst[i] = *reinterpret_cast<const u32x4*>(kg + (size_t)key * D + cp_ch);
+        vst[i] = *reinterpret_cast<const u32x4*>(vg + (size_t)key * D + cp_ch);
+      } else {
+        kst[i] = u32x4{0, 0, 0, 0};
+        vst[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+    const bool part = (e < 0) || (ragged && kb == p.nKB - 1);
+    const int key = kb * BK + mk_key;
+    if (part && key < N) {
+      vec[0] = p.m.lts[mrow + key]; vec[1] = p.m.lte[mrow + key];
+      vec[2] = p.m.uts[mrow + key]; vec[3] = p.m.ute[mrow + key];
+    }
+  };
+  auto store_tile = [&](int e, int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4*>(&sm.k[buf][(cp_row + 16 * i) * KS + cp_ch]) = kst[i];
+      *reinterpret_cast<u32x4*>(&sm.v[buf][(cp_row + 16 * i) * VS + cp_ch]) = vst[i];
+    }
+    const int kb = e & 0x7fffffff;
+    const bool part = (e < 0) || (ragged && kb == p.nKB - 1);
+    if (part) {
+      const int key = kb * BK + mk_key;
+      const int r0 = qb * BQ + mk_wave * 32;
+      sm.mw[buf][mk_wave][mk_key] =
+          key < N ? hidden_rows32(vec[0], vec[1], vec[2], vec[3], r0) : 0xFFFFFFFFu;
+    }
+  };
+
+  if (n_tiles > 0) {
+    load_tile(queue[0]);
+    store_tile(queue[0], 0);
+  }
+  __syncthreads();
+
+  const int arow = perm_rows(l32);
+  // transposing-read coordinates for the V^T operand
+  const int tr_row = (lane & 15) >> 2;                  // + key base
+  const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);  // + d-block base
+
+  for (int it = 0; it < n_tiles; ++it) {
+    const int cur = it & 1;
+    const int e = queue[it];
+    const int kb = e & 0x7fffffff;
+    const bool partial = (e < 0) || (ragged && kb == p.nKB - 1);
+    int en = 0;
+    const bool has_next = it + 1 < n_tiles;
+    if (has_next) {
+      en = queue[it + 1];
+      load_tile(en);
+    }
+
+    // ---- S^T = K Q^T (fp32) ----
+    f32x16 sacc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      sacc[blk] = f32x16{};
+      const bf16* kp = &sm.k[cur][(blk * 32 + arow) * KS + hh * 8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + s * 16);
+        sacc[blk] = mfma32(a, qr[s], sacc[blk]);
+      }
+    }
+
+    // ---- row-interval mask, partial tiles only ----
+    if (partial) {
+      const uint32_t* mw = sm.mw[cur][wave];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const u32x4 w0 = *reinterpret_cast<const u32x4*>(mw + blk * 32 + j * 16 + hh * 8);
+          const u32x4 w1 = *reinterpret_cast<const u32x4*>(mw + blk * 32 + j * 16 + hh * 8 + 4);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const uint32_t w = t < 4 ? w0[t] : w1[t - 4];
+            if ((w >> l32) & 1u) sacc[blk][j * 8 + t] = -INFINITY;
+          }
+        }
+      }
+    }
+
+    // ---- online softmax ----
+    float mx = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
+    mx = max_with_partner32(mx);
+    const float m_new = fmaxf(m_run, mx * p.c);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+
+    bf16x8 pb[4];
+    float psum = 0.f, pbsum = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        u32x4 packed;
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[blk][j * 8 + t], p.c, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[blk][j * 8 + t + 1], p.c, -m_use));
+          psum += p0 + p1;
+          const unsigned u = pack_bf16x2(p0, p1);
+          packed[t / 2] = u;
+          pbsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u),
+                                                  bf16x2{(bf16)1.0f, (bf16)1.0f}, pbsum, false);
+        }
+        pb[blk * 2 + j] = __builtin_bit_cast(bf16x8, packed);
+      }
+    }
+    lf = lf * alpha + psum;
+    lb = lb * alpha + pbsum;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+
+    // ---- O^T += V^T P^T ----
+    const bf16* vb = sm.v[cur];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int key0 = ks * 16 + hh * 8 + tr_row;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const bf16* vp = vb + key0 * VS + d * 32 + tr_col;
+        const bf16x8 a = join_tr(lds_read_tr16(vp), lds_read_tr16(vp + 4 * VS));
+        oacc[d] = mfma32(a, pb[ks], oacc[d]);
+      }
+    }
+
+    if (has_next) store_tile(en, cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l_b, LSE = ln2 * (m + log2 l_f) ----
+  lf = sum_with_partner32(lf);
+  lb = sum_with_partner32(lb);
+  if (row_ok) {
+    const float inv = lb > 0.f ? 1.0f / lb : 0.f;
+    bf16* og = p.o + (size_t)(b * p.Hq + h) * N * D + (size_t)row * D;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[d][g * 4 + 0] * inv, oacc[d][g * 4 + 1] * inv);
+        w[1] = pack_bf16x2(oacc[d][g * 4 + 2] * inv, oacc[d][g * 4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(og + d * 32 + g * 8 + hh * 4) = w;
+      }
+    }
+    if (hh == 0)
+      p.lse[(size_t)(b * p.Hq + h) * N + row] =
+          lf > 0.f ? (m_run + __builtin_amdgcn_logf(lf)) * kLn2 : -INFINITY;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  if (a.B == 0 || a.N == 0 || a.Hq == 0) return hipSuccess;
+  FwdParams p;
+  p.q = static_cast<const bf16*>(a.q);
+  p.k = static_cast<const bf16*>(a.k);
+  p.v = static_cast<const bf16*>(a.v);
+  p.m = a.m;
+  p.o = static_cast<bf16*>(a.o);
+  p.lse = a.lse;
+  p.q_queue = a.q_queue;
+  p.q_count = a.q_count;
+  p.q_order = a.q_order;
+  p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N; p.nQB = a.nQB; p.nKB = a.nKB;
+  p.c = a.scale * kLog2e;
+  const unsigned grid = (unsigned)a.B * (unsigned)a.nQB * (unsigned)a.Hq;
+  if (ev0) (void)hipEventRecord(ev0, s);
+  hipLaunchKernelGGL(k_attn_fwd, dim3(grid), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (ev1) (void)hipEventRecord(ev1, s);
+  return e;
+}
+
+}  // namespace fm

@@ -1,0 +1,91 @@
+// Host-side declarations shared by the libfm translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fm {
+
+constexpr int kHeadDim = 128;
+
+// Tile shapes of the attention kernels.  The forward uses 128 query rows (4 waves x
+// 32) by 64 keys; the backward 64 query rows by 128 keys (4 waves x 32 keys).
+constexpr int kFwdBlockQ = 128;
+constexpr int kFwdBlockK = 64;
+constexpr int kBwdBlockQ = 64;
+constexpr int kBwdBlockK = 128;
+// Query heads handled by one backward work item (dK/dV of a KV block are summed over
+// these heads in registers, then added across items with fp32 atomics).
+constexpr int kBwdHeadChunk = 4;
+// Tile costs in integer units, alpha_partial : alpha_unmasked = 1.3 : 1.
+constexpr int kAlphaPartial = 13;
+constexpr int kAlphaUnmasked = 10;
+// The LPT sort runs in one workgroup with 64-bit keys in LDS.
+constexpr int kMaxSortItems = 8192;
+
+struct MaskPtrs {
+  const int32_t* lts;
+  const int32_t* lte;
+  const int32_t* uts;
+  const int32_t* ute;
+};
+
+// Classification outputs; any of the optional outputs may be null.
+struct TileOut {
+  int32_t* minmax;       // [B][nKB][8]                (required)
+  uint8_t* tile_class;   // [B][nQB][nKB]              (optional)
+  int32_t* q_queue;      // [B][nQB][nKB]              (optional)
+  int32_t* q_count;      // [B][nQB][2]                (required if q_queue)
+  int32_t* q_cost;       // [B*nQB]                    (required if q_queue)
+  int32_t* k_queue;      // [B][nKB][nQB]              (optional)
+  int32_t* k_count;      // [B][nKB][2]                (required if k_queue)
+  int32_t* k_cost;       // [B*nKB]                    (required if k_queue)
+};
+
+hipError_t launch_classify(const MaskPtrs& m, int B, int N, int bq, int bk, const TileOut& out,
+                           hipStream_t s);
+hipError_t launch_lpt_sort(const int32_t* cost, int32_t* order, int count, hipStream_t s);
+hipError_t launch_expand_mask(const MaskPtrs& m, int b, int N, int row0, int row1,
+                              uint8_t* dense, hipStream_t s);
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  MaskPtrs m;
+  void* o;
+  float* lse;
+  const int32_t* q_queue;
+  const int32_t* q_count;
+  const int32_t* q_order;
+  int B, Hq, Hkv, N, nQB, nKB;
+  float scale;
+};
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  MaskPtrs m;
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* k_queue;
+  const int32_t* k_count;
+  const int32_t* k_order;
+  float* lse2;   // [B][Hq][N] log2-domain LSE (+inf for rows that see nothing)
+  float* delta;  // [B][Hq][N] rowsum(dO * O)
+  float* dq_acc; // [B][Hq][N][128] fp32
+  float* dk_acc; // [B][Hkv][N][128] fp32
+  float* dv_acc; // [B][Hkv][N][128] fp32
+  int B, Hq, Hkv, N, nQB, nKB;
+  float scale;
+};
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+
+}  // namespace fm

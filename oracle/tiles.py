@@ -51,22 +51,24 @@ def block_minmax(vec, bk):
 
 
 def classify(lts, lte, uts, ute, bq, bk):
-    """Tile class [B][nQB][nKB] (uint8: 0 skip, 1 partial, 2 unmasked)."""
+    """Tile class [B][nQB][nKB] (uint8: 0 skip, 1 partial, 2 unmasked).
+
+    For each batch row and KV block the rule is evaluated for all Q-blocks at once
+    (q0, q1 as arrays)."""
     B, N = np.asarray(lts).shape
     nqb, nkb = _nblocks(N, bq), _nblocks(N, bk)
     (mnLTS, mxLTS), (mnLTE, mxLTE), (mnUTS, mxUTS), (mnUTE, mxUTE) = (
         block_minmax(x, bk) for x in (lts, lte, uts, ute))
+    q0 = np.arange(nqb, dtype=np.int64) * bq
+    q1 = np.minimum(q0 + bq, N)
     cls = np.zeros((B, nqb, nkb), dtype=np.uint8)
     for b in range(B):
         for kb in range(nkb):
-            for qb in range(nqb):
-                q0 = qb * bq
-                q1 = min(q0 + bq, N)
-                skip = ((q0 >= mxLTS[b, kb] and q1 <= mnLTE[b, kb]) or
-                        (q0 >= mxUTS[b, kb] and q1 <= mnUTE[b, kb]))
-                unmasked = ((q1 <= mnLTS[b, kb] or q0 >= mxLTE[b, kb]) and
-                            (q1 <= mnUTS[b, kb] or q0 >= mxUTE[b, kb]))
-                cls[b, qb, kb] = SKIP if skip else (UNMASKED if unmasked else PARTIAL)
+            skip = (((q0 >= mxLTS[b, kb]) & (q1 <= mnLTE[b, kb])) |
+                    ((q0 >= mxUTS[b, kb]) & (q1 <= mnUTE[b, kb])))
+            unmasked = (((q1 <= mnLTS[b, kb]) | (q0 >= mxLTE[b, kb])) &
+                        ((q1 <= mnUTS[b, kb]) | (q0 >= mxUTE[b, kb])))
+            cls[b, :, kb] = np.where(skip, SKIP, np.where(unmasked, UNMASKED, PARTIAL))
     return cls
 
 
@@ -100,28 +102,22 @@ def queues(cls):
     Queues are returned as int32 arrays padded with -1 after their last entry."""
     cls = np.asarray(cls)
     B, nqb, nkb = cls.shape
-    tag = np.uint32(1 << 31)
+    tag = np.int64(1 << 31)
     q_queue = np.full((B, nqb, nkb), -1, dtype=np.int64)
     q_count = np.zeros((B, nqb, 2), dtype=np.int32)
     k_queue = np.full((B, nkb, nqb), -1, dtype=np.int64)
     k_count = np.zeros((B, nkb, 2), dtype=np.int32)
     for b in range(B):
         for qb in range(nqb):
-            t = 0
-            for kb in range(nkb - 1, -1, -1):
-                c = cls[b, qb, kb]
-                if c != SKIP:
-                    q_queue[b, qb, t] = kb | (int(tag) if c == PARTIAL else 0)
-                    t += 1
-                    q_count[b, qb, 0 if c == PARTIAL else 1] += 1
+            row = cls[b, qb]
+            kbs = np.nonzero(row != SKIP)[0][::-1]           # right to left
+            q_queue[b, qb, :len(kbs)] = kbs + np.where(row[kbs] == PARTIAL, tag, 0)
+            q_count[b, qb] = ((row == PARTIAL).sum(), (row == UNMASKED).sum())
         for kb in range(nkb):
-            t = 0
-            for qb in range(nqb):
-                c = cls[b, qb, kb]
-                if c != SKIP:
-                    k_queue[b, kb, t] = qb | (int(tag) if c == PARTIAL else 0)
-                    t += 1
-                    k_count[b, kb, 0 if c == PARTIAL else 1] += 1
+            col = cls[b, :, kb]
+            qbs = np.nonzero(col != SKIP)[0]                  # ascending
+            k_queue[b, kb, :len(qbs)] = qbs + np.where(col[qbs] == PARTIAL, tag, 0)
+            k_count[b, kb] = ((col == PARTIAL).sum(), (col == UNMASKED).sum())
     as_i32 = lambda a: np.where(a < 0, -1, a).astype(np.uint32).view(np.int32)
     return as_i32(q_queue), q_count, as_i32(k_queue), k_count
 
