@@ -57,7 +57,7 @@ def cpu_baseline(w, q, k, v, do, budget_s):
     except Exception:
         threads = os.cpu_count()
     g = w.heads_q // w.heads_kv
-    heads = list(range(0, w.heads_q, max(1, w.heads_q // 8)))
+    heads = list(range(w.heads_q))
     done, pairs, t_total = [], 0, 0.0
     for b in range(w.batch):
         for h in heads:
