@@ -22,13 +22,15 @@
 #include "fm_device.h"
 #include "fm_internal.h"
 
+#include <type_traits>
+
 namespace fm {
 namespace {
 
 constexpr int BQ = kBwdBlockQ;  // 64 query rows per step
 constexpr int BK = kBwdBlockK;  // 128 keys per workgroup
 constexpr int D = kHeadDim;
-constexpr int QS = D + 8;       // Q / dO row stride in LDS
+constexpr int QS = D + 16;      // Q / dO row stride in LDS (288 B: b128 and transposing reads)
 constexpr int KS = D + 16;      // K row stride in LDS (transposing reads)
 constexpr int SS = BQ + 16;     // dS^T row stride in LDS (transposing reads)
 
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(256) void k_bwd_convert(const float* __restrict__ s
 }
 
 // ---- KE: main backward ------------------------------------------------------------------
-struct BwdSmem {
+struct __attribute__((aligned(16))) BwdSmem {
   bf16 q[2][BQ * QS];
   bf16 dO[2][BQ * QS];
   bf16 k[BK * KS];
@@ -132,30 +134,34 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdParams p) {
   if (nq == 0 || nh <= 0) return;
   const int32_t* queue = p.k_queue + (size_t)item * p.nQB;
   const bool ragged_k = (N % BK) != 0 && kb == p.nKB - 1;
-  const bool ragged_q_any = (N % BQ) != 0;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const uint32_t acc_bytes = (uint32_t)N * D * 4;
 
   // ---- resident K, V (B operands of S = Q K^T and dP = dO V^T), and the lane's key
   const int key = kb * BK + wave * 32 + l32;
-  const bool key_ok = key < N;
-  const bf16* kg = p.k + (size_t)(b * p.Hkv + kvh) * N * D;
-  const bf16* vg = p.v + (size_t)(b * p.Hkv + kvh) * N * D;
-  bf16x8 kr[8], vr[8];
+  const size_t kvbase = (size_t)(b * p.Hkv + kvh) * N * D;
+  const rsrc_t kr_ = make_rsrc(p.k + kvbase, head_bytes);
+  const rsrc_t vr_ = make_rsrc(p.v + kvbase, head_bytes);
+  bf16x8 vr[8];
+  {
+    const uint32_t off = (uint32_t)key * (D * 2) + hh * 16;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    if (key_ok) {
-      kr[s] = *reinterpret_cast<const bf16x8*>(kg + (size_t)key * D + s * 16 + hh * 8);
-      vr[s] = *reinterpret_cast<const bf16x8*>(vg + (size_t)key * D + s * 16 + hh * 8);
-    } else {
-      kr[s] = bf16x8{};
-      vr[s] = bf16x8{};
+    for (int s = 0; s < 8; ++s) {
+      vr[s] = __builtin_bit_cast(bf16x8, buf_load16(vr_, off, s * 32));
+      *reinterpret_cast<u32x4*>(&sm.k[(wave * 32 + l32) * KS + s * 16 + hh * 8]) =
+          buf_load16(kr_, off, s * 32);
     }
-    *reinterpret_cast<bf16x8*>(&sm.k[(wave * 32 + l32) * KS + s * 16 + hh * 8]) = kr[s];
   }
-  int mv[4] = {0, 0, 0, 0};
-  if (key_ok) {
-    const size_t o = (size_t)b * N + key;
-    mv[0] = p.m.lts[o]; mv[1] = p.m.lte[o]; mv[2] = p.m.uts[o]; mv[3] = p.m.ute[o];
+  int mv[4];
+  {
+    const uint32_t vb = (uint32_t)N * 4, vo = (uint32_t)key * 4;
+    const size_t mrow = (size_t)b * N;
+    mv[0] = (int)buf_load4(make_rsrc(p.m.lts + mrow, vb), vo, 0);
+    mv[1] = (int)buf_load4(make_rsrc(p.m.lte + mrow, vb), vo, 0);
+    mv[2] = (int)buf_load4(make_rsrc(p.m.uts + mrow, vb), vo, 0);
+    mv[3] = (int)buf_load4(make_rsrc(p.m.ute + mrow, vb), vo, 0);
   }
+  const bool key_ok = key < N;
 
   f32x16 dk[4], dv[4];
 #pragma unroll
@@ -164,7 +170,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdParams p) {
   // ---- staging of the Q / dO tiles: thread copies rows (tid>>4)+16i, chunk tid&15
   const int cp_row = tid >> 4, cp_ch = (tid & 15) * 8;
   u32x4 qst[4], ost[4];
-  float lst = 0.f, dst_ = 0.f;
+  uint32_t lst = 0u, dst_ = 0u;
   const int nsteps = nh * nq;
 
   auto load_step = [&](int st) {
@@ -172,21 +178,18 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdParams p) {
     const int h = h0 + hi;
     const int qb = queue[it] & 0x7fffffff;
     const size_t base = (size_t)(b * p.Hq + h) * N;
+    const rsrc_t qrs = make_rsrc(p.q + base * D, head_bytes);
+    const rsrc_t ors = make_rsrc(p.dout + base * D, head_bytes);
+    const uint32_t off = (uint32_t)(qb * BQ + cp_row) * (D * 2) + cp_ch * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = qb * BQ + cp_row + 16 * i;
-      if (row < N) {
-        qst[i] = *reinterpret_cast<const u32x4*>(p.q + (base + row) * D + cp_ch);
-        ost[i] = *reinterpret_cast<const u32x4*>(p.dout + (base + row) * D + cp_ch);
-      } else {
-        qst[i] = u32x4{0, 0, 0, 0};
-        ost[i] = u32x4{0, 0, 0, 0};
-      }
+      qst[i] = buf_load16(qrs, off, i * 16 * D * 2);
+      ost[i] = buf_load16(ors, off, i * 16 * D * 2);
     }
     if (tid < BQ) {
-      const int row = qb * BQ + tid;
-      lst = row < N ? p.lse2[base + row] : INFINITY;
-      dst_ = row < N ? p.delta[base + row] : 0.f;
+      const uint32_t ro = (uint32_t)(qb * BQ + tid) * 4;
+      lst = buf_load4(make_rsrc(p.lse2 + base, (uint32_t)N * 4), ro, 0);
+      dst_ = buf_load4(make_rsrc(p.delta + base, (uint32_t)N * 4), ro, 0);
     }
   };
   auto store_step = [&](int buf) {
@@ -196,8 +199,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdParams p) {
       *reinterpret_cast<u32x4*>(&sm.dO[buf][(cp_row + 16 * i) * QS + cp_ch]) = ost[i];
     }
     if (tid < BQ) {
-      sm.lse2[buf][tid] = lst;
-      sm.dl[buf][tid] = dst_;
+      sm.lse2[buf][tid] = __uint_as_float(lst);
+      sm.dl[buf][tid] = __uint_as_float(dst_);
     }
   };
 
@@ -208,6 +211,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdParams p) {
   const int arow = perm_rows(l32);
   const int tr_row = (lane & 15) >> 2;
   const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  // lane part of the dQ accumulator offset: column wave*32 + l32 of row hh*4
+  const uint32_t dq_lane = (uint32_t)((hh * 4) * D + wave * 32 + l32) * 4;
 
   for (int st = 0; st < nsteps; ++st) {
     const int cur = st & 1;
@@ -215,63 +220,72 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdParams p) {
     const int h = h0 + hi;
     const int e = queue[it];
     const int qb = e & 0x7fffffff;
-    const bool partial = (e < 0) || ragged_k || (ragged_q_any && qb == p.nQB - 1);
+    const bool partial = (e < 0) || ragged_k;
     const bool has_next = st + 1 < nsteps;
     if (has_next) load_step(st + 1);
 
     // ---- S = Q K^T and dP = dO V^T (rows q, columns = this wave's keys) ----
     f32x16 sacc[2], pacc[2];
-#pragma unroll
-    for (int qblk = 0; qblk < 2; ++qblk) {
-      sacc[qblk] = f32x16{};
-      pacc[qblk] = f32x16{};
-      const bf16* qp = &sm.q[cur][(qblk * 32 + arow) * QS + hh * 8];
-      const bf16* op = &sm.dO[cur][(qblk * 32 + arow) * QS + hh * 8];
+    {
+      const bf16* kp = &sm.k[(wave * 32 + l32) * KS + hh * 8];
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        sacc[qblk] = mfma32(*reinterpret_cast<const bf16x8*>(qp + s * 16), kr[s], sacc[qblk]);
-        pacc[qblk] = mfma32(*reinterpret_cast<const bf16x8*>(op + s * 16), vr[s], pacc[qblk]);
+        const bf16x8 kb8 = *reinterpret_cast<const bf16x8*>(kp + s * 16);
+#pragma unroll
+        for (int qblk = 0; qblk < 2; ++qblk) {
+          const bf16* qp = &sm.q[cur][(qblk * 32 + arow) * QS + hh * 8 + s * 16];
+          const bf16* op = &sm.dO[cur][(qblk * 32 + arow) * QS + hh * 8 + s * 16];
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qp);
+          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(op);
+          sacc[qblk] = mfma32(qa, kb8, s == 0 ? f32x16{} : sacc[qblk]);
+          pacc[qblk] = mfma32(oa, vr[s], s == 0 ? f32x16{} : pacc[qblk]);
+        }
       }
     }
 
     // ---- P = exp2(S c - LSE2), masked on partial tiles; dS = P (dP - D) ----
     bf16x8 pa[4], sa[4];
+    auto softmax_grad = [&](auto masked) {
+      constexpr bool kMasked = decltype(masked)::value;
 #pragma unroll
-    for (int qblk = 0; qblk < 2; ++qblk) {
-      uint32_t word = 0u;
-      if (partial)
-        word = key_ok ? hidden_rows32(mv[0], mv[1], mv[2], mv[3], qb * BQ + qblk * 32)
-                      : 0xFFFFFFFFu;
+      for (int qblk = 0; qblk < 2; ++qblk) {
+        uint32_t word = 0u;
+        if (kMasked)
+          word = key_ok ? hidden_rows32(mv[0], mv[1], mv[2], mv[3], qb * BQ + qblk * 32)
+                        : 0xFFFFFFFFu;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int q0 = qblk * 32 + j * 16 + hh * 8;
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][q0]);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][q0 + 4]);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sm.dl[cur][q0]);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sm.dl[cur][q0 + 4]);
-        u32x4 pw, sw;
+        for (int j = 0; j < 2; ++j) {
+          const int q0 = qblk * 32 + j * 16 + hh * 8;
+          const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][q0]);
+          const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][q0 + 4]);
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sm.dl[cur][q0]);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sm.dl[cur][q0 + 4]);
+          u32x4 pw, sw;
 #pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-          float pv[2], sv[2];
+          for (int t = 0; t < 8; t += 2) {
+            float pv[2], sv[2];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int tt = t + u;
-            const float l = tt < 4 ? l0[tt] : l1[tt - 4];
-            const float dd = tt < 4 ? d0[tt] : d1[tt - 4];
-            float pp = __builtin_amdgcn_exp2f(fmaf(sacc[qblk][j * 8 + tt], p.c, -l));
-            if (partial && ((word >> (j * 16 + hh * 8 + tt)) & 1u)) pp = 0.f;
-            pv[u] = pp;
-            sv[u] = pp * (pacc[qblk][j * 8 + tt] - dd);
+            for (int u = 0; u < 2; ++u) {
+              const int tt = t + u;
+              const float l = tt < 4 ? l0[tt] : l1[tt - 4];
+              const float dd = tt < 4 ? d0[tt] : d1[tt - 4];
+              float pp = __builtin_amdgcn_exp2f(fmaf(sacc[qblk][j * 8 + tt], p.c, -l));
+              if (kMasked) pp = mask_zero(pp, word, (uint32_t)(j * 16 + hh * 8 + tt));
+              pv[u] = pp;
+              sv[u] = pp * (pacc[qblk][j * 8 + tt] - dd);
+            }
+            pw[t / 2] = pack_bf16x2(pv[0], pv[1]);
+            sw[t / 2] = pack_bf16x2(sv[0], sv[1]);
           }
-          pw[t / 2] = pack_bf16x2(pv[0], pv[1]);
-          sw[t / 2] = pack_bf16x2(sv[0], sv[1]);
+          pa[qblk * 2 + j] = __builtin_bit_cast(bf16x8, pw);
+          sa[qblk * 2 + j] = __builtin_bit_cast(bf16x8, sw);
+          // dS^T to LDS for the dQ product: row = this lane's key, 8 consecutive q
+          *reinterpret_cast<u32x4*>(&sm.dst[(wave * 32 + l32) * SS + q0]) = sw;
         }
-        pa[qblk * 2 + j] = __builtin_bit_cast(bf16x8, pw);
-        sa[qblk * 2 + j] = __builtin_bit_cast(bf16x8, sw);
-        // dS^T to LDS for the dQ product: row = this lane's key, 8 consecutive q
-        *reinterpret_cast<u32x4*>(&sm.dst[(wave * 32 + l32) * SS + q0]) = sw;
       }
-    }
+    };
+    if (partial) softmax_grad(std::true_type{});
+    else softmax_grad(std::false_type{});
 
     // ---- dV += P^T dO, dK += dS^T Q  (B operands through transposing reads) ----
 #pragma unroll
@@ -291,7 +305,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdParams p) {
 
     // ---- dQ (64 x 128) += dS K over this workgroup's 128 keys; wave w: d-block w ----
     {
-      f32x16 qacc[2] = {f32x16{}, f32x16{}};
+      f32x16 qacc[2];
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const int r0 = ks * 16 + hh * 8 + tr_row;
@@ -301,35 +315,32 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdParams p) {
         for (int qblk = 0; qblk < 2; ++qblk) {
           const bf16* sp = &sm.dst[r0 * SS + qblk * 32 + tr_col];
           const bf16x8 as = join_tr(lds_read_tr16(sp), lds_read_tr16(sp + 4 * SS));
-          qacc[qblk] = mfma32(as, bk, qacc[qblk]);
+          qacc[qblk] = mfma32(as, bk, ks == 0 ? f32x16{} : qacc[qblk]);
         }
       }
-      float* dqg = p.dq_acc + (size_t)(b * p.Hq + h) * N * D;
+      const rsrc_t dqr = make_rsrc(p.dq_acc + (size_t)(b * p.Hq + h) * N * D, acc_bytes);
+      const uint32_t sbase = (uint32_t)(qb * BQ) * (D * 4);
 #pragma unroll
-      for (int qblk = 0; qblk < 2; ++qblk) {
+      for (int qblk = 0; qblk < 2; ++qblk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = qb * BQ + qblk * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-          if (row < N)
-            atomicAdd(dqg + (size_t)row * D + wave * 32 + l32, qacc[qblk][i]);
-        }
-      }
+        for (int i = 0; i < 16; ++i)
+          buf_atomic_add(qacc[qblk][i], dqr, dq_lane,
+                         sbase + (uint32_t)((qblk * 32 + (i >> 2) * 8 + (i & 3)) * D * 4));
     }
     __syncthreads();  // dS^T and the current Q/dO buffer are free again
   }
 
-  // ---- dK, dV of this workgroup's keys into the fp32 accumulators ----
-  float* dkg = p.dk_acc + (size_t)(b * p.Hkv + kvh) * N * D;
-  float* dvg = p.dv_acc + (size_t)(b * p.Hkv + kvh) * N * D;
+  // ---- dK, dV of this workgroup's keys into the fp32 accumulators (keys past N dropped)
+  const rsrc_t dkr = make_rsrc(p.dk_acc + kvbase, acc_bytes);
+  const rsrc_t dvr = make_rsrc(p.dv_acc + kvbase, acc_bytes);
+  const uint32_t kl = (uint32_t)((kb * BK + wave * 32 + hh * 4) * D + l32) * 4;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int kk = kb * BK + wave * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-      if (kk < N) {
-        atomicAdd(dkg + (size_t)kk * D + d * 32 + l32, dk[d][i]);
-        atomicAdd(dvg + (size_t)kk * D + d * 32 + l32, dv[d][i]);
-      }
+      const uint32_t so = (uint32_t)(((i >> 2) * 8 + (i & 3)) * D + d * 32) * 4;
+      buf_atomic_add(dk[d][i], dkr, kl, so);
+      buf_atomic_add(dv[d][i], dvr, kl, so);
     }
   }
 }

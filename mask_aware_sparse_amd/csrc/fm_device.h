@@ -93,6 +93,42 @@ __device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// ---------------------------------------------------------------------------
+// Buffer resources (raw, stride 0): loads past `bytes` return 0, stores and atomics
+// past it are dropped, so ragged tails need no per-element branches.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_store8(u32x2 v, rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_store4(uint32_t v, rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_atomic_add(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, voff, soff, 0);
+}
+
+// s if bit `bit` of `word` is clear, -inf if it is set.
+__device__ __forceinline__ float mask_neg_inf(float s, uint32_t word, uint32_t bit) {
+  return ((word >> bit) & 1u) ? -INFINITY : s;
+}
+// p if bit `bit` of `word` is clear, 0 if it is set.
+__device__ __forceinline__ float mask_zero(float p, uint32_t word, uint32_t bit) {
+  return ((word >> bit) & 1u) ? 0.f : p;
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

@@ -29,7 +29,7 @@ constexpr int D = kHeadDim;     // 128
 constexpr int KS = D + 8;       // K row stride in LDS (elements)
 constexpr int VS = D + 16;      // V row stride in LDS (elements)
 
-struct FwdSmem {
+struct __attribute__((aligned(16))) FwdSmem {
   bf16 k[2][BK * KS];
   bf16 v[2][BK * VS];
   uint32_t mw[2][4][BK];  // hidden-row words: [buffer][wave][key]
@@ -41,6 +41,11 @@ struct FwdSmem {
 __device__ __forceinline__ int perm_rows(int a) {
   return (a & 0x13) | ((a & 4) << 1) | ((a & 8) >> 1);
 }
+
+// Lazy rescaling: the exponent offset of a row only moves when the row max exceeds
+// it by more than this many powers of two (p then stays below 2^8, exact in bf16
+// range), so most tiles skip the accumulator rescale.
+constexpr float kRescaleSlack = 8.0f;
 
 struct FwdParams {
   const bf16* __restrict__ q;
@@ -67,53 +72,51 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   const int kvh = h / (p.Hq / p.Hkv);
   const int n_tiles = p.q_count[2 * item] + p.q_count[2 * item + 1];
   const int32_t* queue = p.q_queue + (size_t)item * p.nKB;
-  const bf16* qg = p.q + (size_t)(b * p.Hq + h) * p.N * D;
-  const bf16* kg = p.k + (size_t)(b * p.Hkv + kvh) * p.N * D;
-  const bf16* vg = p.v + (size_t)(b * p.Hkv + kvh) * p.N * D;
-  const size_t mrow = (size_t)b * p.N;
   const int N = p.N;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const rsrc_t qr_ = make_rsrc(p.q + (size_t)(b * p.Hq + h) * N * D, head_bytes);
+  const rsrc_t kr_ = make_rsrc(p.k + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
+  const rsrc_t vr_ = make_rsrc(p.v + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
+  const uint32_t vec_bytes = (uint32_t)N * 4;
+  const size_t mrow = (size_t)b * N;
+  const rsrc_t m0 = make_rsrc(p.m.lts + mrow, vec_bytes), m1 = make_rsrc(p.m.lte + mrow, vec_bytes);
+  const rsrc_t m2 = make_rsrc(p.m.uts + mrow, vec_bytes), m3 = make_rsrc(p.m.ute + mrow, vec_bytes);
   const bool ragged = (N % BK) != 0;
 
   const int row = qb * BQ + wave * 32 + l32;
-  const bool row_ok = row < N;
 
-  // Q^T operand: lane holds Q[row][s*16 + hh*8 .. +7] for s = 0..7
+  // Q^T operand: lane holds Q[row][s*16 + hh*8 .. +7] for s = 0..7 (rows past N read 0)
   bf16x8 qr[8];
+  {
+    const uint32_t off = (uint32_t)row * (D * 2) + hh * 16;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    if (row_ok) qr[s] = *reinterpret_cast<const bf16x8*>(qg + (size_t)row * D + s * 16 + hh * 8);
-    else qr[s] = bf16x8{};
+    for (int s = 0; s < 8; ++s) qr[s] = __builtin_bit_cast(bf16x8, buf_load16(qr_, off, s * 32));
   }
 
   f32x16 oacc[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) oacc[d] = f32x16{};
-  float m_run = -INFINITY, lf = 0.f, lb = 0.f;
+  float m_use = -INFINITY, lf = 0.f, lb = 0.f;
 
   // staging for the tile copy: thread copies rows (tid>>4)+16i, 16-byte chunk tid&15
   const int cp_row = tid >> 4, cp_ch = (tid & 15) * 8;
   const int mk_key = tid & 63, mk_wave = tid >> 6;
   u32x4 kst[4], vst[4];
-  int vec[4];
+  uint32_t vec[4];
 
   auto load_tile = [&](int e) {
     const int kb = e & 0x7fffffff;
+    const uint32_t base = (uint32_t)(kb * BK + cp_row) * (D * 2) + cp_ch * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = kb * BK + cp_row + 16 * i;
-      if (key < N) {
-        kst[i] = *reinterpret_cast<const u32x4*>(kg + (size_t)key * D + cp_ch);
-        vst[i] = *reinterpret_cast<const u32x4*>(vg + (size_t)key * D + cp_ch);
-      } else {
-        kst[i] = u32x4{0, 0, 0, 0};
-        vst[i] = u32x4{0, 0, 0, 0};
-      }
+      kst[i] = buf_load16(kr_, base, i * 16 * D * 2);
+      vst[i] = buf_load16(vr_, base, i * 16 * D * 2);
     }
     const bool part = (e < 0) || (ragged && kb == p.nKB - 1);
-    const int key = kb * BK + mk_key;
-    if (part && key < N) {
-      vec[0] = p.m.lts[mrow + key]; vec[1] = p.m.lte[mrow + key];
-      vec[2] = p.m.uts[mrow + key]; vec[3] = p.m.ute[mrow + key];
+    if (part) {
+      const uint32_t vo = (uint32_t)(kb * BK + mk_key) * 4;
+      vec[0] = buf_load4(m0, vo, 0); vec[1] = buf_load4(m1, vo, 0);
+      vec[2] = buf_load4(m2, vo, 0); vec[3] = buf_load4(m3, vo, 0);
     }
   };
   auto store_tile = [&](int e, int buf) {
@@ -127,8 +130,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     if (part) {
       const int key = kb * BK + mk_key;
       const int r0 = qb * BQ + mk_wave * 32;
-      sm.mw[buf][mk_wave][mk_key] =
-          key < N ? hidden_rows32(vec[0], vec[1], vec[2], vec[3], r0) : 0xFFFFFFFFu;
+      const uint32_t w = hidden_rows32((int)vec[0], (int)vec[1], (int)vec[2], (int)vec[3], r0);
+      sm.mw[buf][mk_wave][mk_key] = key < N ? w : 0xFFFFFFFFu;
     }
   };
 
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
 
   const int arow = perm_rows(l32);
   // transposing-read coordinates for the V^T operand
-  const int tr_row = (lane & 15) >> 2;                  // + key base
+  const int tr_row = (lane & 15) >> 2;                         // + key base
   const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);  // + d-block base
 
   for (int it = 0; it < n_tiles; ++it) {
@@ -159,12 +162,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     f32x16 sacc[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      sacc[blk] = f32x16{};
       const bf16* kp = &sm.k[cur][(blk * 32 + arow) * KS + hh * 8];
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + s * 16);
-        sacc[blk] = mfma32(a, qr[s], sacc[blk]);
+        sacc[blk] = mfma32(a, qr[s], s == 0 ? f32x16{} : sacc[blk]);
       }
     }
 
@@ -178,25 +180,34 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
           const u32x4 w0 = *reinterpret_cast<const u32x4*>(mw + blk * 32 + j * 16 + hh * 8);
           const u32x4 w1 = *reinterpret_cast<const u32x4*>(mw + blk * 32 + j * 16 + hh * 8 + 4);
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const uint32_t w = t < 4 ? w0[t] : w1[t - 4];
-            if ((w >> l32) & 1u) sacc[blk][j * 8 + t] = -INFINITY;
-          }
+          for (int t = 0; t < 8; ++t)
+            sacc[blk][j * 8 + t] = mask_neg_inf(sacc[blk][j * 8 + t], t < 4 ? w0[t] : w1[t - 4],
+                                                (uint32_t)l32);
         }
       }
     }
 
-    // ---- online softmax ----
+    // ---- online softmax (base 2, lazily rescaled) ----
     float mx = -INFINITY;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
-    mx = max_with_partner32(mx);
-    const float m_new = fmaxf(m_run, mx * p.c);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    mx = max_with_partner32(mx) * p.c;
+    const bool need = mx > m_use + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float m_new = need ? mx : m_use;
+      // 0 when m_use = -inf; lanes that keep their offset keep their sums
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_use - m_new) : 1.0f;
+      lf *= alpha;
+      lb *= alpha;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+      m_use = m_new;
+    }
+    const float m_off = (m_use == -INFINITY) ? 0.f : m_use;
 
     bf16x8 pb[4];
     float psum = 0.f, pbsum = 0.f;
@@ -207,8 +218,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
         u32x4 packed;
 #pragma unroll
         for (int t = 0; t < 8; t += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[blk][j * 8 + t], p.c, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[blk][j * 8 + t + 1], p.c, -m_use));
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[blk][j * 8 + t], p.c, -m_off));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[blk][j * 8 + t + 1], p.c, -m_off));
           psum += p0 + p1;
           const unsigned u = pack_bf16x2(p0, p1);
           packed[t / 2] = u;
@@ -218,12 +229,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
         pb[blk * 2 + j] = __builtin_bit_cast(bf16x8, packed);
       }
     }
-    lf = lf * alpha + psum;
-    lb = lb * alpha + pbsum;
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+    lf += psum;
+    lb += pbsum;
 
     // ---- O^T += V^T P^T ----
     const bf16* vb = sm.v[cur];
@@ -245,22 +252,23 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   // ---- epilogue: O = acc / l_b, LSE = ln2 * (m + log2 l_f) ----
   lf = sum_with_partner32(lf);
   lb = sum_with_partner32(lb);
-  if (row_ok) {
-    const float inv = lb > 0.f ? 1.0f / lb : 0.f;
-    bf16* og = p.o + (size_t)(b * p.Hq + h) * N * D + (size_t)row * D;
+  const float inv = lb > 0.f ? 1.0f / lb : 0.f;
+  const rsrc_t orr = make_rsrc(p.o + (size_t)(b * p.Hq + h) * N * D, head_bytes);
+  const uint32_t ooff = (uint32_t)row * (D * 2) + hh * 8;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+  for (int d = 0; d < 4; ++d) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w[0] = pack_bf16x2(oacc[d][g * 4 + 0] * inv, oacc[d][g * 4 + 1] * inv);
-        w[1] = pack_bf16x2(oacc[d][g * 4 + 2] * inv, oacc[d][g * 4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(og + d * 32 + g * 8 + hh * 4) = w;
-      }
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = pack_bf16x2(oacc[d][g * 4 + 0] * inv, oacc[d][g * 4 + 1] * inv);
+      w[1] = pack_bf16x2(oacc[d][g * 4 + 2] * inv, oacc[d][g * 4 + 3] * inv);
+      buf_store8(w, orr, ooff, (d * 32 + g * 8) * 2);
     }
-    if (hh == 0)
-      p.lse[(size_t)(b * p.Hq + h) * N + row] =
-          lf > 0.f ? (m_run + __builtin_amdgcn_logf(lf)) * kLn2 : -INFINITY;
+  }
+  if (hh == 0) {
+    const rsrc_t lr = make_rsrc(p.lse + (size_t)(b * p.Hq + h) * N, (uint32_t)N * 4);
+    const float l = lf > 0.f ? (m_use + __builtin_amdgcn_logf(lf)) * kLn2 : -INFINITY;
+    buf_store4(__float_as_uint(l), lr, (uint32_t)row * 4, 0);
   }
 }
 
