@@ -115,7 +115,7 @@ def main():
     A = attended_pairs(w)
     d = w.head_dim
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)]
           for _ in range(args.steps)]
 
     def step(e=None):
@@ -124,7 +124,7 @@ def main():
         fm.attn_fwd(q, k, v, *vec, ws=ws_f, out=o, lse=lse,
                     events=None if e is None else (e[1], e[2]))
         fm.attn_bwd(q, k, v, o, lse, do, *vec, ws=ws_b, grads=grads,
-                    events=None if e is None else (e[3], e[4]))
+                    events=None if e is None else (e[3], e[4], e[6], e[7]))
         if e is not None:
             e[5].record()
 
@@ -139,12 +139,20 @@ def main():
 
     step_ms = np.array([e[0].elapsed_time(e[5]) for e in ev])
     fwd_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    bwd_ms = np.array([e[3].elapsed_time(e[4]) for e in ev])
+    dkdv_ms = np.array([e[3].elapsed_time(e[4]) for e in ev])
+    dq_ms = np.array([e[6].elapsed_time(e[7]) for e in ev])
     ms = wall * 1e3 / args.steps
     value = 14 * d * A / (ms * 1e-3) / 1e12
-    bwd_flop = 10 * d * A
-    bwd_tflops = bwd_flop / (bwd_ms.mean() * 1e-3) / 1e12
-    fwd_tflops = 4 * d * A / (fwd_ms.mean() * 1e-3) / 1e12
+    # algorithmic flop per attended pair of each attention kernel: forward 4d (QK, PV);
+    # dK/dV kernel 8d (S and dP recomputed once for the backward, dV, dK); dQ kernel 2d
+    # (its second recomputation of S and dP is not algorithmic work)
+    kernels = {
+        "k_attn_fwd": (float(fwd_ms.mean()), 4 * d * A),
+        "k_attn_bwd_dkdv": (float(dkdv_ms.mean()), 8 * d * A),
+        "k_attn_bwd_dq": (float(dq_ms.mean()), 2 * d * A),
+    }
+    tflops = {kname: f / (t * 1e-3) / 1e12 for kname, (t, f) in kernels.items()}
+    dom = max(kernels, key=lambda kname: kernels[kname][0])
 
     cpu = None
     if args.cpu_budget > 0:
@@ -167,14 +175,12 @@ def main():
                    "heads_kv": w.heads_kv, "seq_len": w.seqlen, "head_dim": d,
                    "attended_pairs": A, "seed": args.seed},
         "pct_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
-        "fwd": {"kernel_ms": round(float(fwd_ms.mean()), 4),
-                "kernel_tflops": round(fwd_tflops, 2)},
-        "bwd": {"kernel_ms": round(float(bwd_ms.mean()), 4),
-                "kernel_tflops": round(bwd_tflops, 2)},
+        "kernels": {kname: {"ms": round(t, 4), "algorithmic_tflops": round(tflops[kname], 2)}
+                    for kname, (t, _) in kernels.items()},
         "event_ms_per_step": round(float(step_ms.mean()), 4),
-        "roofline": {"kernel": "k_attn_bwd", "bound": "mfma",
-                     "achieved": round(bwd_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(bwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": {"kernel": dom, "bound": "mfma",
+                     "achieved": round(tflops[dom], 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops[dom] / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None},
         "cpu_baseline": cpu,
     }

@@ -103,14 +103,17 @@ typedef struct {
   int32_t* k_order;
 } fm_tiles;
 
-/* Optional timing hook for fm_attn_fwd / fm_attn_bwd.  start and stop are hipEvent_t
- * handles created by the caller (hipEventCreate, timing enabled); the call records start
- * immediately before and stop immediately after the launch of its main attention kernel
- * on `stream`, so hipEventElapsedTime(start, stop) is that kernel's duration.  Pass NULL
- * for no timing.  The library keeps no reference after the call returns. */
+/* Optional timing hook for fm_attn_fwd / fm_attn_bwd.  Each member is a hipEvent_t
+ * created by the caller (hipEventCreate, timing enabled) or NULL.  fm_attn_fwd records
+ * `start` immediately before and `stop` immediately after the launch of its attention
+ * kernel; fm_attn_bwd records (start, stop) around its dK/dV kernel and (start2, stop2)
+ * around its dQ kernel, so hipEventElapsedTime gives each kernel's duration on `stream`.
+ * Pass NULL for no timing.  The library keeps no reference after the call returns. */
 typedef struct {
   void* start;
   void* stop;
+  void* start2;
+  void* stop2;
 } fm_kernel_events;
 
 /* Workspace bytes an entry point needs for this problem.  For FM_OP_CLASSIFY the tile
@@ -142,9 +145,11 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
                       void* stream, const fm_kernel_events* events);
 
 /* Backward: dQ, dK, dV (bf16) from Q, K, V, the forward's O and LSE, and dO.  Classifies
- * internally, computes D = rowsum(dO * O) in fp32, runs the KV-block-outer kernel that
- * recomputes P = exp(S - LSE) on queued tiles only (LPT order over KV blocks), and
- * converts the fp32 accumulators held in `ws` to bf16.  Any N >= 0. */
+ * internally at both tile shapes (fm_tile_shape(FM_OP_BWD) for dK/dV, FM_OP_FWD for dQ),
+ * computes D = rowsum(dO * O) in fp32, then runs two kernels that recompute
+ * P = exp(S - LSE) on queued tiles only: a KV-block-outer one accumulating dK and dV
+ * (LPT order over KV blocks; fp32 accumulators in `ws`, converted to bf16 at the end) and
+ * a Q-block-outer one accumulating dQ in registers (the forward's LPT order).  Any N >= 0. */
 fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dout, const fm_mask* m,
                       void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream,

@@ -54,7 +54,8 @@ class Mask(ctypes.Structure):
 
 
 class KernelEvents(ctypes.Structure):
-    _fields_ = [("start", ctypes.c_void_p), ("stop", ctypes.c_void_p)]
+    _fields_ = [("start", ctypes.c_void_p), ("stop", ctypes.c_void_p),
+                ("start2", ctypes.c_void_p), ("stop2", ctypes.c_void_p)]
 
 
 class Tiles(ctypes.Structure):
@@ -197,13 +198,17 @@ def _bf16(*ts):
 
 
 def _events(ev):
-    """(start, stop) torch.cuda.Event pair -> fm_kernel_events pointer (or None)."""
+    """Up to four torch.cuda.Event objects (start, stop[, start2, stop2]) ->
+    fm_kernel_events pointer (or None)."""
     if ev is None:
         return None
+    handles = []
     for e in ev:
         if e.cuda_event == 0:          # torch creates the event lazily on first record
             e.record()
-    return ctypes.byref(KernelEvents(ev[0].cuda_event, ev[1].cuda_event))
+        handles.append(e.cuda_event)
+    handles += [0] * (4 - len(handles))
+    return ctypes.byref(KernelEvents(*handles))
 
 
 def attn_fwd(q, k, v, lts, lte, uts, ute, scale=None, ws=None, out=None, lse=None, stream=None,
@@ -226,7 +231,8 @@ def attn_fwd(q, k, v, lts, lte, uts, ute, scale=None, ws=None, out=None, lse=Non
 
 def attn_bwd(q, k, v, o, lse, dout, lts, lte, uts, ute, scale=None, ws=None, grads=None,
              stream=None, events=None):
-    """(dQ, dK, dV) in bf16 via fm_attn_bwd.  `events` as in attn_fwd."""
+    """(dQ, dK, dV) in bf16 via fm_attn_bwd.  `events`: optional (start, stop, start2,
+    stop2) torch.cuda.Event objects timing the dK/dV kernel and the dQ kernel."""
     _bf16(q, k, v, o, dout)
     B, Hq, Hkv, N, d = _shapes(q, k)
     if grads is None:

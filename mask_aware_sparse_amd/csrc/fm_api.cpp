@@ -25,7 +25,7 @@ fm_status check_problem(const fm_problem* p) {
   if (p->heads_q % p->heads_kv != 0) return FM_ERR_INVALID_ARG;
   if (!(p->softmax_scale <= 0.f || std::isfinite(p->softmax_scale))) return FM_ERR_INVALID_ARG;
   if (p->head_dim != fm::kHeadDim) return FM_ERR_UNSUPPORTED;
-  if (p->seqlen >= (1 << 30)) return FM_ERR_UNSUPPORTED;
+  if (p->seqlen > (1 << 22)) return FM_ERR_UNSUPPORTED;  // per-head buffers < 2 GiB
   return FM_OK;
 }
 
@@ -82,19 +82,27 @@ FwdWs fwd_ws(const fm_problem* p, const Blocks& nb) {
   return w;
 }
 
-struct BwdWs { size_t mm, k_queue, k_count, k_cost, k_order, lse2, delta, dq, dk, dv, total; };
-BwdWs bwd_ws(const fm_problem* p, const Blocks& nb) {
+struct BwdWs {
+  size_t mm_k, k_queue, k_count, k_cost, k_order;   // dK/dV tiles
+  size_t mm_q, q_queue, q_count, q_cost, q_order;   // dQ (forward) tiles
+  size_t lse2, delta, dk, dv, total;
+};
+BwdWs bwd_ws(const fm_problem* p, const Blocks& nk, const Blocks& nq) {
   BwdWs w{};
   const size_t B = p->batch, rq = B * p->heads_q * p->seqlen, rk = B * p->heads_kv * p->seqlen;
   size_t off = 0;
-  w.mm = off; off += align_up(B * nb.nKB * 8 * 4);
-  w.k_queue = off; off += align_up(B * nb.nKB * nb.nQB * 4);
-  w.k_count = off; off += align_up(B * nb.nKB * 2 * 4);
-  w.k_cost = off; off += align_up(B * nb.nKB * 4);
-  w.k_order = off; off += align_up(B * nb.nKB * 4);
+  w.mm_k = off; off += align_up(B * nk.nKB * 8 * 4);
+  w.k_queue = off; off += align_up(B * nk.nKB * nk.nQB * 4);
+  w.k_count = off; off += align_up(B * nk.nKB * 2 * 4);
+  w.k_cost = off; off += align_up(B * nk.nKB * 4);
+  w.k_order = off; off += align_up(B * nk.nKB * 4);
+  w.mm_q = off; off += align_up(B * nq.nKB * 8 * 4);
+  w.q_queue = off; off += align_up(B * nq.nQB * nq.nKB * 4);
+  w.q_count = off; off += align_up(B * nq.nQB * 2 * 4);
+  w.q_cost = off; off += align_up(B * nq.nQB * 4);
+  w.q_order = off; off += align_up(B * nq.nQB * 4);
   w.lse2 = off; off += align_up(rq * 4);
   w.delta = off; off += align_up(rq * 4);
-  w.dq = off; off += align_up(rq * fm::kHeadDim * 4);
   w.dk = off; off += align_up(rk * fm::kHeadDim * 4);
   w.dv = off; off += align_up(rk * fm::kHeadDim * 4);
   w.total = off;
@@ -176,9 +184,11 @@ fm_status fm_workspace_size(const fm_problem* p, fm_op op, int32_t block_q, int3
       return FM_OK;
     }
     case FM_OP_BWD: {
-      Blocks nb = blocks(p, fm::kBwdBlockQ, fm::kBwdBlockK);
-      if ((st = check_sort_limits(p, nb)) != FM_OK) return st;
-      *bytes = bwd_ws(p, nb).total;
+      Blocks nk = blocks(p, fm::kBwdBlockQ, fm::kBwdBlockK);
+      Blocks nq = blocks(p, fm::kFwdBlockQ, fm::kFwdBlockK);
+      if ((st = check_sort_limits(p, nk)) != FM_OK) return st;
+      if ((st = check_sort_limits(p, nq)) != FM_OK) return st;
+      *bytes = bwd_ws(p, nk, nq).total;
       return FM_OK;
     }
   }
@@ -261,38 +271,59 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   fm_status st = check_problem(p);
   if (st != FM_OK) return st;
   if ((st = check_mask(p, m)) != FM_OK) return st;
-  Blocks nb = blocks(p, fm::kBwdBlockQ, fm::kBwdBlockK);
-  if ((st = check_sort_limits(p, nb)) != FM_OK) return st;
-  if ((st = check_grid(p, blocks(p, fm::kFwdBlockQ, fm::kFwdBlockK), nb)) != FM_OK) return st;
+  Blocks nk = blocks(p, fm::kBwdBlockQ, fm::kBwdBlockK);
+  Blocks nq = blocks(p, fm::kFwdBlockQ, fm::kFwdBlockK);
+  if ((st = check_sort_limits(p, nk)) != FM_OK) return st;
+  if ((st = check_sort_limits(p, nq)) != FM_OK) return st;
+  if ((st = check_grid(p, nq, nk)) != FM_OK) return st;
   if (empty_problem(p)) return FM_OK;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FM_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return FM_ERR_INVALID_ARG;
-  BwdWs w = bwd_ws(p, nb);
+  BwdWs w = bwd_ws(p, nk, nq);
   if ((st = check_ws(ws, ws_bytes, w.total)) != FM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  fm::TileOut t{};
-  t.minmax = at<int32_t>(ws, w.mm);
-  t.k_queue = at<int32_t>(ws, w.k_queue);
-  t.k_count = at<int32_t>(ws, w.k_count);
-  t.k_cost = at<int32_t>(ws, w.k_cost);
+  fm::TileOut tk{};
+  tk.minmax = at<int32_t>(ws, w.mm_k);
+  tk.k_queue = at<int32_t>(ws, w.k_queue);
+  tk.k_count = at<int32_t>(ws, w.k_count);
+  tk.k_cost = at<int32_t>(ws, w.k_cost);
+  fm::TileOut tq{};
+  tq.minmax = at<int32_t>(ws, w.mm_q);
+  tq.q_queue = at<int32_t>(ws, w.q_queue);
+  tq.q_count = at<int32_t>(ws, w.q_count);
+  tq.q_cost = at<int32_t>(ws, w.q_cost);
+  int32_t* k_order = at<int32_t>(ws, w.k_order);
+  int32_t* q_order = at<int32_t>(ws, w.q_order);
   hipError_t e = fm::launch_classify(mask_ptrs(m), p->batch, p->seqlen, fm::kBwdBlockQ,
-                                     fm::kBwdBlockK, t, s);
-  int32_t* order = at<int32_t>(ws, w.k_order);
-  if (e == hipSuccess) e = fm::launch_lpt_sort(t.k_cost, order, (int)(p->batch * nb.nKB), s);
+                                     fm::kBwdBlockK, tk, s);
+  if (e == hipSuccess) e = fm::launch_lpt_sort(tk.k_cost, k_order, (int)(p->batch * nk.nKB), s);
+  if (e == hipSuccess)
+    e = fm::launch_classify(mask_ptrs(m), p->batch, p->seqlen, fm::kFwdBlockQ, fm::kFwdBlockK,
+                            tq, s);
+  if (e == hipSuccess) e = fm::launch_lpt_sort(tq.q_cost, q_order, (int)(p->batch * nq.nQB), s);
   if (e == hipSuccess) {
     fm::BwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout; a.m = mask_ptrs(m);
     a.dq = dq; a.dk = dk; a.dv = dv;
-    a.k_queue = t.k_queue; a.k_count = t.k_count; a.k_order = order;
+    a.k_queue = tk.k_queue; a.k_count = tk.k_count; a.k_order = k_order;
+    a.q_queue = tq.q_queue; a.q_count = tq.q_count; a.q_order = q_order;
     a.lse2 = at<float>(ws, w.lse2); a.delta = at<float>(ws, w.delta);
-    a.dq_acc = at<float>(ws, w.dq); a.dk_acc = at<float>(ws, w.dk); a.dv_acc = at<float>(ws, w.dv);
+    a.dk_acc = at<float>(ws, w.dk); a.dv_acc = at<float>(ws, w.dv);
     a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.N = p->seqlen;
-    a.nQB = (int)nb.nQB; a.nKB = (int)nb.nKB;
+    a.nQB_k = (int)nk.nQB; a.nKB_k = (int)nk.nKB;
+    a.nQB_q = (int)nq.nQB; a.nKB_q = (int)nq.nKB;
     a.scale = scale_of(p);
-    e = fm::launch_bwd(a, s, ev_start(events), ev_stop(events));
+    fm::BwdEvents ev{};
+    if (events) {
+      ev.dkdv_start = static_cast<hipEvent_t>(events->start);
+      ev.dkdv_stop = static_cast<hipEvent_t>(events->stop);
+      ev.dq_start = static_cast<hipEvent_t>(events->start2);
+      ev.dq_stop = static_cast<hipEvent_t>(events->stop2);
+    }
+    e = fm::launch_bwd(a, s, ev);
   }
   return hip_status(e);
 }

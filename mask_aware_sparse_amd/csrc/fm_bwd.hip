@@ -7,18 +7,24 @@
 // (The guide writes dQ and dK without the softmax scale; the chain rule through
 // S = scale Q K^T puts it there.)
 //
-// Kernels:
-//   k_bwd_pre   D = rowsum(dO o O) in fp32, LSE in log2 units (+inf for rows that see
-//               nothing, so that P = 0 there), zeroes the fp32 dQ accumulator.
-//   k_zero      zeroes the fp32 dK/dV accumulators (a fill kernel, not a memset).
-//   k_attn_bwd  one workgroup per (b, kv head, 128-key KV block, chunk of <= 4 query
-//               heads), numbered in LPT order of the KV blocks' tile costs.  K and V of
-//               the block stay in registers (each of the 4 waves owns 32 keys); the
-//               workgroup walks the block's queue of Q-blocks (64 rows each), tiles
-//               tagged partial get the row-interval mask, and dK/dV accumulate in
-//               registers.  dQ partials go to the fp32 accumulator with atomics; dK/dV
-//               are added to theirs once per workgroup.
-//   k_bwd_convert  fp32 accumulators -> bf16 (with the softmax scale on dQ and dK).
+// Work split.  dK/dV sum over query rows and dQ over keys, so no single tile order
+// serves both without a reduction through memory.  Adding dQ partials with fp32
+// atomics from a KV-block-outer kernel is bound by the L2's atomic rate on MI355X, so
+// the two sums run in two kernels that each own their output tile:
+//   k_bwd_pre        D = rowsum(dO o O) (fp32) and LSE in log2 units (+inf for rows that
+//                    see nothing, so P = 0 there).
+//   k_zero           zeroes the fp32 dK/dV accumulators (a fill kernel, not a memset).
+//   k_attn_bwd_dkdv  one workgroup per (b, kv head, 128-key KV block, chunk of <= 4 query
+//                    heads), numbered in LPT order of the KV blocks' tile costs; each of
+//                    the 4 waves owns 32 keys; the workgroup walks the block's queue of
+//                    64-row Q-blocks (partial tiles masked), recomputes S and dP, and keeps
+//                    dK/dV in registers; they are added to the fp32 accumulators once per
+//                    workgroup (several head chunks share a KV head under GQA/MQA).
+//   k_attn_bwd_dq    one workgroup per (b, 128-row Q-block, query head), numbered in the
+//                    forward's LPT order; walks the forward's queue of 64-key blocks,
+//                    recomputes S^T and dP^T, and accumulates dQ^T = K^T dS^T in registers
+//                    (a lane owns one query row, as in the forward); dQ is written once.
+//   k_bwd_convert    fp32 dK/dV accumulators -> bf16 (softmax scale applied to dK).
 #include "fm_device.h"
 #include "fm_internal.h"
 
@@ -27,12 +33,7 @@
 namespace fm {
 namespace {
 
-constexpr int BQ = kBwdBlockQ;  // 64 query rows per step
-constexpr int BK = kBwdBlockK;  // 128 keys per workgroup
 constexpr int D = kHeadDim;
-constexpr int QS = D + 16;      // Q / dO row stride in LDS (288 B: b128 and transposing reads)
-constexpr int KS = D + 16;      // K row stride in LDS (transposing reads)
-constexpr int SS = BQ + 16;     // dS^T row stride in LDS (transposing reads)
 
 // ---- KD: preprocess -----------------------------------------------------------------
 // 16 lanes per row (16 bytes each); a 256-thread block covers 16 rows.
@@ -40,8 +41,7 @@ __global__ __launch_bounds__(256) void k_bwd_pre(const bf16* __restrict__ o,
                                                  const bf16* __restrict__ dout,
                                                  const float* __restrict__ lse,
                                                  float* __restrict__ lse2,
-                                                 float* __restrict__ delta,
-                                                 float* __restrict__ dq_acc, size_t rows) {
+                                                 float* __restrict__ delta, size_t rows) {
   const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int c = (threadIdx.x & 15) * 8;
   float acc = 0.f;
@@ -51,9 +51,6 @@ __global__ __launch_bounds__(256) void k_bwd_pre(const bf16* __restrict__ o,
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       acc += bf16lo_to_f32(a[t]) * bf16lo_to_f32(g[t]) + bf16hi_to_f32(a[t]) * bf16hi_to_f32(g[t]);
-    float4* z = reinterpret_cast<float4*>(dq_acc + row * D + c);
-    z[0] = float4{0.f, 0.f, 0.f, 0.f};
-    z[1] = float4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
@@ -84,21 +81,30 @@ __global__ __launch_bounds__(256) void k_bwd_convert(const float* __restrict__ s
   }
 }
 
-// ---- KE: main backward ------------------------------------------------------------------
-struct __attribute__((aligned(16))) BwdSmem {
-  bf16 q[2][BQ * QS];
-  bf16 dO[2][BQ * QS];
-  bf16 k[BK * KS];
-  bf16 dst[BK * SS];  // dS^T [key][q]
-  float lse2[2][BQ];
-  float dl[2][BQ];
-};
-
+// A-operand row permutation (bits 2 and 3 of the row index swapped): the accumulator
+// rows a lane then owns are runs of 8 consecutive rows of the source, which is the
+// k-ordering the next product wants for its register operand.
 __device__ __forceinline__ int perm_rows(int a) {
   return (a & 0x13) | ((a & 4) << 1) | ((a & 8) >> 1);
 }
 
-struct BwdParams {
+// ---- KE: dK / dV (KV-block outer) -------------------------------------------------------
+namespace dkdv {
+constexpr int BQ = kBwdBlockQ;  // 64 query rows per step
+constexpr int BK = kBwdBlockK;  // 128 keys per workgroup
+constexpr int QS = D + 16;      // Q / dO row stride in LDS (288 B: b128 and transposing reads)
+constexpr int KS = D + 16;      // K row stride in LDS
+
+struct __attribute__((aligned(16))) Smem {
+  bf16 q[2][BQ * QS];
+  bf16 dO[2][BQ * QS];
+  bf16 k[BK * KS];
+  float lse2[2][BQ];
+  float dl[2][BQ];
+};
+}  // namespace dkdv
+
+struct DkdvParams {
   const bf16* __restrict__ q;
   const bf16* __restrict__ k;
   const bf16* __restrict__ v;
@@ -109,15 +115,15 @@ struct BwdParams {
   const int32_t* __restrict__ k_queue;
   const int32_t* __restrict__ k_count;
   const int32_t* __restrict__ k_order;
-  float* __restrict__ dq_acc;
   float* __restrict__ dk_acc;
   float* __restrict__ dv_acc;
   int B, Hq, Hkv, N, nQB, nKB, hc, nch;
   float c;  // scale * log2(e)
 };
 
-__global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdParams p) {
-  __shared__ BwdSmem sm;
+__global__ __launch_bounds__(256, 1) void k_attn_bwd_dkdv(DkdvParams p) {
+  using namespace dkdv;
+  __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
   const int N = p.N;
@@ -137,7 +143,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdParams p) {
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const uint32_t acc_bytes = (uint32_t)N * D * 4;
 
-  // ---- resident K, V (B operands of S = Q K^T and dP = dO V^T), and the lane's key
+  // ---- K of the block into LDS (B operand of S = Q K^T), V resident in registers
   const int key = kb * BK + wave * 32 + l32;
   const size_t kvbase = (size_t)(b * p.Hkv + kvh) * N * D;
   const rsrc_t kr_ = make_rsrc(p.k + kvbase, head_bytes);
@@ -206,18 +212,15 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdParams p) {
 
   load_step(0);
   store_step(0);
-  __syncthreads();
+  lds_barrier();
 
   const int arow = perm_rows(l32);
   const int tr_row = (lane & 15) >> 2;
   const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
-  // lane part of the dQ accumulator offset: column wave*32 + l32 of row hh*4
-  const uint32_t dq_lane = (uint32_t)((hh * 4) * D + wave * 32 + l32) * 4;
 
   for (int st = 0; st < nsteps; ++st) {
     const int cur = st & 1;
-    const int hi = st / nq, it = st - hi * nq;
-    const int h = h0 + hi;
+    const int it = st % nq;
     const int e = queue[it];
     const int qb = e & 0x7fffffff;
     const bool partial = (e < 0) || ragged_k;
@@ -279,8 +282,6 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdParams p) {
           }
           pa[qblk * 2 + j] = __builtin_bit_cast(bf16x8, pw);
           sa[qblk * 2 + j] = __builtin_bit_cast(bf16x8, sw);
-          // dS^T to LDS for the dQ product: row = this lane's key, 8 consecutive q
-          *reinterpret_cast<u32x4*>(&sm.dst[(wave * 32 + l32) * SS + q0]) = sw;
         }
       }
     };
@@ -301,33 +302,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdParams p) {
     }
 
     if (has_next) store_step(cur ^ 1);
-    __syncthreads();  // dS^T complete
-
-    // ---- dQ (64 x 128) += dS K over this workgroup's 128 keys; wave w: d-block w ----
-    {
-      f32x16 qacc[2];
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int r0 = ks * 16 + hh * 8 + tr_row;
-        const bf16* kp = &sm.k[r0 * KS + wave * 32 + tr_col];
-        const bf16x8 bk = join_tr(lds_read_tr16(kp), lds_read_tr16(kp + 4 * KS));
-#pragma unroll
-        for (int qblk = 0; qblk < 2; ++qblk) {
-          const bf16* sp = &sm.dst[r0 * SS + qblk * 32 + tr_col];
-          const bf16x8 as = join_tr(lds_read_tr16(sp), lds_read_tr16(sp + 4 * SS));
-          qacc[qblk] = mfma32(as, bk, ks == 0 ? f32x16{} : qacc[qblk]);
-        }
-      }
-      const rsrc_t dqr = make_rsrc(p.dq_acc + (size_t)(b * p.Hq + h) * N * D, acc_bytes);
-      const uint32_t sbase = (uint32_t)(qb * BQ) * (D * 4);
-#pragma unroll
-      for (int qblk = 0; qblk < 2; ++qblk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          buf_atomic_add(qacc[qblk][i], dqr, dq_lane,
-                         sbase + (uint32_t)((qblk * 32 + (i >> 2) * 8 + (i & 3)) * D * 4));
-    }
-    __syncthreads();  // dS^T and the current Q/dO buffer are free again
+    lds_barrier();  // next buffer complete, current buffer free
   }
 
   // ---- dK, dV of this workgroup's keys into the fp32 accumulators (keys past N dropped)
@@ -345,6 +320,223 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdParams p) {
   }
 }
 
+// ---- KF: dQ (Q-block outer, same tiling and queues as the forward) ----------------------
+namespace dqk {
+constexpr int BQ = kFwdBlockQ;  // 128 query rows: 4 waves x 32
+constexpr int BK = kFwdBlockK;  // 64 keys per tile
+constexpr int KS = D + 16;      // K row stride (b128 row reads and transposing reads)
+constexpr int VS = D + 8;       // V row stride (b128 row reads)
+
+struct __attribute__((aligned(16))) Smem {
+  bf16 k[2][BK * KS];
+  bf16 v[2][BK * VS];
+  uint32_t mw[2][4][BK];  // hidden-row words: [buffer][wave][key]
+};
+}  // namespace dqk
+
+struct DqParams {
+  const bf16* __restrict__ q;
+  const bf16* __restrict__ k;
+  const bf16* __restrict__ v;
+  const bf16* __restrict__ dout;
+  const float* __restrict__ lse2;
+  const float* __restrict__ delta;
+  MaskPtrs m;
+  bf16* __restrict__ dq;
+  const int32_t* __restrict__ q_queue;
+  const int32_t* __restrict__ q_count;
+  const int32_t* __restrict__ q_order;
+  int B, Hq, Hkv, N, nQB, nKB;
+  float c;      // scale * log2(e)
+  float scale;  // softmax scale (applied to dQ)
+};
+
+__global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
+  using namespace dqk;
+  __shared__ Smem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  const int r = blockIdx.x / p.Hq, h = blockIdx.x - r * p.Hq;
+  const int item = p.q_order[r];
+  const int b = item / p.nQB, qb = item - b * p.nQB;
+  const int kvh = h / (p.Hq / p.Hkv);
+  const int n_tiles = p.q_count[2 * item] + p.q_count[2 * item + 1];
+  const int32_t* queue = p.q_queue + (size_t)item * p.nKB;
+  const int N = p.N;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const size_t qbase = (size_t)(b * p.Hq + h) * N;
+  const rsrc_t kr_ = make_rsrc(p.k + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
+  const rsrc_t vr_ = make_rsrc(p.v + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
+  const uint32_t vec_bytes = (uint32_t)N * 4;
+  const size_t mrow = (size_t)b * N;
+  const rsrc_t m0 = make_rsrc(p.m.lts + mrow, vec_bytes), m1 = make_rsrc(p.m.lte + mrow, vec_bytes);
+  const rsrc_t m2 = make_rsrc(p.m.uts + mrow, vec_bytes), m3 = make_rsrc(p.m.ute + mrow, vec_bytes);
+  const bool ragged = (N % BK) != 0;
+
+  const int row = qb * BQ + wave * 32 + l32;
+
+  // Q^T and dO^T operands: lane holds row `row`, d = s*16 + hh*8 .. +7 (rows past N read 0)
+  bf16x8 qr[8], orr[8];
+  {
+    const rsrc_t qrs = make_rsrc(p.q + qbase * D, head_bytes);
+    const rsrc_t ors = make_rsrc(p.dout + qbase * D, head_bytes);
+    const uint32_t off = (uint32_t)row * (D * 2) + hh * 16;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      qr[s] = __builtin_bit_cast(bf16x8, buf_load16(qrs, off, s * 32));
+      orr[s] = __builtin_bit_cast(bf16x8, buf_load16(ors, off, s * 32));
+    }
+  }
+  const float lse_row =
+      __uint_as_float(buf_load4(make_rsrc(p.lse2 + qbase, vec_bytes), (uint32_t)row * 4, 0));
+  const float d_row =
+      __uint_as_float(buf_load4(make_rsrc(p.delta + qbase, vec_bytes), (uint32_t)row * 4, 0));
+
+  f32x16 qacc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) qacc[d] = f32x16{};
+
+  const int cp_row = tid >> 4, cp_ch = (tid & 15) * 8;
+  const int mk_key = tid & 63, mk_wave = tid >> 6;
+  u32x4 kst[4], vst[4];
+  uint32_t vec[4];
+
+  auto load_tile = [&](int e) {
+    const int kb = e & 0x7fffffff;
+    const uint32_t base = (uint32_t)(kb * BK + cp_row) * (D * 2) + cp_ch * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kst[i] = buf_load16(kr_, base, i * 16 * D * 2);
+      vst[i] = buf_load16(vr_, base, i * 16 * D * 2);
+    }
+    const bool part = (e < 0) || (ragged && kb == p.nKB - 1);
+    if (part) {
+      const uint32_t vo = (uint32_t)(kb * BK + mk_key) * 4;
+      vec[0] = buf_load4(m0, vo, 0); vec[1] = buf_load4(m1, vo, 0);
+      vec[2] = buf_load4(m2, vo, 0); vec[3] = buf_load4(m3, vo, 0);
+    }
+  };
+  auto store_tile = [&](int e, int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4*>(&sm.k[buf][(cp_row + 16 * i) * KS + cp_ch]) = kst[i];
+      *reinterpret_cast<u32x4*>(&sm.v[buf][(cp_row + 16 * i) * VS + cp_ch]) = vst[i];
+    }
+    const int kb = e & 0x7fffffff;
+    const bool part = (e < 0) || (ragged && kb == p.nKB - 1);
+    if (part) {
+      const int key = kb * BK + mk_key;
+      const int r0 = qb * BQ + mk_wave * 32;
+      const uint32_t w = hidden_rows32((int)vec[0], (int)vec[1], (int)vec[2], (int)vec[3], r0);
+      sm.mw[buf][mk_wave][mk_key] = key < N ? w : 0xFFFFFFFFu;
+    }
+  };
+
+  if (n_tiles > 0) {
+    load_tile(queue[0]);
+    store_tile(queue[0], 0);
+  }
+  lds_barrier();
+
+  const int arow = perm_rows(l32);
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+
+  for (int it = 0; it < n_tiles; ++it) {
+    const int cur = it & 1;
+    const int e = queue[it];
+    const int kb = e & 0x7fffffff;
+    const bool partial = (e < 0) || (ragged && kb == p.nKB - 1);
+    int en = 0;
+    const bool has_next = it + 1 < n_tiles;
+    if (has_next) {
+      en = queue[it + 1];
+      load_tile(en);
+    }
+
+    // ---- S^T = K Q^T and dP^T = V dO^T (a lane owns one query row) ----
+    f32x16 sacc[2], pacc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const bf16* kp = &sm.k[cur][(blk * 32 + arow) * KS + hh * 8];
+      const bf16* vp = &sm.v[cur][(blk * 32 + arow) * VS + hh * 8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kp + s * 16);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vp + s * 16);
+        sacc[blk] = mfma32(ka, qr[s], s == 0 ? f32x16{} : sacc[blk]);
+        pacc[blk] = mfma32(va, orr[s], s == 0 ? f32x16{} : pacc[blk]);
+      }
+    }
+
+    if (partial) {
+      const uint32_t* mw = sm.mw[cur][wave];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const u32x4 w0 = *reinterpret_cast<const u32x4*>(mw + blk * 32 + j * 16 + hh * 8);
+          const u32x4 w1 = *reinterpret_cast<const u32x4*>(mw + blk * 32 + j * 16 + hh * 8 + 4);
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            sacc[blk][j * 8 + t] = mask_neg_inf(sacc[blk][j * 8 + t], t < 4 ? w0[t] : w1[t - 4],
+                                                (uint32_t)l32);
+        }
+      }
+    }
+
+    // ---- dS^T = P^T o (dP^T - D), P^T = exp2(S^T c - LSE2) ----
+    bf16x8 dsb[4];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        u32x4 packed;
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+          const int i0 = j * 8 + t;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[blk][i0], p.c, -lse_row));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[blk][i0 + 1], p.c, -lse_row));
+          packed[t / 2] =
+              pack_bf16x2(p0 * (pacc[blk][i0] - d_row), p1 * (pacc[blk][i0 + 1] - d_row));
+        }
+        dsb[blk * 2 + j] = __builtin_bit_cast(bf16x8, packed);
+      }
+    }
+
+    // ---- dQ^T += K^T dS^T (K^T through transposing reads) ----
+    const bf16* kt = sm.k[cur];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int key0 = ks * 16 + hh * 8 + tr_row;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const bf16* kp = kt + key0 * KS + d * 32 + tr_col;
+        const bf16x8 a = join_tr(lds_read_tr16(kp), lds_read_tr16(kp + 4 * KS));
+        qacc[d] = mfma32(a, dsb[ks], qacc[d]);
+      }
+    }
+
+    if (has_next) store_tile(en, cur ^ 1);
+    lds_barrier();
+  }
+
+  // ---- dQ = scale * acc (bf16); rows past N are dropped by the buffer bounds ----
+  const rsrc_t dqr = make_rsrc(p.dq + qbase * D, head_bytes);
+  const uint32_t ooff = (uint32_t)row * (D * 2) + hh * 8;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = pack_bf16x2(qacc[d][g * 4 + 0] * p.scale, qacc[d][g * 4 + 1] * p.scale);
+      w[1] = pack_bf16x2(qacc[d][g * 4 + 2] * p.scale, qacc[d][g * 4 + 3] * p.scale);
+      buf_store8(w, dqr, ooff, (d * 32 + g * 8) * 2);
+    }
+  }
+}
+
 unsigned grid_for(size_t n, unsigned cap) {
   size_t g = (n + 255) / 256;
   return (unsigned)(g < cap ? (g ? g : 1) : cap);
@@ -352,19 +544,19 @@ unsigned grid_for(size_t n, unsigned cap) {
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   if (a.B == 0 || a.N == 0 || a.Hq == 0) return hipSuccess;
   const size_t rows_q = (size_t)a.B * a.Hq * a.N;
   const size_t rows_k = (size_t)a.B * a.Hkv * a.N;
   hipLaunchKernelGGL(k_bwd_pre, dim3((unsigned)((rows_q + 15) / 16)), dim3(256), 0, s,
                      static_cast<const bf16*>(a.o), static_cast<const bf16*>(a.dout), a.lse,
-                     a.lse2, a.delta, a.dq_acc, rows_q);
+                     a.lse2, a.delta, rows_q);
   hipLaunchKernelGGL(k_zero, dim3(grid_for(rows_k * D / 4, 8192)), dim3(256), 0, s,
                      reinterpret_cast<float4*>(a.dk_acc), rows_k * D / 4);
   hipLaunchKernelGGL(k_zero, dim3(grid_for(rows_k * D / 4, 8192)), dim3(256), 0, s,
                      reinterpret_cast<float4*>(a.dv_acc), rows_k * D / 4);
 
-  BwdParams p;
+  DkdvParams p;
   p.q = static_cast<const bf16*>(a.q);
   p.k = static_cast<const bf16*>(a.k);
   p.v = static_cast<const bf16*>(a.v);
@@ -375,21 +567,31 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_
   p.k_queue = a.k_queue;
   p.k_count = a.k_count;
   p.k_order = a.k_order;
-  p.dq_acc = a.dq_acc;
   p.dk_acc = a.dk_acc;
   p.dv_acc = a.dv_acc;
-  p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N; p.nQB = a.nQB; p.nKB = a.nKB;
+  p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N; p.nQB = a.nQB_k; p.nKB = a.nKB_k;
   const int g = a.Hq / a.Hkv;
   p.hc = g < kBwdHeadChunk ? g : kBwdHeadChunk;
   p.nch = (g + p.hc - 1) / p.hc;
   p.c = a.scale * kLog2e;
-  const unsigned grid = (unsigned)a.B * (unsigned)a.nKB * (unsigned)a.Hkv * (unsigned)p.nch;
-  if (ev0) (void)hipEventRecord(ev0, s);
-  hipLaunchKernelGGL(k_attn_bwd, dim3(grid), dim3(256), 0, s, p);
-  if (ev1) (void)hipEventRecord(ev1, s);
+  const unsigned grid = (unsigned)a.B * (unsigned)a.nKB_k * (unsigned)a.Hkv * (unsigned)p.nch;
+  if (ev.dkdv_start) (void)hipEventRecord(ev.dkdv_start, s);
+  hipLaunchKernelGGL(k_attn_bwd_dkdv, dim3(grid), dim3(256), 0, s, p);
+  if (ev.dkdv_stop) (void)hipEventRecord(ev.dkdv_stop, s);
 
-  hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_q * D / 8, 16384)), dim3(256), 0, s,
-                     a.dq_acc, static_cast<bf16*>(a.dq), a.scale, rows_q * D / 8);
+  DqParams q;
+  q.q = p.q; q.k = p.k; q.v = p.v; q.dout = p.dout; q.lse2 = a.lse2; q.delta = a.delta;
+  q.m = a.m;
+  q.dq = static_cast<bf16*>(a.dq);
+  q.q_queue = a.q_queue; q.q_count = a.q_count; q.q_order = a.q_order;
+  q.B = a.B; q.Hq = a.Hq; q.Hkv = a.Hkv; q.N = a.N; q.nQB = a.nQB_q; q.nKB = a.nKB_q;
+  q.c = p.c;
+  q.scale = a.scale;
+  const unsigned qgrid = (unsigned)a.B * (unsigned)a.nQB_q * (unsigned)a.Hq;
+  if (ev.dq_start) (void)hipEventRecord(ev.dq_start, s);
+  hipLaunchKernelGGL(k_attn_bwd_dq, dim3(qgrid), dim3(256), 0, s, q);
+  if (ev.dq_stop) (void)hipEventRecord(ev.dq_stop, s);
+
   hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_k * D / 8, 16384)), dim3(256), 0, s,
                      a.dk_acc, static_cast<bf16*>(a.dk), a.scale, rows_k * D / 8);
   hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_k * D / 8, 16384)), dim3(256), 0, s,

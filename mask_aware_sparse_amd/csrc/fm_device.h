@@ -129,6 +129,15 @@ __device__ __forceinline__ float mask_zero(float p, uint32_t word, uint32_t bit)
   return ((word >> bit) & 1u) ? 0.f : p;
 }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations, not for
+// its outstanding global loads, stores or atomics (waves here exchange data through LDS
+// only, so a full __syncthreads would stall every step on in-flight atomics).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     load_tile(queue[0]);
     store_tile(queue[0], 0);
   }
-  __syncthreads();
+  lds_barrier();
 
   const int arow = perm_rows(l32);
   // transposing-read coordinates for the V^T operand
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     }
 
     if (has_next) store_tile(en, cur ^ 1);
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- epilogue: O = acc / l_b, LSE = ln2 * (m + log2 l_f) ----

@@ -75,17 +75,26 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
+  // KV-block-outer tiles (dK/dV kernel): tile kBwdBlockQ x kBwdBlockK
   const int32_t* k_queue;
   const int32_t* k_count;
   const int32_t* k_order;
+  // Q-block-outer tiles (dQ kernel): the forward's tile kFwdBlockQ x kFwdBlockK
+  const int32_t* q_queue;
+  const int32_t* q_count;
+  const int32_t* q_order;
   float* lse2;   // [B][Hq][N] log2-domain LSE (+inf for rows that see nothing)
   float* delta;  // [B][Hq][N] rowsum(dO * O)
-  float* dq_acc; // [B][Hq][N][128] fp32
   float* dk_acc; // [B][Hkv][N][128] fp32
   float* dv_acc; // [B][Hkv][N][128] fp32
-  int B, Hq, Hkv, N, nQB, nKB;
+  int B, Hq, Hkv, N;
+  int nQB_k, nKB_k;  // block counts at the dK/dV tile
+  int nQB_q, nKB_q;  // block counts at the dQ (forward) tile
   float scale;
 };
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+struct BwdEvents {
+  hipEvent_t dkdv_start, dkdv_stop, dq_start, dq_stop;
+};
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev);
 
 }  // namespace fm
