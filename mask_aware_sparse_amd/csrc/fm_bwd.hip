@@ -14,9 +14,9 @@
 //   k_bwd_pre        D = rowsum(dO o O) (fp32) and LSE in log2 units (+inf for rows that
 //                    see nothing, so P = 0 there).
 //   k_zero           zeroes the fp32 dK/dV accumulators (a fill kernel, not a memset).
-//   k_attn_bwd_dkdv  one workgroup per (b, kv head, 128-key KV block, chunk of <= 4 query
+//   k_attn_bwd_dkdv  one workgroup per (b, kv head, 256-key KV block, chunk of <= 4 query
 //                    heads), numbered in LPT order of the KV blocks' tile costs; each of
-//                    the 4 waves owns 32 keys; the workgroup walks the block's queue of
+//                    the 8 waves owns 32 keys; the workgroup walks the block's queue of
 //                    64-row Q-blocks (partial tiles masked), recomputes S and dP, and keeps
 //                    dK/dV in registers; they are added to the fp32 accumulators once per
 //                    workgroup (several head chunks share a KV head under GQA/MQA).
@@ -89,16 +89,22 @@ __device__ __forceinline__ int perm_rows(int a) {
 }
 
 // ---- KE: dK / dV (KV-block outer) -------------------------------------------------------
+// 8 waves x 32 keys = one 256-key block per workgroup; two waves per SIMD so that one
+// wave's softmax VALU work overlaps the other's MFMA work.  Each 64-row Q-block step is
+// processed as two 32-row halves, which keeps the live registers of a wave under 256.
 namespace dkdv {
+constexpr int kWaves = 8;
 constexpr int BQ = kBwdBlockQ;  // 64 query rows per step
-constexpr int BK = kBwdBlockK;  // 128 keys per workgroup
-constexpr int QS = D + 16;      // Q / dO row stride in LDS (288 B: b128 and transposing reads)
-constexpr int KS = D + 16;      // K row stride in LDS
+constexpr int BK = kBwdBlockK;  // 256 keys per workgroup
+constexpr int KS = D + 8;       // K row stride in LDS (272 B: row reads only)
+static_assert(BK == 32 * kWaves, "one 32-key slice per wave");
 
+// Q / dO tiles use the swizzled 320-byte layout (row reads and transposing reads).
 struct __attribute__((aligned(16))) Smem {
-  bf16 q[2][BQ * QS];
-  bf16 dO[2][BQ * QS];
+  bf16 q[2][BQ * kSwzRow];
+  bf16 dO[2][BQ * kSwzRow];
   bf16 k[BK * KS];
+  int4 mv[BK];  // the four row bounds of each key of the block
   float lse2[2][BQ];
   float dl[2][BQ];
 };
@@ -121,7 +127,7 @@ struct DkdvParams {
   float c;  // scale * log2(e)
 };
 
-__global__ __launch_bounds__(256, 1) void k_attn_bwd_dkdv(DkdvParams p) {
+__global__ __launch_bounds__(512, 2) void k_attn_bwd_dkdv(DkdvParams p) {
   using namespace dkdv;
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -146,10 +152,10 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkdv(DkdvParams p) {
   // ---- K of the block into LDS (B operand of S = Q K^T), V resident in registers
   const int key = kb * BK + wave * 32 + l32;
   const size_t kvbase = (size_t)(b * p.Hkv + kvh) * N * D;
-  const rsrc_t kr_ = make_rsrc(p.k + kvbase, head_bytes);
-  const rsrc_t vr_ = make_rsrc(p.v + kvbase, head_bytes);
   bf16x8 vr[8];
   {
+    const rsrc_t kr_ = make_rsrc(p.k + kvbase, head_bytes);
+    const rsrc_t vr_ = make_rsrc(p.v + kvbase, head_bytes);
     const uint32_t off = (uint32_t)key * (D * 2) + hh * 16;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -158,14 +164,13 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkdv(DkdvParams p) {
           buf_load16(kr_, off, s * 32);
     }
   }
-  int mv[4];
-  {
+  if (hh == 0) {
     const uint32_t vb = (uint32_t)N * 4, vo = (uint32_t)key * 4;
     const size_t mrow = (size_t)b * N;
-    mv[0] = (int)buf_load4(make_rsrc(p.m.lts + mrow, vb), vo, 0);
-    mv[1] = (int)buf_load4(make_rsrc(p.m.lte + mrow, vb), vo, 0);
-    mv[2] = (int)buf_load4(make_rsrc(p.m.uts + mrow, vb), vo, 0);
-    mv[3] = (int)buf_load4(make_rsrc(p.m.ute + mrow, vb), vo, 0);
+    sm.mv[wave * 32 + l32] = int4{(int)buf_load4(make_rsrc(p.m.lts + mrow, vb), vo, 0),
+                                  (int)buf_load4(make_rsrc(p.m.lte + mrow, vb), vo, 0),
+                                  (int)buf_load4(make_rsrc(p.m.uts + mrow, vb), vo, 0),
+                                  (int)buf_load4(make_rsrc(p.m.ute + mrow, vb), vo, 0)};
   }
   const bool key_ok = key < N;
 
@@ -173,9 +178,9 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkdv(DkdvParams p) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) { dk[d] = f32x16{}; dv[d] = f32x16{}; }
 
-  // ---- staging of the Q / dO tiles: thread copies rows (tid>>4)+16i, chunk tid&15
-  const int cp_row = tid >> 4, cp_ch = (tid & 15) * 8;
-  u32x4 qst[4], ost[4];
+  // ---- staging of the Q / dO tiles: thread copies rows (tid>>4)+32i, chunk tid&15
+  const int cp_row = tid >> 4, cp_ch = tid & 15;
+  u32x4 qst[2], ost[2];
   uint32_t lst = 0u, dst_ = 0u;
   const int nsteps = nh * nq;
 
@@ -186,11 +191,11 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkdv(DkdvParams p) {
     const size_t base = (size_t)(b * p.Hq + h) * N;
     const rsrc_t qrs = make_rsrc(p.q + base * D, head_bytes);
     const rsrc_t ors = make_rsrc(p.dout + base * D, head_bytes);
-    const uint32_t off = (uint32_t)(qb * BQ + cp_row) * (D * 2) + cp_ch * 2;
+    const uint32_t off = (uint32_t)(qb * BQ + cp_row) * (D * 2) + cp_ch * 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      qst[i] = buf_load16(qrs, off, i * 16 * D * 2);
-      ost[i] = buf_load16(ors, off, i * 16 * D * 2);
+    for (int i = 0; i < 2; ++i) {
+      qst[i] = buf_load16(qrs, off, i * 32 * D * 2);
+      ost[i] = buf_load16(ors, off, i * 32 * D * 2);
     }
     if (tid < BQ) {
       const uint32_t ro = (uint32_t)(qb * BQ + tid) * 4;
@@ -200,9 +205,10 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkdv(DkdvParams p) {
   };
   auto store_step = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(&sm.q[buf][(cp_row + 16 * i) * QS + cp_ch]) = qst[i];
-      *reinterpret_cast<u32x4*>(&sm.dO[buf][(cp_row + 16 * i) * QS + cp_ch]) = ost[i];
+    for (int i = 0; i < 2; ++i) {
+      const int o = swz(cp_row + 32 * i, cp_ch);
+      *reinterpret_cast<u32x4*>(&sm.q[buf][o]) = qst[i];
+      *reinterpret_cast<u32x4*>(&sm.dO[buf][o]) = ost[i];
     }
     if (tid < BQ) {
       sm.lse2[buf][tid] = __uint_as_float(lst);
@@ -215,8 +221,9 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkdv(DkdvParams p) {
   lds_barrier();
 
   const int arow = perm_rows(l32);
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  const SwzRowRead rr(arow, hh);
+  const SwzTrRead tr(lane, hh);
+  const bf16* kp = &sm.k[(wave * 32 + l32) * KS + hh * 8];
 
   for (int st = 0; st < nsteps; ++st) {
     const int cur = st & 1;
@@ -227,35 +234,30 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkdv(DkdvParams p) {
     const bool has_next = st + 1 < nsteps;
     if (has_next) load_step(st + 1);
 
-    // ---- S = Q K^T and dP = dO V^T (rows q, columns = this wave's keys) ----
-    f32x16 sacc[2], pacc[2];
-    {
-      const bf16* kp = &sm.k[(wave * 32 + l32) * KS + hh * 8];
+#pragma unroll
+    for (int qblk = 0; qblk < 2; ++qblk) {
+      // ---- S = Q K^T and dP = dO V^T for 32 query rows x this wave's 32 keys ----
+      f32x16 sacc, pacc;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
+        const int o = rr.at(s) + qblk * 32 * kSwzRow;
         const bf16x8 kb8 = *reinterpret_cast<const bf16x8*>(kp + s * 16);
-#pragma unroll
-        for (int qblk = 0; qblk < 2; ++qblk) {
-          const bf16* qp = &sm.q[cur][(qblk * 32 + arow) * QS + hh * 8 + s * 16];
-          const bf16* op = &sm.dO[cur][(qblk * 32 + arow) * QS + hh * 8 + s * 16];
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qp);
-          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(op);
-          sacc[qblk] = mfma32(qa, kb8, s == 0 ? f32x16{} : sacc[qblk]);
-          pacc[qblk] = mfma32(oa, vr[s], s == 0 ? f32x16{} : pacc[qblk]);
-        }
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sm.q[cur][o]);
+        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&sm.dO[cur][o]);
+        sacc = mfma32(qa, kb8, s == 0 ? f32x16{} : sacc);
+        pacc = mfma32(oa, vr[s], s == 0 ? f32x16{} : pacc);
       }
-    }
 
-    // ---- P = exp2(S c - LSE2), masked on partial tiles; dS = P (dP - D) ----
-    bf16x8 pa[4], sa[4];
-    auto softmax_grad = [&](auto masked) {
-      constexpr bool kMasked = decltype(masked)::value;
-#pragma unroll
-      for (int qblk = 0; qblk < 2; ++qblk) {
+      // ---- P = exp2(S c - LSE2), masked on partial tiles; dS = P (dP - D) ----
+      bf16x8 pa[2], sa[2];
+      auto softmax_grad = [&](auto masked) {
+        constexpr bool kMasked = decltype(masked)::value;
         uint32_t word = 0u;
-        if (kMasked)
-          word = key_ok ? hidden_rows32(mv[0], mv[1], mv[2], mv[3], qb * BQ + qblk * 32)
+        if (kMasked) {
+          const int4 mv = sm.mv[wave * 32 + l32];
+          word = key_ok ? hidden_rows32(mv.x, mv.y, mv.z, mv.w, qb * BQ + qblk * 32)
                         : 0xFFFFFFFFu;
+        }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int q0 = qblk * 32 + j * 16 + hh * 8;
@@ -272,32 +274,33 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkdv(DkdvParams p) {
               const int tt = t + u;
               const float l = tt < 4 ? l0[tt] : l1[tt - 4];
               const float dd = tt < 4 ? d0[tt] : d1[tt - 4];
-              float pp = __builtin_amdgcn_exp2f(fmaf(sacc[qblk][j * 8 + tt], p.c, -l));
+              float pp = __builtin_amdgcn_exp2f(fmaf(sacc[j * 8 + tt], p.c, -l));
               if (kMasked) pp = mask_zero(pp, word, (uint32_t)(j * 16 + hh * 8 + tt));
               pv[u] = pp;
-              sv[u] = pp * (pacc[qblk][j * 8 + tt] - dd);
+              sv[u] = pp * (pacc[j * 8 + tt] - dd);
             }
             pw[t / 2] = pack_bf16x2(pv[0], pv[1]);
             sw[t / 2] = pack_bf16x2(sv[0], sv[1]);
           }
-          pa[qblk * 2 + j] = __builtin_bit_cast(bf16x8, pw);
-          sa[qblk * 2 + j] = __builtin_bit_cast(bf16x8, sw);
+          pa[j] = __builtin_bit_cast(bf16x8, pw);
+          sa[j] = __builtin_bit_cast(bf16x8, sw);
         }
-      }
-    };
-    if (partial) softmax_grad(std::true_type{});
-    else softmax_grad(std::false_type{});
+      };
+      if (partial) softmax_grad(std::true_type{});
+      else softmax_grad(std::false_type{});
 
-    // ---- dV += P^T dO, dK += dS^T Q  (B operands through transposing reads) ----
+      // ---- dV += P^T dO, dK += dS^T Q over these 32 rows (transposing reads) ----
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int r0 = ks * 16 + hh * 8 + tr_row;
+      for (int j = 0; j < 2; ++j) {
+        const int ks = qblk * 2 + j;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const bf16* op = &sm.dO[cur][r0 * QS + d * 32 + tr_col];
-        const bf16* qp = &sm.q[cur][r0 * QS + d * 32 + tr_col];
-        dv[d] = mfma32(pa[ks], join_tr(lds_read_tr16(op), lds_read_tr16(op + 4 * QS)), dv[d]);
-        dk[d] = mfma32(sa[ks], join_tr(lds_read_tr16(qp), lds_read_tr16(qp + 4 * QS)), dk[d]);
+        for (int d = 0; d < 4; ++d) {
+          const int o0 = tr.at(0, ks, d), o1 = tr.at(1, ks, d);
+          const bf16* op = sm.dO[cur];
+          const bf16* qp = sm.q[cur];
+          dv[d] = mfma32(pa[j], join_tr(lds_read_tr16(op + o0), lds_read_tr16(op + o1)), dv[d]);
+          dk[d] = mfma32(sa[j], join_tr(lds_read_tr16(qp + o0), lds_read_tr16(qp + o1)), dk[d]);
+        }
       }
     }
 
@@ -324,11 +327,11 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkdv(DkdvParams p) {
 namespace dqk {
 constexpr int BQ = kFwdBlockQ;  // 128 query rows: 4 waves x 32
 constexpr int BK = kFwdBlockK;  // 64 keys per tile
-constexpr int KS = D + 16;      // K row stride (b128 row reads and transposing reads)
-constexpr int VS = D + 8;       // V row stride (b128 row reads)
+constexpr int VS = D + 8;       // V row stride (272 B: row reads only)
 
+// K tiles use the swizzled 320-byte layout (row reads and transposing reads).
 struct __attribute__((aligned(16))) Smem {
-  bf16 k[2][BK * KS];
+  bf16 k[2][BK * kSwzRow];
   bf16 v[2][BK * VS];
   uint32_t mw[2][4][BK];  // hidden-row words: [buffer][wave][key]
 };
@@ -420,7 +423,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   auto store_tile = [&](int e, int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(&sm.k[buf][(cp_row + 16 * i) * KS + cp_ch]) = kst[i];
+      *reinterpret_cast<u32x4*>(&sm.k[buf][swz(cp_row + 16 * i, cp_ch >> 3)]) = kst[i];
       *reinterpret_cast<u32x4*>(&sm.v[buf][(cp_row + 16 * i) * VS + cp_ch]) = vst[i];
     }
     const int kb = e & 0x7fffffff;
@@ -440,8 +443,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   lds_barrier();
 
   const int arow = perm_rows(l32);
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  const SwzRowRead rr(arow, hh);
+  const SwzTrRead tr(lane, hh);
 
   for (int it = 0; it < n_tiles; ++it) {
     const int cur = it & 1;
@@ -459,11 +462,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
     f32x16 sacc[2], pacc[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const bf16* kp = &sm.k[cur][(blk * 32 + arow) * KS + hh * 8];
       const bf16* vp = &sm.v[cur][(blk * 32 + arow) * VS + hh * 8];
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kp + s * 16);
+        const bf16x8 ka =
+            *reinterpret_cast<const bf16x8*>(&sm.k[cur][rr.at(s) + blk * 32 * kSwzRow]);
         const bf16x8 va = *reinterpret_cast<const bf16x8*>(vp + s * 16);
         sacc[blk] = mfma32(ka, qr[s], s == 0 ? f32x16{} : sacc[blk]);
         pacc[blk] = mfma32(va, orr[s], s == 0 ? f32x16{} : pacc[blk]);
@@ -509,11 +512,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
     const bf16* kt = sm.k[cur];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int key0 = ks * 16 + hh * 8 + tr_row;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const bf16* kp = kt + key0 * KS + d * 32 + tr_col;
-        const bf16x8 a = join_tr(lds_read_tr16(kp), lds_read_tr16(kp + 4 * KS));
+        const bf16x8 a = join_tr(lds_read_tr16(kt + tr.at(0, ks, d)),
+                                 lds_read_tr16(kt + tr.at(1, ks, d)));
         qacc[d] = mfma32(a, dsb[ks], qacc[d]);
       }
     }
@@ -576,7 +578,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   p.c = a.scale * kLog2e;
   const unsigned grid = (unsigned)a.B * (unsigned)a.nKB_k * (unsigned)a.Hkv * (unsigned)p.nch;
   if (ev.dkdv_start) (void)hipEventRecord(ev.dkdv_start, s);
-  hipLaunchKernelGGL(k_attn_bwd_dkdv, dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_attn_bwd_dkdv, dim3(grid), dim3(64 * dkdv::kWaves), 0, s, p);
   if (ev.dkdv_stop) (void)hipEventRecord(ev.dkdv_stop, s);
 
   DqParams q;

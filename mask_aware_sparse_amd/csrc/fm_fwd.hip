@@ -27,7 +27,7 @@ constexpr int BQ = kFwdBlockQ;  // 128
 constexpr int BK = kFwdBlockK;  // 64
 constexpr int D = kHeadDim;     // 128
 constexpr int KS = D + 8;       // K row stride in LDS (elements)
-constexpr int VS = D + 16;      // V row stride in LDS (elements)
+constexpr int VS = D + 32;      // V row stride in LDS (320 B: conflict-free transposing reads)
 
 struct __attribute__((aligned(16))) FwdSmem {
   bf16 k[2][BK * KS];
