@@ -17,7 +17,7 @@
 //   k_attn_bwd_dkdv  one workgroup per (b, kv head, 256-key KV block, chunk of <= 4 query
 //                    heads), numbered in LPT order of the KV blocks' tile costs; each of
 //                    the 8 waves owns 32 keys; the workgroup walks the block's queue of
-//                    64-row Q-blocks (partial tiles masked), recomputes S and dP, and keeps
+//                    32-row Q-blocks (partial tiles masked), recomputes S and dP, and keeps
 //                    dK/dV in registers; they are added to the fp32 accumulators once per
 //                    workgroup (several head chunks share a KV head under GQA/MQA).
 //   k_attn_bwd_dq    one workgroup per (b, 128-row Q-block, query head), numbered in the
@@ -90,11 +90,11 @@ __device__ __forceinline__ int perm_rows(int a) {
 
 // ---- KE: dK / dV (KV-block outer) -------------------------------------------------------
 // 8 waves x 32 keys = one 256-key block per workgroup; two waves per SIMD so that one
-// wave's softmax VALU work overlaps the other's MFMA work.  Each 64-row Q-block step is
-// processed as two 32-row halves, which keeps the live registers of a wave under 256.
+// wave's softmax VALU work overlaps the other's MFMA work.  Steps are 32-row Q-blocks,
+// which keeps the live registers of a wave within 256.
 namespace dkdv {
 constexpr int kWaves = 8;
-constexpr int BQ = kBwdBlockQ;  // 64 query rows per step
+constexpr int BQ = kBwdBlockQ;  // 32 query rows per step
 constexpr int BK = kBwdBlockK;  // 256 keys per workgroup
 constexpr int KS = D + 8;       // K row stride in LDS (272 B: row reads only)
 static_assert(BK == 32 * kWaves, "one 32-key slice per wave");
@@ -178,9 +178,10 @@ __global__ __launch_bounds__(512, 2) void k_attn_bwd_dkdv(DkdvParams p) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) { dk[d] = f32x16{}; dv[d] = f32x16{}; }
 
-  // ---- staging of the Q / dO tiles: thread copies rows (tid>>4)+32i, chunk tid&15
+  // ---- staging of the Q / dO tiles: thread copies row tid>>4, chunk tid&15
+  static_assert(BQ * 16 == 64 * kWaves, "one 16-byte chunk per thread");
   const int cp_row = tid >> 4, cp_ch = tid & 15;
-  u32x4 qst[2], ost[2];
+  u32x4 qst, ost;
   uint32_t lst = 0u, dst_ = 0u;
   const int nsteps = nh * nq;
 
@@ -192,11 +193,8 @@ __global__ __launch_bounds__(512, 2) void k_attn_bwd_dkdv(DkdvParams p) {
     const rsrc_t qrs = make_rsrc(p.q + base * D, head_bytes);
     const rsrc_t ors = make_rsrc(p.dout + base * D, head_bytes);
     const uint32_t off = (uint32_t)(qb * BQ + cp_row) * (D * 2) + cp_ch * 16;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      qst[i] = buf_load16(qrs, off, i * 32 * D * 2);
-      ost[i] = buf_load16(ors, off, i * 32 * D * 2);
-    }
+    qst = buf_load16(qrs, off, 0);
+    ost = buf_load16(ors, off, 0);
     if (tid < BQ) {
       const uint32_t ro = (uint32_t)(qb * BQ + tid) * 4;
       lst = buf_load4(make_rsrc(p.lse2 + base, (uint32_t)N * 4), ro, 0);
@@ -204,12 +202,9 @@ __global__ __launch_bounds__(512, 2) void k_attn_bwd_dkdv(DkdvParams p) {
     }
   };
   auto store_step = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int o = swz(cp_row + 32 * i, cp_ch);
-      *reinterpret_cast<u32x4*>(&sm.q[buf][o]) = qst[i];
-      *reinterpret_cast<u32x4*>(&sm.dO[buf][o]) = ost[i];
-    }
+    const int o = swz(cp_row, cp_ch);
+    *reinterpret_cast<u32x4*>(&sm.q[buf][o]) = qst;
+    *reinterpret_cast<u32x4*>(&sm.dO[buf][o]) = ost;
     if (tid < BQ) {
       sm.lse2[buf][tid] = __uint_as_float(lst);
       sm.dl[buf][tid] = __uint_as_float(dst_);
@@ -234,8 +229,8 @@ __global__ __launch_bounds__(512, 2) void k_attn_bwd_dkdv(DkdvParams p) {
     const bool has_next = st + 1 < nsteps;
     if (has_next) load_step(st + 1);
 
-#pragma unroll
-    for (int qblk = 0; qblk < 2; ++qblk) {
+    {
+      constexpr int qblk = 0;
       // ---- S = Q K^T and dP = dO V^T for 32 query rows x this wave's 32 keys ----
       f32x16 sacc, pacc;
 #pragma unroll
@@ -489,10 +484,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
       }
     }
 
-    // ---- dS^T = P^T o (dP^T - D), P^T = exp2(S^T c - LSE2) ----
-    bf16x8 dsb[4];
+    // ---- dS^T = P^T o (dP^T - D), P^T = exp2(S^T c - LSE2), then dQ^T += K^T dS^T, one
+    // 32-key half at a time so the VALU work of a half overlaps MFMAs of the other ----
+    const bf16* kt = sm.k[cur];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
+      bf16x8 dsb[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         u32x4 packed;
@@ -504,19 +501,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
           packed[t / 2] =
               pack_bf16x2(p0 * (pacc[blk][i0] - d_row), p1 * (pacc[blk][i0 + 1] - d_row));
         }
-        dsb[blk * 2 + j] = __builtin_bit_cast(bf16x8, packed);
+        dsb[j] = __builtin_bit_cast(bf16x8, packed);
       }
-    }
-
-    // ---- dQ^T += K^T dS^T (K^T through transposing reads) ----
-    const bf16* kt = sm.k[cur];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+      for (int j = 0; j < 2; ++j) {
+        const int ks = blk * 2 + j;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const bf16x8 a = join_tr(lds_read_tr16(kt + tr.at(0, ks, d)),
-                                 lds_read_tr16(kt + tr.at(1, ks, d)));
-        qacc[d] = mfma32(a, dsb[ks], qacc[d]);
+        for (int d = 0; d < 4; ++d) {
+          const bf16x8 a = join_tr(lds_read_tr16(kt + tr.at(0, ks, d)),
+                                   lds_read_tr16(kt + tr.at(1, ks, d)));
+          qacc[d] = mfma32(a, dsb[j], qacc[d]);
+        }
       }
     }
 

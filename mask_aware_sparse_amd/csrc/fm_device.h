@@ -159,13 +159,17 @@ __device__ __forceinline__ void buf_atomic_add(float v, rsrc_t r, uint32_t voff,
   __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, voff, soff, 0);
 }
 
-// s if bit `bit` of `word` is clear, -inf if it is set.
+// s if bit `bit` of `word` is clear, -inf if it is set: a sign-extending bit-field
+// extract gives an all-ones / all-zeros mask and a three-input bitwise select (LUT 0xCA:
+// first ? second : third) picks the bits, two VALU instructions per element.
 __device__ __forceinline__ float mask_neg_inf(float s, uint32_t word, uint32_t bit) {
-  return ((word >> bit) & 1u) ? -INFINITY : s;
+  const unsigned m = (unsigned)__builtin_amdgcn_sbfe((int)word, bit, 1u);
+  return __uint_as_float(__builtin_amdgcn_bitop3_b32(m, 0xff800000u, __float_as_uint(s), 0xCA));
 }
 // p if bit `bit` of `word` is clear, 0 if it is set.
 __device__ __forceinline__ float mask_zero(float p, uint32_t word, uint32_t bit) {
-  return ((word >> bit) & 1u) ? 0.f : p;
+  const unsigned m = (unsigned)__builtin_amdgcn_sbfe((int)word, bit, 1u);
+  return __uint_as_float(__builtin_amdgcn_bitop3_b32(m, 0u, __float_as_uint(p), 0xCA));
 }
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS operations, not for

@@ -187,32 +187,33 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
       }
     }
 
-    // ---- online softmax (base 2, lazily rescaled) ----
-    float mx = -INFINITY;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
-    mx = max_with_partner32(mx) * p.c;
-    const bool need = mx > m_use + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float m_new = need ? mx : m_use;
-      // 0 when m_use = -inf; lanes that keep their offset keep their sums
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_use - m_new) : 1.0f;
-      lf *= alpha;
-      lb *= alpha;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
-      m_use = m_new;
-    }
-    const float m_off = (m_use == -INFINITY) ? 0.f : m_use;
-
-    bf16x8 pb[4];
-    float psum = 0.f, pbsum = 0.f;
+    // ---- online softmax (base 2, lazily rescaled) and O^T += V^T P^T, one 32-key half
+    // at a time: the exponentials of half 0 overlap the MFMAs of half 1's scores, and
+    // the PV product of half 0 overlaps the exponentials of half 1 ----
+    const bf16* vb = sm.v[cur];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
+      mx = max_with_partner32(mx) * p.c;
+      const bool need = mx > m_use + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_new = need ? mx : m_use;
+        // 0 when m_use = -inf; lanes that keep their offset keep their sums
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_use - m_new) : 1.0f;
+        lf *= alpha;
+        lb *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+        m_use = m_new;
+      }
+      const float m_off = (m_use == -INFINITY) ? 0.f : m_use;
+
+      bf16x8 pb[2];
+      float psum = 0.f, pbsum = 0.f;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         u32x4 packed;
@@ -226,22 +227,20 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
           pbsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u),
                                                   bf16x2{(bf16)1.0f, (bf16)1.0f}, pbsum, false);
         }
-        pb[blk * 2 + j] = __builtin_bit_cast(bf16x8, packed);
+        pb[j] = __builtin_bit_cast(bf16x8, packed);
       }
-    }
-    lf += psum;
-    lb += pbsum;
+      lf += psum;
+      lb += pbsum;
 
-    // ---- O^T += V^T P^T ----
-    const bf16* vb = sm.v[cur];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int key0 = ks * 16 + hh * 8 + tr_row;
+      for (int j = 0; j < 2; ++j) {
+        const int key0 = (blk * 2 + j) * 16 + hh * 8 + tr_row;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const bf16* vp = vb + key0 * VS + d * 32 + tr_col;
-        const bf16x8 a = join_tr(lds_read_tr16(vp), lds_read_tr16(vp + 4 * VS));
-        oacc[d] = mfma32(a, pb[ks], oacc[d]);
+        for (int d = 0; d < 4; ++d) {
+          const bf16* vp = vb + key0 * VS + d * 32 + tr_col;
+          const bf16x8 a = join_tr(lds_read_tr16(vp), lds_read_tr16(vp + 4 * VS));
+          oacc[d] = mfma32(a, pb[j], oacc[d]);
+        }
       }
     }
 
