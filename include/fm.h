@@ -147,10 +147,12 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
 
 /* Backward: dQ, dK, dV (bf16) from Q, K, V, the forward's O and LSE, and dO.  Classifies
  * internally at both tile shapes (fm_tile_shape(FM_OP_BWD) for dK/dV, FM_OP_FWD for dQ),
- * computes D = rowsum(dO * O) in fp32, then runs two kernels that recompute
- * P = exp(S - LSE) on queued tiles only: a KV-block-outer one accumulating dK and dV
- * (LPT order over KV blocks; fp32 accumulators in `ws`, converted to bf16 at the end) and
- * a Q-block-outer one accumulating dQ in registers (the forward's LPT order).  Any N >= 0. */
+ * then runs two kernels that recompute P = exp(S - LSE) on queued tiles only: a
+ * Q-block-outer one that also forms D = rowsum(dO * O) (fp32) and accumulates dQ in
+ * registers (the forward's LPT order), and a KV-block-outer one accumulating dK and dV
+ * (LPT order over KV blocks).  When heads_q / heads_kv exceeds 4, several workgroups add
+ * into one KV head's dK/dV: fp32 accumulators in `ws`, converted to bf16 at the end;
+ * otherwise each workgroup stores its bf16 rows directly.  Any N >= 0. */
 fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dout, const fm_mask* m,
                       void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream,

@@ -86,6 +86,7 @@ struct BwdWs {
   size_t mm_k, k_queue, k_count, k_cost, k_order;   // dK/dV tiles
   size_t mm_q, q_queue, q_count, q_cost, q_order;   // dQ (forward) tiles
   size_t lse2, delta, dk, dv, total;
+  bool acc;  // fp32 dK/dV accumulators present
 };
 BwdWs bwd_ws(const fm_problem* p, const Blocks& nk, const Blocks& nq) {
   BwdWs w{};
@@ -103,8 +104,14 @@ BwdWs bwd_ws(const fm_problem* p, const Blocks& nk, const Blocks& nq) {
   w.q_order = off; off += align_up(B * nq.nQB * 4);
   w.lse2 = off; off += align_up(rq * 4);
   w.delta = off; off += align_up(rq * 4);
-  w.dk = off; off += align_up(rk * fm::kHeadDim * 4);
-  w.dv = off; off += align_up(rk * fm::kHeadDim * 4);
+  // fp32 dK/dV accumulators only when several workgroups share a KV block (query-head
+  // groups larger than one head chunk); otherwise the kernel stores bf16 directly
+  const int64_t g = p->heads_kv ? p->heads_q / p->heads_kv : 0;
+  w.acc = g > fm::kBwdHeadChunk;
+  if (w.acc) {
+    w.dk = off; off += align_up(rk * fm::kHeadDim * 4);
+    w.dv = off; off += align_up(rk * fm::kHeadDim * 4);
+  }
   w.total = off;
   return w;
 }
@@ -311,7 +318,7 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
     a.k_queue = tk.k_queue; a.k_count = tk.k_count; a.k_order = k_order;
     a.q_queue = tq.q_queue; a.q_count = tq.q_count; a.q_order = q_order;
     a.lse2 = at<float>(ws, w.lse2); a.delta = at<float>(ws, w.delta);
-    a.dk_acc = at<float>(ws, w.dk); a.dv_acc = at<float>(ws, w.dv);
+    if (w.acc) { a.dk_acc = at<float>(ws, w.dk); a.dv_acc = at<float>(ws, w.dv); }
     a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.N = p->seqlen;
     a.nQB_k = (int)nk.nQB; a.nKB_k = (int)nk.nKB;
     a.nQB_q = (int)nq.nQB; a.nKB_q = (int)nq.nKB;

@@ -11,20 +11,21 @@
 // serves both without a reduction through memory.  Adding dQ partials with fp32
 // atomics from a KV-block-outer kernel is bound by the L2's atomic rate on MI355X, so
 // the two sums run in two kernels that each own their output tile:
-//   k_bwd_pre        D = rowsum(dO o O) (fp32) and LSE in log2 units (+inf for rows that
-//                    see nothing, so P = 0 there).
-//   k_zero           zeroes the fp32 dK/dV accumulators (a fill kernel, not a memset).
+//   k_attn_bwd_dq    one workgroup per (b, 128-row Q-block, query head), numbered in the
+//                    forward's LPT order.  It first forms D = rowsum(dO o O) and LSE in
+//                    log2 units (+inf for rows that see nothing, so P = 0 there) for its
+//                    rows and writes both for the dK/dV kernel; then it walks the forward's
+//                    queue of 64-key blocks, recomputes S^T and dP^T, and accumulates
+//                    dQ^T = K^T dS^T in registers (a lane owns one query row, as in the
+//                    forward); dQ is written once.
 //   k_attn_bwd_dkdv  one workgroup per (b, kv head, 256-key KV block, chunk of <= 4 query
 //                    heads), numbered in LPT order of the KV blocks' tile costs; each of
 //                    the 8 waves owns 32 keys; the workgroup walks the block's queue of
 //                    32-row Q-blocks (partial tiles masked), recomputes S and dP, and keeps
-//                    dK/dV in registers; they are added to the fp32 accumulators once per
-//                    workgroup (several head chunks share a KV head under GQA/MQA).
-//   k_attn_bwd_dq    one workgroup per (b, 128-row Q-block, query head), numbered in the
-//                    forward's LPT order; walks the forward's queue of 64-key blocks,
-//                    recomputes S^T and dP^T, and accumulates dQ^T = K^T dS^T in registers
-//                    (a lane owns one query row, as in the forward); dQ is written once.
-//   k_bwd_convert    fp32 dK/dV accumulators -> bf16 (softmax scale applied to dK).
+//                    dK/dV in registers.  With one head chunk per KV head the workgroup
+//                    owns its dK/dV rows and stores them as bf16; with several (GQA/MQA
+//                    groups above 4 heads) it adds them to fp32 accumulators, which
+//                    k_zero clears before and k_bwd_convert turns into bf16 after.
 #include "fm_device.h"
 #include "fm_internal.h"
 
@@ -34,32 +35,6 @@ namespace fm {
 namespace {
 
 constexpr int D = kHeadDim;
-
-// ---- KD: preprocess -----------------------------------------------------------------
-// 16 lanes per row (16 bytes each); a 256-thread block covers 16 rows.
-__global__ __launch_bounds__(256) void k_bwd_pre(const bf16* __restrict__ o,
-                                                 const bf16* __restrict__ dout,
-                                                 const float* __restrict__ lse,
-                                                 float* __restrict__ lse2,
-                                                 float* __restrict__ delta, size_t rows) {
-  const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int c = (threadIdx.x & 15) * 8;
-  float acc = 0.f;
-  if (row < rows) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * D + c);
-    const u32x4 g = *reinterpret_cast<const u32x4*>(dout + row * D + c);
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      acc += bf16lo_to_f32(a[t]) * bf16lo_to_f32(g[t]) + bf16hi_to_f32(a[t]) * bf16hi_to_f32(g[t]);
-  }
-#pragma unroll
-  for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && (threadIdx.x & 15) == 0) {
-    delta[row] = acc;
-    const float l = lse[row];
-    lse2[row] = (l == -INFINITY) ? INFINITY : l * kLog2e;
-  }
-}
 
 __global__ __launch_bounds__(256) void k_zero(float4* __restrict__ p, size_t n4) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256)
@@ -121,10 +96,13 @@ struct DkdvParams {
   const int32_t* __restrict__ k_queue;
   const int32_t* __restrict__ k_count;
   const int32_t* __restrict__ k_order;
-  float* __restrict__ dk_acc;
+  float* __restrict__ dk_acc;  // fp32 accumulators (nch > 1)
   float* __restrict__ dv_acc;
+  bf16* __restrict__ dk;       // bf16 outputs (nch == 1)
+  bf16* __restrict__ dv;
   int B, Hq, Hkv, N, nQB, nKB, hc, nch;
-  float c;  // scale * log2(e)
+  float c;      // scale * log2(e)
+  float scale;  // softmax scale (applied to dK)
 };
 
 __global__ __launch_bounds__(512, 2) void k_attn_bwd_dkdv(DkdvParams p) {
@@ -143,15 +121,30 @@ __global__ __launch_bounds__(512, 2) void k_attn_bwd_dkdv(DkdvParams p) {
   const int h0 = kvh * g + ch * p.hc;
   const int nh = min(p.hc, kvh * g + g - h0);
   const int nq = p.k_count[2 * item] + p.k_count[2 * item + 1];
-  if (nq == 0 || nh <= 0) return;
-  const int32_t* queue = p.k_queue + (size_t)item * p.nQB;
-  const bool ragged_k = (N % BK) != 0 && kb == p.nKB - 1;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const uint32_t acc_bytes = (uint32_t)N * D * 4;
+  const size_t kvbase = (size_t)(b * p.Hkv + kvh) * N * D;
+  if (nh <= 0) return;
+  if (nq == 0) {
+    // no query row sees these keys: dK = dV = 0 (the accumulators start at zero)
+    if (p.nch == 1) {
+      const rsrc_t dkr = make_rsrc(p.dk + kvbase, head_bytes);
+      const rsrc_t dvr = make_rsrc(p.dv + kvbase, head_bytes);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < BK * D * 2 / (16 * 64 * kWaves); ++i) {
+        const uint32_t off = (uint32_t)kb * (BK * D * 2) + (uint32_t)(i * 64 * kWaves + tid) * 16;
+        buf_store16(z, dkr, off, 0);
+        buf_store16(z, dvr, off, 0);
+      }
+    }
+    return;
+  }
+  const int32_t* queue = p.k_queue + (size_t)item * p.nQB;
+  const bool ragged_k = (N % BK) != 0 && kb == p.nKB - 1;
 
   // ---- K of the block into LDS (B operand of S = Q K^T), V resident in registers
   const int key = kb * BK + wave * 32 + l32;
-  const size_t kvbase = (size_t)(b * p.Hkv + kvh) * N * D;
   bf16x8 vr[8];
   {
     const rsrc_t kr_ = make_rsrc(p.k + kvbase, head_bytes);
@@ -185,8 +178,7 @@ __global__ __launch_bounds__(512, 2) void k_attn_bwd_dkdv(DkdvParams p) {
   uint32_t lst = 0u, dst_ = 0u;
   const int nsteps = nh * nq;
 
-  auto load_step = [&](int st) {
-    const int hi = st / nq, it = st - hi * nq;
+  auto load_step = [&](int hi, int it) {
     const int h = h0 + hi;
     const int qb = queue[it] & 0x7fffffff;
     const size_t base = (size_t)(b * p.Hq + h) * N;
@@ -211,7 +203,7 @@ __global__ __launch_bounds__(512, 2) void k_attn_bwd_dkdv(DkdvParams p) {
     }
   };
 
-  load_step(0);
+  load_step(0, 0);
   store_step(0);
   lds_barrier();
 
@@ -220,14 +212,16 @@ __global__ __launch_bounds__(512, 2) void k_attn_bwd_dkdv(DkdvParams p) {
   const SwzTrRead tr(lane, hh);
   const bf16* kp = &sm.k[(wave * 32 + l32) * KS + hh * 8];
 
+  // steps walk (head hi, queue entry it) with it fastest
+  int hi = 0, it = 0;
   for (int st = 0; st < nsteps; ++st) {
     const int cur = st & 1;
-    const int it = st % nq;
     const int e = queue[it];
     const int qb = e & 0x7fffffff;
     const bool partial = (e < 0) || ragged_k;
+    if (++it == nq) { it = 0; ++hi; }
     const bool has_next = st + 1 < nsteps;
-    if (has_next) load_step(st + 1);
+    if (has_next) load_step(hi, it);
 
     {
       constexpr int qblk = 0;
@@ -303,17 +297,32 @@ __global__ __launch_bounds__(512, 2) void k_attn_bwd_dkdv(DkdvParams p) {
     lds_barrier();  // next buffer complete, current buffer free
   }
 
-  // ---- dK, dV of this workgroup's keys into the fp32 accumulators (keys past N dropped)
-  const rsrc_t dkr = make_rsrc(p.dk_acc + kvbase, acc_bytes);
-  const rsrc_t dvr = make_rsrc(p.dv_acc + kvbase, acc_bytes);
-  const uint32_t kl = (uint32_t)((kb * BK + wave * 32 + hh * 4) * D + l32) * 4;
+  // ---- dK, dV of this workgroup's keys (keys past N dropped by the buffer bounds).  A
+  // lane holds dimension d*32 + l32 of keys wave*32 + hh*4 + (i/4)*8 + i%4.
+  const uint32_t kl = (uint32_t)((kb * BK + wave * 32 + hh * 4) * D + l32);
+  if (p.nch == 1) {
+    const rsrc_t dkr = make_rsrc(p.dk + kvbase, head_bytes);
+    const rsrc_t dvr = make_rsrc(p.dv + kvbase, head_bytes);
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < 4; ++d) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t so = (uint32_t)(((i >> 2) * 8 + (i & 3)) * D + d * 32) * 4;
-      buf_atomic_add(dk[d][i], dkr, kl, so);
-      buf_atomic_add(dv[d][i], dvr, kl, so);
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t so = (uint32_t)(((i >> 2) * 8 + (i & 3)) * D + d * 32) * 2;
+        buf_store2(bf16_bits(dk[d][i] * p.scale), dkr, kl * 2, so);
+        buf_store2(bf16_bits(dv[d][i]), dvr, kl * 2, so);
+      }
+    }
+  } else {
+    const rsrc_t dkr = make_rsrc(p.dk_acc + kvbase, acc_bytes);
+    const rsrc_t dvr = make_rsrc(p.dv_acc + kvbase, acc_bytes);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t so = (uint32_t)(((i >> 2) * 8 + (i & 3)) * D + d * 32) * 4;
+        buf_atomic_add(dk[d][i], dkr, kl * 4, so);
+        buf_atomic_add(dv[d][i], dvr, kl * 4, so);
+      }
     }
   }
 }
@@ -336,9 +345,11 @@ struct DqParams {
   const bf16* __restrict__ q;
   const bf16* __restrict__ k;
   const bf16* __restrict__ v;
+  const bf16* __restrict__ o;
   const bf16* __restrict__ dout;
-  const float* __restrict__ lse2;
-  const float* __restrict__ delta;
+  const float* __restrict__ lse;  // natural-log LSE from the forward
+  float* __restrict__ lse2;       // written: LSE in log2 units (+inf where LSE = -inf)
+  float* __restrict__ delta;      // written: rowsum(dO o O)
   MaskPtrs m;
   bf16* __restrict__ dq;
   const int32_t* __restrict__ q_queue;
@@ -386,17 +397,38 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
       orr[s] = __builtin_bit_cast(bf16x8, buf_load16(ors, off, s * 32));
     }
   }
-  const float lse_row =
-      __uint_as_float(buf_load4(make_rsrc(p.lse2 + qbase, vec_bytes), (uint32_t)row * 4, 0));
-  const float d_row =
-      __uint_as_float(buf_load4(make_rsrc(p.delta + qbase, vec_bytes), (uint32_t)row * 4, 0));
+  // D = rowsum(dO o O) for this lane's row (the two half-waves hold the two halves of each
+  // 16-wide d slice) and the LSE in log2 units; both go to memory for the dK/dV kernel.
+  float d_row;
+  {
+    const rsrc_t ors = make_rsrc(p.o + qbase * D, head_bytes);
+    const uint32_t off = (uint32_t)row * (D * 2) + hh * 16;
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const u32x4 ov = buf_load16(ors, off, s * 32);
+      const u32x4 gv = __builtin_bit_cast(u32x4, orr[s]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        part += bf16lo_to_f32(ov[t]) * bf16lo_to_f32(gv[t]) +
+                bf16hi_to_f32(ov[t]) * bf16hi_to_f32(gv[t]);
+    }
+    d_row = sum_with_partner32(part);
+  }
+  const float lse_nat =
+      __uint_as_float(buf_load4(make_rsrc(p.lse + qbase, vec_bytes), (uint32_t)row * 4, 0));
+  const float lse_row = lse_nat == -INFINITY ? INFINITY : lse_nat * kLog2e;
+  if (hh == 0) {  // rows past N are dropped by the buffer bounds
+    buf_store4(__float_as_uint(lse_row), make_rsrc(p.lse2 + qbase, vec_bytes), (uint32_t)row * 4, 0);
+    buf_store4(__float_as_uint(d_row), make_rsrc(p.delta + qbase, vec_bytes), (uint32_t)row * 4, 0);
+  }
 
   f32x16 qacc[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) qacc[d] = f32x16{};
 
   const int cp_row = tid >> 4, cp_ch = (tid & 15) * 8;
-  const int mk_key = tid & 63, mk_wave = tid >> 6;
+  const int mk_key = lane, mk_wave = __builtin_amdgcn_readfirstlane(wave);
   u32x4 kst[4], vst[4];
   uint32_t vec[4];
 
@@ -543,21 +575,42 @@ unsigned grid_for(size_t n, unsigned cap) {
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   if (a.B == 0 || a.N == 0 || a.Hq == 0) return hipSuccess;
-  const size_t rows_q = (size_t)a.B * a.Hq * a.N;
   const size_t rows_k = (size_t)a.B * a.Hkv * a.N;
-  hipLaunchKernelGGL(k_bwd_pre, dim3((unsigned)((rows_q + 15) / 16)), dim3(256), 0, s,
-                     static_cast<const bf16*>(a.o), static_cast<const bf16*>(a.dout), a.lse,
-                     a.lse2, a.delta, rows_q);
-  hipLaunchKernelGGL(k_zero, dim3(grid_for(rows_k * D / 4, 8192)), dim3(256), 0, s,
-                     reinterpret_cast<float4*>(a.dk_acc), rows_k * D / 4);
-  hipLaunchKernelGGL(k_zero, dim3(grid_for(rows_k * D / 4, 8192)), dim3(256), 0, s,
-                     reinterpret_cast<float4*>(a.dv_acc), rows_k * D / 4);
+  const int g = a.Hq / a.Hkv;
+  const int hc = g < kBwdHeadChunk ? g : kBwdHeadChunk;
+  const int nch = (g + hc - 1) / hc;
+  const float c = a.scale * kLog2e;
+
+  // dQ first: it also writes D and the log2 LSE that the dK/dV kernel reads
+  DqParams q;
+  q.q = static_cast<const bf16*>(a.q);
+  q.k = static_cast<const bf16*>(a.k);
+  q.v = static_cast<const bf16*>(a.v);
+  q.o = static_cast<const bf16*>(a.o);
+  q.dout = static_cast<const bf16*>(a.dout);
+  q.lse = a.lse;
+  q.lse2 = a.lse2;
+  q.delta = a.delta;
+  q.m = a.m;
+  q.dq = static_cast<bf16*>(a.dq);
+  q.q_queue = a.q_queue; q.q_count = a.q_count; q.q_order = a.q_order;
+  q.B = a.B; q.Hq = a.Hq; q.Hkv = a.Hkv; q.N = a.N; q.nQB = a.nQB_q; q.nKB = a.nKB_q;
+  q.c = c;
+  q.scale = a.scale;
+  const unsigned qgrid = (unsigned)a.B * (unsigned)a.nQB_q * (unsigned)a.Hq;
+  if (ev.dq_start) (void)hipEventRecord(ev.dq_start, s);
+  hipLaunchKernelGGL(k_attn_bwd_dq, dim3(qgrid), dim3(256), 0, s, q);
+  if (ev.dq_stop) (void)hipEventRecord(ev.dq_stop, s);
+
+  if (nch > 1) {
+    hipLaunchKernelGGL(k_zero, dim3(grid_for(rows_k * D / 4, 8192)), dim3(256), 0, s,
+                       reinterpret_cast<float4*>(a.dk_acc), rows_k * D / 4);
+    hipLaunchKernelGGL(k_zero, dim3(grid_for(rows_k * D / 4, 8192)), dim3(256), 0, s,
+                       reinterpret_cast<float4*>(a.dv_acc), rows_k * D / 4);
+  }
 
   DkdvParams p;
-  p.q = static_cast<const bf16*>(a.q);
-  p.k = static_cast<const bf16*>(a.k);
-  p.v = static_cast<const bf16*>(a.v);
-  p.dout = static_cast<const bf16*>(a.dout);
+  p.q = q.q; p.k = q.k; p.v = q.v; p.dout = q.dout;
   p.lse2 = a.lse2;
   p.delta = a.delta;
   p.m = a.m;
@@ -566,33 +619,24 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   p.k_order = a.k_order;
   p.dk_acc = a.dk_acc;
   p.dv_acc = a.dv_acc;
+  p.dk = static_cast<bf16*>(a.dk);
+  p.dv = static_cast<bf16*>(a.dv);
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N; p.nQB = a.nQB_k; p.nKB = a.nKB_k;
-  const int g = a.Hq / a.Hkv;
-  p.hc = g < kBwdHeadChunk ? g : kBwdHeadChunk;
-  p.nch = (g + p.hc - 1) / p.hc;
-  p.c = a.scale * kLog2e;
-  const unsigned grid = (unsigned)a.B * (unsigned)a.nKB_k * (unsigned)a.Hkv * (unsigned)p.nch;
+  p.hc = hc;
+  p.nch = nch;
+  p.c = c;
+  p.scale = a.scale;
+  const unsigned grid = (unsigned)a.B * (unsigned)a.nKB_k * (unsigned)a.Hkv * (unsigned)nch;
   if (ev.dkdv_start) (void)hipEventRecord(ev.dkdv_start, s);
   hipLaunchKernelGGL(k_attn_bwd_dkdv, dim3(grid), dim3(64 * dkdv::kWaves), 0, s, p);
   if (ev.dkdv_stop) (void)hipEventRecord(ev.dkdv_stop, s);
 
-  DqParams q;
-  q.q = p.q; q.k = p.k; q.v = p.v; q.dout = p.dout; q.lse2 = a.lse2; q.delta = a.delta;
-  q.m = a.m;
-  q.dq = static_cast<bf16*>(a.dq);
-  q.q_queue = a.q_queue; q.q_count = a.q_count; q.q_order = a.q_order;
-  q.B = a.B; q.Hq = a.Hq; q.Hkv = a.Hkv; q.N = a.N; q.nQB = a.nQB_q; q.nKB = a.nKB_q;
-  q.c = p.c;
-  q.scale = a.scale;
-  const unsigned qgrid = (unsigned)a.B * (unsigned)a.nQB_q * (unsigned)a.Hq;
-  if (ev.dq_start) (void)hipEventRecord(ev.dq_start, s);
-  hipLaunchKernelGGL(k_attn_bwd_dq, dim3(qgrid), dim3(256), 0, s, q);
-  if (ev.dq_stop) (void)hipEventRecord(ev.dq_stop, s);
-
-  hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_k * D / 8, 16384)), dim3(256), 0, s,
-                     a.dk_acc, static_cast<bf16*>(a.dk), a.scale, rows_k * D / 8);
-  hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_k * D / 8, 16384)), dim3(256), 0, s,
-                     a.dv_acc, static_cast<bf16*>(a.dv), 1.0f, rows_k * D / 8);
+  if (nch > 1) {
+    hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_k * D / 8, 16384)), dim3(256), 0, s,
+                       a.dk_acc, static_cast<bf16*>(a.dk), a.scale, rows_k * D / 8);
+    hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_k * D / 8, 16384)), dim3(256), 0, s,
+                       a.dv_acc, static_cast<bf16*>(a.dv), 1.0f, rows_k * D / 8);
+  }
   return hipGetLastError();
 }
 

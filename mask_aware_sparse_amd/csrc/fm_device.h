@@ -59,6 +59,10 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(unsigned, v);
 }
 
+__device__ __forceinline__ uint16_t bf16_bits(float a) {
+  return __builtin_bit_cast(uint16_t, (bf16)a);  // round to nearest even
+}
+
 __device__ __forceinline__ float bf16lo_to_f32(unsigned u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi_to_f32(unsigned u) { return __uint_as_float(u & 0xFFFF0000u); }
 
@@ -149,8 +153,14 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff, uint32_t so
 __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
+__device__ __forceinline__ void buf_store16(u32x4 v, rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
+}
 __device__ __forceinline__ void buf_store8(u32x2 v, rsrc_t r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_store2(uint16_t v, rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, 0);
 }
 __device__ __forceinline__ void buf_store4(uint32_t v, rsrc_t r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, soff, 0);

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
 
   // staging for the tile copy: thread copies rows (tid>>4)+16i, 16-byte chunk tid&15
   const int cp_row = tid >> 4, cp_ch = (tid & 15) * 8;
-  const int mk_key = tid & 63, mk_wave = tid >> 6;
+  const int mk_key = lane, mk_wave = __builtin_amdgcn_readfirstlane(wave);
   u32x4 kst[4], vst[4];
   uint32_t vec[4];
 

@@ -86,8 +86,8 @@ struct BwdArgs {
   const int32_t* q_order;
   float* lse2;   // [B][Hq][N] log2-domain LSE (+inf for rows that see nothing)
   float* delta;  // [B][Hq][N] rowsum(dO * O)
-  float* dk_acc; // [B][Hkv][N][128] fp32
-  float* dv_acc; // [B][Hkv][N][128] fp32
+  float* dk_acc; // [B][Hkv][N][128] fp32, only when Hq/Hkv > kBwdHeadChunk (else null)
+  float* dv_acc; // [B][Hkv][N][128] fp32, likewise
   int B, Hq, Hkv, N;
   int nQB_k, nKB_k;  // block counts at the dK/dV tile
   int nQB_q, nKB_q;  // block counts at the dQ (forward) tile

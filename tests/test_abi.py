@@ -79,8 +79,12 @@ def test_workspace_sizes():
     want = al(B * nkb * 32) + al(B * nqb * nkb * 4) + al(B * nqb * 8) + 2 * al(B * nqb * 4)
     assert fm.workspace_size(B, 4, 2, N, fm.OP_FWD) == want
     assert fm.workspace_size(B, 4, 2, N, fm.OP_CLASSIFY, 64, 32) == al(B * 16 * 4) + al(B * 32 * 4)
-    # backward: fp32 dK and dV accumulators dominate (no dQ accumulator)
-    assert fm.workspace_size(B, 4, 2, N, fm.OP_BWD) > 2 * B * 2 * N * 128 * 4
+    # backward: fp32 dK/dV accumulators exist only for query-head groups above 4 heads
+    # (same Hq, so the same D / LSE buffers; tiles depend on B and N only)
+    with_acc = fm.workspace_size(B, 8, 1, N, fm.OP_BWD)
+    without = fm.workspace_size(B, 8, 2, N, fm.OP_BWD)
+    assert with_acc - without == 2 * al(B * 1 * N * 128 * 4)
+    assert without < 2 * B * 8 * N * 4 + 65536
 
 
 @pytest.mark.parametrize("bad,code", [

@@ -21,6 +21,12 @@ SMALL = {
                                                                 sinks=10),
     "random_eviction_1k": lambda: workloads.random_eviction(0, n=1024, heads_q=2),
     "random_intervals_700": lambda: workloads.random_intervals(3, 700, batch=2, heads_q=2),
+    # query-head groups above 4: several workgroups add into one KV head's dK/dV
+    # (two head chunks of 4 and 2 heads)
+    "random_intervals_520_g6": lambda: workloads.random_intervals(5, 520, batch=1, heads_q=6,
+                                                                  heads_kv=1),
+    "prefix_lm_doc_1k_g8": lambda: workloads.prefix_lm_doc(4, n=1024, batch=1, heads_q=16,
+                                                           heads_kv=2, lo=128, hi=512),
 }
 
 
