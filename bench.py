@@ -6,12 +6,17 @@ backward pre/post kernels) over one batch of seeded synthetic inputs resident in
 
 Metric: effective TFLOP/s counting attended (q, k) pairs only, 4*d flop per pair in
 the forward and 10*d in the backward (14*d = 1792 flop per pair at d = 128), over the
-whole step time.  The roofline entry covers the dominant kernel (the backward attention
-kernel): algorithmic flop per launch (10*d per attended pair) / its average duration,
-measured with HIP events recorded around that kernel on the stream it runs on.
+whole step time.  The roofline entry covers the dominant (longest) attention kernel:
+algorithmic flop per launch / its average duration, measured with HIP events recorded
+around that kernel on the stream it runs on.  Its `traffic` is the HBM bytes per launch
+from a committed rocprofv3 counter summary (profiles/traffic_<kernel>_<workload>.txt),
+reported only while the kernel sources still hash to the value recorded there.
 
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
+`--calibrate-copy MIB` instead runs a plain device-to-device copy of that size (for
+scaling the FETCH_SIZE / WRITE_SIZE counters) and prints its byte count.
 """
+import hashlib
 import argparse
 import json
 import os
@@ -43,6 +48,49 @@ def attended_pairs(w):
         inter = np.where((l1 > 0) & (l2 > 0), inter, 0)
         total += int((n - (l1 + l2 - inter)).sum())
     return total * w.heads_q
+
+
+def source_digest():
+    """sha256 over the library's kernel sources and headers (what the counters measured)."""
+    h = hashlib.sha256()
+    for d in ("mask_aware_sparse_amd/csrc", "include"):
+        for f in sorted(os.listdir(os.path.join(ROOT, d))):
+            if f.endswith((".hip", ".h", ".cpp")):
+                with open(os.path.join(ROOT, d, f), "rb") as fh:
+                    h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter summary,
+    or None when there is none or the sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if "=" in line and not line.lstrip().startswith("#"):
+                key, val = line.split("=", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("source_sha256") != source_digest():
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(mib):
+    """A plain copy of `mib` MiB (read once, written once) for counter calibration."""
+    import torch
+    n = mib * 2**20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}))
 
 
 def cpu_baseline(w, q, k, v, do, budget_s):
@@ -92,11 +140,17 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline sample (0 = skip)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="run only a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; multi-GPU runs are not supported",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy > 0:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import torch
     import mask_aware_sparse_amd as fm
@@ -115,7 +169,9 @@ def main():
     A = attended_pairs(w)
     d = w.head_dim
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    # per step: 0 start, 1/2 fwd kernel, 8 between the calls, 3/4 dK/dV kernel,
+    # 6/7 dQ kernel, 5 end (all on the current stream, which the library launches on)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(9)]
           for _ in range(args.steps)]
 
     def step(e=None):
@@ -123,6 +179,8 @@ def main():
             e[0].record()
         fm.attn_fwd(q, k, v, *vec, ws=ws_f, out=o, lse=lse,
                     events=None if e is None else (e[1], e[2]))
+        if e is not None:
+            e[8].record()
         fm.attn_bwd(q, k, v, o, lse, do, *vec, ws=ws_b, grads=grads,
                     events=None if e is None else (e[3], e[4], e[6], e[7]))
         if e is not None:
@@ -138,6 +196,8 @@ def main():
     wall = time.perf_counter() - t0
 
     step_ms = np.array([e[0].elapsed_time(e[5]) for e in ev])
+    call_fwd_ms = np.array([e[0].elapsed_time(e[8]) for e in ev])
+    call_bwd_ms = np.array([e[8].elapsed_time(e[5]) for e in ev])
     fwd_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     dkdv_ms = np.array([e[3].elapsed_time(e[4]) for e in ev])
     dq_ms = np.array([e[6].elapsed_time(e[7]) for e in ev])
@@ -178,10 +238,15 @@ def main():
         "kernels": {kname: {"ms": round(t, 4), "algorithmic_tflops": round(tflops[kname], 2)}
                     for kname, (t, _) in kernels.items()},
         "event_ms_per_step": round(float(step_ms.mean()), 4),
+        # whole calls, classification and LPT sort included: 4d*A / t_fwd and 10d*A / t_bwd
+        "fwd": {"ms": round(float(call_fwd_ms.mean()), 4),
+                "tflops": round(4 * d * A / (call_fwd_ms.mean() * 1e-3) / 1e12, 2)},
+        "bwd": {"ms": round(float(call_bwd_ms.mean()), 4),
+                "tflops": round(10 * d * A / (call_bwd_ms.mean() * 1e-3) / 1e12, 2)},
         "roofline": {"kernel": dom, "bound": "mfma",
                      "achieved": round(tflops[dom], 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops[dom] / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": stored_traffic(dom, args.workload)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

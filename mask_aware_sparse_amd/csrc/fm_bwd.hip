@@ -366,7 +366,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  const int r = blockIdx.x / p.Hq, h = blockIdx.x - r * p.Hq;
+  const int L = xcd_logical((int)blockIdx.x, (int)gridDim.x);
+  const int r = L / p.Hq, h = L - r * p.Hq;
   const int item = p.q_order[r];
   const int b = item / p.nQB, qb = item - b * p.nQB;
   const int kvh = h / (p.Hq / p.Hkv);

@@ -76,6 +76,28 @@ __device__ __forceinline__ float sum_with_partner32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// ---------------------------------------------------------------------------
+// XCD-aware workgroup numbering.  The dispatcher hands workgroup p to XCD p % 8 and each
+// XCD has its own L2, so consecutive work items (the query heads of one Q-block, which
+// read the same K/V tiles, and neighbouring Q-blocks) would land on 8 different L2s.
+// xcd_logical() gives each XCD runs of kXcdChunk consecutive logical items while the
+// dispatch order still follows the logical (LPT) order band by band; a ragged last band
+// keeps the plain numbering.
+// ---------------------------------------------------------------------------
+constexpr int kXcds = 8;
+#ifndef FM_XCD_CHUNK
+#define FM_XCD_CHUNK 16
+#endif
+constexpr int kXcdChunk = FM_XCD_CHUNK;
+
+__device__ __forceinline__ int xcd_logical(int p, int n) {
+  constexpr int band = kXcds * kXcdChunk;
+  const int full = n - n % band;
+  if (p >= full) return p;
+  const int x = p % kXcds, k = p / kXcds;
+  return (k / kXcdChunk) * band + x * kXcdChunk + k % kXcdChunk;
+}
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -42,10 +42,15 @@ __device__ __forceinline__ int perm_rows(int a) {
   return (a & 0x13) | ((a & 4) << 1) | ((a & 8) >> 1);
 }
 
-// Lazy rescaling: the exponent offset of a row only moves when the row max exceeds
-// it by more than this many powers of two (p then stays below 2^8, exact in bf16
-// range), so most tiles skip the accumulator rescale.
-constexpr float kRescaleSlack = 8.0f;
+// Lazy offset.  A row's exponent offset m (log2 units) is set from the true row max on
+// the row's first visible tile and afterwards only moves when a tile's exponentials
+// grow too large: p = 2^(s c - m) is formed against the current m, and only when a
+// lane's sum of p over the 32-key half exceeds 2^kSumLog2 (or is not finite) does the
+// wave take the slow path (row max, rescale of the accumulator and sums, recompute).
+// bf16 and fp32 share their exponent range, so p up to 2^64 loses no relative precision,
+// and the accumulator stays below 2^(64 + 22 + a few) for any N <= 2^22.  The common
+// path therefore needs no per-tile row max at all.
+constexpr float kSumLimit = 18446744073709551616.0f;  // 2^64
 
 struct FwdParams {
   const bf16* __restrict__ q;
@@ -66,7 +71,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  const int r = blockIdx.x / p.Hq, h = blockIdx.x - r * p.Hq;
+  const int L = xcd_logical((int)blockIdx.x, (int)gridDim.x);
+  const int r = L / p.Hq, h = L - r * p.Hq;
   const int item = p.q_order[r];
   const int b = item / p.nQB, qb = item - b * p.nQB;
   const int kvh = h / (p.Hq / p.Hkv);
@@ -193,41 +199,54 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     const bf16* vb = sm.v[cur];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
-      mx = max_with_partner32(mx) * p.c;
-      const bool need = mx > m_use + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float m_new = need ? mx : m_use;
-        // 0 when m_use = -inf; lanes that keep their offset keep their sums
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_use - m_new) : 1.0f;
-        lf *= alpha;
-        lb *= alpha;
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
-        m_use = m_new;
-      }
-      const float m_off = (m_use == -INFINITY) ? 0.f : m_use;
-
       bf16x8 pb[2];
-      float psum = 0.f, pbsum = 0.f;
+      float psum, pbsum;
+      // p = 2^(s c - off) for this half, packed to bf16, with its fp32 and bf16 sums
+      auto exponentiate = [&](float off) {
+        psum = 0.f;
+        pbsum = 0.f;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        u32x4 packed;
+        for (int j = 0; j < 2; ++j) {
+          u32x4 packed;
 #pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[blk][j * 8 + t], p.c, -m_off));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[blk][j * 8 + t + 1], p.c, -m_off));
-          psum += p0 + p1;
-          const unsigned u = pack_bf16x2(p0, p1);
-          packed[t / 2] = u;
-          pbsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u),
-                                                  bf16x2{(bf16)1.0f, (bf16)1.0f}, pbsum, false);
+          for (int t = 0; t < 8; t += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[blk][j * 8 + t], p.c, -off));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[blk][j * 8 + t + 1], p.c, -off));
+            psum += p0 + p1;
+            const unsigned u = pack_bf16x2(p0, p1);
+            packed[t / 2] = u;
+            pbsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u),
+                                                    bf16x2{(bf16)1.0f, (bf16)1.0f}, pbsum, false);
+          }
+          pb[j] = __builtin_bit_cast(bf16x8, packed);
         }
-        pb[j] = __builtin_bit_cast(bf16x8, packed);
+      };
+      bool slow = m_use == -INFINITY;
+      if (!__builtin_amdgcn_ballot_w64(slow)) {
+        exponentiate(m_use);
+        slow = !(psum <= kSumLimit);
+      }
+      if (__builtin_amdgcn_ballot_w64(slow)) {
+        // row max of this half (both lanes of the row), offset moved up to it if larger
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
+        mx = max_with_partner32(mx) * p.c;
+        const bool need = mx > m_use;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+          const float m_new = need ? mx : m_use;
+          // 0 when m_use = -inf; lanes that keep their offset keep their sums
+          const float alpha = need ? __builtin_amdgcn_exp2f(m_use - m_new) : 1.0f;
+          lf *= alpha;
+          lb *= alpha;
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+          m_use = m_new;
+        }
+        // a row that has seen only masked scores keeps m = -inf and gets p = 0 here
+        exponentiate(m_use == -INFINITY ? 0.f : m_use);
       }
       lf += psum;
       lb += pbsum;
