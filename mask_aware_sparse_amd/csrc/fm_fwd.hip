@@ -15,7 +15,8 @@
 // then O^T += V^T P^T so that the same lane owns that row of the accumulator; the
 // softmax statistics therefore never leave the lane pair.  Q stays in registers; K and
 // V tiles are double-buffered through LDS (row-major; V is read with the transposing
-// ds_read_b64_tr_b16).  Two row sums are kept: l_f (fp32 sum of p) gives the LSE,
+// ds_read_b64_tr_b16), K one tile ahead of V so that the scores of the next tile are
+// computed (MFMA) while the current tile's exponentials run (VALU).  Two row sums are kept: l_f (fp32 sum of p) gives the LSE,
 // l_b (sum of the bf16-rounded p that the PV product actually used) normalises O.
 #include "fm_device.h"
 #include "fm_internal.h"
@@ -109,148 +110,193 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   const int mk_key = lane, mk_wave = __builtin_amdgcn_readfirstlane(wave);
   u32x4 kst[4], vst[4];
   uint32_t vec[4];
+  auto is_partial = [&](int e) {
+    return (e < 0) || (ragged && (e & 0x7fffffff) == p.nKB - 1);
+  };
 
-  auto load_tile = [&](int e) {
+  // Software pipeline.  Iteration t computes the scores of tile t+1 (MFMA) in the same
+  // block as the softmax of tile t (VALU), then tile t's PV product.  K (with the mask
+  // words) therefore runs one tile ahead of V: iteration t reads K/mw buffer (t+1)&1 and
+  // V buffer t&1, and refills K/mw buffer t&1 with tile t+2 and V buffer (t+1)&1 with
+  // tile t+1; one barrier per iteration separates those reads from those writes.
+  auto fetch_k = [&](int e) {
     const int kb = e & 0x7fffffff;
     const uint32_t base = (uint32_t)(kb * BK + cp_row) * (D * 2) + cp_ch * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kst[i] = buf_load16(kr_, base, i * 16 * D * 2);
-      vst[i] = buf_load16(vr_, base, i * 16 * D * 2);
-    }
-    const bool part = (e < 0) || (ragged && kb == p.nKB - 1);
-    if (part) {
+    for (int i = 0; i < 4; ++i) kst[i] = buf_load16(kr_, base, i * 16 * D * 2);
+    if (is_partial(e)) {
       const uint32_t vo = (uint32_t)(kb * BK + mk_key) * 4;
       vec[0] = buf_load4(m0, vo, 0); vec[1] = buf_load4(m1, vo, 0);
       vec[2] = buf_load4(m2, vo, 0); vec[3] = buf_load4(m3, vo, 0);
     }
   };
-  auto store_tile = [&](int e, int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(&sm.k[buf][(cp_row + 16 * i) * KS + cp_ch]) = kst[i];
-      *reinterpret_cast<u32x4*>(&sm.v[buf][(cp_row + 16 * i) * VS + cp_ch]) = vst[i];
-    }
+  auto fetch_v = [&](int e) {
     const int kb = e & 0x7fffffff;
-    const bool part = (e < 0) || (ragged && kb == p.nKB - 1);
-    if (part) {
-      const int key = kb * BK + mk_key;
+    const uint32_t base = (uint32_t)(kb * BK + cp_row) * (D * 2) + cp_ch * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vst[i] = buf_load16(vr_, base, i * 16 * D * 2);
+  };
+  auto put_k = [&](int e, int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(&sm.k[buf][(cp_row + 16 * i) * KS + cp_ch]) = kst[i];
+    if (is_partial(e)) {
+      const int key = (e & 0x7fffffff) * BK + mk_key;
       const int r0 = qb * BQ + mk_wave * 32;
       const uint32_t w = hidden_rows32((int)vec[0], (int)vec[1], (int)vec[2], (int)vec[3], r0);
       sm.mw[buf][mk_wave][mk_key] = key < N ? w : 0xFFFFFFFFu;
     }
   };
-
-  if (n_tiles > 0) {
-    load_tile(queue[0]);
-    store_tile(queue[0], 0);
-  }
-  lds_barrier();
+  auto put_v = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(&sm.v[buf][(cp_row + 16 * i) * VS + cp_ch]) = vst[i];
+  };
 
   const int arow = perm_rows(l32);
   // transposing-read coordinates for the V^T operand
   const int tr_row = (lane & 15) >> 2;                         // + key base
   const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);  // + d-block base
 
-  for (int it = 0; it < n_tiles; ++it) {
-    const int cur = it & 1;
-    const int e = queue[it];
-    const int kb = e & 0x7fffffff;
-    const bool partial = (e < 0) || (ragged && kb == p.nKB - 1);
-    int en = 0;
-    const bool has_next = it + 1 < n_tiles;
-    if (has_next) {
-      en = queue[it + 1];
-      load_tile(en);
-    }
-
-    // ---- S^T = K Q^T (fp32) ----
-    f32x16 sacc[2];
+  // S^T = K Q^T for one 64-key tile (fp32), from K buffer `buf`
+  auto scores = [&](int buf, f32x16 (&acc)[2]) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const bf16* kp = &sm.k[cur][(blk * 32 + arow) * KS + hh * 8];
+      const bf16* kp = &sm.k[buf][(blk * 32 + arow) * KS + hh * 8];
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + s * 16);
-        sacc[blk] = mfma32(a, qr[s], s == 0 ? f32x16{} : sacc[blk]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + s * 16);
+        acc[blk] = mfma32(a, qr[s], s == 0 ? f32x16{} : acc[blk]);
       }
     }
-
-    // ---- row-interval mask, partial tiles only ----
-    if (partial) {
-      const uint32_t* mw = sm.mw[cur][wave];
+  };
+  // row-interval mask on a partial tile: hidden scores -> -inf
+  auto apply_mask = [&](int buf, f32x16 (&acc)[2]) {
+    const uint32_t* mw = sm.mw[buf][wave];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
+    for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const u32x4 w0 = *reinterpret_cast<const u32x4*>(mw + blk * 32 + j * 16 + hh * 8);
-          const u32x4 w1 = *reinterpret_cast<const u32x4*>(mw + blk * 32 + j * 16 + hh * 8 + 4);
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 w0 = *reinterpret_cast<const u32x4*>(mw + blk * 32 + j * 16 + hh * 8);
+        const u32x4 w1 = *reinterpret_cast<const u32x4*>(mw + blk * 32 + j * 16 + hh * 8 + 4);
 #pragma unroll
-          for (int t = 0; t < 8; ++t)
-            sacc[blk][j * 8 + t] = mask_neg_inf(sacc[blk][j * 8 + t], t < 4 ? w0[t] : w1[t - 4],
-                                                (uint32_t)l32);
-        }
+        for (int t = 0; t < 8; ++t)
+          acc[blk][j * 8 + t] =
+              mask_neg_inf(acc[blk][j * 8 + t], t < 4 ? w0[t] : w1[t - 4], (uint32_t)l32);
       }
     }
+  };
 
-    // ---- online softmax (base 2, lazily rescaled) and O^T += V^T P^T, one 32-key half
-    // at a time: the exponentials of half 0 overlap the MFMAs of half 1's scores, and
-    // the PV product of half 0 overlaps the exponentials of half 1 ----
+  f32x16 sacc[2];
+  if (n_tiles > 0) {
+    const int e0 = queue[0];
+    fetch_k(e0);
+    fetch_v(e0);
+    put_k(e0, 0);
+    put_v(0);
+    if (n_tiles > 1) {
+      const int e1 = queue[1];
+      fetch_k(e1);
+      put_k(e1, 1);
+    }
+  }
+  lds_barrier();
+  if (n_tiles > 0) {
+    scores(0, sacc);
+    if (is_partial(queue[0])) apply_mask(0, sacc);
+  }
+
+  for (int it = 0; it < n_tiles; ++it) {
+    const int cur = it & 1, nxt = cur ^ 1;
+    const bool has1 = it + 1 < n_tiles, has2 = it + 2 < n_tiles;
+    const int e1 = has1 ? queue[it + 1] : 0;
+    const int e2 = has2 ? queue[it + 2] : 0;
+    if (has2) fetch_k(e2);
+    if (has1) fetch_v(e1);
+
+    // ---- scores of tile it+1 (MFMA; stale but unused after the last tile) interleaved
+    // with the exponentials of tile it (VALU): step i issues the K fragment read for step
+    // i+2, score MFMA i, and the exponentials of score pair i of the current tile.  The
+    // scheduling barriers keep that order, so the VALU work runs in the MFMAs' shadow. ----
+    f32x16 snext[2];
+    bf16x8 pb[2][2];
+    float psum[2], pbsum[2];
+    // p = 2^(s c - off) for score pair i (half i/8, column group (i%8)/4, rows 2(i%4)+{0,1})
+    u32x4 packed[2][2];
+    auto exp_pair = [&](int i, float off) {
+      const int hb = i / 8, j = (i % 8) / 4, t = (i % 4) * 2;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[hb][j * 8 + t], p.c, -off));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[hb][j * 8 + t + 1], p.c, -off));
+      psum[hb] += p0 + p1;
+      const unsigned u = pack_bf16x2(p0, p1);
+      packed[hb][j][t / 2] = u;
+      pbsum[hb] = __builtin_amdgcn_fdot2_f32_bf16(
+          __builtin_bit_cast(bf16x2, u), bf16x2{(bf16)1.0f, (bf16)1.0f}, pbsum[hb], false);
+    };
+    auto exponentiate_all = [&](float off) {
+      psum[0] = psum[1] = 0.f;
+      pbsum[0] = pbsum[1] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) exp_pair(i, off);
+    };
+    // a row without an offset yet uses 0: exact if it saw nothing so far (p = 0)
+    const float off0 = m_use == -INFINITY ? 0.f : m_use;
+    {
+      psum[0] = psum[1] = 0.f;
+      pbsum[0] = pbsum[1] = 0.f;
+      const bf16* kbase = &sm.k[nxt][arow * KS + hh * 8];
+      auto kread = [&](int i) {
+        return *reinterpret_cast<const bf16x8*>(kbase + (i / 8) * 32 * KS + (i % 8) * 16);
+      };
+      bf16x8 kf[3];
+      kf[0] = kread(0);
+      kf[1] = kread(1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i + 2 < 16) kf[(i + 2) % 3] = kread(i + 2);
+        const int blk = i / 8, st = i % 8;
+        snext[blk] = mfma32(kf[i % 3], qr[st], st == 0 ? f32x16{} : snext[blk]);
+        exp_pair(i, off0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    const bool slow = !(psum[0] <= kSumLimit) || !(psum[1] <= kSumLimit) ||
+                      (m_use == -INFINITY && psum[0] + psum[1] > 0.f);
+    if (__builtin_amdgcn_ballot_w64(slow)) {
+      // row max of the tile (both lanes of the row); offset moved up to it if larger
+      float mx = -INFINITY;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
+      mx = max_with_partner32(mx) * p.c;
+      const bool need = mx > m_use;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_new = need ? mx : m_use;
+        // 0 when m_use = -inf; lanes that keep their offset keep their sums
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_use - m_new) : 1.0f;
+        lf *= alpha;
+        lb *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+        m_use = m_new;
+      }
+      exponentiate_all(m_use == -INFINITY ? 0.f : m_use);
+    }
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) pb[hb][j] = __builtin_bit_cast(bf16x8, packed[hb][j]);
+    lf += psum[0] + psum[1];
+    lb += pbsum[0] + pbsum[1];
+
+    // ---- O^T += V^T P^T for tile it ----
     const bf16* vb = sm.v[cur];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      bf16x8 pb[2];
-      float psum, pbsum;
-      // p = 2^(s c - off) for this half, packed to bf16, with its fp32 and bf16 sums
-      auto exponentiate = [&](float off) {
-        psum = 0.f;
-        pbsum = 0.f;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          u32x4 packed;
-#pragma unroll
-          for (int t = 0; t < 8; t += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[blk][j * 8 + t], p.c, -off));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[blk][j * 8 + t + 1], p.c, -off));
-            psum += p0 + p1;
-            const unsigned u = pack_bf16x2(p0, p1);
-            packed[t / 2] = u;
-            pbsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u),
-                                                    bf16x2{(bf16)1.0f, (bf16)1.0f}, pbsum, false);
-          }
-          pb[j] = __builtin_bit_cast(bf16x8, packed);
-        }
-      };
-      bool slow = m_use == -INFINITY;
-      if (!__builtin_amdgcn_ballot_w64(slow)) {
-        exponentiate(m_use);
-        slow = !(psum <= kSumLimit);
-      }
-      if (__builtin_amdgcn_ballot_w64(slow)) {
-        // row max of this half (both lanes of the row), offset moved up to it if larger
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
-        mx = max_with_partner32(mx) * p.c;
-        const bool need = mx > m_use;
-        if (__builtin_amdgcn_ballot_w64(need)) {
-          const float m_new = need ? mx : m_use;
-          // 0 when m_use = -inf; lanes that keep their offset keep their sums
-          const float alpha = need ? __builtin_amdgcn_exp2f(m_use - m_new) : 1.0f;
-          lf *= alpha;
-          lb *= alpha;
-#pragma unroll
-          for (int d = 0; d < 4; ++d)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
-          m_use = m_new;
-        }
-        // a row that has seen only masked scores keeps m = -inf and gets p = 0 here
-        exponentiate(m_use == -INFINITY ? 0.f : m_use);
-      }
-      lf += psum;
-      lb += pbsum;
-
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int key0 = (blk * 2 + j) * 16 + hh * 8 + tr_row;
@@ -258,13 +304,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
         for (int d = 0; d < 4; ++d) {
           const bf16* vp = vb + key0 * VS + d * 32 + tr_col;
           const bf16x8 a = join_tr(lds_read_tr16(vp), lds_read_tr16(vp + 4 * VS));
-          oacc[d] = mfma32(a, pb[j], oacc[d]);
+          oacc[d] = mfma32(a, pb[blk][j], oacc[d]);
         }
       }
     }
 
-    if (has_next) store_tile(en, cur ^ 1);
+    if (has1 && is_partial(e1)) apply_mask(nxt, snext);
+    if (has2) put_k(e2, cur);
+    if (has1) put_v(nxt);
     lds_barrier();
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) sacc[blk] = snext[blk];
   }
 
   // ---- epilogue: O = acc / l_b, LSE = ln2 * (m + log2 l_f) ----
