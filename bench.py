@@ -15,6 +15,9 @@ reported only while the kernel sources still hash to the value recorded there.
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
 `--calibrate-copy MIB` instead runs a plain device-to-device copy of that size (for
 scaling the FETCH_SIZE / WRITE_SIZE counters) and prints its byte count.
+`--measure-alpha` instead times the relative cost of a partial tile (the alpha_p : alpha_u
+of the FlashMask-3 page's tile cost, §3.3): full attention classified all-unmasked
+against the same attention classified all-partial (empty intervals, nothing hidden).
 """
 import hashlib
 import argparse
@@ -93,6 +96,51 @@ def calibrate_copy(mib):
     print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}))
 
 
+def measure_alpha(steps, warmup, n=8192, heads=64):
+    """Per-kernel time of all-partial vs all-unmasked tiles on identical work (MQA,
+    B = 1, the given N and query heads).  Also checks that both give bit-identical
+    outputs, since nothing is hidden in either."""
+    import torch
+    import mask_aware_sparse_amd as fm
+    runs = {}
+    outs = {}
+    for tag, w in (("unmasked", workloads.full_attention(n, heads_q=heads)),
+                   ("partial", workloads.full_attention_partial_tiles(n, heads_q=heads))):
+        q, k, v, do = workloads.make_tensors(w, seed=0, device="cuda")
+        vec = workloads.mask_tensors(w, device="cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty((1, heads, n), dtype=torch.float32, device="cuda")
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        ws_f = torch.empty(fm.workspace_size(1, heads, 1, n, fm.OP_FWD), dtype=torch.uint8,
+                           device="cuda")
+        ws_b = torch.empty(fm.workspace_size(1, heads, 1, n, fm.OP_BWD), dtype=torch.uint8,
+                           device="cuda")
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+        for i in range(warmup + steps):
+            e = ev[i - warmup] if i >= warmup else None
+            fm.attn_fwd(q, k, v, *vec, ws=ws_f, out=o, lse=lse,
+                        events=None if e is None else (e[0], e[1]))
+            fm.attn_bwd(q, k, v, o, lse, do, *vec, ws=ws_b, grads=grads,
+                        events=None if e is None else (e[2], e[3], e[4], e[5]))
+        torch.cuda.synchronize()
+        runs[tag] = {kname: float(np.median([e[a].elapsed_time(e[b]) for e in ev]))
+                     for kname, a, b in (("k_attn_fwd", 0, 1), ("k_attn_bwd_dkdv", 2, 3),
+                                         ("k_attn_bwd_dq", 4, 5))}
+        outs[tag] = (o.clone(), lse.clone()) + tuple(g.clone() for g in grads)
+    # O, LSE, dQ are written once per element; dK/dV of MQA groups are summed with fp32
+    # atomics in arbitrary order, so only their difference is reported
+    same = all(torch.equal(a, b) for a, b in zip(outs["unmasked"][:3], outs["partial"][:3]))
+    dkdv_diff = max(float((a.float() - b.float()).abs().max())
+                    for a, b in zip(outs["unmasked"][3:], outs["partial"][3:]))
+    ratio = {kname: round(runs["partial"][kname] / runs["unmasked"][kname], 4)
+             for kname in runs["unmasked"]}
+    print(json.dumps({"measure": "alpha_p / alpha_u (partial vs unmasked tile time)",
+                      "config": {"batch": 1, "heads_q": heads, "heads_kv": 1, "seq_len": n,
+                                 "head_dim": 128, "steps": steps, "warmup": warmup},
+                      "ms_median": runs, "ratio": ratio, "o_lse_dq_bit_identical": same,
+                      "dk_dv_max_abs_diff": dkdv_diff}))
+
+
 def cpu_baseline(w, q, k, v, do, budget_s):
     """Time the fp64 oracle on a bounded sample of the same workload: whole (b, h)
     problems, taken in order b = 0.., h spread over the heads, until the budget is
@@ -142,6 +190,8 @@ def main():
                     help="seconds of oracle work for the cpu_baseline sample (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--measure-alpha", action="store_true",
+                    help="time partial against unmasked tiles on identical work")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; multi-GPU runs are not supported",
@@ -150,6 +200,9 @@ def main():
 
     if args.calibrate_copy > 0:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.measure_alpha:
+        measure_alpha(args.steps, args.warmup)
         return
 
     import torch

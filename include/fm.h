@@ -90,7 +90,7 @@ typedef struct {
  *                each entry qb | (partial << 31); then -1 to the end
  *   k_count      [B][nKB][2]   int32: {n_partial, n_unmasked} per KV block
  *   q_order      [B*nQB]       int32: Q-blocks (b*nQB + qb) sorted by cost
- *                13*n_partial + 10*n_unmasked descending, ties ascending
+ *                11*n_partial + 10*n_unmasked descending, ties ascending
  *   k_order      [B*nKB]       int32: the same over KV blocks (b*nKB + kb)          */
 typedef struct {
   int32_t* block_minmax;

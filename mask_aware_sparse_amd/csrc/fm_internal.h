@@ -19,8 +19,10 @@ constexpr int kBwdBlockK = 256;
 // Query heads handled by one backward work item (dK/dV of a KV block are summed over
 // these heads in registers, then added across items with fp32 atomics).
 constexpr int kBwdHeadChunk = 4;
-// Tile costs in integer units, alpha_partial : alpha_unmasked = 1.3 : 1.
-constexpr int kAlphaPartial = 13;
+// Tile costs in integer units, alpha_partial : alpha_unmasked = 1.1 : 1: the FlashMask-3
+// page's 1.3 : 1 (§3.3) is illustrative; 1.1 is the measured cost of a partial tile of these
+// kernels against an unmasked one on identical work (1.11 fwd, 1.08 dQ, 1.05 dK/dV).
+constexpr int kAlphaPartial = 11;
 constexpr int kAlphaUnmasked = 10;
 // The LPT sort runs in one workgroup with 64-bit keys in LDS.
 constexpr int kMaxSortItems = 8192;

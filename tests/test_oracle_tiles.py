@@ -132,7 +132,7 @@ def test_queues_counts_costs_order():
         assert list(got & 0x7FFFFFFF) == live
         assert kc[0, kb].sum() == len(live)
     cost = oracle.tile_costs(qc)
-    assert (cost == 13 * qc[..., 0] + 10 * qc[..., 1]).all()
+    assert (cost == 11 * qc[..., 0] + 10 * qc[..., 1]).all()
     order = oracle.lpt_order(cost)
     flat = cost.reshape(-1)
     assert sorted(order.tolist()) == list(range(flat.size))

@@ -178,6 +178,26 @@ def causal(n: int, batch: int = 1, heads_q: int = 1, heads_kv: int = 1) -> Workl
     return _finish("causal", batch, heads_q, heads_kv, n, (lts, lte, uts, ute), 0, {})
 
 
+def full_attention(n: int, batch: int = 1, heads_q: int = 1, heads_kv: int = 1) -> Workload:
+    """No key hidden from any row: every tile is unmasked."""
+    return _finish("full_attention", batch, heads_q, heads_kv, n, _empty_vectors(batch, n), 0, {})
+
+
+def full_attention_partial_tiles(n: int, batch: int = 1, heads_q: int = 1,
+                                 heads_kv: int = 1) -> Workload:
+    """No key hidden from any row, yet every tile of at least two columns is classified
+    partial: even columns carry the empty lower interval [0, 0) and odd columns [N, N),
+    so each KV block's minimum LTS is 0 and its maximum LTE is N.  The same attention as
+    full_attention() with the mask path switched on everywhere (timing the cost of a
+    partial tile against an unmasked one)."""
+    lts, lte, uts, ute = _empty_vectors(batch, n)
+    odd = (np.arange(n) % 2) == 1
+    lts[:, ~odd] = 0
+    lte[:, ~odd] = 0
+    return _finish("full_attention_partial_tiles", batch, heads_q, heads_kv, n,
+                   (lts, lte, uts, ute), 0, {})
+
+
 def random_intervals(seed: int, n: int, batch: int = 1, heads_q: int = 1,
                      heads_kv: int = 1, p_empty: float = 0.2) -> Workload:
     """Adversarial vectors: both intervals of every column are random, may be
@@ -195,7 +215,7 @@ def random_intervals(seed: int, n: int, batch: int = 1, heads_q: int = 1,
 
 
 # The five benchmark workloads, in order.  Shapes and mask families follow the
-# synthetic stand-ins for the pages' mask families (see the design doc for the recipe).
+# synthetic stand-ins for the mask families the FlashMask-3 page benchmarks.
 CONFIGS = {
     "c1_causal_doc_1k": lambda seed=0: causal_doc(seed),
     "c2_prefix_lm_doc_8k": lambda seed=0: prefix_lm_doc(seed),
