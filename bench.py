@@ -15,6 +15,13 @@ reported only while the kernel sources still hash to the value recorded there.
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
 `--calibrate-copy MIB` instead runs a plain device-to-device copy of that size (for
 scaling the FETCH_SIZE / WRITE_SIZE counters) and prints its byte count.
+`--classify-bandwidth` instead times fm_classify_tiles (block min/max, classes, both queue
+sets, costs, both LPT orders) on the c5 vectors replicated over 4 batch rows (the most the
+single-workgroup LPT sort takes at the forward tile: 4 x 2048 KV blocks), against the
+HBM roofline.
+`--ipo-table` instead runs the host chunk balancer (fm_ipo_balance, HCC-IPO stage 1) on
+seeded instances of the FlashMask-3 page's IPO ablation configurations and prints the
+share of instances above the lower bound after LPT, P2 and P3, the mean gaps and times.
 `--measure-alpha` instead times the relative cost of a partial tile (the alpha_p : alpha_u
 of the FlashMask-3 page's tile cost, §3.3): full attention classified all-unmasked
 against the same attention classified all-partial (empty intervals, nothing hidden).
@@ -94,6 +101,92 @@ def calibrate_copy(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}))
+
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E
+
+
+def classify_bandwidth(steps, warmup, batch=4, block_q=128, block_k=64):
+    """fm_classify_tiles on the c5 (random eviction, N = 131072) vectors replicated to
+    `batch` rows, at the forward's tile shape.  Bytes: the algorithmic traffic (vectors
+    read once; block min/max, classes, one int32 per queued tile per direction, counts,
+    costs and orders written once) and the bytes this layout actually writes (queue rows
+    are fixed-length, filled with -1 past the count)."""
+    import torch
+    import mask_aware_sparse_amd as fm
+    w = workloads.make_workload("c5_random_eviction_128k", 0)
+    n = w.seqlen
+    vec = [torch.from_numpy(np.ascontiguousarray(np.repeat(x[:1], batch, 0))).cuda()
+           for x in w.vectors()]
+    nqb, nkb = -(-n // block_q), -(-n // block_k)
+    ws = torch.empty(fm.workspace_size(batch, 1, 1, n, fm.OP_CLASSIFY, block_q, block_k),
+                     dtype=torch.uint8, device="cuda")
+    out = fm.classify_tiles(*vec, block_q, block_k, ws=ws)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(warmup + steps):
+        e = ev[i - warmup] if i >= warmup else None
+        if e:
+            e[0].record()
+        fm.classify_tiles(*vec, block_q, block_k, out=out, ws=ws)
+        if e:
+            e[1].record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    queued = int((out["tile_class"] != 0).sum())
+    read = 16 * batch * n
+    small = 32 * batch * nkb + 8 * batch * (nqb + nkb) + 8 * batch * (nqb + nkb)  # mm, counts, costs+orders
+    alg = read + small + batch * nqb * nkb + 2 * 4 * queued
+    layout = read + small + batch * nqb * nkb + 2 * 4 * batch * nqb * nkb
+    gbs = lambda b: b / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "measure": "fm_classify_tiles bandwidth",
+        "config": {"vectors": "c5_random_eviction_128k replicated", "batch": batch,
+                   "seq_len": n, "block_q": block_q, "block_k": block_k,
+                   "queued_tiles": queued, "steps": steps, "warmup": warmup},
+        "ms_median": round(ms, 4),
+        "algorithmic_bytes": alg, "layout_bytes": layout,
+        "roofline": {"bound": "hbm", "achieved": round(gbs(alg), 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs(alg) / HBM_PEAK_GBS, 4)},
+        "layout_gbs": round(gbs(layout), 1)}))
+
+
+def ipo_table(instances=200, seed=0):
+    """fm_ipo_balance on the ablation table's configurations (n, P, kappa, w_max).  The
+    page does not give its instance distributions; the stand-ins are: uniform integer
+    weights in [1, w_max]; 'causal' chunk i carrying (i + 1) steps of ceil(w_max / n)
+    plus a uniform jitter below one step (the load of a causal query chunk grows with
+    its position).  Host code: no GPU is touched."""
+    import random
+    import mask_aware_sparse_amd as fm
+    rng = random.Random(seed)
+    cfgs = [("uniform", 64, 16, 4, 1000), ("uniform_wide", 64, 16, 4, 10**4),
+            ("causal", 64, 8, 8, 200), ("uniform_128", 128, 16, 8, 200)]
+    out = []
+    for name, n, P, kappa, wmax in cfgs:
+        rows = []
+        for _ in range(instances if n == 64 else instances // 2):
+            if name == "causal":
+                step = -(-wmax // n)
+                w = [(i + 1) * step + rng.randrange(step) for i in range(n)]
+            else:
+                w = [rng.randint(1, wmax) for _ in range(n)]
+            t0 = time.perf_counter()
+            _, r = fm.ipo_balance(w, P, 3)
+            dt = time.perf_counter() - t0
+            rows.append((r["lpt"] > r["lb"], r["p2"] > r["lb"], r["final"] > r["lb"],
+                         (r["lpt"] - r["lb"]) / r["lb"], (r["p2"] - r["lb"]) / r["lb"],
+                         (r["final"] - r["lb"]) / r["lb"], dt))
+        a = np.array(rows, dtype=float)
+        out.append({"config": {"name": name, "n": n, "P": P, "kappa": kappa, "w_max": wmax,
+                               "instances": len(rows)},
+                    "above_lb": {"lpt": a[:, 0].mean(), "p2": a[:, 1].mean(),
+                                 "p2_p3": a[:, 2].mean()},
+                    "mean_gap_pct": {"lpt": 100 * a[:, 3].mean(), "p2": 100 * a[:, 4].mean(),
+                                     "p2_p3": 100 * a[:, 5].mean()},
+                    "ms_per_instance": {"mean": 1e3 * a[:, 6].mean(), "max": 1e3 * a[:, 6].max()}})
+    print(json.dumps({"measure": "HCC-IPO stage 1 (host) on the IPO ablation configurations",
+                      "results": out}))
 
 
 def measure_alpha(steps, warmup, n=8192, heads=64):
@@ -190,6 +283,10 @@ def main():
                     help="seconds of oracle work for the cpu_baseline sample (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--classify-bandwidth", action="store_true",
+                    help="time fm_classify_tiles on replicated c5 vectors (HBM roofline)")
+    ap.add_argument("--ipo-table", action="store_true",
+                    help="host chunk balancer on the IPO ablation configurations")
     ap.add_argument("--measure-alpha", action="store_true",
                     help="time partial against unmasked tiles on identical work")
     args = ap.parse_args()
@@ -203,6 +300,12 @@ def main():
         return
     if args.measure_alpha:
         measure_alpha(args.steps, args.warmup)
+        return
+    if args.ipo_table:
+        ipo_table()
+        return
+    if args.classify_bandwidth:
+        classify_bandwidth(args.steps, args.warmup)
         return
 
     import torch

@@ -167,6 +167,36 @@ fm_status fm_debug_expand_mask(const fm_problem* p, const fm_mask* m, int32_t b,
 /* Static description of a status code. */
 const char* fm_status_string(fm_status s);
 
+/* ---- Chunk balancing for context parallelism (host code, no GPU) ----------------------
+ * Stage 1 of HCC-IPO (FlashMask-3 page, §3.3 "Balance the work, not the length", and its
+ * IPO ablation table): n_chunks = ranks * kappa chunk loads are assigned to `ranks`
+ * ranks, exactly kappa each, minimising the makespan (largest rank load).  Phases: LPT
+ * under the cardinality constraint, exact pairwise repartition (P2, stages >= 2), and
+ * exact three-rank repartition (P3, stages = 3), repeated until no move improves or the
+ * makespan reaches LB = max(ceil(sum / ranks), max weight), which certifies optimality.
+ * The page gives no pseudo-code; the move order and tie-breaks are fixed in fm_ipo.cpp.
+ *
+ *   weights  host, [n_chunks] int64, each >= 0 (e.g. summed tile costs of a query chunk)
+ *   owner    host, [n_chunks] int32, written: the rank of each chunk
+ *   report   host, written: lb, makespans after LPT / after the first P2 pass / final,
+ *            certified (final == lb), moves (repartitions applied)
+ * Errors: FM_ERR_INVALID_ARG for null pointers, ranks or n_chunks <= 0, n_chunks not a
+ * multiple of ranks, a negative weight, stages outside 1..3; FM_ERR_UNSUPPORTED for
+ * kappa > FM_IPO_MAX_KAPPA (the exact repartitions search 3 * kappa chunks).  Runs
+ * synchronously on the calling thread; nothing is allocated on the device. */
+#define FM_IPO_MAX_KAPPA 16
+typedef struct {
+  int64_t lb;
+  int64_t makespan_lpt;
+  int64_t makespan_p2;
+  int64_t makespan;
+  int32_t certified;
+  int32_t moves;
+} fm_ipo_report;
+
+fm_status fm_ipo_balance(const int64_t* weights, int32_t n_chunks, int32_t ranks, int32_t stages,
+                         int32_t* owner, fm_ipo_report* report);
+
 #ifdef __cplusplus
 }
 #endif

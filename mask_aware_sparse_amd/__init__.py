@@ -20,6 +20,7 @@ import torch
 
 __all__ = [
     "FMError", "library", "library_path", "tile_shape", "workspace_size", "classify_tiles",
+    "ipo_balance", "fm_ipo_balance",
     "attn_fwd", "attn_bwd", "debug_expand_mask", "status_string",
     "fm_tile_shape", "fm_workspace_size", "fm_classify_tiles", "fm_attn_fwd", "fm_attn_bwd",
     "fm_debug_expand_mask", "fm_status_string",
@@ -155,12 +156,57 @@ def _workspace(nbytes, device, ws=None):
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
-def classify_tiles(lts, lte, uts, ute, block_q, block_k, heads_q=1, heads_kv=1, stream=None):
-    """Run fm_classify_tiles; returns a dict of device tensors (see fm_tiles in fm.h)."""
+class IpoReport(ctypes.Structure):
+    _fields_ = [("lb", ctypes.c_int64), ("makespan_lpt", ctypes.c_int64),
+                ("makespan_p2", ctypes.c_int64), ("makespan", ctypes.c_int64),
+                ("certified", ctypes.c_int32), ("moves", ctypes.c_int32)]
+
+
+def ipo_balance(weights, ranks, stages=3):
+    """fm_ipo_balance on host data: returns (owner int32 array, report dict)."""
+    import numpy as np
+    w = np.ascontiguousarray(np.asarray(weights, dtype=np.int64))
+    owner = np.empty(w.shape[0], dtype=np.int32)
+    rep = IpoReport()
+    lib = library()
+    lib.fm_ipo_balance.restype = _STATUS
+    lib.fm_ipo_balance.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(IpoReport)]
+    _check(lib.fm_ipo_balance(w.ctypes.data, int(w.shape[0]), int(ranks), int(stages),
+                              owner.ctypes.data, ctypes.byref(rep)), "fm_ipo_balance")
+    return owner, {"lb": rep.lb, "lpt": rep.makespan_lpt, "p2": rep.makespan_p2,
+                   "final": rep.makespan, "certified": bool(rep.certified),
+                   "moves": rep.moves}
+
+
+def classify_tiles(lts, lte, uts, ute, block_q, block_k, heads_q=1, heads_kv=1, stream=None,
+                   out=None, ws=None):
+    """Run fm_classify_tiles; returns a dict of device tensors (see fm_tiles in fm.h).
+    `out` (a dict as returned by an earlier call of the same shape) and `ws` (uint8 device
+    tensor of at least workspace_size(..., OP_CLASSIFY, block_q, block_k) bytes) may be
+    passed to reuse buffers."""
     B, N = lts.shape
     dev = lts.device
     nqb, nkb = -(-N // block_q), -(-N // block_k)
-    out = {
+    if out is None:
+        out = _tile_buffers(B, N, nqb, nkb, dev)
+    tiles = Tiles(*(out[n].data_ptr() if out[n].numel() else 0 for n, _ in Tiles._fields_))
+    p = _problem(B, heads_q, heads_kv, N)
+    nbytes = workspace_size(B, heads_q, heads_kv, N, OP_CLASSIFY, block_q, block_k)
+    if ws is None:
+        ws = _workspace(nbytes, dev)
+    elif ws.numel() < nbytes:
+        raise ValueError("workspace too small")
+    m = _mask(lts, lte, uts, ute)
+    _check(library().fm_classify_tiles(ctypes.byref(p), ctypes.byref(m), int(block_q),
+                                       int(block_k), ctypes.byref(tiles), _ptr(ws),
+                                       ctypes.c_size_t(nbytes), _stream(dev, stream)),
+           "fm_classify_tiles")
+    return out
+
+
+def _tile_buffers(B, N, nqb, nkb, dev):
+    return {
         "block_minmax": torch.empty((B, nkb, 8), dtype=torch.int32, device=dev),
         "tile_class": torch.empty((B, nqb, nkb), dtype=torch.uint8, device=dev),
         "q_queue": torch.empty((B, nqb, nkb), dtype=torch.int32, device=dev),
@@ -170,16 +216,6 @@ def classify_tiles(lts, lte, uts, ute, block_q, block_k, heads_q=1, heads_kv=1, 
         "q_order": torch.empty((B * nqb,), dtype=torch.int32, device=dev),
         "k_order": torch.empty((B * nkb,), dtype=torch.int32, device=dev),
     }
-    tiles = Tiles(*(out[n].data_ptr() if out[n].numel() else 0 for n, _ in Tiles._fields_))
-    p = _problem(B, heads_q, heads_kv, N)
-    nbytes = workspace_size(B, heads_q, heads_kv, N, OP_CLASSIFY, block_q, block_k)
-    ws = _workspace(nbytes, dev)
-    m = _mask(lts, lte, uts, ute)
-    _check(library().fm_classify_tiles(ctypes.byref(p), ctypes.byref(m), int(block_q),
-                                       int(block_k), ctypes.byref(tiles), _ptr(ws),
-                                       ctypes.c_size_t(nbytes), _stream(dev, stream)),
-           "fm_classify_tiles")
-    return out
 
 
 def _shapes(q, k):
@@ -269,3 +305,5 @@ fm_attn_fwd = attn_fwd
 fm_attn_bwd = attn_bwd
 fm_debug_expand_mask = debug_expand_mask
 fm_status_string = status_string
+
+fm_ipo_balance = ipo_balance

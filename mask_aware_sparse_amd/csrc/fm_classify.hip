@@ -160,15 +160,16 @@ __global__ __launch_bounds__(1024) void k_lpt_sort(const int32_t* __restrict__ c
                               (unsigned)i
                         : ~0ull;
   __syncthreads();
+  // bitonic network; each thread takes compare-exchange pairs (i, i + j) directly, so no
+  // lane idles on the half of the indices that are second members of a pair
   for (int k = 2; k <= P; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P; i += 1024) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const unsigned long long a = keys[i], c = keys[ixj];
-          const bool up = (i & k) == 0;
-          if ((a > c) == up) { keys[i] = c; keys[ixj] = a; }
-        }
+      for (int q = tid; q < (P >> 1); q += 1024) {
+        const int i = ((q & ~(j - 1)) << 1) | (q & (j - 1));
+        const int ixj = i + j;
+        const unsigned long long a = keys[i], c = keys[ixj];
+        const bool up = (i & k) == 0;
+        if ((a > c) == up) { keys[i] = c; keys[ixj] = a; }
       }
       __syncthreads();
     }

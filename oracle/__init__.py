@@ -25,8 +25,8 @@ Contents and the passage each part follows:
                 bound max(ceil(sum/P), max w) and a brute-force optimum
                 (FlashMask-3 page, §3.3 and the IPO ablation table).
 
-Readings taken where the pages are silent are listed in the design doc; the main ones:
-masked intervals are half-open; rows masked everywhere give O = 0, LSE = -inf,
+Readings taken where the pages are silent (the main ones): masked intervals are
+half-open; rows masked everywhere give O = 0, LSE = -inf,
 dQ = 0 and add nothing to dK/dV; query head h uses kv head h // (H_q/H_kv);
 the softmax scale is 1/sqrt(d) and appears in dQ and dK by the chain rule.
 
