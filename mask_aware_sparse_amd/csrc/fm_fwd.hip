@@ -46,8 +46,9 @@ __device__ __forceinline__ int perm_rows(int a) {
 // Lazy offset.  A row's exponent offset m (log2 units) is set from the true row max on
 // the row's first visible tile and afterwards only moves when a tile's exponentials
 // grow too large: p = 2^(s c - m) is formed against the current m, and only when a
-// lane's sum of p over the 32-key half exceeds 2^kSumLog2 (or is not finite) does the
-// wave take the slow path (row max, rescale of the accumulator and sums, recompute).
+// lane's sum of p over the 32-key half exceeds 2^64 (or is not finite), or the row has
+// no offset yet, does the wave take the slow path (row max, rescale of the accumulator
+// and sums, recompute), in which only the rows that triggered it move their offset.
 // bf16 and fp32 share their exponent range, so p up to 2^64 loses no relative precision,
 // and the accumulator stays below 2^(64 + 22 + a few) for any N <= 2^22.  The common
 // path therefore needs no per-tile row max at all.
@@ -271,7 +272,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
       mx = max_with_partner32(mx) * p.c;
-      const bool need = mx > m_use;
+      // only rows that asked for it move their offset, so a row's result never depends
+      // on which rows share its wave
+      const unsigned sf = slow ? 1u : 0u;
+      const auto sp = __builtin_amdgcn_permlane32_swap(sf, sf, false, false);
+      const bool need = (sp[0] | sp[1]) != 0u && mx > m_use;
       if (__builtin_amdgcn_ballot_w64(need)) {
         const float m_new = need ? mx : m_use;
         // 0 when m_use = -inf; lanes that keep their offset keep their sums

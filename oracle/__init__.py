@@ -21,6 +21,10 @@ Contents and the passage each part follows:
                 and the cost-descending (LPT) order (FlashMask-3 page, §3.1 tile
                 rule and KV Index Generator; §3.3 tile costs; FlashMask Guide,
                 "On-Chip Block-Skipping Logic").
+  localize.py   renumbering of the row bounds into one context-parallel rank's own
+                rows (FlashMask-3 page, §3.2, Theorem 1).
+  ipo.py        stage-1 chunk balancing over ranks: LPT, pairwise and three-rank
+                repartition (FlashMask-3 page, §3.3 and the IPO ablation table).
   schedule.py   list scheduling of weighted work items over P slots, the lower
                 bound max(ceil(sum/P), max w) and a brute-force optimum
                 (FlashMask-3 page, §3.3 and the IPO ablation table).
@@ -42,11 +46,14 @@ from .attention import (attention_fwd, attention_bwd, attention_rows, attention_
 from .tiles import (block_minmax, classify, tile_truth, queues, tile_costs, lpt_order,
                     ALPHA_PARTIAL, ALPHA_UNMASKED)
 from .schedule import list_schedule, lower_bound, brute_force_optimum
+from .localize import rank_rows, localize, localize_max_form, localize_vectors
+from . import ipo
 
 __all__ = [
     "masked_rows", "dense_mask", "visible_interval_to_vectors", "encode_causal",
     "encode_packed", "encode_dpo", "attention_fwd", "attention_bwd", "attention_rows",
     "attention_cols", "attention_fwd_bwd", "block_minmax", "classify", "tile_truth",
     "queues", "tile_costs", "lpt_order", "ALPHA_PARTIAL", "ALPHA_UNMASKED",
-    "list_schedule", "lower_bound", "brute_force_optimum",
+    "list_schedule", "lower_bound", "brute_force_optimum", "rank_rows", "localize",
+    "localize_max_form", "localize_vectors", "ipo",
 ]

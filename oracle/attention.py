@@ -84,12 +84,15 @@ def _row_block(qh, kh, vh, vecs, r0, r1, scale, dOh=None):
 
 
 def _check(q, k, v, vecs):
+    """Q [B][H_q][N_q][d], K and V [B][H_kv][N_k][d], vectors [B][N_k] (query-row bounds
+    in [0, N_q]); N_q = N_k for self-attention, N_q < N_k for one rank's share of the
+    query rows under context parallelism with localized vectors."""
     B, Hq, N, d = q.shape
     Bk, Hkv, Nk, dk = k.shape
-    assert (B, N, d) == (Bk, Nk, dk) and v.shape == k.shape
+    assert (B, d) == (Bk, dk) and v.shape == k.shape
     assert Hq % Hkv == 0
     for x in vecs:
-        assert np.asarray(x).shape == (B, N)
+        assert np.asarray(x).shape == (B, Nk)
     return B, Hq, Hkv, N, d, Hq // Hkv
 
 
@@ -122,8 +125,8 @@ def attention_fwd_bwd(q, k, v, do, lts, lte, uts, ute, scale=None, row_block=256
     O = np.zeros((B, Hq, N, d))
     LSE = np.full((B, Hq, N), -np.inf)
     dQ = np.zeros((B, Hq, N, d))
-    dK = np.zeros((B, Hkv, N, d))
-    dV = np.zeros((B, Hkv, N, d))
+    dK = np.zeros((B, Hkv, k.shape[2], d))
+    dV = np.zeros((B, Hkv, k.shape[2], d))
     for b in range(B):
         vb = tuple(np.asarray(x)[b] for x in vecs)
         for h in range(Hq):

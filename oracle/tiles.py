@@ -53,13 +53,15 @@ def block_minmax(vec, bk):
     return mn, mx
 
 
-def classify(lts, lte, uts, ute, bq, bk):
-    """Tile class [B][nQB][nKB] (uint8: 0 skip, 1 partial, 2 unmasked).
+def classify(lts, lte, uts, ute, bq, bk, nq=None):
+    """Tile class [B][nQB][nKB] (uint8: 0 skip, 1 partial, 2 unmasked) for nq query
+    rows (default: as many as key columns) and the vectors' key columns.
 
     For each batch row and KV block the rule is evaluated for all Q-blocks at once
     (q0, q1 as arrays)."""
-    B, N = np.asarray(lts).shape
-    nqb, nkb = _nblocks(N, bq), _nblocks(N, bk)
+    B, Nk = np.asarray(lts).shape
+    N = Nk if nq is None else nq
+    nqb, nkb = _nblocks(N, bq), _nblocks(Nk, bk)
     (mnLTS, mxLTS), (mnLTE, mxLTE), (mnUTS, mxUTS), (mnUTE, mxUTE) = (
         block_minmax(x, bk) for x in (lts, lte, uts, ute))
     q0 = np.arange(nqb, dtype=np.int64) * bq
@@ -75,19 +77,20 @@ def classify(lts, lte, uts, ute, bq, bk):
     return cls
 
 
-def tile_truth(lts, lte, uts, ute, bq, bk):
+def tile_truth(lts, lte, uts, ute, bq, bk, nq=None):
     """Brute force from the dense mask: 0 if every cell of the tile is hidden, 2 if
     none is, 1 otherwise.  The rule's class must agree wherever it says 0 or 2."""
     lts, lte, uts, ute = (np.asarray(x) for x in (lts, lte, uts, ute))
-    B, N = lts.shape
-    nqb, nkb = _nblocks(N, bq), _nblocks(N, bk)
+    B, Nk = lts.shape
+    N = Nk if nq is None else nq
+    nqb, nkb = _nblocks(N, bq), _nblocks(Nk, bk)
     out = np.zeros((B, nqb, nkb), dtype=np.uint8)
     for b in range(B):
         for qb in range(nqb):
             q0, q1 = qb * bq, min(qb * bq + bq, N)
             hid = masked_rows(lts[b], lte[b], uts[b], ute[b], q0, q1)
             for kb in range(nkb):
-                t = hid[:, kb * bk:min(kb * bk + bk, N)]
+                t = hid[:, kb * bk:min(kb * bk + bk, Nk)]
                 out[b, qb, kb] = SKIP if t.all() else (UNMASKED if not t.any() else PARTIAL)
     return out
 
