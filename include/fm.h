@@ -26,16 +26,21 @@
  *    memory and keeps no state between calls.
  *  - Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
  *    their kernels on it and return without synchronizing.
- *  - Layouts (all contiguous, row-major):
- *      Q, O, dO, dQ  bf16  [B][H_q][N][d]
- *      K, V, dK, dV  bf16  [B][H_kv][N][d]
- *      LSE           fp32  [B][H_q][N]      natural log; -inf for a row that sees no key
- *      LTS/LTE/UTS/UTE int32 [B][N]         one set per batch row, shared by all heads
+ *  - Layouts (all contiguous, row-major), with N_q = seqlen query rows and N_k =
+ *    seqlen_kv keys (N_k = N_q for self-attention):
+ *      Q, O, dO, dQ  bf16  [B][H_q][N_q][d]
+ *      K, V, dK, dV  bf16  [B][H_kv][N_k][d]
+ *      LSE           fp32  [B][H_q][N_q]    natural log; -inf for a row that sees no key
+ *      LTS/LTE/UTS/UTE int32 [B][N_k]       query-row bounds in [0, N_q], one set per
+ *                                           batch row, shared by all heads
+ *    N_q < N_k is one context-parallel rank's share of the query rows: its chunks,
+ *    concatenated in ascending order, against every key, with the vectors renumbered
+ *    into its own rows by fm_localize_mask (FlashMask-3 page, §3.2).
  *  - GQA.  Query head h reads kv head h / (H_q / H_kv).
  *  - Rows that see no key get O = 0, LSE = -inf, dQ = 0 and add nothing to dK/dV.
  *  - Errors.  Arguments are validated on the host before anything is enqueued; on an
  *    error nothing is launched and the outputs are untouched.  Vector values outside
- *    [0, N] are not checked and give unspecified (but memory-safe) results.  No C++
+ *    [0, N_q] are not checked and give unspecified (but memory-safe) results.  No C++
  *    exception crosses this interface.
  */
 #ifndef FM_H
@@ -58,9 +63,11 @@ typedef enum {
 
 typedef enum { FM_OP_CLASSIFY = 0, FM_OP_FWD = 1, FM_OP_BWD = 2 } fm_op;
 
-/* Problem shape.  batch, heads and seqlen may be 0 (nothing to do, FM_OK); head_dim must
- * be 128.  softmax_scale <= 0 selects 1/sqrt(head_dim).  Limits: seqlen < 2^30 and
- * batch * ceil(seqlen/block_q) and batch * ceil(seqlen/block_k) at most 8192 work blocks
+/* Problem shape.  batch, heads and the lengths may be 0 (nothing to do beyond zero
+ * outputs, FM_OK); head_dim must be 128.  softmax_scale <= 0 selects 1/sqrt(head_dim).
+ * seqlen is N_q; seqlen_kv is N_k, with 0 meaning N_k = N_q (so N_q > 0 rows without
+ * keys cannot be expressed; their result is O = 0, LSE = -inf).  Limits: N_q, N_k <= 2^22
+ * and batch * ceil(N_q/block_q) and batch * ceil(N_k/block_k) at most 8192 work blocks
  * (the LPT sort runs in one workgroup's LDS); larger problems return FM_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t batch;
@@ -69,9 +76,10 @@ typedef struct {
   int32_t seqlen;
   int32_t head_dim;
   float softmax_scale;
+  int32_t seqlen_kv;
 } fm_problem;
 
-/* The four column vectors, each int32 [B][N] in device memory. */
+/* The four column vectors, each int32 [B][N_k] in device memory. */
 typedef struct {
   const int32_t* lts;
   const int32_t* lte;
@@ -79,8 +87,8 @@ typedef struct {
   const int32_t* ute;
 } fm_mask;
 
-/* Outputs of fm_classify_tiles, all device memory, nQB = ceil(N/block_q),
- * nKB = ceil(N/block_k):
+/* Outputs of fm_classify_tiles, all device memory, nQB = ceil(N_q/block_q),
+ * nKB = ceil(N_k/block_k):
  *   block_minmax [B][nKB][8]  int32: min,max of LTS, LTE, UTS, UTE over the block's columns
  *   tile_class   [B][nQB][nKB] uint8: 0 skipped, 1 partial, 2 unmasked
  *   q_queue      [B][nQB][nKB] int32: per Q-block the non-skipped KV blocks, right to left
@@ -158,11 +166,36 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
                       void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream,
                       const fm_kernel_events* events);
 
-/* Dense expansion of rows [row0, row1) of batch row b: dense[(i-row0)*N + j] = 1 if the
- * mask hides (i, j), else 0 -- the same predicate the attention kernels apply on partial
- * tiles.  For checking only.  0 <= b < batch, 0 <= row0 <= row1 <= N. */
+/* Dense expansion of rows [row0, row1) of batch row b: dense[(i-row0)*N_k + j] = 1 if
+ * the mask hides (i, j), else 0 -- the same predicate the attention kernels apply on
+ * partial tiles.  For checking only.  0 <= b < batch, 0 <= row0 <= row1 <= N_q. */
 fm_status fm_debug_expand_mask(const fm_problem* p, const fm_mask* m, int32_t b, int32_t row0,
                                int32_t row1, uint8_t* dense, void* stream);
+
+/* Mask localization for one context-parallel rank (FlashMask-3 page, §3.2): the rank
+ * owns the query chunks [offsets[i], offsets[i] + chunk_len), i < n_chunks, offsets
+ * strictly ascending by at least chunk_len (non-overlapping), and every key.  Each bound
+ * x of the global vectors (`global`, int32 [B][N_k] with values in [0, N]) becomes the
+ * number of the rank's rows before global row x, sum_i clamp(x - offsets[i], 0,
+ * chunk_len), written to the arrays of `local` (int32 [B][N_k] each, values in
+ * [0, n_chunks * chunk_len]).
+ * Theorem 1 of the page: the local intervals select exactly the rank's rows of the global
+ * intervals, so attention with p->seqlen = n_chunks * chunk_len local query rows (the
+ * chunks' rows of Q concatenated in order) against all N_k keys gives those rows of the
+ * global result.  p->seqlen_kv (or p->seqlen when 0) is N_k; p->heads_* and head_dim are
+ * not used.  offsets: device int32 [n_chunks]; 1 <= n_chunks <= 4096, chunk_len >= 1.
+ * Offsets that are not ascending and non-overlapping give unspecified (but memory-safe)
+ * results. */
+typedef struct {
+  int32_t* lts;
+  int32_t* lte;
+  int32_t* uts;
+  int32_t* ute;
+} fm_mask_out;
+
+fm_status fm_localize_mask(const fm_problem* p, const fm_mask* global, const int32_t* offsets,
+                           int32_t n_chunks, int32_t chunk_len, const fm_mask_out* local,
+                           void* stream);
 
 /* Static description of a status code. */
 const char* fm_status_string(fm_status s);

@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "FMError", "library", "library_path", "tile_shape", "workspace_size", "classify_tiles",
-    "ipo_balance", "fm_ipo_balance",
+    "ipo_balance", "fm_ipo_balance", "localize_mask", "fm_localize_mask",
     "attn_fwd", "attn_bwd", "debug_expand_mask", "status_string",
     "fm_tile_shape", "fm_workspace_size", "fm_classify_tiles", "fm_attn_fwd", "fm_attn_bwd",
     "fm_debug_expand_mask", "fm_status_string",
@@ -46,7 +46,13 @@ class FMError(RuntimeError):
 class Problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32),
                 ("heads_kv", ctypes.c_int32), ("seqlen", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+                ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("seqlen_kv", ctypes.c_int32)]
+
+
+class MaskOut(ctypes.Structure):
+    _fields_ = [("lts", ctypes.c_void_p), ("lte", ctypes.c_void_p),
+                ("uts", ctypes.c_void_p), ("ute", ctypes.c_void_p)]
 
 
 class Mask(ctypes.Structure):
@@ -94,6 +100,8 @@ def library():
                              _P, PE], _STATUS),
             "fm_debug_expand_mask": ([PP, PM, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                       _P, _P], _STATUS),
+            "fm_localize_mask": ([PP, PM, _P, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.POINTER(MaskOut), _P], _STATUS),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -112,9 +120,9 @@ def _check(status, where):
         raise FMError(status, where)
 
 
-def _problem(batch, heads_q, heads_kv, seqlen, scale=None, head_dim=HEAD_DIM):
+def _problem(batch, heads_q, heads_kv, seqlen, scale=None, head_dim=HEAD_DIM, seqlen_kv=0):
     return Problem(int(batch), int(heads_q), int(heads_kv), int(seqlen), int(head_dim),
-                   float(scale) if scale is not None else 0.0)
+                   float(scale) if scale is not None else 0.0, int(seqlen_kv))
 
 
 def _mask(lts, lte, uts, ute):
@@ -140,9 +148,11 @@ def tile_shape(op: int):
     return bq.value, bk.value
 
 
-def workspace_size(batch, heads_q, heads_kv, seqlen, op, block_q=0, block_k=0, head_dim=HEAD_DIM):
+def workspace_size(batch, heads_q, heads_kv, seqlen, op, block_q=0, block_k=0, head_dim=HEAD_DIM,
+                   seqlen_kv=0):
+    """Workspace bytes for N_q = seqlen query rows and N_k = seqlen_kv keys (0: N_q)."""
     n = ctypes.c_size_t()
-    p = _problem(batch, heads_q, heads_kv, seqlen, head_dim=head_dim)
+    p = _problem(batch, heads_q, heads_kv, seqlen, head_dim=head_dim, seqlen_kv=seqlen_kv)
     _check(library().fm_workspace_size(ctypes.byref(p), int(op), int(block_q), int(block_k),
                                        ctypes.byref(n)), "fm_workspace_size")
     return n.value
@@ -180,19 +190,22 @@ def ipo_balance(weights, ranks, stages=3):
 
 
 def classify_tiles(lts, lte, uts, ute, block_q, block_k, heads_q=1, heads_kv=1, stream=None,
-                   out=None, ws=None):
+                   out=None, ws=None, seqlen_q=None):
     """Run fm_classify_tiles; returns a dict of device tensors (see fm_tiles in fm.h).
-    `out` (a dict as returned by an earlier call of the same shape) and `ws` (uint8 device
-    tensor of at least workspace_size(..., OP_CLASSIFY, block_q, block_k) bytes) may be
-    passed to reuse buffers."""
-    B, N = lts.shape
+    The vectors are [B][N_k]; `seqlen_q` is N_q (default N_k).  `out` (a dict as returned
+    by an earlier call of the same shape) and `ws` (uint8 device tensor of at least
+    workspace_size(..., OP_CLASSIFY, block_q, block_k) bytes) may be passed to reuse
+    buffers."""
+    B, Nk = lts.shape
+    N = Nk if seqlen_q is None else int(seqlen_q)
     dev = lts.device
-    nqb, nkb = -(-N // block_q), -(-N // block_k)
+    nqb, nkb = -(-N // block_q), -(-Nk // block_k)
     if out is None:
         out = _tile_buffers(B, N, nqb, nkb, dev)
     tiles = Tiles(*(out[n].data_ptr() if out[n].numel() else 0 for n, _ in Tiles._fields_))
-    p = _problem(B, heads_q, heads_kv, N)
-    nbytes = workspace_size(B, heads_q, heads_kv, N, OP_CLASSIFY, block_q, block_k)
+    p = _problem(B, heads_q, heads_kv, N, seqlen_kv=Nk)
+    nbytes = workspace_size(B, heads_q, heads_kv, N, OP_CLASSIFY, block_q, block_k,
+                            seqlen_kv=Nk)
     if ws is None:
         ws = _workspace(nbytes, dev)
     elif ws.numel() < nbytes:
@@ -219,12 +232,16 @@ def _tile_buffers(B, N, nqb, nkb, dev):
 
 
 def _shapes(q, k):
+    """(B, H_q, H_kv, N_q, N_k, d) from Q [B][H_q][N_q][d] and K [B][H_kv][N_k][d]."""
     if q.dim() != 4 or k.dim() != 4:
-        raise ValueError("expected Q [B][H_q][N][d] and K/V [B][H_kv][N][d]")
+        raise ValueError("expected Q [B][H_q][N_q][d] and K/V [B][H_kv][N_k][d]")
     B, Hq, N, d = q.shape
-    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+    if k.shape[0] != B or k.shape[3] != d:
         raise ValueError("Q and K/V shapes disagree")
-    return B, Hq, k.shape[1], N, d
+    if k.shape[2] == 0 and N > 0:
+        # fm_problem.seqlen_kv = 0 means "as many keys as rows"
+        raise ValueError("query rows without keys cannot be expressed (seqlen_kv = 0 means N_q)")
+    return B, Hq, k.shape[1], N, k.shape[2], d
 
 
 def _bf16(*ts):
@@ -249,14 +266,15 @@ def _events(ev):
 
 def attn_fwd(q, k, v, lts, lte, uts, ute, scale=None, ws=None, out=None, lse=None, stream=None,
              events=None):
-    """O (bf16 [B][H_q][N][d]) and LSE (fp32 [B][H_q][N], natural log) via fm_attn_fwd.
+    """O (bf16 [B][H_q][N_q][d]) and LSE (fp32 [B][H_q][N_q], natural log) via fm_attn_fwd;
+    K/V are [B][H_kv][N_k][d] and the vectors [B][N_k].
     `events`: optional (start, stop) torch.cuda.Event pair timing the attention kernel."""
     _bf16(q, k, v)
-    B, Hq, Hkv, N, d = _shapes(q, k)
+    B, Hq, Hkv, N, Nk, d = _shapes(q, k)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    p = _problem(B, Hq, Hkv, N, scale, head_dim=d)
-    nbytes = workspace_size(B, Hq, Hkv, N, OP_FWD, head_dim=d)
+    p = _problem(B, Hq, Hkv, N, scale, head_dim=d, seqlen_kv=Nk)
+    nbytes = workspace_size(B, Hq, Hkv, N, OP_FWD, head_dim=d, seqlen_kv=Nk)
     w = _workspace(nbytes, q.device, ws)
     m = _mask(lts, lte, uts, ute)
     _check(library().fm_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(m),
@@ -270,12 +288,12 @@ def attn_bwd(q, k, v, o, lse, dout, lts, lte, uts, ute, scale=None, ws=None, gra
     """(dQ, dK, dV) in bf16 via fm_attn_bwd.  `events`: optional (start, stop, start2,
     stop2) torch.cuda.Event objects timing the dK/dV kernel and the dQ kernel."""
     _bf16(q, k, v, o, dout)
-    B, Hq, Hkv, N, d = _shapes(q, k)
+    B, Hq, Hkv, N, Nk, d = _shapes(q, k)
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = grads
-    p = _problem(B, Hq, Hkv, N, scale, head_dim=d)
-    nbytes = workspace_size(B, Hq, Hkv, N, OP_BWD, head_dim=d)
+    p = _problem(B, Hq, Hkv, N, scale, head_dim=d, seqlen_kv=Nk)
+    nbytes = workspace_size(B, Hq, Hkv, N, OP_BWD, head_dim=d, seqlen_kv=Nk)
     w = _workspace(nbytes, q.device, ws)
     m = _mask(lts, lte, uts, ute)
     _check(library().fm_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
@@ -285,16 +303,34 @@ def attn_bwd(q, k, v, o, lse, dout, lts, lte, uts, ute, scale=None, ws=None, gra
     return dq, dk, dv
 
 
-def debug_expand_mask(lts, lte, uts, ute, b, row0, row1, stream=None):
-    """uint8 [row1-row0][N] dense expansion (1 = hidden) by the kernels' predicate."""
+def debug_expand_mask(lts, lte, uts, ute, b, row0, row1, stream=None, seqlen_q=None):
+    """uint8 [row1-row0][N_k] dense expansion (1 = hidden) by the kernels' predicate."""
     B, N = lts.shape
     dense = torch.empty((row1 - row0, N), dtype=torch.uint8, device=lts.device)
-    p = _problem(B, 1, 1, N)
+    p = _problem(B, 1, 1, N if seqlen_q is None else int(seqlen_q), seqlen_kv=N)
     m = _mask(lts, lte, uts, ute)
     _check(library().fm_debug_expand_mask(ctypes.byref(p), ctypes.byref(m), int(b), int(row0),
                                           int(row1), _ptr(dense), _stream(lts.device, stream)),
            "fm_debug_expand_mask")
     return dense
+
+
+def localize_mask(lts, lte, uts, ute, offsets, chunk_len, out=None, stream=None):
+    """fm_localize_mask: the vectors [B][N_k] renumbered into the rows of a rank that owns
+    the query chunks [offsets[i], offsets[i] + chunk_len) (offsets: int32 device tensor,
+    ascending, non-overlapping).  Returns four int32 tensors [B][N_k]."""
+    B, N = lts.shape
+    if offsets.dtype != torch.int32 or not offsets.is_contiguous() or offsets.dim() != 1:
+        raise ValueError("offsets must be a contiguous int32 tensor [n_chunks]")
+    if out is None:
+        out = tuple(torch.empty_like(lts) for _ in range(4))
+    p = _problem(B, 1, 1, 0, seqlen_kv=N)
+    m = _mask(lts, lte, uts, ute)
+    mo = MaskOut(*(t.data_ptr() for t in out))
+    _check(library().fm_localize_mask(ctypes.byref(p), ctypes.byref(m), _ptr(offsets),
+                                      int(offsets.numel()), int(chunk_len), ctypes.byref(mo),
+                                      _stream(lts.device, stream)), "fm_localize_mask")
+    return out
 
 
 # The C names, for callers that prefer them.
@@ -304,6 +340,7 @@ fm_classify_tiles = classify_tiles
 fm_attn_fwd = attn_fwd
 fm_attn_bwd = attn_bwd
 fm_debug_expand_mask = debug_expand_mask
+fm_localize_mask = localize_mask
 fm_status_string = status_string
 
 fm_ipo_balance = ipo_balance

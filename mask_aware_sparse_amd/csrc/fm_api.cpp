@@ -17,25 +17,32 @@ inline bool pow2_in(int32_t x, int32_t lo, int32_t hi) {
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// N_q (query rows) and N_k (keys); N_k = N_q unless seqlen_kv is set.
+inline int32_t nq_of(const fm_problem* p) { return p->seqlen; }
+inline int32_t nk_of(const fm_problem* p) { return p->seqlen_kv > 0 ? p->seqlen_kv : p->seqlen; }
+
 // Problem checks shared by every entry point.
 fm_status check_problem(const fm_problem* p) {
   if (!p) return FM_ERR_INVALID_ARG;
-  if (p->batch < 0 || p->heads_q < 0 || p->heads_kv < 1 || p->seqlen < 0)
+  if (p->batch < 0 || p->heads_q < 0 || p->heads_kv < 1 || p->seqlen < 0 || p->seqlen_kv < 0)
     return FM_ERR_INVALID_ARG;
   if (p->heads_q % p->heads_kv != 0) return FM_ERR_INVALID_ARG;
   if (!(p->softmax_scale <= 0.f || std::isfinite(p->softmax_scale))) return FM_ERR_INVALID_ARG;
   if (p->head_dim != fm::kHeadDim) return FM_ERR_UNSUPPORTED;
-  if (p->seqlen > (1 << 22)) return FM_ERR_UNSUPPORTED;  // per-head buffers < 2 GiB
+  // per-head buffers < 2 GiB
+  if (nq_of(p) > (1 << 22) || nk_of(p) > (1 << 22)) return FM_ERR_UNSUPPORTED;
   return FM_OK;
 }
 
+// Nothing to compute or write at all.  (N_q = 0 with keys still zeroes dK/dV; N_k = 0
+// with rows still writes O = 0 and LSE = -inf.)
 bool empty_problem(const fm_problem* p) {
-  return p->batch == 0 || p->seqlen == 0 || p->heads_q == 0;
+  return p->batch == 0 || p->heads_q == 0 || (nq_of(p) == 0 && nk_of(p) == 0);
 }
 
 fm_status check_mask(const fm_problem* p, const fm_mask* m) {
   if (!m) return FM_ERR_INVALID_ARG;
-  if ((int64_t)p->batch * p->seqlen == 0) return FM_OK;
+  if ((int64_t)p->batch * nk_of(p) == 0) return FM_OK;
   if (!m->lts || !m->lte || !m->uts || !m->ute) return FM_ERR_INVALID_ARG;
   return FM_OK;
 }
@@ -48,7 +55,7 @@ struct Blocks {
   int64_t nQB, nKB;
 };
 Blocks blocks(const fm_problem* p, int bq, int bk) {
-  return {cdiv(p->seqlen, bq), cdiv(p->seqlen, bk)};
+  return {cdiv(nq_of(p), bq), cdiv(nk_of(p), bk)};
 }
 
 fm_status check_sort_limits(const fm_problem* p, const Blocks& nb) {
@@ -90,7 +97,7 @@ struct BwdWs {
 };
 BwdWs bwd_ws(const fm_problem* p, const Blocks& nk, const Blocks& nq) {
   BwdWs w{};
-  const size_t B = p->batch, rq = B * p->heads_q * p->seqlen, rk = B * p->heads_kv * p->seqlen;
+  const size_t B = p->batch, rq = B * p->heads_q * nq_of(p), rk = B * p->heads_kv * nk_of(p);
   size_t off = 0;
   w.mm_k = off; off += align_up(B * nk.nKB * 8 * 4);
   w.k_queue = off; off += align_up(B * nk.nKB * nk.nQB * 4);
@@ -212,7 +219,7 @@ fm_status fm_classify_tiles(const fm_problem* p, const fm_mask* m, int32_t block
   if (!out) return FM_ERR_INVALID_ARG;
   Blocks nb = blocks(p, block_q, block_k);
   if ((st = check_sort_limits(p, nb)) != FM_OK) return st;
-  if (p->batch == 0 || p->seqlen == 0) return FM_OK;
+  if (p->batch == 0 || (nq_of(p) == 0 && nk_of(p) == 0)) return FM_OK;
   if (!out->block_minmax || !out->tile_class || !out->q_queue || !out->q_count ||
       !out->k_queue || !out->k_count || !out->q_order || !out->k_order)
     return FM_ERR_INVALID_ARG;
@@ -228,7 +235,8 @@ fm_status fm_classify_tiles(const fm_problem* p, const fm_mask* m, int32_t block
   t.k_queue = out->k_queue;
   t.k_count = out->k_count;
   t.k_cost = at<int32_t>(ws, w.k_cost);
-  hipError_t e = fm::launch_classify(mask_ptrs(m), p->batch, p->seqlen, block_q, block_k, t, s);
+  hipError_t e =
+      fm::launch_classify(mask_ptrs(m), p->batch, nq_of(p), nk_of(p), block_q, block_k, t, s);
   if (e == hipSuccess) e = fm::launch_lpt_sort(t.q_cost, out->q_order, (int)(p->batch * nb.nQB), s);
   if (e == hipSuccess) e = fm::launch_lpt_sort(t.k_cost, out->k_order, (int)(p->batch * nb.nKB), s);
   return hip_status(e);
@@ -244,7 +252,9 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
   if ((st = check_sort_limits(p, nb)) != FM_OK) return st;
   if ((st = check_grid(p, nb, blocks(p, fm::kBwdBlockQ, fm::kBwdBlockK))) != FM_OK) return st;
   if (empty_problem(p)) return FM_OK;
-  if (!q || !k || !v || !o || !lse) return FM_ERR_INVALID_ARG;
+  // query-side arrays are needed when there are rows, key-side ones when there are keys
+  if (nq_of(p) > 0 && (!q || !o || !lse)) return FM_ERR_INVALID_ARG;
+  if (nk_of(p) > 0 && (!k || !v)) return FM_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FM_ERR_INVALID_ARG;
   FwdWs w = fwd_ws(p, nb);
   if ((st = check_ws(ws, ws_bytes, w.total)) != FM_OK) return st;
@@ -255,15 +265,15 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
   t.q_queue = at<int32_t>(ws, w.q_queue);
   t.q_count = at<int32_t>(ws, w.q_count);
   t.q_cost = at<int32_t>(ws, w.q_cost);
-  hipError_t e = fm::launch_classify(mask_ptrs(m), p->batch, p->seqlen, fm::kFwdBlockQ,
-                                     fm::kFwdBlockK, t, s);
+  hipError_t e = fm::launch_classify(mask_ptrs(m), p->batch, nq_of(p), nk_of(p),
+                                     fm::kFwdBlockQ, fm::kFwdBlockK, t, s);
   int32_t* order = at<int32_t>(ws, w.q_order);
   if (e == hipSuccess) e = fm::launch_lpt_sort(t.q_cost, order, (int)(p->batch * nb.nQB), s);
   if (e == hipSuccess) {
     fm::FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.m = mask_ptrs(m); a.o = o; a.lse = lse;
     a.q_queue = t.q_queue; a.q_count = t.q_count; a.q_order = order;
-    a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.N = p->seqlen;
+    a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.Nq = nq_of(p); a.Nk = nk_of(p);
     a.nQB = (int)nb.nQB; a.nKB = (int)nb.nKB;
     a.scale = scale_of(p);
     e = fm::launch_fwd(a, s, ev_start(events), ev_stop(events));
@@ -284,7 +294,8 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   if ((st = check_sort_limits(p, nq)) != FM_OK) return st;
   if ((st = check_grid(p, nq, nk)) != FM_OK) return st;
   if (empty_problem(p)) return FM_OK;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FM_ERR_INVALID_ARG;
+  if (nq_of(p) > 0 && (!q || !o || !lse || !dout || !dq)) return FM_ERR_INVALID_ARG;
+  if (nk_of(p) > 0 && (!k || !v || !dk || !dv)) return FM_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return FM_ERR_INVALID_ARG;
@@ -304,11 +315,12 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   tq.q_cost = at<int32_t>(ws, w.q_cost);
   int32_t* k_order = at<int32_t>(ws, w.k_order);
   int32_t* q_order = at<int32_t>(ws, w.q_order);
-  hipError_t e = fm::launch_classify(mask_ptrs(m), p->batch, p->seqlen, fm::kBwdBlockQ,
+  hipError_t e = fm::launch_classify(mask_ptrs(m), p->batch, nq_of(p), nk_of(p), fm::kBwdBlockQ,
                                      fm::kBwdBlockK, tk, s);
   if (e == hipSuccess) e = fm::launch_lpt_sort(tk.k_cost, k_order, (int)(p->batch * nk.nKB), s);
   if (e == hipSuccess)
-    e = fm::launch_classify(mask_ptrs(m), p->batch, p->seqlen, fm::kFwdBlockQ, fm::kFwdBlockK,
+    e = fm::launch_classify(mask_ptrs(m), p->batch, nq_of(p), nk_of(p), fm::kFwdBlockQ,
+                            fm::kFwdBlockK,
                             tq, s);
   if (e == hipSuccess) e = fm::launch_lpt_sort(tq.q_cost, q_order, (int)(p->batch * nq.nQB), s);
   if (e == hipSuccess) {
@@ -319,7 +331,7 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
     a.q_queue = tq.q_queue; a.q_count = tq.q_count; a.q_order = q_order;
     a.lse2 = at<float>(ws, w.lse2); a.delta = at<float>(ws, w.delta);
     if (w.acc) { a.dk_acc = at<float>(ws, w.dk); a.dv_acc = at<float>(ws, w.dv); }
-    a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.N = p->seqlen;
+    a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.Nq = nq_of(p); a.Nk = nk_of(p);
     a.nQB_k = (int)nk.nQB; a.nKB_k = (int)nk.nKB;
     a.nQB_q = (int)nq.nQB; a.nKB_q = (int)nq.nKB;
     a.scale = scale_of(p);
@@ -340,12 +352,31 @@ fm_status fm_debug_expand_mask(const fm_problem* p, const fm_mask* m, int32_t b,
   fm_status st = check_problem(p);
   if (st != FM_OK) return st;
   if ((st = check_mask(p, m)) != FM_OK) return st;
-  if (b < 0 || b >= p->batch || row0 < 0 || row1 < row0 || row1 > p->seqlen)
+  if (b < 0 || b >= p->batch || row0 < 0 || row1 < row0 || row1 > nq_of(p))
     return FM_ERR_INVALID_ARG;
-  if (row1 == row0) return FM_OK;
+  if (row1 == row0 || nk_of(p) == 0) return FM_OK;
   if (!dense) return FM_ERR_INVALID_ARG;
-  return hip_status(fm::launch_expand_mask(mask_ptrs(m), b, p->seqlen, row0, row1, dense,
+  return hip_status(fm::launch_expand_mask(mask_ptrs(m), b, nk_of(p), row0, row1, dense,
                                            static_cast<hipStream_t>(stream)));
+}
+
+fm_status fm_localize_mask(const fm_problem* p, const fm_mask* global, const int32_t* offsets,
+                           int32_t n_chunks, int32_t chunk_len, const fm_mask_out* local,
+                           void* stream) {
+  if (!p || !global || !local) return FM_ERR_INVALID_ARG;
+  if (p->batch < 0 || p->seqlen < 0 || p->seqlen_kv < 0) return FM_ERR_INVALID_ARG;
+  if (n_chunks < 1 || chunk_len < 1) return FM_ERR_INVALID_ARG;
+  if (n_chunks > 4096 || nk_of(p) > (1 << 22)) return FM_ERR_UNSUPPORTED;
+  if ((int64_t)n_chunks * chunk_len > (1 << 22)) return FM_ERR_UNSUPPORTED;
+  const int64_t cols = (int64_t)p->batch * nk_of(p);
+  if (cols == 0) return FM_OK;
+  if (!offsets || !global->lts || !global->lte || !global->uts || !global->ute || !local->lts ||
+      !local->lte || !local->uts || !local->ute)
+    return FM_ERR_INVALID_ARG;
+  return hip_status(fm::launch_localize(mask_ptrs(global), offsets, n_chunks, chunk_len,
+                                        fm::MaskOut{local->lts, local->lte, local->uts,
+                                                    local->ute},
+                                        cols, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -100,7 +100,7 @@ struct DkdvParams {
   float* __restrict__ dv_acc;
   bf16* __restrict__ dk;       // bf16 outputs (nch == 1)
   bf16* __restrict__ dv;
-  int B, Hq, Hkv, N, nQB, nKB, hc, nch;
+  int B, Hq, Hkv, Nq, Nk, nQB, nKB, hc, nch;  // Nq query rows, Nk keys
   float c;      // scale * log2(e)
   float scale;  // softmax scale (applied to dK)
 };
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(512, 2) void k_attn_bwd_dkdv(DkdvParams p) {
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int N = p.N;
+  const int N = p.Nk, Nq = p.Nq;  // N: keys (and mask columns)
 
   const int per = p.Hkv * p.nch;
   const int r = blockIdx.x / per, rem = blockIdx.x - r * per;
@@ -181,16 +181,17 @@ __global__ __launch_bounds__(512, 2) void k_attn_bwd_dkdv(DkdvParams p) {
   auto load_step = [&](int hi, int it) {
     const int h = h0 + hi;
     const int qb = queue[it] & 0x7fffffff;
-    const size_t base = (size_t)(b * p.Hq + h) * N;
-    const rsrc_t qrs = make_rsrc(p.q + base * D, head_bytes);
-    const rsrc_t ors = make_rsrc(p.dout + base * D, head_bytes);
+    const size_t base = (size_t)(b * p.Hq + h) * Nq;
+    const uint32_t q_bytes = (uint32_t)Nq * D * 2;
+    const rsrc_t qrs = make_rsrc(p.q + base * D, q_bytes);
+    const rsrc_t ors = make_rsrc(p.dout + base * D, q_bytes);
     const uint32_t off = (uint32_t)(qb * BQ + cp_row) * (D * 2) + cp_ch * 16;
     qst = buf_load16(qrs, off, 0);
     ost = buf_load16(ors, off, 0);
     if (tid < BQ) {
       const uint32_t ro = (uint32_t)(qb * BQ + tid) * 4;
-      lst = buf_load4(make_rsrc(p.lse2 + base, (uint32_t)N * 4), ro, 0);
-      dst_ = buf_load4(make_rsrc(p.delta + base, (uint32_t)N * 4), ro, 0);
+      lst = buf_load4(make_rsrc(p.lse2 + base, (uint32_t)Nq * 4), ro, 0);
+      dst_ = buf_load4(make_rsrc(p.delta + base, (uint32_t)Nq * 4), ro, 0);
     }
   };
   auto store_step = [&](int buf) {
@@ -355,7 +356,7 @@ struct DqParams {
   const int32_t* __restrict__ q_queue;
   const int32_t* __restrict__ q_count;
   const int32_t* __restrict__ q_order;
-  int B, Hq, Hkv, N, nQB, nKB;
+  int B, Hq, Hkv, Nq, Nk, nQB, nKB;  // Nq query rows, Nk keys
   float c;      // scale * log2(e)
   float scale;  // softmax scale (applied to dQ)
 };
@@ -373,12 +374,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   const int kvh = h / (p.Hq / p.Hkv);
   const int n_tiles = p.q_count[2 * item] + p.q_count[2 * item + 1];
   const int32_t* queue = p.q_queue + (size_t)item * p.nKB;
-  const int N = p.N;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const size_t qbase = (size_t)(b * p.Hq + h) * N;
+  const int N = p.Nk, Nq = p.Nq;  // N: keys (and mask columns)
+  const uint32_t head_bytes = (uint32_t)N * D * 2, q_bytes = (uint32_t)Nq * D * 2;
+  const size_t qbase = (size_t)(b * p.Hq + h) * Nq;
   const rsrc_t kr_ = make_rsrc(p.k + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
   const rsrc_t vr_ = make_rsrc(p.v + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
-  const uint32_t vec_bytes = (uint32_t)N * 4;
+  const uint32_t vec_bytes = (uint32_t)N * 4, row_bytes = (uint32_t)Nq * 4;
   const size_t mrow = (size_t)b * N;
   const rsrc_t m0 = make_rsrc(p.m.lts + mrow, vec_bytes), m1 = make_rsrc(p.m.lte + mrow, vec_bytes);
   const rsrc_t m2 = make_rsrc(p.m.uts + mrow, vec_bytes), m3 = make_rsrc(p.m.ute + mrow, vec_bytes);
@@ -386,11 +387,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
 
   const int row = qb * BQ + wave * 32 + l32;
 
-  // Q^T and dO^T operands: lane holds row `row`, d = s*16 + hh*8 .. +7 (rows past N read 0)
+  // Q^T and dO^T operands: lane holds row `row`, d = s*16 + hh*8 .. +7 (rows past Nq read 0)
   bf16x8 qr[8], orr[8];
   {
-    const rsrc_t qrs = make_rsrc(p.q + qbase * D, head_bytes);
-    const rsrc_t ors = make_rsrc(p.dout + qbase * D, head_bytes);
+    const rsrc_t qrs = make_rsrc(p.q + qbase * D, q_bytes);
+    const rsrc_t ors = make_rsrc(p.dout + qbase * D, q_bytes);
     const uint32_t off = (uint32_t)row * (D * 2) + hh * 16;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -402,7 +403,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   // 16-wide d slice) and the LSE in log2 units; both go to memory for the dK/dV kernel.
   float d_row;
   {
-    const rsrc_t ors = make_rsrc(p.o + qbase * D, head_bytes);
+    const rsrc_t ors = make_rsrc(p.o + qbase * D, q_bytes);
     const uint32_t off = (uint32_t)row * (D * 2) + hh * 16;
     float part = 0.f;
 #pragma unroll
@@ -417,11 +418,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
     d_row = sum_with_partner32(part);
   }
   const float lse_nat =
-      __uint_as_float(buf_load4(make_rsrc(p.lse + qbase, vec_bytes), (uint32_t)row * 4, 0));
+      __uint_as_float(buf_load4(make_rsrc(p.lse + qbase, row_bytes), (uint32_t)row * 4, 0));
   const float lse_row = lse_nat == -INFINITY ? INFINITY : lse_nat * kLog2e;
-  if (hh == 0) {  // rows past N are dropped by the buffer bounds
-    buf_store4(__float_as_uint(lse_row), make_rsrc(p.lse2 + qbase, vec_bytes), (uint32_t)row * 4, 0);
-    buf_store4(__float_as_uint(d_row), make_rsrc(p.delta + qbase, vec_bytes), (uint32_t)row * 4, 0);
+  if (hh == 0) {  // rows past Nq are dropped by the buffer bounds
+    buf_store4(__float_as_uint(lse_row), make_rsrc(p.lse2 + qbase, row_bytes), (uint32_t)row * 4, 0);
+    buf_store4(__float_as_uint(d_row), make_rsrc(p.delta + qbase, row_bytes), (uint32_t)row * 4, 0);
   }
 
   f32x16 qacc[4];
@@ -552,8 +553,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
     lds_barrier();
   }
 
-  // ---- dQ = scale * acc (bf16); rows past N are dropped by the buffer bounds ----
-  const rsrc_t dqr = make_rsrc(p.dq + qbase * D, head_bytes);
+  // ---- dQ = scale * acc (bf16); rows past Nq are dropped by the buffer bounds ----
+  const rsrc_t dqr = make_rsrc(p.dq + qbase * D, q_bytes);
   const uint32_t ooff = (uint32_t)row * (D * 2) + hh * 8;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
@@ -575,8 +576,8 @@ unsigned grid_for(size_t n, unsigned cap) {
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
-  if (a.B == 0 || a.N == 0 || a.Hq == 0) return hipSuccess;
-  const size_t rows_k = (size_t)a.B * a.Hkv * a.N;
+  if (a.B == 0 || a.Hq == 0 || (a.Nq == 0 && a.Nk == 0)) return hipSuccess;
+  const size_t rows_k = (size_t)a.B * a.Hkv * a.Nk;
   const int g = a.Hq / a.Hkv;
   const int hc = g < kBwdHeadChunk ? g : kBwdHeadChunk;
   const int nch = (g + hc - 1) / hc;
@@ -595,15 +596,16 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   q.m = a.m;
   q.dq = static_cast<bf16*>(a.dq);
   q.q_queue = a.q_queue; q.q_count = a.q_count; q.q_order = a.q_order;
-  q.B = a.B; q.Hq = a.Hq; q.Hkv = a.Hkv; q.N = a.N; q.nQB = a.nQB_q; q.nKB = a.nKB_q;
+  q.B = a.B; q.Hq = a.Hq; q.Hkv = a.Hkv; q.Nq = a.Nq; q.Nk = a.Nk;
+  q.nQB = a.nQB_q; q.nKB = a.nKB_q;
   q.c = c;
   q.scale = a.scale;
   const unsigned qgrid = (unsigned)a.B * (unsigned)a.nQB_q * (unsigned)a.Hq;
   if (ev.dq_start) (void)hipEventRecord(ev.dq_start, s);
-  hipLaunchKernelGGL(k_attn_bwd_dq, dim3(qgrid), dim3(256), 0, s, q);
+  if (qgrid > 0) hipLaunchKernelGGL(k_attn_bwd_dq, dim3(qgrid), dim3(256), 0, s, q);
   if (ev.dq_stop) (void)hipEventRecord(ev.dq_stop, s);
 
-  if (nch > 1) {
+  if (nch > 1 && rows_k > 0) {
     hipLaunchKernelGGL(k_zero, dim3(grid_for(rows_k * D / 4, 8192)), dim3(256), 0, s,
                        reinterpret_cast<float4*>(a.dk_acc), rows_k * D / 4);
     hipLaunchKernelGGL(k_zero, dim3(grid_for(rows_k * D / 4, 8192)), dim3(256), 0, s,
@@ -622,17 +624,18 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   p.dv_acc = a.dv_acc;
   p.dk = static_cast<bf16*>(a.dk);
   p.dv = static_cast<bf16*>(a.dv);
-  p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N; p.nQB = a.nQB_k; p.nKB = a.nKB_k;
+  p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
+  p.nQB = a.nQB_k; p.nKB = a.nKB_k;
   p.hc = hc;
   p.nch = nch;
   p.c = c;
   p.scale = a.scale;
   const unsigned grid = (unsigned)a.B * (unsigned)a.nKB_k * (unsigned)a.Hkv * (unsigned)nch;
   if (ev.dkdv_start) (void)hipEventRecord(ev.dkdv_start, s);
-  hipLaunchKernelGGL(k_attn_bwd_dkdv, dim3(grid), dim3(64 * dkdv::kWaves), 0, s, p);
+  if (grid > 0) hipLaunchKernelGGL(k_attn_bwd_dkdv, dim3(grid), dim3(64 * dkdv::kWaves), 0, s, p);
   if (ev.dkdv_stop) (void)hipEventRecord(ev.dkdv_stop, s);
 
-  if (nch > 1) {
+  if (nch > 1 && rows_k > 0) {
     hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_k * D / 8, 16384)), dim3(256), 0, s,
                        a.dk_acc, static_cast<bf16*>(a.dk), a.scale, rows_k * D / 8);
     hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_k * D / 8, 16384)), dim3(256), 0, s,

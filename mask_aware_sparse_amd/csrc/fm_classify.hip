@@ -15,13 +15,13 @@ namespace fm {
 
 // ---- A2: block min/max of the four vectors -------------------------------------
 // One wave per (b, kb); lane l reduces columns kb*bk + l + 64t.
-__global__ __launch_bounds__(64) void k_block_minmax(MaskPtrs m, int N, int nKB, int bk,
+__global__ __launch_bounds__(64) void k_block_minmax(MaskPtrs m, int Nk, int nKB, int bk,
                                                      int32_t* __restrict__ mm) {
   const int bkb = blockIdx.x;
   const int b = bkb / nKB, kb = bkb - b * nKB;
   const int lane = threadIdx.x;
-  const size_t rowoff = (size_t)b * N;
-  const int c0 = kb * bk, c1 = min(c0 + bk, N);
+  const size_t rowoff = (size_t)b * Nk;
+  const int c0 = kb * bk, c1 = min(c0 + bk, Nk);
   int v[8] = {INT_MAX, INT_MIN, INT_MAX, INT_MIN, INT_MAX, INT_MIN, INT_MAX, INT_MIN};
   for (int c = c0 + lane; c < c1; c += 64) {
     int x0 = m.lts[rowoff + c], x1 = m.lte[rowoff + c];
@@ -77,7 +77,7 @@ __device__ __forceinline__ ScanResult block_scan_256(bool flag, bool sub, int* s
 }
 
 // ---- A3: classes and per-Q-block queues (KV blocks right to left) --------------
-__global__ __launch_bounds__(256) void k_classify_q(const int32_t* __restrict__ mm, int N,
+__global__ __launch_bounds__(256) void k_classify_q(const int32_t* __restrict__ mm, int Nq,
                                                     int nQB, int nKB, int bq,
                                                     uint8_t* __restrict__ cls,
                                                     int32_t* __restrict__ q_queue,
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void k_classify_q(const int32_t* __restrict__ 
   __shared__ int sh_cnt[4], sh_sub[4];
   const int row = blockIdx.x;  // b * nQB + qb
   const int b = row / nQB, qb = row - b * nQB;
-  const int q0 = qb * bq, q1 = min(q0 + bq, N);
+  const int q0 = qb * bq, q1 = min(q0 + bq, Nq);
   const int tid = threadIdx.x;
   int base = 0, np = 0;
   for (int c0 = 0; c0 < nKB; c0 += 256) {
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void k_classify_q(const int32_t* __restrict__ 
 }
 
 // ---- A3 (backward direction): per-KV-block queues of Q-blocks, ascending -----------
-__global__ __launch_bounds__(256) void k_classify_k(const int32_t* __restrict__ mm, int N,
+__global__ __launch_bounds__(256) void k_classify_k(const int32_t* __restrict__ mm, int Nq,
                                                     int nQB, int nKB, int bq,
                                                     int32_t* __restrict__ k_queue,
                                                     int32_t* __restrict__ k_count,
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void k_classify_k(const int32_t* __restrict__ 
     const int qb = c0 + tid;
     const bool valid = qb < nQB;
     int c = 0;
-    if (valid) c = tile_class(v, qb * bq, min(qb * bq + bq, N));
+    if (valid) c = tile_class(v, qb * bq, min(qb * bq + bq, Nq));
     ScanResult s = block_scan_256(valid && c != 0, c == 1, sh_cnt, sh_sub);
     if (valid && c != 0)
       k_queue[(size_t)row * nQB + base + s.off] = qb | (c == 1 ? (int)0x80000000 : 0);
@@ -178,32 +178,35 @@ __global__ __launch_bounds__(1024) void k_lpt_sort(const int32_t* __restrict__ c
 }
 
 // ---- Dense expansion through the kernels' own predicate (checking only) ----------
-__global__ __launch_bounds__(256) void k_expand_mask(MaskPtrs m, int b, int N, int row0,
+__global__ __launch_bounds__(256) void k_expand_mask(MaskPtrs m, int b, int Nk, int row0,
                                                      int row1, uint8_t* __restrict__ dense) {
   const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= N) return;
-  const size_t o = (size_t)b * N + j;
+  if (j >= Nk) return;
+  const size_t o = (size_t)b * Nk + j;
   const int lts = m.lts[o], lte = m.lte[o], uts = m.uts[o], ute = m.ute[o];
   for (int w = blockIdx.y; row0 + 32 * w < row1; w += gridDim.y) {
     const int r0 = row0 + 32 * w;
     const uint32_t word = hidden_rows32(lts, lte, uts, ute, r0);
     const int nr = min(32, row1 - r0);
     for (int r = 0; r < nr; ++r)
-      dense[(size_t)(r0 - row0 + r) * N + j] = (uint8_t)((word >> r) & 1u);
+      dense[(size_t)(r0 - row0 + r) * Nk + j] = (uint8_t)((word >> r) & 1u);
   }
 }
 
 // ---- host launchers --------------------------------------------------------------
-hipError_t launch_classify(const MaskPtrs& m, int B, int N, int bq, int bk, const TileOut& out,
-                           hipStream_t s) {
-  const int nQB = (N + bq - 1) / bq, nKB = (N + bk - 1) / bk;
-  if (B == 0 || N == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_block_minmax, dim3(B * nKB), dim3(64), 0, s, m, N, nKB, bk, out.minmax);
-  if (out.tile_class || out.q_queue)
-    hipLaunchKernelGGL(k_classify_q, dim3(B * nQB), dim3(256), 0, s, out.minmax, N, nQB, nKB,
+hipError_t launch_classify(const MaskPtrs& m, int B, int Nq, int Nk, int bq, int bk,
+                           const TileOut& out, hipStream_t s) {
+  const int nQB = (Nq + bq - 1) / bq, nKB = (Nk + bk - 1) / bk;
+  if (B == 0) return hipSuccess;
+  if (nKB > 0)
+    hipLaunchKernelGGL(k_block_minmax, dim3(B * nKB), dim3(64), 0, s, m, Nk, nKB, bk,
+                       out.minmax);
+  // with no KV block a Q-block's queue is empty; with no Q-block a KV block's is
+  if ((out.tile_class || out.q_queue) && nQB > 0)
+    hipLaunchKernelGGL(k_classify_q, dim3(B * nQB), dim3(256), 0, s, out.minmax, Nq, nQB, nKB,
                        bq, out.tile_class, out.q_queue, out.q_count, out.q_cost);
-  if (out.k_queue)
-    hipLaunchKernelGGL(k_classify_k, dim3(B * nKB), dim3(256), 0, s, out.minmax, N, nQB, nKB,
+  if (out.k_queue && nKB > 0)
+    hipLaunchKernelGGL(k_classify_k, dim3(B * nKB), dim3(256), 0, s, out.minmax, Nq, nQB, nKB,
                        bq, out.k_queue, out.k_count, out.k_cost);
   return hipGetLastError();
 }
@@ -214,12 +217,49 @@ hipError_t launch_lpt_sort(const int32_t* cost, int32_t* order, int count, hipSt
   return hipGetLastError();
 }
 
-hipError_t launch_expand_mask(const MaskPtrs& m, int b, int N, int row0, int row1,
+hipError_t launch_expand_mask(const MaskPtrs& m, int b, int Nk, int row0, int row1,
                               uint8_t* dense, hipStream_t s) {
-  if (N == 0 || row1 <= row0) return hipSuccess;
+  if (Nk == 0 || row1 <= row0) return hipSuccess;
   const int windows = (row1 - row0 + 31) / 32;
-  dim3 grid((N + 255) / 256, (unsigned)min(windows, 65535));
-  hipLaunchKernelGGL(k_expand_mask, grid, dim3(256), 0, s, m, b, N, row0, row1, dense);
+  dim3 grid((Nk + 255) / 256, (unsigned)min(windows, 65535));
+  hipLaunchKernelGGL(k_expand_mask, grid, dim3(256), 0, s, m, b, Nk, row0, row1, dense);
+  return hipGetLastError();
+}
+
+// ---- Mask localization for one context-parallel rank (FlashMask-3 page, §3.2) ----
+// x_local = sum_i clamp(x - offsets[i], 0, C): the rank's rows before global row x.  The
+// chunk offsets are staged once per workgroup in LDS.
+__global__ __launch_bounds__(256) void k_localize(MaskPtrs g, const int32_t* __restrict__ offsets,
+                                                  int n_chunks, int C, MaskOut out,
+                                                  int64_t cols) {
+  __shared__ int32_t offs[4096];
+  for (int i = threadIdx.x; i < n_chunks; i += 256) offs[i] = offsets[i];
+  __syncthreads();
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < cols;
+       c += (int64_t)gridDim.x * 256) {
+    const int x0 = g.lts[c], x1 = g.lte[c], x2 = g.uts[c], x3 = g.ute[c];
+    int y0 = 0, y1 = 0, y2 = 0, y3 = 0;
+    for (int i = 0; i < n_chunks; ++i) {
+      const int o = offs[i];
+      y0 += min(max(x0 - o, 0), C);
+      y1 += min(max(x1 - o, 0), C);
+      y2 += min(max(x2 - o, 0), C);
+      y3 += min(max(x3 - o, 0), C);
+    }
+    out.lts[c] = y0;
+    out.lte[c] = y1;
+    out.uts[c] = y2;
+    out.ute[c] = y3;
+  }
+}
+
+hipError_t launch_localize(const MaskPtrs& g, const int32_t* offsets, int n_chunks, int chunk_len,
+                           const MaskOut& out, int64_t cols, hipStream_t s) {
+  if (cols <= 0) return hipSuccess;
+  const int64_t blocks = (cols + 255) / 256;
+  const unsigned grid = (unsigned)(blocks < 2048 ? blocks : 2048);
+  hipLaunchKernelGGL(k_localize, dim3(grid), dim3(256), 0, s, g, offsets, n_chunks, chunk_len,
+                     out, cols);
   return hipGetLastError();
 }
 

@@ -64,7 +64,7 @@ struct FwdParams {
   const int32_t* __restrict__ q_queue;
   const int32_t* __restrict__ q_count;
   const int32_t* __restrict__ q_order;
-  int B, Hq, Hkv, N, nQB, nKB;
+  int B, Hq, Hkv, Nq, Nk, nQB, nKB;  // Nq query rows, Nk keys
   float c;  // softmax scale * log2(e)
 };
 
@@ -80,9 +80,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   const int kvh = h / (p.Hq / p.Hkv);
   const int n_tiles = p.q_count[2 * item] + p.q_count[2 * item + 1];
   const int32_t* queue = p.q_queue + (size_t)item * p.nKB;
-  const int N = p.N;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const rsrc_t qr_ = make_rsrc(p.q + (size_t)(b * p.Hq + h) * N * D, head_bytes);
+  const int Nq = p.Nq, N = p.Nk;  // N: keys (and mask columns)
+  const uint32_t q_bytes = (uint32_t)Nq * D * 2, head_bytes = (uint32_t)N * D * 2;
+  const rsrc_t qr_ = make_rsrc(p.q + (size_t)(b * p.Hq + h) * Nq * D, q_bytes);
   const rsrc_t kr_ = make_rsrc(p.k + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
   const rsrc_t vr_ = make_rsrc(p.v + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
   const uint32_t vec_bytes = (uint32_t)N * 4;
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
 
   const int row = qb * BQ + wave * 32 + l32;
 
-  // Q^T operand: lane holds Q[row][s*16 + hh*8 .. +7] for s = 0..7 (rows past N read 0)
+  // Q^T operand: lane holds Q[row][s*16 + hh*8 .. +7] for s = 0..7 (rows past Nq read 0)
   bf16x8 qr[8];
   {
     const uint32_t off = (uint32_t)row * (D * 2) + hh * 16;
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   lf = sum_with_partner32(lf);
   lb = sum_with_partner32(lb);
   const float inv = lb > 0.f ? 1.0f / lb : 0.f;
-  const rsrc_t orr = make_rsrc(p.o + (size_t)(b * p.Hq + h) * N * D, head_bytes);
+  const rsrc_t orr = make_rsrc(p.o + (size_t)(b * p.Hq + h) * Nq * D, q_bytes);
   const uint32_t ooff = (uint32_t)row * (D * 2) + hh * 8;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     }
   }
   if (hh == 0) {
-    const rsrc_t lr = make_rsrc(p.lse + (size_t)(b * p.Hq + h) * N, (uint32_t)N * 4);
+    const rsrc_t lr = make_rsrc(p.lse + (size_t)(b * p.Hq + h) * Nq, (uint32_t)Nq * 4);
     const float l = lf > 0.f ? (m_use + __builtin_amdgcn_logf(lf)) * kLn2 : -INFINITY;
     buf_store4(__float_as_uint(l), lr, (uint32_t)row * 4, 0);
   }
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-  if (a.B == 0 || a.N == 0 || a.Hq == 0) return hipSuccess;
+  if (a.B == 0 || a.Nq == 0 || a.Hq == 0) return hipSuccess;
   FwdParams p;
   p.q = static_cast<const bf16*>(a.q);
   p.k = static_cast<const bf16*>(a.k);
@@ -359,11 +359,11 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_
   p.q_queue = a.q_queue;
   p.q_count = a.q_count;
   p.q_order = a.q_order;
-  p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N; p.nQB = a.nQB; p.nKB = a.nKB;
+  p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk; p.nQB = a.nQB; p.nKB = a.nKB;
   p.c = a.scale * kLog2e;
   const unsigned grid = (unsigned)a.B * (unsigned)a.nQB * (unsigned)a.Hq;
   if (ev0) (void)hipEventRecord(ev0, s);
-  hipLaunchKernelGGL(k_attn_fwd, dim3(grid), dim3(256), 0, s, p);
+  if (grid > 0) hipLaunchKernelGGL(k_attn_fwd, dim3(grid), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (ev1) (void)hipEventRecord(ev1, s);
   return e;

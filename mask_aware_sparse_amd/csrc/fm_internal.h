@@ -46,11 +46,22 @@ struct TileOut {
   int32_t* k_cost;       // [B*nKB]                    (required if k_queue)
 };
 
-hipError_t launch_classify(const MaskPtrs& m, int B, int N, int bq, int bk, const TileOut& out,
-                           hipStream_t s);
+// Nq query rows (Q-blocks of bq), Nk keys (KV blocks of bk); vectors are [B][Nk].
+hipError_t launch_classify(const MaskPtrs& m, int B, int Nq, int Nk, int bq, int bk,
+                           const TileOut& out, hipStream_t s);
 hipError_t launch_lpt_sort(const int32_t* cost, int32_t* order, int count, hipStream_t s);
-hipError_t launch_expand_mask(const MaskPtrs& m, int b, int N, int row0, int row1,
+hipError_t launch_expand_mask(const MaskPtrs& m, int b, int Nk, int row0, int row1,
                               uint8_t* dense, hipStream_t s);
+
+struct MaskOut {
+  int32_t* lts;
+  int32_t* lte;
+  int32_t* uts;
+  int32_t* ute;
+};
+// Renumber every bound of `cols` = B * Nk columns into the rank's rows.
+hipError_t launch_localize(const MaskPtrs& g, const int32_t* offsets, int n_chunks, int chunk_len,
+                           const MaskOut& out, int64_t cols, hipStream_t s);
 
 struct FwdArgs {
   const void* q;
@@ -62,7 +73,7 @@ struct FwdArgs {
   const int32_t* q_queue;
   const int32_t* q_count;
   const int32_t* q_order;
-  int B, Hq, Hkv, N, nQB, nKB;
+  int B, Hq, Hkv, Nq, Nk, nQB, nKB;
   float scale;
 };
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
@@ -86,11 +97,11 @@ struct BwdArgs {
   const int32_t* q_queue;
   const int32_t* q_count;
   const int32_t* q_order;
-  float* lse2;   // [B][Hq][N] log2-domain LSE (+inf for rows that see nothing)
-  float* delta;  // [B][Hq][N] rowsum(dO * O)
-  float* dk_acc; // [B][Hkv][N][128] fp32, only when Hq/Hkv > kBwdHeadChunk (else null)
+  float* lse2;   // [B][Hq][Nq] log2-domain LSE (+inf for rows that see nothing)
+  float* delta;  // [B][Hq][Nq] rowsum(dO * O)
+  float* dk_acc; // [B][Hkv][Nk][128] fp32, only when Hq/Hkv > kBwdHeadChunk (else null)
   float* dv_acc; // [B][Hkv][N][128] fp32, likewise
-  int B, Hq, Hkv, N;
+  int B, Hq, Hkv, Nq, Nk;
   int nQB_k, nKB_k;  // block counts at the dK/dV tile
   int nQB_q, nKB_q;  // block counts at the dQ (forward) tile
   float scale;

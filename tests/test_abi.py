@@ -157,3 +157,47 @@ def test_missing_library_fails_loudly():
             "try:\n    fm.library()\nexcept RuntimeError as e:\n    print('raised', e)\n")
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
     assert "raised" in out.stdout
+
+
+def prob_kv(B=1, Hq=4, Hkv=2, Nq=256, Nk=1024):
+    p = fm.Problem(B, Hq, Hkv, Nq, 128, 0.0)
+    p.seqlen_kv = Nk
+    return p
+
+
+def test_query_share_problem_checks():
+    assert fwd(prob_kv(Nk=-1)) == INVALID
+    assert bwd(prob_kv(Nk=-1)) == INVALID
+    assert fwd(prob_kv(Nk=(1 << 22) + 1)) == UNSUPPORTED
+    # N_q = N_k = 0 is nothing to do; N_q = 0 with keys is not (dK/dV must be zeroed)
+    assert fwd(prob_kv(Nq=0, Nk=0), ws_bytes=0) == FM_OK
+    assert bwd(prob_kv(Nq=0, Nk=0), ws_bytes=0) == FM_OK
+    assert bwd(prob_kv(Nq=0, Nk=512), ws_bytes=0) == WORKSPACE
+
+
+def test_query_share_workspace_sizes():
+    # forward tiles: nQB = N_q / 128 Q-blocks by nKB = N_k / 64 KV blocks
+    al = lambda x: (x + 255) // 256 * 256
+    nqb, nkb = 2, 16
+    want = al(nkb * 32) + al(nqb * nkb * 4) + al(nqb * 8) + 2 * al(nqb * 4)
+    assert fm.workspace_size(1, 4, 2, 256, fm.OP_FWD, seqlen_kv=1024) == want
+    square = fm.workspace_size(1, 4, 2, 256, fm.OP_BWD)
+    assert fm.workspace_size(1, 4, 2, 256, fm.OP_BWD, seqlen_kv=1024) > square
+
+
+def test_localize_argument_checks():
+    lib = fm.library()
+    p = prob_kv(B=2, Nq=0, Nk=100)
+    m = fake_mask()
+    out = fm.MaskOut(0x100000, 0x100000, 0x100000, 0x100000)
+    call = lambda p_, n, c, offs=FAKE, mm=m, o=out: lib.fm_localize_mask(
+        None if p_ is None else ctypes.byref(p_), None if mm is None else ctypes.byref(mm),
+        offs, n, c, None if o is None else ctypes.byref(o), None)
+    assert call(None, 1, 8) == INVALID
+    assert call(p, 1, 8, mm=None) == INVALID
+    assert call(p, 1, 8, o=None) == INVALID
+    assert call(p, 0, 8) == INVALID
+    assert call(p, 1, 0) == INVALID
+    assert call(p, 4097, 8) == UNSUPPORTED
+    assert call(p, 1, 8, offs=None) == INVALID
+    assert call(prob_kv(B=0, Nq=0, Nk=100), 1, 8) == FM_OK     # no columns: nothing to do

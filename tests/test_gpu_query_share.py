@@ -1,0 +1,128 @@
+"""One context-parallel rank's share on one GPU (FlashMask-3 page, §3.2): the mask
+localization kernel against the oracle, attention with N_q local rows against N_k keys
+against the oracle, and Theorem 1 -- the ranks' forward outputs (and dQ) are the global
+ones bit for bit, and the ranks' dK/dV sum to the global ones."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import check_fwd, check_grads, gpu_inputs, log, rel_l2, to_np, GRAD_TOL
+
+pytestmark = pytest.mark.gpu
+
+
+def _rank_chunks(rng, n, C, ranks):
+    """A random assignment of the n // C query chunks to `ranks` ranks (every rank gets
+    at least one); returns the ascending offset list of each rank."""
+    nchunks = n // C
+    owner = rng.permutation(np.arange(nchunks) % ranks)
+    return [sorted(int(c) * C for c in np.nonzero(owner == r)[0]) for r in range(ranks)]
+
+
+def _share(fm, q, k, v, do, vec, offs, C, with_bwd=True):
+    rows = torch.from_numpy(oracle.rank_rows(offs, C)).to(q.device)
+    qr, dor = q[:, :, rows].contiguous(), do[:, :, rows].contiguous()
+    offs_t = torch.tensor(offs, dtype=torch.int32, device=q.device)
+    lv = fm.localize_mask(*vec, offs_t, C)
+    O, L = fm.attn_fwd(qr, k, v, *lv)
+    g = fm.attn_bwd(qr, k, v, O, L, dor, *lv) if with_bwd else None
+    return rows, lv, O, L, g
+
+
+SMALL = {
+    "prefix_lm_doc_1k_gqa": (lambda: workloads.prefix_lm_doc(0, n=1024, batch=2, heads_q=4,
+                                                             heads_kv=2, lo=128, hi=512), 64),
+    "random_intervals_768": (lambda: workloads.random_intervals(2, 768, batch=1, heads_q=2), 32),
+    "sliding_window_2k": (lambda: workloads.sliding_window_sinks(n=2048, heads_q=2, window=300,
+                                                                 sinks=10), 128),
+    "random_eviction_1k_mqa": (lambda: workloads.random_eviction(1, n=1024, heads_q=6), 64),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_localize_matches_oracle(name):
+    import mask_aware_sparse_amd as fm
+    mk, C = SMALL[name]
+    w = mk()
+    rng = np.random.default_rng(5)
+    vec = workloads.mask_tensors(w, device="cuda")
+    for offs in _rank_chunks(rng, w.seqlen, C, 3):
+        offs_t = torch.tensor(offs, dtype=torch.int32, device="cuda")
+        got = fm.localize_mask(*vec, offs_t, C)
+        want = oracle.localize_vectors(w.vectors(), offs, C)
+        for g, r in zip(got, want):
+            assert np.array_equal(g.cpu().numpy(), r)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_rank_share_matches_oracle(name):
+    """Attention of a rank's rows (N_q = its chunks) against all N_k keys."""
+    import mask_aware_sparse_amd as fm
+    mk, C = SMALL[name]
+    w = mk()
+    rng = np.random.default_rng(9)
+    offs = _rank_chunks(rng, w.seqlen, C, 3)[1]
+    log(f"rank share {name} N_k={w.seqlen} chunks={len(offs)}x{C}")
+    q, k, v, do, vec = gpu_inputs(w)
+    rows, lv, O, L, (dq, dk, dv) = _share(fm, q, k, v, do, vec, offs, C)
+    torch.cuda.synchronize()
+    hq, hk, hv, hdo = (to_np(x) for x in (q, k, v, do))
+    r = rows.cpu().numpy()
+    lvn = oracle.localize_vectors(w.vectors(), offs, C)
+    O_ref, L_ref, dQr, dKr, dVr = oracle.attention_fwd_bwd(hq[:, :, r], hk, hv, hdo[:, :, r], *lvn)
+    check_fwd(O, L, O_ref, L_ref, ctx=name)
+    check_grads(dq, dk, dv, (dQr, dKr, dVr), L_ref, ctx=name)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_theorem1_ranks_reproduce_the_global_result(name):
+    import mask_aware_sparse_amd as fm
+    mk, C = SMALL[name]
+    w = mk()
+    rng = np.random.default_rng(13)
+    q, k, v, do, vec = gpu_inputs(w)
+    O, L = fm.attn_fwd(q, k, v, *vec)
+    dq, dk, dv = fm.attn_bwd(q, k, v, O, L, do, *vec)
+    dk_sum = torch.zeros_like(dk, dtype=torch.float32)
+    dv_sum = torch.zeros_like(dv, dtype=torch.float32)
+    seen = torch.zeros(w.seqlen, dtype=torch.bool, device="cuda")
+    for offs in _rank_chunks(rng, w.seqlen, C, 4):
+        rows, _, Or, Lr, (dqr, dkr, dvr) = _share(fm, q, k, v, do, vec, offs, C)
+        assert torch.equal(Or, O[:, :, rows]), f"{name}: O differs"
+        assert torch.equal(Lr, L[:, :, rows]), f"{name}: LSE differs"
+        assert torch.equal(dqr, dq[:, :, rows]), f"{name}: dQ differs"
+        dk_sum += dkr.float()
+        dv_sum += dvr.float()
+        seen[rows] = True
+    torch.cuda.synchronize()
+    assert bool(seen.all())
+    for name_, a, b in (("dK", dk_sum, dk), ("dV", dv_sum, dv)):
+        e = rel_l2(to_np(a), to_np(b))
+        assert e <= GRAD_TOL, f"{name}: summed {name_} rel-L2 {e:.3e}"
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(2, 1), (8, 1)])
+def test_rank_without_rows_zeroes_dk_dv(Hq, Hkv):
+    """A rank that owns no query rows: its dK = dV = 0 (direct stores for a group of 2
+    heads, fp32 accumulators for a group of 8)."""
+    import mask_aware_sparse_amd as fm
+    w = workloads.causal(256, heads_q=Hq, heads_kv=Hkv)
+    q, k, v, do, vec = gpu_inputs(w)
+    empty = q[:, :, :0].contiguous()
+    O, L = fm.attn_fwd(empty, k, v, *vec)
+    dk = torch.full_like(k, 7.0)
+    dv = torch.full_like(v, 7.0)
+    fm.attn_bwd(empty, k, v, O, L, empty, *vec, grads=(empty.clone(), dk, dv))
+    torch.cuda.synchronize()
+    assert (dk == 0).all() and (dv == 0).all()
+
+
+def test_rows_without_keys_are_rejected_by_the_binding():
+    import mask_aware_sparse_amd as fm
+    w = workloads.causal(64, heads_q=2, heads_kv=1)
+    q, k, v, do, vec = gpu_inputs(w)
+    with pytest.raises(ValueError):
+        fm.attn_fwd(q, k[:, :, :0].contiguous(), v[:, :, :0].contiguous(),
+                    *(x[:, :0].contiguous() for x in vec))
