@@ -19,6 +19,11 @@ scaling the FETCH_SIZE / WRITE_SIZE counters) and prints its byte count.
 sets, costs, both LPT orders) on the c5 vectors replicated over 4 batch rows (the most the
 single-workgroup LPT sort takes at the forward tile: 4 x 2048 KV blocks), against the
 HBM roofline.
+`--cp P` instead emulates context parallelism over P ranks on the one GPU: the query
+axis of the workload is cut into 2P chunks, assigned to ranks either contiguously or by
+fm_ipo_balance on the chunks' tile costs; each rank's share (its chunks' rows against
+all keys, vectors renumbered by fm_localize_mask) runs fwd+bwd in turn, and the per-rank
+times, their max/mean and the rate of a job bounded by the slowest rank are reported.
 `--ipo-table` instead runs the host chunk balancer (fm_ipo_balance, HCC-IPO stage 1) on
 seeded instances of the FlashMask-3 page's IPO ablation configurations and prints the
 share of instances above the lower bound after LPT, P2 and P3, the mean gaps and times.
@@ -46,7 +51,8 @@ DEFAULT_WORKLOAD = "c2_prefix_lm_doc_8k"
 
 def attended_pairs(w):
     """Attended (q, k) pairs summed over batch rows and query heads, by interval
-    arithmetic on the column vectors (N minus the union of the two hidden intervals)."""
+    arithmetic on the column vectors (N_q = w.seqlen rows minus the union of the two
+    hidden intervals, per key column)."""
     total = 0
     n = w.seqlen
     for b in range(w.batch):
@@ -149,6 +155,69 @@ def classify_bandwidth(steps, warmup, batch=4, block_q=128, block_k=64):
         "roofline": {"bound": "hbm", "achieved": round(gbs(alg), 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs(alg) / HBM_PEAK_GBS, 4)},
         "layout_gbs": round(gbs(layout), 1)}))
+
+
+def cp_emulation(workload, P, steps, warmup, kappa=2):
+    import torch
+    import mask_aware_sparse_amd as fm
+    w = workloads.make_workload(workload, 0)
+    n = w.seqlen
+    nch = P * kappa
+    if n % nch or (n // nch) % 128:
+        raise SystemExit(f"--cp {P}: N = {n} does not split into {nch} chunks of whole Q-blocks")
+    C = n // nch
+    q, k, v, do = workloads.make_tensors(w, device="cuda")
+    vec = workloads.mask_tensors(w, device="cuda")
+    # chunk loads: the forward tile costs of the chunk's Q-blocks, summed over the batch
+    bq, bk = fm.tile_shape(fm.OP_FWD)
+    t = fm.classify_tiles(*vec, bq, bk)
+    qc = t["q_count"].cpu().numpy().astype(np.int64)          # [B][nQB][2]
+    cost = (11 * qc[..., 0] + 10 * qc[..., 1]).sum(axis=0)     # [nQB]
+    wchunk = cost.reshape(nch, C // bq).sum(axis=1)
+    plans = {"contiguous": [list(range(r * kappa, (r + 1) * kappa)) for r in range(P)]}
+    owner, rep = fm.ipo_balance(wchunk, P, 3)
+    plans["ipo"] = [[int(c) for c in np.nonzero(owner == r)[0]] for r in range(P)]
+    A_all = attended_pairs(w)
+    out = {"measure": f"context parallelism over {P} ranks emulated on one GPU",
+           "config": {"workload": workload, "ranks": P, "chunks": nch, "chunk_rows": C,
+                      "steps": steps, "warmup": warmup},
+           "ipo_report": {k_: (int(v_) if not isinstance(v_, bool) else v_)
+                          for k_, v_ in rep.items()}, "plans": {}}
+    for name, plan in plans.items():
+        ranks = []
+        for r, chunks in enumerate(plan):
+            offs = [c * C for c in sorted(chunks)]
+            rows = torch.cat([torch.arange(o, o + C, device="cuda") for o in offs])
+            qr, dor = q[:, :, rows].contiguous(), do[:, :, rows].contiguous()
+            lv = fm.localize_mask(*vec, torch.tensor(offs, dtype=torch.int32, device="cuda"), C)
+            o = torch.empty_like(qr)
+            lse = torch.empty((w.batch, w.heads_q, qr.shape[2]), dtype=torch.float32,
+                              device="cuda")
+            grads = (torch.empty_like(qr), torch.empty_like(k), torch.empty_like(v))
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for i in range(warmup + steps):
+                e = ev[i - warmup] if i >= warmup else None
+                if e:
+                    e[0].record()
+                fm.attn_fwd(qr, k, v, *lv, out=o, lse=lse)
+                fm.attn_bwd(qr, k, v, o, lse, dor, *lv, grads=grads)
+                if e:
+                    e[1].record()
+            torch.cuda.synchronize()
+            ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+            lw = workloads.Workload(w.name, w.batch, w.heads_q, w.heads_kv, qr.shape[2],
+                                    w.head_dim, *[x.cpu().numpy() for x in lv], w.seed)
+            pairs = attended_pairs(lw)  # N_q local rows, vectors over all N_k keys
+            ranks.append({"rank": r, "chunks": sorted(chunks), "ms": round(ms, 3),
+                          "load": int(wchunk[sorted(chunks)].sum()),
+                          "tflops": round(14 * w.head_dim * pairs / (ms * 1e-3) / 1e12, 1)})
+        t_ms = [x["ms"] for x in ranks]
+        out["plans"][name] = {
+            "ranks": ranks, "max_ms": max(t_ms), "mean_ms": round(float(np.mean(t_ms)), 3),
+            "max_over_mean": round(max(t_ms) / float(np.mean(t_ms)), 3),
+            "job_tflops_if_parallel": round(14 * w.head_dim * A_all / (max(t_ms) * 1e-3) / 1e12, 1)}
+    print(json.dumps(out))
 
 
 def ipo_table(instances=200, seed=0):
@@ -285,6 +354,8 @@ def main():
                     help="run only a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--classify-bandwidth", action="store_true",
                     help="time fm_classify_tiles on replicated c5 vectors (HBM roofline)")
+    ap.add_argument("--cp", type=int, default=0, metavar="P",
+                    help="emulate context parallelism over P ranks (query shares in turn)")
     ap.add_argument("--ipo-table", action="store_true",
                     help="host chunk balancer on the IPO ablation configurations")
     ap.add_argument("--measure-alpha", action="store_true",
@@ -303,6 +374,10 @@ def main():
         return
     if args.ipo_table:
         ipo_table()
+        return
+    if args.cp > 0:
+        cp_emulation(args.workload if args.workload != DEFAULT_WORKLOAD else
+                     "c5_random_eviction_128k", args.cp, min(args.steps, 3), min(args.warmup, 1))
         return
     if args.classify_bandwidth:
         classify_bandwidth(args.steps, args.warmup)
