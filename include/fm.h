@@ -132,7 +132,7 @@ fm_status fm_workspace_size(const fm_problem* p, fm_op op, int32_t block_q, int3
                             size_t* bytes);
 
 /* The tile shape (rows of Q, columns of K per tile) the forward or backward kernel uses
- * and classifies with: 128 x 64 for FM_OP_FWD (also the backward's dQ kernel), 32 x 256
+ * and classifies with: 128 x 64 for FM_OP_FWD (also the backward's dQ kernel), 32 x 128
  * for FM_OP_BWD (the dK/dV kernel).  FM_OP_CLASSIFY is invalid here. */
 fm_status fm_tile_shape(fm_op op, int32_t* block_q, int32_t* block_k);
 

@@ -18,9 +18,9 @@
 //                    queue of 64-key blocks, recomputes S^T and dP^T, and accumulates
 //                    dQ^T = K^T dS^T in registers (a lane owns one query row, as in the
 //                    forward); dQ is written once.
-//   k_attn_bwd_dkdv  one workgroup per (b, kv head, 256-key KV block, chunk of <= 4 query
+//   k_attn_bwd_dkdv  one workgroup per (b, kv head, 128-key KV block, chunk of <= 4 query
 //                    heads), numbered in LPT order of the KV blocks' tile costs; each of
-//                    the 8 waves owns 32 keys; the workgroup walks the block's queue of
+//                    the 4 waves owns 32 keys; the workgroup walks the block's queue of
 //                    32-row Q-blocks (partial tiles masked), recomputes S and dP, and keeps
 //                    dK/dV in registers.  With one head chunk per KV head the workgroup
 //                    owns its dK/dV rows and stores them as bf16; with several (GQA/MQA
@@ -64,13 +64,14 @@ __device__ __forceinline__ int perm_rows(int a) {
 }
 
 // ---- KE: dK / dV (KV-block outer) -------------------------------------------------------
-// 8 waves x 32 keys = one 256-key block per workgroup; two waves per SIMD so that one
-// wave's softmax VALU work overlaps the other's MFMA work.  Steps are 32-row Q-blocks,
-// which keeps the live registers of a wave within 256.
+// 4 waves x 32 keys = one 128-key block per workgroup, two workgroups per CU (78 KB of LDS
+// each), so the two waves on a SIMD belong to different workgroups and their MFMA and
+// softmax phases drift apart instead of meeting at the same barriers.  Steps are 32-row
+// Q-blocks, which keeps the live registers of a wave within 256.
 namespace dkdv {
-constexpr int kWaves = 8;
+constexpr int kWaves = kBwdBlockK / 32;
 constexpr int BQ = kBwdBlockQ;  // 32 query rows per step
-constexpr int BK = kBwdBlockK;  // 256 keys per workgroup
+constexpr int BK = kBwdBlockK;  // 128 keys per workgroup
 constexpr int KS = D + 8;       // K row stride in LDS (272 B: row reads only)
 static_assert(BK == 32 * kWaves, "one 32-key slice per wave");
 
@@ -105,7 +106,7 @@ struct DkdvParams {
   float scale;  // softmax scale (applied to dK)
 };
 
-__global__ __launch_bounds__(512, 2) void k_attn_bwd_dkdv(DkdvParams p) {
+__global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvParams p) {
   using namespace dkdv;
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -171,10 +172,12 @@ __global__ __launch_bounds__(512, 2) void k_attn_bwd_dkdv(DkdvParams p) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) { dk[d] = f32x16{}; dv[d] = f32x16{}; }
 
-  // ---- staging of the Q / dO tiles: thread copies row tid>>4, chunk tid&15
-  static_assert(BQ * 16 == 64 * kWaves, "one 16-byte chunk per thread");
+  // ---- staging of the Q / dO tiles: thread copies rows (tid>>4) + kCpRows*i, chunk tid&15
+  constexpr int kCp = BQ * 16 / (64 * kWaves);  // 16-byte chunks per thread and tensor
+  constexpr int kCpRows = 64 * kWaves / 16;
+  static_assert(kCp * 64 * kWaves == BQ * 16, "whole chunks per thread");
   const int cp_row = tid >> 4, cp_ch = tid & 15;
-  u32x4 qst, ost;
+  u32x4 qst[kCp], ost[kCp];
   uint32_t lst = 0u, dst_ = 0u;
   const int nsteps = nh * nq;
 
@@ -186,8 +189,11 @@ __global__ __launch_bounds__(512, 2) void k_attn_bwd_dkdv(DkdvParams p) {
     const rsrc_t qrs = make_rsrc(p.q + base * D, q_bytes);
     const rsrc_t ors = make_rsrc(p.dout + base * D, q_bytes);
     const uint32_t off = (uint32_t)(qb * BQ + cp_row) * (D * 2) + cp_ch * 16;
-    qst = buf_load16(qrs, off, 0);
-    ost = buf_load16(ors, off, 0);
+#pragma unroll
+    for (int i = 0; i < kCp; ++i) {
+      qst[i] = buf_load16(qrs, off, i * kCpRows * D * 2);
+      ost[i] = buf_load16(ors, off, i * kCpRows * D * 2);
+    }
     if (tid < BQ) {
       const uint32_t ro = (uint32_t)(qb * BQ + tid) * 4;
       lst = buf_load4(make_rsrc(p.lse2 + base, (uint32_t)Nq * 4), ro, 0);
@@ -195,9 +201,12 @@ __global__ __launch_bounds__(512, 2) void k_attn_bwd_dkdv(DkdvParams p) {
     }
   };
   auto store_step = [&](int buf) {
-    const int o = swz(cp_row, cp_ch);
-    *reinterpret_cast<u32x4*>(&sm.q[buf][o]) = qst;
-    *reinterpret_cast<u32x4*>(&sm.dO[buf][o]) = ost;
+#pragma unroll
+    for (int i = 0; i < kCp; ++i) {
+      const int o = swz(cp_row + i * kCpRows, cp_ch);
+      *reinterpret_cast<u32x4*>(&sm.q[buf][o]) = qst[i];
+      *reinterpret_cast<u32x4*>(&sm.dO[buf][o]) = ost[i];
+    }
     if (tid < BQ) {
       sm.lse2[buf][tid] = __uint_as_float(lst);
       sm.dl[buf][tid] = __uint_as_float(dst_);

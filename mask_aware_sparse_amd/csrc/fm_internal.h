@@ -11,11 +11,11 @@ constexpr int kHeadDim = 128;
 
 // Tile shapes of the attention kernels.  The forward (and the backward's dQ kernel) uses
 // 128 query rows (4 waves x 32) by 64 keys; the backward's dK/dV kernel 32 query rows by
-// 256 keys (8 waves x 32 keys).
+// 128 keys (4 waves x 32 keys, two workgroups per CU).
 constexpr int kFwdBlockQ = 128;
 constexpr int kFwdBlockK = 64;
 constexpr int kBwdBlockQ = 32;
-constexpr int kBwdBlockK = 256;
+constexpr int kBwdBlockK = 128;
 // Query heads handled by one backward work item (dK/dV of a KV block are summed over
 // these heads in registers, then added across items with fp32 atomics).
 constexpr int kBwdHeadChunk = 4;

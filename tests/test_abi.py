@@ -66,7 +66,7 @@ def test_status_strings():
 
 def test_tile_shapes():
     assert fm.tile_shape(fm.OP_FWD) == (128, 64)
-    assert fm.tile_shape(fm.OP_BWD) == (32, 256)
+    assert fm.tile_shape(fm.OP_BWD) == (32, 128)
     with pytest.raises(fm.FMError):
         fm.tile_shape(fm.OP_CLASSIFY)
 
