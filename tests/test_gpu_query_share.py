@@ -126,3 +126,37 @@ def test_rows_without_keys_are_rejected_by_the_binding():
     with pytest.raises(ValueError):
         fm.attn_fwd(q, k[:, :, :0].contiguous(), v[:, :, :0].contiguous(),
                     *(x[:, :0].contiguous() for x in vec))
+
+
+@pytest.mark.parametrize("name", ["c5_random_eviction_128k", "c4_sliding_window_128k"])
+def test_full_size_rank_share(name):
+    """A rank's share at full size, in the launch configuration `bench.py --cp 8` times
+    (16 chunks of 8192 rows, two per rank; here the contiguous plan's last rank and an
+    interleaved pair): O, LSE and dQ equal the global run's rows bit for bit, and
+    sampled rows match the oracle."""
+    import mask_aware_sparse_amd as fm
+    w = workloads.make_workload(name)
+    C = w.seqlen // 16
+    q, k, v, do, vec = gpu_inputs(w)
+    O, L = fm.attn_fwd(q, k, v, *vec)
+    dq, _, _ = fm.attn_bwd(q, k, v, O, L, do, *vec)
+    for offs in ([14 * C, 15 * C], [3 * C, 12 * C]):
+        log(f"full-size rank share {name} chunks at {offs}")
+        rows, lv, Or, Lr, (dqr, _, _) = _share(fm, q, k, v, do, vec, offs, C)
+        torch.cuda.synchronize()
+        assert torch.equal(Or, O[:, :, rows]) and torch.equal(Lr, L[:, :, rows])
+        assert torch.equal(dqr, dq[:, :, rows])
+        # sampled local rows (first rows of both chunks, a few random) against the oracle
+        rng = np.random.default_rng(0)
+        loc = sorted({0, 1, C, C + 1, 2 * C - 1} | set(rng.integers(0, 2 * C, 4).tolist()))
+        glob_rows = rows[loc].cpu().numpy()
+        g = w.heads_q // w.heads_kv
+        for h in (0, w.heads_q - 1):
+            hq, hdo = to_np(q[:1, h:h + 1]), to_np(do[:1, h:h + 1])
+            hk, hv = to_np(k[:1, h // g:h // g + 1]), to_np(v[:1, h // g:h // g + 1])
+            o_ref, l_ref, dq_ref = oracle.attention_rows(
+                hq, hk, hv, hdo, *(x[:1] for x in w.vectors()), 0, 0, glob_rows)
+            assert np.abs(to_np(Or[0, h, loc]) - o_ref).max() <= 1e-2
+            fin = np.isfinite(l_ref)
+            assert np.abs(to_np(Lr[0, h, loc])[fin] - l_ref[fin]).max() <= 1e-3
+            assert rel_l2(to_np(dqr[0, h, loc]), dq_ref) <= GRAD_TOL
