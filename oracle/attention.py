@@ -21,6 +21,11 @@ nothing to dK/dV.  Query head h uses kv head h // (H_q / H_kv) (GQA: K/V heads a
 shared by contiguous groups of query heads, Flash MSA guide FAQ).  dK/dV of a kv
 head sum over the query heads of its group.
 
+Mask vectors are one set per batch row, [B][N_k], shared by every head (FlashMask-3
+page, Overview), or -- the per-head variant its list of extensions names without
+defining -- [B][H_m][N_k] with H_m dividing H_q, where query head h uses set
+h // (H_q / H_m) (contiguous groups, as for GQA; H_m = H_q is one set per head).
+
 Rows are processed in blocks; each block expands only its own rows of the mask
 (never the full N x N matrix) and restricts its products to the columns that at
 least one of its rows can see, which is exact because hidden columns contribute 0.
@@ -84,30 +89,42 @@ def _row_block(qh, kh, vh, vecs, r0, r1, scale, dOh=None):
 
 
 def _check(q, k, v, vecs):
-    """Q [B][H_q][N_q][d], K and V [B][H_kv][N_k][d], vectors [B][N_k] (query-row bounds
-    in [0, N_q]); N_q = N_k for self-attention, N_q < N_k for one rank's share of the
-    query rows under context parallelism with localized vectors."""
+    """Q [B][H_q][N_q][d], K and V [B][H_kv][N_k][d], vectors [B][N_k] or [B][H_m][N_k]
+    (query-row bounds in [0, N_q]); N_q = N_k for self-attention, N_q < N_k for one
+    rank's share of the query rows under context parallelism with localized vectors.
+    Returns (B, H_q, H_kv, N_q, d, g, vec_of) with vec_of(b, h) the four [N_k] vectors
+    query head h of batch row b uses."""
     B, Hq, N, d = q.shape
     Bk, Hkv, Nk, dk = k.shape
     assert (B, d) == (Bk, dk) and v.shape == k.shape
     assert Hq % Hkv == 0
-    for x in vecs:
-        assert np.asarray(x).shape == (B, Nk)
-    return B, Hq, Hkv, N, d, Hq // Hkv
+    return (B, Hq, Hkv, N, d, Hq // Hkv) + (_vectors_of(vecs, B, Hq, Nk),)
+
+
+def _vectors_of(vecs, B, Hq, Nk):
+    arrs = [np.asarray(x) for x in vecs]
+    shape = arrs[0].shape
+    assert all(x.shape == shape for x in arrs)
+    if len(shape) == 2:
+        assert shape == (B, Nk)
+        return lambda b, h: tuple(x[b] for x in arrs)
+    assert len(shape) == 3 and shape[0] == B and shape[2] == Nk and Hq % shape[1] == 0
+    per = Hq // shape[1]                      # query heads per mask head
+    return lambda b, h: tuple(x[b, h // per] for x in arrs)
 
 
 def attention_fwd(q, k, v, lts, lte, uts, ute, scale=None, row_block=256):
     """O [B][H_q][N][d] and LSE [B][H_q][N] (natural log) in float64."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     vecs = (lts, lte, uts, ute)
-    B, Hq, Hkv, N, d, g = _check(q, k, v, vecs)
+    B, Hq, Hkv, N, d, g, vec_of = _check(q, k, v, vecs)
     sc = _scale(d, scale)
     O = np.zeros((B, Hq, N, d))
     LSE = np.full((B, Hq, N), -np.inf)
     for b in range(B):
-        vb = tuple(np.asarray(x)[b] for x in vecs)
         for h in range(Hq):
             kv = h // g
+            vb = vec_of(b, h)
             for r0 in range(0, N, row_block):
                 r1 = min(r0 + row_block, N)
                 O[b, h, r0:r1], LSE[b, h, r0:r1] = _row_block(q[b, h], k[b, kv], v[b, kv],
@@ -120,7 +137,7 @@ def attention_fwd_bwd(q, k, v, do, lts, lte, uts, ute, scale=None, row_block=256
     its definition (no statistic comes from anywhere but this function)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     vecs = (lts, lte, uts, ute)
-    B, Hq, Hkv, N, d, g = _check(q, k, v, vecs)
+    B, Hq, Hkv, N, d, g, vec_of = _check(q, k, v, vecs)
     sc = _scale(d, scale)
     O = np.zeros((B, Hq, N, d))
     LSE = np.full((B, Hq, N), -np.inf)
@@ -128,9 +145,9 @@ def attention_fwd_bwd(q, k, v, do, lts, lte, uts, ute, scale=None, row_block=256
     dK = np.zeros((B, Hkv, k.shape[2], d))
     dV = np.zeros((B, Hkv, k.shape[2], d))
     for b in range(B):
-        vb = tuple(np.asarray(x)[b] for x in vecs)
         for h in range(Hq):
             kv = h // g
+            vb = vec_of(b, h)
             for r0 in range(0, N, row_block):
                 r1 = min(r0 + row_block, N)
                 o, lse, dq, cols, dkp, dvp = _row_block(q[b, h], k[b, kv], v[b, kv], vb,
@@ -155,7 +172,7 @@ def attention_rows(q, k, v, do, lts, lte, uts, ute, b, h, rows, scale=None):
     kv = h // (Hq // Hkv)
     d = q.shape[3]
     sc = _scale(d, scale)
-    vb = tuple(np.asarray(x)[b] for x in (lts, lte, uts, ute))
+    vb = _vectors_of((lts, lte, uts, ute), q.shape[0], Hq, k.shape[2])(b, h)
     qh, kh, vh = _f64(q[b, h]), _f64(k[b, kv]), _f64(v[b, kv])
     dOh = None if do is None else _f64(do[b, h])
     O = np.zeros((len(rows), d)); LSE = np.zeros(len(rows)); dQ = np.zeros((len(rows), d))
@@ -176,20 +193,21 @@ def attention_cols(q, k, v, do, lts, lte, uts, ute, b, kv, cols, scale=None, row
     g = Hq // Hkv
     d = q.shape[3]
     sc = _scale(d, scale)
-    lv = [np.asarray(x)[b] for x in (lts, lte, uts, ute)]
-    N = len(lv[0])
+    vec_of = _vectors_of((lts, lte, uts, ute), q.shape[0], Hq, k.shape[2])
+    N = q.shape[2]
     cols = np.asarray(cols)
-    # rows that see at least one selected column
-    need = np.zeros(N, dtype=bool)
-    for c in cols:
-        rows_hidden = masked_rows(*(x[c:c + 1] for x in lv), 0, N)[:, 0]
-        need |= ~rows_hidden
-    # Rows that see none of the selected columns contribute exactly 0 to them, so
-    # whole row blocks that contain at least one needed row can be computed.
-    starts = sorted({int(r) // row_block * row_block for r in np.nonzero(need)[0]})
     kh, vh = _f64(k[b, kv]), _f64(v[b, kv])
     dK = np.zeros((len(cols), d)); dV = np.zeros((len(cols), d))
     for h in range(kv * g, (kv + 1) * g):
+        lv = vec_of(b, h)
+        # rows that see at least one selected column
+        need = np.zeros(N, dtype=bool)
+        for c in cols:
+            rows_hidden = masked_rows(*(x[c:c + 1] for x in lv), 0, N)[:, 0]
+            need |= ~rows_hidden
+        # Rows that see none of the selected columns contribute exactly 0 to them, so
+        # whole row blocks that contain at least one needed row can be computed.
+        starts = sorted({int(r) // row_block * row_block for r in np.nonzero(need)[0]})
         qh, dOh = _f64(q[b, h]), _f64(do[b, h])
         for r0 in starts:
             r1 = min(r0 + row_block, N)

@@ -16,12 +16,13 @@ def rand(shape, seed):
 
 
 def torch_dense(q, k, v, hidden, scale):
-    """Independent dense-mask attention in torch float64 (autograd-capable)."""
+    """Independent dense-mask attention in torch float64 (autograd-capable); `hidden` is
+    [B][N_q][N_k] (every head) or [B][H_q][N_q][N_k] (per head)."""
     g = q.shape[1] // k.shape[1]
     k = k.repeat_interleave(g, dim=1)
     v = v.repeat_interleave(g, dim=1)
     s = scale * q @ k.transpose(-1, -2)
-    s = s.masked_fill(hidden[:, None], float("-inf"))
+    s = s.masked_fill(hidden if hidden.dim() == 4 else hidden[:, None], float("-inf"))
     lse = torch.logsumexp(s, dim=-1)
     p = torch.softmax(s, dim=-1)
     return p @ v, lse
@@ -187,3 +188,65 @@ def test_rows_cols_and_block_size_consistent():
     dKc, dVc = oracle.attention_cols(q, k, v, do, *w.vectors(), 1, 0, cols, row_block=32)
     assert np.abs(dKc - dK[1, 0, cols]).max() < 1e-12
     assert np.abs(dVc - dV[1, 0, cols]).max() < 1e-12
+
+
+# ---- per-head mask sets: vectors [B][H_m][N]; query head h uses set h // (H_q / H_m) ----
+
+@pytest.mark.parametrize("hq,hkv,hm", [(4, 2, 4), (4, 2, 2), (4, 1, 2), (6, 3, 3), (2, 2, 1)])
+def test_per_head_sets_vs_autograd(hq, hkv, hm):
+    """Against autograd through dense attention whose [B][H][N][N] mask is expanded per
+    head from the set the head's group uses (the mapping written out here, per head)."""
+    n, d, B = 40, 16, 2
+    w = workloads.random_intervals(7, n, batch=B, heads_q=hq, heads_kv=hkv, p_empty=0.3,
+                                   mask_heads=hm)
+    vecs = w.vectors()
+    assert vecs[0].shape == (B, hm, n)
+    per = hq // hm
+    hid = torch.from_numpy(np.stack([np.stack([oracle.dense_mask(*(x[b, h // per] for x in vecs))
+                                               for h in range(hq)]) for b in range(B)]))
+    dead = hid.all(dim=-1)                                   # [B][H][N]
+    q, k, v, do = (rand(s, 40 + t) for t, s in
+                   enumerate([(B, hq, n, d), (B, hkv, n, d), (B, hkv, n, d), (B, hq, n, d)]))
+    O, LSE, dQ, dK, dV = oracle.attention_fwd_bwd(q, k, v, do, *vecs)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    hid_t = hid.clone()
+    hid_t[dead] = False
+    To, Tl = torch_dense(tq, tk, tv, hid_t, 1 / np.sqrt(d))
+    live = ~dead
+    (To * torch.from_numpy(do) * live[..., None].to(torch.float64)).sum().backward()
+    L = live.numpy()
+    assert np.abs(O[L] - To.detach().numpy()[L]).max() < 1e-12
+    assert np.abs(LSE[L] - Tl.detach().numpy()[L]).max() < 1e-12
+    assert np.abs(dQ[L] - tq.grad.numpy()[L]).max() < 1e-11
+    assert np.abs(dK - tk.grad.numpy()).max() < 1e-11
+    assert np.abs(dV - tv.grad.numpy()).max() < 1e-11
+    assert (O[~L] == 0).all() and np.isneginf(LSE[~L]).all()
+
+
+def test_per_head_sets_that_agree_equal_the_shared_set():
+    n, d = 64, 16
+    w = workloads.random_intervals(3, n, batch=2, heads_q=4, heads_kv=2)
+    q, do = rand((2, 4, n, d), 1), rand((2, 4, n, d), 2)
+    k, v = rand((2, 2, n, d), 3), rand((2, 2, n, d), 4)
+    shared = oracle.attention_fwd_bwd(q, k, v, do, *w.vectors())
+    stacked = [np.repeat(x[:, None, :], 4, axis=1) for x in w.vectors()]
+    per_head = oracle.attention_fwd_bwd(q, k, v, do, *stacked)
+    for a, b in zip(shared, per_head):
+        assert np.array_equal(a, b)
+
+
+def test_per_head_rows_and_cols_consistent():
+    n, d = 120, 16
+    w = workloads.random_intervals(5, n, batch=1, heads_q=4, heads_kv=1, mask_heads=2)
+    q, do = rand((1, 4, n, d), 1), rand((1, 4, n, d), 2)
+    k, v = rand((1, 1, n, d), 3), rand((1, 1, n, d), 4)
+    O, LSE, dQ, dK, dV = oracle.attention_fwd_bwd(q, k, v, do, *w.vectors())
+    rows = [0, 31, 119]
+    for h in range(4):
+        Or, Lr, dQr = oracle.attention_rows(q, k, v, do, *w.vectors(), 0, h, rows)
+        assert np.abs(Or - O[0, h, rows]).max() < 1e-13
+        assert np.abs(dQr - dQ[0, h, rows]).max() < 1e-13
+    cols = [0, 60, 119]
+    dKc, dVc = oracle.attention_cols(q, k, v, do, *w.vectors(), 0, 0, cols, row_block=16)
+    assert np.abs(dKc - dK[0, 0, cols]).max() < 1e-12
+    assert np.abs(dVc - dV[0, 0, cols]).max() < 1e-12

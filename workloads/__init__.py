@@ -36,7 +36,7 @@ class Workload:
     heads_kv: int
     seqlen: int
     head_dim: int
-    lts: np.ndarray          # int32 [B][N]
+    lts: np.ndarray          # int32 [B][N], or [B][H_m][N] for per-head sets
     lte: np.ndarray
     uts: np.ndarray
     ute: np.ndarray
@@ -45,6 +45,11 @@ class Workload:
 
     def vectors(self):
         return self.lts, self.lte, self.uts, self.ute
+
+    @property
+    def mask_heads(self) -> int:
+        """Vector sets per batch row (1 unless the vectors are [B][H_m][N])."""
+        return 1 if self.lts.ndim == 2 else self.lts.shape[1]
 
 
 def _empty_vectors(batch: int, n: int):
@@ -199,19 +204,44 @@ def full_attention_partial_tiles(n: int, batch: int = 1, heads_q: int = 1,
 
 
 def random_intervals(seed: int, n: int, batch: int = 1, heads_q: int = 1,
-                     heads_kv: int = 1, p_empty: float = 0.2) -> Workload:
+                     heads_kv: int = 1, p_empty: float = 0.2, mask_heads: int = 0) -> Workload:
     """Adversarial vectors: both intervals of every column are random, may be
-    empty (start >= end), may cover every row, and may overlap."""
+    empty (start >= end), may cover every row, and may overlap.  mask_heads > 0 draws
+    that many independent sets per batch row ([B][H_m][N])."""
     rng = np.random.default_rng(seed)
-    a = rng.integers(0, n + 1, (4, batch, n))
+    shape = (batch, n) if mask_heads <= 0 else (batch, mask_heads, n)
+    a = rng.integers(0, n + 1, (4,) + shape)
     lts = np.minimum(a[0], a[1]); lte = np.maximum(a[0], a[1])
     uts = np.minimum(a[2], a[3]); ute = np.maximum(a[2], a[3])
-    e1 = rng.random((batch, n)) < p_empty
-    e2 = rng.random((batch, n)) < p_empty
+    e1 = rng.random(shape) < p_empty
+    e2 = rng.random(shape) < p_empty
     lts = np.where(e1, lte, lts)            # empty lower interval (start == end)
     uts = np.where(e2, ute + 1, uts)         # empty upper interval (start > end)
     uts = np.minimum(uts, n)
     return _finish("random_intervals", batch, heads_q, heads_kv, n, (lts, lte, uts, ute), seed, {})
+
+
+def per_head_windows(seed: int = 0, n: int = 32768, batch: int = 1, heads_q: int = 32,
+                     heads_kv: int = 8, mask_heads: int = 8, windows=None,
+                     sinks: int = 64) -> Workload:
+    """Per-head masks: causal sliding windows whose width differs by head, local heads
+    next to global ones.  Set m hides key j from rows < j and, unless j is one of the
+    first `sinks` keys, from rows >= j + W_m, with W_m = windows[m % len(windows)]
+    (default n/64, n/32, n/16, n/8, n/4, n/2 and two global causal sets).  The work per
+    head therefore differs by up to 30x.  Deterministic; `seed` is recorded only."""
+    if windows is None:
+        windows = [n // 64, n // 32, n // 16, n // 8, n // 4, n // 2, n, n]
+    lts, lte, uts, ute = (np.repeat(x[:, None, :], mask_heads, axis=1)
+                          for x in _empty_vectors(batch, n))
+    j = np.arange(n)
+    for m in range(mask_heads):
+        w = int(windows[m % len(windows)])
+        ute[:, m] = j
+        lts[:, m] = np.minimum(j + w, n)
+        lts[:, m, :sinks] = n
+    return _finish("per_head_windows", batch, heads_q, heads_kv, n, (lts, lte, uts, ute), seed,
+                   {"windows": [int(windows[m % len(windows)]) for m in range(mask_heads)],
+                    "sinks": sinks})
 
 
 # The five benchmark workloads, in order.  Shapes and mask families follow the
@@ -225,9 +255,16 @@ CONFIGS = {
 }
 CONFIG_NAMES = list(CONFIGS)
 
+# Variants beyond the five (widening the mask family the same kernels take).
+VARIANTS = {
+    # per-head masks: 32 query heads, 8 kv heads, one window per kv head's group
+    "v1_per_head_windows_32k": lambda seed=0: per_head_windows(seed),
+}
+VARIANT_NAMES = list(VARIANTS)
+
 
 def make_workload(name: str, seed: int = 0) -> Workload:
-    return CONFIGS[name](seed)
+    return (CONFIGS[name] if name in CONFIGS else VARIANTS[name])(seed)
 
 
 def make_tensors(w: Workload, seed: int | None = None, device: str = "cpu",
