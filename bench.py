@@ -53,18 +53,32 @@ DEFAULT_WORKLOAD = "c2_prefix_lm_doc_8k"
 def attended_pairs(w):
     """Attended (q, k) pairs summed over batch rows and query heads, by interval
     arithmetic on the column vectors (N_q = w.seqlen rows minus the union of the two
-    hidden intervals, per key column)."""
+    hidden intervals, per key column).  Per-head vectors [B][H_m][N] count each set once
+    per query head that uses it (H_q / H_m heads)."""
+    vecs = [np.asarray(x, dtype=np.int64) for x in w.vectors()]
+    if vecs[0].ndim == 2:
+        vecs = [x[:, None, :] for x in vecs]
+    hm = vecs[0].shape[1]
     total = 0
     n = w.seqlen
     for b in range(w.batch):
-        lts, lte, uts, ute = (np.asarray(x[b], dtype=np.int64) for x in w.vectors())
-        a1, b1 = np.clip(lts, 0, n), np.clip(lte, 0, n)
-        a2, b2 = np.clip(uts, 0, n), np.clip(ute, 0, n)
-        l1, l2 = np.maximum(b1 - a1, 0), np.maximum(b2 - a2, 0)
-        inter = np.maximum(np.minimum(b1, b2) - np.maximum(a1, a2), 0)
-        inter = np.where((l1 > 0) & (l2 > 0), inter, 0)
-        total += int((n - (l1 + l2 - inter)).sum())
-    return total * w.heads_q
+        for m in range(hm):
+            lts, lte, uts, ute = (x[b, m] for x in vecs)
+            a1, b1 = np.clip(lts, 0, n), np.clip(lte, 0, n)
+            a2, b2 = np.clip(uts, 0, n), np.clip(ute, 0, n)
+            l1, l2 = np.maximum(b1 - a1, 0), np.maximum(b2 - a2, 0)
+            inter = np.maximum(np.minimum(b1, b2) - np.maximum(a1, a2), 0)
+            inter = np.where((l1 > 0) & (l2 > 0), inter, 0)
+            total += int((n - (l1 + l2 - inter)).sum())
+    return total * (w.heads_q // hm)
+
+
+def head_vectors(w, b, h):
+    """The four vectors [1][N] query head h of batch row b uses."""
+    if w.lts.ndim == 2:
+        return [x[b:b + 1] for x in w.vectors()]
+    m = h // (w.heads_q // w.mask_heads)
+    return [x[b:b + 1, m] for x in w.vectors()]
 
 
 def source_digest():
@@ -322,7 +336,7 @@ def cpu_baseline(w, q, k, v, do, budget_s):
         for h in heads:
             kvh = h // g
             f = lambda t, hh: t[b:b + 1, hh:hh + 1].float().cpu().numpy().astype(np.float64)
-            sub = [x[b:b + 1] for x in w.vectors()]
+            sub = head_vectors(w, b, h)
             args = (f(q, h), f(k, kvh), f(v, kvh), f(do, h))
             t0 = time.perf_counter()
             oracle.attention_fwd_bwd(*args, *sub)
@@ -347,7 +361,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=workloads.CONFIG_NAMES)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    choices=workloads.CONFIG_NAMES + workloads.VARIANT_NAMES)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline sample (0 = skip)")
@@ -394,10 +409,10 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty((w.batch, w.heads_q, w.seqlen), dtype=torch.float32, device=dev)
     grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-    ws_f = torch.empty(fm.workspace_size(w.batch, w.heads_q, w.heads_kv, w.seqlen, fm.OP_FWD),
-                       dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(fm.workspace_size(w.batch, w.heads_q, w.heads_kv, w.seqlen, fm.OP_BWD),
-                       dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(fm.workspace_size(w.batch, w.heads_q, w.heads_kv, w.seqlen, fm.OP_FWD,
+                                         mask_heads=w.mask_heads), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(fm.workspace_size(w.batch, w.heads_q, w.heads_kv, w.seqlen, fm.OP_BWD,
+                                         mask_heads=w.mask_heads), dtype=torch.uint8, device=dev)
     A = attended_pairs(w)
     d = w.head_dim
 
@@ -466,8 +481,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": w.batch, "heads_q": w.heads_q,
-                   "heads_kv": w.heads_kv, "seq_len": w.seqlen, "head_dim": d,
-                   "attended_pairs": A, "seed": args.seed},
+                   "heads_kv": w.heads_kv, "mask_heads": w.mask_heads, "seq_len": w.seqlen,
+                   "head_dim": d, "attended_pairs": A, "seed": args.seed},
         "pct_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
         "kernels": {kname: {"ms": round(t, 4), "algorithmic_tflops": round(tflops[kname], 2)}
                     for kname, (t, _) in kernels.items()},

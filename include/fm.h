@@ -31,12 +31,17 @@
  *      Q, O, dO, dQ  bf16  [B][H_q][N_q][d]
  *      K, V, dK, dV  bf16  [B][H_kv][N_k][d]
  *      LSE           fp32  [B][H_q][N_q]    natural log; -inf for a row that sees no key
- *      LTS/LTE/UTS/UTE int32 [B][N_k]       query-row bounds in [0, N_q], one set per
- *                                           batch row, shared by all heads
+ *      LTS/LTE/UTS/UTE int32 [B][H_m][N_k]  query-row bounds in [0, N_q]; H_m =
+ *                                           mask_heads sets per batch row (1: one set
+ *                                           shared by all heads)
  *    N_q < N_k is one context-parallel rank's share of the query rows: its chunks,
  *    concatenated in ascending order, against every key, with the vectors renumbered
  *    into its own rows by fm_localize_mask (FlashMask-3 page, §3.2).
  *  - GQA.  Query head h reads kv head h / (H_q / H_kv).
+ *  - Per-head masks (a variant the FlashMask-3 page lists among its extensions without
+ *    defining it).  Query head h uses vector set h / (H_q / H_m): contiguous groups of
+ *    query heads share a set, as for GQA; H_m = H_q gives every query head its own.
+ *    Tiles are classified per mask row (b, m), B * H_m of them.
  *  - Rows that see no key get O = 0, LSE = -inf, dQ = 0 and add nothing to dK/dV.
  *  - Errors.  Arguments are validated on the host before anything is enqueued; on an
  *    error nothing is launched and the outputs are untouched.  Vector values outside
@@ -66,9 +71,13 @@ typedef enum { FM_OP_CLASSIFY = 0, FM_OP_FWD = 1, FM_OP_BWD = 2 } fm_op;
 /* Problem shape.  batch, heads and the lengths may be 0 (nothing to do beyond zero
  * outputs, FM_OK); head_dim must be 128.  softmax_scale <= 0 selects 1/sqrt(head_dim).
  * seqlen is N_q; seqlen_kv is N_k, with 0 meaning N_k = N_q (so N_q > 0 rows without
- * keys cannot be expressed; their result is O = 0, LSE = -inf).  Limits: N_q, N_k <= 2^22
- * and batch * ceil(N_q/block_q) and batch * ceil(N_k/block_k) at most 8192 work blocks
- * (the LPT sort runs in one workgroup's LDS); larger problems return FM_ERR_UNSUPPORTED. */
+ * keys cannot be expressed; their result is O = 0, LSE = -inf).  mask_heads is H_m, the
+ * vector sets per batch row; 0 means 1.  H_m must divide heads_q (when heads_q > 0) and
+ * either divide heads_kv or be a multiple of it (so that one kv head's query heads never
+ * straddle a mask set boundary partway); otherwise FM_ERR_INVALID_ARG.  Limits: N_q, N_k
+ * <= 2^22 and batch * H_m * ceil(N_q/block_q) and batch * H_m * ceil(N_k/block_k) at
+ * most 8192 work blocks (the LPT sort runs in one workgroup's LDS); larger problems return
+ * FM_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t batch;
   int32_t heads_q;
@@ -77,9 +86,10 @@ typedef struct {
   int32_t head_dim;
   float softmax_scale;
   int32_t seqlen_kv;
+  int32_t mask_heads;
 } fm_problem;
 
-/* The four column vectors, each int32 [B][N_k] in device memory. */
+/* The four column vectors, each int32 [B][H_m][N_k] in device memory. */
 typedef struct {
   const int32_t* lts;
   const int32_t* lte;
@@ -88,18 +98,18 @@ typedef struct {
 } fm_mask;
 
 /* Outputs of fm_classify_tiles, all device memory, nQB = ceil(N_q/block_q),
- * nKB = ceil(N_k/block_k):
- *   block_minmax [B][nKB][8]  int32: min,max of LTS, LTE, UTS, UTE over the block's columns
- *   tile_class   [B][nQB][nKB] uint8: 0 skipped, 1 partial, 2 unmasked
- *   q_queue      [B][nQB][nKB] int32: per Q-block the non-skipped KV blocks, right to left
+ * nKB = ceil(N_k/block_k), R = B * H_m mask rows (r = b * H_m + m):
+ *   block_minmax [R][nKB][8]  int32: min,max of LTS, LTE, UTS, UTE over the block's columns
+ *   tile_class   [R][nQB][nKB] uint8: 0 skipped, 1 partial, 2 unmasked
+ *   q_queue      [R][nQB][nKB] int32: per Q-block the non-skipped KV blocks, right to left
  *                (descending kb), each entry kb | (partial << 31); then -1 to the end
- *   q_count      [B][nQB][2]   int32: {n_partial, n_unmasked} per Q-block
- *   k_queue      [B][nKB][nQB] int32: per KV block the non-skipped Q-blocks, ascending,
+ *   q_count      [R][nQB][2]   int32: {n_partial, n_unmasked} per Q-block
+ *   k_queue      [R][nKB][nQB] int32: per KV block the non-skipped Q-blocks, ascending,
  *                each entry qb | (partial << 31); then -1 to the end
- *   k_count      [B][nKB][2]   int32: {n_partial, n_unmasked} per KV block
- *   q_order      [B*nQB]       int32: Q-blocks (b*nQB + qb) sorted by cost
+ *   k_count      [R][nKB][2]   int32: {n_partial, n_unmasked} per KV block
+ *   q_order      [R*nQB]       int32: Q-blocks (r*nQB + qb) sorted by cost
  *                11*n_partial + 10*n_unmasked descending, ties ascending
- *   k_order      [B*nKB]       int32: the same over KV blocks (b*nKB + kb)          */
+ *   k_order      [R*nKB]       int32: the same over KV blocks (r*nKB + kb)          */
 typedef struct {
   int32_t* block_minmax;
   uint8_t* tile_class;
@@ -158,32 +168,35 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
  * then runs two kernels that recompute P = exp(S - LSE) on queued tiles only: a
  * Q-block-outer one that also forms D = rowsum(dO * O) (fp32) and accumulates dQ in
  * registers (the forward's LPT order), and a KV-block-outer one accumulating dK and dV
- * (LPT order over KV blocks).  When heads_q / heads_kv exceeds 4, several workgroups add
- * into one KV head's dK/dV: fp32 accumulators in `ws`, converted to bf16 at the end;
- * otherwise each workgroup stores its bf16 rows directly.  Any N >= 0. */
+ * (LPT order over KV blocks).  A dK/dV work item covers at most 4 query heads of one kv
+ * head that share one mask set; when a kv head's KV block needs more than one item
+ * (heads_q / heads_kv above 4, or per-head masks splitting the group), the items add into
+ * fp32 accumulators in `ws`, converted to bf16 at the end; otherwise each workgroup stores
+ * its bf16 rows directly.  Any N >= 0. */
 fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dout, const fm_mask* m,
                       void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream,
                       const fm_kernel_events* events);
 
-/* Dense expansion of rows [row0, row1) of batch row b: dense[(i-row0)*N_k + j] = 1 if
- * the mask hides (i, j), else 0 -- the same predicate the attention kernels apply on
- * partial tiles.  For checking only.  0 <= b < batch, 0 <= row0 <= row1 <= N_q. */
+/* Dense expansion of rows [row0, row1) of mask row b (b = batch row * H_m + mask set):
+ * dense[(i-row0)*N_k + j] = 1 if the mask hides (i, j), else 0 -- the same predicate the
+ * attention kernels apply on partial tiles.  For checking only.  0 <= b < batch * H_m,
+ * 0 <= row0 <= row1 <= N_q. */
 fm_status fm_debug_expand_mask(const fm_problem* p, const fm_mask* m, int32_t b, int32_t row0,
                                int32_t row1, uint8_t* dense, void* stream);
 
 /* Mask localization for one context-parallel rank (FlashMask-3 page, §3.2): the rank
  * owns the query chunks [offsets[i], offsets[i] + chunk_len), i < n_chunks, offsets
  * strictly ascending by at least chunk_len (non-overlapping), and every key.  Each bound
- * x of the global vectors (`global`, int32 [B][N_k] with values in [0, N]) becomes the
- * number of the rank's rows before global row x, sum_i clamp(x - offsets[i], 0,
- * chunk_len), written to the arrays of `local` (int32 [B][N_k] each, values in
+ * x of the global vectors (`global`, int32 [B][H_m][N_k] with values in [0, N]) becomes
+ * the number of the rank's rows before global row x, sum_i clamp(x - offsets[i], 0,
+ * chunk_len), written to the arrays of `local` (int32 [B][H_m][N_k] each, values in
  * [0, n_chunks * chunk_len]).
  * Theorem 1 of the page: the local intervals select exactly the rank's rows of the global
  * intervals, so attention with p->seqlen = n_chunks * chunk_len local query rows (the
  * chunks' rows of Q concatenated in order) against all N_k keys gives those rows of the
- * global result.  p->seqlen_kv (or p->seqlen when 0) is N_k; p->heads_* and head_dim are
- * not used.  offsets: device int32 [n_chunks]; 1 <= n_chunks <= 4096, chunk_len >= 1.
+ * global result.  p->seqlen_kv (or p->seqlen when 0) is N_k and p->mask_heads is H_m
+ * (0 means 1, any H_m >= 1 accepted here); p->heads_* and head_dim are not used.  offsets: device int32 [n_chunks]; 1 <= n_chunks <= 4096, chunk_len >= 1.
  * Offsets that are not ascending and non-overlapping give unspecified (but memory-safe)
  * results. */
 typedef struct {

@@ -47,7 +47,7 @@ class Problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32),
                 ("heads_kv", ctypes.c_int32), ("seqlen", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
-                ("seqlen_kv", ctypes.c_int32)]
+                ("seqlen_kv", ctypes.c_int32), ("mask_heads", ctypes.c_int32)]
 
 
 class MaskOut(ctypes.Structure):
@@ -120,16 +120,29 @@ def _check(status, where):
         raise FMError(status, where)
 
 
-def _problem(batch, heads_q, heads_kv, seqlen, scale=None, head_dim=HEAD_DIM, seqlen_kv=0):
+def _problem(batch, heads_q, heads_kv, seqlen, scale=None, head_dim=HEAD_DIM, seqlen_kv=0,
+             mask_heads=0):
     return Problem(int(batch), int(heads_q), int(heads_kv), int(seqlen), int(head_dim),
-                   float(scale) if scale is not None else 0.0, int(seqlen_kv))
+                   float(scale) if scale is not None else 0.0, int(seqlen_kv), int(mask_heads))
 
 
 def _mask(lts, lte, uts, ute):
     for t in (lts, lte, uts, ute):
         if t.dtype != torch.int32 or not t.is_contiguous():
-            raise ValueError("mask vectors must be contiguous int32 tensors [B][N]")
+            raise ValueError("mask vectors must be contiguous int32 tensors [B][N] or [B][H_m][N]")
+        if t.shape != lts.shape:
+            raise ValueError("the four mask vectors must have one shape")
     return Mask(lts.data_ptr(), lte.data_ptr(), uts.data_ptr(), ute.data_ptr())
+
+
+def _mask_dims(lts):
+    """(B, H_m, N_k) of vectors [B][N_k] (one set per batch row, H_m = 1) or
+    [B][H_m][N_k] (per-head sets: query head h uses set h // (H_q / H_m))."""
+    if lts.dim() == 2:
+        return lts.shape[0], 1, lts.shape[1]
+    if lts.dim() == 3:
+        return tuple(lts.shape)
+    raise ValueError("mask vectors must be [B][N] or [B][H_m][N]")
 
 
 def _stream(device, stream=None):
@@ -149,10 +162,12 @@ def tile_shape(op: int):
 
 
 def workspace_size(batch, heads_q, heads_kv, seqlen, op, block_q=0, block_k=0, head_dim=HEAD_DIM,
-                   seqlen_kv=0):
-    """Workspace bytes for N_q = seqlen query rows and N_k = seqlen_kv keys (0: N_q)."""
+                   seqlen_kv=0, mask_heads=0):
+    """Workspace bytes for N_q = seqlen query rows, N_k = seqlen_kv keys (0: N_q) and
+    mask_heads vector sets per batch row (0: 1)."""
     n = ctypes.c_size_t()
-    p = _problem(batch, heads_q, heads_kv, seqlen, head_dim=head_dim, seqlen_kv=seqlen_kv)
+    p = _problem(batch, heads_q, heads_kv, seqlen, head_dim=head_dim, seqlen_kv=seqlen_kv,
+                 mask_heads=mask_heads)
     _check(library().fm_workspace_size(ctypes.byref(p), int(op), int(block_q), int(block_k),
                                        ctypes.byref(n)), "fm_workspace_size")
     return n.value
@@ -192,20 +207,22 @@ def ipo_balance(weights, ranks, stages=3):
 def classify_tiles(lts, lte, uts, ute, block_q, block_k, heads_q=1, heads_kv=1, stream=None,
                    out=None, ws=None, seqlen_q=None):
     """Run fm_classify_tiles; returns a dict of device tensors (see fm_tiles in fm.h).
-    The vectors are [B][N_k]; `seqlen_q` is N_q (default N_k).  `out` (a dict as returned
-    by an earlier call of the same shape) and `ws` (uint8 device tensor of at least
-    workspace_size(..., OP_CLASSIFY, block_q, block_k) bytes) may be passed to reuse
-    buffers."""
-    B, Nk = lts.shape
+    The vectors are [B][N_k] or [B][H_m][N_k] (tiles per mask row b * H_m + m); `seqlen_q`
+    is N_q (default N_k).  `out` (a dict as returned by an earlier call of the same shape)
+    and `ws` (uint8 device tensor of at least workspace_size(..., OP_CLASSIFY, block_q,
+    block_k) bytes) may be passed to reuse buffers."""
+    B, Hm, Nk = _mask_dims(lts)
+    if Hm > 1 and heads_q == 1 and heads_kv == 1:
+        heads_q = Hm                      # the heads play no part in the classification
     N = Nk if seqlen_q is None else int(seqlen_q)
     dev = lts.device
     nqb, nkb = -(-N // block_q), -(-Nk // block_k)
     if out is None:
-        out = _tile_buffers(B, N, nqb, nkb, dev)
+        out = _tile_buffers(B * Hm, N, nqb, nkb, dev)
     tiles = Tiles(*(out[n].data_ptr() if out[n].numel() else 0 for n, _ in Tiles._fields_))
-    p = _problem(B, heads_q, heads_kv, N, seqlen_kv=Nk)
+    p = _problem(B, heads_q, heads_kv, N, seqlen_kv=Nk, mask_heads=Hm)
     nbytes = workspace_size(B, heads_q, heads_kv, N, OP_CLASSIFY, block_q, block_k,
-                            seqlen_kv=Nk)
+                            seqlen_kv=Nk, mask_heads=Hm)
     if ws is None:
         ws = _workspace(nbytes, dev)
     elif ws.numel() < nbytes:
@@ -231,8 +248,9 @@ def _tile_buffers(B, N, nqb, nkb, dev):
     }
 
 
-def _shapes(q, k):
-    """(B, H_q, H_kv, N_q, N_k, d) from Q [B][H_q][N_q][d] and K [B][H_kv][N_k][d]."""
+def _shapes(q, k, lts):
+    """(B, H_q, H_kv, N_q, N_k, d, H_m) from Q [B][H_q][N_q][d], K [B][H_kv][N_k][d] and
+    the vectors [B][N_k] or [B][H_m][N_k]."""
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("expected Q [B][H_q][N_q][d] and K/V [B][H_kv][N_k][d]")
     B, Hq, N, d = q.shape
@@ -241,7 +259,10 @@ def _shapes(q, k):
     if k.shape[2] == 0 and N > 0:
         # fm_problem.seqlen_kv = 0 means "as many keys as rows"
         raise ValueError("query rows without keys cannot be expressed (seqlen_kv = 0 means N_q)")
-    return B, Hq, k.shape[1], N, k.shape[2], d
+    Bm, Hm, Nm = _mask_dims(lts)
+    if Bm != B or Nm != k.shape[2]:
+        raise ValueError("mask vectors must be [B][N_k] or [B][H_m][N_k]")
+    return B, Hq, k.shape[1], N, k.shape[2], d, Hm
 
 
 def _bf16(*ts):
@@ -267,14 +288,15 @@ def _events(ev):
 def attn_fwd(q, k, v, lts, lte, uts, ute, scale=None, ws=None, out=None, lse=None, stream=None,
              events=None):
     """O (bf16 [B][H_q][N_q][d]) and LSE (fp32 [B][H_q][N_q], natural log) via fm_attn_fwd;
-    K/V are [B][H_kv][N_k][d] and the vectors [B][N_k].
+    K/V are [B][H_kv][N_k][d] and the vectors [B][N_k] or, one set per group of H_q / H_m
+    query heads, [B][H_m][N_k].
     `events`: optional (start, stop) torch.cuda.Event pair timing the attention kernel."""
     _bf16(q, k, v)
-    B, Hq, Hkv, N, Nk, d = _shapes(q, k)
+    B, Hq, Hkv, N, Nk, d, Hm = _shapes(q, k, lts)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    p = _problem(B, Hq, Hkv, N, scale, head_dim=d, seqlen_kv=Nk)
-    nbytes = workspace_size(B, Hq, Hkv, N, OP_FWD, head_dim=d, seqlen_kv=Nk)
+    p = _problem(B, Hq, Hkv, N, scale, head_dim=d, seqlen_kv=Nk, mask_heads=Hm)
+    nbytes = workspace_size(B, Hq, Hkv, N, OP_FWD, head_dim=d, seqlen_kv=Nk, mask_heads=Hm)
     w = _workspace(nbytes, q.device, ws)
     m = _mask(lts, lte, uts, ute)
     _check(library().fm_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(m),
@@ -288,12 +310,12 @@ def attn_bwd(q, k, v, o, lse, dout, lts, lte, uts, ute, scale=None, ws=None, gra
     """(dQ, dK, dV) in bf16 via fm_attn_bwd.  `events`: optional (start, stop, start2,
     stop2) torch.cuda.Event objects timing the dK/dV kernel and the dQ kernel."""
     _bf16(q, k, v, o, dout)
-    B, Hq, Hkv, N, Nk, d = _shapes(q, k)
+    B, Hq, Hkv, N, Nk, d, Hm = _shapes(q, k, lts)
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = grads
-    p = _problem(B, Hq, Hkv, N, scale, head_dim=d, seqlen_kv=Nk)
-    nbytes = workspace_size(B, Hq, Hkv, N, OP_BWD, head_dim=d, seqlen_kv=Nk)
+    p = _problem(B, Hq, Hkv, N, scale, head_dim=d, seqlen_kv=Nk, mask_heads=Hm)
+    nbytes = workspace_size(B, Hq, Hkv, N, OP_BWD, head_dim=d, seqlen_kv=Nk, mask_heads=Hm)
     w = _workspace(nbytes, q.device, ws)
     m = _mask(lts, lte, uts, ute)
     _check(library().fm_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
@@ -304,10 +326,11 @@ def attn_bwd(q, k, v, o, lse, dout, lts, lte, uts, ute, scale=None, ws=None, gra
 
 
 def debug_expand_mask(lts, lte, uts, ute, b, row0, row1, stream=None, seqlen_q=None):
-    """uint8 [row1-row0][N_k] dense expansion (1 = hidden) by the kernels' predicate."""
-    B, N = lts.shape
+    """uint8 [row1-row0][N_k] dense expansion (1 = hidden) by the kernels' predicate, of
+    mask row b (batch row * H_m + set for per-head vectors)."""
+    B, Hm, N = _mask_dims(lts)
     dense = torch.empty((row1 - row0, N), dtype=torch.uint8, device=lts.device)
-    p = _problem(B, 1, 1, N if seqlen_q is None else int(seqlen_q), seqlen_kv=N)
+    p = _problem(B, Hm, 1, N if seqlen_q is None else int(seqlen_q), seqlen_kv=N, mask_heads=Hm)
     m = _mask(lts, lte, uts, ute)
     _check(library().fm_debug_expand_mask(ctypes.byref(p), ctypes.byref(m), int(b), int(row0),
                                           int(row1), _ptr(dense), _stream(lts.device, stream)),
@@ -318,13 +341,14 @@ def debug_expand_mask(lts, lte, uts, ute, b, row0, row1, stream=None, seqlen_q=N
 def localize_mask(lts, lte, uts, ute, offsets, chunk_len, out=None, stream=None):
     """fm_localize_mask: the vectors [B][N_k] renumbered into the rows of a rank that owns
     the query chunks [offsets[i], offsets[i] + chunk_len) (offsets: int32 device tensor,
-    ascending, non-overlapping).  Returns four int32 tensors [B][N_k]."""
-    B, N = lts.shape
+    ascending, non-overlapping).  Returns four int32 tensors of the vectors' shape ([B][N_k]
+    or [B][H_m][N_k])."""
+    B, Hm, N = _mask_dims(lts)
     if offsets.dtype != torch.int32 or not offsets.is_contiguous() or offsets.dim() != 1:
         raise ValueError("offsets must be a contiguous int32 tensor [n_chunks]")
     if out is None:
         out = tuple(torch.empty_like(lts) for _ in range(4))
-    p = _problem(B, 1, 1, 0, seqlen_kv=N)
+    p = _problem(B, 1, 1, 0, seqlen_kv=N, mask_heads=Hm)
     m = _mask(lts, lte, uts, ute)
     mo = MaskOut(*(t.data_ptr() for t in out))
     _check(library().fm_localize_mask(ctypes.byref(p), ctypes.byref(m), _ptr(offsets),

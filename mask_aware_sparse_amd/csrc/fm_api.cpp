@@ -20,13 +20,18 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // N_q (query rows) and N_k (keys); N_k = N_q unless seqlen_kv is set.
 inline int32_t nq_of(const fm_problem* p) { return p->seqlen; }
 inline int32_t nk_of(const fm_problem* p) { return p->seqlen_kv > 0 ? p->seqlen_kv : p->seqlen; }
+// H_m mask sets per batch row (0 means 1) and the mask rows B * H_m the tiles are built for.
+inline int32_t hm_of(const fm_problem* p) { return p->mask_heads > 0 ? p->mask_heads : 1; }
+inline int64_t mask_rows(const fm_problem* p) { return (int64_t)p->batch * hm_of(p); }
 
 // Problem checks shared by every entry point.
 fm_status check_problem(const fm_problem* p) {
   if (!p) return FM_ERR_INVALID_ARG;
-  if (p->batch < 0 || p->heads_q < 0 || p->heads_kv < 1 || p->seqlen < 0 || p->seqlen_kv < 0)
+  if (p->batch < 0 || p->heads_q < 0 || p->heads_kv < 1 || p->seqlen < 0 || p->seqlen_kv < 0 ||
+      p->mask_heads < 0)
     return FM_ERR_INVALID_ARG;
   if (p->heads_q % p->heads_kv != 0) return FM_ERR_INVALID_ARG;
+  if (!fm::head_map_valid(p->heads_q, p->heads_kv, hm_of(p))) return FM_ERR_INVALID_ARG;
   if (!(p->softmax_scale <= 0.f || std::isfinite(p->softmax_scale))) return FM_ERR_INVALID_ARG;
   if (p->head_dim != fm::kHeadDim) return FM_ERR_UNSUPPORTED;
   // per-head buffers < 2 GiB
@@ -42,7 +47,7 @@ bool empty_problem(const fm_problem* p) {
 
 fm_status check_mask(const fm_problem* p, const fm_mask* m) {
   if (!m) return FM_ERR_INVALID_ARG;
-  if ((int64_t)p->batch * nk_of(p) == 0) return FM_OK;
+  if (mask_rows(p) * nk_of(p) == 0) return FM_OK;
   if (!m->lts || !m->lte || !m->uts || !m->ute) return FM_ERR_INVALID_ARG;
   return FM_OK;
 }
@@ -59,8 +64,8 @@ Blocks blocks(const fm_problem* p, int bq, int bk) {
 }
 
 fm_status check_sort_limits(const fm_problem* p, const Blocks& nb) {
-  if ((int64_t)p->batch * nb.nQB > fm::kMaxSortItems) return FM_ERR_UNSUPPORTED;
-  if ((int64_t)p->batch * nb.nKB > fm::kMaxSortItems) return FM_ERR_UNSUPPORTED;
+  if (mask_rows(p) * nb.nQB > fm::kMaxSortItems) return FM_ERR_UNSUPPORTED;
+  if (mask_rows(p) * nb.nKB > fm::kMaxSortItems) return FM_ERR_UNSUPPORTED;
   return FM_OK;
 }
 
@@ -69,8 +74,8 @@ struct ClassifyWs { size_t q_cost, k_cost, total; };
 ClassifyWs classify_ws(const fm_problem* p, const Blocks& nb) {
   ClassifyWs w{};
   size_t off = 0;
-  w.q_cost = off; off += align_up((size_t)p->batch * nb.nQB * 4);
-  w.k_cost = off; off += align_up((size_t)p->batch * nb.nKB * 4);
+  w.q_cost = off; off += align_up((size_t)mask_rows(p) * nb.nQB * 4);
+  w.k_cost = off; off += align_up((size_t)mask_rows(p) * nb.nKB * 4);
   w.total = off;
   return w;
 }
@@ -78,7 +83,7 @@ ClassifyWs classify_ws(const fm_problem* p, const Blocks& nb) {
 struct FwdWs { size_t mm, q_queue, q_count, q_cost, q_order, total; };
 FwdWs fwd_ws(const fm_problem* p, const Blocks& nb) {
   FwdWs w{};
-  const size_t B = p->batch;
+  const size_t B = mask_rows(p);  // tile structures are per mask row
   size_t off = 0;
   w.mm = off; off += align_up(B * nb.nKB * 8 * 4);
   w.q_queue = off; off += align_up(B * nb.nQB * nb.nKB * 4);
@@ -97,7 +102,9 @@ struct BwdWs {
 };
 BwdWs bwd_ws(const fm_problem* p, const Blocks& nk, const Blocks& nq) {
   BwdWs w{};
-  const size_t B = p->batch, rq = B * p->heads_q * nq_of(p), rk = B * p->heads_kv * nk_of(p);
+  const size_t rq = (size_t)p->batch * p->heads_q * nq_of(p);
+  const size_t rk = (size_t)p->batch * p->heads_kv * nk_of(p);
+  const size_t B = mask_rows(p);  // tile structures are per mask row
   size_t off = 0;
   w.mm_k = off; off += align_up(B * nk.nKB * 8 * 4);
   w.k_queue = off; off += align_up(B * nk.nKB * nk.nQB * 4);
@@ -111,10 +118,10 @@ BwdWs bwd_ws(const fm_problem* p, const Blocks& nk, const Blocks& nq) {
   w.q_order = off; off += align_up(B * nq.nQB * 4);
   w.lse2 = off; off += align_up(rq * 4);
   w.delta = off; off += align_up(rq * 4);
-  // fp32 dK/dV accumulators only when several workgroups share a KV block (query-head
-  // groups larger than one head chunk); otherwise the kernel stores bf16 directly
-  const int64_t g = p->heads_kv ? p->heads_q / p->heads_kv : 0;
-  w.acc = g > fm::kBwdHeadChunk;
+  // fp32 dK/dV accumulators only when several workgroups write one kv head's KV block
+  // (query-head groups larger than one head chunk, or split by per-head mask sets);
+  // otherwise the kernel stores bf16 directly
+  w.acc = fm::head_map(p->heads_q, p->heads_kv, hm_of(p)).writers > 1;
   if (w.acc) {
     w.dk = off; off += align_up(rk * fm::kHeadDim * 4);
     w.dv = off; off += align_up(rk * fm::kHeadDim * 4);
@@ -148,11 +155,9 @@ fm_status check_ws(void* ws, size_t have, size_t need) {
 }
 
 fm_status check_grid(const fm_problem* p, const Blocks& fwd, const Blocks& bwd) {
-  const int64_t g = p->heads_q / p->heads_kv;
-  const int64_t hc = g < fm::kBwdHeadChunk ? g : fm::kBwdHeadChunk;
-  const int64_t nch = hc ? cdiv(g, hc) : 0;
+  const fm::HeadMap hm = fm::head_map(p->heads_q, p->heads_kv, hm_of(p));
   if ((int64_t)p->batch * fwd.nQB * p->heads_q >= INT32_MAX) return FM_ERR_UNSUPPORTED;
-  if ((int64_t)p->batch * bwd.nKB * p->heads_kv * nch >= INT32_MAX) return FM_ERR_UNSUPPORTED;
+  if (mask_rows(p) * bwd.nKB * hm.kvpm * hm.cpk >= INT32_MAX) return FM_ERR_UNSUPPORTED;
   return FM_OK;
 }
 
@@ -235,10 +240,10 @@ fm_status fm_classify_tiles(const fm_problem* p, const fm_mask* m, int32_t block
   t.k_queue = out->k_queue;
   t.k_count = out->k_count;
   t.k_cost = at<int32_t>(ws, w.k_cost);
-  hipError_t e =
-      fm::launch_classify(mask_ptrs(m), p->batch, nq_of(p), nk_of(p), block_q, block_k, t, s);
-  if (e == hipSuccess) e = fm::launch_lpt_sort(t.q_cost, out->q_order, (int)(p->batch * nb.nQB), s);
-  if (e == hipSuccess) e = fm::launch_lpt_sort(t.k_cost, out->k_order, (int)(p->batch * nb.nKB), s);
+  const int R = (int)mask_rows(p);
+  hipError_t e = fm::launch_classify(mask_ptrs(m), R, nq_of(p), nk_of(p), block_q, block_k, t, s);
+  if (e == hipSuccess) e = fm::launch_lpt_sort(t.q_cost, out->q_order, (int)(R * nb.nQB), s);
+  if (e == hipSuccess) e = fm::launch_lpt_sort(t.k_cost, out->k_order, (int)(R * nb.nKB), s);
   return hip_status(e);
 }
 
@@ -265,15 +270,17 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
   t.q_queue = at<int32_t>(ws, w.q_queue);
   t.q_count = at<int32_t>(ws, w.q_count);
   t.q_cost = at<int32_t>(ws, w.q_cost);
-  hipError_t e = fm::launch_classify(mask_ptrs(m), p->batch, nq_of(p), nk_of(p),
-                                     fm::kFwdBlockQ, fm::kFwdBlockK, t, s);
+  const int R = (int)mask_rows(p);
+  hipError_t e = fm::launch_classify(mask_ptrs(m), R, nq_of(p), nk_of(p), fm::kFwdBlockQ,
+                                     fm::kFwdBlockK, t, s);
   int32_t* order = at<int32_t>(ws, w.q_order);
-  if (e == hipSuccess) e = fm::launch_lpt_sort(t.q_cost, order, (int)(p->batch * nb.nQB), s);
+  if (e == hipSuccess) e = fm::launch_lpt_sort(t.q_cost, order, (int)(R * nb.nQB), s);
   if (e == hipSuccess) {
     fm::FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.m = mask_ptrs(m); a.o = o; a.lse = lse;
     a.q_queue = t.q_queue; a.q_count = t.q_count; a.q_order = order;
-    a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.Nq = nq_of(p); a.Nk = nk_of(p);
+    a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.Hm = hm_of(p);
+    a.Nq = nq_of(p); a.Nk = nk_of(p);
     a.nQB = (int)nb.nQB; a.nKB = (int)nb.nKB;
     a.scale = scale_of(p);
     e = fm::launch_fwd(a, s, ev_start(events), ev_stop(events));
@@ -315,14 +322,14 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   tq.q_cost = at<int32_t>(ws, w.q_cost);
   int32_t* k_order = at<int32_t>(ws, w.k_order);
   int32_t* q_order = at<int32_t>(ws, w.q_order);
-  hipError_t e = fm::launch_classify(mask_ptrs(m), p->batch, nq_of(p), nk_of(p), fm::kBwdBlockQ,
+  const int R = (int)mask_rows(p);
+  hipError_t e = fm::launch_classify(mask_ptrs(m), R, nq_of(p), nk_of(p), fm::kBwdBlockQ,
                                      fm::kBwdBlockK, tk, s);
-  if (e == hipSuccess) e = fm::launch_lpt_sort(tk.k_cost, k_order, (int)(p->batch * nk.nKB), s);
+  if (e == hipSuccess) e = fm::launch_lpt_sort(tk.k_cost, k_order, (int)(R * nk.nKB), s);
   if (e == hipSuccess)
-    e = fm::launch_classify(mask_ptrs(m), p->batch, nq_of(p), nk_of(p), fm::kFwdBlockQ,
-                            fm::kFwdBlockK,
+    e = fm::launch_classify(mask_ptrs(m), R, nq_of(p), nk_of(p), fm::kFwdBlockQ, fm::kFwdBlockK,
                             tq, s);
-  if (e == hipSuccess) e = fm::launch_lpt_sort(tq.q_cost, q_order, (int)(p->batch * nq.nQB), s);
+  if (e == hipSuccess) e = fm::launch_lpt_sort(tq.q_cost, q_order, (int)(R * nq.nQB), s);
   if (e == hipSuccess) {
     fm::BwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout; a.m = mask_ptrs(m);
@@ -331,7 +338,8 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
     a.q_queue = tq.q_queue; a.q_count = tq.q_count; a.q_order = q_order;
     a.lse2 = at<float>(ws, w.lse2); a.delta = at<float>(ws, w.delta);
     if (w.acc) { a.dk_acc = at<float>(ws, w.dk); a.dv_acc = at<float>(ws, w.dv); }
-    a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.Nq = nq_of(p); a.Nk = nk_of(p);
+    a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.Hm = hm_of(p);
+    a.Nq = nq_of(p); a.Nk = nk_of(p);
     a.nQB_k = (int)nk.nQB; a.nKB_k = (int)nk.nKB;
     a.nQB_q = (int)nq.nQB; a.nKB_q = (int)nq.nKB;
     a.scale = scale_of(p);
@@ -352,7 +360,7 @@ fm_status fm_debug_expand_mask(const fm_problem* p, const fm_mask* m, int32_t b,
   fm_status st = check_problem(p);
   if (st != FM_OK) return st;
   if ((st = check_mask(p, m)) != FM_OK) return st;
-  if (b < 0 || b >= p->batch || row0 < 0 || row1 < row0 || row1 > nq_of(p))
+  if (b < 0 || b >= mask_rows(p) || row0 < 0 || row1 < row0 || row1 > nq_of(p))
     return FM_ERR_INVALID_ARG;
   if (row1 == row0 || nk_of(p) == 0) return FM_OK;
   if (!dense) return FM_ERR_INVALID_ARG;
@@ -364,12 +372,14 @@ fm_status fm_localize_mask(const fm_problem* p, const fm_mask* global, const int
                            int32_t n_chunks, int32_t chunk_len, const fm_mask_out* local,
                            void* stream) {
   if (!p || !global || !local) return FM_ERR_INVALID_ARG;
-  if (p->batch < 0 || p->seqlen < 0 || p->seqlen_kv < 0) return FM_ERR_INVALID_ARG;
+  if (p->batch < 0 || p->seqlen < 0 || p->seqlen_kv < 0 || p->mask_heads < 0)
+    return FM_ERR_INVALID_ARG;
   if (n_chunks < 1 || chunk_len < 1) return FM_ERR_INVALID_ARG;
   if (n_chunks > 4096 || nk_of(p) > (1 << 22)) return FM_ERR_UNSUPPORTED;
   if ((int64_t)n_chunks * chunk_len > (1 << 22)) return FM_ERR_UNSUPPORTED;
-  const int64_t cols = (int64_t)p->batch * nk_of(p);
+  const int64_t cols = mask_rows(p) * nk_of(p);
   if (cols == 0) return FM_OK;
+  if (cols > INT32_MAX) return FM_ERR_UNSUPPORTED;
   if (!offsets || !global->lts || !global->lte || !global->uts || !global->ute || !local->lts ||
       !local->lte || !local->uts || !local->ute)
     return FM_ERR_INVALID_ARG;

@@ -97,11 +97,12 @@ struct DkdvParams {
   const int32_t* __restrict__ k_queue;
   const int32_t* __restrict__ k_count;
   const int32_t* __restrict__ k_order;
-  float* __restrict__ dk_acc;  // fp32 accumulators (nch > 1)
+  float* __restrict__ dk_acc;  // fp32 accumulators (writers > 1)
   float* __restrict__ dv_acc;
-  bf16* __restrict__ dk;       // bf16 outputs (nch == 1)
+  bf16* __restrict__ dk;       // bf16 outputs (writers == 1)
   bf16* __restrict__ dv;
-  int B, Hq, Hkv, Nq, Nk, nQB, nKB, hc, nch;  // Nq query rows, Nk keys
+  int B, Hq, Hkv, Nq, Nk, nQB, nKB;  // Nq query rows, Nk keys
+  HeadMap hm;                        // mask sets, chunking and writers per KV block
   float c;      // scale * log2(e)
   float scale;  // softmax scale (applied to dK)
 };
@@ -113,14 +114,21 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
   const int l32 = lane & 31, hh = lane >> 5;
   const int N = p.Nk, Nq = p.Nq;  // N: keys (and mask columns)
 
-  const int per = p.Hkv * p.nch;
+  // workgroup: LPT item (mask row, KV block), then a kv head of that mask set, then a
+  // chunk of at most hc query heads of that kv head and set
+  const int cpk = p.hm.cpk, per = p.hm.kvpm * cpk;
   const int r = blockIdx.x / per, rem = blockIdx.x - r * per;
-  const int kvh = rem / p.nch, ch = rem - kvh * p.nch;
+  const int kvl = rem / cpk, ch = rem - kvl * cpk;
   const int item = p.k_order[r];
-  const int b = item / p.nKB, kb = item - b * p.nKB;
+  const int mr = item / p.nKB, kb = item - mr * p.nKB;
+  const int b = mr / p.hm.Hm;
   const int g = p.Hq / p.Hkv;
-  const int h0 = kvh * g + ch * p.hc;
-  const int nh = min(p.hc, kvh * g + g - h0);
+  const int hq0 = (mr - b * p.hm.Hm) * p.hm.qpm;  // first query head of the set
+  const int kvh = hq0 / g + kvl;
+  const int hs = max(kvh * g, hq0);              // first query head of (kv head, set)
+  const int h0 = hs + ch * p.hm.hc;
+  const int nh = min(p.hm.hc, hs + p.hm.gq - h0);
+  const bool direct = p.hm.writers == 1;
   const int nq = p.k_count[2 * item] + p.k_count[2 * item + 1];
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const uint32_t acc_bytes = (uint32_t)N * D * 4;
@@ -128,7 +136,7 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
   if (nh <= 0) return;
   if (nq == 0) {
     // no query row sees these keys: dK = dV = 0 (the accumulators start at zero)
-    if (p.nch == 1) {
+    if (direct) {
       const rsrc_t dkr = make_rsrc(p.dk + kvbase, head_bytes);
       const rsrc_t dvr = make_rsrc(p.dv + kvbase, head_bytes);
       const u32x4 z = {0u, 0u, 0u, 0u};
@@ -160,7 +168,7 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
   }
   if (hh == 0) {
     const uint32_t vb = (uint32_t)N * 4, vo = (uint32_t)key * 4;
-    const size_t mrow = (size_t)b * N;
+    const size_t mrow = (size_t)mr * N;
     sm.mv[wave * 32 + l32] = int4{(int)buf_load4(make_rsrc(p.m.lts + mrow, vb), vo, 0),
                                   (int)buf_load4(make_rsrc(p.m.lte + mrow, vb), vo, 0),
                                   (int)buf_load4(make_rsrc(p.m.uts + mrow, vb), vo, 0),
@@ -310,7 +318,7 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
   // ---- dK, dV of this workgroup's keys (keys past N dropped by the buffer bounds).  A
   // lane holds dimension d*32 + l32 of keys wave*32 + hh*4 + (i/4)*8 + i%4.
   const uint32_t kl = (uint32_t)((kb * BK + wave * 32 + hh * 4) * D + l32);
-  if (p.nch == 1) {
+  if (direct) {
     const rsrc_t dkr = make_rsrc(p.dk + kvbase, head_bytes);
     const rsrc_t dvr = make_rsrc(p.dv + kvbase, head_bytes);
 #pragma unroll
@@ -365,7 +373,7 @@ struct DqParams {
   const int32_t* __restrict__ q_queue;
   const int32_t* __restrict__ q_count;
   const int32_t* __restrict__ q_order;
-  int B, Hq, Hkv, Nq, Nk, nQB, nKB;  // Nq query rows, Nk keys
+  int B, Hq, Hkv, Hm, Nq, Nk, nQB, nKB;  // Nq query rows, Nk keys, Hm mask sets per batch row
   float c;      // scale * log2(e)
   float scale;  // softmax scale (applied to dQ)
 };
@@ -376,10 +384,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
 
+  // workgroup L: the (L % qpm)-th query head of the mask set of LPT item L / qpm
   const int L = xcd_logical((int)blockIdx.x, (int)gridDim.x);
-  const int r = L / p.Hq, h = L - r * p.Hq;
+  const int qpm = p.Hq / p.Hm;
+  const int r = L / qpm;
   const int item = p.q_order[r];
-  const int b = item / p.nQB, qb = item - b * p.nQB;
+  const int mr = item / p.nQB, qb = item - mr * p.nQB;  // mask row (b, set) and Q-block
+  const int b = mr / p.Hm;
+  const int h = (mr - b * p.Hm) * qpm + (L - r * qpm);
   const int kvh = h / (p.Hq / p.Hkv);
   const int n_tiles = p.q_count[2 * item] + p.q_count[2 * item + 1];
   const int32_t* queue = p.q_queue + (size_t)item * p.nKB;
@@ -389,7 +401,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   const rsrc_t kr_ = make_rsrc(p.k + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
   const rsrc_t vr_ = make_rsrc(p.v + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
   const uint32_t vec_bytes = (uint32_t)N * 4, row_bytes = (uint32_t)Nq * 4;
-  const size_t mrow = (size_t)b * N;
+  const size_t mrow = (size_t)mr * N;
   const rsrc_t m0 = make_rsrc(p.m.lts + mrow, vec_bytes), m1 = make_rsrc(p.m.lte + mrow, vec_bytes);
   const rsrc_t m2 = make_rsrc(p.m.uts + mrow, vec_bytes), m3 = make_rsrc(p.m.ute + mrow, vec_bytes);
   const bool ragged = (N % BK) != 0;
@@ -587,9 +599,8 @@ unsigned grid_for(size_t n, unsigned cap) {
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   if (a.B == 0 || a.Hq == 0 || (a.Nq == 0 && a.Nk == 0)) return hipSuccess;
   const size_t rows_k = (size_t)a.B * a.Hkv * a.Nk;
-  const int g = a.Hq / a.Hkv;
-  const int hc = g < kBwdHeadChunk ? g : kBwdHeadChunk;
-  const int nch = (g + hc - 1) / hc;
+  const HeadMap hm = head_map(a.Hq, a.Hkv, a.Hm);
+  const bool acc = hm.writers > 1;
   const float c = a.scale * kLog2e;
 
   // dQ first: it also writes D and the log2 LSE that the dK/dV kernel reads
@@ -605,7 +616,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   q.m = a.m;
   q.dq = static_cast<bf16*>(a.dq);
   q.q_queue = a.q_queue; q.q_count = a.q_count; q.q_order = a.q_order;
-  q.B = a.B; q.Hq = a.Hq; q.Hkv = a.Hkv; q.Nq = a.Nq; q.Nk = a.Nk;
+  q.B = a.B; q.Hq = a.Hq; q.Hkv = a.Hkv; q.Hm = a.Hm; q.Nq = a.Nq; q.Nk = a.Nk;
   q.nQB = a.nQB_q; q.nKB = a.nKB_q;
   q.c = c;
   q.scale = a.scale;
@@ -614,7 +625,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   if (qgrid > 0) hipLaunchKernelGGL(k_attn_bwd_dq, dim3(qgrid), dim3(256), 0, s, q);
   if (ev.dq_stop) (void)hipEventRecord(ev.dq_stop, s);
 
-  if (nch > 1 && rows_k > 0) {
+  if (acc && rows_k > 0) {
     hipLaunchKernelGGL(k_zero, dim3(grid_for(rows_k * D / 4, 8192)), dim3(256), 0, s,
                        reinterpret_cast<float4*>(a.dk_acc), rows_k * D / 4);
     hipLaunchKernelGGL(k_zero, dim3(grid_for(rows_k * D / 4, 8192)), dim3(256), 0, s,
@@ -635,16 +646,16 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   p.dv = static_cast<bf16*>(a.dv);
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
   p.nQB = a.nQB_k; p.nKB = a.nKB_k;
-  p.hc = hc;
-  p.nch = nch;
+  p.hm = hm;
   p.c = c;
   p.scale = a.scale;
-  const unsigned grid = (unsigned)a.B * (unsigned)a.nKB_k * (unsigned)a.Hkv * (unsigned)nch;
+  const unsigned grid = (unsigned)a.B * (unsigned)a.Hm * (unsigned)a.nKB_k * (unsigned)hm.kvpm *
+                        (unsigned)hm.cpk;
   if (ev.dkdv_start) (void)hipEventRecord(ev.dkdv_start, s);
   if (grid > 0) hipLaunchKernelGGL(k_attn_bwd_dkdv, dim3(grid), dim3(64 * dkdv::kWaves), 0, s, p);
   if (ev.dkdv_stop) (void)hipEventRecord(ev.dkdv_stop, s);
 
-  if (nch > 1 && rows_k > 0) {
+  if (acc && rows_k > 0) {
     hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_k * D / 8, 16384)), dim3(256), 0, s,
                        a.dk_acc, static_cast<bf16*>(a.dk), a.scale, rows_k * D / 8);
     hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_k * D / 8, 16384)), dim3(256), 0, s,

@@ -64,7 +64,7 @@ struct FwdParams {
   const int32_t* __restrict__ q_queue;
   const int32_t* __restrict__ q_count;
   const int32_t* __restrict__ q_order;
-  int B, Hq, Hkv, Nq, Nk, nQB, nKB;  // Nq query rows, Nk keys
+  int B, Hq, Hkv, Hm, Nq, Nk, nQB, nKB;  // Nq query rows, Nk keys, Hm mask sets per batch row
   float c;  // softmax scale * log2(e)
 };
 
@@ -73,10 +73,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
 
+  // workgroup L: the (L % qpm)-th query head of the mask set of LPT item L / qpm
   const int L = xcd_logical((int)blockIdx.x, (int)gridDim.x);
-  const int r = L / p.Hq, h = L - r * p.Hq;
+  const int qpm = p.Hq / p.Hm;
+  const int r = L / qpm;
   const int item = p.q_order[r];
-  const int b = item / p.nQB, qb = item - b * p.nQB;
+  const int mr = item / p.nQB, qb = item - mr * p.nQB;  // mask row (b, set) and Q-block
+  const int b = mr / p.Hm;
+  const int h = (mr - b * p.Hm) * qpm + (L - r * qpm);
   const int kvh = h / (p.Hq / p.Hkv);
   const int n_tiles = p.q_count[2 * item] + p.q_count[2 * item + 1];
   const int32_t* queue = p.q_queue + (size_t)item * p.nKB;
@@ -86,7 +90,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   const rsrc_t kr_ = make_rsrc(p.k + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
   const rsrc_t vr_ = make_rsrc(p.v + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
   const uint32_t vec_bytes = (uint32_t)N * 4;
-  const size_t mrow = (size_t)b * N;
+  const size_t mrow = (size_t)mr * N;
   const rsrc_t m0 = make_rsrc(p.m.lts + mrow, vec_bytes), m1 = make_rsrc(p.m.lte + mrow, vec_bytes);
   const rsrc_t m2 = make_rsrc(p.m.uts + mrow, vec_bytes), m3 = make_rsrc(p.m.ute + mrow, vec_bytes);
   const bool ragged = (N % BK) != 0;
@@ -359,7 +363,8 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_
   p.q_queue = a.q_queue;
   p.q_count = a.q_count;
   p.q_order = a.q_order;
-  p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk; p.nQB = a.nQB; p.nKB = a.nKB;
+  p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Hm = a.Hm; p.Nq = a.Nq; p.Nk = a.Nk;
+  p.nQB = a.nQB; p.nKB = a.nKB;
   p.c = a.scale * kLog2e;
   const unsigned grid = (unsigned)a.B * (unsigned)a.nQB * (unsigned)a.Hq;
   if (ev0) (void)hipEventRecord(ev0, s);

@@ -27,6 +27,37 @@ constexpr int kAlphaUnmasked = 10;
 // The LPT sort runs in one workgroup with 64-bit keys in LDS.
 constexpr int kMaxSortItems = 8192;
 
+// How query heads, kv heads and mask sets relate.  The vectors are [B][Hm][Nk]; query
+// head h uses set h / (Hq / Hm), and Hm divides Hkv or is a multiple of it.  Tiles are
+// classified per mask row (b, m).  A dK/dV work item is (mask row, KV block, kv head of
+// that set, chunk of at most kBwdHeadChunk query heads of that kv head and set).
+struct HeadMap {
+  int Hm;       // mask sets per batch row
+  int qpm;      // query heads per set
+  int kvpm;     // kv heads per set (1 when a set covers part of one kv head's group)
+  int gq;       // query heads of one (kv head, set) pair
+  int hc;       // query heads per dK/dV item
+  int cpk;      // dK/dV items per (mask row, kv head, KV block)
+  int writers;  // dK/dV items writing one kv head's KV block (> 1: fp32 accumulators)
+};
+inline bool head_map_valid(int Hq, int Hkv, int Hm) {
+  if (Hm < 1 || Hkv < 1) return false;
+  if (Hq > 0 && Hq % Hm != 0) return false;
+  return Hkv % Hm == 0 || Hm % Hkv == 0;
+}
+inline HeadMap head_map(int Hq, int Hkv, int Hm) {
+  HeadMap m{};
+  m.Hm = Hm;
+  m.qpm = Hq / Hm;
+  m.kvpm = Hm <= Hkv ? Hkv / Hm : 1;
+  const int g = Hq / Hkv;
+  m.gq = g < m.qpm ? g : m.qpm;
+  m.hc = m.gq < kBwdHeadChunk ? (m.gq > 0 ? m.gq : 1) : kBwdHeadChunk;
+  m.cpk = (m.gq + m.hc - 1) / m.hc;
+  m.writers = m.gq > 0 ? (g / m.gq) * m.cpk : 0;
+  return m;
+}
+
 struct MaskPtrs {
   const int32_t* lts;
   const int32_t* lte;
@@ -34,7 +65,7 @@ struct MaskPtrs {
   const int32_t* ute;
 };
 
-// Classification outputs; any of the optional outputs may be null.
+// Classification outputs (B here counts mask rows); any of the optional outputs may be null.
 struct TileOut {
   int32_t* minmax;       // [B][nKB][8]                (required)
   uint8_t* tile_class;   // [B][nQB][nKB]              (optional)
@@ -73,7 +104,7 @@ struct FwdArgs {
   const int32_t* q_queue;
   const int32_t* q_count;
   const int32_t* q_order;
-  int B, Hq, Hkv, Nq, Nk, nQB, nKB;
+  int B, Hq, Hkv, Hm, Nq, Nk, nQB, nKB;  // Hm: mask sets per batch row
   float scale;
 };
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
@@ -99,9 +130,9 @@ struct BwdArgs {
   const int32_t* q_order;
   float* lse2;   // [B][Hq][Nq] log2-domain LSE (+inf for rows that see nothing)
   float* delta;  // [B][Hq][Nq] rowsum(dO * O)
-  float* dk_acc; // [B][Hkv][Nk][128] fp32, only when Hq/Hkv > kBwdHeadChunk (else null)
-  float* dv_acc; // [B][Hkv][N][128] fp32, likewise
-  int B, Hq, Hkv, Nq, Nk;
+  float* dk_acc; // [B][Hkv][Nk][128] fp32, only when head_map(...).writers > 1 (else null)
+  float* dv_acc; // [B][Hkv][Nk][128] fp32, likewise
+  int B, Hq, Hkv, Hm, Nq, Nk;
   int nQB_k, nKB_k;  // block counts at the dK/dV tile
   int nQB_q, nKB_q;  // block counts at the dQ (forward) tile
   float scale;

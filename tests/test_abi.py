@@ -201,3 +201,59 @@ def test_localize_argument_checks():
     assert call(p, 4097, 8) == UNSUPPORTED
     assert call(p, 1, 8, offs=None) == INVALID
     assert call(prob_kv(B=0, Nq=0, Nk=100), 1, 8) == FM_OK     # no columns: nothing to do
+
+
+# ---- per-head mask sets (fm_problem.mask_heads) -------------------------------------
+
+def prob_hm(Hq, Hkv, Hm, B=1, N=256):
+    p = fm.Problem(B, Hq, Hkv, N, 128, 0.0)
+    p.mask_heads = Hm
+    return p
+
+
+@pytest.mark.parametrize("Hq,Hkv,Hm", [(8, 4, 3), (12, 4, 6), (4, 2, 8), (4, 2, -1)])
+def test_mask_heads_that_do_not_fit_are_rejected(Hq, Hkv, Hm):
+    # H_m must divide H_q and divide H_kv or be a multiple of it
+    p = prob_hm(Hq, Hkv, Hm)
+    assert fwd(p) == INVALID
+    assert bwd(p) == INVALID
+    n = ctypes.c_size_t()
+    assert fm.library().fm_workspace_size(ctypes.byref(p), 1, 0, 0, ctypes.byref(n)) == INVALID
+
+
+@pytest.mark.parametrize("Hq,Hkv,Hm", [(8, 4, 2), (8, 4, 4), (8, 4, 8), (8, 1, 2), (6, 3, 1),
+                                       (6, 3, 0)])
+def test_mask_heads_that_fit_are_accepted(Hq, Hkv, Hm):
+    n = ctypes.c_size_t()
+    p = prob_hm(Hq, Hkv, Hm)
+    for op in (fm.OP_FWD, fm.OP_BWD):
+        assert fm.library().fm_workspace_size(ctypes.byref(p), op, 0, 0, ctypes.byref(n)) == FM_OK
+
+
+def test_mask_heads_workspace_sizes():
+    al = lambda x: (x + 255) // 256 * 256
+    B, N, Hm = 2, 1000, 4
+    R = B * Hm                                   # tile structures per mask row
+    nqb, nkb = 8, 16
+    want = al(R * nkb * 32) + al(R * nqb * nkb * 4) + al(R * nqb * 8) + 2 * al(R * nqb * 4)
+    assert fm.workspace_size(B, 8, 4, N, fm.OP_FWD, mask_heads=Hm) == want
+    # dK/dV accumulators appear when sets split a kv head's group (two writers per block):
+    # 8 query heads, 4 kv heads (groups of 2), 8 sets -> accumulators; 4 sets -> none
+    al_acc = 2 * al(B * 4 * N * 128 * 4)
+    split = fm.workspace_size(B, 8, 4, N, fm.OP_BWD, mask_heads=8)
+    whole = fm.workspace_size(B, 8, 4, N, fm.OP_BWD, mask_heads=4)
+    tiles_k = al(B * 4 * 8 * 32) + al(B * 4 * 8 * 32 * 4) + al(B * 4 * 8 * 8) + 2 * al(B * 4 * 8 * 4)
+    tiles_q = al(B * 4 * nkb * 32) + al(B * 4 * nqb * nkb * 4) + al(B * 4 * nqb * 8) + \
+        2 * al(B * 4 * nqb * 4)
+    assert split - whole == al_acc + tiles_k + tiles_q    # 8 sets: twice the tile rows
+
+
+def test_mask_heads_sort_limit():
+    # 8192 work blocks per sort: B * H_m * nKB at the forward's 64-key blocks
+    n = ctypes.c_size_t()
+    ok = prob_hm(64, 8, 64, N=8192)              # 64 sets * 128 KV blocks = 8192
+    assert fm.library().fm_workspace_size(ctypes.byref(ok), fm.OP_FWD, 0, 0,
+                                          ctypes.byref(n)) == FM_OK
+    big = prob_hm(64, 8, 64, N=8192 + 64)
+    assert fm.library().fm_workspace_size(ctypes.byref(big), fm.OP_FWD, 0, 0,
+                                          ctypes.byref(n)) == UNSUPPORTED
