@@ -12,7 +12,8 @@ Contents and the passage each part follows:
                 Overview: per-key row bounds LTS/LTE/UTS/UTE); conversion from the
                 two-vector visible-interval form and its closed-form encoders
                 (FlashMask Guide, "Mathematical Formalization of Column-Wise
-                Sparsity").
+                Sparsity"); the multi-interval form, up to 4 active row intervals
+                per column (same Guide, "Multi-Interval Sparse Masks").
   attention.py  masked softmax attention forward (plain two-pass softmax) and its
                 analytic backward (Flash MSA guide, "Why Standard Attention Broke"
                 and "The Backward Pass: The Real Beast"; FlashMask Guide, dense
@@ -40,10 +41,13 @@ brute force, invariants); see tests/test_oracle_*.py.  Full-size numeric outputs
 have no printed values on the pages: beyond those pins they are parity unpinned.
 """
 from .mask import (masked_rows, dense_mask, visible_interval_to_vectors,
-                   encode_causal, encode_packed, encode_dpo)
+                   encode_causal, encode_packed, encode_dpo, hidden_multi_rows,
+                   dense_mask_multi)
 from .attention import (attention_fwd, attention_bwd, attention_rows, attention_cols,
-                        attention_fwd_bwd)
+                        attention_fwd_bwd, attention_fwd_multi, attention_fwd_bwd_multi,
+                        attention_rows_multi, attention_cols_multi)
 from .tiles import (block_minmax, classify, tile_truth, queues, tile_costs, lpt_order,
+                    block_minmax_multi, classify_multi, tile_truth_multi,
                     ALPHA_PARTIAL, ALPHA_UNMASKED)
 from .schedule import list_schedule, lower_bound, brute_force_optimum
 from .localize import rank_rows, localize, localize_max_form, localize_vectors
@@ -51,8 +55,11 @@ from . import ipo
 
 __all__ = [
     "masked_rows", "dense_mask", "visible_interval_to_vectors", "encode_causal",
-    "encode_packed", "encode_dpo", "attention_fwd", "attention_bwd", "attention_rows",
-    "attention_cols", "attention_fwd_bwd", "block_minmax", "classify", "tile_truth",
+    "encode_packed", "encode_dpo", "hidden_multi_rows", "dense_mask_multi",
+    "attention_fwd", "attention_bwd", "attention_rows", "attention_cols",
+    "attention_fwd_bwd", "attention_fwd_multi", "attention_fwd_bwd_multi",
+    "attention_rows_multi", "attention_cols_multi", "block_minmax", "classify",
+    "tile_truth", "block_minmax_multi", "classify_multi", "tile_truth_multi",
     "queues", "tile_costs", "lpt_order", "ALPHA_PARTIAL", "ALPHA_UNMASKED",
     "list_schedule", "lower_bound", "brute_force_optimum", "rank_rows", "localize",
     "localize_max_form", "localize_vectors", "ipo",

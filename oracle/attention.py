@@ -26,13 +26,43 @@ page, Overview), or -- the per-head variant its list of extensions names without
 defining -- [B][H_m][N_k] with H_m dividing H_q, where query head h uses set
 h // (H_q / H_m) (contiguous groups, as for GQA; H_m = H_q is one set per head).
 
+The multi-interval form (FlashMask Guide, "Multi-Interval Sparse Masks"; the *_multi
+functions) gives each column M <= 4 active intervals instead: starts and ends
+[B][M][N_k] or [B][H_m][M][N_k], row i seeing key j iff some interval holds it.
+
 Rows are processed in blocks; each block expands only its own rows of the mask
 (never the full N x N matrix) and restricts its products to the columns that at
 least one of its rows can see, which is exact because hidden columns contribute 0.
 """
 import numpy as np
 
-from .mask import masked_rows
+from .mask import hidden_multi_rows, masked_rows
+
+
+class _FourVectors:
+    """The four-vector form of one (b, h): hidden iff in [LTS, LTE) or [UTS, UTE)."""
+
+    def __init__(self, vecs):
+        self.v = vecs
+
+    def rows(self, r0, r1):
+        return masked_rows(*self.v, r0, r1)
+
+    def column(self, c, n):
+        return masked_rows(*(x[c:c + 1] for x in self.v), 0, n)[:, 0]
+
+
+class _Intervals:
+    """The multi-interval form of one (b, h): visible iff in some [start_m, end_m)."""
+
+    def __init__(self, starts, ends):
+        self.s, self.e = starts, ends
+
+    def rows(self, r0, r1):
+        return hidden_multi_rows(self.s, self.e, r0, r1)
+
+    def column(self, c, n):
+        return hidden_multi_rows(self.s[:, c:c + 1], self.e[:, c:c + 1], 0, n)[:, 0]
 
 
 def _f64(x):
@@ -43,13 +73,13 @@ def _scale(d, scale):
     return 1.0 / np.sqrt(d) if scale is None or scale <= 0 else float(scale)
 
 
-def _row_block(qh, kh, vh, vecs, r0, r1, scale, dOh=None):
-    """Forward (and, if dOh is given, backward) for rows [r0, r1) of one (b, h).
+def _row_block(qh, kh, vh, mask, r0, r1, scale, dOh=None):
+    """Forward (and, if dOh is given, backward) for rows [r0, r1) of one (b, h) whose
+    mask is `mask` (_FourVectors or _Intervals).
 
     Returns O [R][d], LSE [R], and if dOh: dQ [R][d], cols, dK_part, dV_part where
     the parts are [len(cols)][d] contributions to the key columns `cols`."""
-    lts, lte, uts, ute = vecs
-    hid = masked_rows(lts, lte, uts, ute, r0, r1)            # [R][N]
+    hid = mask.rows(r0, r1)                                   # [R][N]
     cols = np.nonzero(~hid.all(axis=0))[0]
     R, d = r1 - r0, qh.shape[1]
     O = np.zeros((R, d))
@@ -88,56 +118,61 @@ def _row_block(qh, kh, vh, vecs, r0, r1, scale, dOh=None):
     return O, lse, dQ, cols, dK_part, dV_part
 
 
-def _check(q, k, v, vecs):
-    """Q [B][H_q][N_q][d], K and V [B][H_kv][N_k][d], vectors [B][N_k] or [B][H_m][N_k]
-    (query-row bounds in [0, N_q]); N_q = N_k for self-attention, N_q < N_k for one
-    rank's share of the query rows under context parallelism with localized vectors.
-    Returns (B, H_q, H_kv, N_q, d, g, vec_of) with vec_of(b, h) the four [N_k] vectors
-    query head h of batch row b uses."""
+def _check(q, k, v):
+    """Q [B][H_q][N_q][d], K and V [B][H_kv][N_k][d]; N_q = N_k for self-attention,
+    N_q < N_k for one rank's share of the query rows under context parallelism with
+    localized vectors.  Returns (B, H_q, H_kv, N_q, d, g)."""
     B, Hq, N, d = q.shape
     Bk, Hkv, Nk, dk = k.shape
     assert (B, d) == (Bk, dk) and v.shape == k.shape
     assert Hq % Hkv == 0
-    return (B, Hq, Hkv, N, d, Hq // Hkv) + (_vectors_of(vecs, B, Hq, Nk),)
+    return B, Hq, Hkv, N, d, Hq // Hkv
 
 
 def _vectors_of(vecs, B, Hq, Nk):
+    """Mask getter (b, h) -> _FourVectors for vectors [B][N_k] or [B][H_m][N_k] (row
+    bounds in [0, N_q])."""
     arrs = [np.asarray(x) for x in vecs]
     shape = arrs[0].shape
     assert all(x.shape == shape for x in arrs)
     if len(shape) == 2:
         assert shape == (B, Nk)
-        return lambda b, h: tuple(x[b] for x in arrs)
+        return lambda b, h: _FourVectors(tuple(x[b] for x in arrs))
     assert len(shape) == 3 and shape[0] == B and shape[2] == Nk and Hq % shape[1] == 0
     per = Hq // shape[1]                      # query heads per mask head
-    return lambda b, h: tuple(x[b, h // per] for x in arrs)
+    return lambda b, h: _FourVectors(tuple(x[b, h // per] for x in arrs))
 
 
-def attention_fwd(q, k, v, lts, lte, uts, ute, scale=None, row_block=256):
-    """O [B][H_q][N][d] and LSE [B][H_q][N] (natural log) in float64."""
-    q, k, v = _f64(q), _f64(k), _f64(v)
-    vecs = (lts, lte, uts, ute)
-    B, Hq, Hkv, N, d, g, vec_of = _check(q, k, v, vecs)
+def _intervals_of(starts, ends, B, Hq, Nk):
+    """Mask getter (b, h) -> _Intervals for starts/ends [B][M][N_k] or [B][H_m][M][N_k]."""
+    s, e = np.asarray(starts), np.asarray(ends)
+    assert s.shape == e.shape and s.shape[-1] == Nk and s.shape[0] == B
+    if s.ndim == 3:
+        assert 1 <= s.shape[1] <= 4
+        return lambda b, h: _Intervals(s[b], e[b])
+    assert s.ndim == 4 and Hq % s.shape[1] == 0 and 1 <= s.shape[2] <= 4
+    per = Hq // s.shape[1]
+    return lambda b, h: _Intervals(s[b, h // per], e[b, h // per])
+
+
+def _fwd(q, k, v, mask_of, scale, row_block):
+    B, Hq, Hkv, N, d, g = _check(q, k, v)
     sc = _scale(d, scale)
     O = np.zeros((B, Hq, N, d))
     LSE = np.full((B, Hq, N), -np.inf)
     for b in range(B):
         for h in range(Hq):
             kv = h // g
-            vb = vec_of(b, h)
+            mk = mask_of(b, h)
             for r0 in range(0, N, row_block):
                 r1 = min(r0 + row_block, N)
                 O[b, h, r0:r1], LSE[b, h, r0:r1] = _row_block(q[b, h], k[b, kv], v[b, kv],
-                                                              vb, r0, r1, sc)
+                                                              mk, r0, r1, sc)
     return O, LSE
 
 
-def attention_fwd_bwd(q, k, v, do, lts, lte, uts, ute, scale=None, row_block=256):
-    """(O, LSE, dQ, dK, dV) in float64; the backward recomputes the softmax from
-    its definition (no statistic comes from anywhere but this function)."""
-    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
-    vecs = (lts, lte, uts, ute)
-    B, Hq, Hkv, N, d, g, vec_of = _check(q, k, v, vecs)
+def _fwd_bwd(q, k, v, do, mask_of, scale, row_block):
+    B, Hq, Hkv, N, d, g = _check(q, k, v)
     sc = _scale(d, scale)
     O = np.zeros((B, Hq, N, d))
     LSE = np.full((B, Hq, N), -np.inf)
@@ -147,15 +182,78 @@ def attention_fwd_bwd(q, k, v, do, lts, lte, uts, ute, scale=None, row_block=256
     for b in range(B):
         for h in range(Hq):
             kv = h // g
-            vb = vec_of(b, h)
+            mk = mask_of(b, h)
             for r0 in range(0, N, row_block):
                 r1 = min(r0 + row_block, N)
-                o, lse, dq, cols, dkp, dvp = _row_block(q[b, h], k[b, kv], v[b, kv], vb,
+                o, lse, dq, cols, dkp, dvp = _row_block(q[b, h], k[b, kv], v[b, kv], mk,
                                                         r0, r1, sc, dOh=do[b, h])
                 O[b, h, r0:r1], LSE[b, h, r0:r1], dQ[b, h, r0:r1] = o, lse, dq
                 dK[b, kv, cols] += dkp
                 dV[b, kv, cols] += dvp
     return O, LSE, dQ, dK, dV
+
+
+def _rows(q, k, v, do, mk, b, h, rows, scale):
+    Hq, Hkv = q.shape[1], k.shape[1]
+    kv = h // (Hq // Hkv)
+    d = q.shape[3]
+    sc = _scale(d, scale)
+    qh, kh, vh = _f64(q[b, h]), _f64(k[b, kv]), _f64(v[b, kv])
+    dOh = None if do is None else _f64(do[b, h])
+    O = np.zeros((len(rows), d)); LSE = np.zeros(len(rows)); dQ = np.zeros((len(rows), d))
+    for t, r in enumerate(rows):
+        res = _row_block(qh, kh, vh, mk, int(r), int(r) + 1, sc, dOh=dOh)
+        O[t], LSE[t] = res[0][0], res[1][0]
+        if dOh is not None:
+            dQ[t] = res[2][0]
+    return O, LSE, (dQ if dOh is not None else None)
+
+
+def _cols(q, k, v, do, mask_of, b, kv, cols, scale, row_block):
+    Hq, Hkv = q.shape[1], k.shape[1]
+    g = Hq // Hkv
+    d = q.shape[3]
+    sc = _scale(d, scale)
+    N = q.shape[2]
+    cols = np.asarray(cols)
+    kh, vh = _f64(k[b, kv]), _f64(v[b, kv])
+    dK = np.zeros((len(cols), d)); dV = np.zeros((len(cols), d))
+    for h in range(kv * g, (kv + 1) * g):
+        mk = mask_of(b, h)
+        # rows that see at least one selected column
+        need = np.zeros(N, dtype=bool)
+        for c in cols:
+            need |= ~mk.column(int(c), N)
+        # Rows that see none of the selected columns contribute exactly 0 to them, so
+        # whole row blocks that contain at least one needed row can be computed.
+        starts = sorted({int(r) // row_block * row_block for r in np.nonzero(need)[0]})
+        qh, dOh = _f64(q[b, h]), _f64(do[b, h])
+        for r0 in starts:
+            r1 = min(r0 + row_block, N)
+            _, _, _, cs, dkp, dvp = _row_block(qh, kh, vh, mk, r0, r1, sc, dOh=dOh)
+            where = np.searchsorted(cs, cols)
+            hit = (where < len(cs)) & (cs[np.minimum(where, len(cs) - 1)] == cols) \
+                if len(cs) else np.zeros(len(cols), dtype=bool)
+            dK[hit] += dkp[where[hit]]
+            dV[hit] += dvp[where[hit]]
+    return dK, dV
+
+
+# ---- four-vector form (LTS/LTE/UTS/UTE) ----------------------------------------------
+
+def attention_fwd(q, k, v, lts, lte, uts, ute, scale=None, row_block=256):
+    """O [B][H_q][N][d] and LSE [B][H_q][N] (natural log) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    of = _vectors_of((lts, lte, uts, ute), q.shape[0], q.shape[1], k.shape[2])
+    return _fwd(q, k, v, of, scale, row_block)
+
+
+def attention_fwd_bwd(q, k, v, do, lts, lte, uts, ute, scale=None, row_block=256):
+    """(O, LSE, dQ, dK, dV) in float64; the backward recomputes the softmax from
+    its definition (no statistic comes from anywhere but this function)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    of = _vectors_of((lts, lte, uts, ute), q.shape[0], q.shape[1], k.shape[2])
+    return _fwd_bwd(q, k, v, do, of, scale, row_block)
 
 
 def attention_bwd(q, k, v, do, lts, lte, uts, ute, scale=None, row_block=256):
@@ -168,20 +266,8 @@ def attention_rows(q, k, v, do, lts, lte, uts, ute, b, h, rows, scale=None):
     """O, LSE and dQ of selected query rows of one (b, h).  Each row is computed
     on its own from the full key axis, so any row of a full-size problem can be
     checked.  `do` may be None (then dQ is None)."""
-    Hq, Hkv = q.shape[1], k.shape[1]
-    kv = h // (Hq // Hkv)
-    d = q.shape[3]
-    sc = _scale(d, scale)
-    vb = _vectors_of((lts, lte, uts, ute), q.shape[0], Hq, k.shape[2])(b, h)
-    qh, kh, vh = _f64(q[b, h]), _f64(k[b, kv]), _f64(v[b, kv])
-    dOh = None if do is None else _f64(do[b, h])
-    O = np.zeros((len(rows), d)); LSE = np.zeros(len(rows)); dQ = np.zeros((len(rows), d))
-    for t, r in enumerate(rows):
-        res = _row_block(qh, kh, vh, vb, int(r), int(r) + 1, sc, dOh=dOh)
-        O[t], LSE[t] = res[0][0], res[1][0]
-        if dOh is not None:
-            dQ[t] = res[2][0]
-    return O, LSE, (dQ if dOh is not None else None)
+    mk = _vectors_of((lts, lte, uts, ute), q.shape[0], q.shape[1], k.shape[2])(b, h)
+    return _rows(q, k, v, do, mk, b, h, rows, scale)
 
 
 def attention_cols(q, k, v, do, lts, lte, uts, ute, b, kv, cols, scale=None, row_block=256):
@@ -189,32 +275,29 @@ def attention_cols(q, k, v, do, lts, lte, uts, ute, b, kv, cols, scale=None, row
     the group that sees any selected column is computed in full (its softmax needs
     the whole row), so this is cheap only where the selected columns are seen by
     few rows."""
-    Hq, Hkv = q.shape[1], k.shape[1]
-    g = Hq // Hkv
-    d = q.shape[3]
-    sc = _scale(d, scale)
-    vec_of = _vectors_of((lts, lte, uts, ute), q.shape[0], Hq, k.shape[2])
-    N = q.shape[2]
-    cols = np.asarray(cols)
-    kh, vh = _f64(k[b, kv]), _f64(v[b, kv])
-    dK = np.zeros((len(cols), d)); dV = np.zeros((len(cols), d))
-    for h in range(kv * g, (kv + 1) * g):
-        lv = vec_of(b, h)
-        # rows that see at least one selected column
-        need = np.zeros(N, dtype=bool)
-        for c in cols:
-            rows_hidden = masked_rows(*(x[c:c + 1] for x in lv), 0, N)[:, 0]
-            need |= ~rows_hidden
-        # Rows that see none of the selected columns contribute exactly 0 to them, so
-        # whole row blocks that contain at least one needed row can be computed.
-        starts = sorted({int(r) // row_block * row_block for r in np.nonzero(need)[0]})
-        qh, dOh = _f64(q[b, h]), _f64(do[b, h])
-        for r0 in starts:
-            r1 = min(r0 + row_block, N)
-            _, _, _, cs, dkp, dvp = _row_block(qh, kh, vh, lv, r0, r1, sc, dOh=dOh)
-            where = np.searchsorted(cs, cols)
-            hit = (where < len(cs)) & (cs[np.minimum(where, len(cs) - 1)] == cols) \
-                if len(cs) else np.zeros(len(cols), dtype=bool)
-            dK[hit] += dkp[where[hit]]
-            dV[hit] += dvp[where[hit]]
-    return dK, dV
+    of = _vectors_of((lts, lte, uts, ute), q.shape[0], q.shape[1], k.shape[2])
+    return _cols(q, k, v, do, of, b, kv, cols, scale, row_block)
+
+
+# ---- multi-interval form (starts/ends [B][M][N_k] or [B][H_m][M][N_k]) -------------------
+
+def attention_fwd_multi(q, k, v, starts, ends, scale=None, row_block=256):
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    of = _intervals_of(starts, ends, q.shape[0], q.shape[1], k.shape[2])
+    return _fwd(q, k, v, of, scale, row_block)
+
+
+def attention_fwd_bwd_multi(q, k, v, do, starts, ends, scale=None, row_block=256):
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    of = _intervals_of(starts, ends, q.shape[0], q.shape[1], k.shape[2])
+    return _fwd_bwd(q, k, v, do, of, scale, row_block)
+
+
+def attention_rows_multi(q, k, v, do, starts, ends, b, h, rows, scale=None):
+    mk = _intervals_of(starts, ends, q.shape[0], q.shape[1], k.shape[2])(b, h)
+    return _rows(q, k, v, do, mk, b, h, rows, scale)
+
+
+def attention_cols_multi(q, k, v, do, starts, ends, b, kv, cols, scale=None, row_block=256):
+    of = _intervals_of(starts, ends, q.shape[0], q.shape[1], k.shape[2])
+    return _cols(q, k, v, do, of, b, kv, cols, scale, row_block)

@@ -26,6 +26,28 @@ def dense_mask(lts, lte, uts, ute):
     return masked_rows(lts, lte, uts, ute, 0, n)
 
 
+def hidden_multi_rows(starts, ends, r0, r1):
+    """Multi-interval form (FlashMask Guide, "Multi-Interval Sparse Masks"): each key
+    column j carries M <= 4 active intervals, and row i sees key j iff
+    starts[m][j] <= i < ends[m][j] for some m.  Reading adopted: half-open like the
+    four-vector form (the Guide's inclusive end FME is ends = FME + 1); an interval
+    whose start is not below its end is empty; the intervals need not be disjoint.
+    Returns the boolean [r1-r0][N] block with True = hidden (no interval holds the row)."""
+    starts = np.asarray(starts, dtype=np.int64)
+    ends = np.asarray(ends, dtype=np.int64)
+    i = np.arange(r0, r1, dtype=np.int64)[:, None]
+    visible = np.zeros((r1 - r0, starts.shape[-1]), dtype=bool)
+    for m in range(starts.shape[0]):
+        visible |= (starts[m][None, :] <= i) & (i < ends[m][None, :])
+    return ~visible
+
+
+def dense_mask_multi(starts, ends, nq=None):
+    """Full dense mask (True = hidden) of the multi-interval form, [N_q][N_k]."""
+    n = np.asarray(starts).shape[-1] if nq is None else nq
+    return hidden_multi_rows(starts, ends, 0, n)
+
+
 def visible_interval_to_vectors(fms, fme, n):
     """FlashMask Guide, "Mathematical Formalization of Column-Wise Sparsity": key
     column j is visible to rows FMS_j <= i <= FME_j (inclusive).  In the four-vector

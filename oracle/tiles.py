@@ -23,7 +23,7 @@ both intervals cover it together (the rule is conservative, never unsound).
 """
 import numpy as np
 
-from .mask import masked_rows
+from .mask import hidden_multi_rows, masked_rows
 
 SKIP, PARTIAL, UNMASKED = 0, 1, 2
 # alpha_p : alpha_u in integer units.  The FlashMask-3 page (§3.3) calls its 1.3 : 1
@@ -92,6 +92,70 @@ def tile_truth(lts, lte, uts, ute, bq, bk, nq=None):
             for kb in range(nkb):
                 t = hid[:, kb * bk:min(kb * bk + bk, Nk)]
                 out[b, qb, kb] = SKIP if t.all() else (UNMASKED if not t.any() else PARTIAL)
+    return out
+
+
+def block_minmax_multi(starts, ends, bk):
+    """Multi-interval form, starts/ends [R][M][N_k]: [R][nKB][4M] int64 holding, for
+    each interval m, (min start, max start, min end, max end) over the block's columns."""
+    starts = np.asarray(starts, dtype=np.int64)
+    ends = np.asarray(ends, dtype=np.int64)
+    R, M, _ = starts.shape
+    parts = []
+    for m in range(M):
+        mn_s, mx_s = block_minmax(starts[:, m], bk)
+        mn_e, mx_e = block_minmax(ends[:, m], bk)
+        parts += [mn_s, mx_s, mn_e, mx_e]
+    return np.stack(parts, axis=-1)
+
+
+def classify_multi(starts, ends, bq, bk, nq=None):
+    """Tile class [R][nQB][nKB] for the multi-interval form (FlashMask Guide,
+    "Multi-Interval Sparse Masks": a column is visible on M <= 4 row intervals).  The
+    Guide gives the skip test for one interval (skip when the rows lie past every
+    column's end or before every column's start); reading adopted for M intervals,
+    from the block min/max of each interval's starts and ends:
+
+      skip     = for every m: q1 <= min start_m  or  q0 >= max end_m
+                 (no interval reaches the tile in any column)
+      unmasked = for some m:  q0 >= max start_m and q1 <= min end_m
+                 (one interval holds the tile's rows in every column)
+      class    = 0 if skip, else 2 if unmasked, else 1
+
+    Sound for any vectors (empty or overlapping intervals only make it conservative)."""
+    mm = block_minmax_multi(starts, ends, bk)
+    R, M, Nk = np.asarray(starts).shape
+    N = Nk if nq is None else nq
+    nqb, nkb = _nblocks(N, bq), _nblocks(Nk, bk)
+    q0 = np.arange(nqb, dtype=np.int64) * bq
+    q1 = np.minimum(q0 + bq, N)
+    cls = np.zeros((R, nqb, nkb), dtype=np.uint8)
+    for r in range(R):
+        for kb in range(nkb):
+            skip = np.ones(nqb, dtype=bool)
+            unmasked = np.zeros(nqb, dtype=bool)
+            for m in range(M):
+                mn_s, mx_s, mn_e, mx_e = mm[r, kb, 4 * m:4 * m + 4]
+                skip &= (q1 <= mn_s) | (q0 >= mx_e)
+                unmasked |= (q0 >= mx_s) & (q1 <= mn_e)
+            cls[r, :, kb] = np.where(skip, SKIP, np.where(unmasked, UNMASKED, PARTIAL))
+    return cls
+
+
+def tile_truth_multi(starts, ends, bq, bk, nq=None):
+    """Brute force from the dense multi-interval mask: 0 all hidden, 2 none, 1 else."""
+    starts, ends = np.asarray(starts), np.asarray(ends)
+    R, M, Nk = starts.shape
+    N = Nk if nq is None else nq
+    nqb, nkb = _nblocks(N, bq), _nblocks(Nk, bk)
+    out = np.zeros((R, nqb, nkb), dtype=np.uint8)
+    for r in range(R):
+        for qb in range(nqb):
+            q0, q1 = qb * bq, min(qb * bq + bq, N)
+            hid = hidden_multi_rows(starts[r], ends[r], q0, q1)
+            for kb in range(nkb):
+                t = hid[:, kb * bk:min(kb * bk + bk, Nk)]
+                out[r, qb, kb] = SKIP if t.all() else (UNMASKED if not t.any() else PARTIAL)
     return out
 
 

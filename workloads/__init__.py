@@ -52,6 +52,34 @@ class Workload:
         return 1 if self.lts.ndim == 2 else self.lts.shape[1]
 
 
+@dataclass
+class MultiWorkload:
+    """Multi-interval form: each key column is visible on up to 4 row intervals
+    [start_m, end_m).  starts/ends are int32 [B][M][N] (shared by every head) or
+    [B][H_m][M][N] (per-head sets)."""
+    name: str
+    batch: int
+    heads_q: int
+    heads_kv: int
+    seqlen: int
+    head_dim: int
+    starts: np.ndarray
+    ends: np.ndarray
+    seed: int
+    info: dict = field(default_factory=dict)
+
+    def intervals(self):
+        return self.starts, self.ends
+
+    @property
+    def n_intervals(self) -> int:
+        return self.starts.shape[-2]
+
+    @property
+    def mask_heads(self) -> int:
+        return 1 if self.starts.ndim == 3 else self.starts.shape[1]
+
+
 def _empty_vectors(batch: int, n: int):
     lts = np.full((batch, n), n, dtype=np.int64)
     lte = np.full((batch, n), n, dtype=np.int64)
@@ -244,6 +272,58 @@ def per_head_windows(seed: int = 0, n: int = 32768, batch: int = 1, heads_q: int
                     "sinks": sinks})
 
 
+def _finish_multi(name, batch, hq, hkv, n, starts, ends, seed, info):
+    return MultiWorkload(name, batch, hq, hkv, n, HEAD_DIM,
+                         np.ascontiguousarray(starts, dtype=np.int32),
+                         np.ascontiguousarray(ends, dtype=np.int32), seed, info)
+
+
+def random_multi_intervals(seed: int, n: int, batch: int = 1, heads_q: int = 1,
+                           heads_kv: int = 1, n_intervals: int = 3, mask_heads: int = 0,
+                           p_empty: float = 0.2) -> MultiWorkload:
+    """Adversarial multi-interval columns: every interval random in [0, N], possibly
+    empty (start >= end), covering every row, or overlapping another."""
+    rng = np.random.default_rng(seed)
+    shape = ((batch,) if mask_heads <= 0 else (batch, mask_heads)) + (n_intervals, n)
+    a = rng.integers(0, n + 1, (2,) + shape)
+    starts, ends = np.minimum(a[0], a[1]), np.maximum(a[0], a[1])
+    empty = rng.random(shape) < p_empty
+    starts = np.where(empty, ends, starts)
+    return _finish_multi("random_multi_intervals", batch, heads_q, heads_kv, n, starts, ends,
+                         seed, {})
+
+
+def block_sparse_window(seed: int = 0, n: int = 32768, batch: int = 1, heads_q: int = 32,
+                        heads_kv: int = 8, window: int = 2048, rand_blocks: int = 3,
+                        block: int = 128, sinks: int = 64) -> MultiWorkload:
+    """Causal local window plus random distant query blocks, written column-wise with
+    four intervals (a block-sparse pattern of the kind the pages list, in the
+    multi-interval form).  Key j sees rows [j, j + window) (interval 0; the first
+    `sinks` keys see every row from j on); each block of `block` keys is also seen by
+    `rand_blocks` query blocks of `block` rows drawn without replacement from those
+    past its window (intervals 1..3, empty where there are too few)."""
+    rng = np.random.default_rng(seed)
+    M = 1 + rand_blocks
+    starts = np.zeros((batch, M, n), dtype=np.int64)
+    ends = np.zeros((batch, M, n), dtype=np.int64)
+    j = np.arange(n)
+    nb = n // block
+    for b in range(batch):
+        starts[b, 0] = j
+        ends[b, 0] = np.minimum(j + window, n)
+        ends[b, 0, :sinks] = n
+        for kb in range(nb):
+            first = (kb * block + block + window + block - 1) // block   # past the window
+            cand = np.arange(first, nb)
+            pick = np.sort(rng.choice(cand, size=min(rand_blocks, len(cand)), replace=False))
+            for t, qb in enumerate(pick):
+                starts[b, 1 + t, kb * block:(kb + 1) * block] = qb * block
+                ends[b, 1 + t, kb * block:(kb + 1) * block] = (qb + 1) * block
+    return _finish_multi("block_sparse_window", batch, heads_q, heads_kv, n, starts, ends, seed,
+                         {"window": window, "rand_blocks": rand_blocks, "block": block,
+                          "sinks": sinks})
+
+
 # The five benchmark workloads, in order.  Shapes and mask families follow the
 # synthetic stand-ins for the mask families the FlashMask-3 page benchmarks.
 CONFIGS = {
@@ -259,6 +339,8 @@ CONFIG_NAMES = list(CONFIGS)
 VARIANTS = {
     # per-head masks: 32 query heads, 8 kv heads, one window per kv head's group
     "v1_per_head_windows_32k": lambda seed=0: per_head_windows(seed),
+    # multi-interval columns: local window + three random distant query blocks per key block
+    "v2_block_sparse_window_32k": lambda seed=0: block_sparse_window(seed),
 }
 VARIANT_NAMES = list(VARIANTS)
 
@@ -292,6 +374,9 @@ def make_tensors(w: Workload, seed: int | None = None, device: str = "cpu",
     return q, k, v, do
 
 
-def mask_tensors(w: Workload, device: str = "cpu"):
+def mask_tensors(w, device: str = "cpu"):
+    """The mask as int32 tensors: the four vectors of a Workload, or (starts, ends) of a
+    MultiWorkload."""
     import torch
-    return tuple(torch.from_numpy(np.ascontiguousarray(x)).to(device) for x in w.vectors())
+    arrs = w.intervals() if isinstance(w, MultiWorkload) else w.vectors()
+    return tuple(torch.from_numpy(np.ascontiguousarray(x)).to(device) for x in arrs)
