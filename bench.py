@@ -73,6 +73,25 @@ def attended_pairs(w):
     return total * (w.heads_q // hm)
 
 
+def attended_pairs_multi(w):
+    """Attended pairs of a multi-interval workload: per key column, the length of the union
+    of its visible intervals clipped to [0, N_q), times the query heads that use the set."""
+    st = np.clip(np.asarray(w.starts, dtype=np.int64), 0, w.seqlen)
+    en = np.clip(np.asarray(w.ends, dtype=np.int64), 0, w.seqlen)
+    if st.ndim == 3:
+        st, en = st[:, None], en[:, None]
+    en = np.maximum(en, st)                      # empty intervals have no length
+    order = np.argsort(st, axis=2, kind="stable")
+    st = np.take_along_axis(st, order, axis=2)
+    en = np.take_along_axis(en, order, axis=2)
+    covered = np.zeros(st.shape[:2] + st.shape[3:], dtype=np.int64)
+    reach = np.zeros_like(covered)               # end of the union so far
+    for m in range(st.shape[2]):
+        covered += np.maximum(en[:, :, m] - np.maximum(st[:, :, m], reach), 0)
+        reach = np.maximum(reach, en[:, :, m])
+    return int(covered.sum()) * (w.heads_q // st.shape[1])
+
+
 def head_vectors(w, b, h):
     """The four vectors [1][N] query head h of batch row b uses."""
     if w.lts.ndim == 2:
@@ -336,14 +355,24 @@ def cpu_baseline(w, q, k, v, do, budget_s):
         for h in heads:
             kvh = h // g
             f = lambda t, hh: t[b:b + 1, hh:hh + 1].float().cpu().numpy().astype(np.float64)
-            sub = head_vectors(w, b, h)
             args = (f(q, h), f(k, kvh), f(v, kvh), f(do, h))
-            t0 = time.perf_counter()
-            oracle.attention_fwd_bwd(*args, *sub)
-            t_total += time.perf_counter() - t0
-            one = workloads.Workload(w.name, 1, 1, 1, w.seqlen, w.head_dim,
-                                     *[np.ascontiguousarray(x) for x in sub], w.seed)
-            pairs += attended_pairs(one)
+            if isinstance(w, workloads.MultiWorkload):
+                m = h // (w.heads_q // w.mask_heads)
+                st, en = ((x[b:b + 1] if x.ndim == 3 else x[b:b + 1, m]) for x in w.intervals())
+                t0 = time.perf_counter()
+                oracle.attention_fwd_bwd_multi(*args, st, en)
+                t_total += time.perf_counter() - t0
+                one = workloads.MultiWorkload(w.name, 1, 1, 1, w.seqlen, w.head_dim,
+                                              st.copy(), en.copy(), w.seed)
+                pairs += attended_pairs_multi(one)
+            else:
+                sub = head_vectors(w, b, h)
+                t0 = time.perf_counter()
+                oracle.attention_fwd_bwd(*args, *sub)
+                t_total += time.perf_counter() - t0
+                one = workloads.Workload(w.name, 1, 1, 1, w.seqlen, w.head_dim,
+                                         *[np.ascontiguousarray(x) for x in sub], w.seed)
+                pairs += attended_pairs(one)
             done.append((b, h))
             if t_total >= budget_s:
                 break
@@ -413,8 +442,11 @@ def main():
                                          mask_heads=w.mask_heads), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(fm.workspace_size(w.batch, w.heads_q, w.heads_kv, w.seqlen, fm.OP_BWD,
                                          mask_heads=w.mask_heads), dtype=torch.uint8, device=dev)
-    A = attended_pairs(w)
+    multi = isinstance(w, workloads.MultiWorkload)
+    A = attended_pairs_multi(w) if multi else attended_pairs(w)
     d = w.head_dim
+    attn_fwd = fm.attn_fwd_multi if multi else fm.attn_fwd
+    attn_bwd = fm.attn_bwd_multi if multi else fm.attn_bwd
 
     # per instrumented step: 0 start, 1/2 fwd kernel, 8 between the calls, 3/4 dK/dV
     # kernel, 6/7 dQ kernel, 5 end (all on the current stream, which the library launches
@@ -426,12 +458,12 @@ def main():
     def step(e=None):
         if e is not None:
             e[0].record()
-        fm.attn_fwd(q, k, v, *vec, ws=ws_f, out=o, lse=lse,
-                    events=None if e is None else (e[1], e[2]))
+        attn_fwd(q, k, v, *vec, ws=ws_f, out=o, lse=lse,
+                 events=None if e is None else (e[1], e[2]))
         if e is not None:
             e[8].record()
-        fm.attn_bwd(q, k, v, o, lse, do, *vec, ws=ws_b, grads=grads,
-                    events=None if e is None else (e[3], e[4], e[6], e[7]))
+        attn_bwd(q, k, v, o, lse, do, *vec, ws=ws_b, grads=grads,
+                 events=None if e is None else (e[3], e[4], e[6], e[7]))
         if e is not None:
             e[5].record()
 
@@ -481,7 +513,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": w.batch, "heads_q": w.heads_q,
-                   "heads_kv": w.heads_kv, "mask_heads": w.mask_heads, "seq_len": w.seqlen,
+                   "heads_kv": w.heads_kv, "mask_heads": w.mask_heads,
+                   "mask_intervals": w.n_intervals if multi else None, "seq_len": w.seqlen,
                    "head_dim": d, "attended_pairs": A, "seed": args.seed},
         "pct_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
         "kernels": {kname: {"ms": round(t, 4), "algorithmic_tflops": round(tflops[kname], 2)}

@@ -210,6 +210,49 @@ fm_status fm_localize_mask(const fm_problem* p, const fm_mask* global, const int
                            int32_t n_chunks, int32_t chunk_len, const fm_mask_out* local,
                            void* stream);
 
+/* ---- Multi-interval column masks -------------------------------------------------------
+ * The FlashMask Guide ("Multi-Interval Sparse Masks") generalizes the column-wise form to
+ * up to 4 active row intervals per key column: key j is visible to query row i iff
+ *
+ *     start[m][j] <= i < end[m][j]   for some m < n_intervals          (half-open)
+ *
+ * (the Guide's inclusive end FME is end = FME + 1).  Intervals may be empty (start >= end)
+ * or overlap.  start and end are int32 [B][H_m][n_intervals][N_k] in device memory, values
+ * in [0, N_q]; H_m = p->mask_heads as for the four-vector form.  Tile rule, from the
+ * block-wise min/max of each interval's starts and ends: skip when every interval lies
+ * outside the tile's rows in every column (q1 <= min start_m or q0 >= max end_m for all
+ * m), unmasked when one interval holds them in every column (q0 >= max start_m and
+ * q1 <= min end_m for some m), partial otherwise.
+ *
+ * The _multi entry points behave exactly as their four-vector counterparts (same problem,
+ * arguments, workspace sizes, outputs and errors), except:
+ *   - fm_tiles.block_minmax is [R][nKB][4 * n_intervals]: per interval {min start, max
+ *     start, min end, max end};
+ *   - FM_ERR_INVALID_ARG for n_intervals outside 1..4;
+ *   - fm_localize_mask_multi renumbers every start and end (R * n_intervals * N_k each) into
+ *     local_start / local_end (device int32, the same shape). */
+typedef struct {
+  const int32_t* start;
+  const int32_t* end;
+  int32_t n_intervals;
+} fm_mask_multi;
+
+fm_status fm_classify_tiles_multi(const fm_problem* p, const fm_mask_multi* m, int32_t block_q,
+                                  int32_t block_k, const fm_tiles* out, void* ws,
+                                  size_t ws_bytes, void* stream);
+fm_status fm_attn_fwd_multi(const fm_problem* p, const void* q, const void* k, const void* v,
+                            const fm_mask_multi* m, void* o, float* lse, void* ws,
+                            size_t ws_bytes, void* stream, const fm_kernel_events* events);
+fm_status fm_attn_bwd_multi(const fm_problem* p, const void* q, const void* k, const void* v,
+                            const void* o, const float* lse, const void* dout,
+                            const fm_mask_multi* m, void* dq, void* dk, void* dv, void* ws,
+                            size_t ws_bytes, void* stream, const fm_kernel_events* events);
+fm_status fm_debug_expand_mask_multi(const fm_problem* p, const fm_mask_multi* m, int32_t b,
+                                     int32_t row0, int32_t row1, uint8_t* dense, void* stream);
+fm_status fm_localize_mask_multi(const fm_problem* p, const fm_mask_multi* global,
+                                 const int32_t* offsets, int32_t n_chunks, int32_t chunk_len,
+                                 int32_t* local_start, int32_t* local_end, void* stream);
+
 /* Static description of a status code. */
 const char* fm_status_string(fm_status s);
 

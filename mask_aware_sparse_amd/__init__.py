@@ -60,6 +60,11 @@ class Mask(ctypes.Structure):
                 ("uts", ctypes.c_void_p), ("ute", ctypes.c_void_p)]
 
 
+class MaskMulti(ctypes.Structure):
+    _fields_ = [("start", ctypes.c_void_p), ("end", ctypes.c_void_p),
+                ("n_intervals", ctypes.c_int32)]
+
+
 class KernelEvents(ctypes.Structure):
     _fields_ = [("start", ctypes.c_void_p), ("stop", ctypes.c_void_p),
                 ("start2", ctypes.c_void_p), ("stop2", ctypes.c_void_p)]
@@ -87,6 +92,7 @@ def library():
         lib = ctypes.CDLL(path)
         PP, PM, PT = ctypes.POINTER(Problem), ctypes.POINTER(Mask), ctypes.POINTER(Tiles)
         PE = ctypes.POINTER(KernelEvents)
+        PX = ctypes.POINTER(MaskMulti)
         sig = {
             "fm_status_string": ([_STATUS], ctypes.c_char_p),
             "fm_tile_shape": ([_STATUS, ctypes.POINTER(ctypes.c_int32),
@@ -102,6 +108,16 @@ def library():
                                       _P, _P], _STATUS),
             "fm_localize_mask": ([PP, PM, _P, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.POINTER(MaskOut), _P], _STATUS),
+            "fm_classify_tiles_multi": ([PP, PX, ctypes.c_int32, ctypes.c_int32, PT, _P,
+                                         ctypes.c_size_t, _P], _STATUS),
+            "fm_attn_fwd_multi": ([PP, _P, _P, _P, PX, _P, _P, _P, ctypes.c_size_t, _P, PE],
+                                  _STATUS),
+            "fm_attn_bwd_multi": ([PP, _P, _P, _P, _P, _P, _P, PX, _P, _P, _P, _P,
+                                   ctypes.c_size_t, _P, PE], _STATUS),
+            "fm_debug_expand_mask_multi": ([PP, PX, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, _P, _P], _STATUS),
+            "fm_localize_mask_multi": ([PP, PX, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P],
+                                       _STATUS),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -204,21 +220,31 @@ def ipo_balance(weights, ranks, stages=3):
                    "moves": rep.moves}
 
 
-def classify_tiles(lts, lte, uts, ute, block_q, block_k, heads_q=1, heads_kv=1, stream=None,
-                   out=None, ws=None, seqlen_q=None):
-    """Run fm_classify_tiles; returns a dict of device tensors (see fm_tiles in fm.h).
-    The vectors are [B][N_k] or [B][H_m][N_k] (tiles per mask row b * H_m + m); `seqlen_q`
-    is N_q (default N_k).  `out` (a dict as returned by an earlier call of the same shape)
-    and `ws` (uint8 device tensor of at least workspace_size(..., OP_CLASSIFY, block_q,
-    block_k) bytes) may be passed to reuse buffers."""
-    B, Hm, Nk = _mask_dims(lts)
+def _mask_multi(starts, ends):
+    """(MaskMulti, B, H_m, M, N_k) for interval starts/ends [B][M][N_k] or [B][H_m][M][N_k]."""
+    for t in (starts, ends):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("interval starts/ends must be contiguous int32 tensors")
+    if starts.shape != ends.shape:
+        raise ValueError("interval starts and ends must have one shape")
+    if starts.dim() == 3:
+        B, M, N = starts.shape
+        Hm = 1
+    elif starts.dim() == 4:
+        B, Hm, M, N = starts.shape
+    else:
+        raise ValueError("interval starts/ends must be [B][M][N] or [B][H_m][M][N]")
+    return MaskMulti(starts.data_ptr(), ends.data_ptr(), int(M)), B, Hm, M, N
+
+
+def _classify(fn, m, B, Hm, Nk, block_q, block_k, heads_q, heads_kv, stream, out, ws, seqlen_q,
+              width, dev):
     if Hm > 1 and heads_q == 1 and heads_kv == 1:
         heads_q = Hm                      # the heads play no part in the classification
     N = Nk if seqlen_q is None else int(seqlen_q)
-    dev = lts.device
     nqb, nkb = -(-N // block_q), -(-Nk // block_k)
     if out is None:
-        out = _tile_buffers(B * Hm, N, nqb, nkb, dev)
+        out = _tile_buffers(B * Hm, N, nqb, nkb, dev, width)
     tiles = Tiles(*(out[n].data_ptr() if out[n].numel() else 0 for n, _ in Tiles._fields_))
     p = _problem(B, heads_q, heads_kv, N, seqlen_kv=Nk, mask_heads=Hm)
     nbytes = workspace_size(B, heads_q, heads_kv, N, OP_CLASSIFY, block_q, block_k,
@@ -227,17 +253,35 @@ def classify_tiles(lts, lte, uts, ute, block_q, block_k, heads_q=1, heads_kv=1, 
         ws = _workspace(nbytes, dev)
     elif ws.numel() < nbytes:
         raise ValueError("workspace too small")
-    m = _mask(lts, lte, uts, ute)
-    _check(library().fm_classify_tiles(ctypes.byref(p), ctypes.byref(m), int(block_q),
-                                       int(block_k), ctypes.byref(tiles), _ptr(ws),
-                                       ctypes.c_size_t(nbytes), _stream(dev, stream)),
-           "fm_classify_tiles")
+    _check(fn(ctypes.byref(p), ctypes.byref(m), int(block_q), int(block_k), ctypes.byref(tiles),
+              _ptr(ws), ctypes.c_size_t(nbytes), _stream(dev, stream)), fn.__name__)
     return out
 
 
-def _tile_buffers(B, N, nqb, nkb, dev):
+def classify_tiles(lts, lte, uts, ute, block_q, block_k, heads_q=1, heads_kv=1, stream=None,
+                   out=None, ws=None, seqlen_q=None):
+    """Run fm_classify_tiles; returns a dict of device tensors (see fm_tiles in fm.h).
+    The vectors are [B][N_k] or [B][H_m][N_k] (tiles per mask row b * H_m + m); `seqlen_q`
+    is N_q (default N_k).  `out` (a dict as returned by an earlier call of the same shape)
+    and `ws` (uint8 device tensor of at least workspace_size(..., OP_CLASSIFY, block_q,
+    block_k) bytes) may be passed to reuse buffers."""
+    B, Hm, Nk = _mask_dims(lts)
+    return _classify(library().fm_classify_tiles, _mask(lts, lte, uts, ute), B, Hm, Nk, block_q,
+                     block_k, heads_q, heads_kv, stream, out, ws, seqlen_q, 8, lts.device)
+
+
+def classify_tiles_multi(starts, ends, block_q, block_k, heads_q=1, heads_kv=1, stream=None,
+                         out=None, ws=None, seqlen_q=None):
+    """fm_classify_tiles_multi for interval starts/ends [B][M][N_k] or [B][H_m][M][N_k];
+    block_minmax is [B*H_m][nKB][4M]."""
+    m, B, Hm, M, Nk = _mask_multi(starts, ends)
+    return _classify(library().fm_classify_tiles_multi, m, B, Hm, Nk, block_q, block_k, heads_q,
+                     heads_kv, stream, out, ws, seqlen_q, 4 * M, starts.device)
+
+
+def _tile_buffers(B, N, nqb, nkb, dev, width=8):
     return {
-        "block_minmax": torch.empty((B, nkb, 8), dtype=torch.int32, device=dev),
+        "block_minmax": torch.empty((B, nkb, width), dtype=torch.int32, device=dev),
         "tile_class": torch.empty((B, nqb, nkb), dtype=torch.uint8, device=dev),
         "q_queue": torch.empty((B, nqb, nkb), dtype=torch.int32, device=dev),
         "q_count": torch.empty((B, nqb, 2), dtype=torch.int32, device=dev),
@@ -248,9 +292,9 @@ def _tile_buffers(B, N, nqb, nkb, dev):
     }
 
 
-def _shapes(q, k, lts):
+def _shapes(q, k, mask_shape):
     """(B, H_q, H_kv, N_q, N_k, d, H_m) from Q [B][H_q][N_q][d], K [B][H_kv][N_k][d] and
-    the vectors [B][N_k] or [B][H_m][N_k]."""
+    the mask's (B, H_m, N_k)."""
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("expected Q [B][H_q][N_q][d] and K/V [B][H_kv][N_k][d]")
     B, Hq, N, d = q.shape
@@ -259,9 +303,9 @@ def _shapes(q, k, lts):
     if k.shape[2] == 0 and N > 0:
         # fm_problem.seqlen_kv = 0 means "as many keys as rows"
         raise ValueError("query rows without keys cannot be expressed (seqlen_kv = 0 means N_q)")
-    Bm, Hm, Nm = _mask_dims(lts)
+    Bm, Hm, Nm = mask_shape
     if Bm != B or Nm != k.shape[2]:
-        raise ValueError("mask vectors must be [B][N_k] or [B][H_m][N_k]")
+        raise ValueError("the mask's batch and key length must match Q and K")
     return B, Hq, k.shape[1], N, k.shape[2], d, Hm
 
 
@@ -285,57 +329,96 @@ def _events(ev):
     return ctypes.byref(KernelEvents(*handles))
 
 
-def attn_fwd(q, k, v, lts, lte, uts, ute, scale=None, ws=None, out=None, lse=None, stream=None,
-             events=None):
-    """O (bf16 [B][H_q][N_q][d]) and LSE (fp32 [B][H_q][N_q], natural log) via fm_attn_fwd;
-    K/V are [B][H_kv][N_k][d] and the vectors [B][N_k] or, one set per group of H_q / H_m
-    query heads, [B][H_m][N_k].
-    `events`: optional (start, stop) torch.cuda.Event pair timing the attention kernel."""
+def _fwd(fn, q, k, v, m, mask_shape, scale, ws, out, lse, stream, events):
     _bf16(q, k, v)
-    B, Hq, Hkv, N, Nk, d, Hm = _shapes(q, k, lts)
+    B, Hq, Hkv, N, Nk, d, Hm = _shapes(q, k, mask_shape)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
     p = _problem(B, Hq, Hkv, N, scale, head_dim=d, seqlen_kv=Nk, mask_heads=Hm)
     nbytes = workspace_size(B, Hq, Hkv, N, OP_FWD, head_dim=d, seqlen_kv=Nk, mask_heads=Hm)
     w = _workspace(nbytes, q.device, ws)
-    m = _mask(lts, lte, uts, ute)
-    _check(library().fm_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(m),
-                                 _ptr(o), _ptr(lse_t), _ptr(w), ctypes.c_size_t(nbytes),
-                                 _stream(q.device, stream), _events(events)), "fm_attn_fwd")
+    _check(fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(m), _ptr(o), _ptr(lse_t),
+              _ptr(w), ctypes.c_size_t(nbytes), _stream(q.device, stream), _events(events)),
+           fn.__name__)
     return o, lse_t
 
 
-def attn_bwd(q, k, v, o, lse, dout, lts, lte, uts, ute, scale=None, ws=None, grads=None,
-             stream=None, events=None):
-    """(dQ, dK, dV) in bf16 via fm_attn_bwd.  `events`: optional (start, stop, start2,
-    stop2) torch.cuda.Event objects timing the dK/dV kernel and the dQ kernel."""
+def _bwd(fn, q, k, v, o, lse, dout, m, mask_shape, scale, ws, grads, stream, events):
     _bf16(q, k, v, o, dout)
-    B, Hq, Hkv, N, Nk, d, Hm = _shapes(q, k, lts)
+    B, Hq, Hkv, N, Nk, d, Hm = _shapes(q, k, mask_shape)
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = grads
     p = _problem(B, Hq, Hkv, N, scale, head_dim=d, seqlen_kv=Nk, mask_heads=Hm)
     nbytes = workspace_size(B, Hq, Hkv, N, OP_BWD, head_dim=d, seqlen_kv=Nk, mask_heads=Hm)
     w = _workspace(nbytes, q.device, ws)
-    m = _mask(lts, lte, uts, ute)
-    _check(library().fm_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                 _ptr(dout), ctypes.byref(m), _ptr(dq), _ptr(dk), _ptr(dv),
-                                 _ptr(w), ctypes.c_size_t(nbytes), _stream(q.device, stream),
-                                 _events(events)), "fm_attn_bwd")
+    _check(fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+              ctypes.byref(m), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(w), ctypes.c_size_t(nbytes),
+              _stream(q.device, stream), _events(events)), fn.__name__)
     return dq, dk, dv
+
+
+def attn_fwd(q, k, v, lts, lte, uts, ute, scale=None, ws=None, out=None, lse=None, stream=None,
+             events=None):
+    """O (bf16 [B][H_q][N_q][d]) and LSE (fp32 [B][H_q][N_q], natural log) via fm_attn_fwd;
+    K/V are [B][H_kv][N_k][d] and the vectors [B][N_k] or, one set per group of H_q / H_m
+    query heads, [B][H_m][N_k].
+    `events`: optional (start, stop) torch.cuda.Event pair timing the attention kernel."""
+    return _fwd(library().fm_attn_fwd, q, k, v, _mask(lts, lte, uts, ute), _mask_dims(lts),
+                scale, ws, out, lse, stream, events)
+
+
+def attn_fwd_multi(q, k, v, starts, ends, scale=None, ws=None, out=None, lse=None, stream=None,
+                   events=None):
+    """fm_attn_fwd_multi: as attn_fwd with the multi-interval mask, starts/ends
+    [B][M][N_k] or [B][H_m][M][N_k] (key j visible to row i iff some interval holds i)."""
+    m, B, Hm, M, Nk = _mask_multi(starts, ends)
+    return _fwd(library().fm_attn_fwd_multi, q, k, v, m, (B, Hm, Nk), scale, ws, out, lse,
+                stream, events)
+
+
+def attn_bwd(q, k, v, o, lse, dout, lts, lte, uts, ute, scale=None, ws=None, grads=None,
+             stream=None, events=None):
+    """(dQ, dK, dV) in bf16 via fm_attn_bwd.  `events`: optional (start, stop, start2,
+    stop2) torch.cuda.Event objects timing the dK/dV kernel and the dQ kernel."""
+    return _bwd(library().fm_attn_bwd, q, k, v, o, lse, dout, _mask(lts, lte, uts, ute),
+                _mask_dims(lts), scale, ws, grads, stream, events)
+
+
+def attn_bwd_multi(q, k, v, o, lse, dout, starts, ends, scale=None, ws=None, grads=None,
+                   stream=None, events=None):
+    """fm_attn_bwd_multi: as attn_bwd with the multi-interval mask."""
+    m, B, Hm, M, Nk = _mask_multi(starts, ends)
+    return _bwd(library().fm_attn_bwd_multi, q, k, v, o, lse, dout, m, (B, Hm, Nk), scale, ws,
+                grads, stream, events)
+
+
+def _expand(fn, m, B, Hm, N, b, row0, row1, stream, seqlen_q, dev):
+    dense = torch.empty((row1 - row0, N), dtype=torch.uint8, device=dev)
+    p = _problem(B, Hm, 1, N if seqlen_q is None else int(seqlen_q), seqlen_kv=N, mask_heads=Hm)
+    _check(fn(ctypes.byref(p), ctypes.byref(m), int(b), int(row0), int(row1), _ptr(dense),
+              _stream(dev, stream)), fn.__name__)
+    return dense
 
 
 def debug_expand_mask(lts, lte, uts, ute, b, row0, row1, stream=None, seqlen_q=None):
     """uint8 [row1-row0][N_k] dense expansion (1 = hidden) by the kernels' predicate, of
     mask row b (batch row * H_m + set for per-head vectors)."""
     B, Hm, N = _mask_dims(lts)
-    dense = torch.empty((row1 - row0, N), dtype=torch.uint8, device=lts.device)
-    p = _problem(B, Hm, 1, N if seqlen_q is None else int(seqlen_q), seqlen_kv=N, mask_heads=Hm)
-    m = _mask(lts, lte, uts, ute)
-    _check(library().fm_debug_expand_mask(ctypes.byref(p), ctypes.byref(m), int(b), int(row0),
-                                          int(row1), _ptr(dense), _stream(lts.device, stream)),
-           "fm_debug_expand_mask")
-    return dense
+    return _expand(library().fm_debug_expand_mask, _mask(lts, lte, uts, ute), B, Hm, N, b, row0,
+                   row1, stream, seqlen_q, lts.device)
+
+
+def debug_expand_mask_multi(starts, ends, b, row0, row1, stream=None, seqlen_q=None):
+    """Dense expansion of mask row b of the multi-interval form (1 = hidden)."""
+    m, B, Hm, M, N = _mask_multi(starts, ends)
+    return _expand(library().fm_debug_expand_mask_multi, m, B, Hm, N, b, row0, row1, stream,
+                   seqlen_q, starts.device)
+
+
+def _offsets(offsets):
+    if offsets.dtype != torch.int32 or not offsets.is_contiguous() or offsets.dim() != 1:
+        raise ValueError("offsets must be a contiguous int32 tensor [n_chunks]")
 
 
 def localize_mask(lts, lte, uts, ute, offsets, chunk_len, out=None, stream=None):
@@ -344,8 +427,7 @@ def localize_mask(lts, lte, uts, ute, offsets, chunk_len, out=None, stream=None)
     ascending, non-overlapping).  Returns four int32 tensors of the vectors' shape ([B][N_k]
     or [B][H_m][N_k])."""
     B, Hm, N = _mask_dims(lts)
-    if offsets.dtype != torch.int32 or not offsets.is_contiguous() or offsets.dim() != 1:
-        raise ValueError("offsets must be a contiguous int32 tensor [n_chunks]")
+    _offsets(offsets)
     if out is None:
         out = tuple(torch.empty_like(lts) for _ in range(4))
     p = _problem(B, 1, 1, 0, seqlen_kv=N, mask_heads=Hm)
@@ -357,6 +439,21 @@ def localize_mask(lts, lte, uts, ute, offsets, chunk_len, out=None, stream=None)
     return out
 
 
+def localize_mask_multi(starts, ends, offsets, chunk_len, out=None, stream=None):
+    """fm_localize_mask_multi: every interval start and end renumbered into the rank's rows.
+    Returns (starts, ends) of the input's shape."""
+    m, B, Hm, M, N = _mask_multi(starts, ends)
+    _offsets(offsets)
+    if out is None:
+        out = (torch.empty_like(starts), torch.empty_like(ends))
+    p = _problem(B, 1, 1, 0, seqlen_kv=N, mask_heads=Hm)
+    _check(library().fm_localize_mask_multi(ctypes.byref(p), ctypes.byref(m), _ptr(offsets),
+                                            int(offsets.numel()), int(chunk_len), _ptr(out[0]),
+                                            _ptr(out[1]), _stream(starts.device, stream)),
+           "fm_localize_mask_multi")
+    return out
+
+
 # The C names, for callers that prefer them.
 fm_tile_shape = tile_shape
 fm_workspace_size = workspace_size
@@ -365,6 +462,11 @@ fm_attn_fwd = attn_fwd
 fm_attn_bwd = attn_bwd
 fm_debug_expand_mask = debug_expand_mask
 fm_localize_mask = localize_mask
+fm_classify_tiles_multi = classify_tiles_multi
+fm_attn_fwd_multi = attn_fwd_multi
+fm_attn_bwd_multi = attn_bwd_multi
+fm_debug_expand_mask_multi = debug_expand_mask_multi
+fm_localize_mask_multi = localize_mask_multi
 fm_status_string = status_string
 
 fm_ipo_balance = ipo_balance

@@ -52,6 +52,23 @@ fm_status check_mask(const fm_problem* p, const fm_mask* m) {
   return FM_OK;
 }
 
+fm_status check_mask(const fm_problem* p, const fm_mask_multi* m) {
+  if (!m) return FM_ERR_INVALID_ARG;
+  if (m->n_intervals < 1 || m->n_intervals > fm::kMaxIntervals) return FM_ERR_INVALID_ARG;
+  if (mask_rows(p) * nk_of(p) == 0) return FM_OK;
+  if (!m->start || !m->end) return FM_ERR_INVALID_ARG;
+  if (mask_rows(p) * m->n_intervals * nk_of(p) > INT32_MAX) return FM_ERR_UNSUPPORTED;
+  return FM_OK;
+}
+
+fm::MaskArgs mask_args(const fm_mask* m) {
+  return fm::MaskArgs{fm::MaskPtrs{m->lts, m->lte, m->uts, m->ute}, nullptr, nullptr, 0};
+}
+fm::MaskArgs mask_args(const fm_mask_multi* m) {
+  return fm::MaskArgs{fm::MaskPtrs{nullptr, nullptr, nullptr, nullptr}, m->start, m->end,
+                      m->n_intervals};
+}
+
 float scale_of(const fm_problem* p) {
   return p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
 }
@@ -85,7 +102,7 @@ FwdWs fwd_ws(const fm_problem* p, const Blocks& nb) {
   FwdWs w{};
   const size_t B = mask_rows(p);  // tile structures are per mask row
   size_t off = 0;
-  w.mm = off; off += align_up(B * nb.nKB * 8 * 4);
+  w.mm = off; off += align_up(B * nb.nKB * fm::kMaxMinmaxWidth * 4);
   w.q_queue = off; off += align_up(B * nb.nQB * nb.nKB * 4);
   w.q_count = off; off += align_up(B * nb.nQB * 2 * 4);
   w.q_cost = off; off += align_up(B * nb.nQB * 4);
@@ -106,12 +123,12 @@ BwdWs bwd_ws(const fm_problem* p, const Blocks& nk, const Blocks& nq) {
   const size_t rk = (size_t)p->batch * p->heads_kv * nk_of(p);
   const size_t B = mask_rows(p);  // tile structures are per mask row
   size_t off = 0;
-  w.mm_k = off; off += align_up(B * nk.nKB * 8 * 4);
+  w.mm_k = off; off += align_up(B * nk.nKB * fm::kMaxMinmaxWidth * 4);
   w.k_queue = off; off += align_up(B * nk.nKB * nk.nQB * 4);
   w.k_count = off; off += align_up(B * nk.nKB * 2 * 4);
   w.k_cost = off; off += align_up(B * nk.nKB * 4);
   w.k_order = off; off += align_up(B * nk.nKB * 4);
-  w.mm_q = off; off += align_up(B * nq.nKB * 8 * 4);
+  w.mm_q = off; off += align_up(B * nq.nKB * fm::kMaxMinmaxWidth * 4);
   w.q_queue = off; off += align_up(B * nq.nQB * nq.nKB * 4);
   w.q_count = off; off += align_up(B * nq.nQB * 2 * 4);
   w.q_cost = off; off += align_up(B * nq.nQB * 4);
@@ -134,8 +151,6 @@ template <typename T>
 T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
-
-MaskPtrs mask_ptrs(const fm_mask* m) { return MaskPtrs{m->lts, m->lte, m->uts, m->ute}; }
 
 hipEvent_t ev_start(const fm_kernel_events* e) {
   return e ? static_cast<hipEvent_t>(e->start) : nullptr;
@@ -214,9 +229,13 @@ fm_status fm_workspace_size(const fm_problem* p, fm_op op, int32_t block_q, int3
   return FM_ERR_INVALID_ARG;
 }
 
-fm_status fm_classify_tiles(const fm_problem* p, const fm_mask* m, int32_t block_q,
-                            int32_t block_k, const fm_tiles* out, void* ws, size_t ws_bytes,
-                            void* stream) {
+}  // extern "C"
+
+namespace {
+
+template <typename MaskT>
+fm_status classify_impl(const fm_problem* p, const MaskT* m, int32_t block_q, int32_t block_k,
+                        const fm_tiles* out, void* ws, size_t ws_bytes, void* stream) {
   fm_status st = check_problem(p);
   if (st != FM_OK) return st;
   if ((st = check_mask(p, m)) != FM_OK) return st;
@@ -241,15 +260,16 @@ fm_status fm_classify_tiles(const fm_problem* p, const fm_mask* m, int32_t block
   t.k_count = out->k_count;
   t.k_cost = at<int32_t>(ws, w.k_cost);
   const int R = (int)mask_rows(p);
-  hipError_t e = fm::launch_classify(mask_ptrs(m), R, nq_of(p), nk_of(p), block_q, block_k, t, s);
+  hipError_t e = fm::launch_classify(mask_args(m), R, nq_of(p), nk_of(p), block_q, block_k, t, s);
   if (e == hipSuccess) e = fm::launch_lpt_sort(t.q_cost, out->q_order, (int)(R * nb.nQB), s);
   if (e == hipSuccess) e = fm::launch_lpt_sort(t.k_cost, out->k_order, (int)(R * nb.nKB), s);
   return hip_status(e);
 }
 
-fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const void* v,
-                      const fm_mask* m, void* o, float* lse, void* ws, size_t ws_bytes,
-                      void* stream, const fm_kernel_events* events) {
+template <typename MaskT>
+fm_status fwd_impl(const fm_problem* p, const void* q, const void* k, const void* v,
+                   const MaskT* m, void* o, float* lse, void* ws, size_t ws_bytes, void* stream,
+                   const fm_kernel_events* events) {
   fm_status st = check_problem(p);
   if (st != FM_OK) return st;
   if ((st = check_mask(p, m)) != FM_OK) return st;
@@ -265,19 +285,20 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
   if ((st = check_ws(ws, ws_bytes, w.total)) != FM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
+  const fm::MaskArgs ma = mask_args(m);
   fm::TileOut t{};
   t.minmax = at<int32_t>(ws, w.mm);
   t.q_queue = at<int32_t>(ws, w.q_queue);
   t.q_count = at<int32_t>(ws, w.q_count);
   t.q_cost = at<int32_t>(ws, w.q_cost);
   const int R = (int)mask_rows(p);
-  hipError_t e = fm::launch_classify(mask_ptrs(m), R, nq_of(p), nk_of(p), fm::kFwdBlockQ,
-                                     fm::kFwdBlockK, t, s);
+  hipError_t e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kFwdBlockQ, fm::kFwdBlockK,
+                                     t, s);
   int32_t* order = at<int32_t>(ws, w.q_order);
   if (e == hipSuccess) e = fm::launch_lpt_sort(t.q_cost, order, (int)(R * nb.nQB), s);
   if (e == hipSuccess) {
     fm::FwdArgs a{};
-    a.q = q; a.k = k; a.v = v; a.m = mask_ptrs(m); a.o = o; a.lse = lse;
+    a.q = q; a.k = k; a.v = v; a.m = ma; a.o = o; a.lse = lse;
     a.q_queue = t.q_queue; a.q_count = t.q_count; a.q_order = order;
     a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.Hm = hm_of(p);
     a.Nq = nq_of(p); a.Nk = nk_of(p);
@@ -288,10 +309,11 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
   return hip_status(e);
 }
 
-fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
-                      const void* o, const float* lse, const void* dout, const fm_mask* m,
-                      void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream,
-                      const fm_kernel_events* events) {
+template <typename MaskT>
+fm_status bwd_impl(const fm_problem* p, const void* q, const void* k, const void* v,
+                   const void* o, const float* lse, const void* dout, const MaskT* m, void* dq,
+                   void* dk, void* dv, void* ws, size_t ws_bytes, void* stream,
+                   const fm_kernel_events* events) {
   fm_status st = check_problem(p);
   if (st != FM_OK) return st;
   if ((st = check_mask(p, m)) != FM_OK) return st;
@@ -310,6 +332,7 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   if ((st = check_ws(ws, ws_bytes, w.total)) != FM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
+  const fm::MaskArgs ma = mask_args(m);
   fm::TileOut tk{};
   tk.minmax = at<int32_t>(ws, w.mm_k);
   tk.k_queue = at<int32_t>(ws, w.k_queue);
@@ -323,16 +346,15 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   int32_t* k_order = at<int32_t>(ws, w.k_order);
   int32_t* q_order = at<int32_t>(ws, w.q_order);
   const int R = (int)mask_rows(p);
-  hipError_t e = fm::launch_classify(mask_ptrs(m), R, nq_of(p), nk_of(p), fm::kBwdBlockQ,
-                                     fm::kBwdBlockK, tk, s);
+  hipError_t e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kBwdBlockQ, fm::kBwdBlockK,
+                                     tk, s);
   if (e == hipSuccess) e = fm::launch_lpt_sort(tk.k_cost, k_order, (int)(R * nk.nKB), s);
   if (e == hipSuccess)
-    e = fm::launch_classify(mask_ptrs(m), R, nq_of(p), nk_of(p), fm::kFwdBlockQ, fm::kFwdBlockK,
-                            tq, s);
+    e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kFwdBlockQ, fm::kFwdBlockK, tq, s);
   if (e == hipSuccess) e = fm::launch_lpt_sort(tq.q_cost, q_order, (int)(R * nq.nQB), s);
   if (e == hipSuccess) {
     fm::BwdArgs a{};
-    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout; a.m = mask_ptrs(m);
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout; a.m = ma;
     a.dq = dq; a.dk = dk; a.dv = dv;
     a.k_queue = tk.k_queue; a.k_count = tk.k_count; a.k_order = k_order;
     a.q_queue = tq.q_queue; a.q_count = tq.q_count; a.q_order = q_order;
@@ -355,8 +377,9 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   return hip_status(e);
 }
 
-fm_status fm_debug_expand_mask(const fm_problem* p, const fm_mask* m, int32_t b, int32_t row0,
-                               int32_t row1, uint8_t* dense, void* stream) {
+template <typename MaskT>
+fm_status expand_impl(const fm_problem* p, const MaskT* m, int32_t b, int32_t row0, int32_t row1,
+                      uint8_t* dense, void* stream) {
   fm_status st = check_problem(p);
   if (st != FM_OK) return st;
   if ((st = check_mask(p, m)) != FM_OK) return st;
@@ -364,8 +387,71 @@ fm_status fm_debug_expand_mask(const fm_problem* p, const fm_mask* m, int32_t b,
     return FM_ERR_INVALID_ARG;
   if (row1 == row0 || nk_of(p) == 0) return FM_OK;
   if (!dense) return FM_ERR_INVALID_ARG;
-  return hip_status(fm::launch_expand_mask(mask_ptrs(m), b, nk_of(p), row0, row1, dense,
+  return hip_status(fm::launch_expand_mask(mask_args(m), b, nk_of(p), row0, row1, dense,
                                            static_cast<hipStream_t>(stream)));
+}
+
+// Shared checks of the localization entry points; `cols` = bounds per array.
+fm_status check_localize(const fm_problem* p, const int32_t* offsets, int32_t n_chunks,
+                         int32_t chunk_len, int64_t cols) {
+  if (n_chunks < 1 || chunk_len < 1) return FM_ERR_INVALID_ARG;
+  if (n_chunks > 4096 || nk_of(p) > (1 << 22)) return FM_ERR_UNSUPPORTED;
+  if ((int64_t)n_chunks * chunk_len > (1 << 22)) return FM_ERR_UNSUPPORTED;
+  if (cols > INT32_MAX) return FM_ERR_UNSUPPORTED;
+  if (cols > 0 && !offsets) return FM_ERR_INVALID_ARG;
+  return FM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fm_status fm_classify_tiles(const fm_problem* p, const fm_mask* m, int32_t block_q,
+                            int32_t block_k, const fm_tiles* out, void* ws, size_t ws_bytes,
+                            void* stream) {
+  return classify_impl(p, m, block_q, block_k, out, ws, ws_bytes, stream);
+}
+
+fm_status fm_classify_tiles_multi(const fm_problem* p, const fm_mask_multi* m, int32_t block_q,
+                                  int32_t block_k, const fm_tiles* out, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  return classify_impl(p, m, block_q, block_k, out, ws, ws_bytes, stream);
+}
+
+fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const void* v,
+                      const fm_mask* m, void* o, float* lse, void* ws, size_t ws_bytes,
+                      void* stream, const fm_kernel_events* events) {
+  return fwd_impl(p, q, k, v, m, o, lse, ws, ws_bytes, stream, events);
+}
+
+fm_status fm_attn_fwd_multi(const fm_problem* p, const void* q, const void* k, const void* v,
+                            const fm_mask_multi* m, void* o, float* lse, void* ws,
+                            size_t ws_bytes, void* stream, const fm_kernel_events* events) {
+  return fwd_impl(p, q, k, v, m, o, lse, ws, ws_bytes, stream, events);
+}
+
+fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
+                      const void* o, const float* lse, const void* dout, const fm_mask* m,
+                      void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream,
+                      const fm_kernel_events* events) {
+  return bwd_impl(p, q, k, v, o, lse, dout, m, dq, dk, dv, ws, ws_bytes, stream, events);
+}
+
+fm_status fm_attn_bwd_multi(const fm_problem* p, const void* q, const void* k, const void* v,
+                            const void* o, const float* lse, const void* dout,
+                            const fm_mask_multi* m, void* dq, void* dk, void* dv, void* ws,
+                            size_t ws_bytes, void* stream, const fm_kernel_events* events) {
+  return bwd_impl(p, q, k, v, o, lse, dout, m, dq, dk, dv, ws, ws_bytes, stream, events);
+}
+
+fm_status fm_debug_expand_mask(const fm_problem* p, const fm_mask* m, int32_t b, int32_t row0,
+                               int32_t row1, uint8_t* dense, void* stream) {
+  return expand_impl(p, m, b, row0, row1, dense, stream);
+}
+
+fm_status fm_debug_expand_mask_multi(const fm_problem* p, const fm_mask_multi* m, int32_t b,
+                                     int32_t row0, int32_t row1, uint8_t* dense, void* stream) {
+  return expand_impl(p, m, b, row0, row1, dense, stream);
 }
 
 fm_status fm_localize_mask(const fm_problem* p, const fm_mask* global, const int32_t* offsets,
@@ -374,19 +460,34 @@ fm_status fm_localize_mask(const fm_problem* p, const fm_mask* global, const int
   if (!p || !global || !local) return FM_ERR_INVALID_ARG;
   if (p->batch < 0 || p->seqlen < 0 || p->seqlen_kv < 0 || p->mask_heads < 0)
     return FM_ERR_INVALID_ARG;
-  if (n_chunks < 1 || chunk_len < 1) return FM_ERR_INVALID_ARG;
-  if (n_chunks > 4096 || nk_of(p) > (1 << 22)) return FM_ERR_UNSUPPORTED;
-  if ((int64_t)n_chunks * chunk_len > (1 << 22)) return FM_ERR_UNSUPPORTED;
   const int64_t cols = mask_rows(p) * nk_of(p);
-  if (cols == 0) return FM_OK;
-  if (cols > INT32_MAX) return FM_ERR_UNSUPPORTED;
-  if (!offsets || !global->lts || !global->lte || !global->uts || !global->ute || !local->lts ||
+  fm_status st = check_localize(p, offsets, n_chunks, chunk_len, cols);
+  if (st != FM_OK || cols == 0) return st;
+  if (!global->lts || !global->lte || !global->uts || !global->ute || !local->lts ||
       !local->lte || !local->uts || !local->ute)
     return FM_ERR_INVALID_ARG;
-  return hip_status(fm::launch_localize(mask_ptrs(global), offsets, n_chunks, chunk_len,
-                                        fm::MaskOut{local->lts, local->lte, local->uts,
-                                                    local->ute},
-                                        cols, static_cast<hipStream_t>(stream)));
+  return hip_status(fm::launch_localize(
+      fm::MaskPtrs{global->lts, global->lte, global->uts, global->ute}, 4, offsets, n_chunks,
+      chunk_len, fm::MaskOut{local->lts, local->lte, local->uts, local->ute}, cols,
+      static_cast<hipStream_t>(stream)));
+}
+
+fm_status fm_localize_mask_multi(const fm_problem* p, const fm_mask_multi* global,
+                                 const int32_t* offsets, int32_t n_chunks, int32_t chunk_len,
+                                 int32_t* local_start, int32_t* local_end, void* stream) {
+  if (!p || !global) return FM_ERR_INVALID_ARG;
+  if (p->batch < 0 || p->seqlen < 0 || p->seqlen_kv < 0 || p->mask_heads < 0)
+    return FM_ERR_INVALID_ARG;
+  if (global->n_intervals < 1 || global->n_intervals > fm::kMaxIntervals)
+    return FM_ERR_INVALID_ARG;
+  const int64_t cols = mask_rows(p) * global->n_intervals * nk_of(p);
+  fm_status st = check_localize(p, offsets, n_chunks, chunk_len, cols);
+  if (st != FM_OK || cols == 0) return st;
+  if (!global->start || !global->end || !local_start || !local_end) return FM_ERR_INVALID_ARG;
+  return hip_status(fm::launch_localize(
+      fm::MaskPtrs{global->start, global->end, nullptr, nullptr}, 2, offsets, n_chunks,
+      chunk_len, fm::MaskOut{local_start, local_end, nullptr, nullptr}, cols,
+      static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -76,11 +76,13 @@ constexpr int KS = D + 8;       // K row stride in LDS (272 B: row reads only)
 static_assert(BK == 32 * kWaves, "one 32-key slice per wave");
 
 // Q / dO tiles use the swizzled 320-byte layout (row reads and transposing reads).
+template <bool kMulti>
 struct __attribute__((aligned(16))) Smem {
   bf16 q[2][BQ * kSwzRow];
   bf16 dO[2][BQ * kSwzRow];
   bf16 k[BK * KS];
-  int4 mv[BK];  // the four row bounds of each key of the block
+  // per key of the block: the four row bounds, or the interval starts ([0]) and ends ([1])
+  int4 mv[kMulti ? 2 : 1][BK];
   float lse2[2][BQ];
   float dl[2][BQ];
 };
@@ -93,7 +95,7 @@ struct DkdvParams {
   const bf16* __restrict__ dout;
   const float* __restrict__ lse2;
   const float* __restrict__ delta;
-  MaskPtrs m;
+  MaskArgs m;
   const int32_t* __restrict__ k_queue;
   const int32_t* __restrict__ k_count;
   const int32_t* __restrict__ k_order;
@@ -107,9 +109,11 @@ struct DkdvParams {
   float scale;  // softmax scale (applied to dK)
 };
 
+// kMulti: the mask is the multi-interval form (else the four-vector form).
+template <bool kMulti>
 __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvParams p) {
   using namespace dkdv;
-  __shared__ Smem sm;
+  __shared__ Smem<kMulti> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
   const int N = p.Nk, Nq = p.Nq;  // N: keys (and mask columns)
@@ -166,13 +170,24 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
           buf_load16(kr_, off, s * 32);
     }
   }
-  if (hh == 0) {
+  if constexpr (!kMulti) {
+    if (hh == 0) {
+      const uint32_t vb = (uint32_t)N * 4, vo = (uint32_t)key * 4;
+      const size_t mrow = (size_t)mr * N;
+      sm.mv[0][wave * 32 + l32] = int4{(int)buf_load4(make_rsrc(p.m.v.lts + mrow, vb), vo, 0),
+                                       (int)buf_load4(make_rsrc(p.m.v.lte + mrow, vb), vo, 0),
+                                       (int)buf_load4(make_rsrc(p.m.v.uts + mrow, vb), vo, 0),
+                                       (int)buf_load4(make_rsrc(p.m.v.ute + mrow, vb), vo, 0)};
+    }
+  } else {
+    // lanes of the first half load the key's interval starts, the second half its ends;
+    // absent intervals read past the row's bounds and load 0 (the empty interval)
     const uint32_t vb = (uint32_t)N * 4, vo = (uint32_t)key * 4;
-    const size_t mrow = (size_t)mr * N;
-    sm.mv[wave * 32 + l32] = int4{(int)buf_load4(make_rsrc(p.m.lts + mrow, vb), vo, 0),
-                                  (int)buf_load4(make_rsrc(p.m.lte + mrow, vb), vo, 0),
-                                  (int)buf_load4(make_rsrc(p.m.uts + mrow, vb), vo, 0),
-                                  (int)buf_load4(make_rsrc(p.m.ute + mrow, vb), vo, 0)};
+    const size_t mrow = (size_t)mr * p.m.n * N;
+    const rsrc_t rs = make_rsrc((hh ? p.m.end : p.m.start) + mrow, (uint32_t)p.m.n * vb);
+    sm.mv[hh][wave * 32 + l32] = int4{(int)buf_load4(rs, vo, 0), (int)buf_load4(rs, vo + vb, 0),
+                                      (int)buf_load4(rs, vo + 2 * vb, 0),
+                                      (int)buf_load4(rs, vo + 3 * vb, 0)};
   }
   const bool key_ok = key < N;
 
@@ -261,9 +276,14 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
         constexpr bool kMasked = decltype(masked)::value;
         uint32_t word = 0u;
         if (kMasked) {
-          const int4 mv = sm.mv[wave * 32 + l32];
-          word = key_ok ? hidden_rows32(mv.x, mv.y, mv.z, mv.w, qb * BQ + qblk * 32)
-                        : 0xFFFFFFFFu;
+          const int r0 = qb * BQ + qblk * 32;
+          if constexpr (!kMulti) {
+            const int4 mv = sm.mv[0][wave * 32 + l32];
+            word = hidden_rows32(mv.x, mv.y, mv.z, mv.w, r0);
+          } else {
+            word = hidden_rows32_multi(sm.mv[0][wave * 32 + l32], sm.mv[1][wave * 32 + l32], r0);
+          }
+          word = key_ok ? word : 0xFFFFFFFFu;
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -368,7 +388,7 @@ struct DqParams {
   const float* __restrict__ lse;  // natural-log LSE from the forward
   float* __restrict__ lse2;       // written: LSE in log2 units (+inf where LSE = -inf)
   float* __restrict__ delta;      // written: rowsum(dO o O)
-  MaskPtrs m;
+  MaskArgs m;
   bf16* __restrict__ dq;
   const int32_t* __restrict__ q_queue;
   const int32_t* __restrict__ q_count;
@@ -378,6 +398,7 @@ struct DqParams {
   float scale;  // softmax scale (applied to dQ)
 };
 
+template <bool kMulti>
 __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   using namespace dqk;
   __shared__ Smem sm;
@@ -401,9 +422,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   const rsrc_t kr_ = make_rsrc(p.k + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
   const rsrc_t vr_ = make_rsrc(p.v + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
   const uint32_t vec_bytes = (uint32_t)N * 4, row_bytes = (uint32_t)Nq * 4;
-  const size_t mrow = (size_t)mr * N;
-  const rsrc_t m0 = make_rsrc(p.m.lts + mrow, vec_bytes), m1 = make_rsrc(p.m.lte + mrow, vec_bytes);
-  const rsrc_t m2 = make_rsrc(p.m.uts + mrow, vec_bytes), m3 = make_rsrc(p.m.ute + mrow, vec_bytes);
+  // mask row mr (multi-interval form: absent intervals load 0, the empty interval)
+  rsrc_t m0, m1, m2, m3;
+  if constexpr (!kMulti) {
+    const size_t mrow = (size_t)mr * N;
+    m0 = make_rsrc(p.m.v.lts + mrow, vec_bytes); m1 = make_rsrc(p.m.v.lte + mrow, vec_bytes);
+    m2 = make_rsrc(p.m.v.uts + mrow, vec_bytes); m3 = make_rsrc(p.m.v.ute + mrow, vec_bytes);
+  } else {
+    const size_t mrow = (size_t)mr * p.m.n * N;
+    m0 = make_rsrc(p.m.start + mrow, (uint32_t)p.m.n * vec_bytes);
+    m1 = make_rsrc(p.m.end + mrow, (uint32_t)p.m.n * vec_bytes);
+    m2 = m0; m3 = m1;
+  }
   const bool ragged = (N % BK) != 0;
 
   const int row = qb * BQ + wave * 32 + l32;
@@ -453,7 +483,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   const int cp_row = tid >> 4, cp_ch = (tid & 15) * 8;
   const int mk_key = lane, mk_wave = __builtin_amdgcn_readfirstlane(wave);
   u32x4 kst[4], vst[4];
-  uint32_t vec[4];
+  uint32_t vec[kMulti ? 2 * kMaxIntervals : 4];
 
   auto load_tile = [&](int e) {
     const int kb = e & 0x7fffffff;
@@ -466,8 +496,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
     const bool part = (e < 0) || (ragged && kb == p.nKB - 1);
     if (part) {
       const uint32_t vo = (uint32_t)(kb * BK + mk_key) * 4;
-      vec[0] = buf_load4(m0, vo, 0); vec[1] = buf_load4(m1, vo, 0);
-      vec[2] = buf_load4(m2, vo, 0); vec[3] = buf_load4(m3, vo, 0);
+      if constexpr (!kMulti) {
+        vec[0] = buf_load4(m0, vo, 0); vec[1] = buf_load4(m1, vo, 0);
+        vec[2] = buf_load4(m2, vo, 0); vec[3] = buf_load4(m3, vo, 0);
+      } else {
+#pragma unroll
+        for (int t = 0; t < kMaxIntervals; ++t) {
+          vec[2 * t] = buf_load4(m0, vo + t * vec_bytes, 0);
+          vec[2 * t + 1] = buf_load4(m1, vo + t * vec_bytes, 0);
+        }
+      }
     }
   };
   auto store_tile = [&](int e, int buf) {
@@ -481,7 +519,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
     if (part) {
       const int key = kb * BK + mk_key;
       const int r0 = qb * BQ + mk_wave * 32;
-      const uint32_t w = hidden_rows32((int)vec[0], (int)vec[1], (int)vec[2], (int)vec[3], r0);
+      uint32_t w;
+      if constexpr (!kMulti)
+        w = hidden_rows32((int)vec[0], (int)vec[1], (int)vec[2], (int)vec[3], r0);
+      else
+        w = hidden_rows32_multi(int4{(int)vec[0], (int)vec[2], (int)vec[4], (int)vec[6]},
+                                int4{(int)vec[1], (int)vec[3], (int)vec[5], (int)vec[7]}, r0);
       sm.mw[buf][mk_wave][mk_key] = key < N ? w : 0xFFFFFFFFu;
     }
   };
@@ -622,7 +665,10 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   q.scale = a.scale;
   const unsigned qgrid = (unsigned)a.B * (unsigned)a.nQB_q * (unsigned)a.Hq;
   if (ev.dq_start) (void)hipEventRecord(ev.dq_start, s);
-  if (qgrid > 0) hipLaunchKernelGGL(k_attn_bwd_dq, dim3(qgrid), dim3(256), 0, s, q);
+  const bool multi = a.m.n > 0;
+  if (qgrid > 0)
+    hipLaunchKernelGGL(multi ? k_attn_bwd_dq<true> : k_attn_bwd_dq<false>, dim3(qgrid),
+                       dim3(256), 0, s, q);
   if (ev.dq_stop) (void)hipEventRecord(ev.dq_stop, s);
 
   if (acc && rows_k > 0) {
@@ -652,7 +698,9 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   const unsigned grid = (unsigned)a.B * (unsigned)a.Hm * (unsigned)a.nKB_k * (unsigned)hm.kvpm *
                         (unsigned)hm.cpk;
   if (ev.dkdv_start) (void)hipEventRecord(ev.dkdv_start, s);
-  if (grid > 0) hipLaunchKernelGGL(k_attn_bwd_dkdv, dim3(grid), dim3(64 * dkdv::kWaves), 0, s, p);
+  if (grid > 0)
+    hipLaunchKernelGGL(multi ? k_attn_bwd_dkdv<true> : k_attn_bwd_dkdv<false>, dim3(grid),
+                       dim3(64 * dkdv::kWaves), 0, s, p);
   if (ev.dkdv_stop) (void)hipEventRecord(ev.dkdv_stop, s);
 
   if (acc && rows_k > 0) {

@@ -47,12 +47,67 @@ __global__ __launch_bounds__(64) void k_block_minmax(MaskPtrs m, int Nk, int nKB
   }
 }
 
-__device__ __forceinline__ void load_mm(const int32_t* __restrict__ mm, size_t idx, int* r) {
-  const int4* p = reinterpret_cast<const int4*>(mm + idx * 8);
-  int4 a = p[0], c = p[1];
-  r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
-  r[4] = c.x; r[5] = c.y; r[6] = c.z; r[7] = c.w;
+// Multi-interval form: one wave per (mask row, kb); for each interval m < n the min and
+// max of its starts and of its ends, written as [row][kb][4n].
+__global__ __launch_bounds__(64) void k_block_minmax_multi(const int32_t* __restrict__ start,
+                                                           const int32_t* __restrict__ end,
+                                                           int n, int Nk, int nKB, int bk,
+                                                           int32_t* __restrict__ mm) {
+  const int bkb = blockIdx.x;
+  const int b = bkb / nKB, kb = bkb - b * nKB;
+  const int lane = threadIdx.x;
+  const int c0 = kb * bk, c1 = min(c0 + bk, Nk);
+  int v[4 * kMaxIntervals];
+#pragma unroll
+  for (int m = 0; m < kMaxIntervals; ++m) {
+    v[4 * m] = INT_MAX; v[4 * m + 1] = INT_MIN; v[4 * m + 2] = INT_MAX; v[4 * m + 3] = INT_MIN;
+    if (m < n) {
+      const size_t rowoff = ((size_t)b * n + m) * Nk;
+      for (int c = c0 + lane; c < c1; c += 64) {
+        const int xs = start[rowoff + c], xe = end[rowoff + c];
+        v[4 * m] = min(v[4 * m], xs); v[4 * m + 1] = max(v[4 * m + 1], xs);
+        v[4 * m + 2] = min(v[4 * m + 2], xe); v[4 * m + 3] = max(v[4 * m + 3], xe);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+#pragma unroll
+    for (int t = 0; t < 4 * kMaxIntervals; t += 2) {
+      v[t] = min(v[t], __shfl_xor(v[t], off));
+      v[t + 1] = max(v[t + 1], __shfl_xor(v[t + 1], off));
+    }
+  }
+  if (lane < 4 * n) {
+    int out = v[0];
+#pragma unroll
+    for (int t = 1; t < 4 * kMaxIntervals; ++t) out = (lane == t) ? v[t] : out;
+    mm[(size_t)bkb * 4 * n + lane] = out;
+  }
 }
+
+// The block min/max of one KV block, and the tile rule of the mask form on it.
+template <bool kMulti>
+struct BlockBounds {
+  int v[kMulti ? 4 * kMaxIntervals : 8];
+  int n;
+  __device__ __forceinline__ void load(const int32_t* __restrict__ mm, size_t idx, int n_) {
+    n = n_;
+    if constexpr (!kMulti) {
+      const int4* p = reinterpret_cast<const int4*>(mm + idx * 8);
+      const int4 a = p[0], c = p[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4 * kMaxIntervals; ++t) v[t] = t < 4 * n ? mm[idx * 4 * n + t] : 0;
+    }
+  }
+  __device__ __forceinline__ int cls(int q0, int q1) const {
+    if constexpr (!kMulti) return tile_class(v, q0, q1);
+    else return tile_class_multi(v, n, q0, q1);
+  }
+};
 
 // Workgroup-wide ordered compaction helper: returns (exclusive offset of this
 // thread among flagged threads, total flagged, total of `sub` among flagged).
@@ -77,7 +132,8 @@ __device__ __forceinline__ ScanResult block_scan_256(bool flag, bool sub, int* s
 }
 
 // ---- A3: classes and per-Q-block queues (KV blocks right to left) --------------
-__global__ __launch_bounds__(256) void k_classify_q(const int32_t* __restrict__ mm, int Nq,
+template <bool kMulti>
+__global__ __launch_bounds__(256) void k_classify_q(const int32_t* __restrict__ mm, int n, int Nq,
                                                     int nQB, int nKB, int bq,
                                                     uint8_t* __restrict__ cls,
                                                     int32_t* __restrict__ q_queue,
@@ -95,9 +151,9 @@ __global__ __launch_bounds__(256) void k_classify_q(const int32_t* __restrict__ 
     const int kb = nKB - 1 - idx;
     int c = 0;
     if (valid) {
-      int v[8];
-      load_mm(mm, (size_t)b * nKB + kb, v);
-      c = tile_class(v, q0, q1);
+      BlockBounds<kMulti> bb;
+      bb.load(mm, (size_t)b * nKB + kb, n);
+      c = bb.cls(q0, q1);
       if (cls) cls[(size_t)row * nKB + kb] = (uint8_t)c;
     }
     ScanResult s = block_scan_256(valid && c != 0, c == 1, sh_cnt, sh_sub);
@@ -117,7 +173,8 @@ __global__ __launch_bounds__(256) void k_classify_q(const int32_t* __restrict__ 
 }
 
 // ---- A3 (backward direction): per-KV-block queues of Q-blocks, ascending -----------
-__global__ __launch_bounds__(256) void k_classify_k(const int32_t* __restrict__ mm, int Nq,
+template <bool kMulti>
+__global__ __launch_bounds__(256) void k_classify_k(const int32_t* __restrict__ mm, int n, int Nq,
                                                     int nQB, int nKB, int bq,
                                                     int32_t* __restrict__ k_queue,
                                                     int32_t* __restrict__ k_count,
@@ -125,14 +182,14 @@ __global__ __launch_bounds__(256) void k_classify_k(const int32_t* __restrict__ 
   __shared__ int sh_cnt[4], sh_sub[4];
   const int row = blockIdx.x;  // b * nKB + kb
   const int tid = threadIdx.x;
-  int v[8];
-  load_mm(mm, (size_t)row, v);
+  BlockBounds<kMulti> bb;
+  bb.load(mm, (size_t)row, n);
   int base = 0, np = 0;
   for (int c0 = 0; c0 < nQB; c0 += 256) {
     const int qb = c0 + tid;
     const bool valid = qb < nQB;
     int c = 0;
-    if (valid) c = tile_class(v, qb * bq, min(qb * bq + bq, Nq));
+    if (valid) c = bb.cls(qb * bq, min(qb * bq + bq, Nq));
     ScanResult s = block_scan_256(valid && c != 0, c == 1, sh_cnt, sh_sub);
     if (valid && c != 0)
       k_queue[(size_t)row * nQB + base + s.off] = qb | (c == 1 ? (int)0x80000000 : 0);
@@ -178,15 +235,30 @@ __global__ __launch_bounds__(1024) void k_lpt_sort(const int32_t* __restrict__ c
 }
 
 // ---- Dense expansion through the kernels' own predicate (checking only) ----------
-__global__ __launch_bounds__(256) void k_expand_mask(MaskPtrs m, int b, int Nk, int row0,
+__global__ __launch_bounds__(256) void k_expand_mask(MaskArgs m, int b, int Nk, int row0,
                                                      int row1, uint8_t* __restrict__ dense) {
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= Nk) return;
-  const size_t o = (size_t)b * Nk + j;
-  const int lts = m.lts[o], lte = m.lte[o], uts = m.uts[o], ute = m.ute[o];
+  int lts = 0, lte = 0, uts = 0, ute = 0;
+  int sv[kMaxIntervals] = {0, 0, 0, 0}, ev[kMaxIntervals] = {0, 0, 0, 0};
+  if (m.n == 0) {
+    const size_t o = (size_t)b * Nk + j;
+    lts = m.v.lts[o]; lte = m.v.lte[o]; uts = m.v.uts[o]; ute = m.v.ute[o];
+  } else {
+    const size_t o = (size_t)b * m.n * Nk + j;
+#pragma unroll
+    for (int t = 0; t < kMaxIntervals; ++t) {
+      if (t < m.n) {
+        sv[t] = m.start[o + (size_t)t * Nk];
+        ev[t] = m.end[o + (size_t)t * Nk];
+      }
+    }
+  }
+  const int4 s = {sv[0], sv[1], sv[2], sv[3]}, e = {ev[0], ev[1], ev[2], ev[3]};
   for (int w = blockIdx.y; row0 + 32 * w < row1; w += gridDim.y) {
     const int r0 = row0 + 32 * w;
-    const uint32_t word = hidden_rows32(lts, lte, uts, ute, r0);
+    const uint32_t word = m.n == 0 ? hidden_rows32(lts, lte, uts, ute, r0)
+                                   : hidden_rows32_multi(s, e, r0);
     const int nr = min(32, row1 - r0);
     for (int r = 0; r < nr; ++r)
       dense[(size_t)(r0 - row0 + r) * Nk + j] = (uint8_t)((word >> r) & 1u);
@@ -194,20 +266,28 @@ __global__ __launch_bounds__(256) void k_expand_mask(MaskPtrs m, int b, int Nk, 
 }
 
 // ---- host launchers --------------------------------------------------------------
-hipError_t launch_classify(const MaskPtrs& m, int B, int Nq, int Nk, int bq, int bk,
+hipError_t launch_classify(const MaskArgs& m, int B, int Nq, int Nk, int bq, int bk,
                            const TileOut& out, hipStream_t s) {
   const int nQB = (Nq + bq - 1) / bq, nKB = (Nk + bk - 1) / bk;
   if (B == 0) return hipSuccess;
-  if (nKB > 0)
-    hipLaunchKernelGGL(k_block_minmax, dim3(B * nKB), dim3(64), 0, s, m, Nk, nKB, bk,
-                       out.minmax);
+  const bool multi = m.n > 0;
+  if (nKB > 0) {
+    if (multi)
+      hipLaunchKernelGGL(k_block_minmax_multi, dim3(B * nKB), dim3(64), 0, s, m.start, m.end,
+                         m.n, Nk, nKB, bk, out.minmax);
+    else
+      hipLaunchKernelGGL(k_block_minmax, dim3(B * nKB), dim3(64), 0, s, m.v, Nk, nKB, bk,
+                         out.minmax);
+  }
   // with no KV block a Q-block's queue is empty; with no Q-block a KV block's is
   if ((out.tile_class || out.q_queue) && nQB > 0)
-    hipLaunchKernelGGL(k_classify_q, dim3(B * nQB), dim3(256), 0, s, out.minmax, Nq, nQB, nKB,
-                       bq, out.tile_class, out.q_queue, out.q_count, out.q_cost);
+    hipLaunchKernelGGL(multi ? k_classify_q<true> : k_classify_q<false>, dim3(B * nQB),
+                       dim3(256), 0, s, out.minmax, m.n, Nq, nQB, nKB, bq, out.tile_class,
+                       out.q_queue, out.q_count, out.q_cost);
   if (out.k_queue && nKB > 0)
-    hipLaunchKernelGGL(k_classify_k, dim3(B * nKB), dim3(256), 0, s, out.minmax, Nq, nQB, nKB,
-                       bq, out.k_queue, out.k_count, out.k_cost);
+    hipLaunchKernelGGL(multi ? k_classify_k<true> : k_classify_k<false>, dim3(B * nKB),
+                       dim3(256), 0, s, out.minmax, m.n, Nq, nQB, nKB, bq, out.k_queue,
+                       out.k_count, out.k_cost);
   return hipGetLastError();
 }
 
@@ -217,7 +297,7 @@ hipError_t launch_lpt_sort(const int32_t* cost, int32_t* order, int count, hipSt
   return hipGetLastError();
 }
 
-hipError_t launch_expand_mask(const MaskPtrs& m, int b, int Nk, int row0, int row1,
+hipError_t launch_expand_mask(const MaskArgs& m, int b, int Nk, int row0, int row1,
                               uint8_t* dense, hipStream_t s) {
   if (Nk == 0 || row1 <= row0) return hipSuccess;
   const int windows = (row1 - row0 + 31) / 32;
@@ -229,7 +309,9 @@ hipError_t launch_expand_mask(const MaskPtrs& m, int b, int Nk, int row0, int ro
 // ---- Mask localization for one context-parallel rank (FlashMask-3 page, §3.2) ----
 // x_local = sum_i clamp(x - offsets[i], 0, C): the rank's rows before global row x.  The
 // chunk offsets are staged once per workgroup in LDS.
-__global__ __launch_bounds__(256) void k_localize(MaskPtrs g, const int32_t* __restrict__ offsets,
+// `four` selects the four arrays of the four-vector form, else the first two (start, end).
+__global__ __launch_bounds__(256) void k_localize(MaskPtrs g, int four,
+                                                  const int32_t* __restrict__ offsets,
                                                   int n_chunks, int C, MaskOut out,
                                                   int64_t cols) {
   __shared__ int32_t offs[4096];
@@ -237,7 +319,8 @@ __global__ __launch_bounds__(256) void k_localize(MaskPtrs g, const int32_t* __r
   __syncthreads();
   for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < cols;
        c += (int64_t)gridDim.x * 256) {
-    const int x0 = g.lts[c], x1 = g.lte[c], x2 = g.uts[c], x3 = g.ute[c];
+    const int x0 = g.lts[c], x1 = g.lte[c];
+    const int x2 = four ? g.uts[c] : 0, x3 = four ? g.ute[c] : 0;
     int y0 = 0, y1 = 0, y2 = 0, y3 = 0;
     for (int i = 0; i < n_chunks; ++i) {
       const int o = offs[i];
@@ -248,18 +331,20 @@ __global__ __launch_bounds__(256) void k_localize(MaskPtrs g, const int32_t* __r
     }
     out.lts[c] = y0;
     out.lte[c] = y1;
-    out.uts[c] = y2;
-    out.ute[c] = y3;
+    if (four) {
+      out.uts[c] = y2;
+      out.ute[c] = y3;
+    }
   }
 }
 
-hipError_t launch_localize(const MaskPtrs& g, const int32_t* offsets, int n_chunks, int chunk_len,
-                           const MaskOut& out, int64_t cols, hipStream_t s) {
+hipError_t launch_localize(const MaskPtrs& g, int arrays, const int32_t* offsets, int n_chunks,
+                           int chunk_len, const MaskOut& out, int64_t cols, hipStream_t s) {
   if (cols <= 0) return hipSuccess;
   const int64_t blocks = (cols + 255) / 256;
   const unsigned grid = (unsigned)(blocks < 2048 ? blocks : 2048);
-  hipLaunchKernelGGL(k_localize, dim3(grid), dim3(256), 0, s, g, offsets, n_chunks, chunk_len,
-                     out, cols);
+  hipLaunchKernelGGL(k_localize, dim3(grid), dim3(256), 0, s, g, arrays == 4 ? 1 : 0, offsets,
+                     n_chunks, chunk_len, out, cols);
   return hipGetLastError();
 }
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fm_internal.h"
+
 namespace fm {
 
 typedef __bf16 bf16;
@@ -40,6 +42,14 @@ __device__ __forceinline__ uint32_t hidden_rows32(int lts, int lte, int uts, int
   return range_bits32(lts, lte, r0) | range_bits32(uts, ute, r0);
 }
 
+// Multi-interval form (FlashMask Guide, "Multi-Interval Sparse Masks"): key column j is
+// visible to row i iff start_m <= i < end_m for one of its (up to four) intervals; a row
+// is hidden when no interval holds it.  Absent intervals are passed as [0, 0).
+__device__ __forceinline__ uint32_t hidden_rows32_multi(int4 s, int4 e, int r0) {
+  return ~(range_bits32(s.x, e.x, r0) | range_bits32(s.y, e.y, r0) |
+           range_bits32(s.z, e.z, r0) | range_bits32(s.w, e.w, r0));
+}
+
 // ---------------------------------------------------------------------------
 // Tile classification rule (FlashMask-3 page, §3.1, generalized to both row
 // intervals).  mm = {minLTS, maxLTS, minLTE, maxLTE, minUTS, maxUTS, minUTE, maxUTE}
@@ -48,6 +58,22 @@ __device__ __forceinline__ uint32_t hidden_rows32(int lts, int lte, int uts, int
 __device__ __forceinline__ int tile_class(const int* mm, int q0, int q1) {
   bool skip = (q0 >= mm[1] && q1 <= mm[2]) || (q0 >= mm[5] && q1 <= mm[6]);
   bool unm = (q1 <= mm[0] || q0 >= mm[3]) && (q1 <= mm[4] || q0 >= mm[7]);
+  return skip ? 0 : (unm ? 2 : 1);
+}
+
+// The rule for n visible intervals per column, mm = {min start, max start, min end, max
+// end} of each interval over the KV block's columns: skipped when every interval lies
+// outside rows [q0, q1) in every column, unmasked when one interval holds them in every
+// column.
+__device__ __forceinline__ int tile_class_multi(const int* mm, int n, int q0, int q1) {
+  bool skip = true, unm = false;
+#pragma unroll
+  for (int m = 0; m < kMaxIntervals; ++m) {
+    if (m < n) {
+      skip = skip && (q1 <= mm[4 * m] || q0 >= mm[4 * m + 3]);
+      unm = unm || (q0 >= mm[4 * m + 1] && q1 <= mm[4 * m + 2]);
+    }
+  }
   return skip ? 0 : (unm ? 2 : 1);
 }
 

@@ -58,7 +58,7 @@ struct FwdParams {
   const bf16* __restrict__ q;
   const bf16* __restrict__ k;
   const bf16* __restrict__ v;
-  MaskPtrs m;
+  MaskArgs m;
   bf16* __restrict__ o;
   float* __restrict__ lse;
   const int32_t* __restrict__ q_queue;
@@ -68,6 +68,8 @@ struct FwdParams {
   float c;  // softmax scale * log2(e)
 };
 
+// kMulti: the mask is the multi-interval form (else the four-vector form).
+template <bool kMulti>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   __shared__ FwdSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -90,9 +92,19 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   const rsrc_t kr_ = make_rsrc(p.k + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
   const rsrc_t vr_ = make_rsrc(p.v + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
   const uint32_t vec_bytes = (uint32_t)N * 4;
-  const size_t mrow = (size_t)mr * N;
-  const rsrc_t m0 = make_rsrc(p.m.lts + mrow, vec_bytes), m1 = make_rsrc(p.m.lte + mrow, vec_bytes);
-  const rsrc_t m2 = make_rsrc(p.m.uts + mrow, vec_bytes), m3 = make_rsrc(p.m.ute + mrow, vec_bytes);
+  // mask row mr: four vectors of N, or n intervals x N starts and ends (absent intervals
+  // m >= n read past the row's bounds and load 0, the empty interval [0, 0))
+  rsrc_t m0, m1, m2, m3;
+  if constexpr (!kMulti) {
+    const size_t mrow = (size_t)mr * N;
+    m0 = make_rsrc(p.m.v.lts + mrow, vec_bytes); m1 = make_rsrc(p.m.v.lte + mrow, vec_bytes);
+    m2 = make_rsrc(p.m.v.uts + mrow, vec_bytes); m3 = make_rsrc(p.m.v.ute + mrow, vec_bytes);
+  } else {
+    const size_t mrow = (size_t)mr * p.m.n * N;
+    m0 = make_rsrc(p.m.start + mrow, (uint32_t)p.m.n * vec_bytes);
+    m1 = make_rsrc(p.m.end + mrow, (uint32_t)p.m.n * vec_bytes);
+    m2 = m0; m3 = m1;
+  }
   const bool ragged = (N % BK) != 0;
 
   const int row = qb * BQ + wave * 32 + l32;
@@ -114,7 +126,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   const int cp_row = tid >> 4, cp_ch = (tid & 15) * 8;
   const int mk_key = lane, mk_wave = __builtin_amdgcn_readfirstlane(wave);
   u32x4 kst[4], vst[4];
-  uint32_t vec[4];
+  uint32_t vec[kMulti ? 2 * kMaxIntervals : 4];
   auto is_partial = [&](int e) {
     return (e < 0) || (ragged && (e & 0x7fffffff) == p.nKB - 1);
   };
@@ -131,8 +143,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     for (int i = 0; i < 4; ++i) kst[i] = buf_load16(kr_, base, i * 16 * D * 2);
     if (is_partial(e)) {
       const uint32_t vo = (uint32_t)(kb * BK + mk_key) * 4;
-      vec[0] = buf_load4(m0, vo, 0); vec[1] = buf_load4(m1, vo, 0);
-      vec[2] = buf_load4(m2, vo, 0); vec[3] = buf_load4(m3, vo, 0);
+      if constexpr (!kMulti) {
+        vec[0] = buf_load4(m0, vo, 0); vec[1] = buf_load4(m1, vo, 0);
+        vec[2] = buf_load4(m2, vo, 0); vec[3] = buf_load4(m3, vo, 0);
+      } else {
+#pragma unroll
+        for (int t = 0; t < kMaxIntervals; ++t) {
+          vec[2 * t] = buf_load4(m0, vo + t * vec_bytes, 0);
+          vec[2 * t + 1] = buf_load4(m1, vo + t * vec_bytes, 0);
+        }
+      }
     }
   };
   auto fetch_v = [&](int e) {
@@ -148,7 +168,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     if (is_partial(e)) {
       const int key = (e & 0x7fffffff) * BK + mk_key;
       const int r0 = qb * BQ + mk_wave * 32;
-      const uint32_t w = hidden_rows32((int)vec[0], (int)vec[1], (int)vec[2], (int)vec[3], r0);
+      uint32_t w;
+      if constexpr (!kMulti)
+        w = hidden_rows32((int)vec[0], (int)vec[1], (int)vec[2], (int)vec[3], r0);
+      else
+        w = hidden_rows32_multi(int4{(int)vec[0], (int)vec[2], (int)vec[4], (int)vec[6]},
+                                int4{(int)vec[1], (int)vec[3], (int)vec[5], (int)vec[7]}, r0);
       sm.mw[buf][mk_wave][mk_key] = key < N ? w : 0xFFFFFFFFu;
     }
   };
@@ -368,7 +393,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_
   p.c = a.scale * kLog2e;
   const unsigned grid = (unsigned)a.B * (unsigned)a.nQB * (unsigned)a.Hq;
   if (ev0) (void)hipEventRecord(ev0, s);
-  if (grid > 0) hipLaunchKernelGGL(k_attn_fwd, dim3(grid), dim3(256), 0, s, p);
+  if (grid > 0)
+    hipLaunchKernelGGL(a.m.n > 0 ? k_attn_fwd<true> : k_attn_fwd<false>, dim3(grid), dim3(256),
+                       0, s, p);
   hipError_t e = hipGetLastError();
   if (ev1) (void)hipEventRecord(ev1, s);
   return e;

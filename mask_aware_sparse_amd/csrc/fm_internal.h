@@ -65,9 +65,24 @@ struct MaskPtrs {
   const int32_t* ute;
 };
 
+// The mask as the kernels take it: the four-vector form (n == 0; rows of Nk per vector) or
+// the multi-interval form (n = 1..4 visible intervals per column; start/end [rows][n][Nk]).
+constexpr int kMaxIntervals = 4;
+struct MaskArgs {
+  MaskPtrs v;
+  const int32_t* start;
+  const int32_t* end;
+  int n;
+};
+// int32 values per KV block in the block min/max array: 8 (min, max of each of the four
+// vectors) or 4 n (min start, max start, min end, max end of each interval).  Workspaces
+// reserve the largest.
+inline int minmax_width(int n) { return n == 0 ? 8 : 4 * n; }
+constexpr int kMaxMinmaxWidth = 4 * kMaxIntervals;
+
 // Classification outputs (B here counts mask rows); any of the optional outputs may be null.
 struct TileOut {
-  int32_t* minmax;       // [B][nKB][8]                (required)
+  int32_t* minmax;       // [B][nKB][minmax_width(n)]  (required)
   uint8_t* tile_class;   // [B][nQB][nKB]              (optional)
   int32_t* q_queue;      // [B][nQB][nKB]              (optional)
   int32_t* q_count;      // [B][nQB][2]                (required if q_queue)
@@ -77,11 +92,11 @@ struct TileOut {
   int32_t* k_cost;       // [B*nKB]                    (required if k_queue)
 };
 
-// Nq query rows (Q-blocks of bq), Nk keys (KV blocks of bk); vectors are [B][Nk].
-hipError_t launch_classify(const MaskPtrs& m, int B, int Nq, int Nk, int bq, int bk,
+// Nq query rows (Q-blocks of bq), Nk keys (KV blocks of bk); B mask rows.
+hipError_t launch_classify(const MaskArgs& m, int B, int Nq, int Nk, int bq, int bk,
                            const TileOut& out, hipStream_t s);
 hipError_t launch_lpt_sort(const int32_t* cost, int32_t* order, int count, hipStream_t s);
-hipError_t launch_expand_mask(const MaskPtrs& m, int b, int Nk, int row0, int row1,
+hipError_t launch_expand_mask(const MaskArgs& m, int b, int Nk, int row0, int row1,
                               uint8_t* dense, hipStream_t s);
 
 struct MaskOut {
@@ -90,15 +105,16 @@ struct MaskOut {
   int32_t* uts;
   int32_t* ute;
 };
-// Renumber every bound of `cols` = B * Nk columns into the rank's rows.
-hipError_t launch_localize(const MaskPtrs& g, const int32_t* offsets, int n_chunks, int chunk_len,
-                           const MaskOut& out, int64_t cols, hipStream_t s);
+// Renumber `cols` row bounds of each of the first `arrays` (2 or 4) arrays of g into the
+// rank's rows.
+hipError_t launch_localize(const MaskPtrs& g, int arrays, const int32_t* offsets, int n_chunks,
+                           int chunk_len, const MaskOut& out, int64_t cols, hipStream_t s);
 
 struct FwdArgs {
   const void* q;
   const void* k;
   const void* v;
-  MaskPtrs m;
+  MaskArgs m;
   void* o;
   float* lse;
   const int32_t* q_queue;
@@ -116,7 +132,7 @@ struct BwdArgs {
   const void* o;
   const float* lse;
   const void* dout;
-  MaskPtrs m;
+  MaskArgs m;
   void* dq;
   void* dk;
   void* dv;

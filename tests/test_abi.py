@@ -72,11 +72,12 @@ def test_tile_shapes():
 
 
 def test_workspace_sizes():
-    # forward: minmax + queue + counts + cost + order, each 256-byte aligned
+    # forward: minmax (16 int32 per block: room for 4 intervals) + queue + counts + cost +
+    # order, each 256-byte aligned
     B, N = 2, 1000
     nqb, nkb = 8, 16
     al = lambda x: (x + 255) // 256 * 256
-    want = al(B * nkb * 32) + al(B * nqb * nkb * 4) + al(B * nqb * 8) + 2 * al(B * nqb * 4)
+    want = al(B * nkb * 64) + al(B * nqb * nkb * 4) + al(B * nqb * 8) + 2 * al(B * nqb * 4)
     assert fm.workspace_size(B, 4, 2, N, fm.OP_FWD) == want
     assert fm.workspace_size(B, 4, 2, N, fm.OP_CLASSIFY, 64, 32) == al(B * 16 * 4) + al(B * 32 * 4)
     # backward: fp32 dK/dV accumulators exist only for query-head groups above 4 heads
@@ -179,7 +180,7 @@ def test_query_share_workspace_sizes():
     # forward tiles: nQB = N_q / 128 Q-blocks by nKB = N_k / 64 KV blocks
     al = lambda x: (x + 255) // 256 * 256
     nqb, nkb = 2, 16
-    want = al(nkb * 32) + al(nqb * nkb * 4) + al(nqb * 8) + 2 * al(nqb * 4)
+    want = al(nkb * 64) + al(nqb * nkb * 4) + al(nqb * 8) + 2 * al(nqb * 4)
     assert fm.workspace_size(1, 4, 2, 256, fm.OP_FWD, seqlen_kv=1024) == want
     square = fm.workspace_size(1, 4, 2, 256, fm.OP_BWD)
     assert fm.workspace_size(1, 4, 2, 256, fm.OP_BWD, seqlen_kv=1024) > square
@@ -235,15 +236,15 @@ def test_mask_heads_workspace_sizes():
     B, N, Hm = 2, 1000, 4
     R = B * Hm                                   # tile structures per mask row
     nqb, nkb = 8, 16
-    want = al(R * nkb * 32) + al(R * nqb * nkb * 4) + al(R * nqb * 8) + 2 * al(R * nqb * 4)
+    want = al(R * nkb * 64) + al(R * nqb * nkb * 4) + al(R * nqb * 8) + 2 * al(R * nqb * 4)
     assert fm.workspace_size(B, 8, 4, N, fm.OP_FWD, mask_heads=Hm) == want
     # dK/dV accumulators appear when sets split a kv head's group (two writers per block):
     # 8 query heads, 4 kv heads (groups of 2), 8 sets -> accumulators; 4 sets -> none
     al_acc = 2 * al(B * 4 * N * 128 * 4)
     split = fm.workspace_size(B, 8, 4, N, fm.OP_BWD, mask_heads=8)
     whole = fm.workspace_size(B, 8, 4, N, fm.OP_BWD, mask_heads=4)
-    tiles_k = al(B * 4 * 8 * 32) + al(B * 4 * 8 * 32 * 4) + al(B * 4 * 8 * 8) + 2 * al(B * 4 * 8 * 4)
-    tiles_q = al(B * 4 * nkb * 32) + al(B * 4 * nqb * nkb * 4) + al(B * 4 * nqb * 8) + \
+    tiles_k = al(B * 4 * 8 * 64) + al(B * 4 * 8 * 32 * 4) + al(B * 4 * 8 * 8) + 2 * al(B * 4 * 8 * 4)
+    tiles_q = al(B * 4 * nkb * 64) + al(B * 4 * nqb * nkb * 4) + al(B * 4 * nqb * 8) + \
         2 * al(B * 4 * nqb * 4)
     assert split - whole == al_acc + tiles_k + tiles_q    # 8 sets: twice the tile rows
 
@@ -257,3 +258,55 @@ def test_mask_heads_sort_limit():
     big = prob_hm(64, 8, 64, N=8192 + 64)
     assert fm.library().fm_workspace_size(ctypes.byref(big), fm.OP_FWD, 0, 0,
                                           ctypes.byref(n)) == UNSUPPORTED
+
+
+# ---- multi-interval masks (fm_mask_multi) --------------------------------------------
+
+def fwd_multi(p, m, ws_bytes=1 << 40):
+    return fm.library().fm_attn_fwd_multi(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(m),
+                                          FAKE, FAKE, FAKE, ctypes.c_size_t(ws_bytes), None, None)
+
+
+def bwd_multi(p, m, ws_bytes=1 << 40):
+    return fm.library().fm_attn_bwd_multi(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          ctypes.byref(m), FAKE, FAKE, FAKE, FAKE,
+                                          ctypes.c_size_t(ws_bytes), None, None)
+
+
+@pytest.mark.parametrize("n", [0, 5, -1])
+def test_multi_interval_count_checked(n):
+    m = fm.MaskMulti(0x100000, 0x100000, n)
+    assert fwd_multi(prob(), m) == INVALID
+    assert bwd_multi(prob(), m) == INVALID
+    t = fm.Tiles(*([0x100000] * 8))
+    assert fm.library().fm_classify_tiles_multi(ctypes.byref(prob()), ctypes.byref(m), 64, 64,
+                                                ctypes.byref(t), FAKE, ctypes.c_size_t(1 << 30),
+                                                None) == INVALID
+    assert fm.library().fm_localize_mask_multi(ctypes.byref(prob()), ctypes.byref(m), FAKE, 1, 8,
+                                               FAKE, FAKE, None) == INVALID
+
+
+def test_multi_null_pointers_and_workspace():
+    assert fwd_multi(prob(), fm.MaskMulti(0, 0x100000, 2)) == INVALID
+    assert bwd_multi(prob(), fm.MaskMulti(0x100000, 0, 2)) == INVALID
+    m = fm.MaskMulti(0x100000, 0x100000, 4)
+    need = fm.workspace_size(1, 4, 2, 256, fm.OP_FWD)
+    assert fwd_multi(prob(), m, ws_bytes=need - 1) == WORKSPACE
+    need = fm.workspace_size(1, 4, 2, 256, fm.OP_BWD)
+    assert bwd_multi(prob(), m, ws_bytes=need - 1) == WORKSPACE
+    # empty problems are no-ops for the multi form too
+    assert fwd_multi(prob(B=0), m, ws_bytes=0) == FM_OK
+    assert bwd_multi(prob(N=0), m, ws_bytes=0) == FM_OK
+
+
+def test_multi_localize_argument_checks():
+    lib = fm.library()
+    p = prob_kv(B=2, Nq=0, Nk=100)
+    m = fm.MaskMulti(0x100000, 0x100000, 3)
+    call = lambda n, c, offs=FAKE, ls=FAKE, le=FAKE: lib.fm_localize_mask_multi(
+        ctypes.byref(p), ctypes.byref(m), offs, n, c, ls, le, None)
+    assert call(0, 8) == INVALID
+    assert call(1, 0) == INVALID
+    assert call(1, 8, offs=None) == INVALID
+    assert call(1, 8, ls=None) == INVALID
+    assert call(4097, 8) == UNSUPPORTED

@@ -1,0 +1,40 @@
+"""Host logic of bench.py (CPU only): the attended-pair counts behind the effective
+TFLOP/s metric, by interval arithmetic, against dense counts from the oracle's mask."""
+import numpy as np
+import pytest
+
+import bench
+import oracle
+import workloads
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_attended_pairs_four_vector_form(seed):
+    w = workloads.random_intervals(seed, 120, batch=2, heads_q=3)
+    dense = sum(int((~oracle.dense_mask(*(x[b] for x in w.vectors()))).sum()) for b in range(2))
+    assert bench.attended_pairs(w) == 3 * dense
+
+
+def test_attended_pairs_per_head_sets():
+    w = workloads.random_intervals(4, 96, batch=2, heads_q=4, mask_heads=2)
+    dense = sum(int((~oracle.dense_mask(*(x[b, m] for x in w.vectors()))).sum())
+                for b in range(2) for m in range(2))
+    assert bench.attended_pairs(w) == 2 * dense     # two query heads per set
+
+
+@pytest.mark.parametrize("M,hm", [(1, 0), (3, 0), (4, 2)])
+def test_attended_pairs_multi_interval(M, hm):
+    w = workloads.random_multi_intervals(M, 110, batch=2, heads_q=4, n_intervals=M,
+                                         mask_heads=hm)
+    sets = [(w.starts[b], w.ends[b]) for b in range(2)] if hm == 0 else \
+        [(w.starts[b, m], w.ends[b, m]) for b in range(2) for m in range(hm)]
+    dense = sum(int((~oracle.dense_mask_multi(s, e)).sum()) for s, e in sets)
+    assert bench.attended_pairs_multi(w) == dense * (4 // max(hm, 1))
+
+
+def test_benchmark_workloads_pair_counts_are_positive():
+    for name in workloads.CONFIG_NAMES[:2] + workloads.VARIANT_NAMES:
+        w = workloads.make_workload(name)
+        multi = isinstance(w, workloads.MultiWorkload)
+        a = bench.attended_pairs_multi(w) if multi else bench.attended_pairs(w)
+        assert 0 < a <= w.batch * w.heads_q * w.seqlen ** 2
