@@ -114,8 +114,11 @@ FwdWs fwd_ws(const fm_problem* p, const Blocks& nb) {
 struct BwdWs {
   size_t mm_k, k_queue, k_count, k_cost, k_order;   // dK/dV tiles
   size_t mm_q, q_queue, q_count, q_cost, q_order;   // dQ (forward) tiles
-  size_t lse2, delta, dk, dv, total;
-  bool acc;  // fp32 dK/dV accumulators present
+  size_t lse2, delta, dk, dv;
+  size_t unit_pair, unit_slot, split_pair, split_slot, split_counts, partials;  // split plan
+  size_t total;
+  bool acc;   // fp32 dK/dV accumulators present
+  int extra;  // extra pair units of the split plan
 };
 BwdWs bwd_ws(const fm_problem* p, const Blocks& nk, const Blocks& nq) {
   BwdWs w{};
@@ -138,10 +141,24 @@ BwdWs bwd_ws(const fm_problem* p, const Blocks& nk, const Blocks& nq) {
   // fp32 dK/dV accumulators only when several workgroups write one kv head's KV block
   // (query-head groups larger than one head chunk, or split by per-head mask sets);
   // otherwise the kernel stores bf16 directly
-  w.acc = fm::head_map(p->heads_q, p->heads_kv, hm_of(p)).writers > 1;
+  const fm::HeadMap hm = fm::head_map(p->heads_q, p->heads_kv, hm_of(p));
+  w.acc = hm.writers > 1;
   if (w.acc) {
     w.dk = off; off += align_up(rk * fm::kHeadDim * 4);
     w.dv = off; off += align_up(rk * fm::kHeadDim * 4);
+  }
+  // split plan of the dK/dV work units; partial sums only where bf16 is stored directly
+  const int64_t pairs = (int64_t)B * nk.nKB;
+  const int per = hm.kvpm * hm.cpk;
+  w.extra = fm::split_extra_pairs(per, pairs);
+  w.unit_pair = off; off += align_up((size_t)(pairs + w.extra) * 4);
+  w.unit_slot = off; off += align_up((size_t)(pairs + w.extra) * 4);
+  w.split_pair = off; off += align_up((size_t)w.extra * 4);
+  w.split_slot = off; off += align_up((size_t)w.extra * 4);
+  w.split_counts = off; off += align_up(2 * 4);
+  if (!w.acc) {
+    w.partials = off;
+    off += align_up((size_t)2 * fm::split_slots(per, w.extra) * fm::kBwdBlockK * fm::kHeadDim * 4);
   }
   w.total = off;
   return w;
@@ -172,7 +189,8 @@ fm_status check_ws(void* ws, size_t have, size_t need) {
 fm_status check_grid(const fm_problem* p, const Blocks& fwd, const Blocks& bwd) {
   const fm::HeadMap hm = fm::head_map(p->heads_q, p->heads_kv, hm_of(p));
   if ((int64_t)p->batch * fwd.nQB * p->heads_q >= INT32_MAX) return FM_ERR_UNSUPPORTED;
-  if (mask_rows(p) * bwd.nKB * hm.kvpm * hm.cpk >= INT32_MAX) return FM_ERR_UNSUPPORTED;
+  if ((mask_rows(p) * bwd.nKB + fm::kSplitExtraUnits) * hm.kvpm * hm.cpk >= INT32_MAX)
+    return FM_ERR_UNSUPPORTED;
   return FM_OK;
 }
 
@@ -360,6 +378,13 @@ fm_status bwd_impl(const fm_problem* p, const void* q, const void* k, const void
     a.q_queue = tq.q_queue; a.q_count = tq.q_count; a.q_order = q_order;
     a.lse2 = at<float>(ws, w.lse2); a.delta = at<float>(ws, w.delta);
     if (w.acc) { a.dk_acc = at<float>(ws, w.dk); a.dv_acc = at<float>(ws, w.dv); }
+    a.unit_pair = at<int32_t>(ws, w.unit_pair);
+    a.unit_slot = at<int32_t>(ws, w.unit_slot);
+    a.split_pair = at<int32_t>(ws, w.split_pair);
+    a.split_slot = at<int32_t>(ws, w.split_slot);
+    a.split_counts = at<int32_t>(ws, w.split_counts);
+    a.partials = w.acc ? nullptr : at<float>(ws, w.partials);
+    a.split_extra = w.extra;
     a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.Hm = hm_of(p);
     a.Nq = nq_of(p); a.Nk = nk_of(p);
     a.nQB_k = (int)nk.nQB; a.nKB_k = (int)nk.nKB;

@@ -26,6 +26,13 @@
 //                    owns its dK/dV rows and stores them as bf16; with several (GQA/MQA
 //                    groups above 4 heads) it adds them to fp32 accumulators, which
 //                    k_zero clears before and k_bwd_convert turns into bf16 after.
+//   k_plan_split     one workgroup: the dK/dV work units.  A (mask row, KV block) pair
+//                    whose queue is long against the average load of a workgroup slot is
+//                    cut into segments of its queue (the sink keys of a window mask are
+//                    seen by every row, so their block would otherwise be one serial chain
+//                    longer than the rest of the launch).  Segments of a pair that would
+//                    store bf16 directly write fp32 partial sums instead, and
+//   k_dkdv_reduce    adds them in segment order (deterministic) and stores bf16.
 #include "fm_device.h"
 #include "fm_internal.h"
 
@@ -105,9 +112,174 @@ struct DkdvParams {
   bf16* __restrict__ dv;
   int B, Hq, Hkv, Nq, Nk, nQB, nKB;  // Nq query rows, Nk keys
   HeadMap hm;                        // mask sets, chunking and writers per KV block
+  const int32_t* __restrict__ unit_pair;     // work units (split plan)
+  const int32_t* __restrict__ unit_slot;
+  const int32_t* __restrict__ split_counts;  // {units, split pairs}
+  float* __restrict__ partials;              // [2][nslots][BK][D] fp32 (dK then dV)
+  int nslots;
   float c;      // scale * log2(e)
   float scale;  // softmax scale (applied to dK)
 };
+
+// The query heads and kv head of one dK/dV workgroup: pair (mask row, KV block) `item`,
+// then the rem-th (kv head of the set, head chunk) of that pair.
+struct DkdvItem {
+  int mr, kb, b, kvh, h0, nh;
+};
+__device__ __forceinline__ DkdvItem dkdv_item(const HeadMap& hm, int Hq, int Hkv, int nKB,
+                                              int item, int rem) {
+  DkdvItem it;
+  const int kvl = rem / hm.cpk, ch = rem - kvl * hm.cpk;
+  it.mr = item / nKB;
+  it.kb = item - it.mr * nKB;
+  it.b = it.mr / hm.Hm;
+  const int g = Hq / Hkv;
+  const int hq0 = (it.mr - it.b * hm.Hm) * hm.qpm;  // first query head of the set
+  it.kvh = hq0 / g + kvl;
+  const int hs = max(it.kvh * g, hq0);             // first query head of (kv head, set)
+  it.h0 = hs + ch * hm.hc;
+  it.nh = min(hm.hc, hs + hm.gq - it.h0);
+  return it;
+}
+
+// ---- Split plan of the dK/dV work units (one workgroup of kPlanThreads) ---------------
+// Pairs r = 0 .. npairs-1 in LPT order.  Each of a pair's `per` workgroups walks
+// u_r = (queue length) x hc tile steps, and the average load of a workgroup slot is
+// L = per * sum_r u_r / slots.  A pair with u_r > L / 2 is cut into
+// s_r = min(kSplitMaxSegs, ceil(2 u_r / L), queue length, u_r / kSplitMinSteps) segments,
+// the extra segments granted in pair order while they fit in `extra`.  Unit table, pairs in
+// LPT order and the segments of a pair consecutive:
+//   unit_pair[u] = r | seg << 16 | s_r << 24;  unit_slot[u] = first partial slot of the
+//   segment (its `per` workgroups use slot + rem) or -1 when unsplit or with_slots == 0;
+//   split_pair[j] = r | s_r << 24, split_slot[j] = the pair's first slot;
+//   counts = {units, split pairs}.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanPerThread = (kMaxSortItems + kPlanThreads - 1) / kPlanThreads;
+
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Exclusive scan of x over the workgroup's threads in thread order; *total = the sum.
+__device__ int block_excl_scan(int x, int* sh, int* total) {
+  constexpr int kW = kPlanThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int inc = wave_incl_scan(x);
+  if (lane == 63) sh[w] = inc;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int i = 0; i < kW; ++i) {
+      const int t = sh[i];
+      sh[i] = acc;
+      acc += t;
+    }
+    sh[kW] = acc;
+  }
+  __syncthreads();
+  const int r = sh[w] + inc - x;
+  *total = sh[kW];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void k_plan_split(
+    const int32_t* __restrict__ k_count, const int32_t* __restrict__ k_order, int npairs, int per,
+    int hc, int slots, int extra, int with_slots, int32_t* __restrict__ unit_pair,
+    int32_t* __restrict__ unit_slot, int32_t* __restrict__ split_pair,
+    int32_t* __restrict__ split_slot, int32_t* __restrict__ counts) {
+  __shared__ long long red[kPlanThreads];
+  __shared__ int sh[kPlanThreads / 64 + 1];
+  const int tid = threadIdx.x;
+  const int c = (npairs + kPlanThreads - 1) / kPlanThreads;  // pairs of this thread (<= 8)
+  const int r0 = tid * c;
+  int nq[kPlanPerThread];
+  long long mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanPerThread; ++i) {
+    const int r = r0 + i;
+    nq[i] = 0;
+    if (i < c && r < npairs) {
+      const int item = k_order[r];
+      nq[i] = k_count[2 * item] + k_count[2 * item + 1];
+      mine += (long long)nq[i] * hc;
+    }
+  }
+  red[tid] = mine;
+  __syncthreads();
+  for (int st = kPlanThreads / 2; st > 0; st >>= 1) {
+    if (tid < st) red[tid] += red[tid + st];
+    __syncthreads();
+  }
+  long long half = red[0] * per / (2LL * slots);  // half the average slot load, in steps
+  if (half < kSplitMinSteps) half = kSplitMinSteps;
+
+  int want[kPlanPerThread];
+  int my_want = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanPerThread; ++i) {
+    const long long u = (long long)nq[i] * hc;
+    long long sg = 1;
+    if (u > half) {
+      sg = (u + half - 1) / half;
+      sg = sg < kSplitMaxSegs ? sg : kSplitMaxSegs;
+      sg = sg < nq[i] ? sg : nq[i];
+      sg = sg < u / kSplitMinSteps ? sg : u / kSplitMinSteps;
+      sg = sg > 1 ? sg : 1;
+    }
+    want[i] = (int)sg - 1;
+    my_want += want[i];
+  }
+  int total;
+  int before = block_excl_scan(my_want, sh, &total);
+  int segs[kPlanPerThread];
+  int my_units = 0, my_split = 0, my_slots = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanPerThread; ++i) {
+    const int allowed = max(0, min(want[i], extra - before));
+    before += want[i];
+    segs[i] = 1 + allowed;
+    if (i < c && r0 + i < npairs) {
+      my_units += segs[i];
+      if (segs[i] > 1) {
+        my_split += 1;
+        my_slots += segs[i] * per;
+      }
+    }
+  }
+  int units_total, split_total, slots_total;
+  int u_pos = block_excl_scan(my_units, sh, &units_total);
+  int j_pos = block_excl_scan(my_split, sh, &split_total);
+  int s_pos = block_excl_scan(my_slots, sh, &slots_total);
+#pragma unroll
+  for (int i = 0; i < kPlanPerThread; ++i) {
+    const int r = r0 + i;
+    if (i < c && r < npairs) {
+      const int sg = segs[i];
+      for (int q = 0; q < sg; ++q) {
+        unit_pair[u_pos + q] = r | (q << 16) | (sg << 24);
+        unit_slot[u_pos + q] = (sg > 1 && with_slots) ? s_pos + q * per : -1;
+      }
+      if (sg > 1) {
+        split_pair[j_pos] = r | (sg << 24);
+        split_slot[j_pos] = with_slots ? s_pos : -1;
+        ++j_pos;
+        s_pos += sg * per;
+      }
+      u_pos += sg;
+    }
+  }
+  if (tid == 0) {
+    counts[0] = units_total;
+    counts[1] = split_total;
+  }
+}
 
 // kMulti: the mask is the multi-interval form (else the four-vector form).
 template <bool kMulti>
@@ -118,22 +290,21 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
   const int l32 = lane & 31, hh = lane >> 5;
   const int N = p.Nk, Nq = p.Nq;  // N: keys (and mask columns)
 
-  // workgroup: LPT item (mask row, KV block), then a kv head of that mask set, then a
-  // chunk of at most hc query heads of that kv head and set
-  const int cpk = p.hm.cpk, per = p.hm.kvpm * cpk;
-  const int r = blockIdx.x / per, rem = blockIdx.x - r * per;
-  const int kvl = rem / cpk, ch = rem - kvl * cpk;
-  const int item = p.k_order[r];
-  const int mr = item / p.nKB, kb = item - mr * p.nKB;
-  const int b = mr / p.hm.Hm;
-  const int g = p.Hq / p.Hkv;
-  const int hq0 = (mr - b * p.hm.Hm) * p.hm.qpm;  // first query head of the set
-  const int kvh = hq0 / g + kvl;
-  const int hs = max(kvh * g, hq0);              // first query head of (kv head, set)
-  const int h0 = hs + ch * p.hm.hc;
-  const int nh = min(p.hm.hc, hs + p.hm.gq - h0);
+  // workgroup: work unit (a segment of the queue of an LPT pair (mask row, KV block)),
+  // then a kv head of that mask set and a chunk of at most hc of its query heads
+  const int per = p.hm.kvpm * p.hm.cpk;
+  const int pu = blockIdx.x / per, rem = blockIdx.x - pu * per;
+  if (pu >= p.split_counts[0]) return;  // the grid covers the largest possible plan
+  const int ue = p.unit_pair[pu];
+  const int seg = (ue >> 16) & 0xff, nseg = ue >> 24;
+  const int slot = p.unit_slot[pu];     // >= 0: a segment writing fp32 partial sums
+  const int item = p.k_order[ue & 0xffff];
+  const DkdvItem wi = dkdv_item(p.hm, p.Hq, p.Hkv, p.nKB, item, rem);
+  const int mr = wi.mr, kb = wi.kb, b = wi.b, kvh = wi.kvh, h0 = wi.h0, nh = wi.nh;
   const bool direct = p.hm.writers == 1;
-  const int nq = p.k_count[2 * item] + p.k_count[2 * item + 1];
+  const int nq_all = p.k_count[2 * item] + p.k_count[2 * item + 1];
+  const int q_lo = seg * nq_all / nseg;
+  const int nq = (seg + 1) * nq_all / nseg - q_lo;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const uint32_t acc_bytes = (uint32_t)N * D * 4;
   const size_t kvbase = (size_t)(b * p.Hkv + kvh) * N * D;
@@ -153,7 +324,7 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
     }
     return;
   }
-  const int32_t* queue = p.k_queue + (size_t)item * p.nQB;
+  const int32_t* queue = p.k_queue + (size_t)item * p.nQB + q_lo;
   const bool ragged_k = (N % BK) != 0 && kb == p.nKB - 1;
 
   // ---- K of the block into LDS (B operand of S = Q K^T), V resident in registers
@@ -338,7 +509,23 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
   // ---- dK, dV of this workgroup's keys (keys past N dropped by the buffer bounds).  A
   // lane holds dimension d*32 + l32 of keys wave*32 + hh*4 + (i/4)*8 + i%4.
   const uint32_t kl = (uint32_t)((kb * BK + wave * 32 + hh * 4) * D + l32);
-  if (direct) {
+  if (slot >= 0) {
+    // one segment of a split pair: fp32 partial sums into its slot, reduced in segment
+    // order by k_dkdv_reduce (scale applied there)
+    const size_t so = (size_t)(slot + rem) * BK * D, half = (size_t)p.nslots * BK * D;
+    float* pk = p.partials + so;
+    float* pv = p.partials + half + so;
+    const int kr = wave * 32 + hh * 4;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int o = (kr + (i >> 2) * 8 + (i & 3)) * D + d * 32 + l32;
+        pk[o] = dk[d][i];
+        pv[o] = dv[d][i];
+      }
+    }
+  } else if (direct) {
     const rsrc_t dkr = make_rsrc(p.dk + kvbase, head_bytes);
     const rsrc_t dvr = make_rsrc(p.dv + kvbase, head_bytes);
 #pragma unroll
@@ -632,6 +819,64 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   }
 }
 
+// ---- Reduction of split pairs' partial dK/dV (pairs that store bf16 directly) ----------
+struct ReduceParams {
+  const int32_t* __restrict__ k_order;
+  const int32_t* __restrict__ split_pair;
+  const int32_t* __restrict__ split_slot;
+  const int32_t* __restrict__ split_counts;
+  const float* __restrict__ partials;  // [2][nslots][BK][D]
+  bf16* __restrict__ dk;
+  bf16* __restrict__ dv;
+  HeadMap hm;
+  int Hq, Hkv, nKB, Nk, nslots;
+  float scale;
+};
+
+// One workgroup per (split pair, kv head of its set): dK = scale * sum_seg partial_dK and
+// dV = sum_seg partial_dV, summed in segment order, stored as bf16 (keys past Nk dropped).
+__global__ __launch_bounds__(256) void k_dkdv_reduce(ReduceParams p) {
+  constexpr int BK = kBwdBlockK;
+  const int per = p.hm.kvpm * p.hm.cpk;
+  const int j = blockIdx.x / per, rem = blockIdx.x - j * per;
+  if (j >= p.split_counts[1]) return;
+  const int sp = p.split_pair[j];
+  const int nseg = sp >> 24, base = p.split_slot[j];
+  const DkdvItem wi = dkdv_item(p.hm, p.Hq, p.Hkv, p.nKB, p.k_order[sp & 0xffff], rem);
+  const size_t half = (size_t)p.nslots * BK * D;
+  const size_t kvbase = (size_t)(wi.b * p.Hkv + wi.kvh) * p.Nk * D;
+  const uint32_t head_bytes = (uint32_t)p.Nk * D * 2;
+  const rsrc_t dkr = make_rsrc(p.dk + kvbase, head_bytes);
+  const rsrc_t dvr = make_rsrc(p.dv + kvbase, head_bytes);
+  for (int t = threadIdx.x; t < BK * D / 4; t += 256) {
+    f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < nseg; ++q) {
+      const size_t so = (size_t)(base + q * per + rem) * BK * D + (size_t)t * 4;
+      sk += *reinterpret_cast<const f32x4*>(p.partials + so);
+      sv += *reinterpret_cast<const f32x4*>(p.partials + half + so);
+    }
+    const uint32_t off = (uint32_t)(wi.kb * BK * D + t * 4) * 2;
+    buf_store8(u32x2{pack_bf16x2(sk[0] * p.scale, sk[1] * p.scale),
+                     pack_bf16x2(sk[2] * p.scale, sk[3] * p.scale)}, dkr, off, 0);
+    buf_store8(u32x2{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])}, dvr, off, 0);
+  }
+}
+
+// Compute units of the current device (cached per device; two dK/dV workgroups fit a CU).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 unsigned grid_for(size_t n, unsigned cap) {
   size_t g = (n + 255) / 256;
   return (unsigned)(g < cap ? (g ? g : 1) : cap);
@@ -678,6 +923,15 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
                        reinterpret_cast<float4*>(a.dv_acc), rows_k * D / 4);
   }
 
+  // work units of the dK/dV kernel: long pairs split along their queues
+  const int per = hm.kvpm * hm.cpk;
+  const int npairs = a.B * a.Hm * a.nKB_k;
+  const int nslots = split_slots(per, a.split_extra);
+  if (npairs > 0)
+    hipLaunchKernelGGL(k_plan_split, dim3(1), dim3(kPlanThreads), 0, s, a.k_count, a.k_order,
+                       npairs, per, hm.hc, 2 * cu_count(), a.split_extra, acc ? 0 : 1,
+                       a.unit_pair, a.unit_slot, a.split_pair, a.split_slot, a.split_counts);
+
   DkdvParams p;
   p.q = q.q; p.k = q.k; p.v = q.v; p.dout = q.dout;
   p.lse2 = a.lse2;
@@ -693,16 +947,37 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
   p.nQB = a.nQB_k; p.nKB = a.nKB_k;
   p.hm = hm;
+  p.unit_pair = a.unit_pair;
+  p.unit_slot = a.unit_slot;
+  p.split_counts = a.split_counts;
+  p.partials = a.partials;
+  p.nslots = nslots;
   p.c = c;
   p.scale = a.scale;
-  const unsigned grid = (unsigned)a.B * (unsigned)a.Hm * (unsigned)a.nKB_k * (unsigned)hm.kvpm *
-                        (unsigned)hm.cpk;
+  // the largest plan: every pair plus the extra units (those past the plan exit at once)
+  const unsigned grid = (unsigned)(npairs + a.split_extra) * (unsigned)per;
   if (ev.dkdv_start) (void)hipEventRecord(ev.dkdv_start, s);
   if (grid > 0)
     hipLaunchKernelGGL(multi ? k_attn_bwd_dkdv<true> : k_attn_bwd_dkdv<false>, dim3(grid),
                        dim3(64 * dkdv::kWaves), 0, s, p);
   if (ev.dkdv_stop) (void)hipEventRecord(ev.dkdv_stop, s);
 
+  if (!acc && a.split_extra > 0 && npairs > 0) {
+    ReduceParams rp;
+    rp.k_order = a.k_order;
+    rp.split_pair = a.split_pair;
+    rp.split_slot = a.split_slot;
+    rp.split_counts = a.split_counts;
+    rp.partials = a.partials;
+    rp.dk = p.dk;
+    rp.dv = p.dv;
+    rp.hm = hm;
+    rp.Hq = a.Hq; rp.Hkv = a.Hkv; rp.nKB = a.nKB_k; rp.Nk = a.Nk;
+    rp.nslots = nslots;
+    rp.scale = a.scale;
+    hipLaunchKernelGGL(k_dkdv_reduce, dim3((unsigned)a.split_extra * (unsigned)per), dim3(256),
+                       0, s, rp);
+  }
   if (acc && rows_k > 0) {
     hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_k * D / 8, 16384)), dim3(256), 0, s,
                        a.dk_acc, static_cast<bf16*>(a.dk), a.scale, rows_k * D / 8);

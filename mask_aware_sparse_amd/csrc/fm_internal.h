@@ -26,6 +26,14 @@ constexpr int kAlphaPartial = 11;
 constexpr int kAlphaUnmasked = 10;
 // The LPT sort runs in one workgroup with 64-bit keys in LDS.
 constexpr int kMaxSortItems = 8192;
+// Splitting of long dK/dV work items.  A (mask row, KV block) pair whose queue is long
+// against the average load per workgroup slot is cut into at most kSplitMaxSegs segments
+// of its queue; at most kSplitExtraUnits extra workgroups are added per launch.  Where the
+// kernel would store bf16 directly, the segments write fp32 partial sums (one slot of
+// kBwdBlockK x 128 per segment and tensor) that a reduction kernel adds in segment order.
+constexpr int kSplitMaxSegs = 16;
+constexpr int kSplitExtraUnits = 512;
+constexpr int kSplitMinSteps = 16;   // no segment shorter than this many tile steps
 
 // How query heads, kv heads and mask sets relate.  The vectors are [B][Hm][Nk]; query
 // head h uses set h / (Hq / Hm), and Hm divides Hkv or is a multiple of it.  Tiles are
@@ -148,11 +156,31 @@ struct BwdArgs {
   float* delta;  // [B][Hq][Nq] rowsum(dO * O)
   float* dk_acc; // [B][Hkv][Nk][128] fp32, only when head_map(...).writers > 1 (else null)
   float* dv_acc; // [B][Hkv][Nk][128] fp32, likewise
+  // dK/dV work units (split plan): unit_pair / unit_slot [pairs + extra], split_pair /
+  // split_slot [extra], counts[2] = {units, split pairs}; partials [2][slots][BK][128] fp32
+  // (only when writers == 1)
+  int32_t* unit_pair;
+  int32_t* unit_slot;
+  int32_t* split_pair;
+  int32_t* split_slot;
+  int32_t* split_counts;
+  float* partials;
+  int split_extra;   // extra pair units allowed (0: no splitting)
   int B, Hq, Hkv, Hm, Nq, Nk;
   int nQB_k, nKB_k;  // block counts at the dK/dV tile
   int nQB_q, nKB_q;  // block counts at the dQ (forward) tile
   float scale;
 };
+// Extra pair units of the split plan for `per` workgroups per pair, and the partial slots
+// it can use (each split pair takes s >= 2 segments of `per` slots, s - 1 of them extra).
+inline int split_extra_pairs(int per, int64_t pair_units) {
+  if (per <= 0) return 0;
+  int64_t e = kSplitExtraUnits / per;
+  const int64_t cap = pair_units;  // never more than doubles the work units
+  return (int)(e < cap ? e : cap);
+}
+inline int split_slots(int per, int extra) { return 2 * extra * per; }
+
 struct BwdEvents {
   hipEvent_t dkdv_start, dkdv_stop, dq_start, dq_stop;
 };

@@ -71,6 +71,16 @@ def test_tile_shapes():
         fm.tile_shape(fm.OP_CLASSIFY)
 
 
+def split_plan_bytes(pairs, per, acc):
+    """Workspace of the dK/dV split plan: unit tables over pairs + extra units, the split
+    pair tables, two counters, and (without fp32 accumulators) 2 x 2 x extra x per partial
+    slots of 128 keys x 128 dims (fp32, dK and dV)."""
+    al = lambda x: (x + 255) // 256 * 256
+    extra = min(512 // per, pairs)
+    b = 2 * al((pairs + extra) * 4) + 2 * al(extra * 4) + al(8)
+    return b if acc else b + al(2 * 2 * extra * per * 128 * 128 * 4)
+
+
 def test_workspace_sizes():
     # forward: minmax (16 int32 per block: room for 4 intervals) + queue + counts + cost +
     # order, each 256-byte aligned
@@ -80,12 +90,13 @@ def test_workspace_sizes():
     want = al(B * nkb * 64) + al(B * nqb * nkb * 4) + al(B * nqb * 8) + 2 * al(B * nqb * 4)
     assert fm.workspace_size(B, 4, 2, N, fm.OP_FWD) == want
     assert fm.workspace_size(B, 4, 2, N, fm.OP_CLASSIFY, 64, 32) == al(B * 16 * 4) + al(B * 32 * 4)
-    # backward: fp32 dK/dV accumulators exist only for query-head groups above 4 heads
-    # (same Hq, so the same D / LSE buffers; tiles depend on B and N only)
+    # backward: fp32 dK/dV accumulators exist only for query-head groups above 4 heads;
+    # without them the split plan keeps fp32 partial slots instead (same Hq, so the same
+    # D / LSE buffers; tiles depend on B and N only; 16 pairs of 2 workgroups each)
     with_acc = fm.workspace_size(B, 8, 1, N, fm.OP_BWD)
     without = fm.workspace_size(B, 8, 2, N, fm.OP_BWD)
-    assert with_acc - without == 2 * al(B * 1 * N * 128 * 4)
-    assert without < 2 * B * 8 * N * 4 + 65536
+    assert with_acc - without == 2 * al(B * 1 * N * 128 * 4) + \
+        split_plan_bytes(16, 2, True) - split_plan_bytes(16, 2, False)
 
 
 @pytest.mark.parametrize("bad,code", [
@@ -246,7 +257,10 @@ def test_mask_heads_workspace_sizes():
     tiles_k = al(B * 4 * 8 * 64) + al(B * 4 * 8 * 32 * 4) + al(B * 4 * 8 * 8) + 2 * al(B * 4 * 8 * 4)
     tiles_q = al(B * 4 * nkb * 64) + al(B * 4 * nqb * nkb * 4) + al(B * 4 * nqb * 8) + \
         2 * al(B * 4 * nqb * 4)
-    assert split - whole == al_acc + tiles_k + tiles_q    # 8 sets: twice the tile rows
+    # 8 sets: twice the tile rows, accumulators, and the plan of 128 pairs without partial
+    # slots against 64 pairs with them
+    assert split - whole == al_acc + tiles_k + tiles_q + split_plan_bytes(128, 1, True) - \
+        split_plan_bytes(64, 1, False)
 
 
 def test_mask_heads_sort_limit():

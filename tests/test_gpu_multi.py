@@ -98,6 +98,8 @@ def _four_vector_twin(n, B, seed):
 
 @pytest.mark.parametrize("hq,hkv", [(2, 1), (6, 1)])
 def test_forms_agree_bit_for_bit(hq, hkv):
+    """Same mask through both entry points: bit-identical, except dK/dV of a group above 4
+    heads, which fp32 atomics sum in arrival order (then within the gradient tolerance)."""
     import mask_aware_sparse_amd as fm
     n, B = 384, 2
     w = workloads.causal(n, batch=B, heads_q=hq, heads_kv=hkv)
@@ -111,8 +113,13 @@ def test_forms_agree_bit_for_bit(hq, hkv):
         ga = fm.attn_bwd_multi(q, k, v, *a, do, s, e)
         gb = fm.attn_bwd(q, k, v, *b, do, *vec)
         torch.cuda.synchronize()
-        for x, y in zip(a + ga, b + gb):
+        for x, y in zip(a + ga[:1], b + gb[:1]):
             assert torch.equal(x, y)
+        for x, y in zip(ga[1:], gb[1:]):
+            if hq // hkv <= 4:
+                assert torch.equal(x, y)
+            else:
+                assert rel_l2(to_np(x), to_np(y)) <= 1e-3
 
 
 def test_multi_localize_and_rank_share():
