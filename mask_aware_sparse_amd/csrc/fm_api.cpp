@@ -33,7 +33,7 @@ fm_status check_problem(const fm_problem* p) {
   if (p->heads_q % p->heads_kv != 0) return FM_ERR_INVALID_ARG;
   if (!fm::head_map_valid(p->heads_q, p->heads_kv, hm_of(p))) return FM_ERR_INVALID_ARG;
   if (!(p->softmax_scale <= 0.f || std::isfinite(p->softmax_scale))) return FM_ERR_INVALID_ARG;
-  if (p->head_dim != fm::kHeadDim) return FM_ERR_UNSUPPORTED;
+  if (!fm::head_dim_supported(p->head_dim)) return FM_ERR_UNSUPPORTED;
   // per-head buffers < 2 GiB
   if (nq_of(p) > (1 << 22) || nk_of(p) > (1 << 22)) return FM_ERR_UNSUPPORTED;
   return FM_OK;
@@ -144,8 +144,8 @@ BwdWs bwd_ws(const fm_problem* p, const Blocks& nk, const Blocks& nq) {
   const fm::HeadMap hm = fm::head_map(p->heads_q, p->heads_kv, hm_of(p));
   w.acc = hm.writers > 1;
   if (w.acc) {
-    w.dk = off; off += align_up(rk * fm::kHeadDim * 4);
-    w.dv = off; off += align_up(rk * fm::kHeadDim * 4);
+    w.dk = off; off += align_up(rk * p->head_dim * 4);
+    w.dv = off; off += align_up(rk * p->head_dim * 4);
   }
   // split plan of the dK/dV work units; partial sums only where bf16 is stored directly
   const int64_t pairs = (int64_t)B * nk.nKB;
@@ -158,7 +158,7 @@ BwdWs bwd_ws(const fm_problem* p, const Blocks& nk, const Blocks& nq) {
   w.split_counts = off; off += align_up(2 * 4);
   if (!w.acc) {
     w.partials = off;
-    off += align_up((size_t)2 * fm::split_slots(per, w.extra) * fm::kBwdBlockK * fm::kHeadDim * 4);
+    off += align_up((size_t)2 * fm::split_slots(per, w.extra) * fm::kBwdBlockK * p->head_dim * 4);
   }
   w.total = off;
   return w;
@@ -319,7 +319,7 @@ fm_status fwd_impl(const fm_problem* p, const void* q, const void* k, const void
     a.q = q; a.k = k; a.v = v; a.m = ma; a.o = o; a.lse = lse;
     a.q_queue = t.q_queue; a.q_count = t.q_count; a.q_order = order;
     a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.Hm = hm_of(p);
-    a.Nq = nq_of(p); a.Nk = nk_of(p);
+    a.Nq = nq_of(p); a.Nk = nk_of(p); a.D = p->head_dim;
     a.nQB = (int)nb.nQB; a.nKB = (int)nb.nKB;
     a.scale = scale_of(p);
     e = fm::launch_fwd(a, s, ev_start(events), ev_stop(events));
@@ -386,7 +386,7 @@ fm_status bwd_impl(const fm_problem* p, const void* q, const void* k, const void
     a.partials = w.acc ? nullptr : at<float>(ws, w.partials);
     a.split_extra = w.extra;
     a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.Hm = hm_of(p);
-    a.Nq = nq_of(p); a.Nk = nk_of(p);
+    a.Nq = nq_of(p); a.Nk = nk_of(p); a.D = p->head_dim;
     a.nQB_k = (int)nk.nQB; a.nKB_k = (int)nk.nKB;
     a.nQB_q = (int)nq.nQB; a.nKB_q = (int)nq.nKB;
     a.scale = scale_of(p);

@@ -41,7 +41,6 @@
 namespace fm {
 namespace {
 
-constexpr int D = kHeadDim;
 
 __global__ __launch_bounds__(256) void k_zero(float4* __restrict__ p, size_t n4) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256)
@@ -79,7 +78,7 @@ namespace dkdv {
 constexpr int kWaves = kBwdBlockK / 32;
 constexpr int BQ = kBwdBlockQ;  // 32 query rows per step
 constexpr int BK = kBwdBlockK;  // 128 keys per workgroup
-constexpr int KS = D + 8;       // K row stride in LDS (272 B: row reads only)
+constexpr int KS = kHeadDim + 8;  // K row stride in LDS (272 B: row reads only)
 static_assert(BK == 32 * kWaves, "one 32-key slice per wave");
 
 // Q / dO tiles use the swizzled 320-byte layout (row reads and transposing reads).
@@ -282,9 +281,12 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_split(
 }
 
 // kMulti: the mask is the multi-interval form (else the four-vector form).
-template <bool kMulti>
+template <int D, bool kMulti>
 __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvParams p) {
   using namespace dkdv;
+  constexpr int kS = D / 16;   // k-steps of a 32x32x16 product over D
+  constexpr int kDB = D / 32;  // 32-column blocks of dK / dV
+  constexpr int kCh = D / 8;   // 16-byte chunks per row
   __shared__ Smem<kMulti> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -329,13 +331,13 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
 
   // ---- K of the block into LDS (B operand of S = Q K^T), V resident in registers
   const int key = kb * BK + wave * 32 + l32;
-  bf16x8 vr[8];
+  bf16x8 vr[kS];
   {
     const rsrc_t kr_ = make_rsrc(p.k + kvbase, head_bytes);
     const rsrc_t vr_ = make_rsrc(p.v + kvbase, head_bytes);
     const uint32_t off = (uint32_t)key * (D * 2) + hh * 16;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < kS; ++s) {
       vr[s] = __builtin_bit_cast(bf16x8, buf_load16(vr_, off, s * 32));
       *reinterpret_cast<u32x4*>(&sm.k[(wave * 32 + l32) * KS + s * 16 + hh * 8]) =
           buf_load16(kr_, off, s * 32);
@@ -362,15 +364,15 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
   }
   const bool key_ok = key < N;
 
-  f32x16 dk[4], dv[4];
+  f32x16 dk[kDB], dv[kDB];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) { dk[d] = f32x16{}; dv[d] = f32x16{}; }
+  for (int d = 0; d < kDB; ++d) { dk[d] = f32x16{}; dv[d] = f32x16{}; }
 
-  // ---- staging of the Q / dO tiles: thread copies rows (tid>>4) + kCpRows*i, chunk tid&15
-  constexpr int kCp = BQ * 16 / (64 * kWaves);  // 16-byte chunks per thread and tensor
-  constexpr int kCpRows = 64 * kWaves / 16;
-  static_assert(kCp * 64 * kWaves == BQ * 16, "whole chunks per thread");
-  const int cp_row = tid >> 4, cp_ch = tid & 15;
+  // ---- staging of the Q / dO tiles: thread copies rows tid/kCh + kCpRows*i, chunk tid%kCh
+  constexpr int kCp = BQ * kCh / (64 * kWaves);  // 16-byte chunks per thread and tensor
+  constexpr int kCpRows = 64 * kWaves / kCh;
+  static_assert(kCp * 64 * kWaves == BQ * kCh, "whole chunks per thread");
+  const int cp_row = tid / kCh, cp_ch = tid % kCh;
   u32x4 qst[kCp], ost[kCp];
   uint32_t lst = 0u, dst_ = 0u;
   const int nsteps = nh * nq;
@@ -432,7 +434,7 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
       // ---- S = Q K^T and dP = dO V^T for 32 query rows x this wave's 32 keys ----
       f32x16 sacc, pacc;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+      for (int s = 0; s < kS; ++s) {
         const int o = rr.at(s) + qblk * 32 * kSwzRow;
         const bf16x8 kb8 = *reinterpret_cast<const bf16x8*>(kp + s * 16);
         const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sm.q[cur][o]);
@@ -492,7 +494,7 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
       for (int j = 0; j < 2; ++j) {
         const int ks = qblk * 2 + j;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
+        for (int d = 0; d < kDB; ++d) {
           const int o0 = tr.at(0, ks, d), o1 = tr.at(1, ks, d);
           const bf16* op = sm.dO[cur];
           const bf16* qp = sm.q[cur];
@@ -517,7 +519,7 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
     float* pv = p.partials + half + so;
     const int kr = wave * 32 + hh * 4;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < kDB; ++d) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int o = (kr + (i >> 2) * 8 + (i & 3)) * D + d * 32 + l32;
@@ -529,7 +531,7 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
     const rsrc_t dkr = make_rsrc(p.dk + kvbase, head_bytes);
     const rsrc_t dvr = make_rsrc(p.dv + kvbase, head_bytes);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < kDB; ++d) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const uint32_t so = (uint32_t)(((i >> 2) * 8 + (i & 3)) * D + d * 32) * 2;
@@ -541,7 +543,7 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
     const rsrc_t dkr = make_rsrc(p.dk_acc + kvbase, acc_bytes);
     const rsrc_t dvr = make_rsrc(p.dv_acc + kvbase, acc_bytes);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < kDB; ++d) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const uint32_t so = (uint32_t)(((i >> 2) * 8 + (i & 3)) * D + d * 32) * 4;
@@ -556,7 +558,7 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
 namespace dqk {
 constexpr int BQ = kFwdBlockQ;  // 128 query rows: 4 waves x 32
 constexpr int BK = kFwdBlockK;  // 64 keys per tile
-constexpr int VS = D + 8;       // V row stride (272 B: row reads only)
+constexpr int VS = kHeadDim + 8;  // V row stride (272 B: row reads only)
 
 // K tiles use the swizzled 320-byte layout (row reads and transposing reads).
 struct __attribute__((aligned(16))) Smem {
@@ -585,9 +587,14 @@ struct DqParams {
   float scale;  // softmax scale (applied to dQ)
 };
 
-template <bool kMulti>
+template <int D, bool kMulti>
 __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   using namespace dqk;
+  constexpr int kS = D / 16;               // k-steps of a 32x32x16 product over D
+  constexpr int kDB = D / 32;              // 32-column blocks of dQ
+  constexpr int kCh = D / 8;               // 16-byte chunks per row
+  constexpr int kRowsPass = 256 / kCh;     // rows one pass of the tile copy covers
+  constexpr int kPasses = BK / kRowsPass;  // passes per 64-row tile
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -626,13 +633,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   const int row = qb * BQ + wave * 32 + l32;
 
   // Q^T and dO^T operands: lane holds row `row`, d = s*16 + hh*8 .. +7 (rows past Nq read 0)
-  bf16x8 qr[8], orr[8];
+  bf16x8 qr[kS], orr[kS];
   {
     const rsrc_t qrs = make_rsrc(p.q + qbase * D, q_bytes);
     const rsrc_t ors = make_rsrc(p.dout + qbase * D, q_bytes);
     const uint32_t off = (uint32_t)row * (D * 2) + hh * 16;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < kS; ++s) {
       qr[s] = __builtin_bit_cast(bf16x8, buf_load16(qrs, off, s * 32));
       orr[s] = __builtin_bit_cast(bf16x8, buf_load16(ors, off, s * 32));
     }
@@ -645,7 +652,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
     const uint32_t off = (uint32_t)row * (D * 2) + hh * 16;
     float part = 0.f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < kS; ++s) {
       const u32x4 ov = buf_load16(ors, off, s * 32);
       const u32x4 gv = __builtin_bit_cast(u32x4, orr[s]);
 #pragma unroll
@@ -663,22 +670,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
     buf_store4(__float_as_uint(d_row), make_rsrc(p.delta + qbase, row_bytes), (uint32_t)row * 4, 0);
   }
 
-  f32x16 qacc[4];
+  f32x16 qacc[kDB];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) qacc[d] = f32x16{};
+  for (int d = 0; d < kDB; ++d) qacc[d] = f32x16{};
 
-  const int cp_row = tid >> 4, cp_ch = (tid & 15) * 8;
+  const int cp_row = tid / kCh, cp_ch = (tid % kCh) * 8;
   const int mk_key = lane, mk_wave = __builtin_amdgcn_readfirstlane(wave);
-  u32x4 kst[4], vst[4];
+  u32x4 kst[kPasses], vst[kPasses];
   uint32_t vec[kMulti ? 2 * kMaxIntervals : 4];
 
   auto load_tile = [&](int e) {
     const int kb = e & 0x7fffffff;
     const uint32_t base = (uint32_t)(kb * BK + cp_row) * (D * 2) + cp_ch * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kst[i] = buf_load16(kr_, base, i * 16 * D * 2);
-      vst[i] = buf_load16(vr_, base, i * 16 * D * 2);
+    for (int i = 0; i < kPasses; ++i) {
+      kst[i] = buf_load16(kr_, base, i * kRowsPass * D * 2);
+      vst[i] = buf_load16(vr_, base, i * kRowsPass * D * 2);
     }
     const bool part = (e < 0) || (ragged && kb == p.nKB - 1);
     if (part) {
@@ -697,9 +704,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   };
   auto store_tile = [&](int e, int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(&sm.k[buf][swz(cp_row + 16 * i, cp_ch >> 3)]) = kst[i];
-      *reinterpret_cast<u32x4*>(&sm.v[buf][(cp_row + 16 * i) * VS + cp_ch]) = vst[i];
+    for (int i = 0; i < kPasses; ++i) {
+      *reinterpret_cast<u32x4*>(&sm.k[buf][swz(cp_row + kRowsPass * i, cp_ch >> 3)]) = kst[i];
+      *reinterpret_cast<u32x4*>(&sm.v[buf][(cp_row + kRowsPass * i) * VS + cp_ch]) = vst[i];
     }
     const int kb = e & 0x7fffffff;
     const bool part = (e < 0) || (ragged && kb == p.nKB - 1);
@@ -744,7 +751,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
     for (int blk = 0; blk < 2; ++blk) {
       const bf16* vp = &sm.v[cur][(blk * 32 + arow) * VS + hh * 8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+      for (int s = 0; s < kS; ++s) {
         const bf16x8 ka =
             *reinterpret_cast<const bf16x8*>(&sm.k[cur][rr.at(s) + blk * 32 * kSwzRow]);
         const bf16x8 va = *reinterpret_cast<const bf16x8*>(vp + s * 16);
@@ -792,7 +799,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
       for (int j = 0; j < 2; ++j) {
         const int ks = blk * 2 + j;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
+        for (int d = 0; d < kDB; ++d) {
           const bf16x8 a = join_tr(lds_read_tr16(kt + tr.at(0, ks, d)),
                                    lds_read_tr16(kt + tr.at(1, ks, d)));
           qacc[d] = mfma32(a, dsb[j], qacc[d]);
@@ -808,7 +815,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   const rsrc_t dqr = make_rsrc(p.dq + qbase * D, q_bytes);
   const uint32_t ooff = (uint32_t)row * (D * 2) + hh * 8;
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
+  for (int d = 0; d < kDB; ++d) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       u32x2 w;
@@ -829,7 +836,7 @@ struct ReduceParams {
   bf16* __restrict__ dk;
   bf16* __restrict__ dv;
   HeadMap hm;
-  int Hq, Hkv, nKB, Nk, nslots;
+  int Hq, Hkv, nKB, Nk, nslots, D;
   float scale;
 };
 
@@ -837,6 +844,7 @@ struct ReduceParams {
 // dV = sum_seg partial_dV, summed in segment order, stored as bf16 (keys past Nk dropped).
 __global__ __launch_bounds__(256) void k_dkdv_reduce(ReduceParams p) {
   constexpr int BK = kBwdBlockK;
+  const int D = p.D;
   const int per = p.hm.kvpm * p.hm.cpk;
   const int j = blockIdx.x / per, rem = blockIdx.x - j * per;
   if (j >= p.split_counts[1]) return;
@@ -911,16 +919,19 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   const unsigned qgrid = (unsigned)a.B * (unsigned)a.nQB_q * (unsigned)a.Hq;
   if (ev.dq_start) (void)hipEventRecord(ev.dq_start, s);
   const bool multi = a.m.n > 0;
-  if (qgrid > 0)
-    hipLaunchKernelGGL(multi ? k_attn_bwd_dq<true> : k_attn_bwd_dq<false>, dim3(qgrid),
-                       dim3(256), 0, s, q);
+  const bool d64 = a.D == 64;
+  if (qgrid > 0) {
+    auto kern = d64 ? (multi ? k_attn_bwd_dq<64, true> : k_attn_bwd_dq<64, false>)
+                    : (multi ? k_attn_bwd_dq<128, true> : k_attn_bwd_dq<128, false>);
+    hipLaunchKernelGGL(kern, dim3(qgrid), dim3(256), 0, s, q);
+  }
   if (ev.dq_stop) (void)hipEventRecord(ev.dq_stop, s);
 
   if (acc && rows_k > 0) {
-    hipLaunchKernelGGL(k_zero, dim3(grid_for(rows_k * D / 4, 8192)), dim3(256), 0, s,
-                       reinterpret_cast<float4*>(a.dk_acc), rows_k * D / 4);
-    hipLaunchKernelGGL(k_zero, dim3(grid_for(rows_k * D / 4, 8192)), dim3(256), 0, s,
-                       reinterpret_cast<float4*>(a.dv_acc), rows_k * D / 4);
+    hipLaunchKernelGGL(k_zero, dim3(grid_for(rows_k * a.D / 4, 8192)), dim3(256), 0, s,
+                       reinterpret_cast<float4*>(a.dk_acc), rows_k * a.D / 4);
+    hipLaunchKernelGGL(k_zero, dim3(grid_for(rows_k * a.D / 4, 8192)), dim3(256), 0, s,
+                       reinterpret_cast<float4*>(a.dv_acc), rows_k * a.D / 4);
   }
 
   // work units of the dK/dV kernel: long pairs split along their queues
@@ -957,9 +968,11 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   // the largest plan: every pair plus the extra units (those past the plan exit at once)
   const unsigned grid = (unsigned)(npairs + a.split_extra) * (unsigned)per;
   if (ev.dkdv_start) (void)hipEventRecord(ev.dkdv_start, s);
-  if (grid > 0)
-    hipLaunchKernelGGL(multi ? k_attn_bwd_dkdv<true> : k_attn_bwd_dkdv<false>, dim3(grid),
-                       dim3(64 * dkdv::kWaves), 0, s, p);
+  if (grid > 0) {
+    auto kern = d64 ? (multi ? k_attn_bwd_dkdv<64, true> : k_attn_bwd_dkdv<64, false>)
+                    : (multi ? k_attn_bwd_dkdv<128, true> : k_attn_bwd_dkdv<128, false>);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * dkdv::kWaves), 0, s, p);
+  }
   if (ev.dkdv_stop) (void)hipEventRecord(ev.dkdv_stop, s);
 
   if (!acc && a.split_extra > 0 && npairs > 0) {
@@ -974,15 +987,16 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
     rp.hm = hm;
     rp.Hq = a.Hq; rp.Hkv = a.Hkv; rp.nKB = a.nKB_k; rp.Nk = a.Nk;
     rp.nslots = nslots;
+    rp.D = a.D;
     rp.scale = a.scale;
     hipLaunchKernelGGL(k_dkdv_reduce, dim3((unsigned)a.split_extra * (unsigned)per), dim3(256),
                        0, s, rp);
   }
   if (acc && rows_k > 0) {
-    hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_k * D / 8, 16384)), dim3(256), 0, s,
-                       a.dk_acc, static_cast<bf16*>(a.dk), a.scale, rows_k * D / 8);
-    hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_k * D / 8, 16384)), dim3(256), 0, s,
-                       a.dv_acc, static_cast<bf16*>(a.dv), 1.0f, rows_k * D / 8);
+    hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_k * a.D / 8, 16384)), dim3(256), 0, s,
+                       a.dk_acc, static_cast<bf16*>(a.dk), a.scale, rows_k * a.D / 8);
+    hipLaunchKernelGGL(k_bwd_convert, dim3(grid_for(rows_k * a.D / 8, 16384)), dim3(256), 0, s,
+                       a.dv_acc, static_cast<bf16*>(a.dv), 1.0f, rows_k * a.D / 8);
   }
   return hipGetLastError();
 }

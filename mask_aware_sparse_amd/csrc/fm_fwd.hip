@@ -26,9 +26,11 @@ namespace {
 
 constexpr int BQ = kFwdBlockQ;  // 128
 constexpr int BK = kFwdBlockK;  // 64
-constexpr int D = kHeadDim;     // 128
-constexpr int KS = D + 8;       // K row stride in LDS (elements)
-constexpr int VS = D + 32;      // V row stride in LDS (320 B: conflict-free transposing reads)
+// LDS row strides are those of the largest head dimension (128) for every D: the bank
+// pattern of a fragment read depends only on the row stride, so the conflict-free layouts
+// carry over to D = 64 (which uses the first half of each row).
+constexpr int KS = kHeadDim + 8;   // K row stride in LDS (elements)
+constexpr int VS = kHeadDim + 32;  // V row stride in LDS (320 B: conflict-free transposing reads)
 
 struct __attribute__((aligned(16))) FwdSmem {
   bf16 k[2][BK * KS];
@@ -68,9 +70,17 @@ struct FwdParams {
   float c;  // softmax scale * log2(e)
 };
 
-// kMulti: the mask is the multi-interval form (else the four-vector form).
-template <bool kMulti>
+// D: head dimension (64 or 128).  kMulti: the mask is the multi-interval form (else the
+// four-vector form).
+template <int D, bool kMulti>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
+  constexpr int kS = D / 16;                // k-steps of a 32x32x16 product over D
+  constexpr int kDB = D / 32;               // 32-column blocks of O
+  constexpr int kCh = D / 8;                // 16-byte chunks per row
+  constexpr int kRowsPass = 256 / kCh;      // rows one pass of the tile copy covers
+  constexpr int kPasses = BK / kRowsPass;   // passes per 64-row tile
+  constexpr int kSteps = 2 * kS;            // score MFMAs per tile
+  constexpr int kExp = 16 / kSteps;         // exponential pairs per score MFMA
   __shared__ FwdSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -110,22 +120,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   const int row = qb * BQ + wave * 32 + l32;
 
   // Q^T operand: lane holds Q[row][s*16 + hh*8 .. +7] for s = 0..7 (rows past Nq read 0)
-  bf16x8 qr[8];
+  bf16x8 qr[kS];
   {
     const uint32_t off = (uint32_t)row * (D * 2) + hh * 16;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qr[s] = __builtin_bit_cast(bf16x8, buf_load16(qr_, off, s * 32));
+    for (int s = 0; s < kS; ++s) qr[s] = __builtin_bit_cast(bf16x8, buf_load16(qr_, off, s * 32));
   }
 
-  f32x16 oacc[4];
+  f32x16 oacc[kDB];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) oacc[d] = f32x16{};
+  for (int d = 0; d < kDB; ++d) oacc[d] = f32x16{};
   float m_use = -INFINITY, lf = 0.f, lb = 0.f;
 
-  // staging for the tile copy: thread copies rows (tid>>4)+16i, 16-byte chunk tid&15
-  const int cp_row = tid >> 4, cp_ch = (tid & 15) * 8;
+  // staging for the tile copy: thread copies rows tid/kCh + kRowsPass*i, chunk tid%kCh
+  const int cp_row = tid / kCh, cp_ch = (tid % kCh) * 8;
   const int mk_key = lane, mk_wave = __builtin_amdgcn_readfirstlane(wave);
-  u32x4 kst[4], vst[4];
+  u32x4 kst[kPasses], vst[kPasses];
   uint32_t vec[kMulti ? 2 * kMaxIntervals : 4];
   auto is_partial = [&](int e) {
     return (e < 0) || (ragged && (e & 0x7fffffff) == p.nKB - 1);
@@ -140,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     const int kb = e & 0x7fffffff;
     const uint32_t base = (uint32_t)(kb * BK + cp_row) * (D * 2) + cp_ch * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kst[i] = buf_load16(kr_, base, i * 16 * D * 2);
+    for (int i = 0; i < kPasses; ++i) kst[i] = buf_load16(kr_, base, i * kRowsPass * D * 2);
     if (is_partial(e)) {
       const uint32_t vo = (uint32_t)(kb * BK + mk_key) * 4;
       if constexpr (!kMulti) {
@@ -159,12 +169,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     const int kb = e & 0x7fffffff;
     const uint32_t base = (uint32_t)(kb * BK + cp_row) * (D * 2) + cp_ch * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vst[i] = buf_load16(vr_, base, i * 16 * D * 2);
+    for (int i = 0; i < kPasses; ++i) vst[i] = buf_load16(vr_, base, i * kRowsPass * D * 2);
   };
   auto put_k = [&](int e, int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(&sm.k[buf][(cp_row + 16 * i) * KS + cp_ch]) = kst[i];
+    for (int i = 0; i < kPasses; ++i)
+      *reinterpret_cast<u32x4*>(&sm.k[buf][(cp_row + kRowsPass * i) * KS + cp_ch]) = kst[i];
     if (is_partial(e)) {
       const int key = (e & 0x7fffffff) * BK + mk_key;
       const int r0 = qb * BQ + mk_wave * 32;
@@ -179,8 +189,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   };
   auto put_v = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(&sm.v[buf][(cp_row + 16 * i) * VS + cp_ch]) = vst[i];
+    for (int i = 0; i < kPasses; ++i)
+      *reinterpret_cast<u32x4*>(&sm.v[buf][(cp_row + kRowsPass * i) * VS + cp_ch]) = vst[i];
   };
 
   const int arow = perm_rows(l32);
@@ -194,7 +204,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     for (int blk = 0; blk < 2; ++blk) {
       const bf16* kp = &sm.k[buf][(blk * 32 + arow) * KS + hh * 8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+      for (int s = 0; s < kS; ++s) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + s * 16);
         acc[blk] = mfma32(a, qr[s], s == 0 ? f32x16{} : acc[blk]);
       }
@@ -276,18 +286,19 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
       pbsum[0] = pbsum[1] = 0.f;
       const bf16* kbase = &sm.k[nxt][arow * KS + hh * 8];
       auto kread = [&](int i) {
-        return *reinterpret_cast<const bf16x8*>(kbase + (i / 8) * 32 * KS + (i % 8) * 16);
+        return *reinterpret_cast<const bf16x8*>(kbase + (i / kS) * 32 * KS + (i % kS) * 16);
       };
       bf16x8 kf[3];
       kf[0] = kread(0);
       kf[1] = kread(1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (i + 2 < 16) kf[(i + 2) % 3] = kread(i + 2);
-        const int blk = i / 8, st = i % 8;
+      for (int i = 0; i < kSteps; ++i) {
+        if (i + 2 < kSteps) kf[(i + 2) % 3] = kread(i + 2);
+        const int blk = i / kS, st = i % kS;
         snext[blk] = mfma32(kf[i % 3], qr[st], st == 0 ? f32x16{} : snext[blk]);
-        exp_pair(i, off0);
+#pragma unroll
+        for (int e = 0; e < kExp; ++e) exp_pair(i * kExp + e, off0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -313,7 +324,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
         lf *= alpha;
         lb *= alpha;
 #pragma unroll
-        for (int d = 0; d < 4; ++d)
+        for (int d = 0; d < kDB; ++d)
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
         m_use = m_new;
@@ -335,7 +346,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
       for (int j = 0; j < 2; ++j) {
         const int key0 = (blk * 2 + j) * 16 + hh * 8 + tr_row;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
+        for (int d = 0; d < kDB; ++d) {
           const bf16* vp = vb + key0 * VS + d * 32 + tr_col;
           const bf16x8 a = join_tr(lds_read_tr16(vp), lds_read_tr16(vp + 4 * VS));
           oacc[d] = mfma32(a, pb[blk][j], oacc[d]);
@@ -358,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   const rsrc_t orr = make_rsrc(p.o + (size_t)(b * p.Hq + h) * Nq * D, q_bytes);
   const uint32_t ooff = (uint32_t)row * (D * 2) + hh * 8;
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
+  for (int d = 0; d < kDB; ++d) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       u32x2 w;
@@ -393,9 +404,12 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_
   p.c = a.scale * kLog2e;
   const unsigned grid = (unsigned)a.B * (unsigned)a.nQB * (unsigned)a.Hq;
   if (ev0) (void)hipEventRecord(ev0, s);
-  if (grid > 0)
-    hipLaunchKernelGGL(a.m.n > 0 ? k_attn_fwd<true> : k_attn_fwd<false>, dim3(grid), dim3(256),
-                       0, s, p);
+  if (grid > 0) {
+    const bool multi = a.m.n > 0;
+    auto kern = a.D == 64 ? (multi ? k_attn_fwd<64, true> : k_attn_fwd<64, false>)
+                          : (multi ? k_attn_fwd<128, true> : k_attn_fwd<128, false>);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, p);
+  }
   hipError_t e = hipGetLastError();
   if (ev1) (void)hipEventRecord(ev1, s);
   return e;

@@ -7,7 +7,10 @@
 
 namespace fm {
 
+// Head dimensions the kernels are built for; buffers and LDS strides are sized for the
+// largest.
 constexpr int kHeadDim = 128;
+inline bool head_dim_supported(int d) { return d == 64 || d == 128; }
 
 // Tile shapes of the attention kernels.  The forward (and the backward's dQ kernel) uses
 // 128 query rows (4 waves x 32) by 64 keys; the backward's dK/dV kernel 32 query rows by
@@ -129,6 +132,7 @@ struct FwdArgs {
   const int32_t* q_count;
   const int32_t* q_order;
   int B, Hq, Hkv, Hm, Nq, Nk, nQB, nKB;  // Hm: mask sets per batch row
+  int D;                                 // head dimension: 64 or 128
   float scale;
 };
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
@@ -167,6 +171,7 @@ struct BwdArgs {
   float* partials;
   int split_extra;   // extra pair units allowed (0: no splitting)
   int B, Hq, Hkv, Hm, Nq, Nk;
+  int D;             // head dimension: 64 or 128
   int nQB_k, nKB_k;  // block counts at the dK/dV tile
   int nQB_q, nKB_q;  // block counts at the dQ (forward) tile
   float scale;

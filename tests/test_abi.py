@@ -104,7 +104,8 @@ def test_workspace_sizes():
     (dict(Hkv=0), INVALID),
     (dict(N=-1), INVALID),
     (dict(B=-2), INVALID),
-    (dict(d=64), UNSUPPORTED),
+    (dict(d=96), UNSUPPORTED),
+    (dict(d=256), UNSUPPORTED),
     (dict(N=1 << 30), UNSUPPORTED),
     (dict(B=65, N=16384), UNSUPPORTED),     # more than 8192 Q-blocks to sort
 ])

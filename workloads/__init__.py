@@ -21,7 +21,7 @@ plainest readings, fixed once so that runs are reproducible.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 
@@ -272,6 +272,11 @@ def per_head_windows(seed: int = 0, n: int = 32768, batch: int = 1, heads_q: int
                     "sinks": sinks})
 
 
+def with_head_dim(w, d: int):
+    """The same workload (mask, heads, lengths) at head dimension d."""
+    return replace(w, head_dim=int(d), name=f"{w.name}_d{int(d)}")
+
+
 def _finish_multi(name, batch, hq, hkv, n, starts, ends, seed, info):
     return MultiWorkload(name, batch, hq, hkv, n, HEAD_DIM,
                          np.ascontiguousarray(starts, dtype=np.int32),
@@ -341,6 +346,8 @@ VARIANTS = {
     "v1_per_head_windows_32k": lambda seed=0: per_head_windows(seed),
     # multi-interval columns: local window + three random distant query blocks per key block
     "v2_block_sparse_window_32k": lambda seed=0: block_sparse_window(seed),
+    # head dimension 64: the prefix-LM document workload (B=4, 32/8 heads, N=8192) at d=64
+    "v3_prefix_lm_doc_8k_d64": lambda seed=0: with_head_dim(prefix_lm_doc(seed), 64),
 }
 VARIANT_NAMES = list(VARIANTS)
 
