@@ -196,6 +196,22 @@ fm_status check_grid(const fm_problem* p, const Blocks& fwd, const Blocks& bwd) 
 
 }  // namespace
 
+namespace fm {
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+}  // namespace fm
+
 extern "C" {
 
 const char* fm_status_string(fm_status s) {

@@ -632,44 +632,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
 
   const int row = qb * BQ + wave * 32 + l32;
 
-  // Q^T and dO^T operands: lane holds row `row`, d = s*16 + hh*8 .. +7 (rows past Nq read 0)
-  bf16x8 qr[kS], orr[kS];
-  {
-    const rsrc_t qrs = make_rsrc(p.q + qbase * D, q_bytes);
-    const rsrc_t ors = make_rsrc(p.dout + qbase * D, q_bytes);
-    const uint32_t off = (uint32_t)row * (D * 2) + hh * 16;
-#pragma unroll
-    for (int s = 0; s < kS; ++s) {
-      qr[s] = __builtin_bit_cast(bf16x8, buf_load16(qrs, off, s * 32));
-      orr[s] = __builtin_bit_cast(bf16x8, buf_load16(ors, off, s * 32));
-    }
-  }
-  // D = rowsum(dO o O) for this lane's row (the two half-waves hold the two halves of each
-  // 16-wide d slice) and the LSE in log2 units; both go to memory for the dK/dV kernel.
-  float d_row;
-  {
-    const rsrc_t ors = make_rsrc(p.o + qbase * D, q_bytes);
-    const uint32_t off = (uint32_t)row * (D * 2) + hh * 16;
-    float part = 0.f;
-#pragma unroll
-    for (int s = 0; s < kS; ++s) {
-      const u32x4 ov = buf_load16(ors, off, s * 32);
-      const u32x4 gv = __builtin_bit_cast(u32x4, orr[s]);
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        part += bf16lo_to_f32(ov[t]) * bf16lo_to_f32(gv[t]) +
-                bf16hi_to_f32(ov[t]) * bf16hi_to_f32(gv[t]);
-    }
-    d_row = sum_with_partner32(part);
-  }
-  const float lse_nat =
-      __uint_as_float(buf_load4(make_rsrc(p.lse + qbase, row_bytes), (uint32_t)row * 4, 0));
-  const float lse_row = lse_nat == -INFINITY ? INFINITY : lse_nat * kLog2e;
-  if (hh == 0) {  // rows past Nq are dropped by the buffer bounds
-    buf_store4(__float_as_uint(lse_row), make_rsrc(p.lse2 + qbase, row_bytes), (uint32_t)row * 4, 0);
-    buf_store4(__float_as_uint(d_row), make_rsrc(p.delta + qbase, row_bytes), (uint32_t)row * 4, 0);
-  }
-
   f32x16 qacc[kDB];
 #pragma unroll
   for (int d = 0; d < kDB; ++d) qacc[d] = f32x16{};
@@ -723,10 +685,47 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
     }
   };
 
-  if (n_tiles > 0) {
-    load_tile(queue[0]);
-    store_tile(queue[0], 0);
+  // Q^T and dO^T operands: lane holds row `row`, d = s*16 + hh*8 .. +7 (rows past Nq read 0)
+  bf16x8 qr[kS], orr[kS];
+  {
+    const rsrc_t qrs = make_rsrc(p.q + qbase * D, q_bytes);
+    const rsrc_t ors = make_rsrc(p.dout + qbase * D, q_bytes);
+    const uint32_t off = (uint32_t)row * (D * 2) + hh * 16;
+#pragma unroll
+    for (int s = 0; s < kS; ++s) {
+      qr[s] = __builtin_bit_cast(bf16x8, buf_load16(qrs, off, s * 32));
+      orr[s] = __builtin_bit_cast(bf16x8, buf_load16(ors, off, s * 32));
+    }
   }
+  // the first tile's loads go out now, so their latency overlaps that of Q, dO and O
+  if (n_tiles > 0) load_tile(queue[0]);
+  // D = rowsum(dO o O) for this lane's row (the two half-waves hold the two halves of each
+  // 16-wide d slice) and the LSE in log2 units; both go to memory for the dK/dV kernel.
+  float d_row;
+  {
+    const rsrc_t ors = make_rsrc(p.o + qbase * D, q_bytes);
+    const uint32_t off = (uint32_t)row * (D * 2) + hh * 16;
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < kS; ++s) {
+      const u32x4 ov = buf_load16(ors, off, s * 32);
+      const u32x4 gv = __builtin_bit_cast(u32x4, orr[s]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        part += bf16lo_to_f32(ov[t]) * bf16lo_to_f32(gv[t]) +
+                bf16hi_to_f32(ov[t]) * bf16hi_to_f32(gv[t]);
+    }
+    d_row = sum_with_partner32(part);
+  }
+  const float lse_nat =
+      __uint_as_float(buf_load4(make_rsrc(p.lse + qbase, row_bytes), (uint32_t)row * 4, 0));
+  const float lse_row = lse_nat == -INFINITY ? INFINITY : lse_nat * kLog2e;
+  if (hh == 0) {  // rows past Nq are dropped by the buffer bounds
+    buf_store4(__float_as_uint(lse_row), make_rsrc(p.lse2 + qbase, row_bytes), (uint32_t)row * 4, 0);
+    buf_store4(__float_as_uint(d_row), make_rsrc(p.delta + qbase, row_bytes), (uint32_t)row * 4, 0);
+  }
+
+  if (n_tiles > 0) store_tile(queue[0], 0);  // its loads were issued with Q and dO
   lds_barrier();
 
   const int arow = perm_rows(l32);
@@ -870,21 +869,6 @@ __global__ __launch_bounds__(256) void k_dkdv_reduce(ReduceParams p) {
   }
 }
 
-// Compute units of the current device (cached per device; two dK/dV workgroups fit a CU).
-int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 unsigned grid_for(size_t n, unsigned cap) {
   size_t g = (n + 255) / 256;
   return (unsigned)(g < cap ? (g ? g : 1) : cap);
@@ -940,7 +924,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   const int nslots = split_slots(per, a.split_extra);
   if (npairs > 0)
     hipLaunchKernelGGL(k_plan_split, dim3(1), dim3(kPlanThreads), 0, s, a.k_count, a.k_order,
-                       npairs, per, hm.hc, 2 * cu_count(), a.split_extra, acc ? 0 : 1,
+                       npairs, per, hm.hc, 2 * device_cu_count(), a.split_extra, acc ? 0 : 1,
                        a.unit_pair, a.unit_slot, a.split_pair, a.split_slot, a.split_counts);
 
   DkdvParams p;

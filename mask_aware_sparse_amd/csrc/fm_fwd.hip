@@ -135,8 +135,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   // staging for the tile copy: thread copies rows tid/kCh + kRowsPass*i, chunk tid%kCh
   const int cp_row = tid / kCh, cp_ch = (tid % kCh) * 8;
   const int mk_key = lane, mk_wave = __builtin_amdgcn_readfirstlane(wave);
+  constexpr int kVec = kMulti ? 2 * kMaxIntervals : 4;
   u32x4 kst[kPasses], vst[kPasses];
-  uint32_t vec[kMulti ? 2 * kMaxIntervals : 4];
+  uint32_t vec[kVec];
   auto is_partial = [&](int e) {
     return (e < 0) || (ragged && (e & 0x7fffffff) == p.nKB - 1);
   };
@@ -146,11 +147,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   // words) therefore runs one tile ahead of V: iteration t reads K/mw buffer (t+1)&1 and
   // V buffer t&1, and refills K/mw buffer t&1 with tile t+2 and V buffer (t+1)&1 with
   // tile t+1; one barrier per iteration separates those reads from those writes.
-  auto fetch_k = [&](int e) {
+  // fetch_k / put_k stage through (ks, vv): kst / vec in the loop; the prologue also
+  // uses a second set so that both K tiles it needs are requested at once
+  auto fetch_k = [&](int e, u32x4 (&ks)[kPasses], uint32_t (&vec)[kVec]) {
     const int kb = e & 0x7fffffff;
     const uint32_t base = (uint32_t)(kb * BK + cp_row) * (D * 2) + cp_ch * 2;
 #pragma unroll
-    for (int i = 0; i < kPasses; ++i) kst[i] = buf_load16(kr_, base, i * kRowsPass * D * 2);
+    for (int i = 0; i < kPasses; ++i) ks[i] = buf_load16(kr_, base, i * kRowsPass * D * 2);
     if (is_partial(e)) {
       const uint32_t vo = (uint32_t)(kb * BK + mk_key) * 4;
       if constexpr (!kMulti) {
@@ -171,10 +174,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < kPasses; ++i) vst[i] = buf_load16(vr_, base, i * kRowsPass * D * 2);
   };
-  auto put_k = [&](int e, int buf) {
+  auto put_k = [&](int e, int buf, const u32x4 (&ks)[kPasses], const uint32_t (&vec)[kVec]) {
 #pragma unroll
     for (int i = 0; i < kPasses; ++i)
-      *reinterpret_cast<u32x4*>(&sm.k[buf][(cp_row + kRowsPass * i) * KS + cp_ch]) = kst[i];
+      *reinterpret_cast<u32x4*>(&sm.k[buf][(cp_row + kRowsPass * i) * KS + cp_ch]) = ks[i];
     if (is_partial(e)) {
       const int key = (e & 0x7fffffff) * BK + mk_key;
       const int r0 = qb * BQ + mk_wave * 32;
@@ -229,16 +232,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
 
   f32x16 sacc[2];
   if (n_tiles > 0) {
+    // tile 0's K and V and tile 1's K in flight together (one memory round trip)
     const int e0 = queue[0];
-    fetch_k(e0);
+    const int e1 = n_tiles > 1 ? queue[1] : 0;
+    u32x4 kst1[kPasses];
+    uint32_t vec1[kVec];
+    fetch_k(e0, kst, vec);
     fetch_v(e0);
-    put_k(e0, 0);
+    if (n_tiles > 1) fetch_k(e1, kst1, vec1);
+    put_k(e0, 0, kst, vec);
     put_v(0);
-    if (n_tiles > 1) {
-      const int e1 = queue[1];
-      fetch_k(e1);
-      put_k(e1, 1);
-    }
+    if (n_tiles > 1) put_k(e1, 1, kst1, vec1);
   }
   lds_barrier();
   if (n_tiles > 0) {
@@ -251,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     const bool has1 = it + 1 < n_tiles, has2 = it + 2 < n_tiles;
     const int e1 = has1 ? queue[it + 1] : 0;
     const int e2 = has2 ? queue[it + 2] : 0;
-    if (has2) fetch_k(e2);
+    if (has2) fetch_k(e2, kst, vec);
     if (has1) fetch_v(e1);
 
     // ---- scores of tile it+1 (MFMA; stale but unused after the last tile) interleaved
@@ -355,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     }
 
     if (has1 && is_partial(e1)) apply_mask(nxt, snext);
-    if (has2) put_k(e2, cur);
+    if (has2) put_k(e2, cur, kst, vec);
     if (has1) put_v(nxt);
     lds_barrier();
 #pragma unroll

@@ -121,6 +121,9 @@ struct MaskOut {
 hipError_t launch_localize(const MaskPtrs& g, int arrays, const int32_t* offsets, int n_chunks,
                            int chunk_len, const MaskOut& out, int64_t cols, hipStream_t s);
 
+// Compute units of the current device (queried once per device and cached).
+int device_cu_count();
+
 struct FwdArgs {
   const void* q;
   const void* k;
