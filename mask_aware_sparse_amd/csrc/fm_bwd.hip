@@ -216,7 +216,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_split(
     if (tid < st) red[tid] += red[tid + st];
     __syncthreads();
   }
-  long long half = red[0] * per / (2LL * slots);  // half the average slot load, in steps
+  // split above half the average slot load; where segments need the partial-sum reduction
+  // (with_slots), only above the full average load
+  long long half = red[0] * per / ((with_slots ? 1LL : 2LL) * slots);
   if (half < kSplitMinSteps) half = kSplitMinSteps;
 
   int want[kPlanPerThread];
