@@ -248,6 +248,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   if (n_tiles > 0) {
     scores(0, sacc);
     if (is_partial(queue[0])) apply_mask(0, sacc);
+    // The first tile sets each row's offset from its own maximum, so its exponentials are
+    // formed once (the lazy test would otherwise send every row through the slow path on
+    // its first tile).  Rows that see nothing here keep -inf.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
+    m_use = max_with_partner32(mx) * p.c;
   }
 
   for (int it = 0; it < n_tiles; ++it) {
