@@ -81,23 +81,26 @@ Blocks blocks(const fm_problem* p, int bq, int bk) {
 }
 
 fm_status check_sort_limits(const fm_problem* p, const Blocks& nb) {
-  if (mask_rows(p) * nb.nQB > fm::kMaxSortItems) return FM_ERR_UNSUPPORTED;
-  if (mask_rows(p) * nb.nKB > fm::kMaxSortItems) return FM_ERR_UNSUPPORTED;
+  if (mask_rows(p) * nb.nQB > fm::kMaxWorkItems) return FM_ERR_UNSUPPORTED;
+  if (mask_rows(p) * nb.nKB > fm::kMaxWorkItems) return FM_ERR_UNSUPPORTED;
   return FM_OK;
 }
+inline int64_t max2(int64_t a, int64_t b) { return a > b ? a : b; }
 
 // ---- workspace layouts ------------------------------------------------------------
-struct ClassifyWs { size_t q_cost, k_cost, total; };
+struct ClassifyWs { size_t q_cost, k_cost, sort, total; };
 ClassifyWs classify_ws(const fm_problem* p, const Blocks& nb) {
   ClassifyWs w{};
   size_t off = 0;
   w.q_cost = off; off += align_up((size_t)mask_rows(p) * nb.nQB * 4);
   w.k_cost = off; off += align_up((size_t)mask_rows(p) * nb.nKB * 4);
+  w.sort = off;
+  off += align_up(fm::lpt_sort_scratch_bytes(max2(mask_rows(p) * nb.nQB, mask_rows(p) * nb.nKB)));
   w.total = off;
   return w;
 }
 
-struct FwdWs { size_t mm, q_queue, q_count, q_cost, q_order, total; };
+struct FwdWs { size_t mm, q_queue, q_count, q_cost, q_order, sort, total; };
 FwdWs fwd_ws(const fm_problem* p, const Blocks& nb) {
   FwdWs w{};
   const size_t B = mask_rows(p);  // tile structures are per mask row
@@ -107,6 +110,7 @@ FwdWs fwd_ws(const fm_problem* p, const Blocks& nb) {
   w.q_count = off; off += align_up(B * nb.nQB * 2 * 4);
   w.q_cost = off; off += align_up(B * nb.nQB * 4);
   w.q_order = off; off += align_up(B * nb.nQB * 4);
+  w.sort = off; off += align_up(fm::lpt_sort_scratch_bytes((int64_t)B * nb.nQB));
   w.total = off;
   return w;
 }
@@ -116,6 +120,7 @@ struct BwdWs {
   size_t mm_q, q_queue, q_count, q_cost, q_order;   // dQ (forward) tiles
   size_t lse2, delta, dk, dv;
   size_t unit_pair, unit_slot, split_pair, split_slot, split_counts, partials;  // split plan
+  size_t sort;  // LPT sort scratch (lists longer than one workgroup sorts)
   size_t total;
   bool acc;   // fp32 dK/dV accumulators present
   int extra;  // extra pair units of the split plan
@@ -156,6 +161,8 @@ BwdWs bwd_ws(const fm_problem* p, const Blocks& nk, const Blocks& nq) {
   w.split_pair = off; off += align_up((size_t)w.extra * 4);
   w.split_slot = off; off += align_up((size_t)w.extra * 4);
   w.split_counts = off; off += align_up(2 * 4);
+  w.sort = off;
+  off += align_up(fm::lpt_sort_scratch_bytes(max2((int64_t)B * nk.nKB, (int64_t)B * nq.nQB)));
   if (!w.acc) {
     w.partials = off;
     off += align_up((size_t)2 * fm::split_slots(per, w.extra) * fm::kBwdBlockK * p->head_dim * 4);
@@ -295,8 +302,9 @@ fm_status classify_impl(const fm_problem* p, const MaskT* m, int32_t block_q, in
   t.k_cost = at<int32_t>(ws, w.k_cost);
   const int R = (int)mask_rows(p);
   hipError_t e = fm::launch_classify(mask_args(m), R, nq_of(p), nk_of(p), block_q, block_k, t, s);
-  if (e == hipSuccess) e = fm::launch_lpt_sort(t.q_cost, out->q_order, (int)(R * nb.nQB), s);
-  if (e == hipSuccess) e = fm::launch_lpt_sort(t.k_cost, out->k_order, (int)(R * nb.nKB), s);
+  void* scr = at<char>(ws, w.sort);
+  if (e == hipSuccess) e = fm::launch_lpt_sort(t.q_cost, out->q_order, (int)(R * nb.nQB), scr, s);
+  if (e == hipSuccess) e = fm::launch_lpt_sort(t.k_cost, out->k_order, (int)(R * nb.nKB), scr, s);
   return hip_status(e);
 }
 
@@ -329,7 +337,8 @@ fm_status fwd_impl(const fm_problem* p, const void* q, const void* k, const void
   hipError_t e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kFwdBlockQ, fm::kFwdBlockK,
                                      t, s);
   int32_t* order = at<int32_t>(ws, w.q_order);
-  if (e == hipSuccess) e = fm::launch_lpt_sort(t.q_cost, order, (int)(R * nb.nQB), s);
+  if (e == hipSuccess)
+    e = fm::launch_lpt_sort(t.q_cost, order, (int)(R * nb.nQB), at<char>(ws, w.sort), s);
   if (e == hipSuccess) {
     fm::FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.m = ma; a.o = o; a.lse = lse;
@@ -382,10 +391,11 @@ fm_status bwd_impl(const fm_problem* p, const void* q, const void* k, const void
   const int R = (int)mask_rows(p);
   hipError_t e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kBwdBlockQ, fm::kBwdBlockK,
                                      tk, s);
-  if (e == hipSuccess) e = fm::launch_lpt_sort(tk.k_cost, k_order, (int)(R * nk.nKB), s);
+  void* scr = at<char>(ws, w.sort);
+  if (e == hipSuccess) e = fm::launch_lpt_sort(tk.k_cost, k_order, (int)(R * nk.nKB), scr, s);
   if (e == hipSuccess)
     e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kFwdBlockQ, fm::kFwdBlockK, tq, s);
-  if (e == hipSuccess) e = fm::launch_lpt_sort(tq.q_cost, q_order, (int)(R * nq.nQB), s);
+  if (e == hipSuccess) e = fm::launch_lpt_sort(tq.q_cost, q_order, (int)(R * nq.nQB), scr, s);
   if (e == hipSuccess) {
     fm::BwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout; a.m = ma;

@@ -148,9 +148,9 @@ __device__ __forceinline__ DkdvItem dkdv_item(const HeadMap& hm, int Hq, int Hkv
 // s_r = min(kSplitMaxSegs, ceil(2 u_r / L), queue length, u_r / kSplitMinSteps) segments,
 // the extra segments granted in pair order while they fit in `extra`.  Unit table, pairs in
 // LPT order and the segments of a pair consecutive:
-//   unit_pair[u] = r | seg << 16 | s_r << 24;  unit_slot[u] = first partial slot of the
+//   unit_pair[u] = r | seg << 24 | (s_r - 1) << 28 (r < 2^24);  unit_slot[u] = first partial slot of the
 //   segment (its `per` workgroups use slot + rem) or -1 when unsplit or with_slots == 0;
-//   split_pair[j] = r | s_r << 24, split_slot[j] = the pair's first slot;
+//   split_pair[j] = r | (s_r - 1) << 28, split_slot[j] = the pair's first slot;
 //   counts = {units, split pairs}.
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanPerThread = (kMaxSortItems + kPlanThreads - 1) / kPlanThreads;
@@ -196,6 +196,18 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_split(
   __shared__ long long red[kPlanThreads];
   __shared__ int sh[kPlanThreads / 64 + 1];
   const int tid = threadIdx.x;
+  if (npairs > kPlanThreads * kPlanPerThread) {
+    // more pairs than the plan handles in one workgroup: one unit per pair, no split
+    for (int r = tid; r < npairs; r += kPlanThreads) {
+      unit_pair[r] = r;
+      unit_slot[r] = -1;
+    }
+    if (tid == 0) {
+      counts[0] = npairs;
+      counts[1] = 0;
+    }
+    return;
+  }
   const int c = (npairs + kPlanThreads - 1) / kPlanThreads;  // pairs of this thread (<= 8)
   const int r0 = tid * c;
   int nq[kPlanPerThread];
@@ -264,11 +276,11 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_split(
     if (i < c && r < npairs) {
       const int sg = segs[i];
       for (int q = 0; q < sg; ++q) {
-        unit_pair[u_pos + q] = r | (q << 16) | (sg << 24);
+        unit_pair[u_pos + q] = (int32_t)((unsigned)r | ((unsigned)q << 24) | ((unsigned)(sg - 1) << 28));
         unit_slot[u_pos + q] = (sg > 1 && with_slots) ? s_pos + q * per : -1;
       }
       if (sg > 1) {
-        split_pair[j_pos] = r | (sg << 24);
+        split_pair[j_pos] = (int32_t)((unsigned)r | ((unsigned)(sg - 1) << 28));
         split_slot[j_pos] = with_slots ? s_pos : -1;
         ++j_pos;
         s_pos += sg * per;
@@ -300,9 +312,9 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
   const int pu = blockIdx.x / per, rem = blockIdx.x - pu * per;
   if (pu >= p.split_counts[0]) return;  // the grid covers the largest possible plan
   const int ue = p.unit_pair[pu];
-  const int seg = (ue >> 16) & 0xff, nseg = ue >> 24;
+  const int seg = (int)(((unsigned)ue >> 24) & 15u), nseg = (int)((unsigned)ue >> 28) + 1;
   const int slot = p.unit_slot[pu];     // >= 0: a segment writing fp32 partial sums
-  const int item = p.k_order[ue & 0xffff];
+  const int item = p.k_order[ue & 0xFFFFFF];
   const DkdvItem wi = dkdv_item(p.hm, p.Hq, p.Hkv, p.nKB, item, rem);
   const int mr = wi.mr, kb = wi.kb, b = wi.b, kvh = wi.kvh, h0 = wi.h0, nh = wi.nh;
   const bool direct = p.hm.writers == 1;
@@ -850,8 +862,8 @@ __global__ __launch_bounds__(256) void k_dkdv_reduce(ReduceParams p) {
   const int j = blockIdx.x / per, rem = blockIdx.x - j * per;
   if (j >= p.split_counts[1]) return;
   const int sp = p.split_pair[j];
-  const int nseg = sp >> 24, base = p.split_slot[j];
-  const DkdvItem wi = dkdv_item(p.hm, p.Hq, p.Hkv, p.nKB, p.k_order[sp & 0xffff], rem);
+  const int nseg = (int)((unsigned)sp >> 28) + 1, base = p.split_slot[j];
+  const DkdvItem wi = dkdv_item(p.hm, p.Hq, p.Hkv, p.nKB, p.k_order[sp & 0xFFFFFF], rem);
   const size_t half = (size_t)p.nslots * BK * D;
   const size_t kvbase = (size_t)(wi.b * p.Hkv + wi.kvh) * p.Nk * D;
   const uint32_t head_bytes = (uint32_t)p.Nk * D * 2;

@@ -205,17 +205,29 @@ __global__ __launch_bounds__(256) void k_classify_k(const int32_t* __restrict__ 
 }
 
 // ---- A4: longest-processing-time-first order ----------------------------------
-// Keys (~cost << 32 | index) sorted ascending = cost descending, index ascending.
+// Keys (~cost << 32 | index) sorted ascending = cost descending, index ascending.  Up to
+// kMaxSortItems keys sort in one workgroup's LDS (bitonic network).  Longer lists are
+// sorted in chunks of kMaxSortItems (one workgroup each) and then merged pairwise, run
+// length doubling per pass: keys are unique (they contain the index), so an element's
+// place in the merged run is its place in its own run plus the number of keys below it in
+// the other run (a binary search), and every element is placed independently.
+__device__ __forceinline__ unsigned long long lpt_key(const int32_t* __restrict__ cost, int i) {
+  return ((unsigned long long)(0xFFFFFFFFu - (unsigned)cost[i]) << 32) | (unsigned)i;
+}
+
+// Sorts keys [c0, c0 + n) (n <= kMaxSortItems) of chunk blockIdx.x; writes the item
+// indices to `order` (single chunk) or the sorted keys to `run` (chunks to be merged).
 __global__ __launch_bounds__(1024) void k_lpt_sort(const int32_t* __restrict__ cost,
-                                                   int32_t* __restrict__ order, int count) {
+                                                   int32_t* __restrict__ order,
+                                                   unsigned long long* __restrict__ run,
+                                                   int count) {
   __shared__ unsigned long long keys[kMaxSortItems];
   const int tid = threadIdx.x;
+  const int c0 = blockIdx.x * kMaxSortItems;
+  const int n = min(kMaxSortItems, count - c0);
   int P = 1;
-  while (P < count) P <<= 1;
-  for (int i = tid; i < P; i += 1024)
-    keys[i] = i < count ? ((unsigned long long)(0xFFFFFFFFu - (unsigned)cost[i]) << 32) |
-                              (unsigned)i
-                        : ~0ull;
+  while (P < n) P <<= 1;
+  for (int i = tid; i < P; i += 1024) keys[i] = i < n ? lpt_key(cost, c0 + i) : ~0ull;
   __syncthreads();
   // bitonic network; each thread takes compare-exchange pairs (i, i + j) directly, so no
   // lane idles on the half of the indices that are second members of a pair
@@ -231,7 +243,40 @@ __global__ __launch_bounds__(1024) void k_lpt_sort(const int32_t* __restrict__ c
       __syncthreads();
     }
   }
-  for (int i = tid; i < count; i += 1024) order[i] = (int32_t)(keys[i] & 0xFFFFFFFFull);
+  if (run) {
+    for (int i = tid; i < n; i += 1024) run[c0 + i] = keys[i];
+  } else {
+    for (int i = tid; i < n; i += 1024) order[i] = (int32_t)(keys[i] & 0xFFFFFFFFull);
+  }
+}
+
+// Number of keys in sorted a[0, n) below x.
+__device__ __forceinline__ int rank_below(const unsigned long long* __restrict__ a, int n,
+                                          unsigned long long x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// One merge pass: runs of `len` sorted keys in src, merged pairwise into dst; the last
+// pass writes the item indices to `order` instead.
+__global__ __launch_bounds__(256) void k_lpt_merge(const unsigned long long* __restrict__ src,
+                                                   unsigned long long* __restrict__ dst,
+                                                   int32_t* __restrict__ order, int count,
+                                                   int len) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < count; i += gridDim.x * 256) {
+    const int base = (i / (2 * len)) * (2 * len);
+    const int na = min(len, count - base);
+    const int nb = max(0, min(len, count - base - len));
+    const unsigned long long x = src[i];
+    const int pos = i - base < len ? (i - base) + rank_below(src + base + len, nb, x)
+                                   : (i - base - len) + rank_below(src + base, na, x);
+    if (order) order[base + pos] = (int32_t)(x & 0xFFFFFFFFull);
+    else dst[base + pos] = x;
+  }
 }
 
 // ---- Dense expansion through the kernels' own predicate (checking only) ----------
@@ -291,9 +336,30 @@ hipError_t launch_classify(const MaskArgs& m, int B, int Nq, int Nk, int bq, int
   return hipGetLastError();
 }
 
-hipError_t launch_lpt_sort(const int32_t* cost, int32_t* order, int count, hipStream_t s) {
+size_t lpt_sort_scratch_bytes(int64_t count) {
+  return count > kMaxSortItems ? 2 * (size_t)count * sizeof(unsigned long long) : 0;
+}
+
+hipError_t launch_lpt_sort(const int32_t* cost, int32_t* order, int count, void* scratch,
+                           hipStream_t s) {
   if (count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_lpt_sort, dim3(1), dim3(1024), 0, s, cost, order, count);
+  if (count <= kMaxSortItems) {
+    hipLaunchKernelGGL(k_lpt_sort, dim3(1), dim3(1024), 0, s, cost, order,
+                       (unsigned long long*)nullptr, count);
+    return hipGetLastError();
+  }
+  unsigned long long* a = static_cast<unsigned long long*>(scratch);
+  unsigned long long* b = a + count;
+  const int chunks = (count + kMaxSortItems - 1) / kMaxSortItems;
+  hipLaunchKernelGGL(k_lpt_sort, dim3(chunks), dim3(1024), 0, s, cost, (int32_t*)nullptr, a,
+                     count);
+  const unsigned grid = (unsigned)min((count + 255) / 256, 4096);
+  for (int len = kMaxSortItems; len < count; len *= 2) {
+    const bool last = 2 * (int64_t)len >= count;
+    hipLaunchKernelGGL(k_lpt_merge, dim3(grid), dim3(256), 0, s, a, b, last ? order : nullptr,
+                       count, len);
+    unsigned long long* t = a; a = b; b = t;
+  }
   return hipGetLastError();
 }
 

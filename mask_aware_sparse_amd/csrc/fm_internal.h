@@ -27,8 +27,11 @@ constexpr int kBwdHeadChunk = 4;
 // kernels against an unmasked one on identical work (1.11 fwd, 1.08 dQ, 1.05 dK/dV).
 constexpr int kAlphaPartial = 11;
 constexpr int kAlphaUnmasked = 10;
-// The LPT sort runs in one workgroup with 64-bit keys in LDS.
+// The LPT sort: up to kMaxSortItems 64-bit keys in one workgroup's LDS; longer lists in
+// chunks of that size, merged pass by pass through a scratch buffer of
+// lpt_sort_scratch_bytes(count) bytes.  Lists are limited to kMaxWorkItems entries.
 constexpr int kMaxSortItems = 8192;
+constexpr int64_t kMaxWorkItems = 1 << 24;
 // Splitting of long dK/dV work items.  A (mask row, KV block) pair whose queue is long
 // against the average load per workgroup slot is cut into at most kSplitMaxSegs segments
 // of its queue; at most kSplitExtraUnits extra workgroups are added per launch.  Where the
@@ -106,7 +109,9 @@ struct TileOut {
 // Nq query rows (Q-blocks of bq), Nk keys (KV blocks of bk); B mask rows.
 hipError_t launch_classify(const MaskArgs& m, int B, int Nq, int Nk, int bq, int bk,
                            const TileOut& out, hipStream_t s);
-hipError_t launch_lpt_sort(const int32_t* cost, int32_t* order, int count, hipStream_t s);
+size_t lpt_sort_scratch_bytes(int64_t count);
+hipError_t launch_lpt_sort(const int32_t* cost, int32_t* order, int count, void* scratch,
+                           hipStream_t s);
 hipError_t launch_expand_mask(const MaskArgs& m, int b, int Nk, int row0, int row1,
                               uint8_t* dense, hipStream_t s);
 
@@ -182,7 +187,7 @@ struct BwdArgs {
 // Extra pair units of the split plan for `per` workgroups per pair, and the partial slots
 // it can use (each split pair takes s >= 2 segments of `per` slots, s - 1 of them extra).
 inline int split_extra_pairs(int per, int64_t pair_units) {
-  if (per <= 0) return 0;
+  if (per <= 0 || pair_units > kMaxSortItems) return 0;  // the plan runs in one workgroup
   int64_t e = kSplitExtraUnits / per;
   const int64_t cap = pair_units;  // never more than doubles the work units
   return (int)(e < cap ? e : cap);

@@ -107,7 +107,7 @@ def test_workspace_sizes():
     (dict(d=96), UNSUPPORTED),
     (dict(d=256), UNSUPPORTED),
     (dict(N=1 << 30), UNSUPPORTED),
-    (dict(B=65, N=16384), UNSUPPORTED),     # more than 8192 Q-blocks to sort
+    (dict(B=1100, N=1 << 21), UNSUPPORTED),  # more than 2^24 KV blocks to sort
 ])
 def test_invalid_problems(bad, code):
     p = prob(**bad)
@@ -265,12 +265,12 @@ def test_mask_heads_workspace_sizes():
 
 
 def test_mask_heads_sort_limit():
-    # 8192 work blocks per sort: B * H_m * nKB at the forward's 64-key blocks
+    # at most 2^24 work blocks per sorted list: B * H_m * nKB at the forward's 64-key blocks
     n = ctypes.c_size_t()
-    ok = prob_hm(64, 8, 64, N=8192)              # 64 sets * 128 KV blocks = 8192
+    ok = prob_hm(64, 8, 64, N=1 << 22)            # 64 sets * 65536 KV blocks = 2^22
     assert fm.library().fm_workspace_size(ctypes.byref(ok), fm.OP_FWD, 0, 0,
                                           ctypes.byref(n)) == FM_OK
-    big = prob_hm(64, 8, 64, N=8192 + 64)
+    big = prob_hm(64, 8, 64, B=5, N=1 << 22)      # 5 * 2^22 > 2^24
     assert fm.library().fm_workspace_size(ctypes.byref(big), fm.OP_FWD, 0, 0,
                                           ctypes.byref(n)) == UNSUPPORTED
 
