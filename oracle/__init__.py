@@ -13,7 +13,9 @@ Contents and the passage each part follows:
                 two-vector visible-interval form and its closed-form encoders
                 (FlashMask Guide, "Mathematical Formalization of Column-Wise
                 Sparsity"); the multi-interval form, up to 4 active row intervals
-                per column (same Guide, "Multi-Interval Sparse Masks").
+                per column (same Guide, "Multi-Interval Sparse Masks"); the block-sparse
+                form, a grid of 128 x 128 blocks each visible or hidden (the
+                block-sparse family the FlashMask-3 page lists).
   attention.py  masked softmax attention forward (plain two-pass softmax) and its
                 analytic backward (Flash MSA guide, "Why Standard Attention Broke"
                 and "The Backward Pass: The Real Beast"; FlashMask Guide, dense
@@ -42,12 +44,14 @@ have no printed values on the pages: beyond those pins they are parity unpinned.
 """
 from .mask import (masked_rows, dense_mask, visible_interval_to_vectors,
                    encode_causal, encode_packed, encode_dpo, hidden_multi_rows,
-                   dense_mask_multi)
+                   dense_mask_multi, hidden_block_rows, dense_mask_blocks, BLOCK)
 from .attention import (attention_fwd, attention_bwd, attention_rows, attention_cols,
                         attention_fwd_bwd, attention_fwd_multi, attention_fwd_bwd_multi,
-                        attention_rows_multi, attention_cols_multi)
+                        attention_rows_multi, attention_cols_multi, attention_fwd_blocks,
+                        attention_fwd_bwd_blocks, attention_rows_blocks, attention_cols_blocks)
 from .tiles import (block_minmax, classify, tile_truth, queues, tile_costs, lpt_order,
-                    block_minmax_multi, classify_multi, tile_truth_multi,
+                    block_minmax_multi, classify_multi, tile_truth_multi, classify_blocks,
+                    tile_truth_blocks,
                     ALPHA_PARTIAL, ALPHA_UNMASKED)
 from .schedule import list_schedule, lower_bound, brute_force_optimum
 from .localize import rank_rows, localize, localize_max_form, localize_vectors
@@ -56,6 +60,9 @@ from . import ipo
 __all__ = [
     "masked_rows", "dense_mask", "visible_interval_to_vectors", "encode_causal",
     "encode_packed", "encode_dpo", "hidden_multi_rows", "dense_mask_multi",
+    "hidden_block_rows", "dense_mask_blocks", "BLOCK", "attention_fwd_blocks",
+    "attention_fwd_bwd_blocks", "attention_rows_blocks", "attention_cols_blocks",
+    "classify_blocks", "tile_truth_blocks",
     "attention_fwd", "attention_bwd", "attention_rows", "attention_cols",
     "attention_fwd_bwd", "attention_fwd_multi", "attention_fwd_bwd_multi",
     "attention_rows_multi", "attention_cols_multi", "block_minmax", "classify",

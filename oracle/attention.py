@@ -36,7 +36,7 @@ least one of its rows can see, which is exact because hidden columns contribute 
 """
 import numpy as np
 
-from .mask import hidden_multi_rows, masked_rows
+from .mask import hidden_block_rows, hidden_multi_rows, masked_rows
 
 
 class _FourVectors:
@@ -71,6 +71,19 @@ def _f64(x):
 
 def _scale(d, scale):
     return 1.0 / np.sqrt(d) if scale is None or scale <= 0 else float(scale)
+
+
+class _Blocks:
+    """The block-sparse form of one (b, h): visible iff its 128 x 128 block is."""
+
+    def __init__(self, blocks, nk):
+        self.blk, self.nk = blocks, nk
+
+    def rows(self, r0, r1):
+        return hidden_block_rows(self.blk, r0, r1, self.nk)
+
+    def column(self, c, n):
+        return hidden_block_rows(self.blk, 0, n, self.nk)[:, c]
 
 
 def _row_block(qh, kh, vh, mask, r0, r1, scale, dOh=None):
@@ -276,6 +289,44 @@ def attention_cols(q, k, v, do, lts, lte, uts, ute, b, kv, cols, scale=None, row
     the whole row), so this is cheap only where the selected columns are seen by
     few rows."""
     of = _vectors_of((lts, lte, uts, ute), q.shape[0], q.shape[1], k.shape[2])
+    return _cols(q, k, v, do, of, b, kv, cols, scale, row_block)
+
+
+def _blocks_of(blocks, B, Hq, Nq, Nk):
+    """Mask getter (b, h) -> _Blocks for a block grid [B][nQB][nKB] or [B][H_m][nQB][nKB]
+    (nQB = ceil(N_q / 128), nKB = ceil(N_k / 128))."""
+    from .mask import BLOCK
+    g = np.asarray(blocks)
+    nqb, nkb = -(-Nq // BLOCK), -(-Nk // BLOCK)
+    if g.ndim == 3:
+        assert g.shape == (B, nqb, nkb)
+        return lambda b, h: _Blocks(g[b], Nk)
+    assert g.ndim == 4 and g.shape[0] == B and g.shape[2:] == (nqb, nkb) and Hq % g.shape[1] == 0
+    per = Hq // g.shape[1]
+    return lambda b, h: _Blocks(g[b, h // per], Nk)
+
+
+# ---- block-sparse form (blocks [B][nQB][nKB] or [B][H_m][nQB][nKB], 128 x 128 blocks) -----
+
+def attention_fwd_blocks(q, k, v, blocks, scale=None, row_block=256):
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    of = _blocks_of(blocks, q.shape[0], q.shape[1], q.shape[2], k.shape[2])
+    return _fwd(q, k, v, of, scale, row_block)
+
+
+def attention_fwd_bwd_blocks(q, k, v, do, blocks, scale=None, row_block=256):
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    of = _blocks_of(blocks, q.shape[0], q.shape[1], q.shape[2], k.shape[2])
+    return _fwd_bwd(q, k, v, do, of, scale, row_block)
+
+
+def attention_rows_blocks(q, k, v, do, blocks, b, h, rows, scale=None):
+    mk = _blocks_of(blocks, q.shape[0], q.shape[1], q.shape[2], k.shape[2])(b, h)
+    return _rows(q, k, v, do, mk, b, h, rows, scale)
+
+
+def attention_cols_blocks(q, k, v, do, blocks, b, kv, cols, scale=None, row_block=256):
+    of = _blocks_of(blocks, q.shape[0], q.shape[1], q.shape[2], k.shape[2])
     return _cols(q, k, v, do, of, b, kv, cols, scale, row_block)
 
 

@@ -95,3 +95,23 @@ def encode_dpo(prompt, chosen, rejected):
     fme[prompt:prompt + chosen] = prompt + chosen - 1
     fme[prompt + chosen:] = n - 1
     return fms, fme
+
+
+BLOCK = 128  # block edge of the block-sparse form
+
+
+def hidden_block_rows(blocks, r0, r1, nk):
+    """Block-sparse form (the block-sparse family the FlashMask-3 page lists among packed
+    long-context masks): a grid of BLOCK x BLOCK blocks, blocks[qb][kb] = 1 if every
+    (row, key) of the block is visible, 0 if every one is hidden; the last block row and
+    column may be cut by N_q and N_k.  Returns the boolean [r1-r0][N_k] block of the
+    dense mask, True = hidden."""
+    blocks = np.asarray(blocks)
+    qb = np.arange(r0, r1) // BLOCK
+    kb = np.arange(nk) // BLOCK
+    return blocks[qb][:, kb] == 0
+
+
+def dense_mask_blocks(blocks, nq, nk):
+    """Full dense mask (True = hidden) of the block-sparse form, [N_q][N_k]."""
+    return hidden_block_rows(blocks, 0, nq, nk)

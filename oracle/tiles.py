@@ -23,7 +23,7 @@ both intervals cover it together (the rule is conservative, never unsound).
 """
 import numpy as np
 
-from .mask import hidden_multi_rows, masked_rows
+from .mask import BLOCK, hidden_block_rows, hidden_multi_rows, masked_rows
 
 SKIP, PARTIAL, UNMASKED = 0, 1, 2
 # alpha_p : alpha_u in integer units.  The FlashMask-3 page (§3.3) calls its 1.3 : 1
@@ -155,6 +155,41 @@ def tile_truth_multi(starts, ends, bq, bk, nq=None):
             hid = hidden_multi_rows(starts[r], ends[r], q0, q1)
             for kb in range(nkb):
                 t = hid[:, kb * bk:min(kb * bk + bk, Nk)]
+                out[r, qb, kb] = SKIP if t.all() else (UNMASKED if not t.any() else PARTIAL)
+    return out
+
+
+def classify_blocks(blocks, bq, bk, nq, nk):
+    """Tile class [R][nQB][nKB] for the block-sparse form (blocks [R][ceil(nq/128)]
+    [ceil(nk/128)]): a tile is skipped when every block it overlaps is hidden, unmasked
+    when every one is visible, and partial otherwise (a tile that straddles blocks of
+    both kinds).  Exact by construction: blocks are uniformly visible or hidden."""
+    blocks = np.asarray(blocks)
+    R = blocks.shape[0]
+    nqb, nkb = _nblocks(nq, bq), _nblocks(nk, bk)
+    cls = np.zeros((R, nqb, nkb), dtype=np.uint8)
+    for r in range(R):
+        for qb in range(nqb):
+            b0, b1 = qb * bq // BLOCK, (min(qb * bq + bq, nq) - 1) // BLOCK + 1
+            for kb in range(nkb):
+                c0, c1 = kb * bk // BLOCK, (min(kb * bk + bk, nk) - 1) // BLOCK + 1
+                sub = blocks[r, b0:b1, c0:c1]
+                cls[r, qb, kb] = SKIP if not sub.any() else (UNMASKED if sub.all() else PARTIAL)
+    return cls
+
+
+def tile_truth_blocks(blocks, bq, bk, nq, nk):
+    """Brute force from the dense block-sparse mask: 0 all hidden, 2 none, 1 else."""
+    blocks = np.asarray(blocks)
+    R = blocks.shape[0]
+    nqb, nkb = _nblocks(nq, bq), _nblocks(nk, bk)
+    out = np.zeros((R, nqb, nkb), dtype=np.uint8)
+    for r in range(R):
+        for qb in range(nqb):
+            q0, q1 = qb * bq, min(qb * bq + bq, nq)
+            hid = hidden_block_rows(blocks[r], q0, q1, nk)
+            for kb in range(nkb):
+                t = hid[:, kb * bk:min(kb * bk + bk, nk)]
                 out[r, qb, kb] = SKIP if t.all() else (UNMASKED if not t.any() else PARTIAL)
     return out
 

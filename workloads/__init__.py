@@ -80,6 +80,28 @@ class MultiWorkload:
         return 1 if self.starts.ndim == 3 else self.starts.shape[1]
 
 
+@dataclass
+class BlockWorkload:
+    """Block-sparse form: uint8 blocks [B][nQB][nKB] (or [B][H_m][nQB][nKB]) over 128 x 128
+    blocks, 1 = visible, 0 = hidden; nQB = ceil(N / 128)."""
+    name: str
+    batch: int
+    heads_q: int
+    heads_kv: int
+    seqlen: int
+    head_dim: int
+    blocks: np.ndarray
+    seed: int
+    info: dict = field(default_factory=dict)
+
+    @property
+    def mask_heads(self) -> int:
+        return 1 if self.blocks.ndim == 3 else self.blocks.shape[1]
+
+
+BLOCK = 128
+
+
 def _empty_vectors(batch: int, n: int):
     lts = np.full((batch, n), n, dtype=np.int64)
     lte = np.full((batch, n), n, dtype=np.int64)
@@ -329,6 +351,41 @@ def block_sparse_window(seed: int = 0, n: int = 32768, batch: int = 1, heads_q: 
                           "sinks": sinks})
 
 
+def random_blocks(seed: int, n: int, batch: int = 1, heads_q: int = 1, heads_kv: int = 1,
+                  density: float = 0.3, mask_heads: int = 0) -> BlockWorkload:
+    """Adversarial block grids: every 128 x 128 block visible with probability `density`,
+    including whole block rows that see nothing (ragged last row and column when N is not a
+    multiple of 128)."""
+    rng = np.random.default_rng(seed)
+    nb = -(-n // BLOCK)
+    shape = ((batch,) if mask_heads <= 0 else (batch, mask_heads)) + (nb, nb)
+    blocks = (rng.random(shape) < density).astype(np.uint8)
+    return BlockWorkload("random_blocks", batch, heads_q, heads_kv, n, HEAD_DIM,
+                         np.ascontiguousarray(blocks), seed, {"density": density})
+
+
+def bigbird_blocks(seed: int = 0, n: int = 32768, batch: int = 1, heads_q: int = 32,
+                   heads_kv: int = 8, window: int = 1, globals_: int = 1,
+                   randoms: int = 3) -> BlockWorkload:
+    """Block-sparse pattern of the BigBird kind on 128 x 128 blocks: each block row sees the
+    blocks within `window` of the diagonal, the first `globals_` block columns, and
+    `randoms` further blocks drawn per row; the first `globals_` block rows see every
+    block."""
+    rng = np.random.default_rng(seed)
+    nb = -(-n // BLOCK)
+    blocks = np.zeros((batch, nb, nb), dtype=np.uint8)
+    for b in range(batch):
+        for qb in range(nb):
+            blocks[b, qb, max(0, qb - window):min(nb, qb + window + 1)] = 1
+            blocks[b, qb, :globals_] = 1
+            rest = np.nonzero(blocks[b, qb] == 0)[0]
+            pick = rng.choice(rest, size=min(randoms, len(rest)), replace=False)
+            blocks[b, qb, pick] = 1
+        blocks[b, :globals_, :] = 1
+    return BlockWorkload("bigbird_blocks", batch, heads_q, heads_kv, n, HEAD_DIM, blocks, seed,
+                         {"window": window, "globals": globals_, "randoms": randoms})
+
+
 # The five benchmark workloads, in order.  Shapes and mask families follow the
 # synthetic stand-ins for the mask families the FlashMask-3 page benchmarks.
 CONFIGS = {
@@ -348,6 +405,8 @@ VARIANTS = {
     "v2_block_sparse_window_32k": lambda seed=0: block_sparse_window(seed),
     # head dimension 64: the prefix-LM document workload (B=4, 32/8 heads, N=8192) at d=64
     "v3_prefix_lm_doc_8k_d64": lambda seed=0: with_head_dim(prefix_lm_doc(seed), 64),
+    # block-sparse masks: BigBird-style 128 x 128 block grid (window, global, random blocks)
+    "v4_bigbird_blocks_32k": lambda seed=0: bigbird_blocks(seed),
 }
 VARIANT_NAMES = list(VARIANTS)
 
@@ -382,8 +441,10 @@ def make_tensors(w: Workload, seed: int | None = None, device: str = "cpu",
 
 
 def mask_tensors(w, device: str = "cpu"):
-    """The mask as int32 tensors: the four vectors of a Workload, or (starts, ends) of a
-    MultiWorkload."""
+    """The mask as tensors: the four int32 vectors of a Workload, (starts, ends) of a
+    MultiWorkload, or (blocks,) (uint8) of a BlockWorkload."""
     import torch
+    if isinstance(w, BlockWorkload):
+        return (torch.from_numpy(np.ascontiguousarray(w.blocks)).to(device),)
     arrs = w.intervals() if isinstance(w, MultiWorkload) else w.vectors()
     return tuple(torch.from_numpy(np.ascontiguousarray(x)).to(device) for x in arrs)
