@@ -92,6 +92,18 @@ def attended_pairs_multi(w):
     return int(covered.sum()) * (w.heads_q // st.shape[1])
 
 
+def attended_pairs_blocks(w):
+    """Attended pairs of a block-sparse workload: the area of every visible 128 x 128 block
+    (cut at N), times the query heads that use the grid."""
+    g = np.asarray(w.blocks, dtype=np.int64)
+    if g.ndim == 3:
+        g = g[:, None]
+    n, blk = w.seqlen, 128
+    edge = np.minimum(np.arange(g.shape[-1]) * blk + blk, n) - np.arange(g.shape[-1]) * blk
+    area = int(np.einsum('bmij,i,j->', g, edge[:g.shape[-2]], edge))
+    return area * (w.heads_q // g.shape[1])
+
+
 def head_vectors(w, b, h):
     """The four vectors [1][N] query head h of batch row b uses."""
     if w.lts.ndim == 2:
@@ -356,7 +368,16 @@ def cpu_baseline(w, q, k, v, do, budget_s):
             kvh = h // g
             f = lambda t, hh: t[b:b + 1, hh:hh + 1].float().cpu().numpy().astype(np.float64)
             args = (f(q, h), f(k, kvh), f(v, kvh), f(do, h))
-            if isinstance(w, workloads.MultiWorkload):
+            if isinstance(w, workloads.BlockWorkload):
+                m = h // (w.heads_q // w.mask_heads)
+                grid = w.blocks[b:b + 1] if w.blocks.ndim == 3 else w.blocks[b:b + 1, m]
+                t0 = time.perf_counter()
+                oracle.attention_fwd_bwd_blocks(*args, grid)
+                t_total += time.perf_counter() - t0
+                one = workloads.BlockWorkload(w.name, 1, 1, 1, w.seqlen, w.head_dim,
+                                              np.ascontiguousarray(grid), w.seed)
+                pairs += attended_pairs_blocks(one)
+            elif isinstance(w, workloads.MultiWorkload):
                 m = h // (w.heads_q // w.mask_heads)
                 st, en = ((x[b:b + 1] if x.ndim == 3 else x[b:b + 1, m]) for x in w.intervals())
                 t0 = time.perf_counter()
@@ -443,10 +464,12 @@ def main():
     ws_b = torch.empty(fm.workspace_size(w.batch, w.heads_q, w.heads_kv, w.seqlen, fm.OP_BWD,
                                          mask_heads=w.mask_heads), dtype=torch.uint8, device=dev)
     multi = isinstance(w, workloads.MultiWorkload)
-    A = attended_pairs_multi(w) if multi else attended_pairs(w)
+    blocks = isinstance(w, workloads.BlockWorkload)
+    A = attended_pairs_blocks(w) if blocks else (attended_pairs_multi(w) if multi
+                                                 else attended_pairs(w))
     d = w.head_dim
-    attn_fwd = fm.attn_fwd_multi if multi else fm.attn_fwd
-    attn_bwd = fm.attn_bwd_multi if multi else fm.attn_bwd
+    attn_fwd = fm.attn_fwd_blocks if blocks else (fm.attn_fwd_multi if multi else fm.attn_fwd)
+    attn_bwd = fm.attn_bwd_blocks if blocks else (fm.attn_bwd_multi if multi else fm.attn_bwd)
 
     # per instrumented step: 0 start, 1/2 fwd kernel, 8 between the calls, 3/4 dK/dV
     # kernel, 6/7 dQ kernel, 5 end (all on the current stream, which the library launches
@@ -514,7 +537,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": w.batch, "heads_q": w.heads_q,
                    "heads_kv": w.heads_kv, "mask_heads": w.mask_heads,
-                   "mask_intervals": w.n_intervals if multi else None, "seq_len": w.seqlen,
+                   "mask_intervals": w.n_intervals if multi else None,
+                   "mask_blocks": "128x128" if blocks else None, "seq_len": w.seqlen,
                    "head_dim": d, "attended_pairs": A, "seed": args.seed},
         "pct_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
         "kernels": {kname: {"ms": round(t, 4), "algorithmic_tflops": round(tflops[kname], 2)}

@@ -253,6 +253,35 @@ fm_status fm_localize_mask_multi(const fm_problem* p, const fm_mask_multi* globa
                                  const int32_t* offsets, int32_t n_chunks, int32_t chunk_len,
                                  int32_t* local_start, int32_t* local_end, void* stream);
 
+/* ---- Block-sparse masks ------------------------------------------------------------------
+ * The block-sparse family (listed on the FlashMask-3 page among the masks of packed
+ * long-context batches): a grid of 128 x 128 blocks over (query rows, keys), each block
+ * wholly visible (1) or wholly hidden (0); the last block row and column may be cut by N_q
+ * and N_k.  blocks: uint8 [B][H_m][ceil(N_q/128)][ceil(N_k/128)] in device memory (H_m =
+ * p->mask_heads, as for the other forms).  Every tile of the attention kernels lies inside
+ * one block, so tiles are only skipped or unmasked (keys past N_k stay hidden); the
+ * classifier's tile of up to 256 x 256 is partial when it straddles blocks of both kinds.
+ * The _blocks entry points behave exactly as their four-vector counterparts (same problem,
+ * arguments, workspace sizes, outputs and errors), except that fm_tiles.block_minmax is not
+ * written (it must still be a valid pointer) and a null `blocks` with a non-empty grid is
+ * FM_ERR_INVALID_ARG.  There is no localization for this form. */
+typedef struct {
+  const uint8_t* blocks;
+} fm_mask_blocks;
+
+fm_status fm_classify_tiles_blocks(const fm_problem* p, const fm_mask_blocks* m, int32_t block_q,
+                                   int32_t block_k, const fm_tiles* out, void* ws,
+                                   size_t ws_bytes, void* stream);
+fm_status fm_attn_fwd_blocks(const fm_problem* p, const void* q, const void* k, const void* v,
+                             const fm_mask_blocks* m, void* o, float* lse, void* ws,
+                             size_t ws_bytes, void* stream, const fm_kernel_events* events);
+fm_status fm_attn_bwd_blocks(const fm_problem* p, const void* q, const void* k, const void* v,
+                             const void* o, const float* lse, const void* dout,
+                             const fm_mask_blocks* m, void* dq, void* dk, void* dv, void* ws,
+                             size_t ws_bytes, void* stream, const fm_kernel_events* events);
+fm_status fm_debug_expand_mask_blocks(const fm_problem* p, const fm_mask_blocks* m, int32_t b,
+                                      int32_t row0, int32_t row1, uint8_t* dense, void* stream);
+
 /* Static description of a status code. */
 const char* fm_status_string(fm_status s);
 

@@ -65,6 +65,10 @@ class MaskMulti(ctypes.Structure):
                 ("n_intervals", ctypes.c_int32)]
 
 
+class MaskBlocks(ctypes.Structure):
+    _fields_ = [("blocks", ctypes.c_void_p)]
+
+
 class KernelEvents(ctypes.Structure):
     _fields_ = [("start", ctypes.c_void_p), ("stop", ctypes.c_void_p),
                 ("start2", ctypes.c_void_p), ("stop2", ctypes.c_void_p)]
@@ -93,6 +97,7 @@ def library():
         PP, PM, PT = ctypes.POINTER(Problem), ctypes.POINTER(Mask), ctypes.POINTER(Tiles)
         PE = ctypes.POINTER(KernelEvents)
         PX = ctypes.POINTER(MaskMulti)
+        PB = ctypes.POINTER(MaskBlocks)
         sig = {
             "fm_status_string": ([_STATUS], ctypes.c_char_p),
             "fm_tile_shape": ([_STATUS, ctypes.POINTER(ctypes.c_int32),
@@ -118,6 +123,14 @@ def library():
                                             ctypes.c_int32, _P, _P], _STATUS),
             "fm_localize_mask_multi": ([PP, PX, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P],
                                        _STATUS),
+            "fm_classify_tiles_blocks": ([PP, PB, ctypes.c_int32, ctypes.c_int32, PT, _P,
+                                          ctypes.c_size_t, _P], _STATUS),
+            "fm_attn_fwd_blocks": ([PP, _P, _P, _P, PB, _P, _P, _P, ctypes.c_size_t, _P, PE],
+                                   _STATUS),
+            "fm_attn_bwd_blocks": ([PP, _P, _P, _P, _P, _P, _P, PB, _P, _P, _P, _P,
+                                    ctypes.c_size_t, _P, PE], _STATUS),
+            "fm_debug_expand_mask_blocks": ([PP, PB, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32, _P, _P], _STATUS),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -237,6 +250,26 @@ def _mask_multi(starts, ends):
     return MaskMulti(starts.data_ptr(), ends.data_ptr(), int(M)), B, Hm, M, N
 
 
+BLOCK = 128  # block edge of the block-sparse form
+
+
+def _mask_blocks(blocks, seqlen_q, seqlen_k):
+    """(MaskBlocks, B, H_m) for a block grid [B][nQB][nKB] or [B][H_m][nQB][nKB] of uint8
+    (1 = visible) over 128 x 128 blocks, checked against ceil(N / 128)."""
+    if blocks.dtype != torch.uint8 or not blocks.is_contiguous():
+        raise ValueError("blocks must be a contiguous uint8 tensor")
+    nqb, nkb = -(-int(seqlen_q) // BLOCK), -(-int(seqlen_k) // BLOCK)
+    if blocks.dim() == 3:
+        B, Hm = blocks.shape[0], 1
+    elif blocks.dim() == 4:
+        B, Hm = blocks.shape[0], blocks.shape[1]
+    else:
+        raise ValueError("blocks must be [B][nQB][nKB] or [B][H_m][nQB][nKB]")
+    if tuple(blocks.shape[-2:]) != (nqb, nkb):
+        raise ValueError(f"blocks must have {nqb} x {nkb} blocks for N_q={seqlen_q}, N_k={seqlen_k}")
+    return MaskBlocks(blocks.data_ptr()), B, Hm
+
+
 def _classify(fn, m, B, Hm, Nk, block_q, block_k, heads_q, heads_kv, stream, out, ws, seqlen_q,
               width, dev):
     if Hm > 1 and heads_q == 1 and heads_kv == 1:
@@ -277,6 +310,15 @@ def classify_tiles_multi(starts, ends, block_q, block_k, heads_q=1, heads_kv=1, 
     m, B, Hm, M, Nk = _mask_multi(starts, ends)
     return _classify(library().fm_classify_tiles_multi, m, B, Hm, Nk, block_q, block_k, heads_q,
                      heads_kv, stream, out, ws, seqlen_q, 4 * M, starts.device)
+
+
+def classify_tiles_blocks(blocks, block_q, block_k, seqlen_q, seqlen_k, heads_q=1, heads_kv=1,
+                          stream=None, out=None, ws=None):
+    """fm_classify_tiles_blocks for a block grid (see _mask_blocks); block_minmax is not
+    written."""
+    m, B, Hm = _mask_blocks(blocks, seqlen_q, seqlen_k)
+    return _classify(library().fm_classify_tiles_blocks, m, B, Hm, int(seqlen_k), block_q,
+                     block_k, heads_q, heads_kv, stream, out, ws, int(seqlen_q), 8, blocks.device)
 
 
 def _tile_buffers(B, N, nqb, nkb, dev, width=8):
@@ -377,6 +419,23 @@ def attn_fwd_multi(q, k, v, starts, ends, scale=None, ws=None, out=None, lse=Non
                 stream, events)
 
 
+def attn_fwd_blocks(q, k, v, blocks, scale=None, ws=None, out=None, lse=None, stream=None,
+                    events=None):
+    """fm_attn_fwd_blocks: as attn_fwd with a block-sparse mask, a uint8 grid [B][nQB][nKB]
+    or [B][H_m][nQB][nKB] over 128 x 128 blocks (1 = visible)."""
+    m, B, Hm = _mask_blocks(blocks, q.shape[2], k.shape[2])
+    return _fwd(library().fm_attn_fwd_blocks, q, k, v, m, (B, Hm, k.shape[2]), scale, ws, out,
+                lse, stream, events)
+
+
+def attn_bwd_blocks(q, k, v, o, lse, dout, blocks, scale=None, ws=None, grads=None, stream=None,
+                    events=None):
+    """fm_attn_bwd_blocks: as attn_bwd with a block-sparse mask."""
+    m, B, Hm = _mask_blocks(blocks, q.shape[2], k.shape[2])
+    return _bwd(library().fm_attn_bwd_blocks, q, k, v, o, lse, dout, m, (B, Hm, k.shape[2]),
+                scale, ws, grads, stream, events)
+
+
 def attn_bwd(q, k, v, o, lse, dout, lts, lte, uts, ute, scale=None, ws=None, grads=None,
              stream=None, events=None):
     """(dQ, dK, dV) in bf16 via fm_attn_bwd.  `events`: optional (start, stop, start2,
@@ -414,6 +473,13 @@ def debug_expand_mask_multi(starts, ends, b, row0, row1, stream=None, seqlen_q=N
     m, B, Hm, M, N = _mask_multi(starts, ends)
     return _expand(library().fm_debug_expand_mask_multi, m, B, Hm, N, b, row0, row1, stream,
                    seqlen_q, starts.device)
+
+
+def debug_expand_mask_blocks(blocks, b, row0, row1, seqlen_q, seqlen_k, stream=None):
+    """Dense expansion of mask row b of a block grid (1 = hidden)."""
+    m, B, Hm = _mask_blocks(blocks, seqlen_q, seqlen_k)
+    return _expand(library().fm_debug_expand_mask_blocks, m, B, Hm, int(seqlen_k), b, row0, row1,
+                   stream, int(seqlen_q), blocks.device)
 
 
 def _offsets(offsets):
@@ -467,6 +533,10 @@ fm_attn_fwd_multi = attn_fwd_multi
 fm_attn_bwd_multi = attn_bwd_multi
 fm_debug_expand_mask_multi = debug_expand_mask_multi
 fm_localize_mask_multi = localize_mask_multi
+fm_classify_tiles_blocks = classify_tiles_blocks
+fm_attn_fwd_blocks = attn_fwd_blocks
+fm_attn_bwd_blocks = attn_bwd_blocks
+fm_debug_expand_mask_blocks = debug_expand_mask_blocks
 fm_status_string = status_string
 
 fm_ipo_balance = ipo_balance

@@ -61,12 +61,35 @@ fm_status check_mask(const fm_problem* p, const fm_mask_multi* m) {
   return FM_OK;
 }
 
-fm::MaskArgs mask_args(const fm_mask* m) {
-  return fm::MaskArgs{fm::MaskPtrs{m->lts, m->lte, m->uts, m->ute}, nullptr, nullptr, 0};
+fm_status check_mask(const fm_problem* p, const fm_mask_blocks* m) {
+  if (!m) return FM_ERR_INVALID_ARG;
+  const int64_t nb = fm::kMaskBlock;
+  if (mask_rows(p) * ((nq_of(p) + nb - 1) / nb) * ((nk_of(p) + nb - 1) / nb) == 0) return FM_OK;
+  if (!m->blocks) return FM_ERR_INVALID_ARG;
+  return FM_OK;
 }
-fm::MaskArgs mask_args(const fm_mask_multi* m) {
+
+fm::MaskArgs mask_args(const fm_problem*, const fm_mask* m) {
+  return fm::MaskArgs{fm::MaskPtrs{m->lts, m->lte, m->uts, m->ute}, nullptr, nullptr, 0,
+                      nullptr, 0};
+}
+fm::MaskArgs mask_args(const fm_problem*, const fm_mask_multi* m) {
   return fm::MaskArgs{fm::MaskPtrs{nullptr, nullptr, nullptr, nullptr}, m->start, m->end,
-                      m->n_intervals};
+                      m->n_intervals, nullptr, 0};
+}
+fm::MaskArgs mask_args(const fm_problem* p, const fm_mask_blocks* m) {
+  return fm::MaskArgs{fm::MaskPtrs{nullptr, nullptr, nullptr, nullptr}, nullptr, nullptr,
+                      fm::kBlocksMode, m->blocks,
+                      (int)((nq_of(p) + fm::kMaskBlock - 1) / fm::kMaskBlock)};
+}
+// The mask the attention kernels read: a block grid runs as all-zero four vectors (the
+// tiles come from the grid's queues; inside a visible block nothing is hidden).
+fm::MaskArgs kernel_mask(const fm::MaskArgs& ma, int32_t* zeros) {
+  if (ma.n != fm::kBlocksMode) return ma;
+  fm::MaskArgs k = ma;
+  k.n = 0;
+  k.v = fm::MaskPtrs{zeros, zeros, zeros, zeros};
+  return k;
 }
 
 float scale_of(const fm_problem* p) {
@@ -100,7 +123,7 @@ ClassifyWs classify_ws(const fm_problem* p, const Blocks& nb) {
   return w;
 }
 
-struct FwdWs { size_t mm, q_queue, q_count, q_cost, q_order, sort, total; };
+struct FwdWs { size_t mm, q_queue, q_count, q_cost, q_order, sort, zeros, total; };
 FwdWs fwd_ws(const fm_problem* p, const Blocks& nb) {
   FwdWs w{};
   const size_t B = mask_rows(p);  // tile structures are per mask row
@@ -111,6 +134,7 @@ FwdWs fwd_ws(const fm_problem* p, const Blocks& nb) {
   w.q_cost = off; off += align_up(B * nb.nQB * 4);
   w.q_order = off; off += align_up(B * nb.nQB * 4);
   w.sort = off; off += align_up(fm::lpt_sort_scratch_bytes((int64_t)B * nb.nQB));
+  w.zeros = off; off += align_up(B * nk_of(p) * 4);  // block-sparse masks only
   w.total = off;
   return w;
 }
@@ -120,7 +144,8 @@ struct BwdWs {
   size_t mm_q, q_queue, q_count, q_cost, q_order;   // dQ (forward) tiles
   size_t lse2, delta, dk, dv;
   size_t unit_pair, unit_slot, split_pair, split_slot, split_counts, partials;  // split plan
-  size_t sort;  // LPT sort scratch (lists longer than one workgroup sorts)
+  size_t sort;   // LPT sort scratch (lists longer than one workgroup sorts)
+  size_t zeros;  // all-zero vectors standing for a block-sparse mask in the kernels
   size_t total;
   bool acc;   // fp32 dK/dV accumulators present
   int extra;  // extra pair units of the split plan
@@ -163,6 +188,7 @@ BwdWs bwd_ws(const fm_problem* p, const Blocks& nk, const Blocks& nq) {
   w.split_counts = off; off += align_up(2 * 4);
   w.sort = off;
   off += align_up(fm::lpt_sort_scratch_bytes(max2((int64_t)B * nk.nKB, (int64_t)B * nq.nQB)));
+  w.zeros = off; off += align_up(B * nk_of(p) * 4);
   if (!w.acc) {
     w.partials = off;
     off += align_up((size_t)2 * fm::split_slots(per, w.extra) * fm::kBwdBlockK * p->head_dim * 4);
@@ -301,7 +327,7 @@ fm_status classify_impl(const fm_problem* p, const MaskT* m, int32_t block_q, in
   t.k_count = out->k_count;
   t.k_cost = at<int32_t>(ws, w.k_cost);
   const int R = (int)mask_rows(p);
-  hipError_t e = fm::launch_classify(mask_args(m), R, nq_of(p), nk_of(p), block_q, block_k, t, s);
+  hipError_t e = fm::launch_classify(mask_args(p, m), R, nq_of(p), nk_of(p), block_q, block_k, t, s);
   void* scr = at<char>(ws, w.sort);
   if (e == hipSuccess) e = fm::launch_lpt_sort(t.q_cost, out->q_order, (int)(R * nb.nQB), scr, s);
   if (e == hipSuccess) e = fm::launch_lpt_sort(t.k_cost, out->k_order, (int)(R * nb.nKB), scr, s);
@@ -327,7 +353,7 @@ fm_status fwd_impl(const fm_problem* p, const void* q, const void* k, const void
   if ((st = check_ws(ws, ws_bytes, w.total)) != FM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  const fm::MaskArgs ma = mask_args(m);
+  const fm::MaskArgs ma = mask_args(p, m);
   fm::TileOut t{};
   t.minmax = at<int32_t>(ws, w.mm);
   t.q_queue = at<int32_t>(ws, w.q_queue);
@@ -339,9 +365,12 @@ fm_status fwd_impl(const fm_problem* p, const void* q, const void* k, const void
   int32_t* order = at<int32_t>(ws, w.q_order);
   if (e == hipSuccess)
     e = fm::launch_lpt_sort(t.q_cost, order, (int)(R * nb.nQB), at<char>(ws, w.sort), s);
+  if (e == hipSuccess && ma.n == fm::kBlocksMode)
+    e = fm::launch_zero_i32(at<int32_t>(ws, w.zeros), (size_t)R * nk_of(p), s);
   if (e == hipSuccess) {
     fm::FwdArgs a{};
-    a.q = q; a.k = k; a.v = v; a.m = ma; a.o = o; a.lse = lse;
+    a.q = q; a.k = k; a.v = v; a.m = kernel_mask(ma, at<int32_t>(ws, w.zeros)); a.o = o;
+    a.lse = lse;
     a.q_queue = t.q_queue; a.q_count = t.q_count; a.q_order = order;
     a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.Hm = hm_of(p);
     a.Nq = nq_of(p); a.Nk = nk_of(p); a.D = p->head_dim;
@@ -375,7 +404,7 @@ fm_status bwd_impl(const fm_problem* p, const void* q, const void* k, const void
   if ((st = check_ws(ws, ws_bytes, w.total)) != FM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  const fm::MaskArgs ma = mask_args(m);
+  const fm::MaskArgs ma = mask_args(p, m);
   fm::TileOut tk{};
   tk.minmax = at<int32_t>(ws, w.mm_k);
   tk.k_queue = at<int32_t>(ws, w.k_queue);
@@ -396,9 +425,12 @@ fm_status bwd_impl(const fm_problem* p, const void* q, const void* k, const void
   if (e == hipSuccess)
     e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kFwdBlockQ, fm::kFwdBlockK, tq, s);
   if (e == hipSuccess) e = fm::launch_lpt_sort(tq.q_cost, q_order, (int)(R * nq.nQB), scr, s);
+  if (e == hipSuccess && ma.n == fm::kBlocksMode)
+    e = fm::launch_zero_i32(at<int32_t>(ws, w.zeros), (size_t)R * nk_of(p), s);
   if (e == hipSuccess) {
     fm::BwdArgs a{};
-    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout; a.m = ma;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+    a.m = kernel_mask(ma, at<int32_t>(ws, w.zeros));
     a.dq = dq; a.dk = dk; a.dv = dv;
     a.k_queue = tk.k_queue; a.k_count = tk.k_count; a.k_order = k_order;
     a.q_queue = tq.q_queue; a.q_count = tq.q_count; a.q_order = q_order;
@@ -438,7 +470,7 @@ fm_status expand_impl(const fm_problem* p, const MaskT* m, int32_t b, int32_t ro
     return FM_ERR_INVALID_ARG;
   if (row1 == row0 || nk_of(p) == 0) return FM_OK;
   if (!dense) return FM_ERR_INVALID_ARG;
-  return hip_status(fm::launch_expand_mask(mask_args(m), b, nk_of(p), row0, row1, dense,
+  return hip_status(fm::launch_expand_mask(mask_args(p, m), b, nk_of(p), row0, row1, dense,
                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -502,6 +534,31 @@ fm_status fm_debug_expand_mask(const fm_problem* p, const fm_mask* m, int32_t b,
 
 fm_status fm_debug_expand_mask_multi(const fm_problem* p, const fm_mask_multi* m, int32_t b,
                                      int32_t row0, int32_t row1, uint8_t* dense, void* stream) {
+  return expand_impl(p, m, b, row0, row1, dense, stream);
+}
+
+fm_status fm_classify_tiles_blocks(const fm_problem* p, const fm_mask_blocks* m, int32_t block_q,
+                                   int32_t block_k, const fm_tiles* out, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  return classify_impl(p, m, block_q, block_k, out, ws, ws_bytes, stream);
+}
+
+fm_status fm_attn_fwd_blocks(const fm_problem* p, const void* q, const void* k, const void* v,
+                             const fm_mask_blocks* m, void* o, float* lse, void* ws,
+                             size_t ws_bytes, void* stream, const fm_kernel_events* events) {
+  return fwd_impl(p, q, k, v, m, o, lse, ws, ws_bytes, stream, events);
+}
+
+fm_status fm_attn_bwd_blocks(const fm_problem* p, const void* q, const void* k, const void* v,
+                             const void* o, const float* lse, const void* dout,
+                             const fm_mask_blocks* m, void* dq, void* dk, void* dv, void* ws,
+                             size_t ws_bytes, void* stream, const fm_kernel_events* events) {
+  return bwd_impl(p, q, k, v, o, lse, dout, m, dq, dk, dv, ws, ws_bytes, stream, events);
+}
+
+fm_status fm_debug_expand_mask_blocks(const fm_problem* p, const fm_mask_blocks* m, int32_t b,
+                                      int32_t row0, int32_t row1, uint8_t* dense,
+                                      void* stream) {
   return expand_impl(p, m, b, row0, row1, dense, stream);
 }
 

@@ -86,14 +86,30 @@ __global__ __launch_bounds__(64) void k_block_minmax_multi(const int32_t* __rest
   }
 }
 
-// The block min/max of one KV block, and the tile rule of the mask form on it.
-template <bool kMulti>
+// The block-sparse grid (only read in kBlocksMode): blocks [rows][nqb][nkb] of kMaskBlock.
+struct GridArgs {
+  const uint8_t* g;
+  int nqb, nkb;  // grid blocks per row and column
+  int bk, Nk, nKB;
+};
+
+// The block min/max of one KV block, and the tile rule of the mask form on it.  kMode: 0
+// four vectors, 1 intervals, 2 block grid (the tile's class read from the blocks it
+// overlaps: skipped if all hidden, unmasked if all visible, partial otherwise).
+template <int kMode>
 struct BlockBounds {
-  int v[kMulti ? 4 * kMaxIntervals : 8];
+  int v[kMode == 1 ? 4 * kMaxIntervals : 8];
   int n;
-  __device__ __forceinline__ void load(const int32_t* __restrict__ mm, size_t idx, int n_) {
+  int r, kb;
+  const GridArgs* ga;
+  __device__ __forceinline__ void load(const int32_t* __restrict__ mm, size_t idx, int n_,
+                                       const GridArgs* ga_) {
     n = n_;
-    if constexpr (!kMulti) {
+    ga = ga_;
+    if constexpr (kMode == 2) {
+      r = (int)(idx / ga->nKB);
+      kb = (int)(idx - (size_t)r * ga->nKB);
+    } else if constexpr (kMode == 0) {
       const int4* p = reinterpret_cast<const int4*>(mm + idx * 8);
       const int4 a = p[0], c = p[1];
       v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
@@ -104,8 +120,22 @@ struct BlockBounds {
     }
   }
   __device__ __forceinline__ int cls(int q0, int q1) const {
-    if constexpr (!kMulti) return tile_class(v, q0, q1);
-    else return tile_class_multi(v, n, q0, q1);
+    if constexpr (kMode == 0) return tile_class(v, q0, q1);
+    else if constexpr (kMode == 1) return tile_class_multi(v, n, q0, q1);
+    else {
+      const uint8_t* row = ga->g + (size_t)r * ga->nqb * ga->nkb;
+      const int b0 = q0 / kMaskBlock, b1 = (q1 - 1) / kMaskBlock;
+      const int k0 = kb * ga->bk;
+      const int c0 = k0 / kMaskBlock, c1 = (min(k0 + ga->bk, ga->Nk) - 1) / kMaskBlock;
+      bool any = false, all = true;
+      for (int br = b0; br <= b1; ++br)
+        for (int bc = c0; bc <= c1; ++bc) {
+          const bool vis = row[(size_t)br * ga->nkb + bc] != 0;
+          any = any || vis;
+          all = all && vis;
+        }
+      return !any ? 0 : (all ? 2 : 1);
+    }
   }
 };
 
@@ -132,9 +162,9 @@ __device__ __forceinline__ ScanResult block_scan_256(bool flag, bool sub, int* s
 }
 
 // ---- A3: classes and per-Q-block queues (KV blocks right to left) --------------
-template <bool kMulti>
-__global__ __launch_bounds__(256) void k_classify_q(const int32_t* __restrict__ mm, int n, int Nq,
-                                                    int nQB, int nKB, int bq,
+template <int kMode>
+__global__ __launch_bounds__(256) void k_classify_q(const int32_t* __restrict__ mm, int n,
+                                                    GridArgs ga, int Nq, int nQB, int nKB, int bq,
                                                     uint8_t* __restrict__ cls,
                                                     int32_t* __restrict__ q_queue,
                                                     int32_t* __restrict__ q_count,
@@ -151,8 +181,8 @@ __global__ __launch_bounds__(256) void k_classify_q(const int32_t* __restrict__ 
     const int kb = nKB - 1 - idx;
     int c = 0;
     if (valid) {
-      BlockBounds<kMulti> bb;
-      bb.load(mm, (size_t)b * nKB + kb, n);
+      BlockBounds<kMode> bb;
+      bb.load(mm, (size_t)b * nKB + kb, n, &ga);
       c = bb.cls(q0, q1);
       if (cls) cls[(size_t)row * nKB + kb] = (uint8_t)c;
     }
@@ -173,17 +203,17 @@ __global__ __launch_bounds__(256) void k_classify_q(const int32_t* __restrict__ 
 }
 
 // ---- A3 (backward direction): per-KV-block queues of Q-blocks, ascending -----------
-template <bool kMulti>
-__global__ __launch_bounds__(256) void k_classify_k(const int32_t* __restrict__ mm, int n, int Nq,
-                                                    int nQB, int nKB, int bq,
+template <int kMode>
+__global__ __launch_bounds__(256) void k_classify_k(const int32_t* __restrict__ mm, int n,
+                                                    GridArgs ga, int Nq, int nQB, int nKB, int bq,
                                                     int32_t* __restrict__ k_queue,
                                                     int32_t* __restrict__ k_count,
                                                     int32_t* __restrict__ k_cost) {
   __shared__ int sh_cnt[4], sh_sub[4];
   const int row = blockIdx.x;  // b * nKB + kb
   const int tid = threadIdx.x;
-  BlockBounds<kMulti> bb;
-  bb.load(mm, (size_t)row, n);
+  BlockBounds<kMode> bb;
+  bb.load(mm, (size_t)row, n, &ga);
   int base = 0, np = 0;
   for (int c0 = 0; c0 < nQB; c0 += 256) {
     const int qb = c0 + tid;
@@ -284,6 +314,14 @@ __global__ __launch_bounds__(256) void k_expand_mask(MaskArgs m, int b, int Nk, 
                                                      int row1, uint8_t* __restrict__ dense) {
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= Nk) return;
+  if (m.n == kBlocksMode) {
+    // block grid of this mask row: grid_rows x ceil(Nk / 128) blocks
+    const int nkb = (Nk + kMaskBlock - 1) / kMaskBlock;
+    const uint8_t* g = m.blocks + (size_t)b * m.grid_rows * nkb;
+    for (int i = row0 + blockIdx.y; i < row1; i += gridDim.y)
+      dense[(size_t)(i - row0) * Nk + j] = g[(size_t)(i / kMaskBlock) * nkb + j / kMaskBlock] ? 0 : 1;
+    return;
+  }
   int lts = 0, lte = 0, uts = 0, ute = 0;
   int sv[kMaxIntervals] = {0, 0, 0, 0}, ev[kMaxIntervals] = {0, 0, 0, 0};
   if (m.n == 0) {
@@ -315,24 +353,41 @@ hipError_t launch_classify(const MaskArgs& m, int B, int Nq, int Nk, int bq, int
                            const TileOut& out, hipStream_t s) {
   const int nQB = (Nq + bq - 1) / bq, nKB = (Nk + bk - 1) / bk;
   if (B == 0) return hipSuccess;
-  const bool multi = m.n > 0;
+  const int mode = m.n == kBlocksMode ? 2 : (m.n > 0 ? 1 : 0);
+  GridArgs ga{m.blocks, (Nq + kMaskBlock - 1) / kMaskBlock, (Nk + kMaskBlock - 1) / kMaskBlock,
+              bk, Nk, nKB};
   if (nKB > 0) {
-    if (multi)
+    if (mode == 1)
       hipLaunchKernelGGL(k_block_minmax_multi, dim3(B * nKB), dim3(64), 0, s, m.start, m.end,
                          m.n, Nk, nKB, bk, out.minmax);
-    else
+    else if (mode == 0)
       hipLaunchKernelGGL(k_block_minmax, dim3(B * nKB), dim3(64), 0, s, m.v, Nk, nKB, bk,
                          out.minmax);
   }
   // with no KV block a Q-block's queue is empty; with no Q-block a KV block's is
-  if ((out.tile_class || out.q_queue) && nQB > 0)
-    hipLaunchKernelGGL(multi ? k_classify_q<true> : k_classify_q<false>, dim3(B * nQB),
-                       dim3(256), 0, s, out.minmax, m.n, Nq, nQB, nKB, bq, out.tile_class,
-                       out.q_queue, out.q_count, out.q_cost);
-  if (out.k_queue && nKB > 0)
-    hipLaunchKernelGGL(multi ? k_classify_k<true> : k_classify_k<false>, dim3(B * nKB),
-                       dim3(256), 0, s, out.minmax, m.n, Nq, nQB, nKB, bq, out.k_queue,
-                       out.k_count, out.k_cost);
+  if ((out.tile_class || out.q_queue) && nQB > 0) {
+    auto kq = mode == 2 ? k_classify_q<2> : (mode == 1 ? k_classify_q<1> : k_classify_q<0>);
+    hipLaunchKernelGGL(kq, dim3(B * nQB), dim3(256), 0, s, out.minmax, m.n, ga, Nq, nQB, nKB, bq,
+                       out.tile_class, out.q_queue, out.q_count, out.q_cost);
+  }
+  if (out.k_queue && nKB > 0) {
+    auto kk = mode == 2 ? k_classify_k<2> : (mode == 1 ? k_classify_k<1> : k_classify_k<0>);
+    hipLaunchKernelGGL(kk, dim3(B * nKB), dim3(256), 0, s, out.minmax, m.n, ga, Nq, nQB, nKB, bq,
+                       out.k_queue, out.k_count, out.k_cost);
+  }
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_zero_i32(int32_t* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    p[i] = 0;
+}
+
+hipError_t launch_zero_i32(int32_t* p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(k_zero_i32, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s,
+                     p, n);
   return hipGetLastError();
 }
 

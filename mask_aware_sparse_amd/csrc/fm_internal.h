@@ -79,14 +79,22 @@ struct MaskPtrs {
   const int32_t* ute;
 };
 
-// The mask as the kernels take it: the four-vector form (n == 0; rows of Nk per vector) or
-// the multi-interval form (n = 1..4 visible intervals per column; start/end [rows][n][Nk]).
+// The mask as the kernels take it: the four-vector form (n == 0; rows of Nk per vector),
+// the multi-interval form (n = 1..4 visible intervals per column; start/end [rows][n][Nk])
+// or, for the classifier only, the block-sparse form (n == kBlocksMode; blocks [rows]
+// [ceil(Nq/128)][ceil(Nk/128)], 1 = visible).  The attention kernels run a block-sparse
+// mask as the four-vector form with all-zero vectors (nothing hidden inside a block; keys
+// past Nk are hidden by the kernels' own bound).
 constexpr int kMaxIntervals = 4;
+constexpr int kBlocksMode = -1;
+constexpr int kMaskBlock = 128;
 struct MaskArgs {
   MaskPtrs v;
   const int32_t* start;
   const int32_t* end;
   int n;
+  const uint8_t* blocks;
+  int grid_rows;  // block rows of the grid: ceil(Nq / kMaskBlock)
 };
 // int32 values per KV block in the block min/max array: 8 (min, max of each of the four
 // vectors) or 4 n (min start, max start, min end, max end of each interval).  Workspaces
@@ -109,6 +117,7 @@ struct TileOut {
 // Nq query rows (Q-blocks of bq), Nk keys (KV blocks of bk); B mask rows.
 hipError_t launch_classify(const MaskArgs& m, int B, int Nq, int Nk, int bq, int bk,
                            const TileOut& out, hipStream_t s);
+hipError_t launch_zero_i32(int32_t* p, size_t n, hipStream_t s);
 size_t lpt_sort_scratch_bytes(int64_t count);
 hipError_t launch_lpt_sort(const int32_t* cost, int32_t* order, int count, void* scratch,
                            hipStream_t s);

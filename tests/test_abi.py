@@ -87,7 +87,8 @@ def test_workspace_sizes():
     B, N = 2, 1000
     nqb, nkb = 8, 16
     al = lambda x: (x + 255) // 256 * 256
-    want = al(B * nkb * 64) + al(B * nqb * nkb * 4) + al(B * nqb * 8) + 2 * al(B * nqb * 4)
+    want = al(B * nkb * 64) + al(B * nqb * nkb * 4) + al(B * nqb * 8) + 2 * al(B * nqb * 4) + \
+        al(B * N * 4)                              # + all-zero vectors for block-sparse masks
     assert fm.workspace_size(B, 4, 2, N, fm.OP_FWD) == want
     assert fm.workspace_size(B, 4, 2, N, fm.OP_CLASSIFY, 64, 32) == al(B * 16 * 4) + al(B * 32 * 4)
     # backward: fp32 dK/dV accumulators exist only for query-head groups above 4 heads;
@@ -192,7 +193,7 @@ def test_query_share_workspace_sizes():
     # forward tiles: nQB = N_q / 128 Q-blocks by nKB = N_k / 64 KV blocks
     al = lambda x: (x + 255) // 256 * 256
     nqb, nkb = 2, 16
-    want = al(nkb * 64) + al(nqb * nkb * 4) + al(nqb * 8) + 2 * al(nqb * 4)
+    want = al(nkb * 64) + al(nqb * nkb * 4) + al(nqb * 8) + 2 * al(nqb * 4) + al(1024 * 4)
     assert fm.workspace_size(1, 4, 2, 256, fm.OP_FWD, seqlen_kv=1024) == want
     square = fm.workspace_size(1, 4, 2, 256, fm.OP_BWD)
     assert fm.workspace_size(1, 4, 2, 256, fm.OP_BWD, seqlen_kv=1024) > square
@@ -248,7 +249,8 @@ def test_mask_heads_workspace_sizes():
     B, N, Hm = 2, 1000, 4
     R = B * Hm                                   # tile structures per mask row
     nqb, nkb = 8, 16
-    want = al(R * nkb * 64) + al(R * nqb * nkb * 4) + al(R * nqb * 8) + 2 * al(R * nqb * 4)
+    want = al(R * nkb * 64) + al(R * nqb * nkb * 4) + al(R * nqb * 8) + 2 * al(R * nqb * 4) + \
+        al(R * N * 4)
     assert fm.workspace_size(B, 8, 4, N, fm.OP_FWD, mask_heads=Hm) == want
     # dK/dV accumulators appear when sets split a kv head's group (two writers per block):
     # 8 query heads, 4 kv heads (groups of 2), 8 sets -> accumulators; 4 sets -> none
@@ -261,7 +263,7 @@ def test_mask_heads_workspace_sizes():
     # 8 sets: twice the tile rows, accumulators, and the plan of 128 pairs without partial
     # slots against 64 pairs with them
     assert split - whole == al_acc + tiles_k + tiles_q + split_plan_bytes(128, 1, True) - \
-        split_plan_bytes(64, 1, False)
+        split_plan_bytes(64, 1, False) + al(16 * N * 4) - al(8 * N * 4)
 
 
 def test_mask_heads_sort_limit():
@@ -325,3 +327,33 @@ def test_multi_localize_argument_checks():
     assert call(1, 8, offs=None) == INVALID
     assert call(1, 8, ls=None) == INVALID
     assert call(4097, 8) == UNSUPPORTED
+
+
+# ---- block-sparse masks (fm_mask_blocks) ----------------------------------------------
+
+def test_blocks_null_grid_and_workspace():
+    lib = fm.library()
+    null = fm.MaskBlocks(0)
+    assert lib.fm_attn_fwd_blocks(ctypes.byref(prob()), FAKE, FAKE, FAKE, ctypes.byref(null), FAKE,
+                                  FAKE, FAKE, ctypes.c_size_t(1 << 40), None, None) == INVALID
+    m = fm.MaskBlocks(0x100000)
+    need = fm.workspace_size(1, 4, 2, 256, fm.OP_FWD)
+    assert lib.fm_attn_fwd_blocks(ctypes.byref(prob()), FAKE, FAKE, FAKE, ctypes.byref(m), FAKE,
+                                  FAKE, FAKE, ctypes.c_size_t(need - 1), None, None) == WORKSPACE
+    need = fm.workspace_size(1, 4, 2, 256, fm.OP_BWD)
+    assert lib.fm_attn_bwd_blocks(ctypes.byref(prob()), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  ctypes.byref(m), FAKE, FAKE, FAKE, FAKE,
+                                  ctypes.c_size_t(need - 1), None, None) == WORKSPACE
+    # an empty problem needs no grid
+    assert lib.fm_attn_fwd_blocks(ctypes.byref(prob(N=0)), FAKE, FAKE, FAKE, ctypes.byref(null),
+                                  FAKE, FAKE, FAKE, ctypes.c_size_t(0), None, None) == FM_OK
+
+
+def test_blocks_binding_checks_the_grid_shape():
+    import torch
+    with pytest.raises(ValueError):
+        fm._mask_blocks(torch.zeros((1, 2, 3), dtype=torch.uint8), 300, 300)   # needs 3 x 3
+    with pytest.raises(ValueError):
+        fm._mask_blocks(torch.zeros((1, 3, 3), dtype=torch.int32), 300, 300)   # uint8 only
+    m, B, Hm = fm._mask_blocks(torch.zeros((2, 4, 3, 3), dtype=torch.uint8), 300, 257)
+    assert (B, Hm) == (2, 4)

@@ -32,9 +32,23 @@ def test_attended_pairs_multi_interval(M, hm):
     assert bench.attended_pairs_multi(w) == dense * (4 // max(hm, 1))
 
 
+@pytest.mark.parametrize("hm", [0, 2])
+def test_attended_pairs_block_sparse(hm):
+    n = 300                                        # ragged last block row and column
+    w = workloads.random_blocks(hm + 1, n, batch=2, heads_q=4, density=0.4, mask_heads=hm)
+    grids = [w.blocks[b] for b in range(2)] if hm == 0 else \
+        [w.blocks[b, m] for b in range(2) for m in range(hm)]
+    dense = sum(int((~oracle.dense_mask_blocks(g, n, n)).sum()) for g in grids)
+    assert bench.attended_pairs_blocks(w) == dense * (4 // max(hm, 1))
+
+
 def test_benchmark_workloads_pair_counts_are_positive():
     for name in workloads.CONFIG_NAMES[:2] + workloads.VARIANT_NAMES:
         w = workloads.make_workload(name)
-        multi = isinstance(w, workloads.MultiWorkload)
-        a = bench.attended_pairs_multi(w) if multi else bench.attended_pairs(w)
+        if isinstance(w, workloads.BlockWorkload):
+            a = bench.attended_pairs_blocks(w)
+        elif isinstance(w, workloads.MultiWorkload):
+            a = bench.attended_pairs_multi(w)
+        else:
+            a = bench.attended_pairs(w)
         assert 0 < a <= w.batch * w.heads_q * w.seqlen ** 2
