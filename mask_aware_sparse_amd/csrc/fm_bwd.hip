@@ -734,10 +734,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   const float lse_nat =
       __uint_as_float(buf_load4(make_rsrc(p.lse + qbase, row_bytes), (uint32_t)row * 4, 0));
   const float lse_row = lse_nat == -INFINITY ? INFINITY : lse_nat * kLog2e;
-  if (hh == 0) {  // rows past Nq are dropped by the buffer bounds
-    buf_store4(__float_as_uint(lse_row), make_rsrc(p.lse2 + qbase, row_bytes), (uint32_t)row * 4, 0);
-    buf_store4(__float_as_uint(d_row), make_rsrc(p.delta + qbase, row_bytes), (uint32_t)row * 4, 0);
-  }
 
   if (n_tiles > 0) store_tile(queue[0], 0);  // its loads were issued with Q and dO
   lds_barrier();
@@ -746,9 +742,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   const SwzRowRead rr(arow, hh);
   const SwzTrRead tr(lane, hh);
 
+  int e = n_tiles > 0 ? queue[0] : 0;
   for (int it = 0; it < n_tiles; ++it) {
     const int cur = it & 1;
-    const int e = queue[it];
     const int kb = e & 0x7fffffff;
     const bool partial = (e < 0) || (ragged && kb == p.nKB - 1);
     int en = 0;
@@ -822,6 +818,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
 
     if (has_next) store_tile(en, cur ^ 1);
     lds_barrier();
+    e = en;
+  }
+
+  // D and the log2 LSE go out after the loop: a store before it would keep the compiler
+  // from reading the queue through the scalar cache (it cannot tell what a buffer store
+  // may overwrite), turning each entry into a vector load waited for in full.  Rows past
+  // Nq are dropped by the buffer bounds.
+  if (hh == 0) {
+    buf_store4(__float_as_uint(lse_row), make_rsrc(p.lse2 + qbase, row_bytes), (uint32_t)row * 4, 0);
+    buf_store4(__float_as_uint(d_row), make_rsrc(p.delta + qbase, row_bytes), (uint32_t)row * 4, 0);
   }
 
   // ---- dQ = scale * acc (bf16); rows past Nq are dropped by the buffer bounds ----

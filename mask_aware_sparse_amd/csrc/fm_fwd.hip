@@ -118,6 +118,23 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   const bool ragged = (N % BK) != 0;
 
   const int row = qb * BQ + wave * 32 + l32;
+  auto out_rsrc = [&]() { return make_rsrc(p.o + (size_t)(b * p.Hq + h) * Nq * D, q_bytes); };
+  auto lse_rsrc = [&]() { return make_rsrc(p.lse + (size_t)(b * p.Hq + h) * Nq, (uint32_t)Nq * 4); };
+
+  // A Q-block that sees no key: O = 0 and LSE = -inf, nothing loaded.  Leaving here keeps
+  // every path into the tile loop behind the first tile's score products, so the compiler
+  // knows Q's loads have landed there and does not wait on the memory counter in the loop.
+  if (n_tiles == 0) {
+    const rsrc_t orr = out_rsrc();
+    const uint32_t ooff = (uint32_t)row * (D * 2) + hh * 8;
+    const u32x2 z = {0u, 0u};
+#pragma unroll
+    for (int d = 0; d < kDB; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) buf_store8(z, orr, ooff, (d * 32 + g * 8) * 2);
+    if (hh == 0) buf_store4(__float_as_uint(-INFINITY), lse_rsrc(), (uint32_t)row * 4, 0);
+    return;
+  }
 
   // Q^T operand: lane holds Q[row][s*16 + hh*8 .. +7] for s = 0..7 (rows past Nq read 0)
   bf16x8 qr[kS];
@@ -231,7 +248,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   };
 
   f32x16 sacc[2];
-  if (n_tiles > 0) {
+  {
     // tile 0's K and V and tile 1's K in flight together (one memory round trip)
     const int e0 = queue[0];
     const int e1 = n_tiles > 1 ? queue[1] : 0;
@@ -245,7 +262,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     if (n_tiles > 1) put_k(e1, 1, kst1, vec1);
   }
   lds_barrier();
-  if (n_tiles > 0) {
+  {
     scores(0, sacc);
     if (is_partial(queue[0])) apply_mask(0, sacc);
     // The first tile sets each row's offset from its own maximum, so its exponentials are
@@ -379,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   lf = sum_with_partner32(lf);
   lb = sum_with_partner32(lb);
   const float inv = lb > 0.f ? 1.0f / lb : 0.f;
-  const rsrc_t orr = make_rsrc(p.o + (size_t)(b * p.Hq + h) * Nq * D, q_bytes);
+  const rsrc_t orr = out_rsrc();
   const uint32_t ooff = (uint32_t)row * (D * 2) + hh * 8;
 #pragma unroll
   for (int d = 0; d < kDB; ++d) {
@@ -392,9 +409,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     }
   }
   if (hh == 0) {
-    const rsrc_t lr = make_rsrc(p.lse + (size_t)(b * p.Hq + h) * Nq, (uint32_t)Nq * 4);
     const float l = lf > 0.f ? (m_use + __builtin_amdgcn_logf(lf)) * kLn2 : -INFINITY;
-    buf_store4(__float_as_uint(l), lr, (uint32_t)row * 4, 0);
+    buf_store4(__float_as_uint(l), lse_rsrc(), (uint32_t)row * 4, 0);
   }
 }
 
