@@ -230,6 +230,43 @@ __device__ __forceinline__ float mask_zero(float p, uint32_t word, uint32_t bit)
   return __uint_as_float(__builtin_amdgcn_bitop3_b32(m, 0u, __float_as_uint(p), 0xCA));
 }
 
+// A read-only array seen through the constant address space: loads from it go through the
+// scalar cache whatever the kernel stores elsewhere (the compiler cannot tell where a
+// buffer store or a buffer-to-LDS load writes, so it would otherwise use vector loads).
+// Only for data no kernel in flight writes.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+__device__ __forceinline__ const_i32_ptr const_view(const int32_t* p) {
+  return (const_i32_ptr)p;
+}
+
+// The resource of make_rsrc as four dwords, for inline assembly.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return i32x4_t{(int)(uint32_t)a, (int)((a >> 32) & 0xFFFFu), (int)bytes, kRsrcWord3};
+}
+// 16 bytes per lane from resource r at byte offset voff into LDS at lds + 16 * lane (lds
+// is wave-uniform).  Written in assembly so that the compiler does not track the LDS write:
+// it would otherwise wait for every such load before any transposing LDS read (it cannot
+// tell their addresses apart).  The caller waits on the memory counter before the data is
+// read.  The no-op covers the wait state between writing M0 and the load that reads it.
+__device__ __forceinline__ void lds_load16_untracked(i32x4_t r, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(r)
+               : "m0");
+}
+
+// A workgroup-shared buffer as the LDS-space pointer the buffer-to-LDS loads take.
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(const void* p) {
+  return (__attribute__((address_space(3))) void*)(const_cast<void*>(p));
+}
+
+// Its LDS byte address (wave-uniform for a wave-uniform p).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_ptr(p));
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS operations, not for
 // its outstanding global loads, stores or atomics (waves here exchange data through LDS
 // only, so a full __syncthreads would stall every step on in-flight atomics).

@@ -95,12 +95,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   const int h = (mr - b * p.Hm) * qpm + (L - r * qpm);
   const int kvh = h / (p.Hq / p.Hkv);
   const int n_tiles = p.q_count[2 * item] + p.q_count[2 * item + 1];
-  const int32_t* queue = p.q_queue + (size_t)item * p.nKB;
+  const const_i32_ptr queue = const_view(p.q_queue + (size_t)item * p.nKB);
   const int Nq = p.Nq, N = p.Nk;  // N: keys (and mask columns)
   const uint32_t q_bytes = (uint32_t)Nq * D * 2, head_bytes = (uint32_t)N * D * 2;
   const rsrc_t qr_ = make_rsrc(p.q + (size_t)(b * p.Hq + h) * Nq * D, q_bytes);
   const rsrc_t kr_ = make_rsrc(p.k + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
   const rsrc_t vr_ = make_rsrc(p.v + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
+  const i32x4_t kw_ = rsrc_words(p.k + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
+  const i32x4_t vw_ = rsrc_words(p.v + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
   const uint32_t vec_bytes = (uint32_t)N * 4;
   // mask row mr: four vectors of N, or n intervals x N starts and ends (absent intervals
   // m >= n read past the row's bounds and load 0, the empty interval [0, 0))
@@ -153,7 +155,27 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   const int cp_row = tid / kCh, cp_ch = (tid % kCh) * 8;
   const int mk_key = lane, mk_wave = __builtin_amdgcn_readfirstlane(wave);
   constexpr int kVec = kMulti ? 2 * kMaxIntervals : 4;
-  u32x4 kst[kPasses], vst[kPasses];
+  // D = 128: tiles go from memory straight into LDS (buffer loads with the LDS flag), no
+  // staging registers.  Each such load writes 64 consecutive 16-byte LDS slots, one per
+  // lane, so lane l of load j covers slot 64 j + l of the padded tile (K: 17 slots a row,
+  // V: 20) and fetches the 16 bytes that belong there; pad slots take a copy of the row's
+  // first chunk.  Wave w issues loads j = w, w + 4, ... (K: 17 loads, V: 20).
+  constexpr bool kDma = D == 128;
+  constexpr int kKSlots = KS * 2 / 16, kVSlots = VS * 2 / 16;
+  constexpr int kKLoads = BK * kKSlots / 64, kVLoads = BK * kVSlots / 64;
+  constexpr int kDmaPer = (kVLoads + 3) / 4;
+  uint32_t koff[kDma ? kDmaPer : 1], voff[kDma ? kDmaPer : 1];
+  if constexpr (kDma) {
+#pragma unroll
+    for (int i = 0; i < kDmaPer; ++i) {
+      const int pk = (wave + 4 * i) * 64 + lane, pv = pk;
+      const int rk = pk / kKSlots, ck = pk - rk * kKSlots;
+      const int rv = pv / kVSlots, cv = pv - rv * kVSlots;
+      koff[i] = (uint32_t)(rk * D * 2 + (ck < D / 8 ? ck * 16 : 0));
+      voff[i] = (uint32_t)(rv * D * 2 + (cv < D / 8 ? cv * 16 : 0));
+    }
+  }
+  u32x4 kst[kDma ? 1 : kPasses], vst[kDma ? 1 : kPasses];
   uint32_t vec[kVec];
   auto is_partial = [&](int e) {
     return (e < 0) || (ragged && (e & 0x7fffffff) == p.nKB - 1);
@@ -166,11 +188,21 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   // tile t+1; one barrier per iteration separates those reads from those writes.
   // fetch_k / put_k stage through (ks, vv): kst / vec in the loop; the prologue also
   // uses a second set so that both K tiles it needs are requested at once
-  auto fetch_k = [&](int e, u32x4 (&ks)[kPasses], uint32_t (&vec)[kVec]) {
+  auto fetch_k = [&](int e, int buf, u32x4 (&ks)[kDma ? 1 : kPasses], uint32_t (&vec)[kVec]) {
     const int kb = e & 0x7fffffff;
-    const uint32_t base = (uint32_t)(kb * BK + cp_row) * (D * 2) + cp_ch * 2;
+    if constexpr (kDma) {
+      const uint32_t tb = (uint32_t)kb * BK * D * 2;
 #pragma unroll
-    for (int i = 0; i < kPasses; ++i) ks[i] = buf_load16(kr_, base, i * kRowsPass * D * 2);
+      for (int i = 0; i < kDmaPer; ++i) {
+        const int j = mk_wave + 4 * i;
+        if (j < kKLoads)
+          lds_load16_untracked(kw_, tb + koff[i], lds_addr(&sm.k[buf][j * 512]));
+      }
+    } else {
+      const uint32_t base = (uint32_t)(kb * BK + cp_row) * (D * 2) + cp_ch * 2;
+#pragma unroll
+      for (int i = 0; i < kPasses; ++i) ks[i] = buf_load16(kr_, base, i * kRowsPass * D * 2);
+    }
     if (is_partial(e)) {
       const uint32_t vo = (uint32_t)(kb * BK + mk_key) * 4;
       if constexpr (!kMulti) {
@@ -185,16 +217,29 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
       }
     }
   };
-  auto fetch_v = [&](int e) {
+  auto fetch_v = [&](int e, int buf) {
     const int kb = e & 0x7fffffff;
-    const uint32_t base = (uint32_t)(kb * BK + cp_row) * (D * 2) + cp_ch * 2;
+    if constexpr (kDma) {
+      const uint32_t tb = (uint32_t)kb * BK * D * 2;
 #pragma unroll
-    for (int i = 0; i < kPasses; ++i) vst[i] = buf_load16(vr_, base, i * kRowsPass * D * 2);
+      for (int i = 0; i < kDmaPer; ++i) {
+        const int j = mk_wave + 4 * i;
+        if (j < kVLoads)
+          lds_load16_untracked(vw_, tb + voff[i], lds_addr(&sm.v[buf][j * 512]));
+      }
+    } else {
+      const uint32_t base = (uint32_t)(kb * BK + cp_row) * (D * 2) + cp_ch * 2;
+#pragma unroll
+      for (int i = 0; i < kPasses; ++i) vst[i] = buf_load16(vr_, base, i * kRowsPass * D * 2);
+    }
   };
-  auto put_k = [&](int e, int buf, const u32x4 (&ks)[kPasses], const uint32_t (&vec)[kVec]) {
+  auto put_k = [&](int e, int buf, const u32x4 (&ks)[kDma ? 1 : kPasses],
+                   const uint32_t (&vec)[kVec]) {
+    if constexpr (!kDma) {
 #pragma unroll
-    for (int i = 0; i < kPasses; ++i)
-      *reinterpret_cast<u32x4*>(&sm.k[buf][(cp_row + kRowsPass * i) * KS + cp_ch]) = ks[i];
+      for (int i = 0; i < kPasses; ++i)
+        *reinterpret_cast<u32x4*>(&sm.k[buf][(cp_row + kRowsPass * i) * KS + cp_ch]) = ks[i];
+    }
     if (is_partial(e)) {
       const int key = (e & 0x7fffffff) * BK + mk_key;
       const int r0 = qb * BQ + mk_wave * 32;
@@ -208,9 +253,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     }
   };
   auto put_v = [&](int buf) {
+    if constexpr (!kDma) {
 #pragma unroll
-    for (int i = 0; i < kPasses; ++i)
-      *reinterpret_cast<u32x4*>(&sm.v[buf][(cp_row + kRowsPass * i) * VS + cp_ch]) = vst[i];
+      for (int i = 0; i < kPasses; ++i)
+        *reinterpret_cast<u32x4*>(&sm.v[buf][(cp_row + kRowsPass * i) * VS + cp_ch]) = vst[i];
+    }
+  };
+  // the loads into LDS are counted by the memory counter only: wait for them before the
+  // barrier that publishes a tile
+  auto tiles_landed = [&]() {
+    if constexpr (kDma) asm volatile("s_waitcnt vmcnt(0)");
   };
 
   const int arow = perm_rows(l32);
@@ -252,15 +304,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     // tile 0's K and V and tile 1's K in flight together (one memory round trip)
     const int e0 = queue[0];
     const int e1 = n_tiles > 1 ? queue[1] : 0;
-    u32x4 kst1[kPasses];
+    u32x4 kst1[kDma ? 1 : kPasses];
     uint32_t vec1[kVec];
-    fetch_k(e0, kst, vec);
-    fetch_v(e0);
-    if (n_tiles > 1) fetch_k(e1, kst1, vec1);
+    fetch_k(e0, 0, kst, vec);
+    fetch_v(e0, 0);
+    if (n_tiles > 1) fetch_k(e1, 1, kst1, vec1);
     put_k(e0, 0, kst, vec);
     put_v(0);
     if (n_tiles > 1) put_k(e1, 1, kst1, vec1);
   }
+  tiles_landed();
   lds_barrier();
   {
     scores(0, sacc);
@@ -281,8 +334,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     const bool has1 = it + 1 < n_tiles, has2 = it + 2 < n_tiles;
     const int e1 = has1 ? queue[it + 1] : 0;
     const int e2 = has2 ? queue[it + 2] : 0;
-    if (has2) fetch_k(e2, kst, vec);
-    if (has1) fetch_v(e1);
+    if (has2) fetch_k(e2, cur, kst, vec);
+    if (has1) fetch_v(e1, nxt);
 
     // ---- scores of tile it+1 (MFMA; stale but unused after the last tile) interleaved
     // with the exponentials of tile it (VALU): step i issues the K fragment read for step
@@ -387,6 +440,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     if (has1 && is_partial(e1)) apply_mask(nxt, snext);
     if (has2) put_k(e2, cur, kst, vec);
     if (has1) put_v(nxt);
+    tiles_landed();
     lds_barrier();
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) sacc[blk] = snext[blk];
