@@ -18,6 +18,8 @@
 // ds_read_b64_tr_b16), K one tile ahead of V so that the scores of the next tile are
 // computed (MFMA) while the current tile's exponentials run (VALU).  Two row sums are kept: l_f (fp32 sum of p) gives the LSE,
 // l_b (sum of the bf16-rounded p that the PV product actually used) normalises O.
+#include <type_traits>
+
 #include "fm_device.h"
 #include "fm_internal.h"
 
@@ -329,8 +331,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     m_use = max_with_partner32(mx) * p.c;
   }
 
-  for (int it = 0; it < n_tiles; ++it) {
-    const int cur = it & 1, nxt = cur ^ 1;
+  // The loop body for tile `it` (it & 1 == Cur, a compile-time buffer index): sc holds tile
+  // it's scores, sn receives tile it+1's.  Two tiles per trip, the score arrays swapping
+  // roles: no copy of the scores per tile, and every LDS buffer index is a constant.
+  auto step = [&](auto cur_c, int it, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
     const bool has1 = it + 1 < n_tiles, has2 = it + 2 < n_tiles;
     const int e1 = has1 ? queue[it + 1] : 0;
     const int e2 = has2 ? queue[it + 2] : 0;
@@ -341,15 +346,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     // with the exponentials of tile it (VALU): step i issues the K fragment read for step
     // i+2, score MFMA i, and the exponentials of score pair i of the current tile.  The
     // scheduling barriers keep that order, so the VALU work runs in the MFMAs' shadow. ----
-    f32x16 snext[2];
     bf16x8 pb[2][2];
     float psum[2], pbsum[2];
     // p = 2^(s c - off) for score pair i (half i/8, column group (i%8)/4, rows 2(i%4)+{0,1})
     u32x4 packed[2][2];
     auto exp_pair = [&](int i, float off) {
       const int hb = i / 8, j = (i % 8) / 4, t = (i % 4) * 2;
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[hb][j * 8 + t], p.c, -off));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[hb][j * 8 + t + 1], p.c, -off));
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[hb][j * 8 + t], p.c, -off));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[hb][j * 8 + t + 1], p.c, -off));
       psum[hb] += p0 + p1;
       const unsigned u = pack_bf16x2(p0, p1);
       packed[hb][j][t / 2] = u;
@@ -379,7 +383,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
       for (int i = 0; i < kSteps; ++i) {
         if (i + 2 < kSteps) kf[(i + 2) % 3] = kread(i + 2);
         const int blk = i / kS, st = i % kS;
-        snext[blk] = mfma32(kf[i % 3], qr[st], st == 0 ? f32x16{} : snext[blk]);
+        sn[blk] = mfma32(kf[i % 3], qr[st], st == 0 ? f32x16{} : sn[blk]);
 #pragma unroll
         for (int e = 0; e < kExp; ++e) exp_pair(i * kExp + e, off0);
         __builtin_amdgcn_sched_barrier(0);
@@ -393,7 +397,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[blk][i]);
       mx = max_with_partner32(mx) * p.c;
       // only rows that asked for it move their offset, so a row's result never depends
       // on which rows share its wave
@@ -437,13 +441,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
       }
     }
 
-    if (has1 && is_partial(e1)) apply_mask(nxt, snext);
+    if (has1 && is_partial(e1)) apply_mask(nxt, sn);
     if (has2) put_k(e2, cur, kst, vec);
     if (has1) put_v(nxt);
     tiles_landed();
     lds_barrier();
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) sacc[blk] = snext[blk];
+  };
+  f32x16 sacc2[2];
+  for (int it = 0; it < n_tiles; it += 2) {
+    step(std::integral_constant<int, 0>{}, it, sacc, sacc2);
+    if (it + 1 < n_tiles) step(std::integral_constant<int, 1>{}, it + 1, sacc2, sacc);
   }
 
   // ---- epilogue: O = acc / l_b, LSE = ln2 * (m + log2 l_f) ----
