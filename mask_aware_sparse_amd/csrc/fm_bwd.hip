@@ -623,12 +623,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   const int h = (mr - b * p.Hm) * qpm + (L - r * qpm);
   const int kvh = h / (p.Hq / p.Hkv);
   const int n_tiles = p.q_count[2 * item] + p.q_count[2 * item + 1];
-  const int32_t* queue = p.q_queue + (size_t)item * p.nKB;
+  const const_i32_ptr queue = const_view(p.q_queue + (size_t)item * p.nKB);
   const int N = p.Nk, Nq = p.Nq;  // N: keys (and mask columns)
   const uint32_t head_bytes = (uint32_t)N * D * 2, q_bytes = (uint32_t)Nq * D * 2;
   const size_t qbase = (size_t)(b * p.Hq + h) * Nq;
   const rsrc_t kr_ = make_rsrc(p.k + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
   const rsrc_t vr_ = make_rsrc(p.v + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
+  const i32x4_t kw_ = rsrc_words(p.k + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
+  const i32x4_t vw_ = rsrc_words(p.v + (size_t)(b * p.Hkv + kvh) * N * D, head_bytes);
   const uint32_t vec_bytes = (uint32_t)N * 4, row_bytes = (uint32_t)Nq * 4;
   // mask row mr (multi-interval form: absent intervals load 0, the empty interval)
   rsrc_t m0, m1, m2, m3;
@@ -652,16 +654,49 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
 
   const int cp_row = tid / kCh, cp_ch = (tid % kCh) * 8;
   const int mk_key = lane, mk_wave = __builtin_amdgcn_readfirstlane(wave);
-  u32x4 kst[kPasses], vst[kPasses];
+  // D = 128: tiles go from memory straight into LDS, one 16-byte slot per lane and load
+  // (load j, lane l: slot 64 j + l of the padded tile; K rows hold 20 slots, 16 of them
+  // data under the XOR swizzle, V rows 17), pad slots taking a copy of the row's first
+  // chunk.  Wave w issues loads j = w, w + 4, ... (K: 20, V: 17).
+  constexpr bool kDma = D == 128;
+  constexpr int kKSlots = kSwzRow * 2 / 16, kVSlots = VS * 2 / 16;
+  constexpr int kKLoads = BK * kKSlots / 64, kVLoads = BK * kVSlots / 64;
+  constexpr int kDmaPer = (kKLoads + 3) / 4;
+  uint32_t koff[kDma ? kDmaPer : 1], voff[kDma ? kDmaPer : 1];
+  if constexpr (kDma) {
+#pragma unroll
+    for (int i = 0; i < kDmaPer; ++i) {
+      const int pp = (wave + 4 * i) * 64 + lane;
+      const int rk = pp / kKSlots, ck = pp - rk * kKSlots;
+      const int rv = pp / kVSlots, cv = pp - rv * kVSlots;
+      koff[i] = (uint32_t)(rk * D * 2 + (ck < D / 8 ? (ck ^ ((rk >> 2) & 3)) * 16 : 0));
+      voff[i] = (uint32_t)(rv * D * 2 + (cv < D / 8 ? cv * 16 : 0));
+    }
+  }
+  u32x4 kst[kDma ? 1 : kPasses], vst[kDma ? 1 : kPasses];
   uint32_t vec[kMulti ? 2 * kMaxIntervals : 4];
 
-  auto load_tile = [&](int e) {
+  // load_tile(e, buf): D = 128 writes buffer buf directly; otherwise stages in registers
+  // for store_tile
+  auto load_tile = [&](int e, int buf) {
     const int kb = e & 0x7fffffff;
-    const uint32_t base = (uint32_t)(kb * BK + cp_row) * (D * 2) + cp_ch * 2;
+    if constexpr (kDma) {
+      const uint32_t tb = (uint32_t)kb * BK * D * 2;
 #pragma unroll
-    for (int i = 0; i < kPasses; ++i) {
-      kst[i] = buf_load16(kr_, base, i * kRowsPass * D * 2);
-      vst[i] = buf_load16(vr_, base, i * kRowsPass * D * 2);
+      for (int i = 0; i < kDmaPer; ++i) {
+        const int j = mk_wave + 4 * i;
+        if (i < kKLoads / 4 || j < kKLoads)
+          lds_load16_untracked(kw_, tb + koff[i], lds_addr(&sm.k[buf][j * 512]));
+        if (i < kVLoads / 4 || j < kVLoads)
+          lds_load16_untracked(vw_, tb + voff[i], lds_addr(&sm.v[buf][j * 512]));
+      }
+    } else {
+      const uint32_t base = (uint32_t)(kb * BK + cp_row) * (D * 2) + cp_ch * 2;
+#pragma unroll
+      for (int i = 0; i < kPasses; ++i) {
+        kst[i] = buf_load16(kr_, base, i * kRowsPass * D * 2);
+        vst[i] = buf_load16(vr_, base, i * kRowsPass * D * 2);
+      }
     }
     const bool part = (e < 0) || (ragged && kb == p.nKB - 1);
     if (part) {
@@ -679,10 +714,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
     }
   };
   auto store_tile = [&](int e, int buf) {
+    if constexpr (!kDma) {
 #pragma unroll
-    for (int i = 0; i < kPasses; ++i) {
-      *reinterpret_cast<u32x4*>(&sm.k[buf][swz(cp_row + kRowsPass * i, cp_ch >> 3)]) = kst[i];
-      *reinterpret_cast<u32x4*>(&sm.v[buf][(cp_row + kRowsPass * i) * VS + cp_ch]) = vst[i];
+      for (int i = 0; i < kPasses; ++i) {
+        *reinterpret_cast<u32x4*>(&sm.k[buf][swz(cp_row + kRowsPass * i, cp_ch >> 3)]) = kst[i];
+        *reinterpret_cast<u32x4*>(&sm.v[buf][(cp_row + kRowsPass * i) * VS + cp_ch]) = vst[i];
+      }
     }
     const int kb = e & 0x7fffffff;
     const bool part = (e < 0) || (ragged && kb == p.nKB - 1);
@@ -712,7 +749,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
     }
   }
   // the first tile's loads go out now, so their latency overlaps that of Q, dO and O
-  if (n_tiles > 0) load_tile(queue[0]);
+  if (n_tiles > 0) load_tile(queue[0], 0);
   // D = rowsum(dO o O) for this lane's row (the two half-waves hold the two halves of each
   // 16-wide d slice) and the LSE in log2 units; both go to memory for the dK/dV kernel.
   float d_row;
@@ -736,6 +773,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   const float lse_row = lse_nat == -INFINITY ? INFINITY : lse_nat * kLog2e;
 
   if (n_tiles > 0) store_tile(queue[0], 0);  // its loads were issued with Q and dO
+  if constexpr (kDma) asm volatile("s_waitcnt vmcnt(0)");  // loads into LDS have landed
   lds_barrier();
 
   const int arow = perm_rows(l32);
@@ -751,21 +789,37 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
     const bool has_next = it + 1 < n_tiles;
     if (has_next) {
       en = queue[it + 1];
-      load_tile(en);
+      load_tile(en, cur ^ 1);
     }
 
-    // ---- S^T = K Q^T and dP^T = V dO^T (a lane owns one query row) ----
+    // ---- S^T = K Q^T and dP^T = V dO^T (a lane owns one query row).  Step i (key half
+    // i / kS, d-step i % kS) reads its K and V fragments two steps ahead; the scheduling
+    // barriers keep the reads ahead of the products. ----
     f32x16 sacc[2], pacc[2];
+    {
+      constexpr int kSt = 2 * kS;
+      auto kread = [&](int i) {
+        return *reinterpret_cast<const bf16x8*>(
+            &sm.k[cur][rr.at(i % kS) + (i / kS) * 32 * kSwzRow]);
+      };
+      auto vread = [&](int i) {
+        return *reinterpret_cast<const bf16x8*>(
+            &sm.v[cur][((i / kS) * 32 + arow) * VS + hh * 8 + (i % kS) * 16]);
+      };
+      bf16x8 kf[3], vf[3];
+      kf[0] = kread(0); vf[0] = vread(0);
+      kf[1] = kread(1); vf[1] = vread(1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const bf16* vp = &sm.v[cur][(blk * 32 + arow) * VS + hh * 8];
-#pragma unroll
-      for (int s = 0; s < kS; ++s) {
-        const bf16x8 ka =
-            *reinterpret_cast<const bf16x8*>(&sm.k[cur][rr.at(s) + blk * 32 * kSwzRow]);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vp + s * 16);
-        sacc[blk] = mfma32(ka, qr[s], s == 0 ? f32x16{} : sacc[blk]);
-        pacc[blk] = mfma32(va, orr[s], s == 0 ? f32x16{} : pacc[blk]);
+      for (int i = 0; i < kSt; ++i) {
+        if (i + 2 < kSt) {
+          kf[(i + 2) % 3] = kread(i + 2);
+          vf[(i + 2) % 3] = vread(i + 2);
+        }
+        const int blk = i / kS, st = i % kS;
+        sacc[blk] = mfma32(kf[i % 3], qr[st], st == 0 ? f32x16{} : sacc[blk]);
+        pacc[blk] = mfma32(vf[i % 3], orr[st], st == 0 ? f32x16{} : pacc[blk]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
@@ -817,6 +871,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
     }
 
     if (has_next) store_tile(en, cur ^ 1);
+    if constexpr (kDma) asm volatile("s_waitcnt vmcnt(0)");  // loads into LDS have landed
     lds_barrier();
     e = en;
   }

@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < kDmaPer; ++i) {
         const int j = mk_wave + 4 * i;
-        if (j < kKLoads)
+        if (i < kKLoads / 4 || j < kKLoads)
           lds_load16_untracked(kw_, tb + koff[i], lds_addr(&sm.k[buf][j * 512]));
       }
     } else {
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < kDmaPer; ++i) {
         const int j = mk_wave + 4 * i;
-        if (j < kVLoads)
+        if (i < kVLoads / 4 || j < kVLoads)
           lds_load16_untracked(vw_, tb + voff[i], lds_addr(&sm.v[buf][j * 512]));
       }
     } else {
