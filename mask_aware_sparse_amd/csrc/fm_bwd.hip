@@ -445,16 +445,27 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
 
     {
       constexpr int qblk = 0;
-      // ---- S = Q K^T and dP = dO V^T for 32 query rows x this wave's 32 keys ----
+      // ---- S = Q K^T and dP = dO V^T for 32 query rows x this wave's 32 keys.  Step s
+      // reads its K, Q and dO fragments one step ahead; the scheduling barriers keep the
+      // reads ahead of the products. ----
       f32x16 sacc, pacc;
+      {
+        bf16x8 kf[2], qf[2], of[2];
+        auto rd = [&](int s, int slot) {
+          const int o = rr.at(s) + qblk * 32 * kSwzRow;
+          kf[slot] = *reinterpret_cast<const bf16x8*>(kp + s * 16);
+          qf[slot] = *reinterpret_cast<const bf16x8*>(&sm.q[cur][o]);
+          of[slot] = *reinterpret_cast<const bf16x8*>(&sm.dO[cur][o]);
+        };
+        rd(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int s = 0; s < kS; ++s) {
-        const int o = rr.at(s) + qblk * 32 * kSwzRow;
-        const bf16x8 kb8 = *reinterpret_cast<const bf16x8*>(kp + s * 16);
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sm.q[cur][o]);
-        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&sm.dO[cur][o]);
-        sacc = mfma32(qa, kb8, s == 0 ? f32x16{} : sacc);
-        pacc = mfma32(oa, vr[s], s == 0 ? f32x16{} : pacc);
+        for (int s = 0; s < kS; ++s) {
+          if (s + 1 < kS) rd(s + 1, (s + 1) & 1);
+          sacc = mfma32(qf[s & 1], kf[s & 1], s == 0 ? f32x16{} : sacc);
+          pacc = mfma32(of[s & 1], vr[s], s == 0 ? f32x16{} : pacc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
 
       // ---- P = exp2(S c - LSE2), masked on partial tiles; dS = P (dP - D) ----
