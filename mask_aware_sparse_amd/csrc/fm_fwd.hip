@@ -330,6 +330,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
     m_use = max_with_partner32(mx) * p.c;
   }
+  // Tile 0's K and mask words (buffer 0) are refilled by the first iteration (tile 2): every
+  // wave's reads of them above come first.
+  lds_barrier();
 
   // The loop body for tile `it` (it & 1 == Cur, a compile-time buffer index): sc holds tile
   // it's scores, sn receives tile it+1's.  Two tiles per trip, the score arrays swapping
