@@ -64,6 +64,24 @@ def test_blocks_classification(bq, bk):
     assert np.array_equal(out["k_order"].cpu().numpy(), oracle.lpt_order(oracle.tile_costs(kc)))
 
 
+def test_blocks_classification_many_tiles():
+    """Many tiles (2 x 256 x 256, every classification workgroup walking 256 blocks in
+    chunks): bit-exact."""
+    import mask_aware_sparse_amd as fm
+    n = 8192
+    w = workloads.random_blocks(13, n, batch=2, density=0.3)
+    (blk,) = workloads.mask_tensors(w, device="cuda")
+    out = fm.classify_tiles_blocks(blk, 32, 32, n, n)
+    torch.cuda.synchronize()
+    cls = oracle.classify_blocks(w.blocks, 32, 32, n, n)
+    qq, qc, kq, kc = oracle.queues(cls)
+    assert np.array_equal(out["tile_class"].cpu().numpy(), cls)
+    assert np.array_equal(out["q_queue"].cpu().numpy(), qq)
+    assert np.array_equal(out["k_queue"].cpu().numpy(), kq)
+    assert np.array_equal(out["q_order"].cpu().numpy(), oracle.lpt_order(oracle.tile_costs(qc)))
+    assert np.array_equal(out["k_order"].cpu().numpy(), oracle.lpt_order(oracle.tile_costs(kc)))
+
+
 def test_blocks_dense_expansion():
     import mask_aware_sparse_amd as fm
     n = 450

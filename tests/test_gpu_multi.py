@@ -72,6 +72,25 @@ def test_multi_classification_matches_oracle(bq, bk, M):
     assert np.array_equal(out["k_order"].cpu().numpy(), oracle.lpt_order(oracle.tile_costs(kc)))
 
 
+def test_multi_classification_many_tiles():
+    """Many tiles (2 x 256 x 256, every classification workgroup walking 256 blocks in
+    chunks): bit-exact as well."""
+    import mask_aware_sparse_amd as fm
+    w = workloads.random_multi_intervals(12, 8192, batch=2, n_intervals=3)
+    s, e = workloads.mask_tensors(w, device="cuda")
+    out = fm.classify_tiles_multi(s, e, 32, 32)
+    torch.cuda.synchronize()
+    cls = oracle.classify_multi(w.starts, w.ends, 32, 32)
+    qq, qc, kq, kc = oracle.queues(cls)
+    assert np.array_equal(out["block_minmax"].cpu().numpy(),
+                          oracle.block_minmax_multi(w.starts, w.ends, 32))
+    assert np.array_equal(out["tile_class"].cpu().numpy(), cls)
+    assert np.array_equal(out["q_queue"].cpu().numpy(), qq)
+    assert np.array_equal(out["k_queue"].cpu().numpy(), kq)
+    assert np.array_equal(out["q_order"].cpu().numpy(), oracle.lpt_order(oracle.tile_costs(qc)))
+    assert np.array_equal(out["k_order"].cpu().numpy(), oracle.lpt_order(oracle.tile_costs(kc)))
+
+
 def test_multi_dense_expansion():
     import mask_aware_sparse_amd as fm
     w = workloads.random_multi_intervals(11, 300, batch=2, n_intervals=4)
