@@ -460,9 +460,11 @@ def main():
     lse = torch.empty((w.batch, w.heads_q, w.seqlen), dtype=torch.float32, device=dev)
     grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     ws_f = torch.empty(fm.workspace_size(w.batch, w.heads_q, w.heads_kv, w.seqlen, fm.OP_FWD,
-                                         mask_heads=w.mask_heads), dtype=torch.uint8, device=dev)
+                                         head_dim=w.head_dim, mask_heads=w.mask_heads),
+                       dtype=torch.uint8, device=dev)
     ws_b = torch.empty(fm.workspace_size(w.batch, w.heads_q, w.heads_kv, w.seqlen, fm.OP_BWD,
-                                         mask_heads=w.mask_heads), dtype=torch.uint8, device=dev)
+                                         head_dim=w.head_dim, mask_heads=w.mask_heads),
+                       dtype=torch.uint8, device=dev)
     multi = isinstance(w, workloads.MultiWorkload)
     blocks = isinstance(w, workloads.BlockWorkload)
     A = attended_pairs_blocks(w) if blocks else (attended_pairs_multi(w) if multi

@@ -61,7 +61,7 @@ extern "C" {
 typedef enum {
   FM_OK = 0,
   FM_ERR_INVALID_ARG = -1, /* null pointer, negative size, H_q % H_kv != 0, bad tile shape */
-  FM_ERR_UNSUPPORTED = -2, /* head_dim not 64 or 128, or a size beyond the limits        */
+  FM_ERR_UNSUPPORTED = -2, /* head_dim not 64, 128 or 256, or a size beyond the limits   */
   FM_ERR_WORKSPACE = -3,   /* ws_bytes smaller than fm_workspace_size() reports           */
   FM_ERR_HIP = -4          /* a HIP launch failed                                         */
 } fm_status;
@@ -69,7 +69,7 @@ typedef enum {
 typedef enum { FM_OP_CLASSIFY = 0, FM_OP_FWD = 1, FM_OP_BWD = 2 } fm_op;
 
 /* Problem shape.  batch, heads and the lengths may be 0 (nothing to do beyond zero
- * outputs, FM_OK); head_dim d must be 64 or 128.  softmax_scale <= 0 selects 1/sqrt(d).
+ * outputs, FM_OK); head_dim d must be 64, 128 or 256.  softmax_scale <= 0 selects 1/sqrt(d).
  * seqlen is N_q; seqlen_kv is N_k, with 0 meaning N_k = N_q (so N_q > 0 rows without
  * keys cannot be expressed; their result is O = 0, LSE = -inf).  mask_heads is H_m, the
  * vector sets per batch row; 0 means 1.  H_m must divide heads_q (when heads_q > 0) and

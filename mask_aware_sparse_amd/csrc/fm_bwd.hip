@@ -78,15 +78,15 @@ namespace dkdv {
 constexpr int kWaves = kBwdBlockK / 32;
 constexpr int BQ = kBwdBlockQ;  // 32 query rows per step
 constexpr int BK = kBwdBlockK;  // 128 keys per workgroup
-constexpr int KS = kHeadDim + 8;  // K row stride in LDS (272 B: row reads only)
 static_assert(BK == 32 * kWaves, "one 32-key slice per wave");
 
-// Q / dO tiles use the swizzled 320-byte layout (row reads and transposing reads).
-template <bool kMulti>
+// Q / dO tiles use the swizzled layout (row reads and transposing reads; 320-byte rows at
+// D <= 128), K rows are read row-wise only (272 bytes).
+template <int D, bool kMulti>
 struct __attribute__((aligned(16))) Smem {
-  bf16 q[2][BQ * kSwzRow];
-  bf16 dO[2][BQ * kSwzRow];
-  bf16 k[BK * KS];
+  bf16 q[2][BQ * LdsRows<D>::SWZ];
+  bf16 dO[2][BQ * LdsRows<D>::SWZ];
+  bf16 k[BK * LdsRows<D>::KS];
   // per key of the block: the four row bounds, or the interval starts ([0]) and ends ([1])
   int4 mv[kMulti ? 2 : 1][BK];
   float lse2[2][BQ];
@@ -296,12 +296,14 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_split(
 
 // kMulti: the mask is the multi-interval form (else the four-vector form).
 template <int D, bool kMulti>
-__global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvParams p) {
+__global__ __launch_bounds__(64 * dkdv::kWaves, D > 128 ? 1 : 2) void k_attn_bwd_dkdv(DkdvParams p) {
   using namespace dkdv;
+  constexpr int KS = LdsRows<D>::KS;    // K row stride in LDS (elements)
+  constexpr int kRow = LdsRows<D>::SWZ;  // swizzled Q / dO row stride
   constexpr int kS = D / 16;   // k-steps of a 32x32x16 product over D
   constexpr int kDB = D / 32;  // 32-column blocks of dK / dV
   constexpr int kCh = D / 8;   // 16-byte chunks per row
-  __shared__ Smem<kMulti> sm;
+  __shared__ Smem<D, kMulti> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
   const int N = p.Nk, Nq = p.Nq;  // N: keys (and mask columns)
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
   auto store_step = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < kCp; ++i) {
-      const int o = swz(cp_row + i * kCpRows, cp_ch);
+      const int o = swz<kRow>(cp_row + i * kCpRows, cp_ch);
       *reinterpret_cast<u32x4*>(&sm.q[buf][o]) = qst[i];
       *reinterpret_cast<u32x4*>(&sm.dO[buf][o]) = ost[i];
     }
@@ -428,8 +430,8 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
   lds_barrier();
 
   const int arow = perm_rows(l32);
-  const SwzRowRead rr(arow, hh);
-  const SwzTrRead tr(lane, hh);
+  const SwzRowRead<kRow> rr(arow, hh);
+  const SwzTrRead<kRow> tr(lane, hh);
   const bf16* kp = &sm.k[(wave * 32 + l32) * KS + hh * 8];
 
   // steps walk (head hi, queue entry it) with it fastest
@@ -452,7 +454,7 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
       {
         bf16x8 kf[2], qf[2], of[2];
         auto rd = [&](int s, int slot) {
-          const int o = rr.at(s) + qblk * 32 * kSwzRow;
+          const int o = rr.at(s) + qblk * 32 * kRow;
           kf[slot] = *reinterpret_cast<const bf16x8*>(kp + s * 16);
           qf[slot] = *reinterpret_cast<const bf16x8*>(&sm.q[cur][o]);
           of[slot] = *reinterpret_cast<const bf16x8*>(&sm.dO[cur][o]);
@@ -583,12 +585,13 @@ __global__ __launch_bounds__(64 * dkdv::kWaves, 2) void k_attn_bwd_dkdv(DkdvPara
 namespace dqk {
 constexpr int BQ = kFwdBlockQ;  // 128 query rows: 4 waves x 32
 constexpr int BK = kFwdBlockK;  // 64 keys per tile
-constexpr int VS = kHeadDim + 8;  // V row stride (272 B: row reads only)
 
-// K tiles use the swizzled 320-byte layout (row reads and transposing reads).
+// K tiles use the swizzled layout (row reads and transposing reads; 320-byte rows at D <=
+// 128), V rows are read row-wise only (272 bytes).
+template <int D>
 struct __attribute__((aligned(16))) Smem {
-  bf16 k[2][BK * kSwzRow];
-  bf16 v[2][BK * VS];
+  bf16 k[2][BK * LdsRows<D>::SWZ];
+  bf16 v[2][BK * LdsRows<D>::KS];
   uint32_t mw[2][4][BK];  // hidden-row words: [buffer][wave][key]
 };
 }  // namespace dqk
@@ -613,14 +616,16 @@ struct DqParams {
 };
 
 template <int D, bool kMulti>
-__global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
+__global__ __launch_bounds__(256, D > 128 ? 1 : 2) void k_attn_bwd_dq(DqParams p) {
   using namespace dqk;
+  constexpr int kRow = LdsRows<D>::SWZ;  // swizzled K row stride (elements)
+  constexpr int VS = LdsRows<D>::KS;     // V row stride (row reads only)
   constexpr int kS = D / 16;               // k-steps of a 32x32x16 product over D
   constexpr int kDB = D / 32;              // 32-column blocks of dQ
   constexpr int kCh = D / 8;               // 16-byte chunks per row
   constexpr int kRowsPass = 256 / kCh;     // rows one pass of the tile copy covers
   constexpr int kPasses = BK / kRowsPass;  // passes per 64-row tile
-  __shared__ Smem sm;
+  __shared__ Smem<D> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
 
@@ -665,12 +670,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
 
   const int cp_row = tid / kCh, cp_ch = (tid % kCh) * 8;
   const int mk_key = lane, mk_wave = __builtin_amdgcn_readfirstlane(wave);
-  // D = 128: tiles go from memory straight into LDS, one 16-byte slot per lane and load
-  // (load j, lane l: slot 64 j + l of the padded tile; K rows hold 20 slots, 16 of them
-  // data under the XOR swizzle, V rows 17), pad slots taking a copy of the row's first
-  // chunk.  Wave w issues loads j = w, w + 4, ... (K: 20, V: 17).
-  constexpr bool kDma = D == 128;
-  constexpr int kKSlots = kSwzRow * 2 / 16, kVSlots = VS * 2 / 16;
+  // D >= 128: tiles go from memory straight into LDS, one 16-byte slot per lane and load
+  // (load j, lane l: slot 64 j + l of the padded tile; at D = 128 K rows hold 20 slots, 16
+  // of them data under the XOR swizzle, V rows 17; at D = 256, 36 (32) and 33), pad slots
+  // taking a copy of the row's first chunk.  Wave w issues loads j = w, w + 4, ...
+  constexpr bool kDma = D >= 128;
+  constexpr int kKSlots = kRow * 2 / 16, kVSlots = VS * 2 / 16;
   constexpr int kKLoads = BK * kKSlots / 64, kVLoads = BK * kVSlots / 64;
   constexpr int kDmaPer = (kKLoads + 3) / 4;
   uint32_t koff[kDma ? kDmaPer : 1], voff[kDma ? kDmaPer : 1];
@@ -687,7 +692,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   u32x4 kst[kDma ? 1 : kPasses], vst[kDma ? 1 : kPasses];
   uint32_t vec[kMulti ? 2 * kMaxIntervals : 4];
 
-  // load_tile(e, buf): D = 128 writes buffer buf directly; otherwise stages in registers
+  // load_tile(e, buf): D >= 128 writes buffer buf directly; otherwise stages in registers
   // for store_tile
   auto load_tile = [&](int e, int buf) {
     const int kb = e & 0x7fffffff;
@@ -728,7 +733,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
     if constexpr (!kDma) {
 #pragma unroll
       for (int i = 0; i < kPasses; ++i) {
-        *reinterpret_cast<u32x4*>(&sm.k[buf][swz(cp_row + kRowsPass * i, cp_ch >> 3)]) = kst[i];
+        *reinterpret_cast<u32x4*>(&sm.k[buf][swz<kRow>(cp_row + kRowsPass * i, cp_ch >> 3)]) = kst[i];
         *reinterpret_cast<u32x4*>(&sm.v[buf][(cp_row + kRowsPass * i) * VS + cp_ch]) = vst[i];
       }
     }
@@ -788,8 +793,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
   lds_barrier();
 
   const int arow = perm_rows(l32);
-  const SwzRowRead rr(arow, hh);
-  const SwzTrRead tr(lane, hh);
+  const SwzRowRead<kRow> rr(arow, hh);
+  const SwzTrRead<kRow> tr(lane, hh);
 
   int e = n_tiles > 0 ? queue[0] : 0;
   for (int it = 0; it < n_tiles; ++it) {
@@ -811,7 +816,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(DqParams p) {
       constexpr int kSt = 2 * kS;
       auto kread = [&](int i) {
         return *reinterpret_cast<const bf16x8*>(
-            &sm.k[cur][rr.at(i % kS) + (i / kS) * 32 * kSwzRow]);
+            &sm.k[cur][rr.at(i % kS) + (i / kS) * 32 * kRow]);
       };
       auto vread = [&](int i) {
         return *reinterpret_cast<const bf16x8*>(
@@ -991,8 +996,9 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   const bool multi = a.m.n > 0;
   const bool d64 = a.D == 64;
   if (qgrid > 0) {
-    auto kern = d64 ? (multi ? k_attn_bwd_dq<64, true> : k_attn_bwd_dq<64, false>)
-                    : (multi ? k_attn_bwd_dq<128, true> : k_attn_bwd_dq<128, false>);
+    auto kern = d64          ? (multi ? k_attn_bwd_dq<64, true> : k_attn_bwd_dq<64, false>)
+                : a.D == 256 ? (multi ? k_attn_bwd_dq<256, true> : k_attn_bwd_dq<256, false>)
+                             : (multi ? k_attn_bwd_dq<128, true> : k_attn_bwd_dq<128, false>);
     hipLaunchKernelGGL(kern, dim3(qgrid), dim3(256), 0, s, q);
   }
   if (ev.dq_stop) (void)hipEventRecord(ev.dq_stop, s);
@@ -1040,6 +1046,8 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   if (ev.dkdv_start) (void)hipEventRecord(ev.dkdv_start, s);
   if (grid > 0) {
     auto kern = d64 ? (multi ? k_attn_bwd_dkdv<64, true> : k_attn_bwd_dkdv<64, false>)
+                : a.D == 256
+                    ? (multi ? k_attn_bwd_dkdv<256, true> : k_attn_bwd_dkdv<256, false>)
                     : (multi ? k_attn_bwd_dkdv<128, true> : k_attn_bwd_dkdv<128, false>);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * dkdv::kWaves), 0, s, p);
   }

@@ -133,19 +133,22 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // 320 bytes with the 16-byte chunk index XORed by bits 2..3 of the row.  Both access
 // patterns then hit distinct LDS banks (measured with the SQ_LDS_BANK_CONFLICT counter:
 // plain 288-byte rows stall row reads, plain 272-byte rows stall transposing reads).
-constexpr int kSwzRow = 160;  // elements per row (320 bytes)
+constexpr int kSwzRow = 160;  // elements per row (320 bytes) of the 128-wide layout
+// (the 256-wide layout uses rows of 288 elements with the same XOR)
+template <int kRow = kSwzRow>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kSwzRow + ((chunk ^ ((row >> 2) & 3)) << 3);
+  return row * kRow + ((chunk ^ ((row >> 2) & 3)) << 3);
 }
 
 // Row-read fragments of a swizzled tile: element offset of the 16-byte fragment for
 // d-step s (columns s*16 + hh*8 .. +7) of `row`.  The XOR only flips the low two chunk
 // bits, so per lane this is one of two bases plus 16*s.
+template <int kRow = kSwzRow>
 struct SwzRowRead {
   int even, odd;
   __device__ __forceinline__ SwzRowRead(int row, int hh) {
     const int f = (row >> 2) & 3;
-    const int base = row * kSwzRow + 8 * (hh ^ (f & 1));
+    const int base = row * kRow + 8 * (hh ^ (f & 1));
     even = base + 16 * (f >> 1);
     odd = base - 16 * (f >> 1);
   }
@@ -153,18 +156,31 @@ struct SwzRowRead {
 };
 // Transposing-read addresses of a swizzled tile for rows r0 + 4u (r0 = 16*ks + 8*hh +
 // (lane&15)/4, u = 0, 1) and the 32-column block d: per lane two bases plus immediates.
+template <int kRow = kSwzRow>
 struct SwzTrRead {
   int b0, b1;
   __device__ __forceinline__ SwzTrRead(int lane, int hh) {
     const int tr_row = (lane & 15) >> 2;
     const int chunk = ((lane >> 4) & 1) * 2 + ((lane & 3) >> 1);
     const int sub = 4 * (lane & 1);
-    b0 = (hh * 8 + tr_row) * kSwzRow + 8 * (chunk ^ (2 * hh)) + sub;
-    b1 = (hh * 8 + tr_row + 4) * kSwzRow + 8 * (chunk ^ (2 * hh + 1)) + sub;
+    b0 = (hh * 8 + tr_row) * kRow + 8 * (chunk ^ (2 * hh)) + sub;
+    b1 = (hh * 8 + tr_row + 4) * kRow + 8 * (chunk ^ (2 * hh + 1)) + sub;
   }
   __device__ __forceinline__ int at(int u, int ks, int d) const {
-    return (u ? b1 : b0) + ks * 16 * kSwzRow + 32 * d;
+    return (u ? b1 : b0) + ks * 16 * kRow + 32 * d;
   }
+};
+
+// LDS row strides (elements) for head dimension D: the 128-wide layouts serve D <= 128 (a
+// fragment read's bank pattern depends only on the row stride, so D = 64 uses the first
+// half of each row); D = 256 has its own.  KS: rows read only row-wise; TS: rows also read
+// by transposing reads (unswizzled); SWZ: swizzled rows.
+template <int D>
+struct LdsRows {
+  static constexpr int W = D > 128 ? D : 128;
+  static constexpr int KS = W + 8;
+  static constexpr int TS = W + 32;
+  static constexpr int SWZ = W + 32;
 };
 
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16

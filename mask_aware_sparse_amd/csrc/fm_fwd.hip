@@ -28,15 +28,12 @@ namespace {
 
 constexpr int BQ = kFwdBlockQ;  // 128
 constexpr int BK = kFwdBlockK;  // 64
-// LDS row strides are those of the largest head dimension (128) for every D: the bank
-// pattern of a fragment read depends only on the row stride, so the conflict-free layouts
-// carry over to D = 64 (which uses the first half of each row).
-constexpr int KS = kHeadDim + 8;   // K row stride in LDS (elements)
-constexpr int VS = kHeadDim + 32;  // V row stride in LDS (320 B: conflict-free transposing reads)
-
+// LDS rows per head dimension (LdsRows): K rows are read row-wise only (128-wide: 272 B),
+// V rows also by transposing reads (128-wide: 320 B, conflict-free for both).
+template <int D>
 struct __attribute__((aligned(16))) FwdSmem {
-  bf16 k[2][BK * KS];
-  bf16 v[2][BK * VS];
+  bf16 k[2][BK * LdsRows<D>::KS];
+  bf16 v[2][BK * LdsRows<D>::TS];
   uint32_t mw[2][4][BK];  // hidden-row words: [buffer][wave][key]
 };
 
@@ -72,18 +69,24 @@ struct FwdParams {
   float c;  // softmax scale * log2(e)
 };
 
-// D: head dimension (64 or 128).  kMulti: the mask is the multi-interval form (else the
-// four-vector form).
+// D: head dimension (64, 128 or 256).  kMulti: the mask is the multi-interval form (else the
+// four-vector form).  D = 256 runs one workgroup per CU (its tiles take 143 KB of LDS), with
+// up to 512 registers per lane.
 template <int D, bool kMulti>
-__global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
+__global__ __launch_bounds__(256, D > 128 ? 1 : 2) void k_attn_fwd(FwdParams p) {
+  constexpr int KS = LdsRows<D>::KS;  // K row stride in LDS (elements)
+  constexpr int VS = LdsRows<D>::TS;  // V row stride in LDS
   constexpr int kS = D / 16;                // k-steps of a 32x32x16 product over D
   constexpr int kDB = D / 32;               // 32-column blocks of O
   constexpr int kCh = D / 8;                // 16-byte chunks per row
   constexpr int kRowsPass = 256 / kCh;      // rows one pass of the tile copy covers
   constexpr int kPasses = BK / kRowsPass;   // passes per 64-row tile
   constexpr int kSteps = 2 * kS;            // score MFMAs per tile
-  constexpr int kExp = 16 / kSteps;         // exponential pairs per score MFMA
-  __shared__ FwdSmem sm;
+  // the 16 exponential pairs of a tile spread over its kSteps score MFMAs: kExp pairs per
+  // step (D <= 128), or one pair every kEvery steps (D = 256)
+  constexpr int kExp = kSteps <= 16 ? 16 / kSteps : 1;
+  constexpr int kEvery = kSteps <= 16 ? 1 : kSteps / 16;
+  __shared__ FwdSmem<D> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
 
@@ -157,12 +160,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
   const int cp_row = tid / kCh, cp_ch = (tid % kCh) * 8;
   const int mk_key = lane, mk_wave = __builtin_amdgcn_readfirstlane(wave);
   constexpr int kVec = kMulti ? 2 * kMaxIntervals : 4;
-  // D = 128: tiles go from memory straight into LDS (buffer loads with the LDS flag), no
+  // D >= 128: tiles go from memory straight into LDS (buffer loads with the LDS flag), no
   // staging registers.  Each such load writes 64 consecutive 16-byte LDS slots, one per
-  // lane, so lane l of load j covers slot 64 j + l of the padded tile (K: 17 slots a row,
-  // V: 20) and fetches the 16 bytes that belong there; pad slots take a copy of the row's
-  // first chunk.  Wave w issues loads j = w, w + 4, ... (K: 17 loads, V: 20).
-  constexpr bool kDma = D == 128;
+  // lane, so lane l of load j covers slot 64 j + l of the padded tile (K: 17 slots a row at
+  // D = 128, 33 at 256; V: 20, 36) and fetches the 16 bytes that belong there; pad slots
+  // take a copy of the row's first chunk.  Wave w issues loads j = w, w + 4, ...
+  constexpr bool kDma = D >= 128;
   constexpr int kKSlots = KS * 2 / 16, kVSlots = VS * 2 / 16;
   constexpr int kKLoads = BK * kKSlots / 64, kVLoads = BK * kVSlots / 64;
   constexpr int kDmaPer = (kVLoads + 3) / 4;
@@ -388,7 +391,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
         const int blk = i / kS, st = i % kS;
         sn[blk] = mfma32(kf[i % 3], qr[st], st == 0 ? f32x16{} : sn[blk]);
 #pragma unroll
-        for (int e = 0; e < kExp; ++e) exp_pair(i * kExp + e, off0);
+        for (int e = 0; e < kExp; ++e)
+          if (i % kEvery == 0) exp_pair((i / kEvery) * kExp + e, off0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -499,8 +503,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_
   if (ev0) (void)hipEventRecord(ev0, s);
   if (grid > 0) {
     const bool multi = a.m.n > 0;
-    auto kern = a.D == 64 ? (multi ? k_attn_fwd<64, true> : k_attn_fwd<64, false>)
-                          : (multi ? k_attn_fwd<128, true> : k_attn_fwd<128, false>);
+    auto kern = a.D == 64    ? (multi ? k_attn_fwd<64, true> : k_attn_fwd<64, false>)
+                : a.D == 256 ? (multi ? k_attn_fwd<256, true> : k_attn_fwd<256, false>)
+                             : (multi ? k_attn_fwd<128, true> : k_attn_fwd<128, false>);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, p);
   }
   hipError_t e = hipGetLastError();

@@ -7,10 +7,10 @@
 
 namespace fm {
 
-// Head dimensions the kernels are built for; buffers and LDS strides are sized for the
-// largest.
+// Head dimensions the kernels are built for.  D = 256 runs one workgroup per CU (its LDS
+// tiles take 143 KB); the others two.
 constexpr int kHeadDim = 128;
-inline bool head_dim_supported(int d) { return d == 64 || d == 128; }
+inline bool head_dim_supported(int d) { return d == 64 || d == 128 || d == 256; }
 
 // Tile shapes of the attention kernels.  The forward (and the backward's dQ kernel) uses
 // 128 query rows (4 waves x 32) by 64 keys; the backward's dK/dV kernel 32 query rows by

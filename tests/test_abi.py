@@ -106,7 +106,8 @@ def test_workspace_sizes():
     (dict(N=-1), INVALID),
     (dict(B=-2), INVALID),
     (dict(d=96), UNSUPPORTED),
-    (dict(d=256), UNSUPPORTED),
+    (dict(d=512), UNSUPPORTED),
+    (dict(d=32), UNSUPPORTED),
     (dict(N=1 << 30), UNSUPPORTED),
     (dict(B=1100, N=1 << 21), UNSUPPORTED),  # more than 2^24 KV blocks to sort
 ])

@@ -407,6 +407,8 @@ VARIANTS = {
     "v3_prefix_lm_doc_8k_d64": lambda seed=0: with_head_dim(prefix_lm_doc(seed), 64),
     # block-sparse masks: BigBird-style 128 x 128 block grid (window, global, random blocks)
     "v4_bigbird_blocks_32k": lambda seed=0: bigbird_blocks(seed),
+    # head dimension 256: the prefix-LM document workload (B=4, 32/8 heads, N=8192) at d=256
+    "v5_prefix_lm_doc_8k_d256": lambda seed=0: with_head_dim(prefix_lm_doc(seed), 256),
 }
 VARIANT_NAMES = list(VARIANTS)
 
