@@ -9,7 +9,6 @@ namespace fm {
 
 // Head dimensions the kernels are built for.  D = 256 runs one workgroup per CU (its LDS
 // tiles take 143 KB); the others two.
-constexpr int kHeadDim = 128;
 inline bool head_dim_supported(int d) { return d == 64 || d == 128 || d == 256; }
 
 // Tile shapes of the attention kernels.  The forward (and the backward's dQ kernel) uses
@@ -36,7 +35,7 @@ constexpr int64_t kMaxWorkItems = 1 << 24;
 // against the average load per workgroup slot is cut into at most kSplitMaxSegs segments
 // of its queue; at most kSplitExtraUnits extra workgroups are added per launch.  Where the
 // kernel would store bf16 directly, the segments write fp32 partial sums (one slot of
-// kBwdBlockK x 128 per segment and tensor) that a reduction kernel adds in segment order.
+// kBwdBlockK x D per segment and tensor) that a reduction kernel adds in segment order.
 constexpr int kSplitMaxSegs = 16;
 constexpr int kSplitExtraUnits = 512;
 constexpr int kSplitMinSteps = 16;   // no segment shorter than this many tile steps
@@ -175,10 +174,10 @@ struct BwdArgs {
   const int32_t* q_order;
   float* lse2;   // [B][Hq][Nq] log2-domain LSE (+inf for rows that see nothing)
   float* delta;  // [B][Hq][Nq] rowsum(dO * O)
-  float* dk_acc; // [B][Hkv][Nk][128] fp32, only when head_map(...).writers > 1 (else null)
-  float* dv_acc; // [B][Hkv][Nk][128] fp32, likewise
+  float* dk_acc; // [B][Hkv][Nk][D] fp32, only when head_map(...).writers > 1 (else null)
+  float* dv_acc; // [B][Hkv][Nk][D] fp32, likewise
   // dK/dV work units (split plan): unit_pair / unit_slot [pairs + extra], split_pair /
-  // split_slot [extra], counts[2] = {units, split pairs}; partials [2][slots][BK][128] fp32
+  // split_slot [extra], counts[2] = {units, split pairs}; partials [2][slots][BK][D] fp32
   // (only when writers == 1)
   int32_t* unit_pair;
   int32_t* unit_slot;
