@@ -28,6 +28,9 @@ Contents and the passage each part follows:
                 rows (FlashMask-3 page, §3.2, Theorem 1).
   ipo.py        stage-1 chunk balancing over ranks: LPT, pairwise and three-rank
                 repartition (FlashMask-3 page, §3.3 and the IPO ablation table).
+  keyorder.py   reordering of the key columns within super-blocks so that columns
+                with similar bounds share tiles (this library's own step; attention
+                is invariant under a joint permutation of K, V and the vectors).
   schedule.py   list scheduling of weighted work items over P slots, the lower
                 bound max(ceil(sum/P), max w) and a brute-force optimum
                 (FlashMask-3 page, §3.3 and the IPO ablation table).
@@ -55,6 +58,7 @@ from .tiles import (block_minmax, classify, tile_truth, queues, tile_costs, lpt_
                     ALPHA_PARTIAL, ALPHA_UNMASKED)
 from .schedule import list_schedule, lower_bound, brute_force_optimum
 from .localize import rank_rows, localize, localize_max_form, localize_vectors
+from .keyorder import key_order, key_order_rows, spread
 from . import ipo
 
 __all__ = [
@@ -69,5 +73,5 @@ __all__ = [
     "tile_truth", "block_minmax_multi", "classify_multi", "tile_truth_multi",
     "queues", "tile_costs", "lpt_order", "ALPHA_PARTIAL", "ALPHA_UNMASKED",
     "list_schedule", "lower_bound", "brute_force_optimum", "rank_rows", "localize",
-    "localize_max_form", "localize_vectors", "ipo",
+    "localize_max_form", "localize_vectors", "ipo", "key_order", "key_order_rows", "spread",
 ]
