@@ -48,6 +48,9 @@ import workloads  # noqa: E402
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16: 256 CU x 2.4 GHz x 4096 flop/clk/CU
 DEFAULT_WORKLOAD = "c2_prefix_lm_doc_8k"
+# workloads timed with their keys reordered (fm_problem.key_order = FM_KEYS_SORTED) unless
+# --key-order says otherwise: the random-eviction mask, whose columns end at scattered rows
+SORTED_KEY_WORKLOADS = {"c5_random_eviction_128k"}
 
 
 def attended_pairs(w):
@@ -426,6 +429,9 @@ def main():
                     help="host chunk balancer on the IPO ablation configurations")
     ap.add_argument("--measure-alpha", action="store_true",
                     help="time partial against unmasked tiles on identical work")
+    ap.add_argument("--key-order", choices=["auto", "natural", "sorted"], default="auto",
+                    help="key order of the four-vector entry points (auto: sorted for the "
+                         "random-eviction workload, natural otherwise)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; multi-GPU runs are not supported",
@@ -459,19 +465,27 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty((w.batch, w.heads_q, w.seqlen), dtype=torch.float32, device=dev)
     grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-    ws_f = torch.empty(fm.workspace_size(w.batch, w.heads_q, w.heads_kv, w.seqlen, fm.OP_FWD,
-                                         head_dim=w.head_dim, mask_heads=w.mask_heads),
-                       dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(fm.workspace_size(w.batch, w.heads_q, w.heads_kv, w.seqlen, fm.OP_BWD,
-                                         head_dim=w.head_dim, mask_heads=w.mask_heads),
-                       dtype=torch.uint8, device=dev)
     multi = isinstance(w, workloads.MultiWorkload)
     blocks = isinstance(w, workloads.BlockWorkload)
+    sorted_keys = (args.key_order == "sorted" or
+                   (args.key_order == "auto" and args.workload in SORTED_KEY_WORKLOADS))
+    if sorted_keys and (multi or blocks):
+        sys.exit("bench.py: --key-order sorted applies to four-vector masks only")
+    key_order = fm.KEYS_SORTED if sorted_keys else fm.KEYS_NATURAL
+    ws_f = torch.empty(fm.workspace_size(w.batch, w.heads_q, w.heads_kv, w.seqlen, fm.OP_FWD,
+                                         head_dim=w.head_dim, mask_heads=w.mask_heads,
+                                         key_order=key_order),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(fm.workspace_size(w.batch, w.heads_q, w.heads_kv, w.seqlen, fm.OP_BWD,
+                                         head_dim=w.head_dim, mask_heads=w.mask_heads,
+                                         key_order=key_order),
+                       dtype=torch.uint8, device=dev)
     A = attended_pairs_blocks(w) if blocks else (attended_pairs_multi(w) if multi
                                                  else attended_pairs(w))
     d = w.head_dim
     attn_fwd = fm.attn_fwd_blocks if blocks else (fm.attn_fwd_multi if multi else fm.attn_fwd)
     attn_bwd = fm.attn_bwd_blocks if blocks else (fm.attn_bwd_multi if multi else fm.attn_bwd)
+    opt = {} if (multi or blocks) else {"key_order": key_order}
 
     # per instrumented step: 0 start, 1/2 fwd kernel, 8 between the calls, 3/4 dK/dV
     # kernel, 6/7 dQ kernel, 5 end (all on the current stream, which the library launches
@@ -484,11 +498,11 @@ def main():
         if e is not None:
             e[0].record()
         attn_fwd(q, k, v, *vec, ws=ws_f, out=o, lse=lse,
-                 events=None if e is None else (e[1], e[2]))
+                 events=None if e is None else (e[1], e[2]), **opt)
         if e is not None:
             e[8].record()
         attn_bwd(q, k, v, o, lse, do, *vec, ws=ws_b, grads=grads,
-                 events=None if e is None else (e[3], e[4], e[6], e[7]))
+                 events=None if e is None else (e[3], e[4], e[6], e[7]), **opt)
         if e is not None:
             e[5].record()
 
@@ -541,7 +555,8 @@ def main():
                    "heads_kv": w.heads_kv, "mask_heads": w.mask_heads,
                    "mask_intervals": w.n_intervals if multi else None,
                    "mask_blocks": "128x128" if blocks else None, "seq_len": w.seqlen,
-                   "head_dim": d, "attended_pairs": A, "seed": args.seed},
+                   "head_dim": d, "attended_pairs": A, "seed": args.seed,
+                   "key_order": "sorted" if sorted_keys else "natural"},
         "pct_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
         "kernels": {kname: {"ms": round(t, 4), "algorithmic_tflops": round(tflops[kname], 2)}
                     for kname, (t, _) in kernels.items()},

@@ -87,7 +87,21 @@ typedef struct {
   float softmax_scale;
   int32_t seqlen_kv;
   int32_t mask_heads;
+  int32_t key_order; /* FM_KEYS_NATURAL (0) or FM_KEYS_SORTED (1), see fm_key_order */
 } fm_problem;
+
+/* Key order of fm_attn_fwd / fm_attn_bwd (four-vector masks).  FM_KEYS_SORTED runs the
+ * attention kernels over the keys in the order fm_key_order gives: K, V and the vectors are
+ * gathered into that order in the workspace first, dK and dV scattered back after, so every
+ * output is in the caller's key order and O, LSE, dQ, dK, dV are the same attention (up to
+ * the fp32 summation order).  It pays where the columns' bounds are scattered (a
+ * random-eviction mask); on masks whose sorted order is not narrower it only adds the
+ * gathers.  FM_KEYS_SORTED is FM_ERR_UNSUPPORTED with the _multi and _blocks entry points
+ * and when mask_heads > heads_kv (one kv head would need two orders).  fm_classify_tiles
+ * ignores key_order (it classifies the vectors as given); values other than 0 and 1 are
+ * FM_ERR_INVALID_ARG everywhere. */
+#define FM_KEYS_NATURAL 0
+#define FM_KEYS_SORTED 1
 
 /* The four column vectors, each int32 [B][H_m][N_k] in device memory. */
 typedef struct {
@@ -209,6 +223,28 @@ typedef struct {
 fm_status fm_localize_mask(const fm_problem* p, const fm_mask* global, const int32_t* offsets,
                            int32_t n_chunks, int32_t chunk_len, const fm_mask_out* local,
                            void* stream);
+
+/* Key order of each mask row (this library's own step; the pages classify blocks of
+ * consecutive keys only).  Attention does not depend on the order of the key columns, but
+ * the tile rule of the FlashMask-3 page (§3.1) sees a block of consecutive columns through
+ * the min/max of their bounds, so columns that end at scattered rows (the page's
+ * random-eviction mask, §4) leave nearly every tile partial.  Per mask row r and super-block
+ * of FM_KEY_ORDER_SPAN consecutive keys [s0, s0 + FM_KEY_ORDER_SPAN) (the last one cut at
+ * N_k), the keys are sorted by LTS, ties by key index; the super-block takes that order iff
+ * its spread is strictly smaller than the natural order's, where spread = the sum, over
+ * groups of FM_KEY_ORDER_GROUP consecutive positions (the last one cut) and over the four
+ * vectors, of max - min of the bounds clipped to [0, N_q].  Keys never leave their
+ * super-block.
+ *   perm      device int32 [B][H_m][N_k], written: position p of row r holds key perm[p]
+ *   permuted  NULL, or device arrays (int32 [B][H_m][N_k] each; members may be NULL)
+ *             receiving the vectors in that order: permuted->lts[p] = lts[perm[p]], ...
+ * p->seqlen (N_q), seqlen_kv, batch and mask_heads are used; heads and head_dim are not.
+ * One workgroup per (mask row, super-block); asynchronous on `stream`.  Errors:
+ * FM_ERR_INVALID_ARG for null pointers with a non-empty problem. */
+#define FM_KEY_ORDER_SPAN 2048
+#define FM_KEY_ORDER_GROUP 64
+fm_status fm_key_order(const fm_problem* p, const fm_mask* m, int32_t* perm,
+                       const fm_mask_out* permuted, void* stream);
 
 /* ---- Multi-interval column masks -------------------------------------------------------
  * The FlashMask Guide ("Multi-Interval Sparse Masks") generalizes the column-wise form to

@@ -24,11 +24,14 @@ __all__ = [
     "attn_fwd", "attn_bwd", "debug_expand_mask", "status_string",
     "fm_tile_shape", "fm_workspace_size", "fm_classify_tiles", "fm_attn_fwd", "fm_attn_bwd",
     "fm_debug_expand_mask", "fm_status_string",
-    "OP_CLASSIFY", "OP_FWD", "OP_BWD", "HEAD_DIM",
+    "OP_CLASSIFY", "OP_FWD", "OP_BWD", "HEAD_DIM", "key_order", "fm_key_order",
+    "KEYS_NATURAL", "KEYS_SORTED", "KEY_ORDER_SPAN", "KEY_ORDER_GROUP",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 OP_CLASSIFY, OP_FWD, OP_BWD = 0, 1, 2
+KEYS_NATURAL, KEYS_SORTED = 0, 1      # fm_problem.key_order
+KEY_ORDER_SPAN, KEY_ORDER_GROUP = 2048, 64
 HEAD_DIM = 128
 FM_OK = 0
 
@@ -47,7 +50,8 @@ class Problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32),
                 ("heads_kv", ctypes.c_int32), ("seqlen", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
-                ("seqlen_kv", ctypes.c_int32), ("mask_heads", ctypes.c_int32)]
+                ("seqlen_kv", ctypes.c_int32), ("mask_heads", ctypes.c_int32),
+                ("key_order", ctypes.c_int32)]
 
 
 class MaskOut(ctypes.Structure):
@@ -113,6 +117,7 @@ def library():
                                       _P, _P], _STATUS),
             "fm_localize_mask": ([PP, PM, _P, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.POINTER(MaskOut), _P], _STATUS),
+            "fm_key_order": ([PP, PM, _P, ctypes.POINTER(MaskOut), _P], _STATUS),
             "fm_classify_tiles_multi": ([PP, PX, ctypes.c_int32, ctypes.c_int32, PT, _P,
                                          ctypes.c_size_t, _P], _STATUS),
             "fm_attn_fwd_multi": ([PP, _P, _P, _P, PX, _P, _P, _P, ctypes.c_size_t, _P, PE],
@@ -150,9 +155,10 @@ def _check(status, where):
 
 
 def _problem(batch, heads_q, heads_kv, seqlen, scale=None, head_dim=HEAD_DIM, seqlen_kv=0,
-             mask_heads=0):
+             mask_heads=0, key_order=KEYS_NATURAL):
     return Problem(int(batch), int(heads_q), int(heads_kv), int(seqlen), int(head_dim),
-                   float(scale) if scale is not None else 0.0, int(seqlen_kv), int(mask_heads))
+                   float(scale) if scale is not None else 0.0, int(seqlen_kv), int(mask_heads),
+                   int(key_order))
 
 
 def _mask(lts, lte, uts, ute):
@@ -191,12 +197,13 @@ def tile_shape(op: int):
 
 
 def workspace_size(batch, heads_q, heads_kv, seqlen, op, block_q=0, block_k=0, head_dim=HEAD_DIM,
-                   seqlen_kv=0, mask_heads=0):
-    """Workspace bytes for N_q = seqlen query rows, N_k = seqlen_kv keys (0: N_q) and
-    mask_heads vector sets per batch row (0: 1)."""
+                   seqlen_kv=0, mask_heads=0, key_order=KEYS_NATURAL):
+    """Workspace bytes for N_q = seqlen query rows, N_k = seqlen_kv keys (0: N_q),
+    mask_heads vector sets per batch row (0: 1) and the key order (KEYS_SORTED adds the
+    permuted K, V, vectors and, backward, dK, dV)."""
     n = ctypes.c_size_t()
     p = _problem(batch, heads_q, heads_kv, seqlen, head_dim=head_dim, seqlen_kv=seqlen_kv,
-                 mask_heads=mask_heads)
+                 mask_heads=mask_heads, key_order=key_order)
     _check(library().fm_workspace_size(ctypes.byref(p), int(op), int(block_q), int(block_k),
                                        ctypes.byref(n)), "fm_workspace_size")
     return n.value
@@ -371,13 +378,15 @@ def _events(ev):
     return ctypes.byref(KernelEvents(*handles))
 
 
-def _fwd(fn, q, k, v, m, mask_shape, scale, ws, out, lse, stream, events):
+def _fwd(fn, q, k, v, m, mask_shape, scale, ws, out, lse, stream, events, key_order=KEYS_NATURAL):
     _bf16(q, k, v)
     B, Hq, Hkv, N, Nk, d, Hm = _shapes(q, k, mask_shape)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    p = _problem(B, Hq, Hkv, N, scale, head_dim=d, seqlen_kv=Nk, mask_heads=Hm)
-    nbytes = workspace_size(B, Hq, Hkv, N, OP_FWD, head_dim=d, seqlen_kv=Nk, mask_heads=Hm)
+    p = _problem(B, Hq, Hkv, N, scale, head_dim=d, seqlen_kv=Nk, mask_heads=Hm,
+                 key_order=key_order)
+    nbytes = workspace_size(B, Hq, Hkv, N, OP_FWD, head_dim=d, seqlen_kv=Nk, mask_heads=Hm,
+                            key_order=key_order)
     w = _workspace(nbytes, q.device, ws)
     _check(fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(m), _ptr(o), _ptr(lse_t),
               _ptr(w), ctypes.c_size_t(nbytes), _stream(q.device, stream), _events(events)),
@@ -385,14 +394,17 @@ def _fwd(fn, q, k, v, m, mask_shape, scale, ws, out, lse, stream, events):
     return o, lse_t
 
 
-def _bwd(fn, q, k, v, o, lse, dout, m, mask_shape, scale, ws, grads, stream, events):
+def _bwd(fn, q, k, v, o, lse, dout, m, mask_shape, scale, ws, grads, stream, events,
+         key_order=KEYS_NATURAL):
     _bf16(q, k, v, o, dout)
     B, Hq, Hkv, N, Nk, d, Hm = _shapes(q, k, mask_shape)
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = grads
-    p = _problem(B, Hq, Hkv, N, scale, head_dim=d, seqlen_kv=Nk, mask_heads=Hm)
-    nbytes = workspace_size(B, Hq, Hkv, N, OP_BWD, head_dim=d, seqlen_kv=Nk, mask_heads=Hm)
+    p = _problem(B, Hq, Hkv, N, scale, head_dim=d, seqlen_kv=Nk, mask_heads=Hm,
+                 key_order=key_order)
+    nbytes = workspace_size(B, Hq, Hkv, N, OP_BWD, head_dim=d, seqlen_kv=Nk, mask_heads=Hm,
+                            key_order=key_order)
     w = _workspace(nbytes, q.device, ws)
     _check(fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
               ctypes.byref(m), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(w), ctypes.c_size_t(nbytes),
@@ -401,13 +413,14 @@ def _bwd(fn, q, k, v, o, lse, dout, m, mask_shape, scale, ws, grads, stream, eve
 
 
 def attn_fwd(q, k, v, lts, lte, uts, ute, scale=None, ws=None, out=None, lse=None, stream=None,
-             events=None):
+             events=None, key_order=KEYS_NATURAL):
     """O (bf16 [B][H_q][N_q][d]) and LSE (fp32 [B][H_q][N_q], natural log) via fm_attn_fwd;
     K/V are [B][H_kv][N_k][d] and the vectors [B][N_k] or, one set per group of H_q / H_m
     query heads, [B][H_m][N_k].
-    `events`: optional (start, stop) torch.cuda.Event pair timing the attention kernel."""
+    `events`: optional (start, stop) torch.cuda.Event pair timing the attention kernel.
+    `key_order`: KEYS_SORTED runs the kernels over the keys in fm_key_order's order."""
     return _fwd(library().fm_attn_fwd, q, k, v, _mask(lts, lte, uts, ute), _mask_dims(lts),
-                scale, ws, out, lse, stream, events)
+                scale, ws, out, lse, stream, events, key_order)
 
 
 def attn_fwd_multi(q, k, v, starts, ends, scale=None, ws=None, out=None, lse=None, stream=None,
@@ -437,11 +450,12 @@ def attn_bwd_blocks(q, k, v, o, lse, dout, blocks, scale=None, ws=None, grads=No
 
 
 def attn_bwd(q, k, v, o, lse, dout, lts, lte, uts, ute, scale=None, ws=None, grads=None,
-             stream=None, events=None):
+             stream=None, events=None, key_order=KEYS_NATURAL):
     """(dQ, dK, dV) in bf16 via fm_attn_bwd.  `events`: optional (start, stop, start2,
-    stop2) torch.cuda.Event objects timing the dK/dV kernel and the dQ kernel."""
+    stop2) torch.cuda.Event objects timing the dK/dV kernel and the dQ kernel.
+    `key_order`: as for attn_fwd; dK and dV come back in the caller's key order."""
     return _bwd(library().fm_attn_bwd, q, k, v, o, lse, dout, _mask(lts, lte, uts, ute),
-                _mask_dims(lts), scale, ws, grads, stream, events)
+                _mask_dims(lts), scale, ws, grads, stream, events, key_order)
 
 
 def attn_bwd_multi(q, k, v, o, lse, dout, starts, ends, scale=None, ws=None, grads=None,
@@ -505,6 +519,21 @@ def localize_mask(lts, lte, uts, ute, offsets, chunk_len, out=None, stream=None)
     return out
 
 
+def key_order(lts, lte, uts, ute, seqlen_q=None, permuted=False, stream=None):
+    """fm_key_order: the key permutation of each mask row (int32, the vectors' shape;
+    position p holds key perm[p]) and, with permuted=True, also the four vectors in that
+    order.  seqlen_q: N_q (default: N_k)."""
+    B, Hm, N = _mask_dims(lts)
+    perm = torch.empty_like(lts)
+    out = tuple(torch.empty_like(lts) for _ in range(4)) if permuted else None
+    p = _problem(B, 1, 1, N if seqlen_q is None else int(seqlen_q), seqlen_kv=N, mask_heads=Hm)
+    m = _mask(lts, lte, uts, ute)
+    mo = ctypes.byref(MaskOut(*(t.data_ptr() for t in out))) if permuted else None
+    _check(library().fm_key_order(ctypes.byref(p), ctypes.byref(m), _ptr(perm), mo,
+                                  _stream(lts.device, stream)), "fm_key_order")
+    return (perm, out) if permuted else perm
+
+
 def localize_mask_multi(starts, ends, offsets, chunk_len, out=None, stream=None):
     """fm_localize_mask_multi: every interval start and end renumbered into the rank's rows.
     Returns (starts, ends) of the input's shape."""
@@ -528,6 +557,7 @@ fm_attn_fwd = attn_fwd
 fm_attn_bwd = attn_bwd
 fm_debug_expand_mask = debug_expand_mask
 fm_localize_mask = localize_mask
+fm_key_order = key_order
 fm_classify_tiles_multi = classify_tiles_multi
 fm_attn_fwd_multi = attn_fwd_multi
 fm_attn_bwd_multi = attn_bwd_multi

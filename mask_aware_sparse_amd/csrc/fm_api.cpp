@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 namespace {
 
@@ -33,6 +34,7 @@ fm_status check_problem(const fm_problem* p) {
   if (p->heads_q % p->heads_kv != 0) return FM_ERR_INVALID_ARG;
   if (!fm::head_map_valid(p->heads_q, p->heads_kv, hm_of(p))) return FM_ERR_INVALID_ARG;
   if (!(p->softmax_scale <= 0.f || std::isfinite(p->softmax_scale))) return FM_ERR_INVALID_ARG;
+  if (p->key_order != FM_KEYS_NATURAL && p->key_order != FM_KEYS_SORTED) return FM_ERR_INVALID_ARG;
   if (!fm::head_dim_supported(p->head_dim)) return FM_ERR_UNSUPPORTED;
   // per-head buffers < 2 GiB
   if (nq_of(p) > (1 << 22) || nk_of(p) > (1 << 22)) return FM_ERR_UNSUPPORTED;
@@ -66,6 +68,16 @@ fm_status check_mask(const fm_problem* p, const fm_mask_blocks* m) {
   const int64_t nb = fm::kMaskBlock;
   if (mask_rows(p) * ((nq_of(p) + nb - 1) / nb) * ((nk_of(p) + nb - 1) / nb) == 0) return FM_OK;
   if (!m->blocks) return FM_ERR_INVALID_ARG;
+  return FM_OK;
+}
+
+// The key-order option: four-vector masks only, and each kv head in one mask set.
+inline bool sorted_keys(const fm_problem* p) { return p->key_order == FM_KEYS_SORTED; }
+template <typename MaskT>
+fm_status check_key_order(const fm_problem* p) {
+  if (!sorted_keys(p)) return FM_OK;
+  if (!std::is_same<MaskT, fm_mask>::value) return FM_ERR_UNSUPPORTED;
+  if (hm_of(p) > p->heads_kv) return FM_ERR_UNSUPPORTED;
   return FM_OK;
 }
 
@@ -123,7 +135,25 @@ ClassifyWs classify_ws(const fm_problem* p, const Blocks& nb) {
   return w;
 }
 
-struct FwdWs { size_t mm, q_queue, q_count, q_cost, q_order, sort, zeros, total; };
+// Buffers of the key-order option: the permutation, the vectors, K and V in that order,
+// and (backward) dK and dV in that order before they are scattered back.
+struct KeyWs { size_t perm, vec[4], k, v, dk, dv; };
+size_t key_ws(const fm_problem* p, size_t off, bool grads, KeyWs* w) {
+  if (!sorted_keys(p)) return off;
+  const size_t cols = (size_t)mask_rows(p) * nk_of(p);
+  const size_t rows = (size_t)p->batch * p->heads_kv * nk_of(p) * p->head_dim * 2;
+  w->perm = off; off += align_up(cols * 4);
+  for (int x = 0; x < 4; ++x) { w->vec[x] = off; off += align_up(cols * 4); }
+  w->k = off; off += align_up(rows);
+  w->v = off; off += align_up(rows);
+  if (grads) {
+    w->dk = off; off += align_up(rows);
+    w->dv = off; off += align_up(rows);
+  }
+  return off;
+}
+
+struct FwdWs { size_t mm, q_queue, q_count, q_cost, q_order, sort, zeros, total; KeyWs key; };
 FwdWs fwd_ws(const fm_problem* p, const Blocks& nb) {
   FwdWs w{};
   const size_t B = mask_rows(p);  // tile structures are per mask row
@@ -135,7 +165,7 @@ FwdWs fwd_ws(const fm_problem* p, const Blocks& nb) {
   w.q_order = off; off += align_up(B * nb.nQB * 4);
   w.sort = off; off += align_up(fm::lpt_sort_scratch_bytes((int64_t)B * nb.nQB));
   w.zeros = off; off += align_up(B * nk_of(p) * 4);  // block-sparse masks only
-  w.total = off;
+  w.total = key_ws(p, off, false, &w.key);
   return w;
 }
 
@@ -146,6 +176,7 @@ struct BwdWs {
   size_t unit_pair, unit_slot, split_pair, split_slot, split_counts, partials;  // split plan
   size_t sort;   // LPT sort scratch (lists longer than one workgroup sorts)
   size_t zeros;  // all-zero vectors standing for a block-sparse mask in the kernels
+  KeyWs key;     // key-order buffers
   size_t total;
   bool acc;   // fp32 dK/dV accumulators present
   int extra;  // extra pair units of the split plan
@@ -193,7 +224,7 @@ BwdWs bwd_ws(const fm_problem* p, const Blocks& nk, const Blocks& nq) {
     w.partials = off;
     off += align_up((size_t)2 * fm::split_slots(per, w.extra) * fm::kBwdBlockK * p->head_dim * 4);
   }
-  w.total = off;
+  w.total = key_ws(p, off, true, &w.key);
   return w;
 }
 
@@ -300,6 +331,25 @@ fm_status fm_workspace_size(const fm_problem* p, fm_op op, int32_t block_q, int3
 
 namespace {
 
+// The key-order option: the permutation and the permuted vectors into the workspace, then K
+// and V gathered into that order; `ma`, `k` and `v` are redirected to the permuted copies.
+hipError_t order_keys(const fm_problem* p, void* ws, const KeyWs& w, fm::MaskArgs& ma,
+                      const void*& k, const void*& v, hipStream_t s) {
+  int32_t* perm = at<int32_t>(ws, w.perm);
+  const fm::MaskOut pv{at<int32_t>(ws, w.vec[0]), at<int32_t>(ws, w.vec[1]),
+                       at<int32_t>(ws, w.vec[2]), at<int32_t>(ws, w.vec[3])};
+  hipError_t e = fm::launch_key_order(ma.v, (int)mask_rows(p), nq_of(p), nk_of(p), perm, pv, s);
+  void* kp = at<char>(ws, w.k);
+  void* vp = at<char>(ws, w.v);
+  if (e == hipSuccess)
+    e = fm::launch_permute_rows(false, k, v, kp, vp, perm, p->batch, p->heads_kv, hm_of(p),
+                                nk_of(p), p->head_dim, s);
+  ma.v = MaskPtrs{pv.lts, pv.lte, pv.uts, pv.ute};
+  k = kp;
+  v = vp;
+  return e;
+}
+
 template <typename MaskT>
 fm_status classify_impl(const fm_problem* p, const MaskT* m, int32_t block_q, int32_t block_k,
                         const fm_tiles* out, void* ws, size_t ws_bytes, void* stream) {
@@ -341,6 +391,7 @@ fm_status fwd_impl(const fm_problem* p, const void* q, const void* k, const void
   fm_status st = check_problem(p);
   if (st != FM_OK) return st;
   if ((st = check_mask(p, m)) != FM_OK) return st;
+  if ((st = check_key_order<MaskT>(p)) != FM_OK) return st;
   Blocks nb = blocks(p, fm::kFwdBlockQ, fm::kFwdBlockK);
   if ((st = check_sort_limits(p, nb)) != FM_OK) return st;
   if ((st = check_grid(p, nb, blocks(p, fm::kBwdBlockQ, fm::kBwdBlockK))) != FM_OK) return st;
@@ -353,15 +404,17 @@ fm_status fwd_impl(const fm_problem* p, const void* q, const void* k, const void
   if ((st = check_ws(ws, ws_bytes, w.total)) != FM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  const fm::MaskArgs ma = mask_args(p, m);
+  fm::MaskArgs ma = mask_args(p, m);
+  hipError_t e = hipSuccess;
+  if (sorted_keys(p)) e = order_keys(p, ws, w.key, ma, k, v, s);
   fm::TileOut t{};
   t.minmax = at<int32_t>(ws, w.mm);
   t.q_queue = at<int32_t>(ws, w.q_queue);
   t.q_count = at<int32_t>(ws, w.q_count);
   t.q_cost = at<int32_t>(ws, w.q_cost);
   const int R = (int)mask_rows(p);
-  hipError_t e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kFwdBlockQ, fm::kFwdBlockK,
-                                     t, s);
+  if (e == hipSuccess)
+    e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kFwdBlockQ, fm::kFwdBlockK, t, s);
   int32_t* order = at<int32_t>(ws, w.q_order);
   if (e == hipSuccess)
     e = fm::launch_lpt_sort(t.q_cost, order, (int)(R * nb.nQB), at<char>(ws, w.sort), s);
@@ -389,6 +442,7 @@ fm_status bwd_impl(const fm_problem* p, const void* q, const void* k, const void
   fm_status st = check_problem(p);
   if (st != FM_OK) return st;
   if ((st = check_mask(p, m)) != FM_OK) return st;
+  if ((st = check_key_order<MaskT>(p)) != FM_OK) return st;
   Blocks nk = blocks(p, fm::kBwdBlockQ, fm::kBwdBlockK);
   Blocks nq = blocks(p, fm::kFwdBlockQ, fm::kFwdBlockK);
   if ((st = check_sort_limits(p, nk)) != FM_OK) return st;
@@ -404,7 +458,17 @@ fm_status bwd_impl(const fm_problem* p, const void* q, const void* k, const void
   if ((st = check_ws(ws, ws_bytes, w.total)) != FM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  const fm::MaskArgs ma = mask_args(p, m);
+  fm::MaskArgs ma = mask_args(p, m);
+  hipError_t e = hipSuccess;
+  // key order: K, V and the vectors gathered here; dK, dV written in that order into the
+  // workspace and scattered to the caller's after the kernels
+  void* dk_out = dk;
+  void* dv_out = dv;
+  if (sorted_keys(p)) {
+    e = order_keys(p, ws, w.key, ma, k, v, s);
+    dk = at<char>(ws, w.key.dk);
+    dv = at<char>(ws, w.key.dv);
+  }
   fm::TileOut tk{};
   tk.minmax = at<int32_t>(ws, w.mm_k);
   tk.k_queue = at<int32_t>(ws, w.k_queue);
@@ -418,8 +482,8 @@ fm_status bwd_impl(const fm_problem* p, const void* q, const void* k, const void
   int32_t* k_order = at<int32_t>(ws, w.k_order);
   int32_t* q_order = at<int32_t>(ws, w.q_order);
   const int R = (int)mask_rows(p);
-  hipError_t e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kBwdBlockQ, fm::kBwdBlockK,
-                                     tk, s);
+  if (e == hipSuccess)
+    e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kBwdBlockQ, fm::kBwdBlockK, tk, s);
   void* scr = at<char>(ws, w.sort);
   if (e == hipSuccess) e = fm::launch_lpt_sort(tk.k_cost, k_order, (int)(R * nk.nKB), scr, s);
   if (e == hipSuccess)
@@ -457,6 +521,9 @@ fm_status bwd_impl(const fm_problem* p, const void* q, const void* k, const void
     }
     e = fm::launch_bwd(a, s, ev);
   }
+  if (e == hipSuccess && sorted_keys(p))
+    e = fm::launch_permute_rows(true, dk, dv, dk_out, dv_out, at<int32_t>(ws, w.key.perm),
+                                p->batch, p->heads_kv, hm_of(p), nk_of(p), p->head_dim, s);
   return hip_status(e);
 }
 
@@ -578,6 +645,24 @@ fm_status fm_localize_mask(const fm_problem* p, const fm_mask* global, const int
       fm::MaskPtrs{global->lts, global->lte, global->uts, global->ute}, 4, offsets, n_chunks,
       chunk_len, fm::MaskOut{local->lts, local->lte, local->uts, local->ute}, cols,
       static_cast<hipStream_t>(stream)));
+}
+
+fm_status fm_key_order(const fm_problem* p, const fm_mask* m, int32_t* perm,
+                       const fm_mask_out* permuted, void* stream) {
+  if (!p || !m) return FM_ERR_INVALID_ARG;
+  if (p->batch < 0 || p->seqlen < 0 || p->seqlen_kv < 0 || p->mask_heads < 0)
+    return FM_ERR_INVALID_ARG;
+  if (nq_of(p) > (1 << 22) || nk_of(p) > (1 << 22)) return FM_ERR_UNSUPPORTED;
+  const int64_t cols = mask_rows(p) * nk_of(p);
+  if (cols == 0) return FM_OK;
+  if (cols > INT32_MAX) return FM_ERR_UNSUPPORTED;
+  if (!m->lts || !m->lte || !m->uts || !m->ute || !perm) return FM_ERR_INVALID_ARG;
+  const fm::MaskOut out = permuted ? fm::MaskOut{permuted->lts, permuted->lte, permuted->uts,
+                                                 permuted->ute}
+                                   : fm::MaskOut{nullptr, nullptr, nullptr, nullptr};
+  return hip_status(fm::launch_key_order(MaskPtrs{m->lts, m->lte, m->uts, m->ute},
+                                         (int)mask_rows(p), nq_of(p), nk_of(p), perm, out,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 fm_status fm_localize_mask_multi(const fm_problem* p, const fm_mask_multi* global,

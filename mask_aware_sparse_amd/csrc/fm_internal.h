@@ -134,6 +134,20 @@ struct MaskOut {
 hipError_t launch_localize(const MaskPtrs& g, int arrays, const int32_t* offsets, int n_chunks,
                            int chunk_len, const MaskOut& out, int64_t cols, hipStream_t s);
 
+// Key reordering (an option of the attention entry points): per mask row and super-block
+// of kKeyOrderSpan keys, the keys sorted by LTS where that narrows the spread of bounds
+// over groups of kKeyOrderGroup positions.  perm [rows][Nk]: position p holds key
+// perm[p]; `permuted` (members may be null) receives the vectors in that order.
+constexpr int kKeyOrderSpan = 2048;
+constexpr int kKeyOrderGroup = 64;
+hipError_t launch_key_order(const MaskPtrs& m, int rows, int Nq, int Nk, int32_t* perm,
+                            const MaskOut& permuted, hipStream_t s);
+// Rows of two [B][Hkv][Nk][D] bf16 tensors moved into (gather) or out of (scatter) the key
+// order of perm; kv head h uses mask set h / (Hkv / Hm), Hm dividing Hkv.
+hipError_t launch_permute_rows(bool scatter, const void* src0, const void* src1, void* dst0,
+                               void* dst1, const int32_t* perm, int B, int Hkv, int Hm, int Nk,
+                               int D, hipStream_t s);
+
 // Compute units of the current device (queried once per device and cached).
 int device_cu_count();
 

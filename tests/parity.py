@@ -68,13 +68,13 @@ def check_grads(dQ, dK, dV, ref, LSE_ref=None, ctx=""):
     return out
 
 
-def full_parity(w, seed=None, scale=None, bwd=True):
+def full_parity(w, seed=None, scale=None, bwd=True, key_order=0):
     """HIP fwd (+bwd) vs the full oracle on workload w (small sizes only)."""
     import mask_aware_sparse_amd as fm
     q, k, v, do, vec = gpu_inputs(w, seed)
-    O, LSE = fm.attn_fwd(q, k, v, *vec, scale=scale)
+    O, LSE = fm.attn_fwd(q, k, v, *vec, scale=scale, key_order=key_order)
     if bwd:
-        dq, dk, dv = fm.attn_bwd(q, k, v, O, LSE, do, *vec, scale=scale)
+        dq, dk, dv = fm.attn_bwd(q, k, v, O, LSE, do, *vec, scale=scale, key_order=key_order)
     torch.cuda.synchronize()
     hq, hk, hv, hdo = (to_np(x) for x in (q, k, v, do))
     if bwd:

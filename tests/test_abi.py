@@ -358,3 +358,63 @@ def test_blocks_binding_checks_the_grid_shape():
         fm._mask_blocks(torch.zeros((1, 3, 3), dtype=torch.int32), 300, 300)   # uint8 only
     m, B, Hm = fm._mask_blocks(torch.zeros((2, 4, 3, 3), dtype=torch.uint8), 300, 257)
     assert (B, Hm) == (2, 4)
+
+
+# ---- key order (fm_problem.key_order, fm_key_order) ------------------------------------
+def test_key_order_values_checked():
+    p = prob()
+    p.key_order = 2
+    assert fwd(p) == INVALID
+    assert bwd(p) == INVALID
+    n = ctypes.c_size_t()
+    assert fm.library().fm_workspace_size(ctypes.byref(p), 1, 0, 0, ctypes.byref(n)) == INVALID
+
+
+def test_key_order_unsupported_forms():
+    lib = fm.library()
+    p = prob()
+    p.key_order = fm.KEYS_SORTED
+    mm = fm.MaskMulti(0x100000, 0x100000, 1)
+    assert lib.fm_attn_fwd_multi(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(mm), FAKE,
+                                 FAKE, FAKE, ctypes.c_size_t(1 << 40), None, None) == UNSUPPORTED
+    mb = fm.MaskBlocks(0x100000)
+    assert lib.fm_attn_bwd_blocks(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  ctypes.byref(mb), FAKE, FAKE, FAKE, FAKE,
+                                  ctypes.c_size_t(1 << 40), None, None) == UNSUPPORTED
+    # a kv head shared by two mask sets would need two key orders
+    ph = fm.Problem(1, 4, 2, 256, 128, 0.0, 0, 4, fm.KEYS_SORTED)
+    assert fwd(ph) == UNSUPPORTED
+    assert bwd(ph) == UNSUPPORTED
+    ph.mask_heads = 2
+    assert fwd(ph, ws_bytes=0) == WORKSPACE
+
+
+def test_key_order_workspace_sizes():
+    al = lambda x: (x + 255) // 256 * 256
+    B, Hq, Hkv, N, d, Hm = 2, 8, 2, 1000, 128, 2
+    nat = {op: fm.workspace_size(B, Hq, Hkv, N, op, mask_heads=Hm) for op in (1, 2)}
+    srt = {op: fm.workspace_size(B, Hq, Hkv, N, op, mask_heads=Hm, key_order=fm.KEYS_SORTED)
+           for op in (1, 2)}
+    cols, rows = al(B * Hm * N * 4), al(B * Hkv * N * d * 2)
+    # the permutation and four vectors; K and V (forward), also dK and dV (backward)
+    assert srt[1] - nat[1] == 5 * cols + 2 * rows
+    assert srt[2] - nat[2] == 5 * cols + 4 * rows
+    # the classifier's workspace ignores the option
+    assert fm.workspace_size(B, Hq, Hkv, N, 0, 64, 64, mask_heads=Hm, key_order=1) == \
+        fm.workspace_size(B, Hq, Hkv, N, 0, 64, 64, mask_heads=Hm)
+
+
+def test_key_order_entry_point_checks():
+    lib = fm.library()
+    m = fake_mask()
+    p = fm.Problem(1, 1, 1, 256, 128, 0.0, 0, 0, 0)
+    assert lib.fm_key_order(None, ctypes.byref(m), FAKE, None, None) == INVALID
+    assert lib.fm_key_order(ctypes.byref(p), None, FAKE, None, None) == INVALID
+    assert lib.fm_key_order(ctypes.byref(p), ctypes.byref(m), None, None, None) == INVALID
+    bad = fm.Mask(0x100000, 0, 0x100000, 0x100000)
+    assert lib.fm_key_order(ctypes.byref(p), ctypes.byref(bad), FAKE, None, None) == INVALID
+    p.seqlen = 1 << 23
+    assert lib.fm_key_order(ctypes.byref(p), ctypes.byref(m), FAKE, None, None) == UNSUPPORTED
+    # nothing to order: no pointer is touched
+    e = fm.Problem(0, 1, 1, 256, 128, 0.0, 0, 0, 0)
+    assert lib.fm_key_order(ctypes.byref(e), ctypes.byref(m), None, None, None) == FM_OK

@@ -16,6 +16,8 @@ from parity import GRAD_TOL, LSE_TOL, O_TOL, gpu_inputs, log, rel_l2, to_np
 pytestmark = pytest.mark.gpu
 
 FULL = workloads.CONFIG_NAMES[1:]   # c1 is covered in full by test_gpu_attention
+# the random-eviction workload also with its keys reordered (fm_problem.key_order = 1)
+FULL = FULL + ["c5_random_eviction_128k:sorted"]
 
 
 def visible_per_column(w, b):
@@ -46,11 +48,13 @@ def run_config(name, cache):
     if name in cache:
         return cache[name]
     import mask_aware_sparse_amd as fm
-    w = workloads.make_workload(name)
+    base, _, variant = name.partition(":")
+    key_order = fm.KEYS_SORTED if variant == "sorted" else fm.KEYS_NATURAL
+    w = workloads.make_workload(base)
     log(f"full-size {name}: B={w.batch} Hq={w.heads_q} Hkv={w.heads_kv} N={w.seqlen}")
     q, k, v, do, vec = gpu_inputs(w)
-    O, LSE = fm.attn_fwd(q, k, v, *vec)
-    dq, dk, dv = fm.attn_bwd(q, k, v, O, LSE, do, *vec)
+    O, LSE = fm.attn_fwd(q, k, v, *vec, key_order=key_order)
+    dq, dk, dv = fm.attn_bwd(q, k, v, O, LSE, do, *vec, key_order=key_order)
     torch.cuda.synchronize()
     cache.clear()
     cache[name] = (w, (q, k, v, do), (O, LSE, dq, dk, dv))
