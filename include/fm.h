@@ -154,6 +154,10 @@ typedef struct {
  * FM_ERR_INVALID_ARG / FM_ERR_UNSUPPORTED for problems the op rejects. */
 fm_status fm_workspace_size(const fm_problem* p, fm_op op, int32_t block_q, int32_t block_k,
                             size_t* bytes);
+/* The same byte count as a return value: 0 when fm_workspace_size would return an error
+ * (a problem that needs no workspace also gives 0, so callers that must tell the two apart
+ * use fm_workspace_size). */
+size_t fm_workspace_bytes(const fm_problem* p, fm_op op, int32_t block_q, int32_t block_k);
 
 /* The tile shape (rows of Q, columns of K per tile) the forward or backward kernel uses
  * and classifies with: 128 x 64 for FM_OP_FWD (also the backward's dQ kernel), 32 x 128

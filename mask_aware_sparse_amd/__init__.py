@@ -108,6 +108,8 @@ def library():
                                ctypes.POINTER(ctypes.c_int32)], _STATUS),
             "fm_workspace_size": ([PP, _STATUS, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.POINTER(ctypes.c_size_t)], _STATUS),
+            "fm_workspace_bytes": ([PP, _STATUS, ctypes.c_int32, ctypes.c_int32],
+                                   ctypes.c_size_t),
             "fm_classify_tiles": ([PP, PM, ctypes.c_int32, ctypes.c_int32, PT, _P,
                                    ctypes.c_size_t, _P], _STATUS),
             "fm_attn_fwd": ([PP, _P, _P, _P, PM, _P, _P, _P, ctypes.c_size_t, _P, PE], _STATUS),

@@ -327,6 +327,11 @@ fm_status fm_workspace_size(const fm_problem* p, fm_op op, int32_t block_q, int3
   return FM_ERR_INVALID_ARG;
 }
 
+size_t fm_workspace_bytes(const fm_problem* p, fm_op op, int32_t block_q, int32_t block_k) {
+  size_t n = 0;
+  return fm_workspace_size(p, op, block_q, block_k, &n) == FM_OK ? n : 0;
+}
+
 }  // extern "C"
 
 namespace {

@@ -418,3 +418,16 @@ def test_key_order_entry_point_checks():
     # nothing to order: no pointer is touched
     e = fm.Problem(0, 1, 1, 256, 128, 0.0, 0, 0, 0)
     assert lib.fm_key_order(ctypes.byref(e), ctypes.byref(m), None, None, None) == FM_OK
+
+
+def test_workspace_bytes_matches_workspace_size():
+    lib = fm.library()
+    for args in [(2, 8, 2, 1000, 1, 0, 0), (2, 8, 1, 1000, 2, 0, 0), (1, 4, 2, 300, 0, 64, 32)]:
+        B, Hq, Hkv, N, op, bq, bk = args
+        p = prob(B=B, Hq=Hq, Hkv=Hkv, N=N)
+        assert lib.fm_workspace_bytes(ctypes.byref(p), op, bq, bk) == \
+            fm.workspace_size(B, Hq, Hkv, N, op, bq, bk)
+    # rejected problems and arguments give 0
+    assert lib.fm_workspace_bytes(ctypes.byref(prob(Hq=3, Hkv=2)), 1, 0, 0) == 0
+    assert lib.fm_workspace_bytes(ctypes.byref(prob()), 0, 48, 64) == 0
+    assert lib.fm_workspace_bytes(None, 1, 0, 0) == 0
