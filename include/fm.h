@@ -96,7 +96,10 @@ typedef struct {
  * output is in the caller's key order and O, LSE, dQ, dK, dV are the same attention (up to
  * the fp32 summation order).  It pays where the columns' bounds are scattered (a
  * random-eviction mask); on masks whose sorted order is not narrower it only adds the
- * gathers.  FM_KEYS_SORTED is FM_ERR_UNSUPPORTED with the _multi and _blocks entry points
+ * gathers.  With FM_KEYS_SORTED and head_dim = 128 the backward's dK/dV kernel takes 256
+ * keys per workgroup (32 x 256 tiles, one 8-wave workgroup per CU): with scattered column
+ * ends its Q/dO rows rarely stay in L2, and each row is then read once per 256 keys
+ * instead of per 128.  FM_KEYS_SORTED is FM_ERR_UNSUPPORTED with the _multi and _blocks entry points
  * and when mask_heads > heads_kv (one kv head would need two orders).  fm_classify_tiles
  * ignores key_order (it classifies the vectors as given); values other than 0 and 1 are
  * FM_ERR_INVALID_ARG everywhere. */
@@ -161,7 +164,8 @@ size_t fm_workspace_bytes(const fm_problem* p, fm_op op, int32_t block_q, int32_
 
 /* The tile shape (rows of Q, columns of K per tile) the forward or backward kernel uses
  * and classifies with: 128 x 64 for FM_OP_FWD (also the backward's dQ kernel), 32 x 128
- * for FM_OP_BWD (the dK/dV kernel).  FM_OP_CLASSIFY is invalid here. */
+ * for FM_OP_BWD (the dK/dV kernel; 32 x 256 when key_order = FM_KEYS_SORTED and
+ * head_dim = 128, see below).  FM_OP_CLASSIFY is invalid here. */
 fm_status fm_tile_shape(fm_op op, int32_t* block_q, int32_t* block_k);
 
 /* Tile classification (FlashMask-3 page, §3.1 tile rule, generalized to all four

@@ -73,6 +73,8 @@ fm_status check_mask(const fm_problem* p, const fm_mask_blocks* m) {
 
 // The key-order option: four-vector masks only, and each kv head in one mask set.
 inline bool sorted_keys(const fm_problem* p) { return p->key_order == FM_KEYS_SORTED; }
+// Keys per dK/dV workgroup (and the KV block of its tiles) for this problem.
+inline int bwd_bk(const fm_problem* p) { return fm::bwd_block_k(p->head_dim, sorted_keys(p)); }
 template <typename MaskT>
 fm_status check_key_order(const fm_problem* p) {
   if (!sorted_keys(p)) return FM_OK;
@@ -222,7 +224,7 @@ BwdWs bwd_ws(const fm_problem* p, const Blocks& nk, const Blocks& nq) {
   w.zeros = off; off += align_up(B * nk_of(p) * 4);
   if (!w.acc) {
     w.partials = off;
-    off += align_up((size_t)2 * fm::split_slots(per, w.extra) * fm::kBwdBlockK * p->head_dim * 4);
+    off += align_up((size_t)2 * fm::split_slots(per, w.extra) * bwd_bk(p) * p->head_dim * 4);
   }
   w.total = key_ws(p, off, true, &w.key);
   return w;
@@ -316,7 +318,7 @@ fm_status fm_workspace_size(const fm_problem* p, fm_op op, int32_t block_q, int3
       return FM_OK;
     }
     case FM_OP_BWD: {
-      Blocks nk = blocks(p, fm::kBwdBlockQ, fm::kBwdBlockK);
+      Blocks nk = blocks(p, fm::kBwdBlockQ, bwd_bk(p));
       Blocks nq = blocks(p, fm::kFwdBlockQ, fm::kFwdBlockK);
       if ((st = check_sort_limits(p, nk)) != FM_OK) return st;
       if ((st = check_sort_limits(p, nq)) != FM_OK) return st;
@@ -399,7 +401,7 @@ fm_status fwd_impl(const fm_problem* p, const void* q, const void* k, const void
   if ((st = check_key_order<MaskT>(p)) != FM_OK) return st;
   Blocks nb = blocks(p, fm::kFwdBlockQ, fm::kFwdBlockK);
   if ((st = check_sort_limits(p, nb)) != FM_OK) return st;
-  if ((st = check_grid(p, nb, blocks(p, fm::kBwdBlockQ, fm::kBwdBlockK))) != FM_OK) return st;
+  if ((st = check_grid(p, nb, blocks(p, fm::kBwdBlockQ, bwd_bk(p)))) != FM_OK) return st;
   if (empty_problem(p)) return FM_OK;
   // query-side arrays are needed when there are rows, key-side ones when there are keys
   if (nq_of(p) > 0 && (!q || !o || !lse)) return FM_ERR_INVALID_ARG;
@@ -448,7 +450,7 @@ fm_status bwd_impl(const fm_problem* p, const void* q, const void* k, const void
   if (st != FM_OK) return st;
   if ((st = check_mask(p, m)) != FM_OK) return st;
   if ((st = check_key_order<MaskT>(p)) != FM_OK) return st;
-  Blocks nk = blocks(p, fm::kBwdBlockQ, fm::kBwdBlockK);
+  Blocks nk = blocks(p, fm::kBwdBlockQ, bwd_bk(p));
   Blocks nq = blocks(p, fm::kFwdBlockQ, fm::kFwdBlockK);
   if ((st = check_sort_limits(p, nk)) != FM_OK) return st;
   if ((st = check_sort_limits(p, nq)) != FM_OK) return st;
@@ -488,7 +490,7 @@ fm_status bwd_impl(const fm_problem* p, const void* q, const void* k, const void
   int32_t* q_order = at<int32_t>(ws, w.q_order);
   const int R = (int)mask_rows(p);
   if (e == hipSuccess)
-    e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kBwdBlockQ, fm::kBwdBlockK, tk, s);
+    e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kBwdBlockQ, bwd_bk(p), tk, s);
   void* scr = at<char>(ws, w.sort);
   if (e == hipSuccess) e = fm::launch_lpt_sort(tk.k_cost, k_order, (int)(R * nk.nKB), scr, s);
   if (e == hipSuccess)
@@ -514,6 +516,7 @@ fm_status bwd_impl(const fm_problem* p, const void* q, const void* k, const void
     a.split_extra = w.extra;
     a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.Hm = hm_of(p);
     a.Nq = nq_of(p); a.Nk = nk_of(p); a.D = p->head_dim;
+    a.bk = bwd_bk(p);
     a.nQB_k = (int)nk.nQB; a.nKB_k = (int)nk.nKB;
     a.nQB_q = (int)nq.nQB; a.nKB_q = (int)nq.nKB;
     a.scale = scale_of(p);

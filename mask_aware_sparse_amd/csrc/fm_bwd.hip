@@ -70,19 +70,19 @@ __device__ __forceinline__ int perm_rows(int a) {
 }
 
 // ---- KE: dK / dV (KV-block outer) -------------------------------------------------------
-// 4 waves x 32 keys = one 128-key block per workgroup, two workgroups per CU (78 KB of LDS
-// each), so the two waves on a SIMD belong to different workgroups and their MFMA and
-// softmax phases drift apart instead of meeting at the same barriers.  Steps are 32-row
-// Q-blocks, which keeps the live registers of a wave within 256.
+// kW waves x 32 keys per workgroup.  kW = 4: one 128-key block per workgroup, two
+// workgroups per CU (78 KB of LDS each), so the two waves on a SIMD belong to different
+// workgroups and their MFMA and softmax phases drift apart instead of meeting at the same
+// barriers.  kW = 8 (sorted keys, D <= 128): one 256-key block per workgroup and CU, which
+// reads each Q/dO row once per 256 keys instead of per 128 (half the bytes from HBM where
+// the rows do not stay in L2).  Steps are 32-row Q-blocks, which keeps the live registers
+// of a wave within 256.
 namespace dkdv {
-constexpr int kWaves = kBwdBlockK / 32;
 constexpr int BQ = kBwdBlockQ;  // 32 query rows per step
-constexpr int BK = kBwdBlockK;  // 128 keys per workgroup
-static_assert(BK == 32 * kWaves, "one 32-key slice per wave");
 
 // Q / dO tiles use the swizzled layout (row reads and transposing reads; 320-byte rows at
 // D <= 128), K rows are read row-wise only (272 bytes).
-template <int D, bool kMulti>
+template <int D, bool kMulti, int BK>
 struct __attribute__((aligned(16))) Smem {
   bf16 q[2][BQ * LdsRows<D>::SWZ];
   bf16 dO[2][BQ * LdsRows<D>::SWZ];
@@ -294,16 +294,19 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_split(
   }
 }
 
-// kMulti: the mask is the multi-interval form (else the four-vector form).
-template <int D, bool kMulti>
-__global__ __launch_bounds__(64 * dkdv::kWaves, D > 128 ? 1 : 2) void k_attn_bwd_dkdv(DkdvParams p) {
+// kMulti: the mask is the multi-interval form (else the four-vector form).  kW: waves (of
+// 32 keys each) per workgroup, 4 or 8.
+template <int D, bool kMulti, int kW>
+__global__ __launch_bounds__(64 * kW, (D > 128 || kW > 4) ? 1 : 2) void k_attn_bwd_dkdv(DkdvParams p) {
   using namespace dkdv;
+  constexpr int kWaves = kW;
+  constexpr int BK = 32 * kW;  // keys per workgroup
   constexpr int KS = LdsRows<D>::KS;    // K row stride in LDS (elements)
   constexpr int kRow = LdsRows<D>::SWZ;  // swizzled Q / dO row stride
   constexpr int kS = D / 16;   // k-steps of a 32x32x16 product over D
   constexpr int kDB = D / 32;  // 32-column blocks of dK / dV
   constexpr int kCh = D / 8;   // 16-byte chunks per row
-  __shared__ Smem<D, kMulti> sm;
+  __shared__ Smem<D, kMulti, BK> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
   const int N = p.Nk, Nq = p.Nq;  // N: keys (and mask columns)
@@ -927,13 +930,14 @@ struct ReduceParams {
   bf16* __restrict__ dv;
   HeadMap hm;
   int Hq, Hkv, nKB, Nk, nslots, D;
+  int bk;  // keys per dK/dV workgroup (128 or 256)
   float scale;
 };
 
 // One workgroup per (split pair, kv head of its set): dK = scale * sum_seg partial_dK and
 // dV = sum_seg partial_dV, summed in segment order, stored as bf16 (keys past Nk dropped).
 __global__ __launch_bounds__(256) void k_dkdv_reduce(ReduceParams p) {
-  constexpr int BK = kBwdBlockK;
+  const int BK = p.bk;
   const int D = p.D;
   const int per = p.hm.kvpm * p.hm.cpk;
   const int j = blockIdx.x / per, rem = blockIdx.x - j * per;
@@ -1010,13 +1014,16 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
                        reinterpret_cast<float4*>(a.dv_acc), rows_k * a.D / 4);
   }
 
-  // work units of the dK/dV kernel: long pairs split along their queues
+  // work units of the dK/dV kernel: long pairs split along their queues.  wide: 256-key
+  // workgroups of 8 waves, one per CU (bk = 256, D = 128 only)
+  const bool wide = a.bk == kBwdBlockKWide;
   const int per = hm.kvpm * hm.cpk;
   const int npairs = a.B * a.Hm * a.nKB_k;
   const int nslots = split_slots(per, a.split_extra);
   if (npairs > 0)
     hipLaunchKernelGGL(k_plan_split, dim3(1), dim3(kPlanThreads), 0, s, a.k_count, a.k_order,
-                       npairs, per, hm.hc, 2 * device_cu_count(), a.split_extra, acc ? 0 : 1,
+                       npairs, per, hm.hc, (wide ? 1 : 2) * device_cu_count(), a.split_extra,
+                       acc ? 0 : 1,
                        a.unit_pair, a.unit_slot, a.split_pair, a.split_slot, a.split_counts);
 
   DkdvParams p;
@@ -1045,11 +1052,12 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   const unsigned grid = (unsigned)(npairs + a.split_extra) * (unsigned)per;
   if (ev.dkdv_start) (void)hipEventRecord(ev.dkdv_start, s);
   if (grid > 0) {
-    auto kern = d64 ? (multi ? k_attn_bwd_dkdv<64, true> : k_attn_bwd_dkdv<64, false>)
+    auto kern = d64 ? (multi ? k_attn_bwd_dkdv<64, true, 4> : k_attn_bwd_dkdv<64, false, 4>)
                 : a.D == 256
-                    ? (multi ? k_attn_bwd_dkdv<256, true> : k_attn_bwd_dkdv<256, false>)
-                    : (multi ? k_attn_bwd_dkdv<128, true> : k_attn_bwd_dkdv<128, false>);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * dkdv::kWaves), 0, s, p);
+                    ? (multi ? k_attn_bwd_dkdv<256, true, 4> : k_attn_bwd_dkdv<256, false, 4>)
+                : wide ? (multi ? k_attn_bwd_dkdv<128, true, 8> : k_attn_bwd_dkdv<128, false, 8>)
+                       : (multi ? k_attn_bwd_dkdv<128, true, 4> : k_attn_bwd_dkdv<128, false, 4>);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(wide ? 512 : 256), 0, s, p);
   }
   if (ev.dkdv_stop) (void)hipEventRecord(ev.dkdv_stop, s);
 
@@ -1066,6 +1074,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
     rp.Hq = a.Hq; rp.Hkv = a.Hkv; rp.nKB = a.nKB_k; rp.Nk = a.Nk;
     rp.nslots = nslots;
     rp.D = a.D;
+    rp.bk = a.bk;
     rp.scale = a.scale;
     hipLaunchKernelGGL(k_dkdv_reduce, dim3((unsigned)a.split_extra * (unsigned)per), dim3(256),
                        0, s, rp);

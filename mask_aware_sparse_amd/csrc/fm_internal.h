@@ -18,6 +18,13 @@ constexpr int kFwdBlockQ = 128;
 constexpr int kFwdBlockK = 64;
 constexpr int kBwdBlockQ = 32;
 constexpr int kBwdBlockK = 128;
+// With sorted keys at D = 128 the dK/dV kernel takes 256 keys per workgroup (8 waves, one
+// workgroup per CU): the Q/dO rows of its steps rarely stay in L2 there, and reading each
+// row once per 256 keys halves those bytes.
+constexpr int kBwdBlockKWide = 256;
+inline int bwd_block_k(int D, bool sorted_keys) {
+  return sorted_keys && D == 128 ? kBwdBlockKWide : kBwdBlockK;
+}
 // Query heads handled by one backward work item (dK/dV of a KV block are summed over
 // these heads in registers, then added across items with fp32 atomics).
 constexpr int kBwdHeadChunk = 4;
@@ -202,6 +209,7 @@ struct BwdArgs {
   int split_extra;   // extra pair units allowed (0: no splitting)
   int B, Hq, Hkv, Hm, Nq, Nk;
   int D;             // head dimension: 64 or 128
+  int bk;            // keys per dK/dV workgroup: bwd_block_k(D, sorted keys)
   int nQB_k, nKB_k;  // block counts at the dK/dV tile
   int nQB_q, nKB_q;  // block counts at the dQ (forward) tile
   float scale;
