@@ -396,8 +396,23 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void k_attn_fwd(FwdParams p) 
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    const bool slow = !(psum[0] <= kSumLimit) || !(psum[1] <= kSumLimit) ||
-                      (m_use == -INFINITY && psum[0] + psum[1] > 0.f);
+    bool slow = !(psum[0] <= kSumLimit) || !(psum[1] <= kSumLimit);
+    // A row without an offset (hidden in every earlier tile) takes the slow path as soon as
+    // it has any finite score in this tile.  Testing its exponentials instead would miss a
+    // row whose visible scores all lie below 2^-126 against offset 0: every p underflows to
+    // zero and the row would end with no weight although it sees keys.  Rows without an
+    // offset are rare (the rows of a diagonal Q-block above its first queued tile), so
+    // the row max is taken only in waves that hold one.
+    const bool no_off = m_use == -INFINITY;
+    if (__builtin_amdgcn_ballot_w64(no_off)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[blk][i]);
+      mx = max_with_partner32(mx);
+      slow = slow || (no_off && mx > -INFINITY);
+    }
     if (__builtin_amdgcn_ballot_w64(slow)) {
       // row max of the tile (both lanes of the row); offset moved up to it if larger
       float mx = -INFINITY;

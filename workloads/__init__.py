@@ -450,3 +450,50 @@ def mask_tensors(w, device: str = "cpu"):
         return (torch.from_numpy(np.ascontiguousarray(w.blocks)).to(device),)
     arrs = w.intervals() if isinstance(w, MultiWorkload) else w.vectors()
     return tuple(torch.from_numpy(np.ascontiguousarray(x)).to(device) for x in arrs)
+
+
+# Per-row factors of the mixed-magnitude inputs (applied to the shared half of each query
+# row) and the values of the random halves: all exact in bf16, and every product and every
+# sum of 128 products is exact in fp32 (multiples of 1/4 below 2^22).
+MIXED_FACTORS = (-32.0, -24.0, -8.0, -1.0, 0.5, 1.0, 8.0, 24.0, 32.0)
+RANDOM_HALF_VALUES = (-1.5, -1.0, -0.5, 0.0, 0.5, 1.0, 1.5)
+
+
+def extreme_logit_tensors(w: Workload, kind: str, seed: int = 0, device: str = "cpu"):
+    """Q, K, V, dO whose scores lie far from zero, for the numerics of the online softmax.
+
+    The first d/2 dimensions of every key row of a kv head hold one random +-1 pattern
+    (shared by all its keys); the other d/2 hold values drawn from RANDOM_HALF_VALUES per
+    key.  A query row is [factor * pattern of its kv head, its own random half] (query
+    head h uses kv head h // (H_q / H_kv)).  So q.k = factor * d/2 + r.k', an exact
+    multiple of 1/4 in fp32, with r.k' of spread 8 giving the keys different weights:
+      "low"   factor -32: q.k = -2048 + r.k' (|r.k'| <= 144), so at the default scale
+              s * log2(e) / sqrt(128) lies in [-280, -243];
+      "high"  factor +32: the same with the shared part's sign reversed;
+      "mixed" a factor per query row drawn from MIXED_FACTORS.
+    The random halves keep dQ = scale * sum_j dS_ij K_j away from the cancellation of the
+    shared half (sum_j dS_ij = 0).  V and dO are N(0,1) rounded to bf16.  Draws come from
+    one CPU generator seeded with `seed`."""
+    import torch
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    B, Hq, Hkv, N, d = w.batch, w.heads_q, w.heads_kv, w.seqlen, w.head_dim
+    h = d // 2
+    vals = torch.tensor(RANDOM_HALF_VALUES)
+    pat = (torch.randint(0, 2, (B, Hkv, 1, h), generator=g) * 2 - 1).float()
+    k = torch.cat([pat.expand(B, Hkv, N, h),
+                   vals[torch.randint(0, len(vals), (B, Hkv, N, d - h), generator=g)]], dim=-1)
+    qpat = pat.repeat_interleave(Hq // Hkv, dim=1).expand(B, Hq, N, h)
+    if kind == "low":
+        fac = torch.full((B, Hq, N, 1), -32.0)
+    elif kind == "high":
+        fac = torch.full((B, Hq, N, 1), 32.0)
+    elif kind == "mixed":
+        idx = torch.randint(0, len(MIXED_FACTORS), (B, Hq, N, 1), generator=g)
+        fac = torch.tensor(MIXED_FACTORS)[idx]
+    else:
+        raise ValueError(f"unknown kind {kind!r}")
+    q = torch.cat([fac * qpat,
+                   vals[torch.randint(0, len(vals), (B, Hq, N, d - h), generator=g)]], dim=-1)
+    v = torch.randn((B, Hkv, N, d), generator=g)
+    do = torch.randn((B, Hq, N, d), generator=g)
+    return tuple(t.to(torch.bfloat16).contiguous().to(device) for t in (q, k, v, do))
