@@ -172,6 +172,39 @@ def _mask(lts, lte, uts, ute):
     return Mask(lts.data_ptr(), lte.data_ptr(), uts.data_ptr(), ute.data_ptr())
 
 
+def _on_device(device, named):
+    """Every tensor of `named` ((name, tensor or None) pairs) on `device`, a GPU.  Runs
+    after the shape and dtype checks, so those are reported first."""
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on the GPU (got {device})")
+    for name, t in named:
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} must be on {device} (got {t.device})")
+
+
+def _expect(t, name, shape, dtype):
+    """A caller-supplied tensor: exact shape, dtype and contiguity (the kernels address it
+    from its base pointer with the problem's strides)."""
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _keep_alive(stream, device, *tensors):
+    """Tensors allocated here and used on a stream other than the current one: tell the
+    caching allocator, so that it does not hand their memory out again while the kernels
+    queued on `stream` may still use it."""
+    if stream is None or stream == torch.cuda.current_stream(device):
+        return
+    for t in tensors:
+        if t is not None and t.numel():
+            t.record_stream(stream)
+
+
 def _mask_dims(lts):
     """(B, H_m, N_k) of vectors [B][N_k] (one set per batch row, H_m = 1) or
     [B][H_m][N_k] (per-head sets: query head h uses set h // (H_q / H_m))."""
@@ -212,11 +245,16 @@ def workspace_size(batch, heads_q, heads_kv, seqlen, op, block_q=0, block_k=0, h
 
 
 def _workspace(nbytes, device, ws=None):
+    """(workspace, allocated here?).  A caller's workspace must be contiguous, on the
+    device and at least `nbytes` long."""
     if ws is not None:
+        if not ws.is_contiguous():
+            raise ValueError("workspace tensor must be contiguous")
         if ws.numel() * ws.element_size() < nbytes:
             raise ValueError("workspace tensor too small")
-        return ws
-    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        _on_device(device, [("workspace", ws)])
+        return ws, False
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device), True
 
 
 class IpoReport(ctypes.Structure):
@@ -279,24 +317,33 @@ def _mask_blocks(blocks, seqlen_q, seqlen_k):
     return MaskBlocks(blocks.data_ptr()), B, Hm
 
 
-def _classify(fn, m, B, Hm, Nk, block_q, block_k, heads_q, heads_kv, stream, out, ws, seqlen_q,
-              width, dev):
+def _classify(fn, m, mask_ts, B, Hm, Nk, block_q, block_k, heads_q, heads_kv, stream, out, ws,
+              seqlen_q, width, dev):
     if Hm > 1 and heads_q == 1 and heads_kv == 1:
         heads_q = Hm                      # the heads play no part in the classification
     N = Nk if seqlen_q is None else int(seqlen_q)
+    if int(block_q) <= 0 or int(block_k) <= 0:
+        raise ValueError("tile shape must be positive")
     nqb, nkb = -(-N // block_q), -(-Nk // block_k)
-    if out is None:
-        out = _tile_buffers(B * Hm, N, nqb, nkb, dev, width)
-    tiles = Tiles(*(out[n].data_ptr() if out[n].numel() else 0 for n, _ in Tiles._fields_))
+    shapes = _tile_shapes(B * Hm, nqb, nkb, width)
+    fresh = out is None
+    if fresh:
+        out = {n: torch.empty(shp, dtype=dt, device=dev) for n, (shp, dt) in shapes.items()}
+    else:
+        for n, (shp, dt) in shapes.items():
+            if n not in out:
+                raise ValueError(f"out lacks {n!r}")
+            _expect(out[n], n, shp, dt)
     p = _problem(B, heads_q, heads_kv, N, seqlen_kv=Nk, mask_heads=Hm)
     nbytes = workspace_size(B, heads_q, heads_kv, N, OP_CLASSIFY, block_q, block_k,
                             seqlen_kv=Nk, mask_heads=Hm)
-    if ws is None:
-        ws = _workspace(nbytes, dev)
-    elif ws.numel() < nbytes:
-        raise ValueError("workspace too small")
+    _on_device(dev, [(f"mask tensor {i}", t) for i, t in enumerate(mask_ts)] +
+               [(n, out[n]) for n in shapes])
+    ws, own_ws = _workspace(nbytes, dev, ws)
+    tiles = Tiles(*(out[n].data_ptr() if out[n].numel() else 0 for n, _ in Tiles._fields_))
     _check(fn(ctypes.byref(p), ctypes.byref(m), int(block_q), int(block_k), ctypes.byref(tiles),
               _ptr(ws), ctypes.c_size_t(nbytes), _stream(dev, stream)), fn.__name__)
+    _keep_alive(stream, dev, *([ws] if own_ws else []), *(out.values() if fresh else ()))
     return out
 
 
@@ -308,8 +355,9 @@ def classify_tiles(lts, lte, uts, ute, block_q, block_k, heads_q=1, heads_kv=1, 
     and `ws` (uint8 device tensor of at least workspace_size(..., OP_CLASSIFY, block_q,
     block_k) bytes) may be passed to reuse buffers."""
     B, Hm, Nk = _mask_dims(lts)
-    return _classify(library().fm_classify_tiles, _mask(lts, lte, uts, ute), B, Hm, Nk, block_q,
-                     block_k, heads_q, heads_kv, stream, out, ws, seqlen_q, 8, lts.device)
+    return _classify(library().fm_classify_tiles, _mask(lts, lte, uts, ute),
+                     (lts, lte, uts, ute), B, Hm, Nk, block_q, block_k, heads_q, heads_kv, stream,
+                     out, ws, seqlen_q, 8, lts.device)
 
 
 def classify_tiles_multi(starts, ends, block_q, block_k, heads_q=1, heads_kv=1, stream=None,
@@ -317,8 +365,8 @@ def classify_tiles_multi(starts, ends, block_q, block_k, heads_q=1, heads_kv=1, 
     """fm_classify_tiles_multi for interval starts/ends [B][M][N_k] or [B][H_m][M][N_k];
     block_minmax is [B*H_m][nKB][4M]."""
     m, B, Hm, M, Nk = _mask_multi(starts, ends)
-    return _classify(library().fm_classify_tiles_multi, m, B, Hm, Nk, block_q, block_k, heads_q,
-                     heads_kv, stream, out, ws, seqlen_q, 4 * M, starts.device)
+    return _classify(library().fm_classify_tiles_multi, m, (starts, ends), B, Hm, Nk, block_q,
+                     block_k, heads_q, heads_kv, stream, out, ws, seqlen_q, 4 * M, starts.device)
 
 
 def classify_tiles_blocks(blocks, block_q, block_k, seqlen_q, seqlen_k, heads_q=1, heads_kv=1,
@@ -326,20 +374,23 @@ def classify_tiles_blocks(blocks, block_q, block_k, seqlen_q, seqlen_k, heads_q=
     """fm_classify_tiles_blocks for a block grid (see _mask_blocks); block_minmax is not
     written."""
     m, B, Hm = _mask_blocks(blocks, seqlen_q, seqlen_k)
-    return _classify(library().fm_classify_tiles_blocks, m, B, Hm, int(seqlen_k), block_q,
-                     block_k, heads_q, heads_kv, stream, out, ws, int(seqlen_q), 8, blocks.device)
+    return _classify(library().fm_classify_tiles_blocks, m, (blocks,), B, Hm, int(seqlen_k),
+                     block_q, block_k, heads_q, heads_kv, stream, out, ws, int(seqlen_q), 8,
+                     blocks.device)
 
 
-def _tile_buffers(B, N, nqb, nkb, dev, width=8):
+def _tile_shapes(R, nqb, nkb, width=8):
+    """(shape, dtype) of each fm_tiles buffer for R mask rows (see fm_tiles in fm.h)."""
+    i32 = torch.int32
     return {
-        "block_minmax": torch.empty((B, nkb, width), dtype=torch.int32, device=dev),
-        "tile_class": torch.empty((B, nqb, nkb), dtype=torch.uint8, device=dev),
-        "q_queue": torch.empty((B, nqb, nkb), dtype=torch.int32, device=dev),
-        "q_count": torch.empty((B, nqb, 2), dtype=torch.int32, device=dev),
-        "k_queue": torch.empty((B, nkb, nqb), dtype=torch.int32, device=dev),
-        "k_count": torch.empty((B, nkb, 2), dtype=torch.int32, device=dev),
-        "q_order": torch.empty((B * nqb,), dtype=torch.int32, device=dev),
-        "k_order": torch.empty((B * nkb,), dtype=torch.int32, device=dev),
+        "block_minmax": ((R, nkb, width), i32),
+        "tile_class": ((R, nqb, nkb), torch.uint8),
+        "q_queue": ((R, nqb, nkb), i32),
+        "q_count": ((R, nqb, 2), i32),
+        "k_queue": ((R, nkb, nqb), i32),
+        "k_count": ((R, nkb, 2), i32),
+        "q_order": ((R * nqb,), i32),
+        "k_order": ((R * nkb,), i32),
     }
 
 
@@ -360,10 +411,10 @@ def _shapes(q, k, mask_shape):
     return B, Hq, k.shape[1], N, k.shape[2], d, Hm
 
 
-def _bf16(*ts):
-    for t in ts:
-        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError("tensors must be contiguous bf16 on the GPU")
+def _bf16(*named):
+    for name, t in named:
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 tensor")
 
 
 def _events(ev):
@@ -380,37 +431,63 @@ def _events(ev):
     return ctypes.byref(KernelEvents(*handles))
 
 
-def _fwd(fn, q, k, v, m, mask_shape, scale, ws, out, lse, stream, events, key_order=KEYS_NATURAL):
-    _bf16(q, k, v)
+def _fwd(fn, q, k, v, m, mask_ts, mask_shape, scale, ws, out, lse, stream, events,
+         key_order=KEYS_NATURAL):
+    _bf16(("q", q), ("k", k), ("v", v))
     B, Hq, Hkv, N, Nk, d, Hm = _shapes(q, k, mask_shape)
+    _expect(v, "v", k.shape, torch.bfloat16)
+    if out is not None:
+        _expect(out, "out", q.shape, torch.bfloat16)
+    if lse is not None:
+        _expect(lse, "lse", (B, Hq, N), torch.float32)
+    dev = q.device
+    _on_device(dev, [("k", k), ("v", v), ("out", out), ("lse", lse)] +
+               [(f"mask tensor {i}", t) for i, t in enumerate(mask_ts)])
     o = torch.empty_like(q) if out is None else out
-    lse_t = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    lse_t = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if lse is None else lse
     p = _problem(B, Hq, Hkv, N, scale, head_dim=d, seqlen_kv=Nk, mask_heads=Hm,
                  key_order=key_order)
     nbytes = workspace_size(B, Hq, Hkv, N, OP_FWD, head_dim=d, seqlen_kv=Nk, mask_heads=Hm,
                             key_order=key_order)
-    w = _workspace(nbytes, q.device, ws)
+    w, own_ws = _workspace(nbytes, dev, ws)
     _check(fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(m), _ptr(o), _ptr(lse_t),
-              _ptr(w), ctypes.c_size_t(nbytes), _stream(q.device, stream), _events(events)),
+              _ptr(w), ctypes.c_size_t(nbytes), _stream(dev, stream), _events(events)),
            fn.__name__)
+    _keep_alive(stream, dev, w if own_ws else None, o if out is None else None,
+                lse_t if lse is None else None)
     return o, lse_t
 
 
-def _bwd(fn, q, k, v, o, lse, dout, m, mask_shape, scale, ws, grads, stream, events,
+def _bwd(fn, q, k, v, o, lse, dout, m, mask_ts, mask_shape, scale, ws, grads, stream, events,
          key_order=KEYS_NATURAL):
-    _bf16(q, k, v, o, dout)
+    _bf16(("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout))
     B, Hq, Hkv, N, Nk, d, Hm = _shapes(q, k, mask_shape)
-    if grads is None:
+    _expect(v, "v", k.shape, torch.bfloat16)
+    _expect(o, "o", q.shape, torch.bfloat16)
+    _expect(dout, "dout", q.shape, torch.bfloat16)
+    _expect(lse, "lse", (B, Hq, N), torch.float32)
+    if grads is not None:
+        if len(grads) != 3:
+            raise ValueError("grads must be (dq, dk, dv)")
+        for name, g, like in zip(("dq", "dk", "dv"), grads, (q, k, k)):
+            _expect(g, name, like.shape, torch.bfloat16)
+    dev = q.device
+    _on_device(dev, [("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse)] +
+               ([] if grads is None else list(zip(("dq", "dk", "dv"), grads))) +
+               [(f"mask tensor {i}", t) for i, t in enumerate(mask_ts)])
+    fresh = grads is None
+    if fresh:
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = grads
     p = _problem(B, Hq, Hkv, N, scale, head_dim=d, seqlen_kv=Nk, mask_heads=Hm,
                  key_order=key_order)
     nbytes = workspace_size(B, Hq, Hkv, N, OP_BWD, head_dim=d, seqlen_kv=Nk, mask_heads=Hm,
                             key_order=key_order)
-    w = _workspace(nbytes, q.device, ws)
+    w, own_ws = _workspace(nbytes, dev, ws)
     _check(fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
               ctypes.byref(m), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(w), ctypes.c_size_t(nbytes),
-              _stream(q.device, stream), _events(events)), fn.__name__)
+              _stream(dev, stream), _events(events)), fn.__name__)
+    _keep_alive(stream, dev, w if own_ws else None, *(grads if fresh else ()))
     return dq, dk, dv
 
 
@@ -421,8 +498,8 @@ def attn_fwd(q, k, v, lts, lte, uts, ute, scale=None, ws=None, out=None, lse=Non
     query heads, [B][H_m][N_k].
     `events`: optional (start, stop) torch.cuda.Event pair timing the attention kernel.
     `key_order`: KEYS_SORTED runs the kernels over the keys in fm_key_order's order."""
-    return _fwd(library().fm_attn_fwd, q, k, v, _mask(lts, lte, uts, ute), _mask_dims(lts),
-                scale, ws, out, lse, stream, events, key_order)
+    return _fwd(library().fm_attn_fwd, q, k, v, _mask(lts, lte, uts, ute), (lts, lte, uts, ute),
+                _mask_dims(lts), scale, ws, out, lse, stream, events, key_order)
 
 
 def attn_fwd_multi(q, k, v, starts, ends, scale=None, ws=None, out=None, lse=None, stream=None,
@@ -430,8 +507,8 @@ def attn_fwd_multi(q, k, v, starts, ends, scale=None, ws=None, out=None, lse=Non
     """fm_attn_fwd_multi: as attn_fwd with the multi-interval mask, starts/ends
     [B][M][N_k] or [B][H_m][M][N_k] (key j visible to row i iff some interval holds i)."""
     m, B, Hm, M, Nk = _mask_multi(starts, ends)
-    return _fwd(library().fm_attn_fwd_multi, q, k, v, m, (B, Hm, Nk), scale, ws, out, lse,
-                stream, events)
+    return _fwd(library().fm_attn_fwd_multi, q, k, v, m, (starts, ends), (B, Hm, Nk), scale,
+                ws, out, lse, stream, events)
 
 
 def attn_fwd_blocks(q, k, v, blocks, scale=None, ws=None, out=None, lse=None, stream=None,
@@ -439,16 +516,16 @@ def attn_fwd_blocks(q, k, v, blocks, scale=None, ws=None, out=None, lse=None, st
     """fm_attn_fwd_blocks: as attn_fwd with a block-sparse mask, a uint8 grid [B][nQB][nKB]
     or [B][H_m][nQB][nKB] over 128 x 128 blocks (1 = visible)."""
     m, B, Hm = _mask_blocks(blocks, q.shape[2], k.shape[2])
-    return _fwd(library().fm_attn_fwd_blocks, q, k, v, m, (B, Hm, k.shape[2]), scale, ws, out,
-                lse, stream, events)
+    return _fwd(library().fm_attn_fwd_blocks, q, k, v, m, (blocks,), (B, Hm, k.shape[2]),
+                scale, ws, out, lse, stream, events)
 
 
 def attn_bwd_blocks(q, k, v, o, lse, dout, blocks, scale=None, ws=None, grads=None, stream=None,
                     events=None):
     """fm_attn_bwd_blocks: as attn_bwd with a block-sparse mask."""
     m, B, Hm = _mask_blocks(blocks, q.shape[2], k.shape[2])
-    return _bwd(library().fm_attn_bwd_blocks, q, k, v, o, lse, dout, m, (B, Hm, k.shape[2]),
-                scale, ws, grads, stream, events)
+    return _bwd(library().fm_attn_bwd_blocks, q, k, v, o, lse, dout, m, (blocks,),
+                (B, Hm, k.shape[2]), scale, ws, grads, stream, events)
 
 
 def attn_bwd(q, k, v, o, lse, dout, lts, lte, uts, ute, scale=None, ws=None, grads=None,
@@ -457,22 +534,27 @@ def attn_bwd(q, k, v, o, lse, dout, lts, lte, uts, ute, scale=None, ws=None, gra
     stop2) torch.cuda.Event objects timing the dK/dV kernel and the dQ kernel.
     `key_order`: as for attn_fwd; dK and dV come back in the caller's key order."""
     return _bwd(library().fm_attn_bwd, q, k, v, o, lse, dout, _mask(lts, lte, uts, ute),
-                _mask_dims(lts), scale, ws, grads, stream, events, key_order)
+                (lts, lte, uts, ute), _mask_dims(lts), scale, ws, grads, stream, events,
+                key_order)
 
 
 def attn_bwd_multi(q, k, v, o, lse, dout, starts, ends, scale=None, ws=None, grads=None,
                    stream=None, events=None):
     """fm_attn_bwd_multi: as attn_bwd with the multi-interval mask."""
     m, B, Hm, M, Nk = _mask_multi(starts, ends)
-    return _bwd(library().fm_attn_bwd_multi, q, k, v, o, lse, dout, m, (B, Hm, Nk), scale, ws,
-                grads, stream, events)
+    return _bwd(library().fm_attn_bwd_multi, q, k, v, o, lse, dout, m, (starts, ends),
+                (B, Hm, Nk), scale, ws, grads, stream, events)
 
 
-def _expand(fn, m, B, Hm, N, b, row0, row1, stream, seqlen_q, dev):
+def _expand(fn, m, mask_ts, B, Hm, N, b, row0, row1, stream, seqlen_q, dev):
+    if not 0 <= int(row0) <= int(row1):
+        raise ValueError("need 0 <= row0 <= row1")
+    _on_device(dev, [(f"mask tensor {i}", t) for i, t in enumerate(mask_ts)])
     dense = torch.empty((row1 - row0, N), dtype=torch.uint8, device=dev)
     p = _problem(B, Hm, 1, N if seqlen_q is None else int(seqlen_q), seqlen_kv=N, mask_heads=Hm)
     _check(fn(ctypes.byref(p), ctypes.byref(m), int(b), int(row0), int(row1), _ptr(dense),
               _stream(dev, stream)), fn.__name__)
+    _keep_alive(stream, dev, dense)
     return dense
 
 
@@ -480,22 +562,22 @@ def debug_expand_mask(lts, lte, uts, ute, b, row0, row1, stream=None, seqlen_q=N
     """uint8 [row1-row0][N_k] dense expansion (1 = hidden) by the kernels' predicate, of
     mask row b (batch row * H_m + set for per-head vectors)."""
     B, Hm, N = _mask_dims(lts)
-    return _expand(library().fm_debug_expand_mask, _mask(lts, lte, uts, ute), B, Hm, N, b, row0,
-                   row1, stream, seqlen_q, lts.device)
+    return _expand(library().fm_debug_expand_mask, _mask(lts, lte, uts, ute),
+                   (lts, lte, uts, ute), B, Hm, N, b, row0, row1, stream, seqlen_q, lts.device)
 
 
 def debug_expand_mask_multi(starts, ends, b, row0, row1, stream=None, seqlen_q=None):
     """Dense expansion of mask row b of the multi-interval form (1 = hidden)."""
     m, B, Hm, M, N = _mask_multi(starts, ends)
-    return _expand(library().fm_debug_expand_mask_multi, m, B, Hm, N, b, row0, row1, stream,
-                   seqlen_q, starts.device)
+    return _expand(library().fm_debug_expand_mask_multi, m, (starts, ends), B, Hm, N, b, row0,
+                   row1, stream, seqlen_q, starts.device)
 
 
 def debug_expand_mask_blocks(blocks, b, row0, row1, seqlen_q, seqlen_k, stream=None):
     """Dense expansion of mask row b of a block grid (1 = hidden)."""
     m, B, Hm = _mask_blocks(blocks, seqlen_q, seqlen_k)
-    return _expand(library().fm_debug_expand_mask_blocks, m, B, Hm, int(seqlen_k), b, row0, row1,
-                   stream, int(seqlen_q), blocks.device)
+    return _expand(library().fm_debug_expand_mask_blocks, m, (blocks,), B, Hm, int(seqlen_k), b,
+                   row0, row1, stream, int(seqlen_q), blocks.device)
 
 
 def _offsets(offsets):
@@ -509,15 +591,24 @@ def localize_mask(lts, lte, uts, ute, offsets, chunk_len, out=None, stream=None)
     ascending, non-overlapping).  Returns four int32 tensors of the vectors' shape ([B][N_k]
     or [B][H_m][N_k])."""
     B, Hm, N = _mask_dims(lts)
+    m = _mask(lts, lte, uts, ute)
     _offsets(offsets)
-    if out is None:
+    fresh = out is None
+    if not fresh:
+        if len(out) != 4:
+            raise ValueError("out must hold four tensors")
+        for i, t in enumerate(out):
+            _expect(t, f"out[{i}]", lts.shape, torch.int32)
+    _on_device(lts.device, [("lte", lte), ("uts", uts), ("ute", ute), ("offsets", offsets)] +
+               ([] if fresh else [(f"out[{i}]", t) for i, t in enumerate(out)]))
+    if fresh:
         out = tuple(torch.empty_like(lts) for _ in range(4))
     p = _problem(B, 1, 1, 0, seqlen_kv=N, mask_heads=Hm)
-    m = _mask(lts, lte, uts, ute)
     mo = MaskOut(*(t.data_ptr() for t in out))
     _check(library().fm_localize_mask(ctypes.byref(p), ctypes.byref(m), _ptr(offsets),
                                       int(offsets.numel()), int(chunk_len), ctypes.byref(mo),
                                       _stream(lts.device, stream)), "fm_localize_mask")
+    _keep_alive(stream, lts.device, *(out if fresh else ()))
     return out
 
 
@@ -526,13 +617,15 @@ def key_order(lts, lte, uts, ute, seqlen_q=None, permuted=False, stream=None):
     position p holds key perm[p]) and, with permuted=True, also the four vectors in that
     order.  seqlen_q: N_q (default: N_k)."""
     B, Hm, N = _mask_dims(lts)
+    m = _mask(lts, lte, uts, ute)
+    _on_device(lts.device, [("lte", lte), ("uts", uts), ("ute", ute)])
     perm = torch.empty_like(lts)
     out = tuple(torch.empty_like(lts) for _ in range(4)) if permuted else None
     p = _problem(B, 1, 1, N if seqlen_q is None else int(seqlen_q), seqlen_kv=N, mask_heads=Hm)
-    m = _mask(lts, lte, uts, ute)
     mo = ctypes.byref(MaskOut(*(t.data_ptr() for t in out))) if permuted else None
     _check(library().fm_key_order(ctypes.byref(p), ctypes.byref(m), _ptr(perm), mo,
                                   _stream(lts.device, stream)), "fm_key_order")
+    _keep_alive(stream, lts.device, perm, *(out or ()))
     return (perm, out) if permuted else perm
 
 
@@ -541,13 +634,22 @@ def localize_mask_multi(starts, ends, offsets, chunk_len, out=None, stream=None)
     Returns (starts, ends) of the input's shape."""
     m, B, Hm, M, N = _mask_multi(starts, ends)
     _offsets(offsets)
-    if out is None:
+    fresh = out is None
+    if not fresh:
+        if len(out) != 2:
+            raise ValueError("out must hold (starts, ends)")
+        for i, t in enumerate(out):
+            _expect(t, f"out[{i}]", starts.shape, torch.int32)
+    _on_device(starts.device, [("ends", ends), ("offsets", offsets)] +
+               ([] if fresh else [(f"out[{i}]", t) for i, t in enumerate(out)]))
+    if fresh:
         out = (torch.empty_like(starts), torch.empty_like(ends))
     p = _problem(B, 1, 1, 0, seqlen_kv=N, mask_heads=Hm)
     _check(library().fm_localize_mask_multi(ctypes.byref(p), ctypes.byref(m), _ptr(offsets),
                                             int(offsets.numel()), int(chunk_len), _ptr(out[0]),
                                             _ptr(out[1]), _stream(starts.device, stream)),
            "fm_localize_mask_multi")
+    _keep_alive(stream, starts.device, *(out if fresh else ()))
     return out
 
 
