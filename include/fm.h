@@ -23,7 +23,8 @@
  *    current HIP device, except the fm_problem / fm_mask / fm_tiles structs themselves,
  *    which are host structs (read during the call only).  The caller owns and allocates
  *    all memory: inputs, outputs and the workspace.  The library never allocates device
- *    memory and keeps no state between calls.
+ *    memory and keeps no state between calls, with one exception: fm_attn_fwd_static
+ *    works in a fixed device array the library holds on each GPU for the process.
  *  - Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
  *    their kernels on it and return without synchronizing.
  *  - Layouts (all contiguous, row-major), with N_q = seqlen query rows and N_k =
@@ -184,6 +185,24 @@ fm_status fm_classify_tiles(const fm_problem* p, const fm_mask* m, int32_t block
 fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const void* v,
                       const fm_mask* m, void* o, float* lse, void* ws, size_t ws_bytes,
                       void* stream, const fm_kernel_events* events);
+
+/* Forward without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same problem, arguments, outputs and errors as fm_attn_fwd, but the workspace is a
+ * device array of FM_STATIC_WORKSPACE_BYTES (16 MiB) that the library holds on every GPU
+ * it runs on until the process ends; nothing is allocated or freed by the call.  A
+ * problem whose forward workspace (fm_workspace_size(p, FM_OP_FWD, ...)) exceeds that
+ * size returns FM_ERR_WORKSPACE and launches nothing: key_order = FM_KEYS_NATURAL covers
+ * N_k up to 131072 keys with one mask row (about 8.6 MiB there); FM_KEYS_SORTED needs room
+ * for permuted copies of K and V and rarely fits.  All calls on one GPU share its array:
+ * calls that overlap on one GPU (issued on different streams with no ordering between
+ * them) race and give undefined results; calls on one stream are safe.  The first call on
+ * a device resolves the array's address there (hipGetSymbolAddress); FM_ERR_HIP if that
+ * fails, FM_ERR_UNSUPPORTED on a device index of 64 or more. */
+#define FM_STATIC_WORKSPACE_BYTES (16u << 20)
+fm_status fm_attn_fwd_static(const fm_problem* p, const void* q, const void* k, const void* v,
+                             const fm_mask* m, void* o, float* lse, void* stream,
+                             const fm_kernel_events* events);
 
 /* Backward: dQ, dK, dV (bf16) from Q, K, V, the forward's O and LSE, and dO.  Classifies
  * internally at both tile shapes (fm_tile_shape(FM_OP_BWD) for dK/dV, FM_OP_FWD for dQ),

@@ -23,7 +23,8 @@ __all__ = [
     "ipo_balance", "fm_ipo_balance", "localize_mask", "fm_localize_mask",
     "attn_fwd", "attn_bwd", "debug_expand_mask", "status_string",
     "fm_tile_shape", "fm_workspace_size", "fm_classify_tiles", "fm_attn_fwd", "fm_attn_bwd",
-    "fm_debug_expand_mask", "fm_status_string",
+    "fm_debug_expand_mask", "fm_status_string", "attn_fwd_static", "fm_attn_fwd_static",
+    "STATIC_WORKSPACE_BYTES",
     "OP_CLASSIFY", "OP_FWD", "OP_BWD", "HEAD_DIM", "key_order", "fm_key_order",
     "KEYS_NATURAL", "KEYS_SORTED", "KEY_ORDER_SPAN", "KEY_ORDER_GROUP",
 ]
@@ -34,6 +35,7 @@ KEYS_NATURAL, KEYS_SORTED = 0, 1      # fm_problem.key_order
 KEY_ORDER_SPAN, KEY_ORDER_GROUP = 2048, 64
 HEAD_DIM = 128
 FM_OK = 0
+STATIC_WORKSPACE_BYTES = 16 << 20   # FM_STATIC_WORKSPACE_BYTES
 
 
 def library_path() -> str:
@@ -113,6 +115,7 @@ def library():
             "fm_classify_tiles": ([PP, PM, ctypes.c_int32, ctypes.c_int32, PT, _P,
                                    ctypes.c_size_t, _P], _STATUS),
             "fm_attn_fwd": ([PP, _P, _P, _P, PM, _P, _P, _P, ctypes.c_size_t, _P, PE], _STATUS),
+            "fm_attn_fwd_static": ([PP, _P, _P, _P, PM, _P, _P, _P, PE], _STATUS),
             "fm_attn_bwd": ([PP, _P, _P, _P, _P, _P, _P, PM, _P, _P, _P, _P, ctypes.c_size_t,
                              _P, PE], _STATUS),
             "fm_debug_expand_mask": ([PP, PM, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -502,6 +505,40 @@ def attn_fwd(q, k, v, lts, lte, uts, ute, scale=None, ws=None, out=None, lse=Non
                 _mask_dims(lts), scale, ws, out, lse, stream, events, key_order)
 
 
+def attn_fwd_static(q, k, v, lts, lte, uts, ute, scale=None, out=None, lse=None, stream=None,
+                    events=None):
+    """fm_attn_fwd_static: attn_fwd on the library's own fixed device workspace (no
+    workspace argument; for callers that cannot allocate).  Pass `out` and `lse` to make the
+    call allocate nothing at all.  Problems whose forward workspace exceeds
+    STATIC_WORKSPACE_BYTES are refused.  Calls that overlap on one GPU (different streams)
+    race on the shared workspace."""
+    m = _mask(lts, lte, uts, ute)
+    mask_ts = (lts, lte, uts, ute)
+    _bf16(("q", q), ("k", k), ("v", v))
+    B, Hq, Hkv, N, Nk, d, Hm = _shapes(q, k, _mask_dims(lts))
+    _expect(v, "v", k.shape, torch.bfloat16)
+    if out is not None:
+        _expect(out, "out", q.shape, torch.bfloat16)
+    if lse is not None:
+        _expect(lse, "lse", (B, Hq, N), torch.float32)
+    need = workspace_size(B, Hq, Hkv, N, OP_FWD, head_dim=d, seqlen_kv=Nk, mask_heads=Hm)
+    if need > STATIC_WORKSPACE_BYTES:
+        raise ValueError(f"the forward workspace of this problem ({need} bytes) exceeds the "
+                         f"static workspace ({STATIC_WORKSPACE_BYTES} bytes); use attn_fwd")
+    dev = q.device
+    _on_device(dev, [("k", k), ("v", v), ("out", out), ("lse", lse)] +
+               [(f"mask tensor {i}", t) for i, t in enumerate(mask_ts)])
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if lse is None else lse
+    p = _problem(B, Hq, Hkv, N, scale, head_dim=d, seqlen_kv=Nk, mask_heads=Hm)
+    _check(library().fm_attn_fwd_static(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                        ctypes.byref(m), _ptr(o), _ptr(lse_t),
+                                        _stream(dev, stream), _events(events)),
+           "fm_attn_fwd_static")
+    _keep_alive(stream, dev, o if out is None else None, lse_t if lse is None else None)
+    return o, lse_t
+
+
 def attn_fwd_multi(q, k, v, starts, ends, scale=None, ws=None, out=None, lse=None, stream=None,
                    events=None):
     """fm_attn_fwd_multi: as attn_fwd with the multi-interval mask, starts/ends
@@ -658,6 +695,7 @@ fm_tile_shape = tile_shape
 fm_workspace_size = workspace_size
 fm_classify_tiles = classify_tiles
 fm_attn_fwd = attn_fwd
+fm_attn_fwd_static = attn_fwd_static
 fm_attn_bwd = attn_bwd
 fm_debug_expand_mask = debug_expand_mask
 fm_localize_mask = localize_mask
