@@ -77,7 +77,10 @@ def test_dense_expansion_sampled_blocks(name):
     w = workloads.make_workload(name)
     vec = workloads.mask_tensors(w, device="cuda")
     rng = np.random.default_rng(0)
-    for r0 in rng.integers(0, w.seqlen // 128, 32) * 128:
+    # 256 distinct seeded 128-row blocks, the first and the last among them
+    nb = w.seqlen // 128
+    picks = np.r_[0, nb - 1, rng.choice(np.arange(1, nb - 1), 254, replace=False)]
+    for r0 in np.sort(picks) * 128:
         dense = fm.debug_expand_mask(*vec, 0, int(r0), int(r0) + 128).cpu().numpy()
         ref = oracle.masked_rows(*(x[0] for x in w.vectors()), int(r0), int(r0) + 128)
         assert np.array_equal(dense.astype(bool), ref), (name, r0)
