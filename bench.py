@@ -13,6 +13,12 @@ other timed step.  Its `traffic` is the HBM bytes per launch
 from a committed rocprofv3 counter summary (profiles/traffic_<kernel>_<workload>.txt),
 reported only while the kernel sources still hash to the value recorded there.
 
+The default run times the random-eviction workload (128K keys, keys sorted) and then the
+share-question (32K) and sliding-window (128K) workloads, reported under "also".  `peak` is
+the published dense bf16 MFMA figure; beside it the line gives the device's CU count, the
+GFX clock sampled (amdsmi) during the timed steps and the MFMA peak at that clock.
+`--schedule natural` dispatches work items in index order instead of LPT order.
+
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
 `--calibrate-copy MIB` instead runs a plain device-to-device copy of that size (for
 scaling the FETCH_SIZE / WRITE_SIZE counters) and prints its byte count.
@@ -47,7 +53,11 @@ sys.path.insert(0, ROOT)
 import workloads  # noqa: E402
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16: 256 CU x 2.4 GHz x 4096 flop/clk/CU
-DEFAULT_WORKLOAD = "c2_prefix_lm_doc_8k"
+MFMA_BF16_FLOP_PER_CLK_CU = 4096
+# The headline runs on the largest single-GPU configuration (random eviction, 128K keys);
+# the other long-context configurations are timed in the same run and reported beside it.
+DEFAULT_WORKLOAD = "c5_random_eviction_128k"
+ALSO_WORKLOADS = ("c3_share_question_32k", "c4_sliding_window_128k")
 # workloads timed with their keys reordered (fm_problem.key_order = FM_KEYS_SORTED) unless
 # --key-order says otherwise: the random-eviction mask, whose columns end at scattered rows
 SORTED_KEY_WORKLOADS = {"c5_random_eviction_128k"}
@@ -352,10 +362,17 @@ def measure_alpha(steps, warmup, n=8192, heads=64):
                       "dk_dv_max_abs_diff": dkdv_diff}))
 
 
+CPU_SAMPLE_ROWS = 8192
+
+
 def cpu_baseline(w, q, k, v, do, budget_s):
-    """Time the fp64 oracle on a bounded sample of the same workload: whole (b, h)
-    problems, taken in order b = 0.., h spread over the heads, until the budget is
-    spent.  Reported in the metric's unit over the sample's attended pairs."""
+    """Time the fp64 oracle on a bounded sample of the same workload, until the budget is
+    spent: whole (b, h) problems for the multi-interval and block forms; for the
+    four-vector form, units of at most CPU_SAMPLE_ROWS query rows of one (b, h) against
+    every key (the rows' vectors renumbered into the unit's rows, as one context-parallel
+    rank's share), taken b = 0.., h = 0.., row chunks in a seeded order so that one long
+    head does not exceed the budget.  Reported in the metric's unit over the sample's
+    attended pairs."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -364,49 +381,222 @@ def cpu_baseline(w, q, k, v, do, budget_s):
     except Exception:
         threads = os.cpu_count()
     g = w.heads_q // w.heads_kv
-    heads = list(range(w.heads_q))
-    done, pairs, t_total = [], 0, 0.0
+    n = w.seqlen
+    four = not isinstance(w, (workloads.BlockWorkload, workloads.MultiWorkload))
+    chunk = min(n, CPU_SAMPLE_ROWS) if four else n
+    n_chunks = -(-n // chunk)
+    chunk_order = np.random.default_rng(0).permutation(n_chunks)
+    units, rows, pairs, t_total = 0, 0, 0, 0.0
+    f = lambda t, b, hh, r0=0, r1=None: \
+        t[b:b + 1, hh:hh + 1, r0:r1].float().cpu().numpy().astype(np.float64)
     for b in range(w.batch):
-        for h in heads:
+        for h in range(w.heads_q):
             kvh = h // g
-            f = lambda t, hh: t[b:b + 1, hh:hh + 1].float().cpu().numpy().astype(np.float64)
-            args = (f(q, h), f(k, kvh), f(v, kvh), f(do, h))
-            if isinstance(w, workloads.BlockWorkload):
-                m = h // (w.heads_q // w.mask_heads)
-                grid = w.blocks[b:b + 1] if w.blocks.ndim == 3 else w.blocks[b:b + 1, m]
-                t0 = time.perf_counter()
-                oracle.attention_fwd_bwd_blocks(*args, grid)
-                t_total += time.perf_counter() - t0
-                one = workloads.BlockWorkload(w.name, 1, 1, 1, w.seqlen, w.head_dim,
-                                              np.ascontiguousarray(grid), w.seed)
-                pairs += attended_pairs_blocks(one)
-            elif isinstance(w, workloads.MultiWorkload):
-                m = h // (w.heads_q // w.mask_heads)
-                st, en = ((x[b:b + 1] if x.ndim == 3 else x[b:b + 1, m]) for x in w.intervals())
-                t0 = time.perf_counter()
-                oracle.attention_fwd_bwd_multi(*args, st, en)
-                t_total += time.perf_counter() - t0
-                one = workloads.MultiWorkload(w.name, 1, 1, 1, w.seqlen, w.head_dim,
-                                              st.copy(), en.copy(), w.seed)
-                pairs += attended_pairs_multi(one)
-            else:
-                sub = head_vectors(w, b, h)
-                t0 = time.perf_counter()
-                oracle.attention_fwd_bwd(*args, *sub)
-                t_total += time.perf_counter() - t0
-                one = workloads.Workload(w.name, 1, 1, 1, w.seqlen, w.head_dim,
-                                         *[np.ascontiguousarray(x) for x in sub], w.seed)
-                pairs += attended_pairs(one)
-            done.append((b, h))
+            for c in (chunk_order if four else [0]):
+                r0, r1 = int(c) * chunk, min(int(c) * chunk + chunk, n)
+                if isinstance(w, workloads.BlockWorkload):
+                    m = h // (w.heads_q // w.mask_heads)
+                    grid = w.blocks[b:b + 1] if w.blocks.ndim == 3 else w.blocks[b:b + 1, m]
+                    args = (f(q, b, h), f(k, b, kvh), f(v, b, kvh), f(do, b, h))
+                    t0 = time.perf_counter()
+                    oracle.attention_fwd_bwd_blocks(*args, grid)
+                    t_total += time.perf_counter() - t0
+                    one = workloads.BlockWorkload(w.name, 1, 1, 1, n, w.head_dim,
+                                                  np.ascontiguousarray(grid), w.seed)
+                    pairs += attended_pairs_blocks(one)
+                elif isinstance(w, workloads.MultiWorkload):
+                    m = h // (w.heads_q // w.mask_heads)
+                    st, en = ((x[b:b + 1] if x.ndim == 3 else x[b:b + 1, m])
+                              for x in w.intervals())
+                    args = (f(q, b, h), f(k, b, kvh), f(v, b, kvh), f(do, b, h))
+                    t0 = time.perf_counter()
+                    oracle.attention_fwd_bwd_multi(*args, st, en)
+                    t_total += time.perf_counter() - t0
+                    one = workloads.MultiWorkload(w.name, 1, 1, 1, n, w.head_dim,
+                                                  st.copy(), en.copy(), w.seed)
+                    pairs += attended_pairs_multi(one)
+                else:
+                    sub = head_vectors(w, b, h)
+                    local = oracle.localize_vectors(sub, [r0], r1 - r0)
+                    args = (f(q, b, h, r0, r1), f(k, b, kvh), f(v, b, kvh), f(do, b, h, r0, r1))
+                    t0 = time.perf_counter()
+                    oracle.attention_fwd_bwd(*args, *local)
+                    t_total += time.perf_counter() - t0
+                    one = workloads.Workload(w.name, 1, 1, 1, r1 - r0, w.head_dim,
+                                             *[np.ascontiguousarray(x) for x in local], w.seed)
+                    pairs += attended_pairs(one)
+                units += 1
+                rows += r1 - r0
+                if t_total >= budget_s:
+                    break
             if t_total >= budget_s:
                 break
         if t_total >= budget_s:
             break
     flop = 14 * w.head_dim * pairs
+    what = (f"{units} units of <= {chunk} query rows of one (b,h) ({rows} rows of "
+            f"{w.batch * w.heads_q * n})" if four else
+            f"{units} of {w.batch * w.heads_q} (b,h) problems")
     return {"value": flop / t_total / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{len(done)} of {w.batch * w.heads_q} (b,h) problems of {w.name}, "
-                      f"fp64 numpy fwd+bwd, {t_total:.1f} s"}
+            "sample": f"{what} of {w.name}, fp64 numpy fwd+bwd, {t_total:.1f} s"}
+
+
+class ClockSampler:
+    """The GFX clock (MHz) sampled by amdsmi every `period` seconds in a thread, between
+    start() and stop(); mean() is None where amdsmi is unavailable."""
+
+    def __init__(self, period=0.02):
+        import threading
+        self.period, self.samples, self._stop = period, [], threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            self._read()
+        except Exception:
+            self._smi = None
+
+    def _read(self):
+        return float(self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)["clk"])
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception:
+                return
+            self._stop.wait(self.period)
+
+    def start(self):
+        import threading
+        if self._smi is not None:
+            self._thread = threading.Thread(target=self._loop, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        if self._smi is not None:
+            try:
+                self._smi.amdsmi_shut_down()
+            except Exception:
+                pass
+
+    def mean(self):
+        return float(np.mean(self.samples)) if self.samples else None
+
+
+def run_workload(name, seed, steps, warmup, key_order_opt, schedule, clock=None):
+    """Time `steps` fwd+bwd steps of workload `name` after `warmup` untimed ones.  Returns a
+    dict of the figures and the input tensors (for the CPU baseline)."""
+    import torch
+    import mask_aware_sparse_amd as fm
+
+    dev = "cuda"
+    w = workloads.make_workload(name, seed)
+    q, k, v, do = workloads.make_tensors(w, device=dev)
+    vec = workloads.mask_tensors(w, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.heads_q, w.seqlen), dtype=torch.float32, device=dev)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    multi = isinstance(w, workloads.MultiWorkload)
+    blocks = isinstance(w, workloads.BlockWorkload)
+    sorted_keys = (key_order_opt == "sorted" or
+                   (key_order_opt == "auto" and name in SORTED_KEY_WORKLOADS))
+    if sorted_keys and (multi or blocks):
+        sys.exit("bench.py: --key-order sorted applies to four-vector masks only")
+    key_order = fm.KEYS_SORTED if sorted_keys else fm.KEYS_NATURAL
+    sched = fm.SCHEDULE_NATURAL if schedule == "natural" else fm.SCHEDULE_LPT
+    ws_f = torch.empty(fm.workspace_size(w.batch, w.heads_q, w.heads_kv, w.seqlen, fm.OP_FWD,
+                                         head_dim=w.head_dim, mask_heads=w.mask_heads,
+                                         key_order=key_order),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(fm.workspace_size(w.batch, w.heads_q, w.heads_kv, w.seqlen, fm.OP_BWD,
+                                         head_dim=w.head_dim, mask_heads=w.mask_heads,
+                                         key_order=key_order),
+                       dtype=torch.uint8, device=dev)
+    A = attended_pairs_blocks(w) if blocks else (attended_pairs_multi(w) if multi
+                                                 else attended_pairs(w))
+    d = w.head_dim
+    attn_fwd = fm.attn_fwd_blocks if blocks else (fm.attn_fwd_multi if multi else fm.attn_fwd)
+    attn_bwd = fm.attn_bwd_blocks if blocks else (fm.attn_bwd_multi if multi else fm.attn_bwd)
+    opt = {"schedule": sched}
+    if not (multi or blocks):
+        opt["key_order"] = key_order
+
+    # per instrumented step: 0 start, 1/2 fwd kernel, 8 between the calls, 3/4 dK/dV
+    # kernel, 6/7 dQ kernel, 5 end (all on the current stream, which the library launches
+    # on).  Every other timed step is instrumented: a timing event costs the stream some
+    # tens of microseconds, which would otherwise be charged to every step's wall time.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(9)]
+          for _ in range((steps + 1) // 2)]
+
+    def step(e=None):
+        if e is not None:
+            e[0].record()
+        attn_fwd(q, k, v, *vec, ws=ws_f, out=o, lse=lse,
+                 events=None if e is None else (e[1], e[2]), **opt)
+        if e is not None:
+            e[8].record()
+        attn_bwd(q, k, v, o, lse, do, *vec, ws=ws_b, grads=grads,
+                 events=None if e is None else (e[3], e[4], e[6], e[7]), **opt)
+        if e is not None:
+            e[5].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    if clock is not None:
+        clock.start()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(ev[i // 2] if i % 2 == 0 else None)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if clock is not None:
+        clock.stop()
+
+    el = lambda a, b: np.array([e[a].elapsed_time(e[b]) for e in ev])
+    step_ms, call_fwd_ms, call_bwd_ms = el(0, 5), el(0, 8), el(8, 5)
+    fwd_ms, dkdv_ms, dq_ms = el(1, 2), el(3, 4), el(6, 7)
+    ms = wall * 1e3 / steps
+    value = 14 * d * A / (ms * 1e-3) / 1e12
+    # algorithmic flop per attended pair of each attention kernel: forward 4d (QK, PV);
+    # dK/dV kernel 8d (S and dP recomputed once for the backward, dV, dK); dQ kernel 2d
+    # (its second recomputation of S and dP is not algorithmic work)
+    kernels = {
+        "k_attn_fwd": (float(fwd_ms.mean()), 4 * d * A),
+        "k_attn_bwd_dkdv": (float(dkdv_ms.mean()), 8 * d * A),
+        "k_attn_bwd_dq": (float(dq_ms.mean()), 2 * d * A),
+    }
+    tflops = {kname: f / (t * 1e-3) / 1e12 for kname, (t, f) in kernels.items()}
+    dom = max(kernels, key=lambda kname: kernels[kname][0])
+    config = {"workload": name, "batch": w.batch, "heads_q": w.heads_q,
+              "heads_kv": w.heads_kv, "mask_heads": w.mask_heads,
+              "mask_intervals": w.n_intervals if multi else None,
+              "mask_blocks": "128x128" if blocks else None, "seq_len": w.seqlen,
+              "head_dim": d, "attended_pairs": A, "seed": seed,
+              "key_order": "sorted" if sorted_keys else "natural", "schedule": schedule}
+    return {
+        "w": w, "tensors": (q, k, v, do), "value": value, "ms": ms, "config": config,
+        "kernels": {kname: {"ms": round(t, 4), "algorithmic_tflops": round(tflops[kname], 2)}
+                    for kname, (t, _) in kernels.items()},
+        "event_ms_per_step": round(float(step_ms.mean()), 4),
+        # whole calls, classification and LPT sort included: 4d*A / t_fwd and 10d*A / t_bwd
+        "fwd": {"ms": round(float(call_fwd_ms.mean()), 4),
+                "tflops": round(4 * d * A / (call_fwd_ms.mean() * 1e-3) / 1e12, 2)},
+        "bwd": {"ms": round(float(call_bwd_ms.mean()), 4),
+                "tflops": round(10 * d * A / (call_bwd_ms.mean() * 1e-3) / 1e12, 2)},
+        "roofline": {"kernel": dom, "bound": "mfma",
+                     "achieved": round(tflops[dom], 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops[dom] / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": stored_traffic(dom, name + ("_sorted_keys" if sorted_keys
+                                                            else ""))},
+    }
 
 
 def main():
@@ -416,6 +606,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     choices=workloads.CONFIG_NAMES + workloads.VARIANT_NAMES)
+    ap.add_argument("--also", default=None,
+                    help="comma-separated workloads timed after the headline one (default: "
+                         "c3 and c4 with the default workload, none otherwise; '' for none)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline sample (0 = skip)")
@@ -432,6 +625,8 @@ def main():
     ap.add_argument("--key-order", choices=["auto", "natural", "sorted"], default="auto",
                     help="key order of the four-vector entry points (auto: sorted for the "
                          "random-eviction workload, natural otherwise)")
+    ap.add_argument("--schedule", choices=["lpt", "natural"], default="lpt",
+                    help="dispatch order of the attention kernels' work items")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; multi-GPU runs are not supported",
@@ -448,129 +643,70 @@ def main():
         ipo_table()
         return
     if args.cp > 0:
-        cp_emulation(args.workload if args.workload != DEFAULT_WORKLOAD else
-                     "c5_random_eviction_128k", args.cp, min(args.steps, 3), min(args.warmup, 1))
+        cp_emulation(args.workload, args.cp, min(args.steps, 3), min(args.warmup, 1))
         return
     if args.classify_bandwidth:
         classify_bandwidth(args.steps, args.warmup)
         return
 
     import torch
-    import mask_aware_sparse_amd as fm
 
-    dev = "cuda"
-    w = workloads.make_workload(args.workload, args.seed)
-    q, k, v, do = workloads.make_tensors(w, device=dev)
-    vec = workloads.mask_tensors(w, device=dev)
-    o = torch.empty_like(q)
-    lse = torch.empty((w.batch, w.heads_q, w.seqlen), dtype=torch.float32, device=dev)
-    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-    multi = isinstance(w, workloads.MultiWorkload)
-    blocks = isinstance(w, workloads.BlockWorkload)
-    sorted_keys = (args.key_order == "sorted" or
-                   (args.key_order == "auto" and args.workload in SORTED_KEY_WORKLOADS))
-    if sorted_keys and (multi or blocks):
-        sys.exit("bench.py: --key-order sorted applies to four-vector masks only")
-    key_order = fm.KEYS_SORTED if sorted_keys else fm.KEYS_NATURAL
-    ws_f = torch.empty(fm.workspace_size(w.batch, w.heads_q, w.heads_kv, w.seqlen, fm.OP_FWD,
-                                         head_dim=w.head_dim, mask_heads=w.mask_heads,
-                                         key_order=key_order),
-                       dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(fm.workspace_size(w.batch, w.heads_q, w.heads_kv, w.seqlen, fm.OP_BWD,
-                                         head_dim=w.head_dim, mask_heads=w.mask_heads,
-                                         key_order=key_order),
-                       dtype=torch.uint8, device=dev)
-    A = attended_pairs_blocks(w) if blocks else (attended_pairs_multi(w) if multi
-                                                 else attended_pairs(w))
-    d = w.head_dim
-    attn_fwd = fm.attn_fwd_blocks if blocks else (fm.attn_fwd_multi if multi else fm.attn_fwd)
-    attn_bwd = fm.attn_bwd_blocks if blocks else (fm.attn_bwd_multi if multi else fm.attn_bwd)
-    opt = {} if (multi or blocks) else {"key_order": key_order}
-
-    # per instrumented step: 0 start, 1/2 fwd kernel, 8 between the calls, 3/4 dK/dV
-    # kernel, 6/7 dQ kernel, 5 end (all on the current stream, which the library launches
-    # on).  Every other timed step is instrumented: a timing event costs the stream some
-    # tens of microseconds, which would otherwise be charged to every step's wall time.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(9)]
-          for _ in range((args.steps + 1) // 2)]
-
-    def step(e=None):
-        if e is not None:
-            e[0].record()
-        attn_fwd(q, k, v, *vec, ws=ws_f, out=o, lse=lse,
-                 events=None if e is None else (e[1], e[2]), **opt)
-        if e is not None:
-            e[8].record()
-        attn_bwd(q, k, v, o, lse, do, *vec, ws=ws_b, grads=grads,
-                 events=None if e is None else (e[3], e[4], e[6], e[7]), **opt)
-        if e is not None:
-            e[5].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(ev[i // 2] if i % 2 == 0 else None)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    step_ms = np.array([e[0].elapsed_time(e[5]) for e in ev])
-    call_fwd_ms = np.array([e[0].elapsed_time(e[8]) for e in ev])
-    call_bwd_ms = np.array([e[8].elapsed_time(e[5]) for e in ev])
-    fwd_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    dkdv_ms = np.array([e[3].elapsed_time(e[4]) for e in ev])
-    dq_ms = np.array([e[6].elapsed_time(e[7]) for e in ev])
-    ms = wall * 1e3 / args.steps
-    value = 14 * d * A / (ms * 1e-3) / 1e12
-    # algorithmic flop per attended pair of each attention kernel: forward 4d (QK, PV);
-    # dK/dV kernel 8d (S and dP recomputed once for the backward, dV, dK); dQ kernel 2d
-    # (its second recomputation of S and dP is not algorithmic work)
-    kernels = {
-        "k_attn_fwd": (float(fwd_ms.mean()), 4 * d * A),
-        "k_attn_bwd_dkdv": (float(dkdv_ms.mean()), 8 * d * A),
-        "k_attn_bwd_dq": (float(dq_ms.mean()), 2 * d * A),
-    }
-    tflops = {kname: f / (t * 1e-3) / 1e12 for kname, (t, f) in kernels.items()}
-    dom = max(kernels, key=lambda kname: kernels[kname][0])
-
+    if args.also is None:
+        also = list(ALSO_WORKLOADS) if args.workload == DEFAULT_WORKLOAD else []
+    else:
+        also = [x for x in args.also.split(",") if x]
+    clock = ClockSampler()
+    r = run_workload(args.workload, args.seed, args.steps, args.warmup, args.key_order,
+                     args.schedule, clock)
     cpu = None
     if args.cpu_budget > 0:
-        cpu = cpu_baseline(w, q, k, v, do, args.cpu_budget)
-
+        cpu = cpu_baseline(r["w"], *r["tensors"], args.cpu_budget)
+    r["tensors"] = None
+    torch.cuda.empty_cache()
+    cu = int(torch.cuda.get_device_properties(0).multi_processor_count)
+    mhz = clock.mean()
+    peak_at_clock = cu * MFMA_BF16_FLOP_PER_CLK_CU * mhz * 1e6 / 1e12 if mhz else None
+    extra = {}
+    for name in also:
+        x = run_workload(name, args.seed, args.steps, args.warmup, args.key_order,
+                         args.schedule)
+        x["tensors"] = None
+        torch.cuda.empty_cache()
+        extra[name] = {"value": round(x["value"], 3), "unit": "TFLOP/s",
+                       "ms_per_step": round(x["ms"], 4),
+                       "pct_mfma_peak": round(100 * x["value"] / MFMA_BF16_PEAK_TFLOPS, 2),
+                       "key_order": x["config"]["key_order"], "kernels": x["kernels"],
+                       "fwd": x["fwd"], "bwd": x["bwd"],
+                       "roofline": {k_: x["roofline"][k_] for k_ in ("kernel", "achieved", "frac",
+                                                                     "traffic")}}
     out = {
         "metric": "effective TFLOP/s (attended pairs only) fwd+bwd, bf16 d=128; % MFMA peak",
-        "value": round(value, 3),
+        "value": round(r["value"], 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": round(r["ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": w.batch, "heads_q": w.heads_q,
-                   "heads_kv": w.heads_kv, "mask_heads": w.mask_heads,
-                   "mask_intervals": w.n_intervals if multi else None,
-                   "mask_blocks": "128x128" if blocks else None, "seq_len": w.seqlen,
-                   "head_dim": d, "attended_pairs": A, "seed": args.seed,
-                   "key_order": "sorted" if sorted_keys else "natural"},
-        "pct_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
-        "kernels": {kname: {"ms": round(t, 4), "algorithmic_tflops": round(tflops[kname], 2)}
-                    for kname, (t, _) in kernels.items()},
-        "event_ms_per_step": round(float(step_ms.mean()), 4),
-        # whole calls, classification and LPT sort included: 4d*A / t_fwd and 10d*A / t_bwd
-        "fwd": {"ms": round(float(call_fwd_ms.mean()), 4),
-                "tflops": round(4 * d * A / (call_fwd_ms.mean() * 1e-3) / 1e12, 2)},
-        "bwd": {"ms": round(float(call_bwd_ms.mean()), 4),
-                "tflops": round(10 * d * A / (call_bwd_ms.mean() * 1e-3) / 1e12, 2)},
-        "roofline": {"kernel": dom, "bound": "mfma",
-                     "achieved": round(tflops[dom], 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops[dom] / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": stored_traffic(dom, args.workload)},
+        "config": r["config"],
+        "pct_mfma_peak": round(100 * r["value"] / MFMA_BF16_PEAK_TFLOPS, 2),
+        "device": {"compute_units": cu, "gfx_clock_mhz_mean": round(mhz, 1) if mhz else None,
+                   "clock_samples": len(clock.samples),
+                   "mfma_bf16_peak_at_clock_tflops": round(peak_at_clock, 1)
+                   if peak_at_clock else None,
+                   "pct_mfma_peak_at_clock": round(100 * r["value"] / peak_at_clock, 2)
+                   if peak_at_clock else None},
+        "kernels": r["kernels"],
+        "event_ms_per_step": r["event_ms_per_step"],
+        "fwd": r["fwd"],
+        "bwd": r["bwd"],
+        "roofline": r["roofline"],
         "cpu_baseline": cpu,
+        "also": extra,
     }
     print(json.dumps(out))
 

@@ -89,7 +89,19 @@ typedef struct {
   int32_t seqlen_kv;
   int32_t mask_heads;
   int32_t key_order; /* FM_KEYS_NATURAL (0) or FM_KEYS_SORTED (1), see fm_key_order */
+  int32_t schedule;  /* FM_SCHEDULE_LPT (0) or FM_SCHEDULE_NATURAL (1), see below */
 } fm_problem;
+
+/* Dispatch order of the attention kernels' work items (fm_attn_fwd, fm_attn_bwd and their
+ * _multi / _blocks / _static forms).  FM_SCHEDULE_LPT: cost-descending, the q_order /
+ * k_order of fm_classify_tiles (FlashMask-3 page, §3.3, longest processing time first).
+ * FM_SCHEDULE_NATURAL: index order (mask row, then block), for measuring what the LPT order
+ * buys; the outputs are the same attention (O, LSE and dQ bit for bit; dK/dV up to the
+ * fp32 summation order: the dK/dV split plan grants its extra segments in dispatch order,
+ * and atomic additions follow it).
+ * fm_classify_tiles always writes the LPT orders.  Other values: FM_ERR_INVALID_ARG. */
+#define FM_SCHEDULE_LPT 0
+#define FM_SCHEDULE_NATURAL 1
 
 /* Key order of fm_attn_fwd / fm_attn_bwd (four-vector masks).  FM_KEYS_SORTED runs the
  * attention kernels over the keys in the order fm_key_order gives: K, V and the vectors are

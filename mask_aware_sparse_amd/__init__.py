@@ -26,12 +26,14 @@ __all__ = [
     "fm_debug_expand_mask", "fm_status_string", "attn_fwd_static", "fm_attn_fwd_static",
     "STATIC_WORKSPACE_BYTES",
     "OP_CLASSIFY", "OP_FWD", "OP_BWD", "HEAD_DIM", "key_order", "fm_key_order",
-    "KEYS_NATURAL", "KEYS_SORTED", "KEY_ORDER_SPAN", "KEY_ORDER_GROUP",
+    "KEYS_NATURAL", "KEYS_SORTED", "KEY_ORDER_SPAN", "KEY_ORDER_GROUP", "SCHEDULE_LPT",
+    "SCHEDULE_NATURAL",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 OP_CLASSIFY, OP_FWD, OP_BWD = 0, 1, 2
 KEYS_NATURAL, KEYS_SORTED = 0, 1      # fm_problem.key_order
+SCHEDULE_LPT, SCHEDULE_NATURAL = 0, 1  # fm_problem.schedule
 KEY_ORDER_SPAN, KEY_ORDER_GROUP = 2048, 64
 HEAD_DIM = 128
 FM_OK = 0
@@ -53,7 +55,7 @@ class Problem(ctypes.Structure):
                 ("heads_kv", ctypes.c_int32), ("seqlen", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("seqlen_kv", ctypes.c_int32), ("mask_heads", ctypes.c_int32),
-                ("key_order", ctypes.c_int32)]
+                ("key_order", ctypes.c_int32), ("schedule", ctypes.c_int32)]
 
 
 class MaskOut(ctypes.Structure):
@@ -160,10 +162,10 @@ def _check(status, where):
 
 
 def _problem(batch, heads_q, heads_kv, seqlen, scale=None, head_dim=HEAD_DIM, seqlen_kv=0,
-             mask_heads=0, key_order=KEYS_NATURAL):
+             mask_heads=0, key_order=KEYS_NATURAL, schedule=SCHEDULE_LPT):
     return Problem(int(batch), int(heads_q), int(heads_kv), int(seqlen), int(head_dim),
                    float(scale) if scale is not None else 0.0, int(seqlen_kv), int(mask_heads),
-                   int(key_order))
+                   int(key_order), int(schedule))
 
 
 def _mask(lts, lte, uts, ute):
@@ -435,7 +437,7 @@ def _events(ev):
 
 
 def _fwd(fn, q, k, v, m, mask_ts, mask_shape, scale, ws, out, lse, stream, events,
-         key_order=KEYS_NATURAL):
+         key_order=KEYS_NATURAL, schedule=SCHEDULE_LPT):
     _bf16(("q", q), ("k", k), ("v", v))
     B, Hq, Hkv, N, Nk, d, Hm = _shapes(q, k, mask_shape)
     _expect(v, "v", k.shape, torch.bfloat16)
@@ -449,7 +451,7 @@ def _fwd(fn, q, k, v, m, mask_ts, mask_shape, scale, ws, out, lse, stream, event
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if lse is None else lse
     p = _problem(B, Hq, Hkv, N, scale, head_dim=d, seqlen_kv=Nk, mask_heads=Hm,
-                 key_order=key_order)
+                 key_order=key_order, schedule=schedule)
     nbytes = workspace_size(B, Hq, Hkv, N, OP_FWD, head_dim=d, seqlen_kv=Nk, mask_heads=Hm,
                             key_order=key_order)
     w, own_ws = _workspace(nbytes, dev, ws)
@@ -462,7 +464,7 @@ def _fwd(fn, q, k, v, m, mask_ts, mask_shape, scale, ws, out, lse, stream, event
 
 
 def _bwd(fn, q, k, v, o, lse, dout, m, mask_ts, mask_shape, scale, ws, grads, stream, events,
-         key_order=KEYS_NATURAL):
+         key_order=KEYS_NATURAL, schedule=SCHEDULE_LPT):
     _bf16(("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout))
     B, Hq, Hkv, N, Nk, d, Hm = _shapes(q, k, mask_shape)
     _expect(v, "v", k.shape, torch.bfloat16)
@@ -483,7 +485,7 @@ def _bwd(fn, q, k, v, o, lse, dout, m, mask_ts, mask_shape, scale, ws, grads, st
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = grads
     p = _problem(B, Hq, Hkv, N, scale, head_dim=d, seqlen_kv=Nk, mask_heads=Hm,
-                 key_order=key_order)
+                 key_order=key_order, schedule=schedule)
     nbytes = workspace_size(B, Hq, Hkv, N, OP_BWD, head_dim=d, seqlen_kv=Nk, mask_heads=Hm,
                             key_order=key_order)
     w, own_ws = _workspace(nbytes, dev, ws)
@@ -495,14 +497,15 @@ def _bwd(fn, q, k, v, o, lse, dout, m, mask_ts, mask_shape, scale, ws, grads, st
 
 
 def attn_fwd(q, k, v, lts, lte, uts, ute, scale=None, ws=None, out=None, lse=None, stream=None,
-             events=None, key_order=KEYS_NATURAL):
+             events=None, key_order=KEYS_NATURAL, schedule=SCHEDULE_LPT):
     """O (bf16 [B][H_q][N_q][d]) and LSE (fp32 [B][H_q][N_q], natural log) via fm_attn_fwd;
     K/V are [B][H_kv][N_k][d] and the vectors [B][N_k] or, one set per group of H_q / H_m
     query heads, [B][H_m][N_k].
     `events`: optional (start, stop) torch.cuda.Event pair timing the attention kernel.
-    `key_order`: KEYS_SORTED runs the kernels over the keys in fm_key_order's order."""
+    `key_order`: KEYS_SORTED runs the kernels over the keys in fm_key_order's order.
+    `schedule`: SCHEDULE_LPT (cost-descending dispatch) or SCHEDULE_NATURAL (index order)."""
     return _fwd(library().fm_attn_fwd, q, k, v, _mask(lts, lte, uts, ute), (lts, lte, uts, ute),
-                _mask_dims(lts), scale, ws, out, lse, stream, events, key_order)
+                _mask_dims(lts), scale, ws, out, lse, stream, events, key_order, schedule)
 
 
 def attn_fwd_static(q, k, v, lts, lte, uts, ute, scale=None, out=None, lse=None, stream=None,
@@ -540,47 +543,47 @@ def attn_fwd_static(q, k, v, lts, lte, uts, ute, scale=None, out=None, lse=None,
 
 
 def attn_fwd_multi(q, k, v, starts, ends, scale=None, ws=None, out=None, lse=None, stream=None,
-                   events=None):
+                   events=None, schedule=SCHEDULE_LPT):
     """fm_attn_fwd_multi: as attn_fwd with the multi-interval mask, starts/ends
     [B][M][N_k] or [B][H_m][M][N_k] (key j visible to row i iff some interval holds i)."""
     m, B, Hm, M, Nk = _mask_multi(starts, ends)
     return _fwd(library().fm_attn_fwd_multi, q, k, v, m, (starts, ends), (B, Hm, Nk), scale,
-                ws, out, lse, stream, events)
+                ws, out, lse, stream, events, schedule=schedule)
 
 
 def attn_fwd_blocks(q, k, v, blocks, scale=None, ws=None, out=None, lse=None, stream=None,
-                    events=None):
+                    events=None, schedule=SCHEDULE_LPT):
     """fm_attn_fwd_blocks: as attn_fwd with a block-sparse mask, a uint8 grid [B][nQB][nKB]
     or [B][H_m][nQB][nKB] over 128 x 128 blocks (1 = visible)."""
     m, B, Hm = _mask_blocks(blocks, q.shape[2], k.shape[2])
     return _fwd(library().fm_attn_fwd_blocks, q, k, v, m, (blocks,), (B, Hm, k.shape[2]),
-                scale, ws, out, lse, stream, events)
+                scale, ws, out, lse, stream, events, schedule=schedule)
 
 
 def attn_bwd_blocks(q, k, v, o, lse, dout, blocks, scale=None, ws=None, grads=None, stream=None,
-                    events=None):
+                    events=None, schedule=SCHEDULE_LPT):
     """fm_attn_bwd_blocks: as attn_bwd with a block-sparse mask."""
     m, B, Hm = _mask_blocks(blocks, q.shape[2], k.shape[2])
     return _bwd(library().fm_attn_bwd_blocks, q, k, v, o, lse, dout, m, (blocks,),
-                (B, Hm, k.shape[2]), scale, ws, grads, stream, events)
+                (B, Hm, k.shape[2]), scale, ws, grads, stream, events, schedule=schedule)
 
 
 def attn_bwd(q, k, v, o, lse, dout, lts, lte, uts, ute, scale=None, ws=None, grads=None,
-             stream=None, events=None, key_order=KEYS_NATURAL):
+             stream=None, events=None, key_order=KEYS_NATURAL, schedule=SCHEDULE_LPT):
     """(dQ, dK, dV) in bf16 via fm_attn_bwd.  `events`: optional (start, stop, start2,
     stop2) torch.cuda.Event objects timing the dK/dV kernel and the dQ kernel.
     `key_order`: as for attn_fwd; dK and dV come back in the caller's key order."""
     return _bwd(library().fm_attn_bwd, q, k, v, o, lse, dout, _mask(lts, lte, uts, ute),
                 (lts, lte, uts, ute), _mask_dims(lts), scale, ws, grads, stream, events,
-                key_order)
+                key_order, schedule)
 
 
 def attn_bwd_multi(q, k, v, o, lse, dout, starts, ends, scale=None, ws=None, grads=None,
-                   stream=None, events=None):
+                   stream=None, events=None, schedule=SCHEDULE_LPT):
     """fm_attn_bwd_multi: as attn_bwd with the multi-interval mask."""
     m, B, Hm, M, Nk = _mask_multi(starts, ends)
     return _bwd(library().fm_attn_bwd_multi, q, k, v, o, lse, dout, m, (starts, ends),
-                (B, Hm, Nk), scale, ws, grads, stream, events)
+                (B, Hm, Nk), scale, ws, grads, stream, events, schedule=schedule)
 
 
 def _expand(fn, m, mask_ts, B, Hm, N, b, row0, row1, stream, seqlen_q, dev):

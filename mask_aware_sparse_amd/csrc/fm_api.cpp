@@ -35,6 +35,8 @@ fm_status check_problem(const fm_problem* p) {
   if (!fm::head_map_valid(p->heads_q, p->heads_kv, hm_of(p))) return FM_ERR_INVALID_ARG;
   if (!(p->softmax_scale <= 0.f || std::isfinite(p->softmax_scale))) return FM_ERR_INVALID_ARG;
   if (p->key_order != FM_KEYS_NATURAL && p->key_order != FM_KEYS_SORTED) return FM_ERR_INVALID_ARG;
+  if (p->schedule != FM_SCHEDULE_LPT && p->schedule != FM_SCHEDULE_NATURAL)
+    return FM_ERR_INVALID_ARG;
   if (!fm::head_dim_supported(p->head_dim)) return FM_ERR_UNSUPPORTED;
   // per-head buffers < 2 GiB
   if (nq_of(p) > (1 << 22) || nk_of(p) > (1 << 22)) return FM_ERR_UNSUPPORTED;
@@ -69,6 +71,14 @@ fm_status check_mask(const fm_problem* p, const fm_mask_blocks* m) {
   if (mask_rows(p) * ((nq_of(p) + nb - 1) / nb) * ((nk_of(p) + nb - 1) / nb) == 0) return FM_OK;
   if (!m->blocks) return FM_ERR_INVALID_ARG;
   return FM_OK;
+}
+
+// The dispatch order of the attention kernels' work items: cost-descending (LPT, the sort)
+// or index order (FM_SCHEDULE_NATURAL, for measuring what the LPT order buys).
+hipError_t dispatch_order(const fm_problem* p, const int32_t* cost, int32_t* order, int count,
+                          void* scratch, hipStream_t s) {
+  if (p->schedule == FM_SCHEDULE_NATURAL) return fm::launch_iota_i32(order, count, s);
+  return fm::launch_lpt_sort(cost, order, count, scratch, s);
 }
 
 // The key-order option: four-vector masks only, and each kv head in one mask set.
@@ -424,7 +434,7 @@ fm_status fwd_impl(const fm_problem* p, const void* q, const void* k, const void
     e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kFwdBlockQ, fm::kFwdBlockK, t, s);
   int32_t* order = at<int32_t>(ws, w.q_order);
   if (e == hipSuccess)
-    e = fm::launch_lpt_sort(t.q_cost, order, (int)(R * nb.nQB), at<char>(ws, w.sort), s);
+    e = dispatch_order(p, t.q_cost, order, (int)(R * nb.nQB), at<char>(ws, w.sort), s);
   if (e == hipSuccess && ma.n == fm::kBlocksMode)
     e = fm::launch_zero_i32(at<int32_t>(ws, w.zeros), (size_t)R * nk_of(p), s);
   if (e == hipSuccess) {
@@ -492,10 +502,10 @@ fm_status bwd_impl(const fm_problem* p, const void* q, const void* k, const void
   if (e == hipSuccess)
     e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kBwdBlockQ, bwd_bk(p), tk, s);
   void* scr = at<char>(ws, w.sort);
-  if (e == hipSuccess) e = fm::launch_lpt_sort(tk.k_cost, k_order, (int)(R * nk.nKB), scr, s);
+  if (e == hipSuccess) e = dispatch_order(p, tk.k_cost, k_order, (int)(R * nk.nKB), scr, s);
   if (e == hipSuccess)
     e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kFwdBlockQ, fm::kFwdBlockK, tq, s);
-  if (e == hipSuccess) e = fm::launch_lpt_sort(tq.q_cost, q_order, (int)(R * nq.nQB), scr, s);
+  if (e == hipSuccess) e = dispatch_order(p, tq.q_cost, q_order, (int)(R * nq.nQB), scr, s);
   if (e == hipSuccess && ma.n == fm::kBlocksMode)
     e = fm::launch_zero_i32(at<int32_t>(ws, w.zeros), (size_t)R * nk_of(p), s);
   if (e == hipSuccess) {

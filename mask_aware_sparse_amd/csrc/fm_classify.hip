@@ -391,6 +391,17 @@ hipError_t launch_zero_i32(int32_t* p, size_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void k_iota_i32(int32_t* __restrict__ p, int n) {
+  for (int i = (int)(blockIdx.x * 256 + threadIdx.x); i < n; i += (int)(gridDim.x * 256)) p[i] = i;
+}
+
+hipError_t launch_iota_i32(int32_t* p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(k_iota_i32, dim3(blocks < 4096 ? blocks : 4096), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 size_t lpt_sort_scratch_bytes(int64_t count) {
   return count > kMaxSortItems ? 2 * (size_t)count * sizeof(unsigned long long) : 0;
 }

@@ -124,6 +124,8 @@ struct TileOut {
 hipError_t launch_classify(const MaskArgs& m, int B, int Nq, int Nk, int bq, int bk,
                            const TileOut& out, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* p, size_t n, hipStream_t s);
+// order[i] = i for i < n: the natural dispatch order (fm_problem.schedule)
+hipError_t launch_iota_i32(int32_t* p, int n, hipStream_t s);
 size_t lpt_sort_scratch_bytes(int64_t count);
 hipError_t launch_lpt_sort(const int32_t* cost, int32_t* order, int count, void* scratch,
                            hipStream_t s);

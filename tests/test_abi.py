@@ -436,3 +436,16 @@ def test_workspace_bytes_matches_workspace_size():
     assert lib.fm_workspace_bytes(ctypes.byref(prob(Hq=3, Hkv=2)), 1, 0, 0) == 0
     assert lib.fm_workspace_bytes(ctypes.byref(prob()), 0, 48, 64) == 0
     assert lib.fm_workspace_bytes(None, 1, 0, 0) == 0
+
+
+def test_schedule_values_checked():
+    """fm_problem.schedule: FM_SCHEDULE_LPT (0) or FM_SCHEDULE_NATURAL (1); others rejected
+    before anything is launched."""
+    for bad in (2, -1):
+        p = fm.Problem(1, 4, 2, 256, 128, 0.0, 0, 0, 0, bad)
+        assert fwd(p) == INVALID
+        assert bwd(p) == INVALID
+    n = ctypes.c_size_t()
+    ok = fm.Problem(1, 4, 2, 256, 128, 0.0, 0, 0, 0, fm.SCHEDULE_NATURAL)
+    assert fm.library().fm_workspace_size(ctypes.byref(ok), fm.OP_FWD, 0, 0, ctypes.byref(n)) == 0
+    assert n.value == fm.workspace_size(1, 4, 2, 256, fm.OP_FWD)

@@ -124,3 +124,26 @@ def test_partial_path_with_nothing_hidden_is_bit_identical():
         outs.append((O, LSE, dq, dk, dv))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["prefix_lm_doc_1k_gqa", "random_intervals_520_g6",
+                                  "sliding_window_2k"])
+def test_natural_schedule_same_outputs(name):
+    """Index-order dispatch (fm_problem.schedule = natural) against the LPT order: O, LSE and
+    dQ bit for bit (each row is written by one workgroup whatever the order); dK/dV up to the
+    fp32 summation order (the split plan grants its extra segments in dispatch order, and
+    atomic sums follow it)."""
+    import mask_aware_sparse_amd as fm
+    w = SMALL[name]()
+    log(f"natural vs LPT schedule {name}")
+    q, k, v, do, vec = gpu_inputs(w)
+    outs = []
+    for sched in (fm.SCHEDULE_LPT, fm.SCHEDULE_NATURAL):
+        O, LSE = fm.attn_fwd(q, k, v, *vec, schedule=sched)
+        dq, dk, dv = fm.attn_bwd(q, k, v, O, LSE, do, *vec, schedule=sched)
+        torch.cuda.synchronize()
+        outs.append((O, LSE, dq, dk, dv))
+    (O1, L1, dq1, dk1, dv1), (O2, L2, dq2, dk2, dv2) = outs
+    assert torch.equal(O1, O2) and torch.equal(L1, L2) and torch.equal(dq1, dq2)
+    for a, b in ((dk1, dk2), (dv1, dv2)):
+        assert ((a.float() - b.float()).norm() / b.float().norm()) < 1e-2
