@@ -448,7 +448,32 @@ __global__ __launch_bounds__(64 * kW, (D > 128 || kW > 4) ? 1 : 2) void k_attn_b
     const bool has_next = st + 1 < nsteps;
     if (has_next) load_step(hi, it);
 
-    {
+    // Hidden-row word of this lane's key over the step's 32 rows (partial steps only).
+    auto mask_word = [&]() {
+      const int r0 = qb * BQ;
+      uint32_t w;
+      if constexpr (!kMulti) {
+        const int4 mv = sm.mv[0][wave * 32 + l32];
+        w = hidden_rows32(mv.x, mv.y, mv.z, mv.w, r0);
+      } else {
+        w = hidden_rows32_multi(sm.mv[0][wave * 32 + l32], sm.mv[1][wave * 32 + l32], r0);
+      }
+      return key_ok ? w : 0xFFFFFFFFu;
+    };
+    // At D <= 128 a wave whose 32 keys are hidden from all 32 rows of a partial step adds
+    // nothing to dK/dV there and skips the step's products and softmax gradient, leaving
+    // the cycles to the other wave on its SIMD.  (At D = 256 the word is formed inside the
+    // softmax gradient: kept live across the larger products it would spill.)
+    constexpr bool kSkipDead = D <= 128;
+    uint32_t word = 0u;
+    bool live = true;
+    if constexpr (kSkipDead) {
+      if (partial) {
+        word = mask_word();
+        live = __builtin_amdgcn_ballot_w64(word != 0xFFFFFFFFu) != 0;
+      }
+    }
+    if (live) {
       constexpr int qblk = 0;
       // ---- S = Q K^T and dP = dO V^T for 32 query rows x this wave's 32 keys.  Step s
       // reads its K, Q and dO fragments one step ahead; the scheduling barriers keep the
@@ -477,17 +502,7 @@ __global__ __launch_bounds__(64 * kW, (D > 128 || kW > 4) ? 1 : 2) void k_attn_b
       bf16x8 pa[2], sa[2];
       auto softmax_grad = [&](auto masked) {
         constexpr bool kMasked = decltype(masked)::value;
-        uint32_t word = 0u;
-        if (kMasked) {
-          const int r0 = qb * BQ + qblk * 32;
-          if constexpr (!kMulti) {
-            const int4 mv = sm.mv[0][wave * 32 + l32];
-            word = hidden_rows32(mv.x, mv.y, mv.z, mv.w, r0);
-          } else {
-            word = hidden_rows32_multi(sm.mv[0][wave * 32 + l32], sm.mv[1][wave * 32 + l32], r0);
-          }
-          word = key_ok ? word : 0xFFFFFFFFu;
-        }
+        if constexpr (kMasked && !kSkipDead) word = mask_word();
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int q0 = qblk * 32 + j * 16 + hh * 8;
