@@ -69,18 +69,16 @@ def encode_causal(n):
 
 
 def encode_packed(lengths, causal=True):
-    """Packed documents (same section): for key j in document [s_k, e_k]
-    FMS_j = j (causal) or s_k (bidirectional), FME_j = e_k."""
-    n = int(sum(lengths))
-    fms = np.zeros(n, dtype=np.int64)
-    fme = np.zeros(n, dtype=np.int64)
-    s = 0
-    for length in lengths:
-        e = s + length - 1
-        for j in range(s, e + 1):
-            fms[j] = j if causal else s
-            fme[j] = e
-        s = e + 1
+    """Packed documents (FlashMask Guide, "Mathematical Formalization of Column-Wise
+    Sparsity", the document closed form): a key j inside document k, which spans rows
+    [s_k, e_k] (inclusive), is visible from FMS_j = j (causal) or s_k (bidirectional) down
+    to FME_j = e_k.  Each document's start and last row are repeated over its keys."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    ends = np.cumsum(lengths)                       # one past each document's last row
+    starts = ends - lengths
+    doc_start = np.repeat(starts, lengths)          # s_k of the document holding key j
+    fme = np.repeat(ends - 1, lengths)              # e_k
+    fms = np.arange(int(ends[-1]) if len(ends) else 0, dtype=np.int64) if causal else doc_start
     return fms, fme
 
 
