@@ -46,8 +46,9 @@
  *  - Rows that see no key get O = 0, LSE = -inf, dQ = 0 and add nothing to dK/dV.
  *  - Errors.  Arguments are validated on the host before anything is enqueued; on an
  *    error nothing is launched and the outputs are untouched.  Vector values outside
- *    [0, N_q] are not checked and give unspecified (but memory-safe) results.  No C++
- *    exception crosses this interface.
+ *    [0, N_q] are not checked by the attention calls and give unspecified (but memory-safe)
+ *    results; fm_check_mask counts them on the device.  No C++ exception crosses this
+ *    interface.
  */
 #ifndef FM_H
 #define FM_H
@@ -356,6 +357,19 @@ fm_status fm_attn_bwd_blocks(const fm_problem* p, const void* q, const void* k, 
                              size_t ws_bytes, void* stream, const fm_kernel_events* events);
 fm_status fm_debug_expand_mask_blocks(const fm_problem* p, const fm_mask_blocks* m, int32_t b,
                                       int32_t row0, int32_t row1, uint8_t* dense, void* stream);
+
+/* Range check of the mask (a debugging aid; the attention entry points do not check values).
+ * Writes to *bad (device int32, cleared first) the number of row bounds outside [0, N_q]:
+ * over the four vectors, or over the interval starts and ends of the multi-interval form
+ * (R * n_intervals * N_k each).  Asynchronous on `stream`, no host synchronization and no
+ * allocation; read *bad after the stream has reached it.  A nonzero count means the
+ * attention results for that mask are unspecified (though memory-safe).  p->seqlen (N_q),
+ * seqlen_kv, batch and mask_heads are used.  FM_ERR_INVALID_ARG for null pointers (the
+ * arrays may be null only for an empty mask) and, for the multi form, n_intervals outside
+ * 1..4. */
+fm_status fm_check_mask(const fm_problem* p, const fm_mask* m, int32_t* bad, void* stream);
+fm_status fm_check_mask_multi(const fm_problem* p, const fm_mask_multi* m, int32_t* bad,
+                              void* stream);
 
 /* Static description of a status code. */
 const char* fm_status_string(fm_status s);

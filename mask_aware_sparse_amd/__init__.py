@@ -24,7 +24,8 @@ __all__ = [
     "attn_fwd", "attn_bwd", "debug_expand_mask", "status_string",
     "fm_tile_shape", "fm_workspace_size", "fm_classify_tiles", "fm_attn_fwd", "fm_attn_bwd",
     "fm_debug_expand_mask", "fm_status_string", "attn_fwd_static", "fm_attn_fwd_static",
-    "STATIC_WORKSPACE_BYTES",
+    "STATIC_WORKSPACE_BYTES", "check_mask", "check_mask_multi", "fm_check_mask",
+    "fm_check_mask_multi",
     "OP_CLASSIFY", "OP_FWD", "OP_BWD", "HEAD_DIM", "key_order", "fm_key_order",
     "KEYS_NATURAL", "KEYS_SORTED", "KEY_ORDER_SPAN", "KEY_ORDER_GROUP", "SCHEDULE_LPT",
     "SCHEDULE_NATURAL",
@@ -125,6 +126,8 @@ def library():
             "fm_localize_mask": ([PP, PM, _P, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.POINTER(MaskOut), _P], _STATUS),
             "fm_key_order": ([PP, PM, _P, ctypes.POINTER(MaskOut), _P], _STATUS),
+            "fm_check_mask": ([PP, PM, _P, _P], _STATUS),
+            "fm_check_mask_multi": ([PP, PX, _P, _P], _STATUS),
             "fm_classify_tiles_multi": ([PP, PX, ctypes.c_int32, ctypes.c_int32, PT, _P,
                                          ctypes.c_size_t, _P], _STATUS),
             "fm_attn_fwd_multi": ([PP, _P, _P, _P, PX, _P, _P, _P, ctypes.c_size_t, _P, PE],
@@ -669,6 +672,36 @@ def key_order(lts, lte, uts, ute, seqlen_q=None, permuted=False, stream=None):
     return (perm, out) if permuted else perm
 
 
+def check_mask(lts, lte, uts, ute, seqlen_q=None, out=None, stream=None, sync=True):
+    """fm_check_mask: the number of row bounds outside [0, N_q] (seqlen_q, default N_k).  With
+    sync=False the device int32 tensor `out` (allocated if None) is returned unread."""
+    B, Hm, N = _mask_dims(lts)
+    m = _mask(lts, lte, uts, ute)
+    if out is not None:
+        _expect(out, "out", (1,), torch.int32)
+    _on_device(lts.device, [("lte", lte), ("uts", uts), ("ute", ute), ("out", out)])
+    bad = torch.empty(1, dtype=torch.int32, device=lts.device) if out is None else out
+    p = _problem(B, 1, 1, N if seqlen_q is None else int(seqlen_q), seqlen_kv=N, mask_heads=Hm)
+    _check(library().fm_check_mask(ctypes.byref(p), ctypes.byref(m), _ptr(bad),
+                                   _stream(lts.device, stream)), "fm_check_mask")
+    _keep_alive(stream, lts.device, bad if out is None else None)
+    return int(bad.item()) if sync else bad
+
+
+def check_mask_multi(starts, ends, seqlen_q=None, out=None, stream=None, sync=True):
+    """fm_check_mask_multi: as check_mask over the interval starts and ends."""
+    m, B, Hm, M, N = _mask_multi(starts, ends)
+    if out is not None:
+        _expect(out, "out", (1,), torch.int32)
+    _on_device(starts.device, [("ends", ends), ("out", out)])
+    bad = torch.empty(1, dtype=torch.int32, device=starts.device) if out is None else out
+    p = _problem(B, 1, 1, N if seqlen_q is None else int(seqlen_q), seqlen_kv=N, mask_heads=Hm)
+    _check(library().fm_check_mask_multi(ctypes.byref(p), ctypes.byref(m), _ptr(bad),
+                                         _stream(starts.device, stream)), "fm_check_mask_multi")
+    _keep_alive(stream, starts.device, bad if out is None else None)
+    return int(bad.item()) if sync else bad
+
+
 def localize_mask_multi(starts, ends, offsets, chunk_len, out=None, stream=None):
     """fm_localize_mask_multi: every interval start and end renumbered into the rank's rows.
     Returns (starts, ends) of the input's shape."""
@@ -703,6 +736,8 @@ fm_attn_bwd = attn_bwd
 fm_debug_expand_mask = debug_expand_mask
 fm_localize_mask = localize_mask
 fm_key_order = key_order
+fm_check_mask = check_mask
+fm_check_mask_multi = check_mask_multi
 fm_classify_tiles_multi = classify_tiles_multi
 fm_attn_fwd_multi = attn_fwd_multi
 fm_attn_bwd_multi = attn_bwd_multi

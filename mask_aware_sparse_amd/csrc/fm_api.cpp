@@ -665,6 +665,29 @@ fm_status fm_localize_mask(const fm_problem* p, const fm_mask* global, const int
       static_cast<hipStream_t>(stream)));
 }
 
+fm_status fm_check_mask(const fm_problem* p, const fm_mask* m, int32_t* bad, void* stream) {
+  if (!p || !m || !bad) return FM_ERR_INVALID_ARG;
+  if (p->batch < 0 || p->seqlen < 0 || p->seqlen_kv < 0 || p->mask_heads < 0)
+    return FM_ERR_INVALID_ARG;
+  const int64_t cols = mask_rows(p) * nk_of(p);
+  if (cols > 0 && (!m->lts || !m->lte || !m->uts || !m->ute)) return FM_ERR_INVALID_ARG;
+  return hip_status(fm::launch_check_bounds(MaskPtrs{m->lts, m->lte, m->uts, m->ute}, 4, cols,
+                                            nq_of(p), bad, static_cast<hipStream_t>(stream)));
+}
+
+fm_status fm_check_mask_multi(const fm_problem* p, const fm_mask_multi* m, int32_t* bad,
+                              void* stream) {
+  if (!p || !m || !bad) return FM_ERR_INVALID_ARG;
+  if (p->batch < 0 || p->seqlen < 0 || p->seqlen_kv < 0 || p->mask_heads < 0)
+    return FM_ERR_INVALID_ARG;
+  if (m->n_intervals < 1 || m->n_intervals > fm::kMaxIntervals) return FM_ERR_INVALID_ARG;
+  const int64_t cols = mask_rows(p) * m->n_intervals * nk_of(p);
+  if (cols > 0 && (!m->start || !m->end)) return FM_ERR_INVALID_ARG;
+  return hip_status(fm::launch_check_bounds(MaskPtrs{m->start, m->end, nullptr, nullptr}, 2,
+                                            cols, nq_of(p), bad,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 fm_status fm_key_order(const fm_problem* p, const fm_mask* m, int32_t* perm,
                        const fm_mask_out* permuted, void* stream) {
   if (!p || !m) return FM_ERR_INVALID_ARG;

@@ -480,4 +480,40 @@ hipError_t launch_localize(const MaskPtrs& g, int arrays, const int32_t* offsets
   return hipGetLastError();
 }
 
+// ---- Range check of the row bounds ----
+// Counts the values of `arrays` int32 arrays of `cols` entries each that lie outside
+// [0, hi]; one global atomic per workgroup.  `bad` must start at zero (the launcher clears
+// it with a fill kernel first).
+__global__ __launch_bounds__(256) void k_check_bounds(MaskPtrs g, int arrays, int64_t cols,
+                                                      int hi, int32_t* __restrict__ bad) {
+  __shared__ int count;
+  if (threadIdx.x == 0) count = 0;
+  __syncthreads();
+  int mine = 0;
+  const int32_t* a[4] = {g.lts, g.lte, g.uts, g.ute};
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < cols;
+       c += (int64_t)gridDim.x * 256) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      if (x < arrays) {
+        const int v = a[x][c];
+        mine += (v < 0 || v > hi) ? 1 : 0;
+      }
+    }
+  }
+  if (mine) atomicAdd(&count, mine);
+  __syncthreads();
+  if (threadIdx.x == 0 && count) atomicAdd(bad, count);
+}
+
+hipError_t launch_check_bounds(const MaskPtrs& g, int arrays, int64_t cols, int hi, int32_t* bad,
+                               hipStream_t s) {
+  hipError_t e = launch_zero_i32(bad, 1, s);
+  if (e != hipSuccess || cols <= 0) return e;
+  const int64_t blocks = (cols + 255) / 256;
+  const unsigned grid = (unsigned)(blocks < 2048 ? blocks : 2048);
+  hipLaunchKernelGGL(k_check_bounds, dim3(grid), dim3(256), 0, s, g, arrays, cols, hi, bad);
+  return hipGetLastError();
+}
+
 }  // namespace fm

@@ -140,6 +140,9 @@ struct MaskOut {
 };
 // Renumber `cols` row bounds of each of the first `arrays` (2 or 4) arrays of g into the
 // rank's rows.
+// Number of values of `arrays` (2 or 4) arrays of `cols` int32 outside [0, hi] into *bad.
+hipError_t launch_check_bounds(const MaskPtrs& g, int arrays, int64_t cols, int hi, int32_t* bad,
+                               hipStream_t s);
 hipError_t launch_localize(const MaskPtrs& g, int arrays, const int32_t* offsets, int n_chunks,
                            int chunk_len, const MaskOut& out, int64_t cols, hipStream_t s);
 

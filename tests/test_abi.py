@@ -449,3 +449,19 @@ def test_schedule_values_checked():
     ok = fm.Problem(1, 4, 2, 256, 128, 0.0, 0, 0, 0, fm.SCHEDULE_NATURAL)
     assert fm.library().fm_workspace_size(ctypes.byref(ok), fm.OP_FWD, 0, 0, ctypes.byref(n)) == 0
     assert n.value == fm.workspace_size(1, 4, 2, 256, fm.OP_FWD)
+
+
+def test_check_mask_argument_checks():
+    """fm_check_mask / _multi: null problem, mask or count, and a bad interval count, are
+    rejected before anything is launched."""
+    lib = fm.library()
+    p = prob()
+    m = fake_mask()
+    assert lib.fm_check_mask(None, ctypes.byref(m), FAKE, None) == INVALID
+    assert lib.fm_check_mask(ctypes.byref(p), None, FAKE, None) == INVALID
+    assert lib.fm_check_mask(ctypes.byref(p), ctypes.byref(m), None, None) == INVALID
+    nulls = fm.Mask(0, 0x100000, 0x100000, 0x100000)
+    assert lib.fm_check_mask(ctypes.byref(p), ctypes.byref(nulls), FAKE, None) == INVALID
+    for n in (0, 5):
+        mm = fm.MaskMulti(0x100000, 0x100000, n)
+        assert lib.fm_check_mask_multi(ctypes.byref(p), ctypes.byref(mm), FAKE, None) == INVALID
