@@ -280,6 +280,26 @@ __global__ __launch_bounds__(1024) void k_lpt_sort(const int32_t* __restrict__ c
   }
 }
 
+// Short lists (count <= kRankSortItems, one key per thread): the keys are unique, so each
+// key's place in the sorted order is the number of keys below it, counted against all of
+// them in LDS after one barrier.  The same order as the bitonic network, without its
+// log^2 barrier-separated stages (the lists of problems up to 131072 rows at the
+// attention kernels' tiles are at most 1024 long per batch row).
+constexpr int kRankSortItems = 1024;
+__global__ __launch_bounds__(1024) void k_lpt_rank(const int32_t* __restrict__ cost,
+                                                   int32_t* __restrict__ order, int count) {
+  __shared__ unsigned long long keys[kRankSortItems];
+  const int tid = threadIdx.x;
+  const unsigned long long mine = tid < count ? lpt_key(cost, tid) : ~0ull;
+  keys[tid] = mine;
+  __syncthreads();
+  if (tid < count) {
+    int rank = 0;
+    for (int i = 0; i < count; ++i) rank += keys[i] < mine ? 1 : 0;
+    order[rank] = tid;
+  }
+}
+
 // Number of keys in sorted a[0, n) below x.
 __device__ __forceinline__ int rank_below(const unsigned long long* __restrict__ a, int n,
                                           unsigned long long x) {
@@ -409,6 +429,10 @@ size_t lpt_sort_scratch_bytes(int64_t count) {
 hipError_t launch_lpt_sort(const int32_t* cost, int32_t* order, int count, void* scratch,
                            hipStream_t s) {
   if (count <= 0) return hipSuccess;
+  if (count <= kRankSortItems) {
+    hipLaunchKernelGGL(k_lpt_rank, dim3(1), dim3(1024), 0, s, cost, order, count);
+    return hipGetLastError();
+  }
   if (count <= kMaxSortItems) {
     hipLaunchKernelGGL(k_lpt_sort, dim3(1), dim3(1024), 0, s, cost, order,
                        (unsigned long long*)nullptr, count);
