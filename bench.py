@@ -616,6 +616,8 @@ def main():
                     help="run only a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--classify-bandwidth", action="store_true",
                     help="time fm_classify_tiles on replicated c5 vectors (HBM roofline)")
+    ap.add_argument("--classify-batch", type=int, default=4,
+                    help="batch rows of the replicated c5 vectors for --classify-bandwidth")
     ap.add_argument("--cp", type=int, default=0, metavar="P",
                     help="emulate context parallelism over P ranks (query shares in turn)")
     ap.add_argument("--ipo-table", action="store_true",
@@ -646,7 +648,7 @@ def main():
         cp_emulation(args.workload, args.cp, min(args.steps, 3), min(args.warmup, 1))
         return
     if args.classify_bandwidth:
-        classify_bandwidth(args.steps, args.warmup)
+        classify_bandwidth(args.steps, args.warmup, batch=args.classify_batch)
         return
 
     import torch

@@ -5,7 +5,8 @@
 // Index Generator emits per Q-block a queue of the KV blocks to visit (right to left),
 // each tagged partial or unmasked.  §3.3: a tile costs 0, alpha_p or alpha_u; work is
 // balanced by those costs.  Here the queues are built by one HBM pass over the
-// vectors plus one pass per queue row; the LPT order is a bitonic sort in LDS.
+// vectors plus one pass per queue row; the LPT order is a rank sort in LDS (merged
+// across workgroups for long lists).
 #include "fm_device.h"
 #include "fm_internal.h"
 
@@ -14,36 +15,66 @@
 namespace fm {
 
 // ---- A2: block min/max of the four vectors -------------------------------------
-// One wave per (b, kb); lane l reduces columns kb*bk + l + 64t.
-__global__ __launch_bounds__(64) void k_block_minmax(MaskPtrs m, int Nk, int nKB, int bk,
-                                                     int32_t* __restrict__ mm) {
-  const int bkb = blockIdx.x;
-  const int b = bkb / nKB, kb = bkb - b * nKB;
-  const int lane = threadIdx.x;
-  const size_t rowoff = (size_t)b * Nk;
-  const int c0 = kb * bk, c1 = min(c0 + bk, Nk);
-  int v[8] = {INT_MAX, INT_MIN, INT_MAX, INT_MIN, INT_MAX, INT_MIN, INT_MAX, INT_MIN};
-  for (int c = c0 + lane; c < c1; c += 64) {
-    int x0 = m.lts[rowoff + c], x1 = m.lte[rowoff + c];
-    int x2 = m.uts[rowoff + c], x3 = m.ute[rowoff + c];
-    v[0] = min(v[0], x0); v[1] = max(v[1], x0);
-    v[2] = min(v[2], x1); v[3] = max(v[3], x1);
-    v[4] = min(v[4], x2); v[5] = max(v[5], x2);
-    v[6] = min(v[6], x3); v[7] = max(v[7], x3);
-  }
+// A wave takes 256 columns of one mask row at a time (four waves per workgroup striding
+// over all of them): lane l loads columns 4l .. 4l + 3 of each vector, sixteen independent
+// loads in flight, and the bk / 4 lanes of each KV block reduce among themselves.
+__global__ __launch_bounds__(256) void k_block_minmax(MaskPtrs m, int Nk, int nKB, int bk,
+                                                      int n_sc, int total,
+                                                      int32_t* __restrict__ mm) {
+  const int lane = threadIdx.x & 63;
+  const int G = bk >> 2;  // lanes per KV block (2 .. 64)
+  // 16-byte loads where every row starts on a 16-byte boundary
+  const bool vec4 = (Nk & 3) == 0 &&
+                    ((reinterpret_cast<uintptr_t>(m.lts) | reinterpret_cast<uintptr_t>(m.lte) |
+                      reinterpret_cast<uintptr_t>(m.uts) | reinterpret_cast<uintptr_t>(m.ute)) &
+                     15) == 0;
+  for (int sc = blockIdx.x * 4 + (threadIdx.x >> 6); sc < total; sc += gridDim.x * 4) {
+    const int b = sc / n_sc, c0 = (sc - b * n_sc) * 256 + 4 * lane;
+    const size_t rowoff = (size_t)b * Nk;
+    int x[4][4];
+    if (vec4 && c0 + 3 < Nk) {
+      // whole aligned quad: one 16-byte load per vector
+      const int32_t* src[4] = {m.lts, m.lte, m.uts, m.ute};
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
+      for (int t = 0; t < 4; ++t) {
+        const int4 q = *reinterpret_cast<const int4*>(src[t] + rowoff + c0);
+        x[t][0] = q.x; x[t][1] = q.y; x[t][2] = q.z; x[t][3] = q.w;
+      }
+    } else {
 #pragma unroll
-    for (int t = 0; t < 8; t += 2) {
-      v[t] = min(v[t], __shfl_xor(v[t], off));
-      v[t + 1] = max(v[t + 1], __shfl_xor(v[t + 1], off));
+      for (int j = 0; j < 4; ++j) {
+        const bool in = c0 + j < Nk;
+        const size_t o = rowoff + (in ? c0 + j : 0);
+        x[0][j] = in ? m.lts[o] : INT_MAX;
+        x[1][j] = in ? m.lte[o] : INT_MAX;
+        x[2][j] = in ? m.uts[o] : INT_MAX;
+        x[3][j] = in ? m.ute[o] : INT_MAX;
+      }
     }
-  }
-  if (lane < 8) {
-    int out = v[0];
+    int v[8];
 #pragma unroll
-    for (int t = 1; t < 8; ++t) out = (lane == t) ? v[t] : out;
-    mm[(size_t)bkb * 8 + lane] = out;
+    for (int t = 0; t < 4; ++t) {
+      int lo = INT_MAX, hi = INT_MIN;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (c0 + j < Nk) { lo = min(lo, x[t][j]); hi = max(hi, x[t][j]); }
+      }
+      v[2 * t] = lo;
+      v[2 * t + 1] = hi;
+    }
+    for (int off = 1; off < G; off <<= 1) {
+#pragma unroll
+      for (int t = 0; t < 8; t += 2) {
+        v[t] = min(v[t], __shfl_xor(v[t], off));
+        v[t + 1] = max(v[t + 1], __shfl_xor(v[t + 1], off));
+      }
+    }
+    const int kb = c0 / bk;
+    if ((lane & (G - 1)) == 0 && kb < nKB) {
+      int32_t* dst = mm + ((size_t)b * nKB + kb) * 8;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) dst[t] = v[t];
+    }
   }
 }
 
@@ -162,42 +193,75 @@ __device__ __forceinline__ ScanResult block_scan_256(bool flag, bool sub, int* s
 }
 
 // ---- A3: classes and per-Q-block queues (KV blocks right to left) --------------
-template <int kMode>
+// One workgroup per kR consecutive Q-blocks of one mask row: each chunk of 256 KV blocks
+// has its bounds loaded once and classified against the kR Q-blocks, and one exclusive
+// scan over the workgroup (two barriers) places the queued tiles of all kR rows.  kR > 1
+// only for long lists (many mask rows), where reading every KV block's bounds once per
+// Q-block made the kernel bound by L2 reads.
+template <int kMode, int kR>
 __global__ __launch_bounds__(256) void k_classify_q(const int32_t* __restrict__ mm, int n,
                                                     GridArgs ga, int Nq, int nQB, int nKB, int bq,
-                                                    uint8_t* __restrict__ cls,
+                                                    int groups, uint8_t* __restrict__ cls,
                                                     int32_t* __restrict__ q_queue,
                                                     int32_t* __restrict__ q_count,
                                                     int32_t* __restrict__ q_cost) {
-  __shared__ int sh_cnt[4], sh_sub[4];
-  const int row = blockIdx.x;  // b * nQB + qb
-  const int b = row / nQB, qb = row - b * nQB;
-  const int q0 = qb * bq, q1 = min(q0 + bq, Nq);
-  const int tid = threadIdx.x;
-  int base = 0, np = 0;
+  __shared__ int sh_cnt[kR][4], sh_sub[kR][4];
+  const int b = blockIdx.x / groups, qb0 = (blockIdx.x - b * groups) * kR;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int base[kR], np[kR];
+#pragma unroll
+  for (int r = 0; r < kR; ++r) { base[r] = 0; np[r] = 0; }
   for (int c0 = 0; c0 < nKB; c0 += 256) {
     const int idx = c0 + tid;
     const bool valid = idx < nKB;
     const int kb = nKB - 1 - idx;
-    int c = 0;
-    if (valid) {
-      BlockBounds<kMode> bb;
-      bb.load(mm, (size_t)b * nKB + kb, n, &ga);
-      c = bb.cls(q0, q1);
-      if (cls) cls[(size_t)row * nKB + kb] = (uint8_t)c;
+    BlockBounds<kMode> bb;
+    if (valid) bb.load(mm, (size_t)b * nKB + kb, n, &ga);
+    int c[kR];
+    unsigned long long bal[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int qb = qb0 + r;
+      c[r] = 0;
+      if (valid && qb < nQB) {
+        const int q0 = qb * bq;
+        c[r] = bb.cls(q0, min(q0 + bq, Nq));
+        if (cls) cls[((size_t)b * nQB + qb) * nKB + kb] = (uint8_t)c[r];
+      }
+      bal[r] = __ballot(c[r] != 0);
+      const unsigned long long bsub = __ballot(c[r] == 1);
+      if (lane == 0) { sh_cnt[r][w] = __popcll(bal[r]); sh_sub[r][w] = __popcll(bsub); }
     }
-    ScanResult s = block_scan_256(valid && c != 0, c == 1, sh_cnt, sh_sub);
-    if (q_queue && valid && c != 0)
-      q_queue[(size_t)row * nKB + base + s.off] = kb | (c == 1 ? (int)0x80000000 : 0);
-    base += s.total;
-    np += s.sub;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      int off = __popcll(bal[r] & ((1ull << lane) - 1ull)), total = 0, sub = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < w) off += sh_cnt[r][i];
+        total += sh_cnt[r][i];
+        sub += sh_sub[r][i];
+      }
+      if (q_queue && c[r] != 0)
+        q_queue[((size_t)b * nQB + qb0 + r) * nKB + base[r] + off] =
+            kb | (c[r] == 1 ? (int)0x80000000 : 0);
+      base[r] += total;
+      np[r] += sub;
+    }
+    __syncthreads();  // the counts are rewritten by the next chunk
   }
   if (q_queue) {
-    for (int p = base + tid; p < nKB; p += 256) q_queue[(size_t)row * nKB + p] = -1;
-    if (tid == 0) {
-      q_count[(size_t)row * 2] = np;
-      q_count[(size_t)row * 2 + 1] = base - np;
-      q_cost[row] = kAlphaPartial * np + kAlphaUnmasked * (base - np);
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int qb = qb0 + r;
+      if (qb >= nQB) break;
+      const size_t row = (size_t)b * nQB + qb;
+      for (int p = base[r] + tid; p < nKB; p += 256) q_queue[row * nKB + p] = -1;
+      if (tid == 0) {
+        q_count[row * 2] = np[r];
+        q_count[row * 2 + 1] = base[r] - np[r];
+        q_cost[row] = kAlphaPartial * np[r] + kAlphaUnmasked * (base[r] - np[r]);
+      }
     }
   }
 }
@@ -235,68 +299,37 @@ __global__ __launch_bounds__(256) void k_classify_k(const int32_t* __restrict__ 
 }
 
 // ---- A4: longest-processing-time-first order ----------------------------------
-// Keys (~cost << 32 | index) sorted ascending = cost descending, index ascending.  Up to
-// kMaxSortItems keys sort in one workgroup's LDS (bitonic network).  Longer lists are
-// sorted in chunks of kMaxSortItems (one workgroup each) and then merged pairwise, run
-// length doubling per pass: keys are unique (they contain the index), so an element's
-// place in the merged run is its place in its own run plus the number of keys below it in
-// the other run (a binary search), and every element is placed independently.
+// Keys (~cost << 32 | index) sorted ascending = cost descending, index ascending.  Lists of
+// up to kRankSortItems keys sort in one workgroup; longer lists are sorted in chunks of
+// that size (one workgroup each) and then merged pairwise, run length doubling per pass:
+// keys are unique (they contain the index), so an element's place in the merged run is its
+// place in its own run plus the number of keys below it in the other run (a binary
+// search), and every element is placed independently.
 __device__ __forceinline__ unsigned long long lpt_key(const int32_t* __restrict__ cost, int i) {
   return ((unsigned long long)(0xFFFFFFFFu - (unsigned)cost[i]) << 32) | (unsigned)i;
 }
 
-// Sorts keys [c0, c0 + n) (n <= kMaxSortItems) of chunk blockIdx.x; writes the item
-// indices to `order` (single chunk) or the sorted keys to `run` (chunks to be merged).
-__global__ __launch_bounds__(1024) void k_lpt_sort(const int32_t* __restrict__ cost,
+// One key per thread: the keys are unique, so each key's place in its chunk's sorted order
+// is the number of the chunk's keys below it, counted against all of them in LDS after one
+// barrier.  Chunk blockIdx.x holds keys [c0, c0 + n); a single chunk writes the item indices
+// to `order`, several write their sorted keys to `run` for merging.
+constexpr int kRankSortItems = 1024;
+__global__ __launch_bounds__(1024) void k_lpt_rank(const int32_t* __restrict__ cost,
                                                    int32_t* __restrict__ order,
                                                    unsigned long long* __restrict__ run,
                                                    int count) {
-  __shared__ unsigned long long keys[kMaxSortItems];
-  const int tid = threadIdx.x;
-  const int c0 = blockIdx.x * kMaxSortItems;
-  const int n = min(kMaxSortItems, count - c0);
-  int P = 1;
-  while (P < n) P <<= 1;
-  for (int i = tid; i < P; i += 1024) keys[i] = i < n ? lpt_key(cost, c0 + i) : ~0ull;
-  __syncthreads();
-  // bitonic network; each thread takes compare-exchange pairs (i, i + j) directly, so no
-  // lane idles on the half of the indices that are second members of a pair
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int q = tid; q < (P >> 1); q += 1024) {
-        const int i = ((q & ~(j - 1)) << 1) | (q & (j - 1));
-        const int ixj = i + j;
-        const unsigned long long a = keys[i], c = keys[ixj];
-        const bool up = (i & k) == 0;
-        if ((a > c) == up) { keys[i] = c; keys[ixj] = a; }
-      }
-      __syncthreads();
-    }
-  }
-  if (run) {
-    for (int i = tid; i < n; i += 1024) run[c0 + i] = keys[i];
-  } else {
-    for (int i = tid; i < n; i += 1024) order[i] = (int32_t)(keys[i] & 0xFFFFFFFFull);
-  }
-}
-
-// Short lists (count <= kRankSortItems, one key per thread): the keys are unique, so each
-// key's place in the sorted order is the number of keys below it, counted against all of
-// them in LDS after one barrier.  The same order as the bitonic network, without its
-// log^2 barrier-separated stages (the lists of problems up to 131072 rows at the
-// attention kernels' tiles are at most 1024 long per batch row).
-constexpr int kRankSortItems = 1024;
-__global__ __launch_bounds__(1024) void k_lpt_rank(const int32_t* __restrict__ cost,
-                                                   int32_t* __restrict__ order, int count) {
   __shared__ unsigned long long keys[kRankSortItems];
   const int tid = threadIdx.x;
-  const unsigned long long mine = tid < count ? lpt_key(cost, tid) : ~0ull;
+  const int c0 = blockIdx.x * kRankSortItems;
+  const int n = min(kRankSortItems, count - c0);
+  const unsigned long long mine = tid < n ? lpt_key(cost, c0 + tid) : ~0ull;
   keys[tid] = mine;
   __syncthreads();
-  if (tid < count) {
+  if (tid < n) {
     int rank = 0;
-    for (int i = 0; i < count; ++i) rank += keys[i] < mine ? 1 : 0;
-    order[rank] = tid;
+    for (int i = 0; i < n; ++i) rank += keys[i] < mine ? 1 : 0;
+    if (run) run[c0 + rank] = mine;
+    else order[rank] = tid;
   }
 }
 
@@ -380,15 +413,29 @@ hipError_t launch_classify(const MaskArgs& m, int B, int Nq, int Nk, int bq, int
     if (mode == 1)
       hipLaunchKernelGGL(k_block_minmax_multi, dim3(B * nKB), dim3(64), 0, s, m.start, m.end,
                          m.n, Nk, nKB, bk, out.minmax);
-    else if (mode == 0)
-      hipLaunchKernelGGL(k_block_minmax, dim3(B * nKB), dim3(64), 0, s, m.v, Nk, nKB, bk,
-                         out.minmax);
+    else if (mode == 0) {
+      const int n_sc = (Nk + 255) / 256, total = B * n_sc;
+      const int grid = min((total + 3) / 4, 2048);
+      hipLaunchKernelGGL(k_block_minmax, dim3(grid), dim3(256), 0, s, m.v, Nk, nKB, bk, n_sc,
+                         total, out.minmax);
+    }
   }
   // with no KV block a Q-block's queue is empty; with no Q-block a KV block's is
   if ((out.tile_class || out.q_queue) && nQB > 0) {
-    auto kq = mode == 2 ? k_classify_q<2> : (mode == 1 ? k_classify_q<1> : k_classify_q<0>);
-    hipLaunchKernelGGL(kq, dim3(B * nQB), dim3(256), 0, s, out.minmax, m.n, ga, Nq, nQB, nKB, bq,
-                       out.tile_class, out.q_queue, out.q_count, out.q_cost);
+    // rows per workgroup: 1 up to 4096 queue rows (every attention call at its own tile
+    // shapes), more for longer lists, keeping at least 2048 workgroups
+    const int64_t rows = (int64_t)B * nQB;
+    const int R = rows >= 16384 ? 8 : rows >= 8192 ? 4 : rows > 4096 ? 2 : 1;
+    const int groups = (nQB + R - 1) / R;
+    using KQ = void (*)(const int32_t*, int, GridArgs, int, int, int, int, int, uint8_t*,
+                        int32_t*, int32_t*, int32_t*);
+    KQ kq;
+    if (R == 8) kq = mode == 2 ? k_classify_q<2, 8> : (mode == 1 ? k_classify_q<1, 8> : k_classify_q<0, 8>);
+    else if (R == 4) kq = mode == 2 ? k_classify_q<2, 4> : (mode == 1 ? k_classify_q<1, 4> : k_classify_q<0, 4>);
+    else if (R == 2) kq = mode == 2 ? k_classify_q<2, 2> : (mode == 1 ? k_classify_q<1, 2> : k_classify_q<0, 2>);
+    else kq = mode == 2 ? k_classify_q<2, 1> : (mode == 1 ? k_classify_q<1, 1> : k_classify_q<0, 1>);
+    hipLaunchKernelGGL(kq, dim3(B * groups), dim3(256), 0, s, out.minmax, m.n, ga, Nq, nQB, nKB,
+                       bq, groups, out.tile_class, out.q_queue, out.q_count, out.q_cost);
   }
   if (out.k_queue && nKB > 0) {
     auto kk = mode == 2 ? k_classify_k<2> : (mode == 1 ? k_classify_k<1> : k_classify_k<0>);
@@ -423,28 +470,24 @@ hipError_t launch_iota_i32(int32_t* p, int n, hipStream_t s) {
 }
 
 size_t lpt_sort_scratch_bytes(int64_t count) {
-  return count > kMaxSortItems ? 2 * (size_t)count * sizeof(unsigned long long) : 0;
+  return count > kRankSortItems ? 2 * (size_t)count * sizeof(unsigned long long) : 0;
 }
 
 hipError_t launch_lpt_sort(const int32_t* cost, int32_t* order, int count, void* scratch,
                            hipStream_t s) {
   if (count <= 0) return hipSuccess;
   if (count <= kRankSortItems) {
-    hipLaunchKernelGGL(k_lpt_rank, dim3(1), dim3(1024), 0, s, cost, order, count);
-    return hipGetLastError();
-  }
-  if (count <= kMaxSortItems) {
-    hipLaunchKernelGGL(k_lpt_sort, dim3(1), dim3(1024), 0, s, cost, order,
+    hipLaunchKernelGGL(k_lpt_rank, dim3(1), dim3(kRankSortItems), 0, s, cost, order,
                        (unsigned long long*)nullptr, count);
     return hipGetLastError();
   }
   unsigned long long* a = static_cast<unsigned long long*>(scratch);
   unsigned long long* b = a + count;
-  const int chunks = (count + kMaxSortItems - 1) / kMaxSortItems;
-  hipLaunchKernelGGL(k_lpt_sort, dim3(chunks), dim3(1024), 0, s, cost, (int32_t*)nullptr, a,
-                     count);
+  const int chunks = (count + kRankSortItems - 1) / kRankSortItems;
+  hipLaunchKernelGGL(k_lpt_rank, dim3(chunks), dim3(kRankSortItems), 0, s, cost,
+                     (int32_t*)nullptr, a, count);
   const unsigned grid = (unsigned)min((count + 255) / 256, 4096);
-  for (int len = kMaxSortItems; len < count; len *= 2) {
+  for (int len = kRankSortItems; len < count; len *= 2) {
     const bool last = 2 * (int64_t)len >= count;
     hipLaunchKernelGGL(k_lpt_merge, dim3(grid), dim3(256), 0, s, a, b, last ? order : nullptr,
                        count, len);

@@ -33,9 +33,10 @@ constexpr int kBwdHeadChunk = 4;
 // kernels against an unmasked one on identical work (1.11 fwd, 1.08 dQ, 1.05 dK/dV).
 constexpr int kAlphaPartial = 11;
 constexpr int kAlphaUnmasked = 10;
-// The LPT sort: up to kMaxSortItems 64-bit keys in one workgroup's LDS; longer lists in
-// chunks of that size, merged pass by pass through a scratch buffer of
-// lpt_sort_scratch_bytes(count) bytes.  Lists are limited to kMaxWorkItems entries.
+// The LPT sort: up to 1024 64-bit keys in one workgroup's LDS; longer lists in chunks of
+// that size, merged pass by pass through a scratch buffer of lpt_sort_scratch_bytes(count)
+// bytes.  Lists are limited to kMaxWorkItems entries.  The dK/dV split plan runs in one
+// workgroup over at most kMaxSortItems (mask row, KV block) pairs.
 constexpr int kMaxSortItems = 8192;
 constexpr int64_t kMaxWorkItems = 1 << 24;
 // Splitting of long dK/dV work items.  A (mask row, KV block) pair whose queue is long

@@ -45,6 +45,16 @@ def test_configs_bit_exact(name, tile):
     compare(workloads.make_workload(name), *tile)
 
 
+# Long queue lists: 2, 4 or 8 Q-blocks of one mask row per classification workgroup (more
+# than 4096, 8192 or 16384 queue rows), with a Q-block count that R does not divide.
+@pytest.mark.parametrize("batch,n,bq,bk", [(3, 1499 * 16 - 5, 16, 128),
+                                           (5, 1999 * 16 - 3, 16, 256),
+                                           (3, 5555 * 16 - 7, 16, 256)])
+def test_rows_per_workgroup(batch, n, bq, bk):
+    w = workloads.random_intervals(21 + batch, n, batch=batch, p_empty=0.3)
+    compare(w, bq, bk)
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_adversarial_and_ragged(seed):
     rng = np.random.default_rng(100 + seed)
