@@ -318,7 +318,7 @@ __global__ __launch_bounds__(1024) void k_lpt_rank(const int32_t* __restrict__ c
                                                    int32_t* __restrict__ order,
                                                    unsigned long long* __restrict__ run,
                                                    int count) {
-  __shared__ unsigned long long keys[kRankSortItems];
+  __shared__ __align__(16) unsigned long long keys[kRankSortItems];
   const int tid = threadIdx.x;
   const int c0 = blockIdx.x * kRankSortItems;
   const int n = min(kRankSortItems, count - c0);
@@ -326,8 +326,18 @@ __global__ __launch_bounds__(1024) void k_lpt_rank(const int32_t* __restrict__ c
   keys[tid] = mine;
   __syncthreads();
   if (tid < n) {
+    // past n the keys are ~0, above every real key: count up to n rounded to 8, two keys
+    // per 16-byte read, four reads in flight
+    const int n8 = (n + 7) & ~7;
+    const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(keys);
     int rank = 0;
-    for (int i = 0; i < n; ++i) rank += keys[i] < mine ? 1 : 0;
+    for (int i = 0; i < n8 / 2; i += 4) {
+      ulonglong2 a[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = k2[i + j];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rank += (a[j].x < mine ? 1 : 0) + (a[j].y < mine ? 1 : 0);
+    }
     if (run) run[c0 + rank] = mine;
     else order[rank] = tid;
   }
