@@ -82,6 +82,25 @@ def test_blocks_classification_many_tiles():
     assert np.array_equal(out["k_order"].cpu().numpy(), oracle.lpt_order(oracle.tile_costs(kc)))
 
 
+@pytest.mark.parametrize("batch,n,bq,bk", [(3, 1499 * 16 - 5, 16, 128), (5, 1999 * 16 - 3, 16, 256)])
+def test_blocks_classification_long_lists(batch, n, bq, bk):
+    """More than 4096 / 8192 queue rows (2 / 4 Q-blocks per classification workgroup, a
+    Q-block count neither divides): bit-exact."""
+    import mask_aware_sparse_amd as fm
+    w = workloads.random_blocks(32, n, batch=batch, density=0.3)
+    (blk,) = workloads.mask_tensors(w, device="cuda")
+    out = fm.classify_tiles_blocks(blk, bq, bk, n, n)
+    torch.cuda.synchronize()
+    cls = oracle.classify_blocks(w.blocks, bq, bk, n, n)
+    qq, qc, kq, kc = oracle.queues(cls)
+    assert np.array_equal(out["tile_class"].cpu().numpy(), cls)
+    assert np.array_equal(out["q_queue"].cpu().numpy(), qq)
+    assert np.array_equal(out["q_count"].cpu().numpy(), qc)
+    assert np.array_equal(out["k_queue"].cpu().numpy(), kq)
+    assert np.array_equal(out["q_order"].cpu().numpy(), oracle.lpt_order(oracle.tile_costs(qc)))
+    assert np.array_equal(out["k_order"].cpu().numpy(), oracle.lpt_order(oracle.tile_costs(kc)))
+
+
 def test_blocks_dense_expansion():
     import mask_aware_sparse_amd as fm
     n = 450

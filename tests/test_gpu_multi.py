@@ -91,6 +91,27 @@ def test_multi_classification_many_tiles():
     assert np.array_equal(out["k_order"].cpu().numpy(), oracle.lpt_order(oracle.tile_costs(kc)))
 
 
+@pytest.mark.parametrize("n,bq,bk", [(1499 * 16 - 5, 16, 128), (5555 * 16 - 7, 16, 256)])
+def test_multi_classification_long_lists(n, bq, bk):
+    """More than 4096 / 16384 queue rows (2 / 8 Q-blocks per classification workgroup, a
+    Q-block count neither divides): bit-exact."""
+    import mask_aware_sparse_amd as fm
+    w = workloads.random_multi_intervals(31, n, batch=3, n_intervals=3)
+    s, e = workloads.mask_tensors(w, device="cuda")
+    out = fm.classify_tiles_multi(s, e, bq, bk)
+    torch.cuda.synchronize()
+    cls = oracle.classify_multi(w.starts, w.ends, bq, bk)
+    qq, qc, kq, kc = oracle.queues(cls)
+    assert np.array_equal(out["block_minmax"].cpu().numpy(),
+                          oracle.block_minmax_multi(w.starts, w.ends, bk))
+    assert np.array_equal(out["tile_class"].cpu().numpy(), cls)
+    assert np.array_equal(out["q_queue"].cpu().numpy(), qq)
+    assert np.array_equal(out["q_count"].cpu().numpy(), qc)
+    assert np.array_equal(out["k_queue"].cpu().numpy(), kq)
+    assert np.array_equal(out["q_order"].cpu().numpy(), oracle.lpt_order(oracle.tile_costs(qc)))
+    assert np.array_equal(out["k_order"].cpu().numpy(), oracle.lpt_order(oracle.tile_costs(kc)))
+
+
 def test_multi_dense_expansion():
     import mask_aware_sparse_amd as fm
     w = workloads.random_multi_intervals(11, 300, batch=2, n_intervals=4)
