@@ -43,9 +43,24 @@ def gpu_inputs(w, seed=None, device="cuda"):
     return q, k, v, do, vec
 
 
-def check_fwd(O, LSE, O_ref, LSE_ref, ctx=""):
+def bf16_half_ulp(x):
+    """Half the spacing of bfloat16 (8 significant bits) at |x|: the distance from x to the
+    nearest bf16 value is at most this."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(ax, np.finfo(np.float64).tiny)))
+    return np.exp2(e - 8)
+
+
+def check_fwd(O, LSE, O_ref, LSE_ref, ctx="", format_slack=False):
+    """O max-abs <= O_TOL; with format_slack, per element O_TOL plus half a bf16 ulp of the
+    exact value (an output stored in bf16 cannot be nearer to it than that, which is above
+    O_TOL once |O| >= 4)."""
     O, LSE = to_np(O), to_np(LSE)
-    err = np.abs(O - O_ref).max() if O.size else 0.0
+    if format_slack and O.size:
+        excess = np.abs(O - O_ref) - bf16_half_ulp(O_ref)
+        err = max(float(excess.max()), 0.0)
+    else:
+        err = np.abs(O - O_ref).max() if O.size else 0.0
     fin = np.isfinite(LSE_ref)
     assert np.array_equal(np.isneginf(LSE), np.isneginf(LSE_ref)), f"{ctx}: -inf LSE rows differ"
     lerr = np.abs(LSE[fin] - LSE_ref[fin]).max() if fin.any() else 0.0
