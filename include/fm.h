@@ -78,7 +78,7 @@ typedef enum { FM_OP_CLASSIFY = 0, FM_OP_FWD = 1, FM_OP_BWD = 2 } fm_op;
  * either divide heads_kv or be a multiple of it (so that one kv head's query heads never
  * straddle a mask set boundary partway); otherwise FM_ERR_INVALID_ARG.  Limits: N_q, N_k
  * <= 2^22 and batch * H_m * ceil(N_q/block_q) and batch * H_m * ceil(N_k/block_k) at
- * most 2^24 work blocks per sorted list (lists above 8192 blocks are sorted in chunks and
+ * most 2^24 work blocks per sorted list (lists above 1024 blocks are sorted in chunks and
  * merged, in workspace); larger problems return FM_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t batch;
