@@ -179,7 +179,10 @@ size_t fm_workspace_bytes(const fm_problem* p, fm_op op, int32_t block_q, int32_
 /* The tile shape (rows of Q, columns of K per tile) the forward or backward kernel uses
  * and classifies with: 128 x 64 for FM_OP_FWD (also the backward's dQ kernel), 32 x 128
  * for FM_OP_BWD (the dK/dV kernel; 32 x 256 when key_order = FM_KEYS_SORTED and
- * head_dim = 128, see below).  FM_OP_CLASSIFY is invalid here. */
+ * head_dim = 128, see below).  FM_OP_CLASSIFY is invalid here.  Where heads_q / heads_kv
+ * and heads_q / mask_heads are both multiples of 4, four query heads of one kv head share
+ * a forward (and dQ) workgroup, one per wave, over 32 rows: the forward's tile is then
+ * 32 x 64 (same work per tile and workgroup, four times as many Q-blocks and queue rows). */
 fm_status fm_tile_shape(fm_op op, int32_t* block_q, int32_t* block_k);
 
 /* Tile classification (FlashMask-3 page, §3.1 tile rule, generalized to all four
@@ -206,8 +209,9 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
  * it runs on until the process ends; nothing is allocated or freed by the call.  A
  * problem whose forward workspace (fm_workspace_size(p, FM_OP_FWD, ...)) exceeds that
  * size returns FM_ERR_WORKSPACE and launches nothing: key_order = FM_KEYS_NATURAL covers
- * N_k up to 131072 keys with one mask row (about 8.6 MiB there); FM_KEYS_SORTED needs room
- * for permuted copies of K and V and rarely fits.  All calls on one GPU share its array:
+ * N_k up to 131072 keys with one mask row (about 8.6 MiB there) at the 128-row forward tile,
+ * and up to 65536 keys at the 32-row tile of four packed query heads (about 8.4 MiB);
+ * FM_KEYS_SORTED needs room for permuted copies of K and V and rarely fits.  All calls on one GPU share its array:
  * calls that overlap on one GPU (issued on different streams with no ordering between
  * them) race and give undefined results; calls on one stream are safe.  The first call on
  * a device resolves the array's address there (hipGetSymbolAddress); FM_ERR_HIP if that

@@ -85,6 +85,11 @@ hipError_t dispatch_order(const fm_problem* p, const int32_t* cost, int32_t* ord
 inline bool sorted_keys(const fm_problem* p) { return p->key_order == FM_KEYS_SORTED; }
 // Keys per dK/dV workgroup (and the KV block of its tiles) for this problem.
 inline int bwd_bk(const fm_problem* p) { return fm::bwd_block_k(p->head_dim, sorted_keys(p)); }
+// Query heads per forward / dQ workgroup, and the rows of their Q-blocks.
+inline int fwd_pack_of(const fm_problem* p) {
+  return fm::fwd_pack(p->heads_q, p->heads_kv, hm_of(p));
+}
+inline int fwd_bq(const fm_problem* p) { return fm::fwd_block_q(fwd_pack_of(p)); }
 template <typename MaskT>
 fm_status check_key_order(const fm_problem* p) {
   if (!sorted_keys(p)) return FM_OK;
@@ -322,14 +327,14 @@ fm_status fm_workspace_size(const fm_problem* p, fm_op op, int32_t block_q, int3
       return FM_OK;
     }
     case FM_OP_FWD: {
-      Blocks nb = blocks(p, fm::kFwdBlockQ, fm::kFwdBlockK);
+      Blocks nb = blocks(p, fwd_bq(p), fm::kFwdBlockK);
       if ((st = check_sort_limits(p, nb)) != FM_OK) return st;
       *bytes = fwd_ws(p, nb).total;
       return FM_OK;
     }
     case FM_OP_BWD: {
       Blocks nk = blocks(p, fm::kBwdBlockQ, bwd_bk(p));
-      Blocks nq = blocks(p, fm::kFwdBlockQ, fm::kFwdBlockK);
+      Blocks nq = blocks(p, fwd_bq(p), fm::kFwdBlockK);
       if ((st = check_sort_limits(p, nk)) != FM_OK) return st;
       if ((st = check_sort_limits(p, nq)) != FM_OK) return st;
       *bytes = bwd_ws(p, nk, nq).total;
@@ -409,7 +414,7 @@ fm_status fwd_impl(const fm_problem* p, const void* q, const void* k, const void
   if (st != FM_OK) return st;
   if ((st = check_mask(p, m)) != FM_OK) return st;
   if ((st = check_key_order<MaskT>(p)) != FM_OK) return st;
-  Blocks nb = blocks(p, fm::kFwdBlockQ, fm::kFwdBlockK);
+  Blocks nb = blocks(p, fwd_bq(p), fm::kFwdBlockK);
   if ((st = check_sort_limits(p, nb)) != FM_OK) return st;
   if ((st = check_grid(p, nb, blocks(p, fm::kBwdBlockQ, bwd_bk(p)))) != FM_OK) return st;
   if (empty_problem(p)) return FM_OK;
@@ -431,7 +436,7 @@ fm_status fwd_impl(const fm_problem* p, const void* q, const void* k, const void
   t.q_cost = at<int32_t>(ws, w.q_cost);
   const int R = (int)mask_rows(p);
   if (e == hipSuccess)
-    e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kFwdBlockQ, fm::kFwdBlockK, t, s);
+    e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fwd_bq(p), fm::kFwdBlockK, t, s);
   int32_t* order = at<int32_t>(ws, w.q_order);
   if (e == hipSuccess)
     e = dispatch_order(p, t.q_cost, order, (int)(R * nb.nQB), at<char>(ws, w.sort), s);
@@ -445,6 +450,7 @@ fm_status fwd_impl(const fm_problem* p, const void* q, const void* k, const void
     a.B = p->batch; a.Hq = p->heads_q; a.Hkv = p->heads_kv; a.Hm = hm_of(p);
     a.Nq = nq_of(p); a.Nk = nk_of(p); a.D = p->head_dim;
     a.nQB = (int)nb.nQB; a.nKB = (int)nb.nKB;
+    a.pack = fwd_pack_of(p);
     a.scale = scale_of(p);
     e = fm::launch_fwd(a, s, ev_start(events), ev_stop(events));
   }
@@ -461,7 +467,7 @@ fm_status bwd_impl(const fm_problem* p, const void* q, const void* k, const void
   if ((st = check_mask(p, m)) != FM_OK) return st;
   if ((st = check_key_order<MaskT>(p)) != FM_OK) return st;
   Blocks nk = blocks(p, fm::kBwdBlockQ, bwd_bk(p));
-  Blocks nq = blocks(p, fm::kFwdBlockQ, fm::kFwdBlockK);
+  Blocks nq = blocks(p, fwd_bq(p), fm::kFwdBlockK);
   if ((st = check_sort_limits(p, nk)) != FM_OK) return st;
   if ((st = check_sort_limits(p, nq)) != FM_OK) return st;
   if ((st = check_grid(p, nq, nk)) != FM_OK) return st;
@@ -504,7 +510,7 @@ fm_status bwd_impl(const fm_problem* p, const void* q, const void* k, const void
   void* scr = at<char>(ws, w.sort);
   if (e == hipSuccess) e = dispatch_order(p, tk.k_cost, k_order, (int)(R * nk.nKB), scr, s);
   if (e == hipSuccess)
-    e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kFwdBlockQ, fm::kFwdBlockK, tq, s);
+    e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fwd_bq(p), fm::kFwdBlockK, tq, s);
   if (e == hipSuccess) e = dispatch_order(p, tq.q_cost, q_order, (int)(R * nq.nQB), scr, s);
   if (e == hipSuccess && ma.n == fm::kBlocksMode)
     e = fm::launch_zero_i32(at<int32_t>(ws, w.zeros), (size_t)R * nk_of(p), s);
@@ -529,6 +535,7 @@ fm_status bwd_impl(const fm_problem* p, const void* q, const void* k, const void
     a.bk = bwd_bk(p);
     a.nQB_k = (int)nk.nQB; a.nKB_k = (int)nk.nKB;
     a.nQB_q = (int)nq.nQB; a.nKB_q = (int)nq.nKB;
+    a.pack = fwd_pack_of(p);
     a.scale = scale_of(p);
     fm::BwdEvents ev{};
     if (events) {

@@ -629,6 +629,7 @@ struct DqParams {
   const int32_t* __restrict__ q_count;
   const int32_t* __restrict__ q_order;
   int B, Hq, Hkv, Hm, Nq, Nk, nQB, nKB;  // Nq query rows, Nk keys, Hm mask sets per batch row
+  int pack;     // query heads per workgroup: 1 (128 rows of one head) or 4 (32 rows of four)
   float c;      // scale * log2(e)
   float scale;  // softmax scale (applied to dQ)
 };
@@ -647,15 +648,21 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void k_attn_bwd_dq(DqParams p
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // workgroup L: the (L % qpm)-th query head of the mask set of LPT item L / qpm
+  // workgroup L: the (L % gpi)-th group of p.pack query heads of the mask set of LPT item
+  // L / gpi, the forward's decode: packed, wave w takes head 4 g + w over the Q-block's 32
+  // rows; else the one head's 128 rows, 32 per wave.
   const int L = xcd_logical((int)blockIdx.x, (int)gridDim.x);
   const int qpm = p.Hq / p.Hm;
-  const int r = L / qpm;
+  const int gpi = qpm / p.pack;
+  const int r = L / gpi;
   const int item = p.q_order[r];
   const int mr = item / p.nQB, qb = item - mr * p.nQB;  // mask row (b, set) and Q-block
   const int b = mr / p.Hm;
-  const int h = (mr - b * p.Hm) * qpm + (L - r * qpm);
-  const int kvh = h / (p.Hq / p.Hkv);
+  const bool packed = p.pack > 1;
+  const int hg = (mr - b * p.Hm) * qpm + (L - r * gpi) * p.pack;  // first head of the group
+  const int kvh = hg / (p.Hq / p.Hkv);
+  const int h = hg + (packed ? __builtin_amdgcn_readfirstlane(wave) : 0);  // this wave's
+  const int bq = packed ? BQ / kFwdPack : BQ;  // rows of the Q-block
   const int n_tiles = p.q_count[2 * item] + p.q_count[2 * item + 1];
   const const_i32_ptr queue = const_view(p.q_queue + (size_t)item * p.nKB);
   const int N = p.Nk, Nq = p.Nq;  // N: keys (and mask columns)
@@ -680,7 +687,7 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void k_attn_bwd_dq(DqParams p
   }
   const bool ragged = (N % BK) != 0;
 
-  const int row = qb * BQ + wave * 32 + l32;
+  const int row = qb * bq + (packed ? 0 : wave * 32) + l32;
 
   f32x16 qacc[kDB];
 #pragma unroll
@@ -759,7 +766,7 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void k_attn_bwd_dq(DqParams p
     const bool part = (e < 0) || (ragged && kb == p.nKB - 1);
     if (part) {
       const int key = kb * BK + mk_key;
-      const int r0 = qb * BQ + mk_wave * 32;
+      const int r0 = qb * bq + (packed ? 0 : mk_wave * 32);
       uint32_t w;
       if constexpr (!kMulti)
         w = hidden_rows32((int)vec[0], (int)vec[1], (int)vec[2], (int)vec[3], r0);
@@ -1008,9 +1015,10 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s, const BwdEvents& ev) {
   q.q_queue = a.q_queue; q.q_count = a.q_count; q.q_order = a.q_order;
   q.B = a.B; q.Hq = a.Hq; q.Hkv = a.Hkv; q.Hm = a.Hm; q.Nq = a.Nq; q.Nk = a.Nk;
   q.nQB = a.nQB_q; q.nKB = a.nKB_q;
+  q.pack = a.pack > 1 ? kFwdPack : 1;
   q.c = c;
   q.scale = a.scale;
-  const unsigned qgrid = (unsigned)a.B * (unsigned)a.nQB_q * (unsigned)a.Hq;
+  const unsigned qgrid = (unsigned)a.B * (unsigned)a.nQB_q * (unsigned)(a.Hq / q.pack);
   if (ev.dq_start) (void)hipEventRecord(ev.dq_start, s);
   const bool multi = a.m.n > 0;
   const bool d64 = a.D == 64;

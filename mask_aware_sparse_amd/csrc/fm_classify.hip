@@ -311,21 +311,27 @@ __device__ __forceinline__ unsigned long long lpt_key(const int32_t* __restrict_
 
 // One key per thread: the keys are unique, so each key's place in its chunk's sorted order
 // is the number of the chunk's keys below it, counted against all of them in LDS after one
-// barrier.  Chunk blockIdx.x holds keys [c0, c0 + n); a single chunk writes the item indices
-// to `order`, several write their sorted keys to `run` for merging.
+// barrier.  Chunk blockIdx.x holds keys [c0, c0 + n); its kRankSortItems / 256 workgroups
+// (blockIdx.y) each load the whole chunk and rank 256 of its keys, so one chunk's counting
+// spreads over several CUs.  A single chunk writes the item indices to `order`, several
+// write their sorted keys to `run` for merging.
 constexpr int kRankSortItems = 1024;
-__global__ __launch_bounds__(1024) void k_lpt_rank(const int32_t* __restrict__ cost,
-                                                   int32_t* __restrict__ order,
-                                                   unsigned long long* __restrict__ run,
-                                                   int count) {
+constexpr int kRankThreads = 256;
+__global__ __launch_bounds__(kRankThreads) void k_lpt_rank(const int32_t* __restrict__ cost,
+                                                           int32_t* __restrict__ order,
+                                                           unsigned long long* __restrict__ run,
+                                                           int count) {
   __shared__ __align__(16) unsigned long long keys[kRankSortItems];
   const int tid = threadIdx.x;
   const int c0 = blockIdx.x * kRankSortItems;
   const int n = min(kRankSortItems, count - c0);
-  const unsigned long long mine = tid < n ? lpt_key(cost, c0 + tid) : ~0ull;
-  keys[tid] = mine;
+#pragma unroll
+  for (int i = tid; i < kRankSortItems; i += kRankThreads)
+    keys[i] = i < n ? lpt_key(cost, c0 + i) : ~0ull;
   __syncthreads();
-  if (tid < n) {
+  const int me = blockIdx.y * kRankThreads + tid;  // this thread's key in the chunk
+  if (me < n) {
+    const unsigned long long mine = keys[me];
     // past n the keys are ~0, above every real key: count up to n rounded to 8, two keys
     // per 16-byte read, four reads in flight
     const int n8 = (n + 7) & ~7;
@@ -339,7 +345,7 @@ __global__ __launch_bounds__(1024) void k_lpt_rank(const int32_t* __restrict__ c
       for (int j = 0; j < 4; ++j) rank += (a[j].x < mine ? 1 : 0) + (a[j].y < mine ? 1 : 0);
     }
     if (run) run[c0 + rank] = mine;
-    else order[rank] = tid;
+    else order[rank] = me;
   }
 }
 
@@ -487,15 +493,16 @@ hipError_t launch_lpt_sort(const int32_t* cost, int32_t* order, int count, void*
                            hipStream_t s) {
   if (count <= 0) return hipSuccess;
   if (count <= kRankSortItems) {
-    hipLaunchKernelGGL(k_lpt_rank, dim3(1), dim3(kRankSortItems), 0, s, cost, order,
+    const unsigned parts = (unsigned)((count + kRankThreads - 1) / kRankThreads);
+    hipLaunchKernelGGL(k_lpt_rank, dim3(1, parts), dim3(kRankThreads), 0, s, cost, order,
                        (unsigned long long*)nullptr, count);
     return hipGetLastError();
   }
   unsigned long long* a = static_cast<unsigned long long*>(scratch);
   unsigned long long* b = a + count;
   const int chunks = (count + kRankSortItems - 1) / kRankSortItems;
-  hipLaunchKernelGGL(k_lpt_rank, dim3(chunks), dim3(kRankSortItems), 0, s, cost,
-                     (int32_t*)nullptr, a, count);
+  hipLaunchKernelGGL(k_lpt_rank, dim3(chunks, kRankSortItems / kRankThreads), dim3(kRankThreads),
+                     0, s, cost, (int32_t*)nullptr, a, count);
   const unsigned grid = (unsigned)min((count + 255) / 256, 4096);
   for (int len = kRankSortItems; len < count; len *= 2) {
     const bool last = 2 * (int64_t)len >= count;

@@ -66,7 +66,8 @@ struct FwdParams {
   const int32_t* __restrict__ q_count;
   const int32_t* __restrict__ q_order;
   int B, Hq, Hkv, Hm, Nq, Nk, nQB, nKB;  // Nq query rows, Nk keys, Hm mask sets per batch row
-  float c;  // softmax scale * log2(e)
+  int pack;  // query heads per workgroup: 1 (128 rows of one head) or 4 (32 rows of four)
+  float c;   // softmax scale * log2(e)
 };
 
 // D: head dimension (64, 128 or 256).  kMulti: the mask is the multi-interval form (else the
@@ -90,15 +91,21 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void k_attn_fwd(FwdParams p) 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // workgroup L: the (L % qpm)-th query head of the mask set of LPT item L / qpm
+  // workgroup L: the (L % gpi)-th group of p.pack query heads of the mask set of LPT item
+  // L / gpi.  Packed (p.pack = 4), wave w takes head 4 g + w over the Q-block's 32 rows; else
+  // the one head's 128 rows, 32 per wave.  The heads of a group share one kv head.
   const int L = xcd_logical((int)blockIdx.x, (int)gridDim.x);
   const int qpm = p.Hq / p.Hm;
-  const int r = L / qpm;
+  const int gpi = qpm / p.pack;
+  const int r = L / gpi;
   const int item = p.q_order[r];
   const int mr = item / p.nQB, qb = item - mr * p.nQB;  // mask row (b, set) and Q-block
   const int b = mr / p.Hm;
-  const int h = (mr - b * p.Hm) * qpm + (L - r * qpm);
-  const int kvh = h / (p.Hq / p.Hkv);
+  const bool packed = p.pack > 1;
+  const int hg = (mr - b * p.Hm) * qpm + (L - r * gpi) * p.pack;  // first head of the group
+  const int kvh = hg / (p.Hq / p.Hkv);
+  const int h = hg + (packed ? __builtin_amdgcn_readfirstlane(wave) : 0);  // this wave's
+  const int bq = packed ? BQ / kFwdPack : BQ;  // rows of the Q-block
   const int n_tiles = p.q_count[2 * item] + p.q_count[2 * item + 1];
   const const_i32_ptr queue = const_view(p.q_queue + (size_t)item * p.nKB);
   const int Nq = p.Nq, N = p.Nk;  // N: keys (and mask columns)
@@ -124,7 +131,7 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void k_attn_fwd(FwdParams p) 
   }
   const bool ragged = (N % BK) != 0;
 
-  const int row = qb * BQ + wave * 32 + l32;
+  const int row = qb * bq + (packed ? 0 : wave * 32) + l32;
   auto out_rsrc = [&]() { return make_rsrc(p.o + (size_t)(b * p.Hq + h) * Nq * D, q_bytes); };
   auto lse_rsrc = [&]() { return make_rsrc(p.lse + (size_t)(b * p.Hq + h) * Nq, (uint32_t)Nq * 4); };
 
@@ -247,7 +254,7 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void k_attn_fwd(FwdParams p) 
     }
     if (is_partial(e)) {
       const int key = (e & 0x7fffffff) * BK + mk_key;
-      const int r0 = qb * BQ + mk_wave * 32;
+      const int r0 = qb * bq + (packed ? 0 : mk_wave * 32);
       uint32_t w;
       if constexpr (!kMulti)
         w = hidden_rows32((int)vec[0], (int)vec[1], (int)vec[2], (int)vec[3], r0);
@@ -513,8 +520,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_
   p.q_order = a.q_order;
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Hm = a.Hm; p.Nq = a.Nq; p.Nk = a.Nk;
   p.nQB = a.nQB; p.nKB = a.nKB;
+  p.pack = a.pack > 1 ? kFwdPack : 1;
   p.c = a.scale * kLog2e;
-  const unsigned grid = (unsigned)a.B * (unsigned)a.nQB * (unsigned)a.Hq;
+  const unsigned grid = (unsigned)a.B * (unsigned)a.nQB * (unsigned)(a.Hq / p.pack);
   if (ev0) (void)hipEventRecord(ev0, s);
   if (grid > 0) {
     const bool multi = a.m.n > 0;

@@ -25,6 +25,16 @@ constexpr int kBwdBlockKWide = 256;
 inline int bwd_block_k(int D, bool sorted_keys) {
   return sorted_keys && D == 128 ? kBwdBlockKWide : kBwdBlockK;
 }
+// Forward and dQ workgroups are 4 waves of 32 query rows.  Where every four consecutive
+// query heads share a kv head and a mask set, a workgroup takes the same 32 rows of four
+// heads (one per wave) instead of 128 rows of one head: Q-blocks of 32 rows, so tiles of
+// 32 x 64 that follow the mask more closely, at the same work per workgroup and tile.
+constexpr int kFwdPack = 4;
+inline int fwd_pack(int Hq, int Hkv, int Hm) {
+  if (Hq <= 0 || Hkv <= 0 || Hm <= 0) return 1;
+  return (Hq / Hkv) % kFwdPack == 0 && (Hq / Hm) % kFwdPack == 0 ? kFwdPack : 1;
+}
+inline int fwd_block_q(int pack) { return kFwdBlockQ / pack; }
 // Query heads handled by one backward work item (dK/dV of a KV block are summed over
 // these heads in registers, then added across items with fp32 atomics).
 constexpr int kBwdHeadChunk = 4;
@@ -175,7 +185,8 @@ struct FwdArgs {
   const int32_t* q_count;
   const int32_t* q_order;
   int B, Hq, Hkv, Hm, Nq, Nk, nQB, nKB;  // Hm: mask sets per batch row
-  int D;                                 // head dimension: 64 or 128
+  int D;                                 // head dimension: 64, 128 or 256
+  int pack;                              // query heads per workgroup: fwd_pack(...)
   float scale;
 };
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
@@ -195,7 +206,7 @@ struct BwdArgs {
   const int32_t* k_queue;
   const int32_t* k_count;
   const int32_t* k_order;
-  // Q-block-outer tiles (dQ kernel): the forward's tile kFwdBlockQ x kFwdBlockK
+  // Q-block-outer tiles (dQ kernel): the forward's tile fwd_block_q(pack) x kFwdBlockK
   const int32_t* q_queue;
   const int32_t* q_count;
   const int32_t* q_order;
@@ -218,6 +229,7 @@ struct BwdArgs {
   int bk;            // keys per dK/dV workgroup: bwd_block_k(D, sorted keys)
   int nQB_k, nKB_k;  // block counts at the dK/dV tile
   int nQB_q, nKB_q;  // block counts at the dQ (forward) tile
+  int pack;          // query heads per dQ workgroup: fwd_pack(...)
   float scale;
 };
 // Extra pair units of the split plan for `per` workgroups per pair, and the partial slots
