@@ -10,9 +10,10 @@ offset of 0, every p would underflow; with scores near +255 every p would overfl
 Inputs (workloads.extreme_logit_tensors): half of each key row is one shared +-1 pattern,
 the other half exact small random values; queries put a factor of +-32 on the shared
 half, so every q.k is exact in fp32.  The masks
-put rows of diagonal Q-blocks above their first queued tile (queues run right to left):
-causal documents, share-question packing, prefix-LM documents and plain causal with a
-ragged tail.  Bars as everywhere: O max-abs 1e-2, LSE max-abs 1e-3 with -inf rows equal,
+put rows of diagonal Q-blocks above their first queued tile (queues run right to left) at
+the forward's tile for their heads (128 rows, or 32 rows of four packed query heads):
+causal documents, share-question packing, prefix-LM documents (also packed) and plain
+causal with a ragged tail.  Bars as everywhere: O max-abs 1e-2, LSE max-abs 1e-3 with -inf rows equal,
 dQ/dK/dV relative L2 2e-2."""
 import numpy as np
 import pytest
@@ -22,13 +23,25 @@ import oracle
 import workloads
 from parity import check_fwd, check_grads, log, to_np
 
-FWD_BQ, FWD_BK = 128, 64   # the forward's tile: 128 query rows x 64 keys
+FWD_BK = 64   # keys per forward tile
+
+
+def fwd_bq(w):
+    """Query rows per forward tile: 32 where four query heads of one kv head and mask set
+    share a workgroup (head groups of four), else 128."""
+    g, qpm = w.heads_q // w.heads_kv, w.heads_q // max(getattr(w, "mask_heads", 0) or 1, 1)
+    return 32 if g % 4 == 0 and qpm % 4 == 0 else 128
 
 MASKS = {
     "causal_doc_1k": lambda: workloads.causal_doc(0, heads_q=2, heads_kv=1),
-    "share_question_2k_mqa": lambda: workloads.share_question(0, n=2048, heads_q=4, heads_kv=1,
+    "share_question_2k_mqa": lambda: workloads.share_question(0, n=2048, heads_q=2, heads_kv=1,
                                                               prompt_range=(128, 256),
                                                               answer_range=(64, 128)),
+    # four query heads per kv head: the forward's packed 32-row tiles, where the rows above
+    # a document boundary see nothing of the next document's bidirectional prefix
+    "prefix_lm_doc_1k_mqa4_packed": lambda: workloads.prefix_lm_doc(1, n=1024, batch=2,
+                                                                    heads_q=4, heads_kv=1,
+                                                                    lo=128, hi=512),
     "prefix_lm_doc_1k_gqa": lambda: workloads.prefix_lm_doc(1, n=1024, batch=2, heads_q=4,
                                                             heads_kv=2, lo=128, hi=512),
     "causal_777": lambda: workloads.causal(777, heads_q=2, heads_kv=2),
@@ -38,7 +51,8 @@ KINDS = ("low", "high", "mixed")
 
 def rows_hidden_in_first_tile(w):
     """Rows that see some key but none of their Q-block's first queued forward tile."""
-    cls = oracle.classify(*w.vectors(), FWD_BQ, FWD_BK)
+    bq = fwd_bq(w)
+    cls = oracle.classify(*w.vectors(), bq, FWD_BK)
     out = []
     for b in range(w.batch):
         hid = oracle.masked_rows(*(x[b] for x in w.vectors()), 0, w.seqlen)
@@ -47,7 +61,7 @@ def rows_hidden_in_first_tile(w):
             if live.size == 0:
                 continue
             kb = live.max()                                    # queues run right to left
-            r0, r1 = qb * FWD_BQ, min(qb * FWD_BQ + FWD_BQ, w.seqlen)
+            r0, r1 = qb * bq, min(qb * bq + bq, w.seqlen)
             k0, k1 = kb * FWD_BK, min(kb * FWD_BK + FWD_BK, w.seqlen)
             sub = hid[r0:r1]
             rows = np.nonzero(sub[:, k0:k1].all(1) & ~sub.all(1))[0] + r0
