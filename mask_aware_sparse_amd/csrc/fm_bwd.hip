@@ -424,7 +424,7 @@ __global__ __launch_bounds__(64 * kW, (D > 128 || kW > 4) ? 1 : 2) void k_attn_b
     }
     if (tid < BQ) {
       sm.lse2[buf][tid] = __uint_as_float(lst);
-      sm.dl[buf][tid] = __uint_as_float(dst_);
+      sm.dl[buf][tid] = -__uint_as_float(dst_);  // -D: the dP products start from it
     }
   };
 
@@ -478,7 +478,19 @@ __global__ __launch_bounds__(64 * kW, (D > 128 || kW > 4) ? 1 : 2) void k_attn_b
       // ---- S = Q K^T and dP = dO V^T for 32 query rows x this wave's 32 keys.  Step s
       // reads its K, Q and dO fragments one step ahead; the scheduling barriers keep the
       // reads ahead of the products. ----
+      // dP - D in one: the dP products accumulate onto -D of each row, which lies in LDS in
+      // the accumulator's element order (element j*8 + t: row j*16 + hh*8 + t)
       f32x16 sacc, pacc;
+      {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int q0 = qblk * 32 + j * 16 + hh * 8;
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sm.dl[cur][q0]);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sm.dl[cur][q0 + 4]);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) { pacc[j * 8 + t] = d0[t]; pacc[j * 8 + 4 + t] = d1[t]; }
+        }
+      }
       {
         bf16x8 kf[2], qf[2], of[2];
         auto rd = [&](int s, int slot) {
@@ -493,7 +505,7 @@ __global__ __launch_bounds__(64 * kW, (D > 128 || kW > 4) ? 1 : 2) void k_attn_b
         for (int s = 0; s < kS; ++s) {
           if (s + 1 < kS) rd(s + 1, (s + 1) & 1);
           sacc = mfma32(qf[s & 1], kf[s & 1], s == 0 ? f32x16{} : sacc);
-          pacc = mfma32(of[s & 1], vr[s], s == 0 ? f32x16{} : pacc);
+          pacc = mfma32(of[s & 1], vr[s], pacc);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -508,8 +520,6 @@ __global__ __launch_bounds__(64 * kW, (D > 128 || kW > 4) ? 1 : 2) void k_attn_b
           const int q0 = qblk * 32 + j * 16 + hh * 8;
           const f32x4 l0 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][q0]);
           const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][q0 + 4]);
-          const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sm.dl[cur][q0]);
-          const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sm.dl[cur][q0 + 4]);
           u32x4 pw, sw;
 #pragma unroll
           for (int t = 0; t < 8; t += 2) {
@@ -518,11 +528,10 @@ __global__ __launch_bounds__(64 * kW, (D > 128 || kW > 4) ? 1 : 2) void k_attn_b
             for (int u = 0; u < 2; ++u) {
               const int tt = t + u;
               const float l = tt < 4 ? l0[tt] : l1[tt - 4];
-              const float dd = tt < 4 ? d0[tt] : d1[tt - 4];
               float pp = __builtin_amdgcn_exp2f(fmaf(sacc[j * 8 + tt], p.c, -l));
               if (kMasked) pp = mask_zero(pp, word, (uint32_t)(j * 16 + hh * 8 + tt));
               pv[u] = pp;
-              sv[u] = pp * (pacc[j * 8 + tt] - dd);
+              sv[u] = pp * pacc[j * 8 + tt];
             }
             pw[t / 2] = pack_bf16x2(pv[0], pv[1]);
             sw[t / 2] = pack_bf16x2(sv[0], sv[1]);
