@@ -486,8 +486,13 @@ class ClockSampler:
             except Exception:
                 pass
 
+    # below this many samples (0.2 s of timed steps at the default period) the readings
+    # catch the clock ramping up or idle between launches and say nothing of the kernels'
+    MIN_SAMPLES = 10
+
     def mean(self):
-        return float(np.mean(self.samples)) if self.samples else None
+        """Mean of the samples, or None with fewer than MIN_SAMPLES of them."""
+        return float(np.mean(self.samples)) if len(self.samples) >= self.MIN_SAMPLES else None
 
 
 def run_workload(name, seed, steps, warmup, key_order_opt, schedule, clock=None):

@@ -52,3 +52,13 @@ def test_benchmark_workloads_pair_counts_are_positive():
         else:
             a = bench.attended_pairs(w)
         assert 0 < a <= w.batch * w.heads_q * w.seqlen ** 2
+
+
+def test_clock_mean_needs_enough_samples():
+    """A mean clock is reported only from MIN_SAMPLES readings on: short runs catch the clock
+    ramping or idle between launches."""
+    c = bench.ClockSampler.__new__(bench.ClockSampler)
+    c.samples = [1900.0] * (bench.ClockSampler.MIN_SAMPLES - 1)
+    assert c.mean() is None
+    c.samples.append(1800.0)
+    assert abs(c.mean() - (1900.0 * (len(c.samples) - 1) + 1800.0) / len(c.samples)) < 1e-9
