@@ -495,9 +495,12 @@ class ClockSampler:
         return float(np.mean(self.samples)) if len(self.samples) >= self.MIN_SAMPLES else None
 
 
-def run_workload(name, seed, steps, warmup, key_order_opt, schedule, clock=None):
+def run_workload(name, seed, steps, warmup, key_order_opt, schedule, clock=None, graph=False):
     """Time `steps` fwd+bwd steps of workload `name` after `warmup` untimed ones.  Returns a
-    dict of the figures and the input tensors (for the CPU baseline)."""
+    dict of the figures and the input tensors (for the CPU baseline).  With `graph`, the
+    timed steps are replays of one HIP graph holding a whole step (both calls: every
+    classification, sort and attention kernel), captured after the eager steps, which still
+    give the per-kernel times; the eager wall time per step is reported beside it."""
     import torch
     import mask_aware_sparse_amd as fm
 
@@ -555,13 +558,30 @@ def run_workload(name, seed, steps, warmup, key_order_opt, schedule, clock=None)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    if clock is not None:
+    if clock is not None and not graph:
         clock.start()
     t0 = time.perf_counter()
     for i in range(steps):
         step(ev[i // 2] if i % 2 == 0 else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    eager_ms = wall * 1e3 / steps
+    if graph:
+        # the library allocates nothing, issues no memset and never synchronizes inside a
+        # call, so one step captures whole (the same buffers, replayed on the same stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        if clock is not None:
+            clock.start()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     if clock is not None:
         clock.stop()
 
@@ -585,12 +605,14 @@ def run_workload(name, seed, steps, warmup, key_order_opt, schedule, clock=None)
               "mask_intervals": w.n_intervals if multi else None,
               "mask_blocks": "128x128" if blocks else None, "seq_len": w.seqlen,
               "head_dim": d, "attended_pairs": A, "seed": seed,
-              "key_order": "sorted" if sorted_keys else "natural", "schedule": schedule}
+              "key_order": "sorted" if sorted_keys else "natural", "schedule": schedule,
+              "launch": "hip_graph" if graph else "eager"}
     return {
         "w": w, "tensors": (q, k, v, do), "value": value, "ms": ms, "config": config,
         "kernels": {kname: {"ms": round(t, 4), "algorithmic_tflops": round(tflops[kname], 2)}
                     for kname, (t, _) in kernels.items()},
         "event_ms_per_step": round(float(step_ms.mean()), 4),
+        "eager_ms_per_step": round(eager_ms, 4),
         # whole calls, classification and LPT sort included: 4d*A / t_fwd and 10d*A / t_bwd
         "fwd": {"ms": round(float(call_fwd_ms.mean()), 4),
                 "tflops": round(4 * d * A / (call_fwd_ms.mean() * 1e-3) / 1e12, 2)},
@@ -634,6 +656,9 @@ def main():
                          "random-eviction workload, natural otherwise)")
     ap.add_argument("--schedule", choices=["lpt", "natural"], default="lpt",
                     help="dispatch order of the attention kernels' work items")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one HIP graph holding a whole step (launch gaps "
+                         "removed; per-kernel times still come from eager steps)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; multi-GPU runs are not supported",
@@ -664,7 +689,7 @@ def main():
         also = [x for x in args.also.split(",") if x]
     clock = ClockSampler()
     r = run_workload(args.workload, args.seed, args.steps, args.warmup, args.key_order,
-                     args.schedule, clock)
+                     args.schedule, clock, graph=args.graph)
     cpu = None
     if args.cpu_budget > 0:
         cpu = cpu_baseline(r["w"], *r["tensors"], args.cpu_budget)
@@ -676,11 +701,12 @@ def main():
     extra = {}
     for name in also:
         x = run_workload(name, args.seed, args.steps, args.warmup, args.key_order,
-                         args.schedule)
+                         args.schedule, graph=args.graph)
         x["tensors"] = None
         torch.cuda.empty_cache()
         extra[name] = {"value": round(x["value"], 3), "unit": "TFLOP/s",
                        "ms_per_step": round(x["ms"], 4),
+                       "eager_ms_per_step": x["eager_ms_per_step"],
                        "pct_mfma_peak": round(100 * x["value"] / MFMA_BF16_PEAK_TFLOPS, 2),
                        "key_order": x["config"]["key_order"], "kernels": x["kernels"],
                        "fwd": x["fwd"], "bwd": x["bwd"],
@@ -709,6 +735,7 @@ def main():
                    if peak_at_clock else None},
         "kernels": r["kernels"],
         "event_ms_per_step": r["event_ms_per_step"],
+        "eager_ms_per_step": r["eager_ms_per_step"],
         "fwd": r["fwd"],
         "bwd": r["bwd"],
         "roofline": r["roofline"],

@@ -505,13 +505,22 @@ fm_status bwd_impl(const fm_problem* p, const void* q, const void* k, const void
   int32_t* k_order = at<int32_t>(ws, w.k_order);
   int32_t* q_order = at<int32_t>(ws, w.q_order);
   const int R = (int)mask_rows(p);
+  // both tile shapes' classifications (the dK/dV kernel's per-KV-block queues, the dQ
+  // kernel's per-Q-block queues) in shared launches: one block min/max pass, one classify
+  // launch, one sort launch for short lists
   if (e == hipSuccess)
-    e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fm::kBwdBlockQ, bwd_bk(p), tk, s);
+    e = fm::launch_classify_pair(ma, R, nq_of(p), nk_of(p), fm::kBwdBlockQ, bwd_bk(p), tk,
+                                 fwd_bq(p), fm::kFwdBlockK, tq, s);
   void* scr = at<char>(ws, w.sort);
-  if (e == hipSuccess) e = dispatch_order(p, tk.k_cost, k_order, (int)(R * nk.nKB), scr, s);
-  if (e == hipSuccess)
-    e = fm::launch_classify(ma, R, nq_of(p), nk_of(p), fwd_bq(p), fm::kFwdBlockK, tq, s);
-  if (e == hipSuccess) e = dispatch_order(p, tq.q_cost, q_order, (int)(R * nq.nQB), scr, s);
+  if (e == hipSuccess) {
+    if (p->schedule == FM_SCHEDULE_NATURAL) {
+      e = dispatch_order(p, tk.k_cost, k_order, (int)(R * nk.nKB), scr, s);
+      if (e == hipSuccess) e = dispatch_order(p, tq.q_cost, q_order, (int)(R * nq.nQB), scr, s);
+    } else {
+      e = fm::launch_lpt_sort_pair(tk.k_cost, k_order, (int)(R * nk.nKB), tq.q_cost, q_order,
+                                   (int)(R * nq.nQB), scr, s);
+    }
+  }
   if (e == hipSuccess && ma.n == fm::kBlocksMode)
     e = fm::launch_zero_i32(at<int32_t>(ws, w.zeros), (size_t)R * nk_of(p), s);
   if (e == hipSuccess) {

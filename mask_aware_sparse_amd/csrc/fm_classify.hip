@@ -17,12 +17,16 @@ namespace fm {
 // ---- A2: block min/max of the four vectors -------------------------------------
 // A wave takes 256 columns of one mask row at a time (four waves per workgroup striding
 // over all of them): lane l loads columns 4l .. 4l + 3 of each vector, sixteen independent
-// loads in flight, and the bk / 4 lanes of each KV block reduce among themselves.
+// loads in flight, and the bk / 4 lanes of each KV block reduce among themselves.  With
+// mm2, the min/max of the smaller blocks of bk2 < bk keys is written on the way (the
+// backward needs both of its tile shapes' block bounds: one pass instead of two).
 __global__ __launch_bounds__(256) void k_block_minmax(MaskPtrs m, int Nk, int nKB, int bk,
                                                       int n_sc, int total,
-                                                      int32_t* __restrict__ mm) {
+                                                      int32_t* __restrict__ mm, int bk2,
+                                                      int nKB2, int32_t* __restrict__ mm2) {
   const int lane = threadIdx.x & 63;
   const int G = bk >> 2;  // lanes per KV block (2 .. 64)
+  const int G2 = mm2 ? bk2 >> 2 : 0;  // lanes per smaller block (1 .. G / 2), 0: none
   // 16-byte loads where every row starts on a 16-byte boundary
   const bool vec4 = (Nk & 3) == 0 &&
                     ((reinterpret_cast<uintptr_t>(m.lts) | reinterpret_cast<uintptr_t>(m.lte) |
@@ -63,6 +67,15 @@ __global__ __launch_bounds__(256) void k_block_minmax(MaskPtrs m, int Nk, int nK
       v[2 * t + 1] = hi;
     }
     for (int off = 1; off < G; off <<= 1) {
+      if (off == G2) {
+        // lanes of each bk2-block have combined their columns: its first lane writes them
+        const int kb2 = c0 / bk2;
+        if ((lane & (G2 - 1)) == 0 && kb2 < nKB2) {
+          int32_t* dst = mm2 + ((size_t)b * nKB2 + kb2) * 8;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) dst[t] = v[t];
+        }
+      }
 #pragma unroll
       for (int t = 0; t < 8; t += 2) {
         v[t] = min(v[t], __shfl_xor(v[t], off));
@@ -198,15 +211,35 @@ __device__ __forceinline__ ScanResult block_scan_256(bool flag, bool sub, int* s
 // scan over the workgroup (two barriers) places the queued tiles of all kR rows.  kR > 1
 // only for long lists (many mask rows), where reading every KV block's bounds once per
 // Q-block made the kernel bound by L2 reads.
+struct ClassifyQArgs {
+  const int32_t* mm;
+  GridArgs ga;
+  int Nq, nQB, nKB, bq, groups;
+  uint8_t* cls;
+  int32_t* q_queue;
+  int32_t* q_count;
+  int32_t* q_cost;
+};
+struct ClassifyKArgs {
+  const int32_t* mm;
+  GridArgs ga;
+  int Nq, nQB, nKB, bq;
+  int32_t* k_queue;
+  int32_t* k_count;
+  int32_t* k_cost;
+};
+
 template <int kMode, int kR>
-__global__ __launch_bounds__(256) void k_classify_q(const int32_t* __restrict__ mm, int n,
-                                                    GridArgs ga, int Nq, int nQB, int nKB, int bq,
-                                                    int groups, uint8_t* __restrict__ cls,
-                                                    int32_t* __restrict__ q_queue,
-                                                    int32_t* __restrict__ q_count,
-                                                    int32_t* __restrict__ q_cost) {
+__device__ __forceinline__ void classify_q_body(const ClassifyQArgs& a, int n, int blk) {
   __shared__ int sh_cnt[kR][4], sh_sub[kR][4];
-  const int b = blockIdx.x / groups, qb0 = (blockIdx.x - b * groups) * kR;
+  const int32_t* __restrict__ mm = a.mm;
+  const GridArgs ga = a.ga;
+  const int Nq = a.Nq, nQB = a.nQB, nKB = a.nKB, bq = a.bq, groups = a.groups;
+  uint8_t* __restrict__ cls = a.cls;
+  int32_t* __restrict__ q_queue = a.q_queue;
+  int32_t* __restrict__ q_count = a.q_count;
+  int32_t* __restrict__ q_cost = a.q_cost;
+  const int b = blk / groups, qb0 = (blk - b * groups) * kR;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int base[kR], np[kR];
 #pragma unroll
@@ -266,15 +299,22 @@ __global__ __launch_bounds__(256) void k_classify_q(const int32_t* __restrict__ 
   }
 }
 
+template <int kMode, int kR>
+__global__ __launch_bounds__(256) void k_classify_q(ClassifyQArgs a, int n) {
+  classify_q_body<kMode, kR>(a, n, (int)blockIdx.x);
+}
+
 // ---- A3 (backward direction): per-KV-block queues of Q-blocks, ascending -----------
 template <int kMode>
-__global__ __launch_bounds__(256) void k_classify_k(const int32_t* __restrict__ mm, int n,
-                                                    GridArgs ga, int Nq, int nQB, int nKB, int bq,
-                                                    int32_t* __restrict__ k_queue,
-                                                    int32_t* __restrict__ k_count,
-                                                    int32_t* __restrict__ k_cost) {
+__device__ __forceinline__ void classify_k_body(const ClassifyKArgs& a, int n, int row) {
   __shared__ int sh_cnt[4], sh_sub[4];
-  const int row = blockIdx.x;  // b * nKB + kb
+  const int32_t* __restrict__ mm = a.mm;
+  const GridArgs ga = a.ga;
+  const int Nq = a.Nq, nQB = a.nQB, bq = a.bq;
+  int32_t* __restrict__ k_queue = a.k_queue;
+  int32_t* __restrict__ k_count = a.k_count;
+  int32_t* __restrict__ k_cost = a.k_cost;
+  // row = b * nKB + kb
   const int tid = threadIdx.x;
   BlockBounds<kMode> bb;
   bb.load(mm, (size_t)row, n, &ga);
@@ -298,6 +338,21 @@ __global__ __launch_bounds__(256) void k_classify_k(const int32_t* __restrict__ 
   }
 }
 
+template <int kMode>
+__global__ __launch_bounds__(256) void k_classify_k(ClassifyKArgs a, int n) {
+  classify_k_body<kMode>(a, n, (int)blockIdx.x);
+}
+
+// Both directions in one launch (the backward's two tile shapes): workgroups below nk run
+// the per-KV-block queues of `ka`, the rest the per-Q-block queues of `qa`.
+template <int kMode, int kR>
+__global__ __launch_bounds__(256) void k_classify_pair(ClassifyKArgs ka, ClassifyQArgs qa,
+                                                       int n, int nk) {
+  const int blk = (int)blockIdx.x;
+  if (blk < nk) classify_k_body<kMode>(ka, n, blk);
+  else classify_q_body<kMode, kR>(qa, n, blk - nk);
+}
+
 // ---- A4: longest-processing-time-first order ----------------------------------
 // Keys (~cost << 32 | index) sorted ascending = cost descending, index ascending.  Lists of
 // up to kRankSortItems keys sort in one workgroup; longer lists are sorted in chunks of
@@ -317,13 +372,13 @@ __device__ __forceinline__ unsigned long long lpt_key(const int32_t* __restrict_
 // write their sorted keys to `run` for merging.
 constexpr int kRankSortItems = 1024;
 constexpr int kRankThreads = 256;
-__global__ __launch_bounds__(kRankThreads) void k_lpt_rank(const int32_t* __restrict__ cost,
-                                                           int32_t* __restrict__ order,
-                                                           unsigned long long* __restrict__ run,
-                                                           int count) {
+__device__ __forceinline__ void lpt_rank_body(const int32_t* __restrict__ cost,
+                                              int32_t* __restrict__ order,
+                                              unsigned long long* __restrict__ run, int count,
+                                              int chunk) {
   __shared__ __align__(16) unsigned long long keys[kRankSortItems];
   const int tid = threadIdx.x;
-  const int c0 = blockIdx.x * kRankSortItems;
+  const int c0 = chunk * kRankSortItems;
   const int n = min(kRankSortItems, count - c0);
 #pragma unroll
   for (int i = tid; i < kRankSortItems; i += kRankThreads)
@@ -347,6 +402,21 @@ __global__ __launch_bounds__(kRankThreads) void k_lpt_rank(const int32_t* __rest
     if (run) run[c0 + rank] = mine;
     else order[rank] = me;
   }
+}
+
+__global__ __launch_bounds__(kRankThreads) void k_lpt_rank(const int32_t* __restrict__ cost,
+                                                           int32_t* __restrict__ order,
+                                                           unsigned long long* __restrict__ run,
+                                                           int count) {
+  lpt_rank_body(cost, order, run, count, (int)blockIdx.x);
+}
+
+// Two lists of at most kRankSortItems keys each, sorted in one launch (blockIdx.x = list).
+__global__ __launch_bounds__(kRankThreads) void k_lpt_rank_pair(
+    const int32_t* __restrict__ cost0, int32_t* __restrict__ order0, int count0,
+    const int32_t* __restrict__ cost1, int32_t* __restrict__ order1, int count1) {
+  if (blockIdx.x == 0) lpt_rank_body(cost0, order0, nullptr, count0, 0);
+  else lpt_rank_body(cost1, order1, nullptr, count1, 0);
 }
 
 // Number of keys in sorted a[0, n) below x.
@@ -418,46 +488,111 @@ __global__ __launch_bounds__(256) void k_expand_mask(MaskArgs m, int b, int Nk, 
 }
 
 // ---- host launchers --------------------------------------------------------------
+namespace {
+
+// Rows of Q-blocks per k_classify_q workgroup: 1 up to 4096 queue rows (every attention call
+// at its own tile shapes), more for longer lists, keeping at least 2048 workgroups.
+int classify_rows_per_wg(int64_t rows) {
+  return rows >= 16384 ? 8 : rows >= 8192 ? 4 : rows > 4096 ? 2 : 1;
+}
+
+template <int kMode>
+void* classify_q_kernel(int R) {
+  return R == 8 ? (void*)k_classify_q<kMode, 8>
+         : R == 4 ? (void*)k_classify_q<kMode, 4>
+         : R == 2 ? (void*)k_classify_q<kMode, 2>
+                  : (void*)k_classify_q<kMode, 1>;
+}
+template <int kMode>
+void* classify_pair_kernel(int R) {
+  return R == 8 ? (void*)k_classify_pair<kMode, 8>
+         : R == 4 ? (void*)k_classify_pair<kMode, 4>
+         : R == 2 ? (void*)k_classify_pair<kMode, 2>
+                  : (void*)k_classify_pair<kMode, 1>;
+}
+int mask_mode(const MaskArgs& m) { return m.n == kBlocksMode ? 2 : (m.n > 0 ? 1 : 0); }
+
+// Block min/max of B mask rows at bk keys per block into mm; with mm2 (four-vector form
+// only), also at bk2 < bk into mm2 in the same pass.
+void launch_minmax(const MaskArgs& m, int B, int Nk, int bk, int32_t* mm, int bk2,
+                   int32_t* mm2, hipStream_t s) {
+  const int nKB = (Nk + bk - 1) / bk;
+  if (nKB == 0) return;
+  const int mode = mask_mode(m);
+  if (mode == 1) {
+    hipLaunchKernelGGL(k_block_minmax_multi, dim3(B * nKB), dim3(64), 0, s, m.start, m.end,
+                       m.n, Nk, nKB, bk, mm);
+  } else if (mode == 0) {
+    const int n_sc = (Nk + 255) / 256, total = B * n_sc;
+    const int grid = min((total + 3) / 4, 2048);
+    const int nKB2 = mm2 ? (Nk + bk2 - 1) / bk2 : 0;
+    hipLaunchKernelGGL(k_block_minmax, dim3(grid), dim3(256), 0, s, m.v, Nk, nKB, bk, n_sc,
+                       total, mm, bk2, nKB2, mm2);
+  }
+}
+
+}  // namespace
+
 hipError_t launch_classify(const MaskArgs& m, int B, int Nq, int Nk, int bq, int bk,
                            const TileOut& out, hipStream_t s) {
   const int nQB = (Nq + bq - 1) / bq, nKB = (Nk + bk - 1) / bk;
   if (B == 0) return hipSuccess;
-  const int mode = m.n == kBlocksMode ? 2 : (m.n > 0 ? 1 : 0);
+  const int mode = mask_mode(m);
   GridArgs ga{m.blocks, (Nq + kMaskBlock - 1) / kMaskBlock, (Nk + kMaskBlock - 1) / kMaskBlock,
               bk, Nk, nKB};
-  if (nKB > 0) {
-    if (mode == 1)
-      hipLaunchKernelGGL(k_block_minmax_multi, dim3(B * nKB), dim3(64), 0, s, m.start, m.end,
-                         m.n, Nk, nKB, bk, out.minmax);
-    else if (mode == 0) {
-      const int n_sc = (Nk + 255) / 256, total = B * n_sc;
-      const int grid = min((total + 3) / 4, 2048);
-      hipLaunchKernelGGL(k_block_minmax, dim3(grid), dim3(256), 0, s, m.v, Nk, nKB, bk, n_sc,
-                         total, out.minmax);
-    }
-  }
+  launch_minmax(m, B, Nk, bk, out.minmax, 0, nullptr, s);
   // with no KV block a Q-block's queue is empty; with no Q-block a KV block's is
   if ((out.tile_class || out.q_queue) && nQB > 0) {
-    // rows per workgroup: 1 up to 4096 queue rows (every attention call at its own tile
-    // shapes), more for longer lists, keeping at least 2048 workgroups
-    const int64_t rows = (int64_t)B * nQB;
-    const int R = rows >= 16384 ? 8 : rows >= 8192 ? 4 : rows > 4096 ? 2 : 1;
+    const int R = classify_rows_per_wg((int64_t)B * nQB);
     const int groups = (nQB + R - 1) / R;
-    using KQ = void (*)(const int32_t*, int, GridArgs, int, int, int, int, int, uint8_t*,
-                        int32_t*, int32_t*, int32_t*);
-    KQ kq;
-    if (R == 8) kq = mode == 2 ? k_classify_q<2, 8> : (mode == 1 ? k_classify_q<1, 8> : k_classify_q<0, 8>);
-    else if (R == 4) kq = mode == 2 ? k_classify_q<2, 4> : (mode == 1 ? k_classify_q<1, 4> : k_classify_q<0, 4>);
-    else if (R == 2) kq = mode == 2 ? k_classify_q<2, 2> : (mode == 1 ? k_classify_q<1, 2> : k_classify_q<0, 2>);
-    else kq = mode == 2 ? k_classify_q<2, 1> : (mode == 1 ? k_classify_q<1, 1> : k_classify_q<0, 1>);
-    hipLaunchKernelGGL(kq, dim3(B * groups), dim3(256), 0, s, out.minmax, m.n, ga, Nq, nQB, nKB,
-                       bq, groups, out.tile_class, out.q_queue, out.q_count, out.q_cost);
+    ClassifyQArgs qa{out.minmax, ga, Nq, nQB, nKB, bq, groups, out.tile_class, out.q_queue,
+                     out.q_count, out.q_cost};
+    void* kq = mode == 2 ? classify_q_kernel<2>(R)
+               : mode == 1 ? classify_q_kernel<1>(R) : classify_q_kernel<0>(R);
+    hipLaunchKernelGGL((void (*)(ClassifyQArgs, int))kq, dim3(B * groups), dim3(256), 0, s, qa,
+                       m.n);
   }
   if (out.k_queue && nKB > 0) {
+    ClassifyKArgs ka{out.minmax, ga, Nq, nQB, nKB, bq, out.k_queue, out.k_count, out.k_cost};
     auto kk = mode == 2 ? k_classify_k<2> : (mode == 1 ? k_classify_k<1> : k_classify_k<0>);
-    hipLaunchKernelGGL(kk, dim3(B * nKB), dim3(256), 0, s, out.minmax, m.n, ga, Nq, nQB, nKB, bq,
-                       out.k_queue, out.k_count, out.k_cost);
+    hipLaunchKernelGGL(kk, dim3(B * nKB), dim3(256), 0, s, ka, m.n);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_classify_pair(const MaskArgs& m, int B, int Nq, int Nk, int bq_k, int bk_k,
+                                const TileOut& out_k, int bq_q, int bk_q, const TileOut& out_q,
+                                hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const int mode = mask_mode(m);
+  const int nQB_k = (Nq + bq_k - 1) / bq_k, nKB_k = (Nk + bk_k - 1) / bk_k;
+  const int nQB_q = (Nq + bq_q - 1) / bq_q, nKB_q = (Nk + bk_q - 1) / bk_q;
+  // block bounds at both block sizes: one pass over the vectors when the K side's blocks
+  // are the larger ones
+  if (mode == 0 && bk_q < bk_k && bk_k % bk_q == 0) {
+    launch_minmax(m, B, Nk, bk_k, out_k.minmax, bk_q, out_q.minmax, s);
+  } else {
+    launch_minmax(m, B, Nk, bk_k, out_k.minmax, 0, nullptr, s);
+    launch_minmax(m, B, Nk, bk_q, out_q.minmax, 0, nullptr, s);
+  }
+  const int nk = (out_k.k_queue && nKB_k > 0) ? B * nKB_k : 0;  // K-side workgroups
+  const bool q_side = (out_q.tile_class || out_q.q_queue) && nQB_q > 0;
+  const int R = classify_rows_per_wg((int64_t)B * nQB_q);
+  const int groups = (nQB_q + R - 1) / R;
+  const int nq = q_side ? B * groups : 0;
+  if (nk + nq == 0) return hipGetLastError();
+  GridArgs ga_k{m.blocks, (Nq + kMaskBlock - 1) / kMaskBlock,
+                (Nk + kMaskBlock - 1) / kMaskBlock, bk_k, Nk, nKB_k};
+  GridArgs ga_q{m.blocks, (Nq + kMaskBlock - 1) / kMaskBlock,
+                (Nk + kMaskBlock - 1) / kMaskBlock, bk_q, Nk, nKB_q};
+  ClassifyKArgs ka{out_k.minmax, ga_k, Nq, nQB_k, nKB_k, bq_k, out_k.k_queue, out_k.k_count,
+                   out_k.k_cost};
+  ClassifyQArgs qa{out_q.minmax, ga_q, Nq, nQB_q, nKB_q, bq_q, groups, out_q.tile_class,
+                   out_q.q_queue, out_q.q_count, out_q.q_cost};
+  void* kp = mode == 2 ? classify_pair_kernel<2>(R)
+             : mode == 1 ? classify_pair_kernel<1>(R) : classify_pair_kernel<0>(R);
+  hipLaunchKernelGGL((void (*)(ClassifyKArgs, ClassifyQArgs, int, int))kp, dim3(nk + nq),
+                     dim3(256), 0, s, ka, qa, m.n, nk);
   return hipGetLastError();
 }
 
@@ -510,6 +645,20 @@ hipError_t launch_lpt_sort(const int32_t* cost, int32_t* order, int count, void*
                        count, len);
     unsigned long long* t = a; a = b; b = t;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_lpt_sort_pair(const int32_t* cost0, int32_t* order0, int count0,
+                                const int32_t* cost1, int32_t* order1, int count1,
+                                void* scratch, hipStream_t s) {
+  if (count0 <= 0 || count1 <= 0 || count0 > kRankSortItems || count1 > kRankSortItems) {
+    hipError_t e = launch_lpt_sort(cost0, order0, count0, scratch, s);
+    if (e == hipSuccess) e = launch_lpt_sort(cost1, order1, count1, scratch, s);
+    return e;
+  }
+  const unsigned parts = (unsigned)((max(count0, count1) + kRankThreads - 1) / kRankThreads);
+  hipLaunchKernelGGL(k_lpt_rank_pair, dim3(2, parts), dim3(kRankThreads), 0, s, cost0, order0,
+                     count0, cost1, order1, count1);
   return hipGetLastError();
 }
 

@@ -134,12 +134,22 @@ struct TileOut {
 // Nq query rows (Q-blocks of bq), Nk keys (KV blocks of bk); B mask rows.
 hipError_t launch_classify(const MaskArgs& m, int B, int Nq, int Nk, int bq, int bk,
                            const TileOut& out, hipStream_t s);
+// The backward's two classifications in fewer launches: K-side queues (out_k.k_queue) at
+// bq_k x bk_k and Q-side queues (out_q.q_queue) at bq_q x bk_q; one block min/max pass
+// where the K side's blocks are a multiple of the Q side's, then one classify launch.
+hipError_t launch_classify_pair(const MaskArgs& m, int B, int Nq, int Nk, int bq_k, int bk_k,
+                                const TileOut& out_k, int bq_q, int bk_q, const TileOut& out_q,
+                                hipStream_t s);
 hipError_t launch_zero_i32(int32_t* p, size_t n, hipStream_t s);
 // order[i] = i for i < n: the natural dispatch order (fm_problem.schedule)
 hipError_t launch_iota_i32(int32_t* p, int n, hipStream_t s);
 size_t lpt_sort_scratch_bytes(int64_t count);
 hipError_t launch_lpt_sort(const int32_t* cost, int32_t* order, int count, void* scratch,
                            hipStream_t s);
+// Two LPT orders; one launch when both lists are short (at most 1024 items), else two sorts.
+hipError_t launch_lpt_sort_pair(const int32_t* cost0, int32_t* order0, int count0,
+                                const int32_t* cost1, int32_t* order1, int count1,
+                                void* scratch, hipStream_t s);
 hipError_t launch_expand_mask(const MaskArgs& m, int b, int Nk, int row0, int row1,
                               uint8_t* dense, hipStream_t s);
 
