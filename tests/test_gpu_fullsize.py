@@ -18,6 +18,11 @@ pytestmark = pytest.mark.gpu
 FULL = workloads.CONFIG_NAMES[1:]   # c1 is covered in full by test_gpu_attention
 # the random-eviction workload also with its keys reordered (fm_problem.key_order = 1)
 FULL = FULL + ["c5_random_eviction_128k:sorted"]
+# the seeded workloads at other seeds too ("@seed": the mask draw and the tensors; the sliding
+# window's mask does not depend on the seed): c2 at seeds 1 and 2, the 32K and 128K workloads
+# at seed 1 (their column checks take most of a minute each)
+FULL = FULL + ["c2_prefix_lm_doc_8k@1", "c2_prefix_lm_doc_8k@2", "c3_share_question_32k@1",
+               "c5_random_eviction_128k:sorted@1"]
 
 
 def visible_per_column(w, b):
@@ -39,31 +44,33 @@ def sample_rows(w, b, rng, k=10):
     return sorted(rows)
 
 
-@pytest.fixture(scope="module")
-def runs():
-    return {}
-
-
-def run_config(name, cache):
-    if name in cache:
-        return cache[name]
+def run_config(name):
     import mask_aware_sparse_amd as fm
-    base, _, variant = name.partition(":")
+    spec, _, seed = name.partition("@")
+    base, _, variant = spec.partition(":")
     key_order = fm.KEYS_SORTED if variant == "sorted" else fm.KEYS_NATURAL
-    w = workloads.make_workload(base)
-    log(f"full-size {name}: B={w.batch} Hq={w.heads_q} Hkv={w.heads_kv} N={w.seqlen}")
+    w = workloads.make_workload(base, int(seed) if seed else 0)
+    log(f"full-size {name}: B={w.batch} Hq={w.heads_q} Hkv={w.heads_kv} N={w.seqlen} "
+        f"seed={w.seed}")
     q, k, v, do, vec = gpu_inputs(w)
     O, LSE = fm.attn_fwd(q, k, v, *vec, key_order=key_order)
     dq, dk, dv = fm.attn_bwd(q, k, v, O, LSE, do, *vec, key_order=key_order)
     torch.cuda.synchronize()
-    cache.clear()
-    cache[name] = (w, (q, k, v, do), (O, LSE, dq, dk, dv))
-    return cache[name]
+    return name, w, (q, k, v, do), (O, LSE, dq, dk, dv)
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_sampled_rows(name, runs):
-    w, (q, k, v, do), (O, LSE, dq, dk, dv) = run_config(name, runs)
+# One run per configuration: a module-scoped parametrized fixture makes pytest group the
+# tests by configuration, so each workload is computed once and freed before the next.
+@pytest.fixture(scope="module", params=FULL)
+def run(request):
+    r = run_config(request.param)
+    yield r
+    del r
+    torch.cuda.empty_cache()
+
+
+def test_sampled_rows(run):
+    name, w, (q, k, v, do), (O, LSE, dq, dk, dv) = run
     rng = np.random.default_rng(1)
     g = w.heads_q // w.heads_kv
     heads = sorted({0, w.heads_q - 1, int(rng.integers(0, w.heads_q))})
@@ -86,9 +93,8 @@ def test_sampled_rows(name, runs):
         log(f"  rows ok b={b} heads={heads} rows={len(rows)}")
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_sampled_columns(name, runs):
-    w, (q, k, v, do), (O, LSE, dq, dk, dv) = run_config(name, runs)
+def test_sampled_columns(run):
+    name, w, (q, k, v, do), (O, LSE, dq, dk, dv) = run
     g = w.heads_q // w.heads_kv
     for b in sorted({0, w.batch - 1}):
         vis = visible_per_column(w, b)
@@ -111,9 +117,8 @@ def test_sampled_columns(name, runs):
         assert eK <= GRAD_TOL and eV <= GRAD_TOL, (name, b)
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_gradient_sum_invariants(name, runs):
-    w, (q, k, v, do), (O, LSE, dq, dk, dv) = run_config(name, runs)
+def test_gradient_sum_invariants(run):
+    name, w, (q, k, v, do), (O, LSE, dq, dk, dv) = run
     g = w.heads_q // w.heads_kv
     live = torch.isfinite(LSE).unsqueeze(-1)
     dO_live = (do.double() * live).view(w.batch, w.heads_kv, g, w.seqlen, 128).sum((2, 3))
