@@ -3,6 +3,8 @@ oracle, on the benchmark's calls.
 
   c2_prefix_lm_doc_8k        the prefix-LM document workload (B=4, 32/8 heads, N=8192), at
                              seeds 0 and 1 (document lengths and tensors)
+  c3_share_question_32k      the share-question workload (B=1, 64 heads on one kv head,
+                             N=32768): 64 heads of the oracle, about a minute on the box
   window4096_sinks64_32k_g8  the sliding-window-with-sinks mask at N=32768, 8 query heads on
                              one kv head: the sink block is seen by every row, so the dK/dV
                              split plan cuts its item into segments that add into the fp32
@@ -27,6 +29,7 @@ pytestmark = pytest.mark.gpu
 WHOLE = {
     "c2_prefix_lm_doc_8k": lambda: workloads.make_workload("c2_prefix_lm_doc_8k"),
     "c2_prefix_lm_doc_8k_seed1": lambda: workloads.make_workload("c2_prefix_lm_doc_8k", 1),
+    "c3_share_question_32k": lambda: workloads.make_workload("c3_share_question_32k"),
     "window4096_sinks64_32k_g8": lambda: workloads.sliding_window_sinks(n=32768, heads_q=8,
                                                                          heads_kv=1),
     "window4096_sinks64_32k_g4": lambda: workloads.sliding_window_sinks(n=32768, heads_q=4,
