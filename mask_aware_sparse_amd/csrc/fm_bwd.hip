@@ -731,14 +731,16 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void k_attn_bwd_dq(DqParams p
   auto load_tile = [&](int e, int buf) {
     const int kb = e & 0x7fffffff;
     if constexpr (kDma) {
+      // the tile's resources in scalar registers: the per-lane offsets stay constant
       const uint32_t tb = (uint32_t)kb * BK * D * 2;
+      const i32x4_t kt_ = rsrc_advance(kw_, tb), vt_ = rsrc_advance(vw_, tb);
 #pragma unroll
       for (int i = 0; i < kDmaPer; ++i) {
         const int j = mk_wave + 4 * i;
         if (i < kKLoads / 4 || j < kKLoads)
-          lds_load16_untracked(kw_, tb + koff[i], lds_addr(&sm.k[buf][j * 512]));
+          lds_load16_untracked(kt_, koff[i], lds_addr(&sm.k[buf][j * 512]));
         if (i < kVLoads / 4 || j < kVLoads)
-          lds_load16_untracked(vw_, tb + voff[i], lds_addr(&sm.v[buf][j * 512]));
+          lds_load16_untracked(vt_, voff[i], lds_addr(&sm.v[buf][j * 512]));
       }
     } else {
       const uint32_t base = (uint32_t)(kb * BK + cp_row) * (D * 2) + cp_ch * 2;

@@ -261,6 +261,19 @@ __device__ __forceinline__ i32x4_t rsrc_words(const void* base, uint32_t bytes) 
   const uint64_t a = (uint64_t)(uintptr_t)base;
   return i32x4_t{(int)(uint32_t)a, (int)((a >> 32) & 0xFFFFu), (int)bytes, kRsrcWord3};
 }
+// The resource r moved forward by `off` bytes (wave-uniform, a multiple of 4, below r's
+// byte count): offsets past the end of r stay past the end of the result, so the bounds
+// check that turns reads past the tensor into zeros is unchanged.  (The scalar offset operand
+// of a buffer load would be cheaper still but is not part of that check.)  Scalar arithmetic.
+__device__ __forceinline__ i32x4_t rsrc_advance(i32x4_t r, uint32_t off) {
+  const uint32_t r0 = __builtin_amdgcn_readfirstlane((uint32_t)r[0]);
+  const uint32_t r1 = __builtin_amdgcn_readfirstlane((uint32_t)r[1]);
+  const uint32_t n = __builtin_amdgcn_readfirstlane((uint32_t)r[2]);
+  const uint32_t o = __builtin_amdgcn_readfirstlane(off);
+  const uint64_t a = ((uint64_t)r0 | ((uint64_t)(r1 & 0xFFFFu) << 32)) + o;
+  // callers pass off < records (a tile that starts inside the tensor)
+  return i32x4_t{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)(n - o), r[3]};
+}
 // 16 bytes per lane from resource r at byte offset voff into LDS at lds + 16 * lane (lds
 // is wave-uniform).  Written in assembly so that the compiler does not track the LDS write:
 // it would otherwise wait for every such load before any transposing LDS read (it cannot

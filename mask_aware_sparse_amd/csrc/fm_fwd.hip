@@ -203,12 +203,13 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void k_attn_fwd(FwdParams p) 
   auto fetch_k = [&](int e, int buf, u32x4 (&ks)[kDma ? 1 : kPasses], uint32_t (&vec)[kVec]) {
     const int kb = e & 0x7fffffff;
     if constexpr (kDma) {
-      const uint32_t tb = (uint32_t)kb * BK * D * 2;
+      // the tile's resource in scalar registers: the per-lane offsets stay constant
+      const i32x4_t kt_ = rsrc_advance(kw_, (uint32_t)kb * BK * D * 2);
 #pragma unroll
       for (int i = 0; i < kDmaPer; ++i) {
         const int j = mk_wave + 4 * i;
         if (i < kKLoads / 4 || j < kKLoads)
-          lds_load16_untracked(kw_, tb + koff[i], lds_addr(&sm.k[buf][j * 512]));
+          lds_load16_untracked(kt_, koff[i], lds_addr(&sm.k[buf][j * 512]));
       }
     } else {
       const uint32_t base = (uint32_t)(kb * BK + cp_row) * (D * 2) + cp_ch * 2;
@@ -232,12 +233,12 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void k_attn_fwd(FwdParams p) 
   auto fetch_v = [&](int e, int buf) {
     const int kb = e & 0x7fffffff;
     if constexpr (kDma) {
-      const uint32_t tb = (uint32_t)kb * BK * D * 2;
+      const i32x4_t vt_ = rsrc_advance(vw_, (uint32_t)kb * BK * D * 2);
 #pragma unroll
       for (int i = 0; i < kDmaPer; ++i) {
         const int j = mk_wave + 4 * i;
         if (i < kVLoads / 4 || j < kVLoads)
-          lds_load16_untracked(vw_, tb + voff[i], lds_addr(&sm.v[buf][j * 512]));
+          lds_load16_untracked(vt_, voff[i], lds_addr(&sm.v[buf][j * 512]));
       }
     } else {
       const uint32_t base = (uint32_t)(kb * BK + cp_row) * (D * 2) + cp_ch * 2;
@@ -368,10 +369,15 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void k_attn_fwd(FwdParams p) 
       const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[hb][j * 8 + t], p.c, -off));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[hb][j * 8 + t + 1], p.c, -off));
       psum[hb] += p0 + p1;
-      const unsigned u = pack_bf16x2(p0, p1);
+      // the packing and the row-sum dot product stay here, among the score MFMAs: left to
+      // itself the compiler sinks them past the slow-path branch, where they hold 32 fp32
+      // values live and run as a block of their own
+      unsigned u = pack_bf16x2(p0, p1);
+      asm volatile("" : "+v"(u));
       packed[hb][j][t / 2] = u;
       pbsum[hb] = __builtin_amdgcn_fdot2_f32_bf16(
           __builtin_bit_cast(bf16x2, u), bf16x2{(bf16)1.0f, (bf16)1.0f}, pbsum[hb], false);
+      asm volatile("" : "+v"(pbsum[hb]));
     };
     auto exponentiate_all = [&](float off) {
       psum[0] = psum[1] = 0.f;
