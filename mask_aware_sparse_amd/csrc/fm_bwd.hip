@@ -845,8 +845,8 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void k_attn_bwd_dq(DqParams p
   const SwzTrRead<kRow> tr(lane, hh);
 
   int e = n_tiles > 0 ? queue[0] : 0;
-  for (int it = 0; it < n_tiles; ++it) {
-    const int cur = it & 1;
+  auto tile = [&](auto cur_c, int it) {
+    const int cur = cur_c;  // the tile's LDS buffer (a constant in the unrolled loop below)
     const int kb = e & 0x7fffffff;
     const bool partial = (e < 0) || (ragged && kb == p.nKB - 1);
     int en = 0;
@@ -938,6 +938,16 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void k_attn_bwd_dq(DqParams p
     if constexpr (kDma) asm volatile("s_waitcnt vmcnt(0)");  // loads into LDS have landed
     lds_barrier();
     e = en;
+  };
+  if constexpr (D <= 128) {
+    // two tiles per trip: each tile's buffer is a constant, its LDS addresses immediates
+    // (dQ 1.2-1.4% faster on the 128K workloads, no spills)
+    for (int it = 0; it < n_tiles; it += 2) {
+      tile(std::integral_constant<int, 0>{}, it);
+      if (it + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, it + 1);
+    }
+  } else {
+    for (int it = 0; it < n_tiles; ++it) tile(it & 1, it);
   }
 
   // D and the log2 LSE go out after the loop: a store before it would keep the compiler

@@ -368,7 +368,9 @@ __global__ __launch_bounds__(256, D > 128 ? 1 : 2) void k_attn_fwd(FwdParams p) 
       const int hb = i / 8, j = (i % 8) / 4, t = (i % 4) * 2;
       const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[hb][j * 8 + t], p.c, -off));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[hb][j * 8 + t + 1], p.c, -off));
-      psum[hb] += p0 + p1;
+      // the first pair of a half starts its sum (an add to 0 cannot be folded: -0 + 0 = +0)
+      if (i % 8 == 0) psum[hb] = p0 + p1;
+      else psum[hb] += p0 + p1;
       // the packing and the row-sum dot product stay here, among the score MFMAs: left to
       // itself the compiler sinks them past the slow-path branch, where they hold 32 fp32
       // values live and run as a block of their own
