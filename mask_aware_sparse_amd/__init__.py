@@ -28,7 +28,7 @@ __all__ = [
     "fm_check_mask_multi",
     "OP_CLASSIFY", "OP_FWD", "OP_BWD", "HEAD_DIM", "key_order", "fm_key_order",
     "KEYS_NATURAL", "KEYS_SORTED", "KEY_ORDER_SPAN", "KEY_ORDER_GROUP", "SCHEDULE_LPT",
-    "SCHEDULE_NATURAL",
+    "SCHEDULE_NATURAL", "flashmask_attention",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -724,6 +724,39 @@ def localize_mask_multi(starts, ends, offsets, chunk_len, out=None, stream=None)
            "fm_localize_mask_multi")
     _keep_alive(stream, starts.device, *(out if fresh else ()))
     return out
+
+
+class _FlashMaskAttention(torch.autograd.Function):
+    """Autograd glue over fm_attn_fwd / fm_attn_bwd: the forward keeps O and the LSE, the
+    backward recomputes P from them in the library's backward kernels."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, lts, lte, uts, ute, scale, key_order):
+        o, lse = attn_fwd(q, k, v, lts, lte, uts, ute, scale=scale, key_order=key_order)
+        ctx.save_for_backward(q, k, v, o, lse, lts, lte, uts, ute)
+        ctx.scale, ctx.key_order = scale, key_order
+        return o
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, o, lse, lts, lte, uts, ute = ctx.saved_tensors
+        if dout.dtype != torch.bfloat16:
+            raise TypeError(f"flashmask_attention: the output gradient must be bfloat16, "
+                            f"got {dout.dtype}")
+        dq, dk, dv = attn_bwd(q, k, v, o, lse, dout.contiguous(), lts, lte, uts, ute,
+                              scale=ctx.scale, key_order=ctx.key_order)
+        return dq, dk, dv, None, None, None, None, None, None
+
+
+def flashmask_attention(q, k, v, lts, lte, uts, ute, scale=None, key_order=KEYS_NATURAL):
+    """O = softmax(Q K^T * scale, masked) V with gradients for q, k and v: the drop-in for a
+    dense-mask scaled-dot-product attention that the FlashMask Guide's integration section
+    describes, taking the column-wise vectors instead of the N x N mask.  Shapes, dtypes and
+    the mask convention are attn_fwd's (bf16 q [B][H_q][N_q][d], k and v [B][H_kv][N_k][d],
+    int32 vectors [B][N_k] or [B][H_m][N_k]; key column j hides rows [LTS_j, LTE_j) and
+    [UTS_j, UTE_j)).  A visible row range [FMS_j, FME_j] of the guide's two-vector form is
+    UTS_j = 0, UTE_j = FMS_j, LTS_j = FME_j + 1, LTE_j = N_q.  The vectors take no gradient."""
+    return _FlashMaskAttention.apply(q, k, v, lts, lte, uts, ute, scale, key_order)
 
 
 # The C names, for callers that prefer them.
