@@ -19,7 +19,7 @@ the published dense bf16 MFMA figure; beside it the line gives the device's CU c
 GFX clock sampled (amdsmi) during the timed steps and the MFMA peak at that clock.
 `--schedule natural` dispatches work items in index order instead of LPT order.
 
-Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
+Prints ONE JSON line.  `--gpus N` with N > 1 exits: the benchmark runs on one GPU.
 `--calibrate-copy MIB` instead runs a plain device-to-device copy of that size (for
 scaling the FETCH_SIZE / WRITE_SIZE counters) and prints its byte count.
 `--classify-bandwidth` instead times fm_classify_tiles (block min/max, classes, both queue
@@ -661,7 +661,7 @@ def main():
                          "removed; per-kernel times still come from eager steps)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; multi-GPU runs are not supported",
+        print("bench.py: the benchmark runs on one GPU only; multi-GPU runs are not supported",
               file=sys.stderr)
         sys.exit(2)
 
