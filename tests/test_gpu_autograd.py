@@ -1,7 +1,8 @@
 """flashmask_attention, the autograd wrapper over fm_attn_fwd / fm_attn_bwd, on the GPU:
 
   * gradients taken by torch.autograd equal the direct calls bit for bit (same kernels;
-    a problem whose dK/dV items store directly, so the backward is deterministic);
+    problems whose dK/dV items store directly, so the backward is deterministic), in the
+    natural key order and with keys regrouped;
   * the guide's two-vector form (key j visible to rows FMS_j..FME_j inclusive; FlashMask
     Guide, "Mathematical Formalization of Column-Wise Sparsity") through the conversion the
     wrapper documents, against the fp64 oracle at the parity tolerances."""
@@ -20,17 +21,28 @@ def _leaf(t):
     return t.detach().clone().requires_grad_(True)
 
 
-def test_autograd_equals_direct_calls():
+CASES = {
+    "prefix_lm_doc_1k_gqa": (lambda: workloads.prefix_lm_doc(0, n=1024, batch=2, heads_q=4,
+                                                             heads_kv=2, lo=128, hi=512), 0),
+    # keys regrouped in super-blocks (key_order = 1): the 256-key dK/dV kernel
+    "random_eviction_4k_sorted": (lambda: workloads.random_eviction(1, n=4096, heads_q=2), 1),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_autograd_equals_direct_calls(name):
     import mask_aware_sparse_amd as fm
-    w = workloads.prefix_lm_doc(0, n=1024, batch=2, heads_q=4, heads_kv=2, lo=128, hi=512)
-    log("autograd vs direct calls: prefix-LM documents N=1024 B=2 Hq=4 Hkv=2")
+    make, key_order = CASES[name]
+    w = make()
+    log(f"autograd vs direct calls: {name} N={w.seqlen} B={w.batch} Hq={w.heads_q} "
+        f"Hkv={w.heads_kv} key_order={key_order}")
     q, k, v, do, vec = gpu_inputs(w)
     ql, kl, vl = _leaf(q), _leaf(k), _leaf(v)
-    o = fm.flashmask_attention(ql, kl, vl, *vec)
+    o = fm.flashmask_attention(ql, kl, vl, *vec, key_order=key_order)
     # d(sum(o * do)) / do = do, exactly representable in bf16
     (o.float() * do.float()).sum().backward()
-    O, LSE = fm.attn_fwd(q, k, v, *vec)
-    dq, dk, dv = fm.attn_bwd(q, k, v, O, LSE, do, *vec)
+    O, LSE = fm.attn_fwd(q, k, v, *vec, key_order=key_order)
+    dq, dk, dv = fm.attn_bwd(q, k, v, O, LSE, do, *vec, key_order=key_order)
     torch.cuda.synchronize()
     assert torch.equal(o.detach(), O)
     assert torch.equal(ql.grad, dq) and torch.equal(kl.grad, dk) and torch.equal(vl.grad, dv)
