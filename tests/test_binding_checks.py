@@ -156,3 +156,15 @@ def test_mixed_devices_refused_on_the_gpu():
         fm.attn_fwd(q, k, v, *gvec, ws=torch.zeros(1 << 24, dtype=torch.uint8))
     with pytest.raises(ValueError, match="k must be on"):
         fm.attn_fwd(q, k.cpu(), v, *gvec)
+
+
+def test_flashmask_attention_checks_like_attn_fwd():
+    """The autograd wrapper validates through attn_fwd: the same refusals, before any call."""
+    q, k, v, vec = inputs()
+    assert "flashmask_attention" in fm.__all__
+    with pytest.raises(ValueError, match="on the GPU"):
+        fm.flashmask_attention(q.clone().requires_grad_(True), k, v, *vec)
+    with pytest.raises(ValueError):
+        fm.flashmask_attention(q, k, v[:, :, :-1].contiguous(), *vec)
+    with pytest.raises(ValueError):
+        fm.flashmask_attention(q, k, v, *vec[:3], vec[3].to(torch.int64))
